@@ -1,0 +1,152 @@
+"""Convolution weight-gradient oracle -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The GPU library (``implicit_gemm_amd``)
+never imports it, and the two share no code.
+
+The arithmetic lives in ``wgrad_ref.c`` (plain C, OpenMP, fp64 accumulation):
+the weight gradient of a 2-D convolution over NHWC tensors, written out as its
+definition (rocm-libraries PR #11188, section Motivation: the ``weight.grad``
+of ``nn.Conv2d``).  This module only compiles that file, marshals numpy arrays
+into it and finishes the normalised-error metric.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "wgrad_ref.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle_wgrad.so")
+_lib = None
+_lock = threading.Lock()
+
+
+def build(force: bool = True, src: str = _SRC, out: str = _LIB_PATH, strict: bool = True) -> str:
+    """Compile the C oracle into a shared library with gcc (-O2, OpenMP)."""
+    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(src):
+        return out
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-Wall"]
+    cmd += ["-Werror"] if strict else []
+    cmd += ["-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def load(path: str | None = None):
+    """Load (building if absent) the oracle library and declare its signatures."""
+    global _lib
+    if path is None and _lib is not None:
+        return _lib
+    with _lock:
+        if path is None and _lib is not None:
+            return _lib
+        p = path or _LIB_PATH
+        if path is None and (not os.path.exists(p) or os.path.getmtime(p) < os.path.getmtime(_SRC)):
+            build(force=True)
+        lib = ctypes.CDLL(p)
+        i64 = ctypes.c_int64
+        lib.oracle_out_size.restype = i64
+        lib.oracle_out_size.argtypes = [i64] * 5
+        lib.oracle_wgrad_accumulate.restype = ctypes.c_int
+        lib.oracle_wgrad_accumulate.argtypes = [i64] * 11 + [ctypes.c_void_p] * 4 + [ctypes.c_int]
+        lib.oracle_max_threads.restype = ctypes.c_int
+        lib.oracle_max_threads.argtypes = []
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def default_threads() -> int:
+    return max(1, len(os.sched_getaffinity(0)))
+
+
+def out_size(n_in: int, k: int, pad: int, stride: int, dil: int, lib=None) -> int:
+    """Output extent along one axis, from the C oracle."""
+    return int((lib or load()).oracle_out_size(n_in, k, pad, stride, dil))
+
+
+class WgradAccumulator:
+    """Streams images through the oracle: dW and the |dY||X| sums in fp64.
+
+    ``add(x, dy)`` adds the contribution of a chunk of images; ``dw`` and
+    ``den`` give the fp64 result [K, R, S, Cg] and max of the |dY|*|X| sums.
+    """
+
+    def __init__(self, C, H, W, K, R, S, pad=0, stride=1, dilation=1, groups=1,
+                 nthreads=None, lib=None):
+        self.lib = lib or load()
+        self.C, self.H, self.W, self.K = C, H, W, K
+        self.R, self.S = R, S
+        self.pad, self.stride, self.dilation, self.groups = pad, stride, dilation, groups
+        if C % groups or K % groups:
+            raise ValueError("C and K must be divisible by groups")
+        self.Cg = C // groups
+        self.Ho = out_size(H, R, pad, stride, dilation, self.lib)
+        self.Wo = out_size(W, S, pad, stride, dilation, self.lib)
+        if self.Ho < 1 or self.Wo < 1:
+            raise ValueError("empty output")
+        self.nthreads = nthreads or default_threads()
+        self._dw = np.zeros((K, R, S, self.Cg), np.float64)
+        self._abs = np.zeros((K, R, S, self.Cg), np.float64)
+        self.images = 0
+
+    def add(self, x: np.ndarray, dy: np.ndarray) -> None:
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        dy = np.ascontiguousarray(dy, dtype=np.float32)
+        nc = x.shape[0]
+        if x.shape != (nc, self.H, self.W, self.C):
+            raise ValueError("x shape %r" % (x.shape,))
+        if dy.shape != (nc, self.Ho, self.Wo, self.K):
+            raise ValueError("dy shape %r, expected %r" % (dy.shape, (nc, self.Ho, self.Wo, self.K)))
+        rc = self.lib.oracle_wgrad_accumulate(
+            nc, self.C, self.H, self.W, self.K, self.R, self.S, self.pad, self.stride,
+            self.dilation, self.groups, x.ctypes.data, dy.ctypes.data, self._dw.ctypes.data,
+            self._abs.ctypes.data, self.nthreads)
+        if rc != 0:
+            raise RuntimeError("oracle_wgrad_accumulate failed: %d" % rc)
+        self.images += nc
+
+    @property
+    def dw(self) -> np.ndarray:
+        return self._dw.copy()
+
+    @property
+    def abs_sum(self) -> np.ndarray:
+        return self._abs.copy()
+
+    @property
+    def den(self) -> float:
+        return float(self._abs.max()) if self._abs.size else 0.0
+
+
+def wgrad_ref(x, dy, R, S, pad=0, stride=1, dilation=1, groups=1, nthreads=None, lib=None):
+    """dW (fp64, [K, R, S, C/groups]) and the error denominator for NHWC x, dy."""
+    x = np.asarray(x)
+    dy = np.asarray(dy)
+    _, H, W, C = x.shape
+    K = dy.shape[3]
+    acc = WgradAccumulator(C, H, W, K, R, S, pad, stride, dilation, groups, nthreads, lib)
+    acc.add(x, dy)
+    return acc.dw, acc.den
+
+
+def normalised_error(dw_test, dw_ref, den) -> float:
+    """max |dW - dW_ref| / max(sum |X||dY|); inf when dw_test has NaN/Inf."""
+    dw_test = np.asarray(dw_test, dtype=np.float64)
+    if not np.all(np.isfinite(dw_test)):
+        return float("inf")
+    diff = float(np.max(np.abs(dw_test - dw_ref))) if dw_ref.size else 0.0
+    if den == 0.0:
+        return 0.0 if diff == 0.0 else float("inf")
+    return diff / den
+
+
+# Acceptance bars of the normalised error: fp32 inputs, and bf16/fp16 inputs.
+TOL = {"f32": 1e-5, "bf16": 4e-3, "f16": 4e-3}

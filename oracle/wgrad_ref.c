@@ -1,0 +1,129 @@
+/*
+ * Convolution weight-gradient oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the test suite, the smoke check and the CPU-baseline leg of the
+ * benchmark may load this library.  The GPU library never links or calls it,
+ * and it shares no source, header or table with the GPU library.
+ *
+ * What it computes: the weight gradient of a 2-D convolution ("weight.grad"
+ * of nn.Conv2d, as in rocm-libraries PR #11188, "fix silent zero wgrad",
+ * section Motivation) over NHWC tensors with groups:
+ *
+ *   dW[k, r, s, c] = sum over n, ho, wo of
+ *       dY[n, ho, wo, k] * Xpad[n, ho*stride + r*dil - pad,
+ *                                  wo*stride + s*dil - pad, g(k)*Cg + c]
+ *
+ *   Cg = C / groups, Kg = K / groups, g(k) = k / Kg,
+ *   Xpad = X inside [0,H) x [0,W) and 0 outside (zero padding, same pad on
+ *   all four sides),
+ *   Ho = (H + 2*pad - dil*(R-1) - 1) / stride + 1, Wo likewise.
+ *
+ * Every product of two fp32 (or bf16/fp16 widened to fp32) values is exact in
+ * fp64, and the sum is accumulated in fp64.  Alongside dW the oracle
+ * accumulates A[k,r,s,c] = sum |dY| * |Xpad| over the same terms; the
+ * largest A is the denominator of the normalised error metric.
+ *
+ * This is the plain definition written out as loops: no blocking, no
+ * reordering beyond splitting the (n, ho) rows over threads.  Each thread
+ * owns a private fp64 copy of dW and A; the copies are added in thread-index
+ * order, so the result is deterministic for a given thread count.
+ *
+ * The "accumulate" form adds the contribution of a chunk of images to dW and
+ * A, so very large batches can be streamed through bounded host memory.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Output extent of one spatial axis (textbook floor formula). */
+int64_t oracle_out_size(int64_t in, int64_t k, int64_t pad, int64_t stride, int64_t dil) {
+  int64_t span = in + 2 * pad - dil * (k - 1) - 1;
+  if (span < 0) return 0;
+  return span / stride + 1;
+}
+
+/*
+ * Add the contribution of nc images to dw and absacc (both [K][R][S][Cg],
+ * fp64, row-major).  x is [nc][H][W][C], dy is [nc][Ho][Wo][K], both fp32.
+ * Returns 0 on success, -1 on invalid arguments, -2 on allocation failure.
+ */
+int oracle_wgrad_accumulate(int64_t nc, int64_t C, int64_t H, int64_t W, int64_t K,
+                            int64_t R, int64_t S, int64_t pad, int64_t stride, int64_t dil,
+                            int64_t groups, const float* x, const float* dy, double* dw,
+                            double* absacc, int nthreads) {
+  if (nc < 0 || C < 1 || H < 1 || W < 1 || K < 1 || R < 1 || S < 1 || pad < 0 ||
+      stride < 1 || dil < 1 || groups < 1 || C % groups != 0 || K % groups != 0)
+    return -1;
+  const int64_t Ho = oracle_out_size(H, R, pad, stride, dil);
+  const int64_t Wo = oracle_out_size(W, S, pad, stride, dil);
+  if (Ho < 1 || Wo < 1) return -1;
+  const int64_t Cg = C / groups, Kg = K / groups;
+  const int64_t E = K * R * S * Cg;
+  if (nc == 0) return 0;
+  if (nthreads < 1) nthreads = 1;
+
+  const int64_t rows = nc * Ho; /* one row = one (n, ho) pair */
+  double* priv = (double*)calloc((size_t)(2 * E * nthreads), sizeof(double));
+  if (!priv) return -2;
+
+#pragma omp parallel num_threads(nthreads)
+  {
+    int t = 0, T = 1;
+#ifdef _OPENMP
+    t = omp_get_thread_num();
+    T = omp_get_num_threads();
+#endif
+    double* my_dw = priv + (int64_t)t * 2 * E;
+    double* my_abs = my_dw + E;
+    const int64_t row_lo = rows * t / T, row_hi = rows * (t + 1) / T;
+    for (int64_t row = row_lo; row < row_hi; ++row) {
+      const int64_t n = row / Ho, ho = row % Ho;
+      for (int64_t wo = 0; wo < Wo; ++wo) {
+        const float* dy_px = dy + ((n * Ho + ho) * Wo + wo) * K;
+        for (int64_t k = 0; k < K; ++k) {
+          const double g = (double)dy_px[k];
+          const int64_t grp = k / Kg;
+          for (int64_t r = 0; r < R; ++r) {
+            const int64_t h = ho * stride + r * dil - pad;
+            if (h < 0 || h >= H) continue; /* zero padding */
+            for (int64_t s = 0; s < S; ++s) {
+              const int64_t w = wo * stride + s * dil - pad;
+              if (w < 0 || w >= W) continue; /* zero padding */
+              const float* x_px = x + ((n * H + h) * W + w) * C + grp * Cg;
+              double* d = my_dw + ((k * R + r) * S + s) * Cg;
+              double* a = my_abs + ((k * R + r) * S + s) * Cg;
+              for (int64_t c = 0; c < Cg; ++c) {
+                const double v = (double)x_px[c];
+                d[c] += g * v;
+                a[c] += fabs(g) * fabs(v);
+              }
+            }
+          }
+        }
+      }
+    }
+  }
+  /* Fold the per-thread copies in ascending thread order. */
+  for (int t = 0; t < nthreads; ++t) {
+    const double* p = priv + (int64_t)t * 2 * E;
+    for (int64_t e = 0; e < E; ++e) {
+      dw[e] += p[e];
+      absacc[e] += p[E + e];
+    }
+  }
+  free(priv);
+  return 0;
+}
+
+/* Number of threads the OpenMP runtime would give a parallel region. */
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
