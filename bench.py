@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X convolution weight gradient (one GPU).
+
+A step is one full weight-gradient call (stage 1 + the slab reduce when the
+plan has several slices) on inputs already resident in HBM.  The default
+workload is the 3x3 fp32 wgrad, N=32, C=K=64, H=W=56, pad 1.  Prints one
+JSON line:
+
+  value           TFLOP/s of the whole call over K back-to-back steps
+  roofline        the stage-1 kernel alone, timed with HIP events recorded on
+                  its own stream around each launch in the timed region,
+                  against the MI355X peak of its bound (f32 MFMA or HBM)
+  cold_cache      per-call event times with a 1 GiB cache flush before each call
+  cpu_baseline    the CPU oracle (test infrastructure) timed on the host cores
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {  # MI355X published peaks
+    "hbm_gbs": 8000.0,
+    "mfma_tflops": {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6},
+}
+DEFAULT_CONFIG = "c2_3x3_f32"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Hip:
+    """HIP events through the runtime torch already loaded (same SONAME)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        ev = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(ev)) == 0
+        return ev.value
+
+    def record(self, ev, stream):
+        assert self.lib.hipEventRecord(ev, stream) == 0
+
+    def elapsed_ms(self, a, b):
+        assert self.lib.hipEventSynchronize(b) == 0
+        ms = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return float(ms.value)
+
+    def destroy(self, ev):
+        self.lib.hipEventDestroy(ev)
+
+
+def roofline_for(shape, dtype, seconds):
+    import wgrad_data as wd
+    flops = shape.flops()
+    nbytes = shape.algorithmic_bytes(wd.IN_BYTES[dtype])
+    t_mfma = flops / (PEAK["mfma_tflops"][dtype] * 1e12)
+    t_hbm = nbytes / (PEAK["hbm_gbs"] * 1e9)
+    bound = "mfma" if t_mfma >= t_hbm else "hbm"
+    if shape.groups > 1 and shape.Cg <= 8:
+        bound = "hbm"  # direct small-group path: its metric is achieved HBM bandwidth
+    if bound == "mfma":
+        achieved = flops / seconds / 1e12
+        return {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK["mfma_tflops"][dtype],
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK["mfma_tflops"][dtype], 4),
+                "traffic": None}
+    achieved = nbytes / seconds / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm_gbs"], "unit": "GB/s",
+            "frac": round(achieved / PEAK["hbm_gbs"], 4), "traffic": None}
+
+
+def cpu_baseline(wl, x, dy, reps):
+    import oracle
+    s = wl.shape
+    threads = oracle.default_threads()
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        oracle.wgrad_ref(x, dy, s.R, s.S, s.pad, s.stride, s.dilation, s.groups, nthreads=threads)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    return {"value": round(s.flops() / t / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "whole workload (%s), median of %d runs, fp64 C oracle, %.2f s per run"
+                      % (wl.name, reps, t)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default=DEFAULT_CONFIG)
+    ap.add_argument("--split-k", type=int, default=-1)
+    ap.add_argument("--cold", type=int, default=20, help="cold-cache calls (0 = skip)")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the weight-gradient path runs on a single MI355X "
+              "(--gpus %d is not supported)" % args.gpus, file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import implicit_gemm_amd as iga
+    import wgrad_data as wd
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    wl = wd.WORKLOADS[args.config]
+    s = wl.shape
+    if s.N > 64 and wl.n_sweep:
+        s = s.with_n(64)
+        wl = wd.Workload(wl.name, s, wl.dtype, wl.x_dist, wl.dy_dist, wl.seed, wl.note)
+    log("workload", wl.name, s, wl.dtype)
+    x_h, dy_h = wd.make_inputs(wl)
+    dev = torch.device("cuda:0")
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[wl.dtype]
+    x = torch.from_numpy(x_h).to(tdt).to(dev)
+    dy = torch.from_numpy(dy_h).to(tdt).to(dev)
+    d = iga.desc_for(x, dy, s.R, s.S, s.pad, s.stride, s.dilation, s.groups, args.split_k)
+    plan = iga.get_plan(d)
+    dw = torch.empty((s.K, s.R, s.S, s.Cg), dtype=torch.float32, device=dev)
+    ws_bytes = int(plan.ws_bytes)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    hip = Hip()
+    torch.cuda.synchronize()
+
+    def step(ev0=0, ev1=0):
+        iga.conv_wgrad_timed(d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(),
+                             ws.data_ptr() if ws_bytes else 0, ws_bytes, sp, ev0, ev1)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: K back-to-back steps; events around every stage-1 launch.
+    evs = [(hip.event(), hip.event()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(*evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k_ms = [hip.elapsed_ms(a, b) for a, b in evs]
+    for a, b in evs:
+        hip.destroy(a)
+        hip.destroy(b)
+
+    # Cold-cache calls (outside the timed region): a 1 GiB write before each.
+    cold = None
+    if args.cold > 0:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        e0, e1, e2 = hip.event(), hip.event(), hip.event()
+        whole, stage1 = [], []
+        for _ in range(args.cold):
+            flush.fill_(1.0)
+            hip.record(e0, sp)
+            step(e1, e2)
+            e3 = hip.event()
+            hip.record(e3, sp)
+            whole.append(hip.elapsed_ms(e0, e3))
+            stage1.append(hip.elapsed_ms(e1, e2))
+            hip.destroy(e3)
+        whole.sort()
+        cold = {"call_ms_median": round(statistics.median(whole), 5), "call_ms_min": round(whole[0], 5),
+                "call_ms_p90": round(whole[int(0.9 * (len(whole) - 1))], 5),
+                "stage1_ms_median": round(statistics.median(stage1), 5),
+                "tflops_median": round(s.flops() / (statistics.median(whole) * 1e-3) / 1e12, 3)}
+        del flush
+
+    torch.cuda.synchronize()
+    dw_h = dw.cpu().numpy()
+    zeros = int((dw_h == 0).sum())
+    finite = bool(np.isfinite(dw_h).all())
+
+    ms_per_step = wall / args.steps * 1e3
+    value = s.flops() / (wall / args.steps) / 1e12
+    stage1_avg_s = statistics.mean(k_ms) * 1e-3
+    roof = roofline_for(s, wl.dtype, stage1_avg_s)
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(wl, x_h, dy_h, args.cpu_reps)
+
+    out = {
+        "metric": "wgrad TFLOP/s and % of MFMA-or-HBM roofline per conv shape, 1xMI355X",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded PCG64 per image)",
+        "config": {"workload": wl.name, "note": wl.note, "N": s.N, "C": s.C, "H": s.H, "W": s.W,
+                   "K": s.K, "R": s.R, "S": s.S, "pad": s.pad, "stride": s.stride,
+                   "dilation": s.dilation, "groups": s.groups, "split_k": args.split_k,
+                   "ks_count": int(plan.ks_count), "path": int(plan.path), "variant": int(plan.variant),
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "stage1_ms_mean": round(stage1_avg_s * 1e3, 5),
+        "cold_cache": cold,
+        "cpu_baseline": cpu,
+        "check": {"zeros": zeros, "finite": finite},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

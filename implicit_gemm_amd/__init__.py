@@ -1,0 +1,185 @@
+"""MI355X (gfx950) convolution weight gradient: thin Python binding of libconvwgrad.so.
+
+Every step of the computation runs in the library's HIP kernels; this module
+only marshals arguments (descriptor, device pointers, the current HIP stream)
+through ctypes.  PyTorch is used for device memory and streams.  There is no
+fallback: if the library is missing or a call fails, an exception is raised.
+
+    dw = wgrad(x, dy, R=3, S=3, pad=1)          # x [N,H,W,C], dy [N,Ho,Wo,K] -> dw [K,R,S,C/groups] fp32
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libconvwgrad.so")
+
+F32, BF16, F16 = 0, 1, 2
+PATH_DENSE, PATH_DIRECT = 0, 1
+
+STATUS = {
+    0: "OK", 1: "ERR_NULL_ARG", 2: "ERR_BAD_SHAPE", 3: "ERR_BAD_DTYPE", 4: "ERR_BAD_SPLIT",
+    5: "ERR_UNSUPPORTED", 6: "ERR_MISALIGNED", 7: "ERR_WORKSPACE", 8: "ERR_HIP",
+}
+
+
+class Desc(ctypes.Structure):
+    """conv_wgrad_desc_t."""
+    _fields_ = [(n, ctypes.c_int64) for n in
+                ("N", "C", "H", "W", "K", "R", "S", "pad", "stride", "dilation", "groups")] + \
+               [("dtype", ctypes.c_int32), ("split_k", ctypes.c_int32)]
+
+
+class Plan(ctypes.Structure):
+    """conv_wgrad_plan_t."""
+    _fields_ = [("path", ctypes.c_int32), ("variant", ctypes.c_int32),
+                ("Ho", ctypes.c_int64), ("Wo", ctypes.c_int64), ("L", ctypes.c_int64),
+                ("E", ctypes.c_int64), ("unit_rows", ctypes.c_int64), ("units", ctypes.c_int64),
+                ("units_per_slice", ctypes.c_int64), ("ks_count", ctypes.c_int32),
+                ("needs_reduce", ctypes.c_int32), ("tiles", ctypes.c_int64), ("grid", ctypes.c_int64),
+                ("slab_stride", ctypes.c_int64), ("ws_bytes", ctypes.c_uint64),
+                ("x_bytes", ctypes.c_uint64), ("dy_bytes", ctypes.c_uint64),
+                ("dw_bytes", ctypes.c_uint64), ("windows_4g", ctypes.c_int64)]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class ConvWgradError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        self.name = STATUS.get(status, "UNKNOWN")
+        msg = "%s (%d)" % (self.name, status)
+        try:
+            msg += ": " + load().conv_wgrad_status_string(status).decode()
+        except Exception:  # library itself unavailable
+            pass
+        super().__init__(msg + (" [%s]" % what if what else ""))
+
+
+_lib = None
+
+
+def load():
+    """Load libconvwgrad.so (built in-tree by implicit_gemm_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libconvwgrad.so is not built (%s); run `python -m implicit_gemm_amd.build`"
+                          % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    lib.conv_wgrad_status_string.restype = ctypes.c_char_p
+    lib.conv_wgrad_status_string.argtypes = [ctypes.c_int]
+    lib.conv_wgrad_workspace_size.restype = ctypes.c_int
+    lib.conv_wgrad_workspace_size.argtypes = [P(Desc), P(ctypes.c_size_t)]
+    lib.conv_wgrad_get_plan.restype = ctypes.c_int
+    lib.conv_wgrad_get_plan.argtypes = [P(Desc), P(Plan)]
+    lib.conv_wgrad.restype = ctypes.c_int
+    lib.conv_wgrad.argtypes = [P(Desc), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                               ctypes.c_void_p, ctypes.c_void_p]
+    lib.conv_wgrad_ex.restype = ctypes.c_int
+    lib.conv_wgrad_ex.argtypes = [P(Desc), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.conv_wgrad_timed.restype = ctypes.c_int
+    lib.conv_wgrad_timed.argtypes = [P(Desc), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_void_p]
+    _lib = lib
+    return lib
+
+
+def make_desc(N, C, H, W, K, R, S, pad=0, stride=1, dilation=1, groups=1, dtype=F32,
+              split_k=-1) -> Desc:
+    return Desc(N, C, H, W, K, R, S, pad, stride, dilation, groups, dtype, split_k)
+
+
+def get_plan(desc: Desc) -> Plan:
+    p = Plan()
+    st = load().conv_wgrad_get_plan(ctypes.byref(desc), ctypes.byref(p))
+    if st != 0:
+        raise ConvWgradError(st, "get_plan")
+    return p
+
+
+def workspace_size(desc: Desc) -> int:
+    n = ctypes.c_size_t(0)
+    st = load().conv_wgrad_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if st != 0:
+        raise ConvWgradError(st, "workspace_size")
+    return int(n.value)
+
+
+def conv_wgrad(desc: Desc, x_ptr: int, dy_ptr: int, dw_ptr: int, ws_ptr: int, stream: int) -> None:
+    """Raw call: device pointers as integers; raises on a non-OK status."""
+    st = load().conv_wgrad(ctypes.byref(desc), x_ptr, dy_ptr, dw_ptr, ws_ptr or None, stream or None)
+    if st != 0:
+        raise ConvWgradError(st, "conv_wgrad")
+
+
+def conv_wgrad_ex(desc: Desc, x_ptr: int, dy_ptr: int, dw_ptr: int, ws_ptr: int, ws_bytes: int,
+                  stream: int) -> None:
+    st = load().conv_wgrad_ex(ctypes.byref(desc), x_ptr, dy_ptr, dw_ptr, ws_ptr or None, ws_bytes,
+                              stream or None)
+    if st != 0:
+        raise ConvWgradError(st, "conv_wgrad_ex")
+
+
+def conv_wgrad_timed(desc: Desc, x_ptr: int, dy_ptr: int, dw_ptr: int, ws_ptr: int, ws_bytes: int,
+                     stream: int, ev_begin: int, ev_end: int) -> None:
+    """conv_wgrad with HIP events recorded around the stage-1 kernel."""
+    st = load().conv_wgrad_timed(ctypes.byref(desc), x_ptr, dy_ptr, dw_ptr, ws_ptr or None, ws_bytes,
+                                 stream or None, ev_begin or None, ev_end or None)
+    if st != 0:
+        raise ConvWgradError(st, "conv_wgrad_timed")
+
+
+def _dtype_code(t):
+    import torch
+    codes = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+    if t.dtype not in codes:
+        raise TypeError("x / dy must be float32, bfloat16 or float16, got %s" % t.dtype)
+    return codes[t.dtype]
+
+
+def desc_for(x, dy, R, S, pad=0, stride=1, dilation=1, groups=1, split_k=-1) -> Desc:
+    """Descriptor for NHWC torch tensors x [N,H,W,C] and dy [N,Ho,Wo,K]."""
+    if x.dim() != 4 or dy.dim() != 4:
+        raise ValueError("x and dy must be 4-D NHWC tensors")
+    if x.dtype != dy.dtype:
+        raise TypeError("x and dy must have the same dtype")
+    N, H, W, C = x.shape
+    K = dy.shape[3]
+    return make_desc(N, C, H, W, K, R, S, pad, stride, dilation, groups, _dtype_code(x), split_k)
+
+
+def wgrad(x, dy, R, S, pad=0, stride=1, dilation=1, groups=1, split_k=-1, dw=None, workspace=None,
+          stream=None):
+    """Weight gradient dW [K, R, S, C/groups] (fp32) of NHWC x and dy on the current HIP stream."""
+    import torch
+    d = desc_for(x, dy, R, S, pad, stride, dilation, groups, split_k)
+    plan = get_plan(d)
+    if tuple(dy.shape) != (d.N, plan.Ho, plan.Wo, d.K):
+        raise ValueError("dy shape %s does not match [N, Ho, Wo, K] = %s"
+                         % (tuple(dy.shape), (d.N, plan.Ho, plan.Wo, d.K)))
+    if not (x.is_cuda and dy.is_cuda) or x.device != dy.device:
+        raise ValueError("x and dy must be on the same GPU")
+    if not (x.is_contiguous() and dy.is_contiguous()):
+        raise ValueError("x and dy must be contiguous NHWC")
+    shape = (d.K, d.R, d.S, d.C // d.groups)
+    if dw is None:
+        dw = torch.empty(shape, dtype=torch.float32, device=x.device)
+    elif tuple(dw.shape) != shape or dw.dtype != torch.float32 or not dw.is_contiguous():
+        raise ValueError("dw must be a contiguous float32 tensor of shape %s" % (shape,))
+    ws_bytes = plan.ws_bytes
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    conv_wgrad_ex(d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(),
+                  workspace.data_ptr() if ws_bytes else 0,
+                  workspace.numel() * workspace.element_size() if ws_bytes else 0,
+                  stream.cuda_stream)
+    return dw

@@ -1,0 +1,140 @@
+// C ABI: validation, plan cache and launch sequencing.
+//
+// conv_wgrad validates synchronously, looks the plan up (or builds it), then
+// enqueues stage 1 and, when the plan has more than one slice, the slab
+// reduce, on the caller's stream, and returns without synchronising.  The
+// plan (and everything packed from it) is built once per descriptor, outside
+// any timed loop (the launch-binding lesson of rocm-libraries PR #14393,
+// section Benchmark).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <unordered_map>
+
+#include "../../include/conv_wgrad.h"
+#include "kernels.h"
+#include "plan.h"
+
+namespace {
+
+std::mutex g_mutex;
+std::unordered_map<std::string, cw::Plan>* g_plans = nullptr;
+
+conv_wgrad_status_t get_plan(const conv_wgrad_desc_t* desc, cw::Plan* out) {
+  if (!desc) return CONV_WGRAD_ERR_NULL_ARG;
+  const std::string key(reinterpret_cast<const char*>(desc), sizeof(*desc));
+  {
+    std::lock_guard<std::mutex> lock(g_mutex);
+    if (g_plans) {
+      auto it = g_plans->find(key);
+      if (it != g_plans->end()) {
+        *out = it->second;
+        return CONV_WGRAD_OK;
+      }
+    }
+  }
+  conv_wgrad_status_t st = cw::make_plan(desc, out);
+  if (st != CONV_WGRAD_OK) return st;
+  std::lock_guard<std::mutex> lock(g_mutex);
+  if (!g_plans) g_plans = new std::unordered_map<std::string, cw::Plan>();
+  if (g_plans->size() > 4096) g_plans->clear();  // bound the cache; plans are cheap to rebuild
+  (*g_plans)[key] = *out;
+  return CONV_WGRAD_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+conv_wgrad_status_t run(const conv_wgrad_desc_t* desc, const void* x, const void* dy, float* dw,
+                        void* workspace, bool check_ws, size_t ws_bytes, void* stream,
+                        void* ev_begin = nullptr, void* ev_end = nullptr) {
+  cw::Plan plan;
+  conv_wgrad_status_t st = get_plan(desc, &plan);
+  if (st != CONV_WGRAD_OK) return st;
+  if (!x || !dy || !dw) return CONV_WGRAD_ERR_NULL_ARG;
+  if (plan.pub.ws_bytes > 0 && !workspace) return CONV_WGRAD_ERR_NULL_ARG;
+  if (check_ws && ws_bytes < plan.pub.ws_bytes) return CONV_WGRAD_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(dy) || !aligned16(dw) ||
+      (plan.pub.ws_bytes > 0 && !aligned16(workspace)))
+    return CONV_WGRAD_ERR_MISALIGNED;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  cw::Stage1Out out;
+  if (plan.pub.needs_reduce) {
+    out.base = static_cast<float*>(workspace);
+    out.slab_stride = plan.pub.slab_stride;
+  } else {
+    out.base = dw;
+    out.slab_stride = 0;
+  }
+  hipError_t err;
+  if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess)
+    return CONV_WGRAD_ERR_HIP;
+  err = plan.pub.path == CONV_WGRAD_PATH_DIRECT ? cw::launch_direct(plan, x, dy, out, s)
+                                                : cw::launch_dense(plan, x, dy, out, s);
+  if (err != hipSuccess) return CONV_WGRAD_ERR_HIP;
+  if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), s) != hipSuccess)
+    return CONV_WGRAD_ERR_HIP;
+  if (plan.pub.needs_reduce) {
+    err = cw::launch_slab_reduce(plan, static_cast<const float*>(workspace), dw, s);
+    if (err != hipSuccess) return CONV_WGRAD_ERR_HIP;
+  }
+  return CONV_WGRAD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* conv_wgrad_status_string(conv_wgrad_status_t status) {
+  switch (status) {
+    case CONV_WGRAD_OK: return "ok";
+    case CONV_WGRAD_ERR_NULL_ARG: return "null argument";
+    case CONV_WGRAD_ERR_BAD_SHAPE: return "invalid shape";
+    case CONV_WGRAD_ERR_BAD_DTYPE: return "invalid dtype";
+    case CONV_WGRAD_ERR_BAD_SPLIT: return "invalid split_k (must be -1 or >= 1)";
+    case CONV_WGRAD_ERR_UNSUPPORTED: return "unsupported problem (outside documented limits)";
+    case CONV_WGRAD_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+    case CONV_WGRAD_ERR_WORKSPACE: return "workspace too small";
+    case CONV_WGRAD_ERR_HIP: return "HIP runtime error at launch";
+  }
+  return "unknown status";
+}
+
+conv_wgrad_status_t conv_wgrad_get_plan(const conv_wgrad_desc_t* desc, conv_wgrad_plan_t* plan) {
+  if (!desc || !plan) return CONV_WGRAD_ERR_NULL_ARG;
+  cw::Plan p;
+  conv_wgrad_status_t st = get_plan(desc, &p);
+  if (st != CONV_WGRAD_OK) return st;
+  *plan = p.pub;
+  return CONV_WGRAD_OK;
+}
+
+conv_wgrad_status_t conv_wgrad_workspace_size(const conv_wgrad_desc_t* desc, size_t* bytes) {
+  if (!desc || !bytes) return CONV_WGRAD_ERR_NULL_ARG;
+  cw::Plan p;
+  conv_wgrad_status_t st = get_plan(desc, &p);
+  if (st != CONV_WGRAD_OK) return st;
+  *bytes = (size_t)p.pub.ws_bytes;
+  return CONV_WGRAD_OK;
+}
+
+conv_wgrad_status_t conv_wgrad(const conv_wgrad_desc_t* desc, const void* x, const void* dy,
+                               float* dw, void* workspace, void* stream) {
+  return run(desc, x, dy, dw, workspace, false, 0, stream);
+}
+
+conv_wgrad_status_t conv_wgrad_ex(const conv_wgrad_desc_t* desc, const void* x, const void* dy,
+                                  float* dw, void* workspace, size_t ws_bytes, void* stream) {
+  return run(desc, x, dy, dw, workspace, true, ws_bytes, stream);
+}
+
+conv_wgrad_status_t conv_wgrad_timed(const conv_wgrad_desc_t* desc, const void* x, const void* dy,
+                                     float* dw, void* workspace, size_t ws_bytes, void* stream,
+                                     void* stage1_begin, void* stage1_end) {
+  return run(desc, x, dy, dw, workspace, true, ws_bytes, stream, stage1_begin, stage1_end);
+}
+
+}  // extern "C"

@@ -1,0 +1,38 @@
+// Small device helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cw {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Element types of x / dy as stored in memory.
+struct Bf16 { uint16_t bits; };
+struct F16 { _Float16 v; };
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(Bf16 v) { return __uint_as_float((uint32_t)v.bits << 16); }
+__device__ __forceinline__ float to_f32(F16 v) { return (float)v.v; }
+
+// Load 4 consecutive elements (16 B for fp32, 8 B for 16-bit) from an
+// address aligned to 4 elements, widened to fp32.
+__device__ __forceinline__ void load4(const float* p, float out[4]) {
+  const float4 v = *reinterpret_cast<const float4*>(p);
+  out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+}
+__device__ __forceinline__ void load4(const Bf16* p, float out[4]) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  out[0] = __uint_as_float(v.x << 16);
+  out[1] = __uint_as_float(v.x & 0xffff0000u);
+  out[2] = __uint_as_float(v.y << 16);
+  out[3] = __uint_as_float(v.y & 0xffff0000u);
+}
+__device__ __forceinline__ void load4(const F16* p, float out[4]) {
+  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+  const h4 v = *reinterpret_cast<const h4*>(p);
+  out[0] = (float)v[0]; out[1] = (float)v[1]; out[2] = (float)v[2]; out[3] = (float)v[3];
+}
+
+}  // namespace cw

@@ -1,0 +1,171 @@
+// Problem validation and execution planning (host, integer-only).
+#include "plan.h"
+
+#include <string.h>
+
+namespace cw {
+
+namespace {
+
+// Checked a * b for non-negative operands; false on overflow.
+bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+
+bool mul3(int64_t a, int64_t b, int64_t c, int64_t* out) {
+  int64_t t;
+  return mul_ok(a, b, &t) && mul_ok(t, c, out);
+}
+
+bool mul4(int64_t a, int64_t b, int64_t c, int64_t d, int64_t* out) {
+  int64_t t;
+  return mul3(a, b, c, &t) && mul_ok(t, d, out);
+}
+
+// Output extent along one axis; -1 when it would be < 1 or overflows.
+int64_t extent(int64_t in, int64_t k, int64_t pad, int64_t stride, int64_t dil) {
+  int64_t span_k, twice_pad, span;
+  if (!mul_ok(dil, k - 1, &span_k) || !mul_ok(pad, 2, &twice_pad)) return -1;
+  if (__builtin_add_overflow(in, twice_pad, &span)) return -1;
+  span = span - span_k - 1;
+  if (span < 0) return -1;
+  return span / stride + 1;
+}
+
+constexpr int64_t kI32Max = 2147483647;
+// Reduction rows stay below 2^31 with room for one rounded-up slice.
+constexpr int64_t kMaxRows = kI32Max - 65536;
+
+}  // namespace
+
+conv_wgrad_status_t canonicalise(const conv_wgrad_desc_t* d, Problem* o) {
+  if (!d || !o) return CONV_WGRAD_ERR_NULL_ARG;
+  memset(o, 0, sizeof(*o));
+  if (d->dtype != CONV_WGRAD_F32 && d->dtype != CONV_WGRAD_BF16 && d->dtype != CONV_WGRAD_F16)
+    return CONV_WGRAD_ERR_BAD_DTYPE;
+  if (d->split_k == 0 || d->split_k < -1) return CONV_WGRAD_ERR_BAD_SPLIT;
+  if (d->N < 1 || d->C < 1 || d->H < 1 || d->W < 1 || d->K < 1 || d->R < 1 || d->S < 1 ||
+      d->pad < 0 || d->stride < 1 || d->dilation < 1 || d->groups < 1)
+    return CONV_WGRAD_ERR_BAD_SHAPE;
+  if (d->C % d->groups != 0 || d->K % d->groups != 0) return CONV_WGRAD_ERR_BAD_SHAPE;
+  o->N = d->N; o->C = d->C; o->H = d->H; o->W = d->W; o->K = d->K; o->R = d->R; o->S = d->S;
+  o->pad = d->pad; o->stride = d->stride; o->dil = d->dilation; o->groups = d->groups;
+  o->dtype = d->dtype;
+  o->esize = d->dtype == CONV_WGRAD_F32 ? 4 : 2;
+  o->Ho = extent(d->H, d->R, d->pad, d->stride, d->dilation);
+  o->Wo = extent(d->W, d->S, d->pad, d->stride, d->dilation);
+  if (o->Ho < 1 || o->Wo < 1) return CONV_WGRAD_ERR_BAD_SHAPE;
+  o->Cg = d->C / d->groups;
+  o->Kg = d->K / d->groups;
+  int64_t x_elems, dy_elems, t;
+  if (!mul3(o->N, o->Ho, o->Wo, &o->L) || !mul3(o->R, o->S, o->Cg, &o->cols) ||
+      !mul_ok(o->K, o->cols, &o->E) || !mul3(o->H, o->W, o->C, &o->x_img) ||
+      !mul3(o->Ho, o->Wo, o->K, &o->dy_img) || !mul_ok(o->N, o->x_img, &x_elems) ||
+      !mul_ok(o->N, o->dy_img, &dy_elems) || !mul_ok(x_elems, o->esize, &t) ||
+      !mul_ok(dy_elems, o->esize, &t) || !mul_ok(o->E, 4, &t))
+    return CONV_WGRAD_ERR_BAD_SHAPE;
+  o->x_bytes = (uint64_t)x_elems * (uint64_t)o->esize;
+  o->dy_bytes = (uint64_t)dy_elems * (uint64_t)o->esize;
+  o->dw_bytes = (uint64_t)o->E * 4u;
+  // Documented limits: offsets inside one image, the reduction index and the
+  // dW index are 32-bit in the kernels; bases of images are 64-bit.
+  if (o->x_img > kI32Max || o->dy_img > kI32Max || o->L > kMaxRows || o->E > kI32Max ||
+      o->H > kI32Max / 2 || o->W > kI32Max / 2 || o->pad > kI32Max / 4 ||
+      o->stride > kI32Max / 4 || o->dil > kI32Max / 4 || o->R > kI32Max / 4 || o->S > kI32Max / 4)
+    return CONV_WGRAD_ERR_UNSUPPORTED;
+  return CONV_WGRAD_OK;
+}
+
+conv_wgrad_status_t choose_split(int64_t units, int64_t tiles, int32_t requested, int64_t min_units,
+                                 int64_t target_groups, const Problem& p, conv_wgrad_plan_t* pub) {
+  int64_t degree;
+  if (requested >= 1) {
+    degree = requested;
+  } else {
+    // Auto: enough workgroups to fill the device, each slice at least
+    // min_units deep, and slab traffic (written once, read once) at most a
+    // quarter of the algorithmic bytes.
+    degree = ceil_div(target_groups, tiles);
+    int64_t by_depth = units / (min_units > 0 ? min_units : 1);
+    if (by_depth < 1) by_depth = 1;
+    if (degree > by_depth) degree = by_depth;
+    uint64_t alg = p.x_bytes + p.dy_bytes + p.dw_bytes;
+    uint64_t slab = (uint64_t)p.E * 8u;  // 4 bytes written + 4 bytes read per slab element
+    int64_t by_traffic = (int64_t)(alg / (4u * slab));
+    if (by_traffic < 1) by_traffic = 1;
+    if (degree > by_traffic) degree = by_traffic;
+    if (degree < 1) degree = 1;
+  }
+  if (degree > units) degree = units;
+  pub->units = units;
+  pub->units_per_slice = ceil_div(units, degree);
+  int64_t ks = ceil_div(units, pub->units_per_slice);
+  if (ks > kI32Max) return CONV_WGRAD_ERR_UNSUPPORTED;
+  pub->ks_count = (int32_t)ks;
+  pub->needs_reduce = ks > 1 ? 1 : 0;
+  pub->tiles = tiles;
+  int64_t grid;
+  if (!mul_ok(tiles, ks, &grid) || grid > kI32Max) return CONV_WGRAD_ERR_UNSUPPORTED;
+  pub->grid = grid;
+  pub->slab_stride = ceil_div(p.E, 64) * 64;
+  int64_t ws_elems;
+  if (ks > 1) {
+    if (!mul_ok(pub->slab_stride, ks, &ws_elems) || ws_elems > INT64_MAX / 4)
+      return CONV_WGRAD_ERR_UNSUPPORTED;
+    pub->ws_bytes = (uint64_t)ws_elems * 4u;
+  } else {
+    pub->ws_bytes = 0;
+  }
+  return CONV_WGRAD_OK;
+}
+
+namespace {
+
+int vec_width(int64_t n) { return n % 4 == 0 ? 4 : 1; }
+
+}  // namespace
+
+conv_wgrad_status_t make_plan(const conv_wgrad_desc_t* desc, Plan* out) {
+  if (!desc || !out) return CONV_WGRAD_ERR_NULL_ARG;
+  memset(out, 0, sizeof(*out));
+  Problem& p = out->p;
+  conv_wgrad_status_t st = canonicalise(desc, &p);
+  if (st != CONV_WGRAD_OK) return st;
+  conv_wgrad_plan_t& pub = out->pub;
+  pub.Ho = p.Ho;
+  pub.Wo = p.Wo;
+  pub.L = p.L;
+  pub.E = p.E;
+  pub.x_bytes = p.x_bytes;
+  pub.dy_bytes = p.dy_bytes;
+  pub.dw_bytes = p.dw_bytes;
+  const uint64_t big = p.x_bytes > p.dy_bytes ? p.x_bytes : p.dy_bytes;
+  pub.windows_4g = (int64_t)((big + ((uint64_t)1 << 32) - 1) >> 32);
+
+  const bool small_groups = p.groups > 1 && p.Cg <= 8 && p.Kg <= 8;
+  if (small_groups) {
+    // Direct path: one dW element per lane; a unit is 64 output pixels.
+    pub.path = CONV_WGRAD_PATH_DIRECT;
+    pub.variant = kDirectElem;
+    out->threads = 256;
+    pub.unit_rows = 64;
+    int64_t units = ceil_div(p.L, pub.unit_rows);
+    int64_t tiles = ceil_div(p.E, out->threads);
+    return choose_split(units, tiles, desc->split_k, 16, 2048, p, &pub);
+  }
+  // Dense implicit GEMM per group.
+  pub.path = CONV_WGRAD_PATH_DENSE;
+  pub.variant = kDenseLds;
+  out->bm = 64;
+  out->bn = 64;
+  out->bk = 32;
+  out->m_tiles = ceil_div(p.Kg, out->bm);
+  out->n_tiles = ceil_div(p.cols, out->bn);
+  out->vec_a = vec_width(p.Kg);
+  out->vec_b = vec_width(p.Cg);
+  pub.unit_rows = out->bk;
+  int64_t units = ceil_div(p.L, pub.unit_rows);
+  int64_t tiles;
+  if (!mul3(p.groups, out->m_tiles, out->n_tiles, &tiles)) return CONV_WGRAD_ERR_UNSUPPORTED;
+  return choose_split(units, tiles, desc->split_k, 8, 1024, p, &pub);
+}
+
+}  // namespace cw

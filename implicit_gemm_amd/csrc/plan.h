@@ -1,0 +1,59 @@
+// Host-side problem canonicalisation and execution planning.
+//
+// Pure integer code: no HIP call, no floating point.  Every ceiling division
+// is the exact integer form (a + b - 1) / b on non-negative 64-bit values; the
+// truncating "ceil of an integer quotient" idiom is what let one dispatch
+// address more than ~4 GB in rocm-libraries PR #11188 (section Technical
+// Details).
+#pragma once
+
+#include <stdint.h>
+
+#include "../../include/conv_wgrad.h"
+
+namespace cw {
+
+// Kernel variants (conv_wgrad_plan_t::variant).
+enum Variant : int32_t {
+  kDenseLds = 0,      // dense implicit GEMM, LDS-staged tiles, f32 MFMA 16x16x4
+  kDirectElem = 10,   // direct small-group kernel, one dW element per lane
+};
+
+struct Problem {
+  int64_t N, C, H, W, K, R, S, pad, stride, dil, groups;
+  int32_t dtype;
+  int32_t esize;         // bytes per x / dy element
+  int64_t Ho, Wo, Cg, Kg;
+  int64_t L;             // N * Ho * Wo
+  int64_t cols;          // R * S * Cg (GEMM N extent per group)
+  int64_t E;             // K * R * S * Cg
+  int64_t x_img, dy_img; // elements per image of x and dy
+  uint64_t x_bytes, dy_bytes, dw_bytes;
+};
+
+struct Plan {
+  conv_wgrad_plan_t pub;
+  Problem p;
+  // Dense path tiling.
+  int32_t bm, bn, bk;      // tile of output channels, tile of GEMM columns, rows per unit
+  int64_t m_tiles, n_tiles;
+  int32_t vec_a, vec_b;    // elements per vector load of dy / x (1 or 4)
+  // Direct path.
+  int32_t threads;         // lanes per workgroup
+};
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Validate and canonicalise desc.  Returns CONV_WGRAD_OK or the error code.
+conv_wgrad_status_t canonicalise(const conv_wgrad_desc_t* desc, Problem* out);
+
+// Build the full plan (calls canonicalise).
+conv_wgrad_status_t make_plan(const conv_wgrad_desc_t* desc, Plan* out);
+
+// Split policy shared by all paths.  `units` reduction units, `tiles` output
+// tiles per slice, `requested` the descriptor's split_k (-1 = auto).  Fills
+// units_per_slice, ks_count, needs_reduce, grid, slab_stride and ws_bytes.
+conv_wgrad_status_t choose_split(int64_t units, int64_t tiles, int32_t requested, int64_t min_units,
+                                 int64_t target_groups, const Problem& p, conv_wgrad_plan_t* pub);
+
+}  // namespace cw

@@ -1,0 +1,175 @@
+/*
+ * conv_wgrad.h -- C ABI of the MI355X (gfx950) convolution weight-gradient library.
+ *
+ * Operation (the weight gradient of a 2-D convolution, "weight.grad" of
+ * nn.Conv2d in rocm-libraries PR #11188 "fix silent zero wgrad", section
+ * Motivation; for a 1x1 filter it equals dY^T X on the [N*H*W, .] matrices,
+ * the "F.linear on the reshaped tensor" equivalence of the same section):
+ *
+ *   dW[k, r, s, c] = sum_{n, ho, wo} dY[n, ho, wo, k]
+ *                    * X[n, ho*stride + r*dilation - pad, wo*stride + s*dilation - pad, g(k)*Cg + c]
+ *
+ *   Cg = C / groups, Kg = K / groups, g(k) = k / Kg; X is zero outside the
+ *   H x W image (the same pad on all four sides; stride and dilation are the
+ *   same on both axes); Ho = (H + 2*pad - dilation*(R-1) - 1) / stride + 1,
+ *   Wo likewise.
+ *
+ * Layouts (dense, row-major, no strides):
+ *   x  : [N][H][W][C]    element type desc->dtype
+ *   dy : [N][Ho][Wo][K]  element type desc->dtype
+ *   dw : [K][R][S][Cg]   fp32, always (fp32 accumulation for every dtype)
+ *
+ * Execution: the reduction over N*Ho*Wo is cut into ks_count slices
+ * ("split-K", the two-stage scheme of rocm-libraries PR #14393 "split-K
+ * forward implicit-GEMM convolution on gfx1250", section "Two-stage split-K").
+ * With ks_count > 1 every stage-1 workgroup writes its fp32 partial tile into
+ * slab `slice` of the workspace exactly once, and a second kernel folds the
+ * slabs in ascending slice order; with ks_count == 1 stage 1 writes dw
+ * directly.  Results are therefore bit-identical from run to run for a fixed
+ * split degree, and the workspace needs no clearing.  Tensor base addresses
+ * and image offsets are 64-bit, so tensors larger than 4 GB are handled in
+ * one launch (the failure mode of rocm-libraries PR #11188, sections
+ * Motivation and Technical Details, where a truncating split computation let
+ * one dispatch address more than ~4 GB and silently return zeros).
+ *
+ * Errors are returned, never hidden: validation is synchronous and happens
+ * before anything is enqueued; on any error nothing is enqueued and dw is not
+ * touched.  There is no fallback path.
+ */
+#ifndef CONV_WGRAD_H_
+#define CONV_WGRAD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of x and dy.  dw is always fp32. */
+typedef enum conv_wgrad_dtype {
+  CONV_WGRAD_F32 = 0,
+  CONV_WGRAD_BF16 = 1,
+  CONV_WGRAD_F16 = 2
+} conv_wgrad_dtype_t;
+
+/*
+ * Problem descriptor.  All fields are read; the struct is copied, never kept.
+ *   N, C, H, W : input batch, channels, height, width (each >= 1)
+ *   K, R, S    : output channels, filter height, filter width (each >= 1)
+ *   pad >= 0, stride >= 1, dilation >= 1 (same value for both spatial axes)
+ *   groups >= 1, dividing both C and K
+ *   dtype      : conv_wgrad_dtype_t of x and dy
+ *   split_k    : -1 = choose the number of reduction slices automatically;
+ *                n >= 1 = pin it.  The pinned degree is honoured except that
+ *                no slice may be empty: with U reduction units the plan uses
+ *                ceil(U / ceil(U / n)) slices (never more than n).  Any other
+ *                value (0, < -1) is CONV_WGRAD_ERR_BAD_SPLIT, as in the
+ *                split-K validators of rocm-libraries PR #14393 (section
+ *                "Review follow-ups": split_k <= 0 is rejected).
+ */
+typedef struct conv_wgrad_desc {
+  int64_t N, C, H, W, K, R, S;
+  int64_t pad, stride, dilation, groups;
+  int32_t dtype;
+  int32_t split_k;
+} conv_wgrad_desc_t;
+
+typedef enum conv_wgrad_status {
+  CONV_WGRAD_OK = 0,
+  CONV_WGRAD_ERR_NULL_ARG = 1,     /* desc, x, dy, dw or a needed workspace is NULL */
+  CONV_WGRAD_ERR_BAD_SHAPE = 2,    /* a dimension < 1, pad < 0, stride/dilation < 1,
+                                      C or K not divisible by groups, Ho or Wo < 1,
+                                      or a size that overflows int64 */
+  CONV_WGRAD_ERR_BAD_DTYPE = 3,    /* dtype is not a conv_wgrad_dtype_t */
+  CONV_WGRAD_ERR_BAD_SPLIT = 4,    /* split_k is 0 or < -1 */
+  CONV_WGRAD_ERR_UNSUPPORTED = 5,  /* valid, but outside the library's documented
+                                      limits (see conv_wgrad_get_plan) */
+  CONV_WGRAD_ERR_MISALIGNED = 6,   /* x, dy, dw or workspace not 16-byte aligned */
+  CONV_WGRAD_ERR_WORKSPACE = 7,    /* conv_wgrad_ex: ws_bytes smaller than required */
+  CONV_WGRAD_ERR_HIP = 8           /* the HIP runtime reported an error at launch */
+} conv_wgrad_status_t;
+
+/* Which stage-1 kernel family a plan uses. */
+typedef enum conv_wgrad_path {
+  CONV_WGRAD_PATH_DENSE = 0,   /* implicit GEMM per group on MFMA */
+  CONV_WGRAD_PATH_DIRECT = 1   /* direct per-group kernel for small groups (depthwise, <= 8 ch/group) */
+} conv_wgrad_path_t;
+
+/*
+ * The execution plan the library derives from a descriptor (pure host
+ * integer arithmetic; no GPU needed).  Exposed for tests and diagnostics.
+ */
+typedef struct conv_wgrad_plan {
+  int32_t path;            /* conv_wgrad_path_t */
+  int32_t variant;         /* kernel variant within the path (diagnostic) */
+  int64_t Ho, Wo;          /* output extents */
+  int64_t L;               /* reduction length N*Ho*Wo */
+  int64_t E;               /* dW elements K*R*S*Cg */
+  int64_t unit_rows;       /* reduction rows per unit (a unit is the smallest slice grain) */
+  int64_t units;           /* reduction units: ceil(L / unit_rows) or per-path equivalent */
+  int64_t units_per_slice; /* ceil(units / requested degree) */
+  int32_t ks_count;        /* slices: ceil(units / units_per_slice) >= 1; no slice is empty */
+  int32_t needs_reduce;    /* 1 iff ks_count > 1: the only condition for launching stage 2 */
+  int64_t tiles;           /* output tiles per slice */
+  int64_t grid;            /* stage-1 workgroups = tiles * ks_count */
+  int64_t slab_stride;     /* fp32 elements between workspace slabs (multiple of 64) */
+  uint64_t ws_bytes;       /* workspace bytes: ks_count * slab_stride * 4, or 0 */
+  uint64_t x_bytes, dy_bytes, dw_bytes;  /* tensor sizes in bytes */
+  int64_t windows_4g;      /* ceil(max(x_bytes, dy_bytes) / 2^32): 4-GiB address windows the
+                              tensors span (diagnostic; one launch covers them all) */
+} conv_wgrad_plan_t;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* conv_wgrad_status_string(conv_wgrad_status_t status);
+
+/*
+ * Workspace bytes conv_wgrad needs for desc (0 when the plan has one slice).
+ * Pure host function.  Errors: NULL_ARG (desc or bytes NULL), BAD_*, UNSUPPORTED.
+ */
+conv_wgrad_status_t conv_wgrad_workspace_size(const conv_wgrad_desc_t* desc, size_t* bytes);
+
+/*
+ * Fill *plan with the plan for desc.  Pure host function (no HIP call); the
+ * same validation as conv_wgrad.
+ */
+conv_wgrad_status_t conv_wgrad_get_plan(const conv_wgrad_desc_t* desc, conv_wgrad_plan_t* plan);
+
+/*
+ * Enqueue the weight gradient on `stream` (a hipStream_t; NULL = the null
+ * stream of the current device) and return without synchronising.
+ *   x, dy     : device pointers, layouts above, 16-byte aligned
+ *   dw        : device pointer, fp32 [K][R][S][Cg], 16-byte aligned; overwritten
+ *               (every element written exactly once; no accumulate)
+ *   workspace : device pointer of at least conv_wgrad_workspace_size bytes,
+ *               16-byte aligned; may be NULL when that size is 0.  Its content on
+ *               entry is irrelevant.  The caller owns every buffer; the library
+ *               never allocates or frees device memory.
+ * Buffers must not overlap.  Concurrent calls on different streams need
+ * different workspaces.
+ */
+conv_wgrad_status_t conv_wgrad(const conv_wgrad_desc_t* desc, const void* x, const void* dy,
+                               float* dw, void* workspace, void* stream);
+
+/* As conv_wgrad, also checking that ws_bytes covers the workspace the plan needs
+ * (CONV_WGRAD_ERR_WORKSPACE otherwise). */
+conv_wgrad_status_t conv_wgrad_ex(const conv_wgrad_desc_t* desc, const void* x, const void* dy,
+                                  float* dw, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Profiling variant of conv_wgrad: identical work on `stream`, and the caller's
+ * HIP events (hipEvent_t, created by the caller; either may be NULL) are
+ * recorded on `stream` immediately before and immediately after the stage-1
+ * kernel, so the caller can time that kernel alone (the slab reduce, when
+ * launched, follows the second event).  The events are only recorded, never
+ * synchronised or destroyed.
+ */
+conv_wgrad_status_t conv_wgrad_timed(const conv_wgrad_desc_t* desc, const void* x, const void* dy,
+                                     float* dw, void* workspace, size_t ws_bytes, void* stream,
+                                     void* stage1_begin, void* stage1_end);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONV_WGRAD_H_ */

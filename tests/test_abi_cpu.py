@@ -1,0 +1,193 @@
+"""The C-ABI library without a GPU: exported symbols, validation errors and the
+planner (pure host integer code reached through conv_wgrad_get_plan)."""
+import ctypes
+import json
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import implicit_gemm_amd as iga
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "conv_wgrad.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(conv_wgrad\w*)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = iga.load()
+    names = declared_functions()
+    assert set(names) == {"conv_wgrad", "conv_wgrad_ex", "conv_wgrad_get_plan", "conv_wgrad_timed",
+                          "conv_wgrad_status_string", "conv_wgrad_workspace_size"}
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", iga.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
+    assert set(names) <= exported
+
+
+def test_struct_sizes_match_header_layout():
+    # 11 int64 + 2 int32; plan: see conv_wgrad_plan_t field order.
+    assert ctypes.sizeof(iga.Desc) == 11 * 8 + 2 * 4
+    assert ctypes.sizeof(iga.Plan) == 8 + 8 * 7 + 4 + 4 + 8 * 3 + 8 * 4 + 8
+
+
+def test_status_strings():
+    lib = iga.load()
+    for code in range(9):
+        s = lib.conv_wgrad_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.conv_wgrad_status_string(99).decode() == "unknown status"
+
+
+def D(**kw):
+    base = dict(N=2, C=8, H=8, W=8, K=4, R=3, S=3, pad=1, stride=1, dilation=1, groups=1,
+                dtype=iga.F32, split_k=-1)
+    base.update(kw)
+    return iga.make_desc(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=0), 2), (dict(C=0), 2), (dict(H=0), 2), (dict(W=-1), 2), (dict(K=0), 2),
+    (dict(R=0), 2), (dict(S=0), 2), (dict(pad=-1), 2), (dict(stride=0), 2),
+    (dict(dilation=0), 2), (dict(groups=0), 2), (dict(groups=3), 2), (dict(C=6, K=4, groups=3), 2),
+    (dict(H=2, R=5, pad=0), 2), (dict(W=2, S=3, dilation=2, pad=0), 2),
+    (dict(dtype=3), 3), (dict(dtype=-1), 3),
+    (dict(split_k=0), 4), (dict(split_k=-2), 4), (dict(split_k=-100), 4),
+    (dict(N=1 << 40, C=1 << 20, H=1 << 20, W=1 << 20), 2),
+    (dict(H=1 << 16, W=1 << 16, C=1024), 5),
+])
+def test_invalid_desc_is_rejected_before_any_launch(kw, code):
+    d = D(**kw)
+    with pytest.raises(iga.ConvWgradError) as ei:
+        iga.get_plan(d)
+    assert ei.value.status == code
+    with pytest.raises(iga.ConvWgradError) as ei:
+        iga.workspace_size(d)
+    assert ei.value.status == code
+    lib = iga.load()
+    # conv_wgrad itself validates before touching pointers or the GPU.
+    assert lib.conv_wgrad(ctypes.byref(d), 16, 16, 16, 16, None) == code
+
+
+def test_null_arguments():
+    lib = iga.load()
+    d = D()
+    assert lib.conv_wgrad(None, 16, 16, 16, 16, None) == 1
+    assert lib.conv_wgrad(ctypes.byref(d), None, 16, 16, 16, None) == 1
+    assert lib.conv_wgrad(ctypes.byref(d), 16, None, 16, 16, None) == 1
+    assert lib.conv_wgrad(ctypes.byref(d), 16, 16, None, 16, None) == 1
+    assert lib.conv_wgrad_get_plan(ctypes.byref(d), None) == 1
+    assert lib.conv_wgrad_workspace_size(ctypes.byref(d), None) == 1
+    # A plan with several slices needs a workspace.
+    d = D(N=8, H=32, W=32, split_k=4)
+    assert iga.get_plan(d).ks_count > 1
+    assert lib.conv_wgrad(ctypes.byref(d), 16, 16, 16, None, None) == 1
+
+
+def test_misaligned_and_small_workspace():
+    lib = iga.load()
+    d = D(N=8, H=32, W=32, split_k=4)
+    ws = iga.workspace_size(d)
+    assert ws > 0
+    assert lib.conv_wgrad(ctypes.byref(d), 18, 16, 16, 16, None) == 6
+    assert lib.conv_wgrad(ctypes.byref(d), 16, 20, 16, 16, None) == 6
+    assert lib.conv_wgrad(ctypes.byref(d), 16, 16, 24, 16, None) == 6
+    assert lib.conv_wgrad(ctypes.byref(d), 16, 16, 16, 8, None) == 6
+    assert lib.conv_wgrad_ex(ctypes.byref(d), 16, 16, 16, 16, ws - 1, None) == 7
+
+
+def check_plan_invariants(d, p):
+    """Every plan: exact ceil-division slices covering all units, no empty slice."""
+    Ho = (d.H + 2 * d.pad - d.dilation * (d.R - 1) - 1) // d.stride + 1
+    Wo = (d.W + 2 * d.pad - d.dilation * (d.S - 1) - 1) // d.stride + 1
+    assert (p.Ho, p.Wo) == (Ho, Wo)
+    assert p.L == d.N * Ho * Wo
+    assert p.E == d.K * d.R * d.S * (d.C // d.groups)
+    assert p.units == -(-p.L // p.unit_rows) or p.path == iga.PATH_DIRECT
+    ups, ks = p.units_per_slice, p.ks_count
+    assert ks >= 1 and ups >= 1
+    assert (ks - 1) * ups < p.units <= ks * ups       # last slice non-empty, all covered
+    assert ks == -(-p.units // ups)
+    if d.split_k >= 1:
+        assert ks <= d.split_k
+        assert ups == -(-p.units // min(d.split_k, p.units))
+    assert p.needs_reduce == (1 if ks > 1 else 0)
+    assert p.grid == p.tiles * ks
+    assert p.slab_stride % 64 == 0 and p.slab_stride >= p.E
+    assert p.ws_bytes == (ks * p.slab_stride * 4 if ks > 1 else 0)
+    esz = 4 if d.dtype == iga.F32 else 2
+    assert p.x_bytes == d.N * d.H * d.W * d.C * esz
+    assert p.dy_bytes == d.N * Ho * Wo * d.K * esz
+    assert p.windows_4g == -(-max(p.x_bytes, p.dy_bytes) // (1 << 32))
+
+
+def test_planner_random_descs():
+    rng = np.random.default_rng(7)
+    for _ in range(3000):
+        groups = int(rng.choice([1, 1, 2, 4, 8, 32]))
+        C = groups * int(rng.integers(1, 12))
+        K = groups * int(rng.integers(1, 12))
+        H, W = int(rng.integers(1, 80)), int(rng.integers(1, 80))
+        R, S = int(rng.integers(1, 8)), int(rng.integers(1, 8))
+        pad, stride, dil = int(rng.integers(0, 4)), int(rng.integers(1, 4)), int(rng.integers(1, 3))
+        if (H + 2 * pad - dil * (R - 1) - 1) < 0 or (W + 2 * pad - dil * (S - 1) - 1) < 0:
+            continue
+        split = int(rng.choice([-1, 1, 2, 3, 7, 64, 1000]))
+        d = iga.make_desc(int(rng.integers(1, 40)), C, H, W, K, R, S, pad, stride, dil, groups,
+                          int(rng.integers(0, 3)), split)
+        check_plan_invariants(d, iga.get_plan(d))
+
+
+def test_planner_large_tensor_geometry_sweep():
+    """The 1x1 96->64 conv on 512x512 images of the MIOpen ticket, N = 1..256, without allocation."""
+    g = json.load(open(os.path.join(GOLDEN, "p1_ticket.json")))
+    c = g["conv"]
+    img_x = c["H"] * c["W"] * c["C"] * 4
+    img_dy = c["H"] * c["W"] * c["K"] * 4
+    for N in range(1, 257):
+        d = iga.make_desc(N, c["C"], c["H"], c["W"], c["K"], 1, 1, split_k=-1)
+        p = iga.get_plan(d)
+        check_plan_invariants(d, p)
+        assert p.x_bytes == N * img_x and p.dy_bytes == N * img_dy
+        for split in (1, 5, 43, 1000):
+            d2 = iga.make_desc(N, c["C"], c["H"], c["W"], c["K"], 1, 1, split_k=split)
+            check_plan_invariants(d2, iga.get_plan(d2))
+    lo, hi = g["sweep_range"]
+    # Every sweep point past the first 4 GiB window; the ticket's dY is exactly 2^32 bytes.
+    for N in g["sweep_points"]:
+        assert lo <= N <= hi
+        p = iga.get_plan(iga.make_desc(N, c["C"], c["H"], c["W"], c["K"], 1, 1))
+        assert p.x_bytes > 1 << 32
+        assert p.windows_4g == -(-(N * img_x) // (1 << 32))
+        # A truncating quotient would claim one window fewer than the tensor spans.
+        assert p.windows_4g == (N * img_x + (1 << 32) - 1) // (1 << 32)
+        assert p.windows_4g > (N * img_x) // (1 << 32) or (N * img_x) % (1 << 32) == 0
+    p = iga.get_plan(iga.make_desc(g["ticket_batch"], c["C"], c["H"], c["W"], c["K"], 1, 1))
+    assert p.dy_bytes == 1 << 32
+    assert p.windows_4g == 2
+    assert p.x_bytes == g["ticket_batch"] * 96 * 512 * 512 * 4
+
+
+def test_split_pinning_and_auto():
+    d = D(N=32, C=64, H=56, W=56, K=64, split_k=1)
+    p = iga.get_plan(d)
+    assert p.ks_count == 1 and p.needs_reduce == 0 and p.ws_bytes == 0
+    assert iga.workspace_size(d) == 0
+    for ks in (2, 3, 7, 64):
+        p = iga.get_plan(D(N=32, C=64, H=56, W=56, K=64, split_k=ks))
+        assert p.ks_count == ks
+    # More slices than units: every slice keeps at least one unit.
+    p = iga.get_plan(D(N=1, H=2, W=2, R=1, S=1, pad=0, split_k=1000))
+    assert p.ks_count == p.units
+    pa = iga.get_plan(D(N=32, C=64, H=56, W=56, K=64, split_k=-1))
+    assert pa.ks_count >= 1 and pa.grid >= 256

@@ -1,0 +1,172 @@
+"""GPU path vs the oracle, element by element, through the C ABI."""
+import numpy as np
+import pytest
+
+import oracle
+import wgrad_data as wd
+from gpu_util import check_against_oracle, log, run_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+SMALL_CONFIGS = ["c1_1x1_tiny_f32", "c2_3x3_f32", "c3_dw7x7_bf16", "c4a_grp3x3_cpg4_f16",
+                 "c4b_grp3x3_cpg8_f16"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import implicit_gemm_amd as iga
+    iga.load()
+
+
+@pytest.mark.parametrize("name", SMALL_CONFIGS)
+def test_workload_parity(name):
+    wl = wd.WORKLOADS[name]
+    log("parity", name, wl.shape, wl.dtype)
+    x, dy = wd.make_inputs(wl)
+    err = check_against_oracle(x, dy, wl.shape, wl.dtype)
+    log("  err %.3e" % err)
+
+
+def test_hand_examples_on_gpu():
+    import json, os
+    cases = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_examples.json")))["cases"]
+    for c in cases:
+        shape = wd.ConvShape(c["N"], c["C"], c["H"], c["W"], c["K"], c["R"], c["S"], c["pad"],
+                             c["stride"], c["dilation"], c["groups"])
+        log("hand", c["name"])
+        x = np.array(c["x"], np.float32)
+        dy = np.array(c["dy"], np.float32)
+        got = run_gpu(x, dy, shape, "f32")
+        assert np.array_equal(got, np.array(c["dw"], np.float64)), c["name"]
+
+
+def _random_shapes(seed, count):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        kind = rng.integers(0, 4)
+        if kind == 0:      # dense, mixed channel counts (vector and scalar loads)
+            groups = 1
+            C, K = int(rng.integers(1, 100)), int(rng.integers(1, 150))
+        elif kind == 1:    # grouped with large groups (dense per group)
+            groups = int(rng.choice([2, 3, 4]))
+            C, K = groups * int(rng.integers(9, 40)), groups * int(rng.integers(9, 40))
+        elif kind == 2:    # depthwise
+            C = int(rng.integers(1, 80))
+            groups, K = C, C
+        else:              # small groups (<= 8 channels per group)
+            groups = int(rng.integers(2, 12))
+            C, K = groups * int(rng.integers(1, 9)), groups * int(rng.integers(1, 9))
+        H, W = int(rng.integers(1, 30)), int(rng.integers(1, 30))
+        R, S = int(rng.integers(1, 6)), int(rng.integers(1, 6))
+        pad, stride, dil = int(rng.integers(0, 4)), int(rng.integers(1, 4)), int(rng.integers(1, 3))
+        N = int(rng.integers(1, 5))
+        shp = wd.ConvShape(N, C, H, W, K, R, S, pad, stride, dil, groups)
+        if shp.Ho < 1 or shp.Wo < 1:
+            continue
+        out.append((shp, ["f32", "bf16", "f16"][int(rng.integers(0, 3))]))
+    return out
+
+
+@pytest.mark.parametrize("idx", range(40))
+def test_random_shapes(idx):
+    shp, dtype = _random_shapes(1234, 40)[idx]
+    log("random", idx, shp, dtype)
+    x, dy = wd.random_inputs(shp, dtype, seed=1000 + idx)
+    check_against_oracle(x, dy, shp, dtype)
+
+
+EDGE = [
+    (wd.ConvShape(1, 1, 1, 1, 1, 1, 1), "f32"),                       # single element
+    (wd.ConvShape(1, 3, 1, 1, 5, 3, 3, pad=1), "f32"),                 # 1x1 image, 3x3 filter
+    (wd.ConvShape(2, 4, 5, 5, 4, 7, 7, pad=3), "bf16"),                # filter larger than image
+    (wd.ConvShape(1, 64, 9, 9, 64, 9, 9, pad=0), "f32"),               # Ho = Wo = 1
+    (wd.ConvShape(3, 130, 7, 5, 70, 1, 1), "f32"),                     # ragged tiles in both M and N
+    (wd.ConvShape(2, 96, 17, 13, 200, 2, 3, pad=1, stride=2), "f16"),  # R != S, stride 2
+    (wd.ConvShape(1, 8, 40, 3, 8, 3, 3, pad=2, dilation=2, groups=8), "bf16"),
+    (wd.ConvShape(5, 12, 11, 11, 24, 3, 3, pad=1, stride=3, groups=3), "f32"),  # Cg=4, Kg=8 direct
+    (wd.ConvShape(2, 16, 9, 9, 16, 5, 5, pad=0, stride=1, groups=2), "bf16"),   # Cg=8 dense? (Kg=8) direct
+    (wd.ConvShape(1, 2, 300, 3, 2, 1, 1, groups=2), "f16"),            # long reduction, tiny output
+]
+
+
+@pytest.mark.parametrize("idx", range(len(EDGE)))
+def test_edge_cases(idx):
+    shp, dtype = EDGE[idx]
+    log("edge", idx, shp, dtype)
+    x, dy = wd.random_inputs(shp, dtype, seed=77 + idx)
+    check_against_oracle(x, dy, shp, dtype)
+
+
+@pytest.mark.parametrize("name", ["c2_3x3_f32", "c4b_grp3x3_cpg8_f16", "c1_1x1_tiny_f32"])
+@pytest.mark.parametrize("split_k", [1, 2, 3, 7, 64, -1])
+def test_split_invariance(name, split_k):
+    wl = wd.WORKLOADS[name]
+    if name == "c2_3x3_f32":  # a smaller batch keeps the oracle quick
+        wl = wd.Workload(wl.name, wl.shape.with_n(4), wl.dtype, wl.x_dist, wl.dy_dist, wl.seed)
+    log("split", name, split_k)
+    x, dy = wd.make_inputs(wl)
+    check_against_oracle(x, dy, wl.shape, wl.dtype, split_k=split_k)
+
+
+@pytest.mark.parametrize("name,split_k", [("c2_3x3_f32", 5), ("c3_dw7x7_bf16", -1),
+                                          ("c4a_grp3x3_cpg4_f16", 3), ("c1_1x1_tiny_f32", 1)])
+def test_bitwise_determinism_and_full_overwrite(name, split_k):
+    """Three runs at a fixed split degree agree bit for bit; dw and the workspace start as NaN."""
+    import torch
+    import implicit_gemm_amd as iga
+    wl = wd.WORKLOADS[name]
+    s = wl.shape
+    log("determinism", name, split_k)
+    x, dy = wd.make_inputs(wl)
+    xd, dyd = to_device(x, wl.dtype), to_device(dy, wl.dtype)
+    d = iga.desc_for(xd, dyd, s.R, s.S, s.pad, s.stride, s.dilation, s.groups, split_k)
+    plan = iga.get_plan(d)
+    ws_bytes = plan.ws_bytes
+    results = []
+    for _ in range(3):
+        dw = torch.full((s.K, s.R, s.S, s.Cg), float("nan"), dtype=torch.float32, device="cuda")
+        ws = torch.full((max(ws_bytes, 16) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+        iga.conv_wgrad(d, xd.data_ptr(), dyd.data_ptr(), dw.data_ptr(), ws.data_ptr() if ws_bytes else 0,
+                       torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        results.append(dw.cpu().numpy())
+    assert np.all(np.isfinite(results[0]))
+    for r in results[1:]:
+        assert np.array_equal(r.view(np.uint32), results[0].view(np.uint32))
+    check_against_oracle(x, dy, s, wl.dtype, dw_gpu=results[0].astype(np.float64))
+
+
+def test_device_pointer_errors():
+    import torch
+    import implicit_gemm_amd as iga
+    x = torch.zeros(64 * 64, dtype=torch.float32, device="cuda")
+    d = iga.make_desc(1, 4, 4, 4, 4, 1, 1)
+    with pytest.raises(iga.ConvWgradError) as ei:
+        iga.conv_wgrad(d, x.data_ptr() + 4, x.data_ptr(), x.data_ptr(), 0, 0)
+    assert ei.value.name == "ERR_MISALIGNED"
+    with pytest.raises(iga.ConvWgradError) as ei:
+        iga.conv_wgrad(iga.make_desc(1, 4, 4, 4, 4, 1, 1, split_k=0), x.data_ptr(), x.data_ptr(),
+                       x.data_ptr(), 0, 0)
+    assert ei.value.name == "ERR_BAD_SPLIT"
+
+
+def test_nonzero_result_stream_and_default_stream():
+    """Runs on a non-default stream give the same bits as on the current stream."""
+    import torch
+    import implicit_gemm_amd as iga
+    wl = wd.WORKLOADS["c4b_grp3x3_cpg8_f16"]
+    s = wl.shape
+    x, dy = wd.make_inputs(wl)
+    xd, dyd = to_device(x, wl.dtype), to_device(dy, wl.dtype)
+    a = iga.wgrad(xd, dyd, s.R, s.S, s.pad, s.stride, s.dilation, s.groups)
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        b = iga.wgrad(xd, dyd, s.R, s.S, s.pad, s.stride, s.dilation, s.groups)
+    st.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert int((a == 0).sum()) == 0
