@@ -72,13 +72,17 @@ conv_wgrad_status_t run(const conv_wgrad_desc_t* desc, const void* x, const void
   hipError_t err;
   if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess)
     return CONV_WGRAD_ERR_HIP;
-  err = plan.pub.path == CONV_WGRAD_PATH_DIRECT ? cw::launch_direct(plan, x, dy, out, s)
-                                                : cw::launch_dense(plan, x, dy, out, s);
+  switch (plan.pub.variant) {
+    case cw::kDirectElem: err = cw::launch_direct(plan, x, dy, out, s); break;
+    case cw::kDenseRows: err = cw::launch_dense_rows(plan, x, dy, out, s); break;
+    case cw::kDense1x1: err = cw::launch_dense_1x1(plan, x, dy, out, s); break;
+    default: err = cw::launch_dense(plan, x, dy, out, s); break;
+  }
   if (err != hipSuccess) return CONV_WGRAD_ERR_HIP;
   if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), s) != hipSuccess)
     return CONV_WGRAD_ERR_HIP;
   if (plan.pub.needs_reduce) {
-    err = cw::launch_slab_reduce(plan, static_cast<const float*>(workspace), dw, s);
+    err = cw::launch_slab_reduce(plan, static_cast<float*>(workspace), dw, s);
     if (err != hipSuccess) return CONV_WGRAD_ERR_HIP;
   }
   return CONV_WGRAD_OK;

@@ -1,0 +1,174 @@
+// 1x1, stride-1, unpadded dense weight gradient: dW_g = dY_g^T X_g streamed
+// from HBM straight into MFMA operand registers (gfx950, fp32).
+//
+// For a 1x1 filter the weight gradient is the product of the reshaped
+// [N*H*W, K] and [N*H*W, C] matrices (the "F.linear on the reshaped tensor"
+// equivalence of rocm-libraries PR #11188, section Motivation), a GEMM with a
+// tiny output and a reduction of N*H*W rows: HBM-bound with an arithmetic
+// intensity at the f32-MFMA ridge, so no LDS staging is used at all.
+//
+// One wave owns one slice of rows.  Lane (i, g) = (lane % 16, lane / 16)
+// loads, for row 4*b + g of batch b, the AV consecutive output channels
+// m0 + AV*i .. of dY and the BV consecutive input channels c0 + BV*i .. of X:
+// 16 lanes read one whole row (256 B of dY, 384 B of X for K=64, C=96) and
+// the 4 lane groups read 4 consecutive rows.  Register j of the dY load is the
+// A operand of v_mfma_f32_16x16x4_f32 for output channels {m0 + AV*i + j},
+// register j' of the X load the B operand for input channels
+// {c0 + BV*i + j'}, so AV*BV MFMAs per 4 rows cover the whole M x N tile with
+// no data movement between load and MFMA.  Loads run PF batches ahead.
+// Row offsets are 64-bit (tensors may span many 4 GiB windows).
+#include "device_common.h"
+#include "kernels.h"
+
+namespace cw {
+
+namespace {
+
+constexpr int kPf = 4;  // row batches in flight per wave
+
+struct OneByOneArgs {
+  const float* x;
+  const float* dy;
+  float* out;
+  int64_t slab_stride;
+  int32_t C, K, Cg, Kg, groups;
+  int32_t m_tiles, c_tiles;
+  int64_t L;            // rows
+  int64_t rows_per_slice;
+  int32_t ks_count;
+};
+
+template <int AV, int BV>
+__device__ __forceinline__ void load_batch(const float* dyp, const float* xp, bool ok,
+                                           float (&a)[AV], float (&b)[BV]) {
+  if (ok) {
+    if (AV == 4) {
+      const float4 v = *reinterpret_cast<const float4*>(dyp);
+      a[0] = v.x; a[1] = v.y; a[2] = v.z; a[3] = v.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < AV; ++j) a[j] = dyp[j];
+    }
+    if (BV % 4 == 0) {
+#pragma unroll
+      for (int j = 0; j < BV; j += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(xp + j);
+        b[j] = v.x; b[j + 1] = v.y; b[j + 2] = v.z; b[j + 3] = v.w;
+      }
+    } else if (BV % 2 == 0) {
+#pragma unroll
+      for (int j = 0; j < BV; j += 2) {
+        const float2 v = *reinterpret_cast<const float2*>(xp + j);
+        b[j] = v.x; b[j + 1] = v.y;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < BV; ++j) b[j] = xp[j];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < AV; ++j) a[j] = 0.f;
+#pragma unroll
+    for (int j = 0; j < BV; ++j) b[j] = 0.f;
+  }
+}
+
+template <int AV, int BV>
+__global__ __launch_bounds__(64) void dense_1x1_kernel(OneByOneArgs a) {
+  const int lane = threadIdx.x;
+  const int li = lane & 15, lg = lane >> 4;
+  const int bid = blockIdx.x;
+  const int slice = bid % a.ks_count;
+  int tile = bid / a.ks_count;
+  const int ct = tile % a.c_tiles;
+  tile /= a.c_tiles;
+  const int mt = tile % a.m_tiles;
+  const int g = tile / a.m_tiles;
+  const int m0 = mt * 16 * AV, c0 = ct * 16 * BV;
+
+  const int64_t r_begin = (int64_t)slice * a.rows_per_slice;
+  const int64_t r_end = min(a.L, r_begin + a.rows_per_slice);
+  const int64_t nb = (r_end - r_begin + 3) >> 2;  // 4-row batches
+
+  const float* dyp = a.dy + (r_begin + lg) * a.K + (int64_t)g * a.Kg + m0 + AV * li;
+  const float* xp = a.x + (r_begin + lg) * a.C + (int64_t)g * a.Cg + c0 + BV * li;
+  const int64_t dy_step = 4 * (int64_t)a.K, x_step = 4 * (int64_t)a.C;
+  int64_t row = r_begin + lg;
+
+  f32x4 acc[AV][BV];
+#pragma unroll
+  for (int i = 0; i < AV; ++i)
+#pragma unroll
+    for (int j = 0; j < BV; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  float ra[kPf][AV], rb[kPf][BV];
+#pragma unroll
+  for (int p = 0; p < kPf; ++p) {
+    load_batch<AV, BV>(dyp, xp, row < r_end, ra[p], rb[p]);
+    dyp += dy_step; xp += x_step; row += 4;
+  }
+  for (int64_t b = 0; b < nb; b += kPf) {
+#pragma unroll
+    for (int p = 0; p < kPf; ++p) {
+      if (b + p < nb) {
+#pragma unroll
+        for (int i = 0; i < AV; ++i)
+#pragma unroll
+          for (int j = 0; j < BV; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ra[p][i], rb[p][j], acc[i][j], 0, 0, 0);
+        load_batch<AV, BV>(dyp, xp, row < r_end, ra[p], rb[p]);
+        dyp += dy_step; xp += x_step; row += 4;
+      }
+    }
+  }
+
+  // acc[i][j][v] is dW[m0 + AV*(4*lg + v) + i][c0 + BV*li + j].
+  float* out = a.out + (int64_t)slice * a.slab_stride;
+  const int64_t cols = a.Cg;
+#pragma unroll
+  for (int i = 0; i < AV; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = m0 + AV * (4 * lg + v) + i;
+      float* o = out + ((int64_t)g * a.Kg + m) * cols + c0 + BV * li;
+#pragma unroll
+      for (int j = 0; j < BV; ++j) o[j] = acc[i][j][v];
+    }
+}
+
+template <int AV, int BV>
+hipError_t launch_ab(const OneByOneArgs& args, int64_t grid, hipStream_t stream) {
+  return launch_kernel(dense_1x1_kernel<AV, BV>, dim3((unsigned)grid), dim3(64), args, stream);
+}
+
+}  // namespace
+
+hipError_t launch_dense_1x1(const Plan& plan, const void* x, const void* dy, Stage1Out out,
+                            hipStream_t stream) {
+  const Problem& p = plan.p;
+  OneByOneArgs a;
+  a.x = static_cast<const float*>(x);
+  a.dy = static_cast<const float*>(dy);
+  a.out = out.base;
+  a.slab_stride = out.slab_stride;
+  a.C = (int32_t)p.C; a.K = (int32_t)p.K; a.Cg = (int32_t)p.Cg; a.Kg = (int32_t)p.Kg;
+  a.groups = (int32_t)p.groups;
+  a.m_tiles = (int32_t)plan.m_tiles;
+  a.c_tiles = (int32_t)plan.c_tiles;
+  a.L = p.L;
+  a.rows_per_slice = plan.pub.units_per_slice * plan.pub.unit_rows;
+  a.ks_count = plan.pub.ks_count;
+  const int64_t grid = plan.pub.grid;
+  switch (plan.bv) {
+    case 1: return launch_ab<4, 1>(a, grid, stream);
+    case 2: return launch_ab<4, 2>(a, grid, stream);
+    case 3: return launch_ab<4, 3>(a, grid, stream);
+    case 4: return launch_ab<4, 4>(a, grid, stream);
+    case 5: return launch_ab<4, 5>(a, grid, stream);
+    case 6: return launch_ab<4, 6>(a, grid, stream);
+    case 7: return launch_ab<4, 7>(a, grid, stream);
+    default: return launch_ab<4, 8>(a, grid, stream);
+  }
+}
+
+}  // namespace cw

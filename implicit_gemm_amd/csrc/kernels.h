@@ -24,8 +24,12 @@ inline hipError_t launch_kernel(void (*kernel)(Args), dim3 grid, dim3 block, con
 
 hipError_t launch_dense(const Plan& plan, const void* x, const void* dy, Stage1Out out,
                         hipStream_t stream);
+hipError_t launch_dense_rows(const Plan& plan, const void* x, const void* dy, Stage1Out out,
+                             hipStream_t stream);
+hipError_t launch_dense_1x1(const Plan& plan, const void* x, const void* dy, Stage1Out out,
+                            hipStream_t stream);
 hipError_t launch_direct(const Plan& plan, const void* x, const void* dy, Stage1Out out,
                          hipStream_t stream);
-hipError_t launch_slab_reduce(const Plan& plan, const float* ws, float* dw, hipStream_t stream);
+hipError_t launch_slab_reduce(const Plan& plan, float* ws, float* dw, hipStream_t stream);
 
 }  // namespace cw

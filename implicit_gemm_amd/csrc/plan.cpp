@@ -33,6 +33,8 @@ int64_t extent(int64_t in, int64_t k, int64_t pad, int64_t stride, int64_t dil) 
 constexpr int64_t kI32Max = 2147483647;
 // Reduction rows stay below 2^31 with room for one rounded-up slice.
 constexpr int64_t kMaxRows = kI32Max - 65536;
+// Upper bound on the split degree (the slab fold launches one workgroup row per run).
+constexpr int64_t kMaxSlices = 65536;
 
 }  // namespace
 
@@ -75,26 +77,25 @@ conv_wgrad_status_t canonicalise(const conv_wgrad_desc_t* d, Problem* o) {
 }
 
 conv_wgrad_status_t choose_split(int64_t units, int64_t tiles, int32_t requested, int64_t min_units,
-                                 int64_t target_groups, const Problem& p, conv_wgrad_plan_t* pub) {
+                                 int64_t target_groups, int64_t traffic_div, const Problem& p,
+                                 conv_wgrad_plan_t* pub) {
   int64_t degree;
   if (requested >= 1) {
     degree = requested;
   } else {
-    // Auto: enough workgroups to fill the device, each slice at least
-    // min_units deep, and slab traffic (written once, read once) at most a
-    // quarter of the algorithmic bytes.
-    degree = ceil_div(target_groups, tiles);
+    degree = target_groups / tiles;
     int64_t by_depth = units / (min_units > 0 ? min_units : 1);
     if (by_depth < 1) by_depth = 1;
     if (degree > by_depth) degree = by_depth;
     uint64_t alg = p.x_bytes + p.dy_bytes + p.dw_bytes;
     uint64_t slab = (uint64_t)p.E * 8u;  // 4 bytes written + 4 bytes read per slab element
-    int64_t by_traffic = (int64_t)(alg / (4u * slab));
+    int64_t by_traffic = (int64_t)(alg / ((uint64_t)traffic_div * slab));
     if (by_traffic < 1) by_traffic = 1;
     if (degree > by_traffic) degree = by_traffic;
     if (degree < 1) degree = 1;
   }
   if (degree > units) degree = units;
+  if (degree > kMaxSlices) degree = kMaxSlices;
   pub->units = units;
   pub->units_per_slice = ceil_div(units, degree);
   int64_t ks = ceil_div(units, pub->units_per_slice);
@@ -120,6 +121,53 @@ conv_wgrad_status_t choose_split(int64_t units, int64_t tiles, int32_t requested
 namespace {
 
 int vec_width(int64_t n) { return n % 4 == 0 ? 4 : 1; }
+
+// Limits of the row-unit kernel's LDS tiles (see dense_rows.hip).
+constexpr int kRowsMaxWt = 64, kRowsMaxXSpan = 80;
+
+// Row-unit dense kernel: channel counts in whole quads, and a staged X
+// segment of at most 80 pixels for at least 16 output pixels per unit.
+bool plan_dense_rows(const Problem& p, Plan* out) {
+  if (p.Kg % 4 != 0 || p.Cg % 4 != 0) return false;
+  const int64_t sb = p.S < 4 ? p.S : 4;
+  int64_t wt = 0;
+  for (int64_t cand = kRowsMaxWt; cand >= 16; cand -= 16) {
+    if ((cand - 1) * p.stride + (sb - 1) * p.dil + 1 <= kRowsMaxXSpan) {
+      wt = cand;
+      break;
+    }
+  }
+  if (wt == 0) return false;
+  const int64_t wo16 = ceil_div(p.Wo, 16) * 16;
+  if (wt > wo16) wt = wo16;
+  out->sb = (int32_t)sb;
+  out->wt = (int32_t)wt;
+  out->xspan = (int32_t)((wt - 1) * p.stride + (sb - 1) * p.dil + 1);
+  out->s_blocks = ceil_div(p.S, sb);
+  out->c_tiles = ceil_div(p.Cg, 64);
+  out->m_tiles = ceil_div(p.Kg, 64);
+  out->wchunks = ceil_div(p.Wo, wt);
+  return true;
+}
+
+// 1x1 streaming kernel: fp32, unpadded stride-1 1x1 filter, output channels in
+// whole 64-channel tiles and input channels in 16-channel lane groups.
+bool plan_dense_1x1(const Problem& p, Plan* out) {
+  if (p.dtype != CONV_WGRAD_F32 || p.R != 1 || p.S != 1 || p.pad != 0 || p.stride != 1) return false;
+  if (p.Kg % 64 != 0 || p.Cg % 16 != 0) return false;
+  const int64_t q = p.Cg / 16;
+  int32_t bv = 1;
+  for (int32_t cand = 8; cand >= 1; --cand) {
+    if (q % cand == 0) {
+      bv = cand;
+      break;
+    }
+  }
+  out->bv = bv;
+  out->m_tiles = p.Kg / 64;
+  out->c_tiles = q / bv;
+  return true;
+}
 
 }  // namespace
 
@@ -149,10 +197,30 @@ conv_wgrad_status_t make_plan(const conv_wgrad_desc_t* desc, Plan* out) {
     pub.unit_rows = 64;
     int64_t units = ceil_div(p.L, pub.unit_rows);
     int64_t tiles = ceil_div(p.E, out->threads);
-    return choose_split(units, tiles, desc->split_k, 16, 2048, p, &pub);
+    return choose_split(units, tiles, desc->split_k, 16, 2048, 4, p, &pub);
   }
   // Dense implicit GEMM per group.
   pub.path = CONV_WGRAD_PATH_DENSE;
+  if (plan_dense_1x1(p, out)) {
+    pub.variant = kDense1x1;
+    pub.unit_rows = 64;
+    int64_t tiles;
+    if (!mul3(p.groups, out->m_tiles, out->c_tiles, &tiles)) return CONV_WGRAD_ERR_UNSUPPORTED;
+    // One-wave workgroups, about eight per CU.
+    return choose_split(ceil_div(p.L, 64), tiles, desc->split_k, 4, 2048, 4, p, &pub);
+  }
+  if (plan_dense_rows(p, out)) {
+    pub.variant = kDenseRows;
+    pub.unit_rows = out->wt;
+    int64_t units, tiles;
+    if (!mul3(p.N, p.Ho, out->wchunks, &units)) return CONV_WGRAD_ERR_UNSUPPORTED;
+    if (!mul4(p.groups, out->m_tiles, p.R, out->s_blocks, &tiles) ||
+        !mul_ok(tiles, out->c_tiles, &tiles))
+      return CONV_WGRAD_ERR_UNSUPPORTED;
+    // One 256-lane workgroup per CU (256 CUs); slabs may cost up to the
+    // algorithmic bytes, since this kernel is MFMA-bound on the shapes it takes.
+    return choose_split(units, tiles, desc->split_k, 2, 256, 1, p, &pub);
+  }
   pub.variant = kDenseLds;
   out->bm = 64;
   out->bn = 64;
@@ -165,7 +233,7 @@ conv_wgrad_status_t make_plan(const conv_wgrad_desc_t* desc, Plan* out) {
   int64_t units = ceil_div(p.L, pub.unit_rows);
   int64_t tiles;
   if (!mul3(p.groups, out->m_tiles, out->n_tiles, &tiles)) return CONV_WGRAD_ERR_UNSUPPORTED;
-  return choose_split(units, tiles, desc->split_k, 8, 1024, p, &pub);
+  return choose_split(units, tiles, desc->split_k, 8, 1024, 4, p, &pub);
 }
 
 }  // namespace cw

@@ -15,7 +15,9 @@ namespace cw {
 
 // Kernel variants (conv_wgrad_plan_t::variant).
 enum Variant : int32_t {
-  kDenseLds = 0,      // dense implicit GEMM, LDS-staged tiles, f32 MFMA 16x16x4
+  kDenseLds = 0,      // dense implicit GEMM, LDS-staged tiles, f32 MFMA 16x16x4 (any geometry)
+  kDenseRows = 1,     // dense implicit GEMM over output-row units, per-filter-row tiles
+  kDense1x1 = 2,      // 1x1 stride-1 unpadded fp32: rows streamed into MFMA registers
   kDirectElem = 10,   // direct small-group kernel, one dW element per lane
 };
 
@@ -38,6 +40,10 @@ struct Plan {
   int32_t bm, bn, bk;      // tile of output channels, tile of GEMM columns, rows per unit
   int64_t m_tiles, n_tiles;
   int32_t vec_a, vec_b;    // elements per vector load of dy / x (1 or 4)
+  // Row-unit dense kernel.
+  int32_t sb, wt, xspan;   // taps per tile, output pixels per unit, staged X pixels per unit
+  int64_t c_tiles, s_blocks, wchunks;
+  int32_t bv;              // 1x1 kernel: input channels per lane
   // Direct path.
   int32_t threads;         // lanes per workgroup
 };
@@ -53,7 +59,13 @@ conv_wgrad_status_t make_plan(const conv_wgrad_desc_t* desc, Plan* out);
 // Split policy shared by all paths.  `units` reduction units, `tiles` output
 // tiles per slice, `requested` the descriptor's split_k (-1 = auto).  Fills
 // units_per_slice, ks_count, needs_reduce, grid, slab_stride and ws_bytes.
+//
+// Auto degree: floor(target_groups / tiles) slices (so the grid never exceeds
+// target_groups), at most units / min_units, and with the slab traffic
+// (each slab element written once and read once) at most the algorithmic
+// bytes divided by traffic_div.
 conv_wgrad_status_t choose_split(int64_t units, int64_t tiles, int32_t requested, int64_t min_units,
-                                 int64_t target_groups, const Problem& p, conv_wgrad_plan_t* pub);
+                                 int64_t target_groups, int64_t traffic_div, const Problem& p,
+                                 conv_wgrad_plan_t* pub);
 
 }  // namespace cw

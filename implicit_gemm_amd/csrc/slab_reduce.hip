@@ -1,10 +1,20 @@
 // Stage 2: deterministic fold of the fp32 partial slabs (gfx950).
 //
-// dw[e] = (((ws[0][e] + ws[1][e]) + ws[2][e]) + ... ) + ws[ks-1][e], fp32
-// round-to-nearest-even adds in ascending slice order, then a plain store: no
-// epilogue is applied to partial sums (the two-stage split-K of
-// rocm-libraries PR #14393, sections "Two-stage split-K" and "Review
-// follow-ups").  Each lane folds 4 consecutive elements with 16-byte loads.
+// The slabs are summed with fp32 round-to-nearest-even adds in one fixed
+// order and then stored; no epilogue is applied to partial sums (the
+// two-stage split-K of rocm-libraries PR #14393, sections "Two-stage split-K"
+// and "Review follow-ups").
+//
+// One fold pass sums, for every output group o, the input slabs
+// [o*G, min(n, (o+1)*G)).  A workgroup owns 32 element chunks (4 floats
+// each) of one group; the group's slabs are cut into kParts consecutive
+// parts, lane (chunk, part) sums its part left to right with all its loads in
+// flight, and part sums are then added in ascending part order through LDS:
+//   out = ((sum(part 0) + sum(part 1)) + sum(part 2)) + ...
+// With at most 256 slabs a single pass writes dw; with more, a first pass
+// folds runs of 32 slabs into the first slab of each run and a second pass
+// folds those run sums.  The order depends only on the slab count, so the
+// result is bit-identical from run to run.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -12,43 +22,98 @@ namespace cw {
 
 namespace {
 
-struct ReduceArgs {
-  const float* ws;
-  float* dw;
-  int64_t E, slab_stride;
-  int32_t ks;
+constexpr int kParts = 8;         // lanes sharing one element chunk
+constexpr int kChunks = 32;       // element chunks per workgroup (256 lanes)
+constexpr int kRun = 32;          // slabs per run in the first of two passes
+constexpr int kMaxSinglePass = 256;
+constexpr int kBatch = 8;         // loads issued before their adds
+
+struct FoldArgs {
+  const float* src;   // input slab 0
+  int64_t src_step;   // floats between consecutive input slabs
+  int32_t n;          // input slabs
+  int32_t group;      // input slabs per output
+  float* dst;         // output 0
+  int64_t dst_step;   // floats between outputs
+  int64_t E;          // elements per slab
 };
 
-__global__ __launch_bounds__(256) void slab_reduce_kernel(ReduceArgs a) {
-  const float* __restrict__ ws = a.ws;
-  float* __restrict__ dw = a.dw;
-  const int64_t E = a.E, slab_stride = a.slab_stride;
-  const int32_t ks = a.ks;
-  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (i >= E) return;
-  if (i + 4 <= E) {
-    float4 acc = *reinterpret_cast<const float4*>(ws + i);
-    for (int32_t j = 1; j < ks; ++j) {
-      const float4 v = *reinterpret_cast<const float4*>(ws + (int64_t)j * slab_stride + i);
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+__device__ __forceinline__ float4 add4(float4 a, float4 b) {
+  return float4{a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w};
+}
+
+__global__ __launch_bounds__(256) void slab_fold_kernel(FoldArgs a) {
+  __shared__ float4 part_sum[kParts][kChunks];
+  __shared__ int part_len[kParts];
+  const int c = threadIdx.x % kChunks, p = threadIdx.x / kChunks;
+  const int64_t i = ((int64_t)blockIdx.x * kChunks + c) * 4;  // first element of the chunk
+  const int o = blockIdx.y;
+  const int first = o * a.group;
+  const int len = min(a.group, a.n - first);
+  const int lo = first + (int)((int64_t)p * len / kParts);
+  const int hi = first + (int)((int64_t)(p + 1) * len / kParts);
+  if (c == 0) part_len[p] = hi - lo;
+  const bool full = i + 4 <= a.E;
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (i < a.E && hi > lo) {
+    const float* s = a.src + (int64_t)lo * a.src_step + i;
+    if (full) {
+      acc = *reinterpret_cast<const float4*>(s);
+      int j = lo + 1;
+      for (; j + kBatch <= hi; j += kBatch) {
+        float4 v[kBatch];
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b)
+          v[b] = *reinterpret_cast<const float4*>(s + (int64_t)(j - lo + b) * a.src_step);
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) acc = add4(acc, v[b]);
+      }
+      for (; j < hi; ++j) acc = add4(acc, *reinterpret_cast<const float4*>(s + (int64_t)(j - lo) * a.src_step));
+    } else {
+      float t[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int e = 0; e < 4 && i + e < a.E; ++e) {
+        t[e] = s[e];
+        for (int j = lo + 1; j < hi; ++j) t[e] += s[(int64_t)(j - lo) * a.src_step + e];
+      }
+      acc = float4{t[0], t[1], t[2], t[3]};
     }
-    *reinterpret_cast<float4*>(dw + i) = acc;  // dw is 16-byte aligned (checked by the ABI)
-  } else {
-    for (int64_t e = i; e < E; ++e) {
-      float acc = ws[e];
-      for (int32_t j = 1; j < ks; ++j) acc += ws[(int64_t)j * slab_stride + e];
-      dw[e] = acc;
+  }
+  part_sum[p][c] = acc;
+  __syncthreads();  // every read of this group's slabs is done before the in-place store below
+  if (p == 0 && i < a.E) {
+    int q = 0;
+    while (part_len[q] == 0) ++q;  // the group has >= 1 slab, so some part is non-empty
+    float4 r = part_sum[q][c];
+    for (++q; q < kParts; ++q)
+      if (part_len[q] > 0) r = add4(r, part_sum[q][c]);
+    float* d = a.dst + (int64_t)o * a.dst_step + i;
+    if (full) {
+      *reinterpret_cast<float4*>(d) = r;  // dw and the slabs are 16-byte aligned
+    } else {
+      const float rv[4] = {r.x, r.y, r.z, r.w};
+      for (int e = 0; e < 4 && i + e < a.E; ++e) d[e] = rv[e];
     }
   }
 }
 
+hipError_t fold(const FoldArgs& a, int outputs, hipStream_t stream) {
+  const int64_t chunks = (a.E + 3) / 4;
+  const dim3 grid((unsigned)((chunks + kChunks - 1) / kChunks), (unsigned)outputs);
+  return launch_kernel(slab_fold_kernel, grid, dim3(256), a, stream);
+}
+
 }  // namespace
 
-hipError_t launch_slab_reduce(const Plan& plan, const float* ws, float* dw, hipStream_t stream) {
-  const int64_t E = plan.p.E;
-  const int64_t blocks = (E + 1023) / 1024;
-  ReduceArgs a{ws, dw, E, plan.pub.slab_stride, plan.pub.ks_count};
-  return launch_kernel(slab_reduce_kernel, dim3((unsigned)blocks), dim3(256), a, stream);
+hipError_t launch_slab_reduce(const Plan& plan, float* ws, float* dw, hipStream_t stream) {
+  const int64_t E = plan.p.E, stride = plan.pub.slab_stride;
+  const int32_t ks = plan.pub.ks_count;
+  if (ks <= kMaxSinglePass) return fold(FoldArgs{ws, stride, ks, ks, dw, 0, E}, 1, stream);
+  // Pass 1: run r of kRun slabs -> slab r*kRun (each workgroup reads all of
+  // its run before writing that run's first slab).
+  const int32_t runs = (ks + kRun - 1) / kRun;
+  hipError_t err = fold(FoldArgs{ws, stride, ks, kRun, ws, stride * kRun, E}, runs, stream);
+  if (err != hipSuccess) return err;
+  return fold(FoldArgs{ws, stride * kRun, runs, runs, dw, 0, E}, 1, stream);
 }
 
 }  // namespace cw

@@ -24,8 +24,10 @@
  * forward implicit-GEMM convolution on gfx1250", section "Two-stage split-K").
  * With ks_count > 1 every stage-1 workgroup writes its fp32 partial tile into
  * slab `slice` of the workspace exactly once, and a second kernel folds the
- * slabs in ascending slice order; with ks_count == 1 stage 1 writes dw
- * directly.  Results are therefore bit-identical from run to run for a fixed
+ * slabs in one fixed order that depends only on ks_count (8 consecutive
+ * parts of the slab range, each summed in ascending slab order, then the part
+ * sums in ascending part order; beyond 256 slabs, runs of 32 slabs are folded
+ * first the same way); with ks_count == 1 stage 1 writes dw directly.  Results are therefore bit-identical from run to run for a fixed
  * split degree, and the workspace needs no clearing.  Tensor base addresses
  * and image offsets are 64-bit, so tensors larger than 4 GB are handled in
  * one launch (the failure mode of rocm-libraries PR #11188, sections
@@ -63,7 +65,8 @@ typedef enum conv_wgrad_dtype {
  *   split_k    : -1 = choose the number of reduction slices automatically;
  *                n >= 1 = pin it.  The pinned degree is honoured except that
  *                no slice may be empty: with U reduction units the plan uses
- *                ceil(U / ceil(U / n)) slices (never more than n).  Any other
+ *                ceil(U / ceil(U / n')) slices with n' = min(n, 65536)
+ *                (never more than n).  Any other
  *                value (0, < -1) is CONV_WGRAD_ERR_BAD_SPLIT, as in the
  *                split-K validators of rocm-libraries PR #14393 (section
  *                "Review follow-ups": split_k <= 0 is rejected).

@@ -144,7 +144,7 @@ def test_device_pointer_errors():
     import torch
     import implicit_gemm_amd as iga
     x = torch.zeros(64 * 64, dtype=torch.float32, device="cuda")
-    d = iga.make_desc(1, 4, 4, 4, 4, 1, 1)
+    d = iga.make_desc(1, 4, 4, 4, 4, 1, 1, split_k=1)  # one slice: no workspace needed
     with pytest.raises(iga.ConvWgradError) as ei:
         iga.conv_wgrad(d, x.data_ptr() + 4, x.data_ptr(), x.data_ptr(), 0, 0)
     assert ei.value.name == "ERR_MISALIGNED"
