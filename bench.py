@@ -114,6 +114,8 @@ def main():
     ap.add_argument("--cold", type=int, default=20, help="cold-cache calls (0 = skip)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run 3 device-to-device copies of 1 GiB (scale for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the weight-gradient path runs on a single MI355X "
@@ -128,6 +130,14 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         return 1
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": src.numel() * 4, "copies": 3}))
+        return 0
     wl = wd.WORKLOADS[args.config]
     s = wl.shape
     if s.N > 64 and wl.n_sweep:

@@ -24,7 +24,7 @@ namespace cw {
 
 namespace {
 
-constexpr int kPf = 4;  // row batches in flight per wave
+constexpr int kPf = 8;  // row batches in flight per wave
 
 struct OneByOneArgs {
   const float* x;

@@ -1,0 +1,360 @@
+// Small-group 16-bit weight gradient on block-diagonal 16x16x32 MFMA (gfx950).
+//
+// Grouped convolutions with few channels per group (4 and 8 per group: the
+// cpg4 / cpg8 cases of rocm-libraries PR #14157, "depthwise 7x7 and grouped
+// cpg4/8 wgrad", section Technical Details) are computed as dense 16 x 16
+// products over "super-groups" of 16 consecutive channels, keeping only the
+// block-diagonal outputs where the output channel and the input channel belong
+// to the same group.  The discarded products cost MFMA issue slots, which are
+// plentiful here; the HBM bytes, the real bound, are each read once.
+//
+//   out[k][c] (tap r,s) += sum over 32 output pixels p of dY[p][k] * X[p + (r,s)][c]
+//
+// A workgroup owns 64 channels (4 waves x one super-group) and a slice of
+// units; a unit is up to 4 output rows x 32 output pixels of one image.  The
+// unit's dY pixels and the X pixels it needs (with zero padding) are staged in
+// LDS in their NHWC order (64 channels per pixel, 160-byte pixel pitch).  The
+// MFMA operands need 8 consecutive pixels of one channel per lane, which is a
+// transpose of that layout; ds_read_b64_tr_b16 does it on the read: within a
+// 16-lane group, lane j points at 4 channels of pixel j/4 and lane i receives
+// channel i of 4 consecutive pixels.  One A operand (dY) per output row serves
+// all R*S taps; each tap reads its B operand (X) at the tap's pixel offset.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace cw {
+
+namespace {
+
+constexpr int kCh = 64;                 // channels per workgroup
+constexpr int kPitchE = 80;             // 16-bit elements per staged pixel (64 + pad)
+constexpr int kWoT = 32;                // output pixels per unit row (one MFMA k-step)
+constexpr int kMaxRU = 4;               // output rows per unit
+constexpr int kMaxXRows = 8;
+constexpr int kMaxXPix = 40;
+constexpr int kMaxTaps = 9;
+constexpr int kDyPix = kMaxRU * kWoT;               // 128 staged dY pixels
+constexpr int kXPix = kMaxXRows * kMaxXPix;          // 320 staged X pixels
+constexpr int kLoaders = 256 / 8;                    // pixels per loader pass (8 x 16 B per pixel)
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+struct G16Args {
+  const void* x;
+  const void* dy;
+  float* out;
+  int64_t slab_stride;
+  int64_t x_img;
+  int32_t H, W, C, K, Ho, Wo, R, S, pad, dil, Cg, Kg, taps;
+  int32_t ru, hblocks, wchunks, xrows, xpix;
+  int32_t c_blocks, units, units_per_slice, ks_count;
+};
+
+__device__ __forceinline__ s16x4 tr_read(const unsigned short* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
+
+template <bool kBf16>
+__device__ __forceinline__ f32x4 mfma16(s16x8 a, s16x8 b, f32x4 c) {
+  if constexpr (kBf16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// RT x ST: compile-time filter size (0 x 0 = runtime size, at most kMaxTaps taps).
+template <bool kBf16, int RT, int ST>
+__global__ __launch_bounds__(256, 2) void grouped16_kernel(G16Args a) {
+  constexpr int kTaps = RT * ST > 0 ? RT * ST : kMaxTaps;
+  const int taps = RT * ST > 0 ? RT * ST : a.taps;
+  const int S = ST > 0 ? ST : a.S;
+  __shared__ __attribute__((aligned(16))) unsigned short s_dy[kDyPix * kPitchE];
+  __shared__ __attribute__((aligned(16))) unsigned short s_x[kXPix * kPitchE];
+  const unsigned short* __restrict__ x = static_cast<const unsigned short*>(a.x);
+  const unsigned short* __restrict__ dy = static_cast<const unsigned short*>(a.dy);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bid = blockIdx.x;
+  const int slice = bid % a.ks_count;
+  const int cb = bid / a.ks_count;
+  const int c0 = cb * kCh;
+  const int u_begin = slice * a.units_per_slice;
+  const int u_end = min(a.units, u_begin + a.units_per_slice);
+
+  // Loader role: pixel slot tid/8 (+32 per pass), 16-byte chunk q of the 64 channels.
+  const int q = tid & 7, pslot = tid >> 3;
+  const bool ch_ok = c0 + 8 * q < a.C;  // C % 8 == 0: a chunk is all in or all out
+  uint4 rdy[kDyPix / kLoaders];
+  uint4 rx[kXPix / kLoaders];
+
+  auto load_unit = [&](int u) {
+    const int wc = u % a.wchunks;
+    const int t = u / a.wchunks;
+    const int hb = t % a.hblocks, n = t / a.hblocks;
+    const int ho0 = hb * a.ru, wo0 = wc * kWoT;
+#pragma unroll
+    for (int i = 0; i < kDyPix / kLoaders; ++i) {
+      const int pp = pslot + kLoaders * i;
+      const int rho = pp / kWoT, p = pp % kWoT;
+      const int ho = ho0 + rho, wo = wo0 + p;
+      rdy[i] = uint4{0u, 0u, 0u, 0u};
+      if (ch_ok && rho < a.ru && ho < a.Ho && wo < a.Wo)
+        rdy[i] = *reinterpret_cast<const uint4*>(
+            dy + ((int64_t)(n * a.Ho + ho) * a.Wo + wo) * a.K + c0 + 8 * q);
+    }
+    const int h0 = ho0 - a.pad, w0 = wo0 - a.pad;
+#pragma unroll
+    for (int i = 0; i < kXPix / kLoaders; ++i) {
+      const int pp = pslot + kLoaders * i;
+      const int xr = pp / kMaxXPix, xp = pp % kMaxXPix;
+      const int h = h0 + xr, w = w0 + xp;
+      rx[i] = uint4{0u, 0u, 0u, 0u};
+      if (ch_ok && xr < a.xrows && xp < a.xpix && h >= 0 && h < a.H && w >= 0 && w < a.W)
+        rx[i] = *reinterpret_cast<const uint4*>(
+            x + (int64_t)n * a.x_img + ((int64_t)h * a.W + w) * a.C + c0 + 8 * q);
+    }
+  };
+  auto store_unit = [&]() {
+#pragma unroll
+    for (int i = 0; i < kDyPix / kLoaders; ++i)
+      *reinterpret_cast<uint4*>(&s_dy[(pslot + kLoaders * i) * kPitchE + 8 * q]) = rdy[i];
+#pragma unroll
+    for (int i = 0; i < kXPix / kLoaders; ++i)
+      *reinterpret_cast<uint4*>(&s_x[(pslot + kLoaders * i) * kPitchE + 8 * q]) = rx[i];
+  };
+
+  // Transposed-read addressing: in 16-lane group g, lane j points at pixel
+  // 8g + (j >> 2) (+4 for the second half of the k-step) and channels
+  // 16*wave + 4*(j & 3) .. +3.
+  const int j = lane & 15, g = lane >> 4;
+  const int pix_lane = 8 * g + (j >> 2);
+  const int ch_lane = 16 * wave + 4 * (j & 3);
+  int tap_off[kTaps];  // X pixel offset of tap t in the staged tile
+#pragma unroll
+  for (int t = 0; t < kTaps; ++t) {
+    const int tt = t < taps ? t : 0;
+    tap_off[t] = ((tt / S) * a.dil * kMaxXPix + (tt % S) * a.dil) * kPitchE;
+  }
+
+  f32x4 acc[kTaps];
+#pragma unroll
+  for (int t = 0; t < kTaps; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Operands of one output row: A (dY) and the B (X) of every tap.  All reads
+  // of a row are issued before its MFMAs, and the next row's reads before the
+  // current row's MFMAs.
+  s16x8 fa0, fa1, fb0[kTaps], fb1[kTaps];
+  auto read_row = [&](int rho, s16x8& fa, s16x8 (&fb)[kTaps]) {
+    const unsigned short* pa = s_dy + (rho * kWoT + pix_lane) * kPitchE + ch_lane;
+    fa = __builtin_shufflevector(tr_read(pa), tr_read(pa + 4 * kPitchE), 0, 1, 2, 3, 4, 5, 6, 7);
+    const unsigned short* pb = s_x + (rho * kMaxXPix + pix_lane) * kPitchE + ch_lane;
+#pragma unroll
+    for (int t = 0; t < kTaps; ++t) {
+      if (RT * ST > 0 || t < taps) {
+        const unsigned short* pt = pb + tap_off[t];
+        fb[t] = __builtin_shufflevector(tr_read(pt), tr_read(pt + 4 * kPitchE), 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    }
+  };
+  auto mfma_row = [&](const s16x8& fa, const s16x8 (&fb)[kTaps]) {
+#pragma unroll
+    for (int t = 0; t < kTaps; ++t)
+      if (RT * ST > 0 || t < taps) acc[t] = mfma16<kBf16>(fa, fb[t], acc[t]);
+  };
+
+  if (u_begin < u_end) load_unit(u_begin);
+  for (int u = u_begin; u < u_end; ++u) {
+    __syncthreads();  // previous unit's reads of the tiles are done
+    store_unit();
+    __syncthreads();
+    if (u + 1 < u_end) load_unit(u + 1);
+    read_row(0, fa0, fb0);
+    for (int rho = 0; rho < a.ru; rho += 2) {
+      if (rho + 1 < a.ru) read_row(rho + 1, fa1, fb1);
+      mfma_row(fa0, fb0);
+      if (rho + 1 < a.ru) {
+        if (rho + 2 < a.ru) read_row(rho + 2, fa0, fb0);
+        mfma_row(fa1, fb1);
+      }
+    }
+  }
+
+  // acc[t][v] = out[k = c0 + 16*wave + 4*g + v][c = c0 + 16*wave + j] for tap t;
+  // only same-group pairs are outputs.
+  float* out = a.out + (int64_t)slice * a.slab_stride;
+  const int c = c0 + 16 * wave + j;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int k = c0 + 16 * wave + 4 * g + v;
+    if (k < a.K && c < a.C && k / a.Kg == c / a.Cg) {
+      float* o = out + (int64_t)k * taps * a.Cg + (c % a.Cg);
+#pragma unroll
+      for (int t = 0; t < kTaps; ++t)
+        if (t < taps) o[t * a.Cg] = acc[t][v];
+    }
+  }
+}
+
+// Fast path for stride 1, dilation 1 and a compile-time R x S filter with 4
+// output rows per unit.  The loop runs over the staged X rows instead of the
+// output rows: X row t is read once per tap column s (S transposed reads) and
+// multiplied with every dY row t - r that uses it, whose A operands stay in
+// registers.  Per unit and wave: 4 A reads + (4 + R - 1) * S B reads for
+// 4 * R * S MFMAs.  The LDS tiles are sized exactly (three workgroups per CU
+// for 3 x 3).
+template <bool kBf16, int R, int S>
+__global__ __launch_bounds__(256, 3) void grouped16_win_kernel(G16Args a) {
+  constexpr int RU = 4, XR = RU + R - 1, XP = kWoT + S - 1;
+  constexpr int kDy = RU * kWoT, kX = XR * XP;
+  __shared__ __attribute__((aligned(16))) unsigned short s_dy[kDy * kPitchE];
+  __shared__ __attribute__((aligned(16))) unsigned short s_x[kX * kPitchE];
+  const unsigned short* __restrict__ x = static_cast<const unsigned short*>(a.x);
+  const unsigned short* __restrict__ dy = static_cast<const unsigned short*>(a.dy);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bid = blockIdx.x;
+  const int slice = bid % a.ks_count;
+  const int c0 = (bid / a.ks_count) * kCh;
+  const int u_begin = slice * a.units_per_slice;
+  const int u_end = min(a.units, u_begin + a.units_per_slice);
+
+  const int q = tid & 7, pslot = tid >> 3;
+  const bool ch_ok = c0 + 8 * q < a.C;
+  constexpr int kDyLoads = (kDy + kLoaders - 1) / kLoaders;
+  constexpr int kXLoads = (kX + kLoaders - 1) / kLoaders;
+  uint4 rdy[kDyLoads], rx[kXLoads];
+
+  auto load_unit = [&](int u) {
+    const int wc = u % a.wchunks;
+    const int t = u / a.wchunks;
+    const int hb = t % a.hblocks, n = t / a.hblocks;
+    const int ho0 = hb * RU, wo0 = wc * kWoT;
+#pragma unroll
+    for (int i = 0; i < kDyLoads; ++i) {
+      const int pp = pslot + kLoaders * i;
+      const int rho = pp / kWoT, p = pp % kWoT;
+      const int ho = ho0 + rho, wo = wo0 + p;
+      rdy[i] = uint4{0u, 0u, 0u, 0u};
+      if (ch_ok && pp < kDy && ho < a.Ho && wo < a.Wo)
+        rdy[i] = *reinterpret_cast<const uint4*>(
+            dy + ((int64_t)(n * a.Ho + ho) * a.Wo + wo) * a.K + c0 + 8 * q);
+    }
+    const int h0 = ho0 - a.pad, w0 = wo0 - a.pad;
+#pragma unroll
+    for (int i = 0; i < kXLoads; ++i) {
+      const int pp = pslot + kLoaders * i;
+      const int xr = pp / XP, xp = pp % XP;
+      const int h = h0 + xr, w = w0 + xp;
+      rx[i] = uint4{0u, 0u, 0u, 0u};
+      if (ch_ok && pp < kX && h >= 0 && h < a.H && w >= 0 && w < a.W)
+        rx[i] = *reinterpret_cast<const uint4*>(
+            x + (int64_t)n * a.x_img + ((int64_t)h * a.W + w) * a.C + c0 + 8 * q);
+    }
+  };
+  auto store_unit = [&]() {
+#pragma unroll
+    for (int i = 0; i < kDyLoads; ++i)
+      if (pslot + kLoaders * i < kDy)
+        *reinterpret_cast<uint4*>(&s_dy[(pslot + kLoaders * i) * kPitchE + 8 * q]) = rdy[i];
+#pragma unroll
+    for (int i = 0; i < kXLoads; ++i)
+      if (pslot + kLoaders * i < kX)
+        *reinterpret_cast<uint4*>(&s_x[(pslot + kLoaders * i) * kPitchE + 8 * q]) = rx[i];
+  };
+
+  const int j = lane & 15, g = lane >> 4;
+  const int lane_off = (8 * g + (j >> 2)) * kPitchE + 16 * wave + 4 * (j & 3);
+  auto tr8 = [&](const unsigned short* p) {
+    return __builtin_shufflevector(tr_read(p), tr_read(p + 4 * kPitchE), 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+
+  f32x4 acc[R * S];
+#pragma unroll
+  for (int t = 0; t < R * S; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (u_begin < u_end) load_unit(u_begin);
+  for (int u = u_begin; u < u_end; ++u) {
+    __syncthreads();
+    store_unit();
+    __syncthreads();
+    if (u + 1 < u_end) load_unit(u + 1);
+    s16x8 fa[RU];
+#pragma unroll
+    for (int t = 0; t < XR; ++t) {
+      if (t < RU) fa[t] = tr8(s_dy + t * kWoT * kPitchE + lane_off);
+      s16x8 fb[S];
+#pragma unroll
+      for (int s = 0; s < S; ++s) fb[s] = tr8(s_x + (t * XP + s) * kPitchE + lane_off);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int rho = t - r;
+        if (rho >= 0 && rho < RU) {
+#pragma unroll
+          for (int s = 0; s < S; ++s) acc[r * S + s] = mfma16<kBf16>(fa[rho], fb[s], acc[r * S + s]);
+        }
+      }
+    }
+  }
+
+  float* out = a.out + (int64_t)slice * a.slab_stride;
+  const int c = c0 + 16 * wave + j;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int k = c0 + 16 * wave + 4 * g + v;
+    if (k < a.K && c < a.C && k / a.Kg == c / a.Cg) {
+      float* o = out + (int64_t)k * (R * S) * a.Cg + (c % a.Cg);
+#pragma unroll
+      for (int t = 0; t < R * S; ++t) o[t * a.Cg] = acc[t][v];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_grouped16(const Plan& plan, const void* x, const void* dy, Stage1Out out,
+                            hipStream_t stream) {
+  const Problem& p = plan.p;
+  G16Args a;
+  a.x = x;
+  a.dy = dy;
+  a.out = out.base;
+  a.slab_stride = out.slab_stride;
+  a.x_img = p.x_img;
+  a.H = (int32_t)p.H; a.W = (int32_t)p.W; a.C = (int32_t)p.C; a.K = (int32_t)p.K;
+  a.Ho = (int32_t)p.Ho; a.Wo = (int32_t)p.Wo; a.R = (int32_t)p.R; a.S = (int32_t)p.S;
+  a.pad = (int32_t)p.pad; a.dil = (int32_t)p.dil;
+  a.Cg = (int32_t)p.Cg; a.Kg = (int32_t)p.Kg; a.taps = (int32_t)(p.R * p.S);
+  a.ru = plan.ru;
+  a.hblocks = (int32_t)ceil_div(p.Ho, plan.ru);
+  a.wchunks = (int32_t)ceil_div(p.Wo, kWoT);
+  a.xrows = plan.xrows;
+  a.xpix = plan.xspan;
+  a.c_blocks = (int32_t)ceil_div(p.C, kCh);
+  a.units = (int32_t)plan.pub.units;
+  a.units_per_slice = (int32_t)plan.pub.units_per_slice;
+  a.ks_count = plan.pub.ks_count;
+  const dim3 grid((unsigned)plan.pub.grid), block(256);
+  const bool bf = p.dtype == CONV_WGRAD_BF16;
+  if (plan.ru == 4 && p.dil == 1 && p.R == 3 && p.S == 3)
+    return bf ? launch_kernel(grouped16_win_kernel<true, 3, 3>, grid, block, a, stream)
+              : launch_kernel(grouped16_win_kernel<false, 3, 3>, grid, block, a, stream);
+  if (plan.ru == 4 && p.dil == 1 && p.R == 1 && p.S == 1)
+    return bf ? launch_kernel(grouped16_win_kernel<true, 1, 1>, grid, block, a, stream)
+              : launch_kernel(grouped16_win_kernel<false, 1, 1>, grid, block, a, stream);
+  if (p.R == 3 && p.S == 3)
+    return bf ? launch_kernel(grouped16_kernel<true, 3, 3>, grid, block, a, stream)
+              : launch_kernel(grouped16_kernel<false, 3, 3>, grid, block, a, stream);
+  if (p.R == 1 && p.S == 1)
+    return bf ? launch_kernel(grouped16_kernel<true, 1, 1>, grid, block, a, stream)
+              : launch_kernel(grouped16_kernel<false, 1, 1>, grid, block, a, stream);
+  return bf ? launch_kernel(grouped16_kernel<true, 0, 0>, grid, block, a, stream)
+            : launch_kernel(grouped16_kernel<false, 0, 0>, grid, block, a, stream);
+}
+
+}  // namespace cw

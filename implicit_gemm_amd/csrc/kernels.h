@@ -28,6 +28,10 @@ hipError_t launch_dense_rows(const Plan& plan, const void* x, const void* dy, St
                              hipStream_t stream);
 hipError_t launch_dense_1x1(const Plan& plan, const void* x, const void* dy, Stage1Out out,
                             hipStream_t stream);
+hipError_t launch_grouped16(const Plan& plan, const void* x, const void* dy, Stage1Out out,
+                            hipStream_t stream);
+hipError_t launch_depthwise(const Plan& plan, const void* x, const void* dy, Stage1Out out,
+                            hipStream_t stream);
 hipError_t launch_direct(const Plan& plan, const void* x, const void* dy, Stage1Out out,
                          hipStream_t stream);
 hipError_t launch_slab_reduce(const Plan& plan, float* ws, float* dw, hipStream_t stream);

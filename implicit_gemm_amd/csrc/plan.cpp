@@ -169,6 +169,54 @@ bool plan_dense_1x1(const Problem& p, Plan* out) {
   return true;
 }
 
+// Block-diagonal 16-bit kernel (grouped16.hip): stride 1, equal channels per
+// group dividing 16, channel count in 16-channel super-groups, at most 9 taps,
+// and a staged tile of at most 8 X rows x 40 X pixels.
+bool plan_grouped16(const Problem& p, Plan* out) {
+  if (p.dtype == CONV_WGRAD_F32 || p.stride != 1 || p.Cg != p.Kg || 16 % p.Cg != 0) return false;
+  if (p.C % 16 != 0 || p.R * p.S > 9 || (p.S - 1) * p.dil + 32 > 40) return false;
+  int32_t ru = 0;
+  for (int32_t cand = 4; cand >= 1; cand /= 2) {
+    if ((cand - 1) + (p.R - 1) * p.dil + 1 <= 8) {
+      ru = cand;
+      break;
+    }
+  }
+  if (ru == 0) return false;
+  out->ru = ru;
+  out->xrows = (int32_t)((ru - 1) + (p.R - 1) * p.dil + 1);
+  out->xspan = (int32_t)(31 + (p.S - 1) * p.dil + 1);
+  out->c_tiles = ceil_div(p.C, 64);
+  out->wchunks = ceil_div(p.Wo, 32);
+  return true;
+}
+
+// Depthwise 4x4x4 kernel (depthwise_mfma.hip): 16-bit, one channel per group,
+// stride 1, no dilation, channels in whole 16-channel waves, filter up to
+// 8 x 8, rows of at most 128 columns.  Staged row lengths are odd multiples of
+// 8 elements and the ring slot pitch is 8 mod 256 bytes, which keeps the
+// operand reads of a wave at the minimum two bank passes.
+bool plan_depthwise(const Problem& p, Plan* out) {
+  if (p.dtype == CONV_WGRAD_F32 || p.Cg != 1 || p.Kg != 1 || p.stride != 1 || p.dil != 1) return false;
+  if (p.C % 16 != 0 || p.R > 8 || p.S > 8 || p.W > 120 || p.Wo + 4 > 128) return false;
+  int64_t xl = 8;
+  while (xl < p.W) xl += 16;
+  int64_t xslot = 32 * xl;
+  xslot += ((8 - xslot) % 256 + 256) % 256;
+  int64_t need = p.Wo + 16;
+  if (need < 8 + p.pad + xl + 2) need = 8 + p.pad + xl + 2;
+  int64_t dl = 8;
+  while (dl < need) dl += 16;
+  const int64_t lds = ceil_div(8 * xslot + 2 * 16 * dl * 2, 16) * 16;
+  if (lds > 64 * 1024) return false;
+  out->dw_xl = (int32_t)xl;
+  out->dw_dl = (int32_t)dl;
+  out->dw_xslot = (int32_t)xslot;
+  out->dw_lds = (int32_t)lds;
+  out->c_tiles = p.C / 16;
+  return true;
+}
+
 }  // namespace
 
 conv_wgrad_status_t make_plan(const conv_wgrad_desc_t* desc, Plan* out) {
@@ -189,6 +237,32 @@ conv_wgrad_status_t make_plan(const conv_wgrad_desc_t* desc, Plan* out) {
   pub.windows_4g = (int64_t)((big + ((uint64_t)1 << 32) - 1) >> 32);
 
   const bool small_groups = p.groups > 1 && p.Cg <= 8 && p.Kg <= 8;
+  if (small_groups && plan_depthwise(p, out)) {
+    pub.path = CONV_WGRAD_PATH_DIRECT;
+    pub.variant = kDepthwise;
+    pub.unit_rows = p.Wo;  // a unit is one output row
+    int64_t units;
+    if (!mul_ok(p.N, p.Ho, &units)) return CONV_WGRAD_ERR_UNSUPPORTED;
+    // One-wave workgroups, about eight per CU.
+    st = choose_split(units, out->c_tiles, desc->split_k, 8, 2048, 4, p, &pub);
+    if (st != CONV_WGRAD_OK) return st;
+    // Launch grid of the XCD-aware mapping: 32 blocks per 8 (slice, channel
+    // quad) pairs; blocks past the work return at once.
+    int64_t grid;
+    if (!mul_ok(ceil_div((int64_t)pub.ks_count * ceil_div(p.C, 64), 8), 32, &grid) || grid > kI32Max)
+      return CONV_WGRAD_ERR_UNSUPPORTED;
+    pub.grid = grid;
+    return CONV_WGRAD_OK;
+  }
+  if (small_groups && plan_grouped16(p, out)) {
+    pub.path = CONV_WGRAD_PATH_DIRECT;
+    pub.variant = kGrouped16;
+    pub.unit_rows = (int64_t)out->ru * 32;
+    int64_t units;
+    if (!mul3(p.N, ceil_div(p.Ho, out->ru), out->wchunks, &units)) return CONV_WGRAD_ERR_UNSUPPORTED;
+    // 2 (3 for the 3x3 and 1x1 fast path) workgroups per CU fit in LDS.
+    return choose_split(units, out->c_tiles, desc->split_k, 2, 768, 4, p, &pub);
+  }
   if (small_groups) {
     // Direct path: one dW element per lane; a unit is 64 output pixels.
     pub.path = CONV_WGRAD_PATH_DIRECT;

@@ -19,6 +19,8 @@ enum Variant : int32_t {
   kDenseRows = 1,     // dense implicit GEMM over output-row units, per-filter-row tiles
   kDense1x1 = 2,      // 1x1 stride-1 unpadded fp32: rows streamed into MFMA registers
   kDirectElem = 10,   // direct small-group kernel, one dW element per lane
+  kGrouped16 = 11,    // 16-bit small groups: block-diagonal 16x16x32 MFMA, transposed LDS reads
+  kDepthwise = 12,    // 16-bit depthwise: batched 4x4x4 MFMA, one wave per 16 channels
 };
 
 struct Problem {
@@ -44,6 +46,8 @@ struct Plan {
   int32_t sb, wt, xspan;   // taps per tile, output pixels per unit, staged X pixels per unit
   int64_t c_tiles, s_blocks, wchunks;
   int32_t bv;              // 1x1 kernel: input channels per lane
+  int32_t ru, xrows;       // grouped16: output rows per unit, staged X rows
+  int32_t dw_xl, dw_dl, dw_xslot, dw_lds;  // depthwise: staged row lengths, ring slot bytes, LDS bytes
   // Direct path.
   int32_t threads;         // lanes per workgroup
 };

@@ -6,7 +6,7 @@
 // and "Review follow-ups").
 //
 // One fold pass sums, for every output group o, the input slabs
-// [o*G, min(n, (o+1)*G)).  A workgroup owns 32 element chunks (4 floats
+// [o*G, min(n, (o+1)*G)).  A workgroup owns 16 element chunks (4 floats
 // each) of one group; the group's slabs are cut into kParts consecutive
 // parts, lane (chunk, part) sums its part left to right with all its loads in
 // flight, and part sums are then added in ascending part order through LDS:
@@ -22,8 +22,8 @@ namespace cw {
 
 namespace {
 
-constexpr int kParts = 8;         // lanes sharing one element chunk
-constexpr int kChunks = 32;       // element chunks per workgroup (256 lanes)
+constexpr int kParts = 16;        // lanes sharing one element chunk
+constexpr int kChunks = 16;       // element chunks per workgroup (256 lanes)
 constexpr int kRun = 32;          // slabs per run in the first of two passes
 constexpr int kMaxSinglePass = 256;
 constexpr int kBatch = 8;         // loads issued before their adds

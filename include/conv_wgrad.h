@@ -24,7 +24,7 @@
  * forward implicit-GEMM convolution on gfx1250", section "Two-stage split-K").
  * With ks_count > 1 every stage-1 workgroup writes its fp32 partial tile into
  * slab `slice` of the workspace exactly once, and a second kernel folds the
- * slabs in one fixed order that depends only on ks_count (8 consecutive
+ * slabs in one fixed order that depends only on ks_count (16 consecutive
  * parts of the slab range, each summed in ascending slab order, then the part
  * sums in ascending part order; beyond 256 slabs, runs of 32 slabs are folded
  * first the same way); with ks_count == 1 stage 1 writes dw directly.  Results are therefore bit-identical from run to run for a fixed

@@ -115,6 +115,11 @@ def check_plan_invariants(d, p):
     assert p.E == d.K * d.R * d.S * (d.C // d.groups)
     if p.path == iga.PATH_DENSE and p.variant == 1:   # row units: (n, ho, chunk of Wo)
         assert p.units == d.N * Ho * -(-Wo // p.unit_rows)
+    elif p.variant == 12:                             # depthwise: one output row per unit
+        assert p.units == d.N * Ho and p.unit_rows == Wo
+    elif p.variant == 11:                             # units of ru rows x 32 pixels
+        ru = p.unit_rows // 32
+        assert p.units == d.N * -(-Ho // ru) * -(-Wo // 32)
     else:
         assert p.units == -(-p.L // p.unit_rows)
     ups, ks = p.units_per_slice, p.ks_count
@@ -125,7 +130,10 @@ def check_plan_invariants(d, p):
         assert ks <= d.split_k
         assert ups == -(-p.units // min(d.split_k, p.units))
     assert p.needs_reduce == (1 if ks > 1 else 0)
-    assert p.grid == p.tiles * ks
+    if p.variant == 12:   # depthwise: XCD-aware grid, 32 blocks per 8 (slice, channel quad) pairs
+        assert p.grid == 32 * -(-(ks * -(-d.C // 64)) // 8) and p.grid >= p.tiles * ks
+    else:
+        assert p.grid == p.tiles * ks
     assert p.slab_stride % 64 == 0 and p.slab_stride >= p.E
     assert p.ws_bytes == (ks * p.slab_stride * 4 if ks > 1 else 0)
     esz = 4 if d.dtype == iga.F32 else 2

@@ -170,3 +170,35 @@ def test_nonzero_result_stream_and_default_stream():
     torch.cuda.synchronize()
     assert torch.equal(a, b)
     assert int((a == 0).sum()) == 0
+
+
+SMALL_GROUP_CASES = [
+    # depthwise on the 4x4x4 kernel: filter sizes 1..8, pads, widths, ragged rows
+    (wd.ConvShape(2, 16, 9, 11, 16, 7, 7, pad=3, groups=16), "bf16", -1),
+    (wd.ConvShape(1, 32, 12, 120, 32, 5, 3, pad=2, groups=32), "f16", -1),
+    (wd.ConvShape(3, 48, 7, 7, 48, 3, 3, pad=1, groups=48), "bf16", 5),
+    (wd.ConvShape(2, 16, 10, 13, 16, 8, 8, pad=4, groups=16), "f16", 3),
+    (wd.ConvShape(2, 16, 6, 30, 16, 1, 1, pad=0, groups=16), "bf16", -1),
+    (wd.ConvShape(2, 32, 15, 17, 32, 2, 6, pad=0, groups=32), "bf16", 7),
+    (wd.ConvShape(4, 16, 5, 6, 16, 7, 7, pad=3, groups=16), "f16", 1),
+    (wd.ConvShape(2, 16, 9, 9, 16, 7, 7, pad=0, groups=16), "bf16", -1),      # Ho = Wo = 3
+    # grouped 16-bit: windowed 3x3 / 1x1 paths and the generic path (dilation, 2x2)
+    (wd.ConvShape(3, 64, 10, 37, 64, 3, 3, pad=1, groups=16), "f16", -1),
+    (wd.ConvShape(2, 128, 9, 9, 128, 1, 1, pad=0, groups=16), "bf16", 3),
+    (wd.ConvShape(2, 48, 11, 12, 48, 3, 3, pad=2, dilation=2, groups=6), "bf16", -1),
+    (wd.ConvShape(2, 32, 8, 8, 32, 2, 2, pad=1, groups=4), "f16", -1),
+    (wd.ConvShape(2, 80, 6, 70, 80, 3, 3, pad=1, groups=10), "bf16", -1),     # two 32-pixel chunks + ragged
+]
+
+
+@pytest.mark.parametrize("idx", range(len(SMALL_GROUP_CASES)))
+def test_small_group_kernels(idx):
+    import implicit_gemm_amd as iga
+    shp, dtype, split_k = SMALL_GROUP_CASES[idx]
+    d = iga.make_desc(shp.N, shp.C, shp.H, shp.W, shp.K, shp.R, shp.S, shp.pad, shp.stride,
+                      shp.dilation, shp.groups, {"f32": 0, "bf16": 1, "f16": 2}[dtype], split_k)
+    plan = iga.get_plan(d)
+    log("small-group", idx, shp, dtype, "split", split_k, "variant", plan.variant, "ks", plan.ks_count)
+    x, dy = wd.random_inputs(shp, dtype, seed=500 + idx, x_dist=wd.Dist("normal", 1.0),
+                             dy_dist=wd.Dist("normal", 0.1))
+    check_against_oracle(x, dy, shp, dtype, split_k=split_k)
