@@ -7,22 +7,35 @@
 // grouped cpg4/8 wgrad on batched mfma 4x4x4", Technical Details), one
 // v_mfma_f32_4x4x4_16b instruction computes 16 independent 4 x 4 x 4 products,
 // here one per channel: block b = channel, M = 4 filter rows r, N = 4 filter
-// columns s, K = 4 input columns w.  2 x 2 instructions (RB x SB) cover a
-// filter of up to 8 x 8.
+// columns s, K = 4 input columns w.  RB x SB (up to 2 x 2) instructions cover
+// a filter of up to 8 x 8.
 //
 //   A_b[i][k] = X[ho - pad + 4*rb + i][w0 + k]        (4 consecutive columns of one row)
 //   B_b[k][j] = dY[ho][w0 + k - (4*sb + j) + pad]     (a shifted dY row segment)
 //
-// Each one-wave workgroup owns 16 channels and a slice of output rows.  Rows
-// are staged in LDS per channel with columns contiguous, so A is one aligned
-// 8-byte read.  B starts at a column that depends on the lane's j; every dY row
-// is stored twice, the second copy shifted by one element, so each lane reads
-// its window dword-aligned from one of the two copies.  The B operand of
-// s-block 1 at column step w0 equals the s-block-0 operand of step w0 - 4, so
-// it is carried in registers.  X rows live in an 8-row ring (a row is loaded
-// once per slice); the NHWC -> per-channel transpose happens in registers
-// (v_perm_b32) between the global load and the LDS store, and rows are
-// prefetched four steps ahead.  The wave never waits on another wave.
+// A workgroup of four waves owns 64 consecutive channels (one 128-byte pixel
+// segment of X and dY) and a slice of output rows; wave w computes channels
+// w, w + 4, ..., w + 60 of them.  Per step the workgroup loads one X row and
+// one dY row with full-line 16-byte loads (8 lanes per pixel) and stages them
+// in LDS per channel with columns contiguous:
+//  * Raw buffer loads whose range is the valid part of the row (empty for rows
+//    outside the image or the segment) supply the zero padding.
+//  * A lane holds 2 pixels x 8 channels and transposes them to 8 channel
+//    dwords with v_perm_b32.  Interleaving channels across waves puts the
+//    8 octets of one store instruction in 8 different 32-byte bank groups.
+//  * X rows live in a ring of 4 or 8 rows.  The channel pitch is 16 mod 32
+//    bytes and the slot pitch 64 mod 256 bytes, so the A reads (one 16-byte
+//    read gives the operands of two column steps) are free of bank conflicts.
+//  * dY rows alternate between two buffers.  A lane's B window starts at a
+//    column that depends on its filter column j; it is cut out of two aligned
+//    8-byte blocks with three selects and two v_perm_b32 (per-lane choices).
+//    The B operand of s-block 1 at column step w0 equals the s-block-0
+//    operand of step w0 - 4, so it is carried in registers.
+// The staged row length is a template parameter: every LDS offset is an
+// immediate and a row's column loop is fully unrolled.  One barrier per step
+// (waiting for LDS only, so global loads stay kPf steps ahead) separates the
+// staging of step t from the MFMAs of step t; the ring holds R + 1 rows and
+// the dY buffers alternate, so step t + 1 can be staged while step t computes.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -30,13 +43,14 @@ namespace cw {
 
 namespace {
 
-constexpr int kChW = 16;     // channels per wave (MFMA blocks)
-constexpr int kRing = 8;     // X rows held
-constexpr int kOff = 8;      // leading zero columns of a staged dY row
-constexpr int kPf = 4;       // steps prefetched ahead
+constexpr int kThreads = 256;
+constexpr int kQuadCh = 64;   // channels per workgroup
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) const unsigned char lds_cu8;
 
 struct DwArgs {
   const void* x;
@@ -45,11 +59,23 @@ struct DwArgs {
   int64_t slab_stride;
   int64_t x_img, dy_img;   // elements per image
   int32_t H, W, C, Ho, Wo, R, S, pad;
-  int32_t xl, dl;          // staged row lengths (elements) of X and dY
-  int32_t x_slot;          // bytes between X ring slots
+  int32_t dy_off;          // column of dY element 0 in a staged dY row
   int32_t rows, rows_per_slice, ks_count;  // rows = N * Ho
-  int32_t quads;           // ceil(C / 64): channel quads of four 16-channel groups
-  int32_t lds_bytes;
+  int32_t quads;           // ceil(C / 64)
+};
+
+// LDS layout for staged rows of XL columns.
+template <int XL, int RING>
+struct DwLayout {
+  static constexpr int kCs = 2 * XL;              // bytes per X channel row
+  static constexpr int kXWave = 16 * kCs;         // bytes per wave in a ring slot
+  static constexpr int kSlot = 64 * kCs + 64;     // ring slot pitch (64 mod 256)
+  static constexpr int kDl = XL + 16;             // dY row length (elements, 8 mod 16)
+  static constexpr int kDs = 2 * kDl;             // bytes per dY channel row
+  static constexpr int kDWave = 16 * kDs;
+  static constexpr int kDBuf = 64 * kDs;          // bytes per dY buffer
+  static constexpr int kDyBase = RING * kSlot;
+  static constexpr int kBytes = kDyBase + 2 * kDBuf;
 };
 
 template <bool kBf16>
@@ -61,111 +87,119 @@ __device__ __forceinline__ f32x4 mfma4(s16x4 a, s16x4 b, f32x4 c) {
                                               __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
 }
 
-// 4 pixels x 8 channels of one row, as loaded (pixel-major).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const unsigned char* base, int nbytes) {
+  // gfx9 raw buffer: stride 0, default data format; offsets >= nbytes read 0.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(base), (short)0, nbytes,
+                                           0x00020000);
+}
+
+// Workgroup barrier that waits for this wave's LDS accesses only (not for
+// its outstanding global loads); the memory clobber keeps the compiler from
+// moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Pixels 2pp, 2pp + 1 x 8 channels per pass, as loaded (pixel-major).
+template <int NP>
 struct Item {
-  uint4 p[4];
+  u32x4 p[NP][2];
 };
 
-__device__ __forceinline__ void fetch(const unsigned short* base, int64_t row_off, int n_pix,
-                                      int cstride, int pg, bool active, Item& it) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int w = 4 * pg + q;
-    it.p[q] = uint4{0u, 0u, 0u, 0u};
-    if (active && w < n_pix)
-      it.p[q] = *reinterpret_cast<const uint4*>(base + row_off + (int64_t)w * cstride);
-  }
-}
-
-__device__ __forceinline__ uint32_t word(const uint4& v, int k) {
-  return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
-}
-
-// Channel cc of the item: pixels (0,1) and (2,3) packed as two dwords.
-__device__ __forceinline__ void channel_pair(const Item& it, int cc, uint32_t& lo, uint32_t& hi) {
-  const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
-  lo = __builtin_amdgcn_perm(word(it.p[1], cc >> 1), word(it.p[0], cc >> 1), sel);
-  hi = __builtin_amdgcn_perm(word(it.p[3], cc >> 1), word(it.p[2], cc >> 1), sel);
-}
-
-template <bool kBf16, int RB, int SB>
-__global__ __launch_bounds__(64) void depthwise_mfma_kernel(DwArgs a) {
+template <bool kBf16, int RB, int SB, int XL>
+__global__ __launch_bounds__(kThreads) void depthwise_mfma_kernel(DwArgs a) {
+  constexpr int NP = XL > 64 ? 2 : 1;   // pixel-pair passes per row
+  constexpr int kPf = NP == 1 ? 4 : 2;  // steps fetched ahead (even: dY buffer parity is static)
+  constexpr int RING = RB == 1 ? 4 : 8;
+  constexpr int NPAIRS = XL / 8;
+  using L = DwLayout<XL, RING>;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  const unsigned short* __restrict__ x = static_cast<const unsigned short*>(a.x);
-  const unsigned short* __restrict__ dy = static_cast<const unsigned short*>(a.dy);
-  const int lane = threadIdx.x;
-  // Workgroups are dispatched to the 8 XCDs round-robin (block i on XCD i % 8).
-  // The four 16-channel groups that share a 128-byte pixel segment of X and dY
-  // are given block ids 8 apart (same XCD, adjacent in dispatch order), so the
-  // lines one group fetches are served from that XCD's L2 to the other three.
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7, jq = bid >> 3;
-  const int work = (jq >> 2) * 8 + xcd;          // (slice, channel quad) pair
-  if (work >= a.ks_count * a.quads) return;
-  const int slice = work % a.ks_count;
-  const int group = (work / a.ks_count) * 4 + (jq & 3);
-  if (group * kChW >= a.C) return;
-  const int c0 = group * kChW;
+  const unsigned char* __restrict__ xg = static_cast<const unsigned char*>(a.x);
+  const unsigned char* __restrict__ dyg = static_cast<const unsigned char*>(a.dy);
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  // Consecutive blocks take the channel quads of one slice: the workgroups
+  // that read the same pixel rows run together.
+  const int quad = blockIdx.x % a.quads;
+  const int slice = blockIdx.x / a.quads;
+  const int c0 = quad * kQuadCh;
   const int r_begin = slice * a.rows_per_slice;
   const int r_end = min(a.rows, r_begin + a.rows_per_slice);
 
-  unsigned char* xring = lds;
-  unsigned char* dyrow = lds + kRing * a.x_slot;              // copy 0; copy 1 follows
-  const int dy_copy = kChW * a.dl * 2;                         // bytes per copy
-  for (int i = lane * 16; i < a.lds_bytes; i += 64 * 16)
+  // Zero both dY buffers once: their columns outside the dY row are never written.
+  for (int i = L::kDyBase + tid * 16; i < L::kBytes; i += kThreads * 16)
     *reinterpret_cast<uint4*>(lds + i) = uint4{0u, 0u, 0u, 0u};
 
-  // Loader role: pixel group pg (pixels 4pg..4pg+3), channel half hh (8 channels).
-  const int pg = lane >> 1, hh = lane & 1;
-  const bool x_act = 4 * pg < a.xl;
-  const bool dy_act = 4 * pg < a.Wo + 4;
-  const unsigned short* xb = x + c0 + 8 * hh;
-  const unsigned short* dyb = dy + c0 + 8 * hh;
-
-  auto x_slot_of = [&](int h) { return ((h % kRing) + kRing) % kRing; };
-  auto fetch_x = [&](int n, int h, Item& it) {
-    const bool ok = x_act && h >= 0 && h < a.H;
-    fetch(xb, (int64_t)n * a.x_img + (int64_t)h * a.W * a.C, a.W, a.C, pg, ok, it);
-  };
-  auto fetch_dy = [&](int n, int ho, Item& it) {
-    fetch(dyb, (int64_t)n * a.dy_img + (int64_t)ho * a.Wo * a.C, a.Wo, a.C, pg, dy_act, it);
-  };
-  auto store_x = [&](int slot, const Item& it) {
-    if (!x_act) return;
-    unsigned char* base = xring + slot * a.x_slot + (8 * hh) * a.xl * 2 + 8 * pg;
+  // Loader role: pixel pair pp (+ 32 per pass), channel octet o of the quad.
+  const int o = tid & 7, pp = tid >> 3;
+  const int row_bytes_x = (a.W * a.C - c0) * 2;     // valid bytes from the quad's first channel
+  const int row_bytes_dy = (a.Wo * a.C - c0) * 2;
+  const int pix_bytes = a.C * 2;
+  int vo[NP];
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc) {
-      uint32_t lo, hi;
-      channel_pair(it, cc, lo, hi);
-      *reinterpret_cast<uint2*>(base + cc * a.xl * 2) = uint2{lo, hi};
+  for (int p = 0; p < NP; ++p) vo[p] = 2 * (pp + 32 * p) * pix_bytes + 16 * o;
+  auto fetch = [&](__amdgpu_buffer_rsrc_t rs, Item<NP>& it) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      it.p[p][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, vo[p], 0, 0));
+      it.p[p][1] = __builtin_bit_cast(u32x4,
+                                      __builtin_amdgcn_raw_buffer_load_b128(rs, vo[p] + pix_bytes, 0, 0));
     }
   };
-  auto store_dy = [&](const Item& it) {
-    if (!dy_act) return;
-    // copy 0: element e at column e + kOff; copy 1: element e at column e + kOff + 1.
-    unsigned char* b0 = dyrow + (8 * hh) * a.dl * 2 + (4 * pg + kOff) * 2;
-    unsigned char* b1 = b0 + dy_copy + 2;
+  // Channel cc of the octet for pixels (2pp, 2pp + 1) as one dword.
+  auto chan = [](const u32x4& p0, const u32x4& p1, int cc) {
+    return __builtin_amdgcn_perm(p1[cc >> 1], p0[cc >> 1], (cc & 1) ? 0x07060302u : 0x05040100u);
+  };
+  // Quad channel ch = 8o + cc belongs to wave ch & 3 (= cc & 3), block ch >> 2.
+  unsigned char* const xw = lds + 2 * o * L::kCs + 4 * pp;
+  unsigned char* const dw0 = lds + L::kDyBase + 2 * o * L::kDs + 2 * a.dy_off + 4 * pp;
+  auto store_x = [&](int slot, const Item<NP>& it) {
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc) {
-      uint32_t lo, hi;
-      channel_pair(it, cc, lo, hi);
-      *reinterpret_cast<uint2*>(b0 + cc * a.dl * 2) = uint2{lo, hi};
-      unsigned char* p1 = b1 + cc * a.dl * 2;
-      *reinterpret_cast<unsigned short*>(p1) = (unsigned short)(lo & 0xffffu);
-      *reinterpret_cast<uint32_t*>(p1 + 2) = __builtin_amdgcn_perm(hi, lo, 0x05040302u);
-      *reinterpret_cast<unsigned short*>(p1 + 6) = (unsigned short)(hi >> 16);
+    for (int p = 0; p < NP; ++p) {
+      if (2 * (pp + 32 * p) < XL) {
+        unsigned char* d = xw + slot * L::kSlot + 128 * p;
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc)
+          *reinterpret_cast<uint32_t*>(d + (cc & 3) * L::kXWave + (cc >> 2) * L::kCs) =
+              chan(it.p[p][0], it.p[p][1], cc);
+      }
+    }
+  };
+  auto store_dy = [&](int buf, const Item<NP>& it) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      if (2 * (pp + 32 * p) < a.Wo) {
+        unsigned char* d = dw0 + buf * L::kDBuf + 128 * p;
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc)
+          *reinterpret_cast<uint32_t*>(d + (cc & 3) * L::kDWave + (cc >> 2) * L::kDs) =
+              chan(it.p[p][0], it.p[p][1], cc);
+      }
     }
   };
 
-  // MFMA operand addressing.  Lane = 4*b + q: block b = channel c0 + b.
+  // MFMA operand addressing.  Lane = 4*b + q: block b = channel c0 + wave + 4b.
   const int b = lane >> 2, q = lane & 3;
-  const int a_lane = b * a.xl * 2;                 // + slot * x_slot + 2*w0
-  // The B window of s-block 0 starts at dY element w0 + pad - q, stored at
-  // column w0 + col0 of copy 0 (col0 = kOff + pad - q) or one column later in
-  // copy 1; the lane takes the copy in which that column is even, so its two
-  // dword reads are aligned.
-  const int col0 = kOff + a.pad - q;
-  const int b_lane = b * a.dl * 2 + ((col0 & 1) ? dy_copy + 2 * (col0 + 1) : 2 * col0);
+  // The s-block-0 window of lane q at column step w0 starts at dY element
+  // w0 + pad - q, staged at column w0 + d with d = dy_off + pad - q >= 4: it is
+  // elements u..u+3 (u = d mod 4) of the aligned blocks at columns w0 + 4m and
+  // w0 + 4m + 4 (m = d / 4).
+  const int d0 = a.dy_off + a.pad - q;
+  const bool bhi = (d0 & 2) != 0;                                 // u >= 2: start in the second dword
+  const uint32_t bsel = (d0 & 1) ? 0x05040302u : 0x03020100u;     // u odd: shift by one element
+  lds_cu8* const bq = (lds_cu8*)lds + L::kDyBase + wave * L::kDWave + b * L::kDs + 2 * (d0 & ~3);
+  // Separate base registers keep the two block reads of a pair from being
+  // merged into one ds_read2_b64, which is slower than two ds_read_b64.
+  lds_cu8* bq4 = bq + 8;
+  asm volatile("" : "+v"(bq4));
+  auto window = [&](u32x2 q0, u32x2 q1) {
+    const uint32_t lo = bhi ? q0.y : q0.x;
+    const uint32_t mid = bhi ? q1.x : q0.y;
+    const uint32_t hi = bhi ? q1.y : q1.x;
+    const u32x2 v{__builtin_amdgcn_perm(mid, lo, bsel), __builtin_amdgcn_perm(hi, mid, bsel)};
+    return __builtin_bit_cast(s16x4, v);
+  };
+  const unsigned char* const xr = lds + wave * L::kXWave + b * L::kCs;
 
   f32x4 acc[RB][SB];
 #pragma unroll
@@ -173,87 +207,109 @@ __global__ __launch_bounds__(64) void depthwise_mfma_kernel(DwArgs a) {
 #pragma unroll
     for (int j = 0; j < SB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute_row = [&](int ho) {
-    int slot_a[RB];
+  // One row: NPAIRS pairs of column steps, fully unrolled.
+  auto compute_row = [&](int ho, int buf) {
+    const unsigned char* ap[RB];
 #pragma unroll
-    for (int i = 0; i < RB; ++i) slot_a[i] = x_slot_of(ho - a.pad + 4 * i + q) * a.x_slot + a_lane;
-    const unsigned char* bp = dyrow + b_lane;
-    s16x4 bprev = {0, 0, 0, 0};
-    if (SB > 1) {  // window of column step -4: dY columns -4 - q + pad (zero padding)
-      const uint32_t* p = reinterpret_cast<const uint32_t*>(bp - 8);
-      bprev = __builtin_bit_cast(s16x4, uint2{p[0], p[1]});
-    }
-    // Operands of column step w0 + 4 are read while the MFMAs of step w0 run.
-    auto read_a = [&](int w0, s16x4 (&fa)[RB]) {
+    for (int i = 0; i < RB; ++i) ap[i] = xr + ((ho - a.pad + 4 * i + q) & (RING - 1)) * L::kSlot;
+    lds_cu8* bp = bq + buf * L::kDBuf;
+    lds_cu8* bp4 = bq4 + buf * L::kDBuf;
+    auto blk = [](lds_cu8* ptr) { return *reinterpret_cast<__attribute__((address_space(3))) const u32x2*>(ptr); };
+    u32x2 qprev = blk(bp - 8);    // block of step -4
+    u32x2 qcur = blk(bp);         // block of step 0
+    s16x4 b1 = window(qprev, qcur);                           // s-block 1 of step 0
+    // Operands of pair pr + 1 are read before the MFMAs of pair pr; the empty
+    // asm between pairs also keeps the block reads of different pairs from
+    // being merged into ds_read2_b64.
+    u32x4 fa[NPAIRS][RB];
+    u32x2 q1[NPAIRS], q2[NPAIRS];
+    auto load_pair = [&](int pr) {
 #pragma unroll
-      for (int i = 0; i < RB; ++i)
-        fa[i] = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2*>(xring + slot_a[i] + 2 * w0));
+      for (int i = 0; i < RB; ++i) fa[pr][i] = *reinterpret_cast<const u32x4*>(ap[i] + 16 * pr);
+      q1[pr] = blk(bp4 + 16 * pr);        // block of step 8pr + 4
+      q2[pr] = blk(bp + 16 * pr + 16);    // block of step 8pr + 8
     };
-    auto read_b = [&](int w0) {
-      const uint32_t* p = reinterpret_cast<const uint32_t*>(bp + 2 * w0);
-      return __builtin_bit_cast(s16x4, uint2{p[0], p[1]});
-    };
-    auto mfma_step = [&](const s16x4 (&fa)[RB], const s16x4& fb) {
+    load_pair(0);
+#pragma unroll
+    for (int pr = 0; pr < NPAIRS; ++pr) {
+      if (pr + 1 < NPAIRS) load_pair(pr + 1);
+      asm volatile("" ::: "memory");
+      s16x4 b0 = window(qcur, q1[pr]);
 #pragma unroll
       for (int i = 0; i < RB; ++i) {
-        acc[i][0] = mfma4<kBf16>(fa[i], fb, acc[i][0]);
-        if (SB > 1) acc[i][1] = mfma4<kBf16>(fa[i], bprev, acc[i][1]);
+        const s16x4 av = __builtin_bit_cast(s16x4, u32x2{fa[pr][i].x, fa[pr][i].y});
+        acc[i][0] = mfma4<kBf16>(av, b0, acc[i][0]);
+        if (SB > 1) acc[i][1] = mfma4<kBf16>(av, b1, acc[i][1]);
       }
-      bprev = fb;
-    };
-    // Two named operand sets, so the reads of one step stay in flight while
-    // the other step's MFMAs issue.  xl is a multiple of 8.
-    s16x4 fa0[RB], fa1[RB], fb0, fb1;
-    read_a(0, fa0);
-    fb0 = read_b(0);
-    for (int w0 = 0; w0 < a.xl; w0 += 8) {
-      read_a(w0 + 4, fa1);
-      fb1 = read_b(w0 + 4);
-      mfma_step(fa0, fb0);
-      const int wn = w0 + 8 < a.xl ? w0 + 8 : w0;
-      read_a(wn, fa0);
-      fb0 = read_b(wn);
-      mfma_step(fa1, fb1);
+      b1 = b0;
+      b0 = window(q1[pr], q2[pr]);
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        const s16x4 av = __builtin_bit_cast(s16x4, u32x2{fa[pr][i].z, fa[pr][i].w});
+        acc[i][0] = mfma4<kBf16>(av, b0, acc[i][0]);
+        if (SB > 1) acc[i][1] = mfma4<kBf16>(av, b1, acc[i][1]);
+      }
+      b1 = b0;
+      qcur = q2[pr];
     }
   };
 
+  lds_barrier();
+
   // Stream the slice one image segment at a time.  Step t of a segment that
-  // starts at output row ho0 brings X row ho0 - pad + t into the ring and, from
-  // step R - 1 on, dY row ho = ho0 + t - (R - 1), after which the ring holds X
-  // rows ho - pad .. ho - pad + R - 1 and row ho is computed.  Loads run kPf
-  // steps ahead of their use.
-  Item qx[kPf], qd[kPf];
+  // starts at output row ho0 brings X row ho0 - pad + t into the ring and dY
+  // row ho = ho0 + t - (R - 1) into dY buffer t & 1; from step R - 1 on, the
+  // ring then holds X rows ho - pad .. ho - pad + R - 1 and row ho is
+  // computed.  Ring rows past R - 1 that the 4 * RB operand rows include feed
+  // only accumulator rows r >= R, which are never stored.  A step's staging
+  // overwrites the ring slot and the dY buffer that step t - 1 did not use,
+  // except for R = 8, where a second barrier guards the ring.  Every step
+  // issues the same loads (rows outside the image or the segment have an
+  // empty range and read 0), so the load counters are static.
+  const bool guard_ring = a.R + 1 > RING;
+  Item<NP> qx[kPf], qd[kPf];
   int row = r_begin;
   while (row < r_end) {
     const int n = row / a.Ho, ho0 = row % a.Ho;
     const int seg = min(r_end - row, a.Ho - ho0);
     const int steps = seg + a.R - 1;
-    auto fetch_step = [&](int t, Item& ix, Item& id) {
-      fetch_x(n, ho0 - a.pad + t, ix);
-      if (t >= a.R - 1) fetch_dy(n, ho0 + t - (a.R - 1), id);
+    const int last = ho0 + seg;                    // first output row past the segment
+    auto fetch_step = [&](int t, Item<NP>& ix, Item<NP>& id) {
+      const int h = ho0 - a.pad + t;
+      const bool x_in = h >= 0 && h < a.H && t < steps;
+      const int64_t ex = (int64_t)n * a.x_img + (int64_t)(x_in ? h : 0) * a.W * a.C + c0;
+      fetch(row_rsrc(xg + 2 * ex, x_in ? row_bytes_x : 0), ix);
+      const int ho = ho0 + t - (a.R - 1);
+      const bool d_in = ho >= ho0 && ho < last;
+      const int64_t ed = (int64_t)n * a.dy_img + (int64_t)(d_in ? ho : ho0) * a.Wo * a.C + c0;
+      fetch(row_rsrc(dyg + 2 * ed, d_in ? row_bytes_dy : 0), id);
     };
 #pragma unroll
-    for (int k = 0; k < kPf; ++k)
-      if (k < steps) fetch_step(k, qx[k], qd[k]);
+    for (int k = 0; k < kPf; ++k) fetch_step(k, qx[k], qd[k]);
     for (int t = 0; t < steps; t += kPf) {
 #pragma unroll
       for (int k = 0; k < kPf; ++k) {
         const int tk = t + k;
-        if (tk < steps) {
-          store_x(x_slot_of(ho0 - a.pad + tk), qx[k]);
-          const bool has_dy = tk >= a.R - 1;
-          if (has_dy) store_dy(qd[k]);
-          if (tk + kPf < steps) fetch_step(tk + kPf, qx[k], qd[k]);
-          if (has_dy) compute_row(ho0 + tk - (a.R - 1));
+        store_x((ho0 - a.pad + tk) & (RING - 1), qx[k]);
+        store_dy(k & 1, qd[k]);
+        fetch_step(tk + kPf, qx[k], qd[k]);
+        lds_barrier();
+        if (tk >= a.R - 1 && tk < steps) {
+          compute_row(ho0 + tk - (a.R - 1), k & 1);
+          if (guard_ring) lds_barrier();
         }
       }
     }
+    // The next segment restarts at step 0 (buffer 0, ring slot of its first
+    // row); all waves finish this segment's last row before it is overwritten.
+    lds_barrier();
     row += seg;
   }
 
-  // acc[rb][sb][v] = dW[c0 + b][4*rb + v][4*sb + q]
-  float* out = a.out + (int64_t)slice * a.slab_stride + (int64_t)(c0 + b) * a.R * a.S;
-  if (c0 + b < a.C) {
+  // acc[rb][sb][v] = dW[c0 + wave + 4b][4*rb + v][4*sb + q]
+  const int c = c0 + wave + 4 * b;
+  if (c < a.C) {
+    float* out = a.out + (int64_t)slice * a.slab_stride + (int64_t)c * a.R * a.S;
 #pragma unroll
     for (int i = 0; i < RB; ++i)
 #pragma unroll
@@ -266,28 +322,58 @@ __global__ __launch_bounds__(64) void depthwise_mfma_kernel(DwArgs a) {
   }
 }
 
-template <bool kBf16, int RB, int SB>
-hipError_t launch_rs(const DwArgs& args, int64_t grid, hipStream_t stream) {
-  const void* fn = reinterpret_cast<const void*>(depthwise_mfma_kernel<kBf16, RB, SB>);
-  if (args.lds_bytes > 64 * 1024) {
-    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, args.lds_bytes);
+template <bool kBf16, int RB, int SB, int XL>
+hipError_t launch_xl(const DwArgs& args, int64_t grid, hipStream_t stream) {
+  using L = DwLayout<XL, RB == 1 ? 4 : 8>;
+  const void* fn = reinterpret_cast<const void*>(depthwise_mfma_kernel<kBf16, RB, SB, XL>);
+  if (L::kBytes > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, L::kBytes);
     if (e != hipSuccess) return e;
   }
   void* params[] = {const_cast<DwArgs*>(&args)};
-  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(64), params, (size_t)args.lds_bytes, stream);
+  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), params, (size_t)L::kBytes, stream);
+}
+
+template <bool kBf16, int RB, int SB>
+hipError_t launch_rs(int xl, const DwArgs& a, int64_t grid, hipStream_t stream) {
+  switch (xl) {
+    case 8: return launch_xl<kBf16, RB, SB, 8>(a, grid, stream);
+    case 24: return launch_xl<kBf16, RB, SB, 24>(a, grid, stream);
+    case 40: return launch_xl<kBf16, RB, SB, 40>(a, grid, stream);
+    case 56: return launch_xl<kBf16, RB, SB, 56>(a, grid, stream);
+    case 72: return launch_xl<kBf16, RB, SB, 72>(a, grid, stream);
+    case 88: return launch_xl<kBf16, RB, SB, 88>(a, grid, stream);
+    case 104: return launch_xl<kBf16, RB, SB, 104>(a, grid, stream);
+    case 120: return launch_xl<kBf16, RB, SB, 120>(a, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <bool kBf16>
 hipError_t launch_b(const Plan& plan, const DwArgs& a, hipStream_t stream) {
   const int64_t grid = plan.pub.grid;
+  const int xl = plan.dw_xl;
   const bool r2 = a.R > 4, s2 = a.S > 4;
-  if (r2 && s2) return launch_rs<kBf16, 2, 2>(a, grid, stream);
-  if (r2) return launch_rs<kBf16, 2, 1>(a, grid, stream);
-  if (s2) return launch_rs<kBf16, 1, 2>(a, grid, stream);
-  return launch_rs<kBf16, 1, 1>(a, grid, stream);
+  if (r2 && s2) return launch_rs<kBf16, 2, 2>(xl, a, grid, stream);
+  if (r2) return launch_rs<kBf16, 2, 1>(xl, a, grid, stream);
+  if (s2) return launch_rs<kBf16, 1, 2>(xl, a, grid, stream);
+  return launch_rs<kBf16, 1, 1>(xl, a, grid, stream);
 }
 
 }  // namespace
+
+// LDS bytes the depthwise kernel uses for a staged row length (0 if unsupported).
+int32_t depthwise_lds_bytes(int32_t xl, int32_t R) {
+  const bool big = R > 4;
+  switch (xl) {
+#define CW_DW_CASE(V) \
+  case V: return big ? DwLayout<V, 8>::kBytes : DwLayout<V, 4>::kBytes;
+    CW_DW_CASE(8) CW_DW_CASE(24) CW_DW_CASE(40) CW_DW_CASE(56)
+    CW_DW_CASE(72) CW_DW_CASE(88) CW_DW_CASE(104) CW_DW_CASE(120)
+#undef CW_DW_CASE
+    default: return 0;
+  }
+}
 
 hipError_t launch_depthwise(const Plan& plan, const void* x, const void* dy, Stage1Out out,
                             hipStream_t stream) {
@@ -302,14 +388,11 @@ hipError_t launch_depthwise(const Plan& plan, const void* x, const void* dy, Sta
   a.H = (int32_t)p.H; a.W = (int32_t)p.W; a.C = (int32_t)p.C;
   a.Ho = (int32_t)p.Ho; a.Wo = (int32_t)p.Wo;
   a.R = (int32_t)p.R; a.S = (int32_t)p.S; a.pad = (int32_t)p.pad;
-  a.xl = plan.dw_xl;
-  a.dl = plan.dw_dl;
-  a.x_slot = plan.dw_xslot;
+  a.dy_off = plan.dw_off;
   a.rows = (int32_t)(p.N * p.Ho);
   a.rows_per_slice = (int32_t)plan.pub.units_per_slice;
   a.ks_count = plan.pub.ks_count;
   a.quads = (int32_t)ceil_div(p.C, 64);
-  a.lds_bytes = plan.dw_lds;
   if (p.dtype == CONV_WGRAD_BF16) return launch_b<true>(plan, a, stream);
   return launch_b<false>(plan, a, stream);
 }

@@ -33,6 +33,7 @@ int64_t extent(int64_t in, int64_t k, int64_t pad, int64_t stride, int64_t dil) 
 constexpr int64_t kI32Max = 2147483647;
 // Reduction rows stay below 2^31 with room for one rounded-up slice.
 constexpr int64_t kMaxRows = kI32Max - 65536;
+constexpr int64_t kDwLdsMax = 160 * 1024;  // LDS per CU
 // Upper bound on the split degree (the slab fold launches one workgroup row per run).
 constexpr int64_t kMaxSlices = 65536;
 
@@ -192,28 +193,27 @@ bool plan_grouped16(const Problem& p, Plan* out) {
 }
 
 // Depthwise 4x4x4 kernel (depthwise_mfma.hip): 16-bit, one channel per group,
-// stride 1, no dilation, channels in whole 16-channel waves, filter up to
-// 8 x 8, rows of at most 128 columns.  Staged row lengths are odd multiples of
-// 8 elements and the ring slot pitch is 8 mod 256 bytes, which keeps the
-// operand reads of a wave at the minimum two bank passes.
+// stride 1, no dilation, channels in whole 16-channel groups, filter up to
+// 8 x 8, rows of at most 120 columns staged as 8 mod 16 columns, padding up
+// to 12.  A staged dY row holds element 0 at an even column off with
+// 7 <= pad + off <= 12, so every lane's window blocks, from one column step
+// before column 0 to one past the row, lie in the xl + 16 staged columns.
 bool plan_depthwise(const Problem& p, Plan* out) {
   if (p.dtype == CONV_WGRAD_F32 || p.Cg != 1 || p.Kg != 1 || p.stride != 1 || p.dil != 1) return false;
-  if (p.C % 16 != 0 || p.R > 8 || p.S > 8 || p.W > 120 || p.Wo + 4 > 128) return false;
+  if (p.C % 16 != 0 || p.C > (1 << 20) || p.R > 8 || p.S > 8 || p.pad > 12) return false;
+  if (p.W > 120 || p.Wo > 128 || p.W * p.C * 2 > kI32Max) return false;
   int64_t xl = 8;
   while (xl < p.W) xl += 16;
-  int64_t xslot = 32 * xl;
-  xslot += ((8 - xslot) % 256 + 256) % 256;
-  int64_t need = p.Wo + 16;
-  if (need < 8 + p.pad + xl + 2) need = 8 + p.pad + xl + 2;
-  int64_t dl = 8;
-  while (dl < need) dl += 16;
-  const int64_t lds = ceil_div(8 * xslot + 2 * 16 * dl * 2, 16) * 16;
-  if (lds > 64 * 1024) return false;
+  const int64_t np = xl > 64 ? 2 : 1;
+  int64_t off = (8 - p.pad) & ~(int64_t)1;
+  if (off < 0) off = 0;
+  if (p.Wo > 64 * np || 2 * ceil_div(p.Wo, 2) + off > xl + 16) return false;
+  const int32_t lds = depthwise_lds_bytes((int32_t)xl, (int32_t)p.R);
+  if (lds <= 0 || lds > kDwLdsMax) return false;
   out->dw_xl = (int32_t)xl;
-  out->dw_dl = (int32_t)dl;
-  out->dw_xslot = (int32_t)xslot;
-  out->dw_lds = (int32_t)lds;
-  out->c_tiles = p.C / 16;
+  out->dw_lds = lds;
+  out->dw_off = (int32_t)off;
+  out->c_tiles = ceil_div(p.C, 64);
   return true;
 }
 
@@ -243,16 +243,9 @@ conv_wgrad_status_t make_plan(const conv_wgrad_desc_t* desc, Plan* out) {
     pub.unit_rows = p.Wo;  // a unit is one output row
     int64_t units;
     if (!mul_ok(p.N, p.Ho, &units)) return CONV_WGRAD_ERR_UNSUPPORTED;
-    // One-wave workgroups, about eight per CU.
-    st = choose_split(units, out->c_tiles, desc->split_k, 8, 2048, 4, p, &pub);
-    if (st != CONV_WGRAD_OK) return st;
-    // Launch grid of the XCD-aware mapping: 32 blocks per 8 (slice, channel
-    // quad) pairs; blocks past the work return at once.
-    int64_t grid;
-    if (!mul_ok(ceil_div((int64_t)pub.ks_count * ceil_div(p.C, 64), 8), 32, &grid) || grid > kI32Max)
-      return CONV_WGRAD_ERR_UNSUPPORTED;
-    pub.grid = grid;
-    return CONV_WGRAD_OK;
+    // Four-wave workgroups, as many per CU as the LDS holds.
+    const int64_t per_cu = kDwLdsMax / out->dw_lds;
+    return choose_split(units, out->c_tiles, desc->split_k, 8, 256 * per_cu, 4, p, &pub);
   }
   if (small_groups && plan_grouped16(p, out)) {
     pub.path = CONV_WGRAD_PATH_DIRECT;

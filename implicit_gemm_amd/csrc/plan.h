@@ -47,7 +47,8 @@ struct Plan {
   int64_t c_tiles, s_blocks, wchunks;
   int32_t bv;              // 1x1 kernel: input channels per lane
   int32_t ru, xrows;       // grouped16: output rows per unit, staged X rows
-  int32_t dw_xl, dw_dl, dw_xslot, dw_lds;  // depthwise: staged row lengths, ring slot bytes, LDS bytes
+  // Depthwise: staged X row length (elements), LDS bytes, column of dY element 0.
+  int32_t dw_xl, dw_lds, dw_off;
   // Direct path.
   int32_t threads;         // lanes per workgroup
 };
@@ -56,6 +57,10 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Validate and canonicalise desc.  Returns CONV_WGRAD_OK or the error code.
 conv_wgrad_status_t canonicalise(const conv_wgrad_desc_t* desc, Problem* out);
+
+// LDS bytes of the depthwise kernel for staged rows of xl columns and R filter
+// rows (0 if xl is not a supported length); defined with the kernel.
+int32_t depthwise_lds_bytes(int32_t xl, int32_t R);
 
 // Build the full plan (calls canonicalise).
 conv_wgrad_status_t make_plan(const conv_wgrad_desc_t* desc, Plan* out);

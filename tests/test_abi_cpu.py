@@ -130,10 +130,9 @@ def check_plan_invariants(d, p):
         assert ks <= d.split_k
         assert ups == -(-p.units // min(d.split_k, p.units))
     assert p.needs_reduce == (1 if ks > 1 else 0)
-    if p.variant == 12:   # depthwise: XCD-aware grid, 32 blocks per 8 (slice, channel quad) pairs
-        assert p.grid == 32 * -(-(ks * -(-d.C // 64)) // 8) and p.grid >= p.tiles * ks
-    else:
-        assert p.grid == p.tiles * ks
+    if p.variant == 12:   # depthwise: one workgroup per (slice, 64-channel quad)
+        assert p.tiles == -(-d.C // 64)
+    assert p.grid == p.tiles * ks
     assert p.slab_stride % 64 == 0 and p.slab_stride >= p.E
     assert p.ws_bytes == (ks * p.slab_stride * 4 if ks > 1 else 0)
     esz = 4 if d.dtype == iga.F32 else 2

@@ -182,6 +182,12 @@ SMALL_GROUP_CASES = [
     (wd.ConvShape(2, 32, 15, 17, 32, 2, 6, pad=0, groups=32), "bf16", 7),
     (wd.ConvShape(4, 16, 5, 6, 16, 7, 7, pad=3, groups=16), "f16", 1),
     (wd.ConvShape(2, 16, 9, 9, 16, 7, 7, pad=0, groups=16), "bf16", -1),      # Ho = Wo = 3
+    (wd.ConvShape(2, 80, 6, 120, 80, 3, 3, pad=1, groups=80), "bf16", -1),    # two pixel passes, 5 groups
+    (wd.ConvShape(1, 16, 5, 1, 16, 3, 3, pad=1, groups=16), "f16", -1),       # one column
+    (wd.ConvShape(2, 32, 7, 20, 32, 3, 3, pad=4, groups=32), "bf16", 2),      # Ho > H, Wo > W
+    (wd.ConvShape(2, 64, 8, 64, 64, 5, 5, pad=2, groups=64), "bf16", -1),     # even pad, 72-column rows
+    (wd.ConvShape(3, 16, 4, 33, 16, 6, 2, pad=1, groups=16), "f16", 4),       # odd Wo
+    (wd.ConvShape(3, 384, 14, 14, 384, 7, 7, pad=3, groups=384), "bf16", 5),  # slices across images
     # grouped 16-bit: windowed 3x3 / 1x1 paths and the generic path (dilation, 2x2)
     (wd.ConvShape(3, 64, 10, 37, 64, 3, 3, pad=1, groups=16), "f16", -1),
     (wd.ConvShape(2, 128, 9, 9, 128, 1, 1, pad=0, groups=16), "bf16", 3),
