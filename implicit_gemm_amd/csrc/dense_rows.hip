@@ -10,12 +10,17 @@
 //     consecutive taps s, 64 input channels), so its B operand for tap s is
 //     the staged X row segment shifted by s*dil pixels -- an LDS address
 //     offset, not another load;
-//   * the unit's dY rows [wt][64] and X segment [xspan][64] are staged once in
-//     LDS (widened to fp32), double-buffered so the global loads of unit u+1
-//     overlap the MFMA work of unit u, with one barrier per unit;
-//   * wave w owns input channels 16w..16w+15 of the tile and all 64 output
-//     channels: 4*SB independent v_mfma_f32_16x16x4_f32 accumulators, fed by
-//     4 + SB LDS reads per 4 reduction rows.
+//   * a unit's dY rows [wt][64] and X segment [xspan][64] are staged once in
+//     LDS (widened to fp32); within a wave, 4*SB independent
+//     v_mfma_f32_16x16x4_f32 accumulators (all 64 output channels x 16 input
+//     channels) are fed by 4 + SB LDS reads per 4 reduction rows;
+//   * ping-pong: the workgroup has two halves of four waves (one wave of each
+//     per SIMD) that take alternate units of the slice, each with its own LDS
+//     buffer.  Phases separated by workgroup barriers alternate the roles, so
+//     while one half stages its next unit (global loads issued two phases
+//     ahead, fp32 widening, LDS stores) the other half's MFMAs run on the same
+//     SIMDs.  At the end the halves' accumulators are added (half 1 into
+//     half 0, a fixed order) and half 0 writes the slab.
 //
 // Rows of the LDS tiles are 80 floats apart (16 mod 32 and 16 mod 64 banks),
 // so the 4 pixel rows a wave reads per MFMA fall in disjoint bank groups.
@@ -44,14 +49,20 @@ struct RowsArgs {
   int32_t units, units_per_slice, ks_count;
 };
 
-template <typename T, int SB>
-__global__ __launch_bounds__(256, 1) void dense_rows_kernel(RowsArgs a) {
+// kUnit: stride 1 and dilation 1 are compile-time (every LDS offset of the
+// MFMA loop is an immediate); otherwise they are read from the arguments.
+template <typename T, int SB, bool kUnit>
+__global__ __launch_bounds__(512, 1) void dense_rows_kernel(RowsArgs a) {
   extern __shared__ float smem[];
-  constexpr int kBuf = (kMaxWt + kMaxXSpan) * kPitch;  // floats per buffer
+  constexpr int kBuf = (kMaxWt + kMaxXSpan) * kPitch;  // floats per half's buffer
   const T* __restrict__ x = static_cast<const T*>(a.x);
   const T* __restrict__ dy = static_cast<const T*>(a.dy);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // The half index is wave-uniform; readfirstlane lets the compiler keep the
+  // values derived from it (unit indices, buffer resources) in SGPRs.
+  const int tid = threadIdx.x & 255;
+  const int half = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);
+  const int lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
   const int bid = blockIdx.x;
   const int slice = bid % a.ks_count;
@@ -67,20 +78,29 @@ __global__ __launch_bounds__(256, 1) void dense_rows_kernel(RowsArgs a) {
   const int m0 = mt * 64, c0 = ct * 64, s0 = sb * SB;
 
   const int u_begin = slice * a.units_per_slice;
-  const int u_end = min(a.units, u_begin + a.units_per_slice);
+  const int nu = min(a.units, u_begin + a.units_per_slice) - u_begin;   // units in the slice
 
-  // Loader role: pixel rows p0 + 16*i, channel quad q (4 channels).
+  // Loader role within the half: pixel rows p0 + 16*i, channel quad q (4 channels).
+  // Rows are fetched with buffer loads whose range ends at the valid data, so
+  // pixels past the unit, columns outside the image and rows outside it read
+  // zero; lane byte offsets are fixed per lane (plus the unit's first column).
+  constexpr int kEs = sizeof(T);
   const int q = tid & 15, p0 = tid >> 4;
-  const bool a_ok = m0 + 4 * q < a.Kg;   // Kg % 4 == 0: the quad is all in or all out
-  const bool b_ok = c0 + 4 * q < a.Cg;
-  const int64_t dy_col = (int64_t)g * a.Kg + m0 + 4 * q;
-  const int64_t x_col = (int64_t)g * a.Cg + c0 + 4 * q;
+  const int dy_col0 = g * a.Kg + m0;         // first output channel of the tile
+  const int x_col0 = g * a.Cg + c0;          // first input channel of the tile
   const int dh = r * a.dil - a.pad;
   const int xw_off = s0 * a.dil - a.pad;
+  int oa[kMaxWt / 16], ob[kMaxXSpan / 16];
+#pragma unroll
+  for (int i = 0; i < kMaxWt / 16; ++i) oa[i] = ((p0 + 16 * i) * a.K + 4 * q) * kEs;
+#pragma unroll
+  for (int i = 0; i < kMaxXSpan / 16; ++i) ob[i] = ((p0 + 16 * i) * a.C + 4 * q) * kEs;
+  const int x_row_bytes = (a.W * a.C - x_col0) * kEs;
 
+  // Staged operands of one unit, as loaded.
   float ra[kMaxWt / 16][4];
   float rb[kMaxXSpan / 16][4];
-  int npix_next = 0;
+  int npix_reg = 0;
 
   auto load_unit = [&](int u) {
     const int wc = u % a.wchunks;
@@ -88,36 +108,23 @@ __global__ __launch_bounds__(256, 1) void dense_rows_kernel(RowsArgs a) {
     const int ho = t % a.Ho, n = t / a.Ho;
     const int wo0 = wc * a.wt;
     const int npix = min(a.wt, a.Wo - wo0);
-    npix_next = npix;
-    const T* dyp = dy + ((int64_t)(n * a.Ho + ho) * a.Wo + wo0) * a.K + dy_col;
+    npix_reg = npix;
+    const T* dyp = dy + ((int64_t)(n * a.Ho + ho) * a.Wo + wo0) * a.K + dy_col0;
+    const __amdgpu_buffer_rsrc_t rs_a = buf_rsrc(dyp, (npix * a.K - dy_col0) * kEs);
 #pragma unroll
-    for (int i = 0; i < kMaxWt / 16; ++i) {
-      const int p = p0 + 16 * i;
-      if (a_ok && p < npix) {
-        load4(dyp + (int64_t)p * a.K, ra[i]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ra[i][e] = 0.f;
-      }
-    }
+    for (int i = 0; i < kMaxWt / 16; ++i) buf_load4(rs_a, oa[i], dyp, ra[i]);
     const int h = ho * a.stride + dh;
-    const bool row_ok = b_ok && h >= 0 && h < a.H;
+    const bool row_ok = h >= 0 && h < a.H;
     const int w0 = wo0 * a.stride + xw_off;
-    const T* xp = x + (int64_t)n * a.x_img + ((int64_t)h * a.W) * a.C + x_col;
+    const T* xp = x + (int64_t)n * a.x_img + (int64_t)(row_ok ? h : 0) * a.W * a.C + x_col0;
+    const __amdgpu_buffer_rsrc_t rs_b = buf_rsrc(xp, row_ok ? x_row_bytes : 0);
+    const int wb = w0 * a.C * kEs;
 #pragma unroll
-    for (int i = 0; i < kMaxXSpan / 16; ++i) {
-      const int p = p0 + 16 * i;
-      const int w = w0 + p;
-      if (row_ok && p < a.xspan && w >= 0 && w < a.W) {
-        load4(xp + (int64_t)w * a.C, rb[i]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) rb[i][e] = 0.f;
-      }
-    }
+    for (int i = 0; i < kMaxXSpan / 16; ++i) buf_load4(rs_b, ob[i] + wb, xp, rb[i]);
   };
 
-  auto store_unit = [&](float* buf) {
+  float* const buf = smem + half * kBuf;
+  auto store_unit = [&]() {
 #pragma unroll
     for (int i = 0; i < kMaxWt / 16; ++i)
       *reinterpret_cast<float4*>(&buf[(p0 + 16 * i) * kPitch + 4 * q]) =
@@ -135,47 +142,82 @@ __global__ __launch_bounds__(256, 1) void dense_rows_kernel(RowsArgs a) {
 #pragma unroll
     for (int j = 0; j < SB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int a_lane = lg * kPitch + li;                  // + 4*kstep rows, + 16*mt
-  const int b_lane = lg * a.stride * kPitch + 16 * wave + li;
-  const int b_kstep = 4 * a.stride * kPitch;
-  const int b_tap = a.dil * kPitch;
+  const int stride = kUnit ? 1 : a.stride;
+  const float* const A = buf + lg * kPitch + li;                       // + 4*kstep rows, + 16*mt
+  const float* const B = buf + kMaxWt * kPitch + lg * stride * kPitch + 16 * wave + li;
+  const int b_kstep = 4 * stride * kPitch;
+  const int b_tap = (kUnit ? 1 : a.dil) * kPitch;
 
-  load_unit(u_begin);
-  int buf_id = 0;
-  for (int u = u_begin; u < u_end; ++u) {
-    float* buf = smem + buf_id * kBuf;
-    const int npix = npix_next;
-    store_unit(buf);
-    __syncthreads();
-    if (u + 1 < u_end) load_unit(u + 1);
-    const float* A = buf + a_lane;
-    const float* B = buf + kMaxWt * kPitch + b_lane;
+  auto compute_unit = [&](int npix) {
     const int nk = (npix + 3) >> 2;
-    // Fragments of k-step k+1 are read while the MFMAs of k-step k run.
-    float fa[4], fb[SB];
+    // Two operand sets alternate: the fragments of k-step k + 1 are read
+    // before the MFMAs of k-step k issue.  The last read of an even count
+    // repeats a k-step in range and is not used.
+    float pa[4], pb[SB], qa[4], qb[SB];
+    auto read_k = [&](int k, float (&fa)[4], float (&fb)[SB]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = A[16 * i];
+      for (int i = 0; i < 4; ++i) fa[i] = A[4 * k * kPitch + 16 * i];
 #pragma unroll
-    for (int s = 0; s < SB; ++s) fb[s] = B[s * b_tap];
-    for (int k = 0; k < nk; ++k) {
-      const int kn = k + 1 < nk ? k + 1 : k;
-      float na[4], nb[SB];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) na[i] = A[4 * kn * kPitch + 16 * i];
-#pragma unroll
-      for (int s = 0; s < SB; ++s) nb[s] = B[kn * b_kstep + s * b_tap];
+      for (int s = 0; s < SB; ++s) fb[s] = B[k * b_kstep + s * b_tap];
+      // Keep the scheduler from hoisting the following MFMAs above the reads.
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto mfma_k = [&](const float (&fa)[4], const float (&fb)[SB]) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int s = 0; s < SB; ++s)
           acc[i][s] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[i], fb[s], acc[i][s], 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = na[i];
-#pragma unroll
-      for (int s = 0; s < SB; ++s) fb[s] = nb[s];
+    };
+    read_k(0, pa, pb);
+    int k = 0;
+    for (; k + 1 < nk; k += 2) {
+      read_k(k + 1, qa, qb);
+      mfma_k(pa, pb);
+      read_k(k + 2 < nk ? k + 2 : k + 1, pa, pb);
+      mfma_k(qa, qb);
     }
-    buf_id ^= 1;
+    if (k < nk) mfma_k(pa, pb);
+  };
+
+  // Half h takes units h, h + 2, ... of the slice.  In phase p the half with
+  // parity p stages unit p and the other half computes unit p - 1; a
+  // workgroup barrier ends every phase.
+  if (half < nu) load_unit(u_begin + half);
+  int npix_cur = 0;
+  for (int p = 0; p <= nu; ++p) {
+    const bool stage = (p & 1) == half && p < nu;
+    const bool comp = (p & 1) != half && p >= 1;
+    if (stage) {
+      npix_cur = npix_reg;
+      store_unit();
+      if (p + 2 < nu) load_unit(u_begin + p + 2);
+    }
+    // Called on every phase (with no pixels when staging) so that the
+    // accumulators take one path through the loop.
+    compute_unit(comp ? npix_cur : 0);
+    __syncthreads();
   }
+
+  // Half 1 hands its accumulators to half 0 through LDS (both buffers are
+  // free after the last barrier); half 0 adds them and writes the slab.
+  float* xfer = smem + tid;
+  if (half == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int s = 0; s < SB; ++s)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) xfer[((i * SB + s) * 4 + v) * 256] = acc[i][s][v];
+  }
+  __syncthreads();
+  if (half == 1) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int s = 0; s < SB; ++s)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[i][s][v] += xfer[((i * SB + s) * 4 + v) * 256];
 
   float* out = a.out + (int64_t)slice * a.slab_stride;
   const int c = c0 + 16 * wave + li;
@@ -192,27 +234,33 @@ __global__ __launch_bounds__(256, 1) void dense_rows_kernel(RowsArgs a) {
       }
 }
 
-template <typename T, int SB>
+template <typename T, int SB, bool kUnit>
 hipError_t launch_sb(const RowsArgs& args, int64_t grid, hipStream_t stream) {
   constexpr size_t kLds = 2 * (kMaxWt + kMaxXSpan) * kPitch * sizeof(float);
-  const void* fn = reinterpret_cast<const void*>(dense_rows_kernel<T, SB>);
+  const void* fn = reinterpret_cast<const void*>(dense_rows_kernel<T, SB, kUnit>);
   // More than 64 KB of dynamic LDS must be enabled per kernel (once).
   static const hipError_t attr =
       hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
   if (attr != hipSuccess) return attr;
   void* params[] = {const_cast<RowsArgs*>(&args)};
-  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), params, kLds, stream);
+  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(512), params, kLds, stream);
+}
+
+template <typename T, bool kUnit>
+hipError_t launch_u(const Plan& plan, const RowsArgs& args, hipStream_t stream) {
+  const int64_t grid = plan.pub.grid;
+  switch (plan.sb) {
+    case 1: return launch_sb<T, 1, kUnit>(args, grid, stream);
+    case 2: return launch_sb<T, 2, kUnit>(args, grid, stream);
+    case 3: return launch_sb<T, 3, kUnit>(args, grid, stream);
+    default: return launch_sb<T, 4, kUnit>(args, grid, stream);
+  }
 }
 
 template <typename T>
 hipError_t launch_t(const Plan& plan, const RowsArgs& args, hipStream_t stream) {
-  const int64_t grid = plan.pub.grid;
-  switch (plan.sb) {
-    case 1: return launch_sb<T, 1>(args, grid, stream);
-    case 2: return launch_sb<T, 2>(args, grid, stream);
-    case 3: return launch_sb<T, 3>(args, grid, stream);
-    default: return launch_sb<T, 4>(args, grid, stream);
-  }
+  if (args.stride == 1 && args.dil == 1) return launch_u<T, true>(plan, args, stream);
+  return launch_u<T, false>(plan, args, stream);
 }
 
 }  // namespace

@@ -35,4 +35,31 @@ __device__ __forceinline__ void load4(const F16* p, float out[4]) {
   out[0] = (float)v[0]; out[1] = (float)v[1]; out[2] = (float)v[2]; out[3] = (float)v[3];
 }
 
+// Raw buffer resource over nbytes from base (gfx9: stride 0, default data
+// format).  Loads at offsets >= nbytes, or negative offsets (read as large
+// unsigned values, so nbytes must stay below 2^31), return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, 0x00020000);
+}
+
+// Buffer load of 4 consecutive elements at byte offset off, widened to fp32.
+__device__ __forceinline__ void buf_load4(__amdgpu_buffer_rsrc_t r, int off, const float*, float out[4]) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  const f4 v = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
+}
+__device__ __forceinline__ void buf_load4(__amdgpu_buffer_rsrc_t r, int off, const Bf16*, float out[4]) {
+  typedef unsigned u2 __attribute__((ext_vector_type(2)));
+  const u2 v = __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+  out[0] = __uint_as_float(v[0] << 16);
+  out[1] = __uint_as_float(v[0] & 0xffff0000u);
+  out[2] = __uint_as_float(v[1] << 16);
+  out[3] = __uint_as_float(v[1] & 0xffff0000u);
+}
+__device__ __forceinline__ void buf_load4(__amdgpu_buffer_rsrc_t r, int off, const F16*, float out[4]) {
+  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+  const h4 v = __builtin_bit_cast(h4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+  out[0] = (float)v[0]; out[1] = (float)v[1]; out[2] = (float)v[2]; out[3] = (float)v[3];
+}
+
 }  // namespace cw

@@ -130,6 +130,8 @@ constexpr int kRowsMaxWt = 64, kRowsMaxXSpan = 80;
 // segment of at most 80 pixels for at least 16 output pixels per unit.
 bool plan_dense_rows(const Problem& p, Plan* out) {
   if (p.Kg % 4 != 0 || p.Cg % 4 != 0) return false;
+  // Buffer loads address one X or dY row with 32-bit byte offsets.
+  if (p.W * p.C * p.esize > kI32Max / 2 || p.Wo * p.K * p.esize > kI32Max / 2) return false;
   const int64_t sb = p.S < 4 ? p.S : 4;
   int64_t wt = 0;
   for (int64_t cand = kRowsMaxWt; cand >= 16; cand -= 16) {
