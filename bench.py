@@ -9,7 +9,10 @@ JSON line:
   value           TFLOP/s of the whole call over K back-to-back steps
   roofline        the stage-1 kernel alone, timed with HIP events recorded on
                   its own stream around each launch in the timed region,
-                  against the MI355X peak of its bound (f32 MFMA or HBM)
+                  against the MI355X peak of its bound (f32 MFMA or HBM);
+                  traffic = HBM bytes per launch from the FETCH_SIZE /
+                  WRITE_SIZE counter table in profiles/hbm_traffic.md when
+                  it was taken on the current kernel source, else null
   cold_cache      per-call event times with a 1 GiB cache flush before each call
   cpu_baseline    the CPU oracle (test infrastructure) timed on the host cores
 
@@ -33,6 +36,42 @@ PEAK = {  # MI355X published peaks
     "mfma_tflops": {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6},
 }
 DEFAULT_CONFIG = "c2_3x3_f32"
+
+# Stage-1 kernel source of each plan variant; with the shared headers and the
+# planner it identifies the code a counter measurement was taken on.
+CSRC = os.path.join(ROOT, "implicit_gemm_amd", "csrc")
+VARIANT_SOURCE = {0: "dense_lds.hip", 1: "dense_rows.hip", 2: "dense_1x1.hip", 10: "direct_elem.hip",
+                  11: "grouped16.hip", 12: "depthwise_mfma.hip"}
+SHARED_SOURCES = ("device_common.h", "kernels.h", "plan.h", "plan.cpp")
+TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+CPU_SAMPLE_FLOPS = 1.0e12   # at most ~20 s of oracle work on 16 host cores
+
+
+def source_digest(variant):
+    """sha256 (16 hex digits) of the stage-1 kernel source, shared headers and planner."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in (VARIANT_SOURCE[int(variant)],) + SHARED_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, digest):
+    """HBM bytes per stage-1 launch from the counter table, if taken on this source."""
+    try:
+        with open(TRAFFIC_TABLE) as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return None
+    for line in lines:
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) >= 9 and cells[0] == workload and cells[2] == digest:
+            try:
+                return int(cells[8].replace(",", ""))
+            except ValueError:
+                return None
+    return None
 
 
 def log(*a):
@@ -69,7 +108,7 @@ class Hip:
         self.lib.hipEventDestroy(ev)
 
 
-def roofline_for(shape, dtype, seconds):
+def roofline_for(shape, dtype, seconds, traffic=None):
     import wgrad_data as wd
     flops = shape.flops()
     nbytes = shape.algorithmic_bytes(wd.IN_BYTES[dtype])
@@ -82,26 +121,32 @@ def roofline_for(shape, dtype, seconds):
         achieved = flops / seconds / 1e12
         return {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK["mfma_tflops"][dtype],
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK["mfma_tflops"][dtype], 4),
-                "traffic": None}
+                "traffic": traffic}
     achieved = nbytes / seconds / 1e9
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm_gbs"], "unit": "GB/s",
-            "frac": round(achieved / PEAK["hbm_gbs"], 4), "traffic": None}
+            "frac": round(achieved / PEAK["hbm_gbs"], 4), "traffic": traffic}
 
 
 def cpu_baseline(wl, x, dy, reps):
+    """The fp64 oracle on the host cores, on the first images of the workload
+    (all of them unless that exceeds CPU_SAMPLE_FLOPS), in TFLOP/s."""
     import oracle
     s = wl.shape
     threads = oracle.default_threads()
+    per_image = s.flops() / s.N
+    n_s = int(max(1, min(s.N, CPU_SAMPLE_FLOPS // per_image)))
+    xs, dys = x[:n_s], dy[:n_s]
     times = []
     for _ in range(reps):
         t0 = time.perf_counter()
-        oracle.wgrad_ref(x, dy, s.R, s.S, s.pad, s.stride, s.dilation, s.groups, nthreads=threads)
+        oracle.wgrad_ref(xs, dys, s.R, s.S, s.pad, s.stride, s.dilation, s.groups, nthreads=threads)
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
-    return {"value": round(s.flops() / t / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
+    what = "whole workload" if n_s == s.N else "first %d of %d images" % (n_s, s.N)
+    return {"value": round(per_image * n_s / t / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
-            "sample": "whole workload (%s), median of %d runs, fp64 C oracle, %.2f s per run"
-                      % (wl.name, reps, t)}
+            "sample": "%s (%s), median of %d runs, fp64 C oracle, %.2f s per run"
+                      % (what, wl.name, reps, t)}
 
 
 def main():
@@ -116,6 +161,8 @@ def main():
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run 3 device-to-device copies of 1 GiB (scale for HBM byte counters)")
+    ap.add_argument("--digest", action="store_true",
+                    help="print the stage-1 source digest of --config and exit (no GPU needed)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the weight-gradient path runs on a single MI355X "
@@ -126,6 +173,15 @@ def main():
     import torch
     import implicit_gemm_amd as iga
     import wgrad_data as wd
+
+    if args.digest:
+        s = wd.WORKLOADS[args.config].shape
+        d = iga.make_desc(s.N, s.C, s.H, s.W, s.K, s.R, s.S, s.pad, s.stride, s.dilation, s.groups,
+                          {"f32": 0, "bf16": 1, "f16": 2}[wd.WORKLOADS[args.config].dtype], args.split_k)
+        v = int(iga.get_plan(d).variant)
+        print(json.dumps({"workload": args.config, "variant": v, "source": VARIANT_SOURCE[v],
+                          "digest": source_digest(v)}))
+        return 0
 
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
@@ -210,7 +266,8 @@ def main():
     ms_per_step = wall / args.steps * 1e3
     value = s.flops() / (wall / args.steps) / 1e12
     stage1_avg_s = statistics.mean(k_ms) * 1e-3
-    roof = roofline_for(s, wl.dtype, stage1_avg_s)
+    roof = roofline_for(s, wl.dtype, stage1_avg_s,
+                        measured_traffic(wl.name, source_digest(plan.variant)))
 
     cpu = None
     if not args.no_cpu:

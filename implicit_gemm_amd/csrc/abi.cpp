@@ -16,7 +16,29 @@
 
 #include "../../include/conv_wgrad.h"
 #include "kernels.h"
+
+#include <hip/hip_ext.h>
 #include "plan.h"
+
+namespace cw {
+
+Stage1Events& stage1_events() {
+  static thread_local Stage1Events ev;
+  return ev;
+}
+
+hipError_t launch_raw(const void* fn, dim3 grid, dim3 block, void** params, size_t shmem,
+                      hipStream_t stream) {
+  Stage1Events& ev = stage1_events();
+  if (ev.begin || ev.end) {
+    const Stage1Events use = ev;
+    ev = Stage1Events{};
+    return hipExtLaunchKernel(fn, grid, block, params, shmem, stream, use.begin, use.end, 0);
+  }
+  return hipLaunchKernel(fn, grid, block, params, shmem, stream);
+}
+
+}  // namespace cw
 
 namespace {
 
@@ -70,8 +92,15 @@ conv_wgrad_status_t run(const conv_wgrad_desc_t* desc, const void* x, const void
     out.slab_stride = 0;
   }
   hipError_t err;
-  if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess)
-    return CONV_WGRAD_ERR_HIP;
+  // The stage-1 launch takes the events (timestamps of its own dispatch); the
+  // guard clears them again whatever happens, so no later launch records them.
+  struct EventsGuard {
+    EventsGuard(void* b, void* e) {
+      cw::stage1_events().begin = static_cast<hipEvent_t>(b);
+      cw::stage1_events().end = static_cast<hipEvent_t>(e);
+    }
+    ~EventsGuard() { cw::stage1_events() = cw::Stage1Events{}; }
+  } guard(ev_begin, ev_end);
   switch (plan.pub.variant) {
     case cw::kDirectElem: err = cw::launch_direct(plan, x, dy, out, s); break;
     case cw::kGrouped16: err = cw::launch_grouped16(plan, x, dy, out, s); break;
@@ -81,8 +110,6 @@ conv_wgrad_status_t run(const conv_wgrad_desc_t* desc, const void* x, const void
     default: err = cw::launch_dense(plan, x, dy, out, s); break;
   }
   if (err != hipSuccess) return CONV_WGRAD_ERR_HIP;
-  if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), s) != hipSuccess)
-    return CONV_WGRAD_ERR_HIP;
   if (plan.pub.needs_reduce) {
     err = cw::launch_slab_reduce(plan, static_cast<float*>(workspace), dw, s);
     if (err != hipSuccess) return CONV_WGRAD_ERR_HIP;

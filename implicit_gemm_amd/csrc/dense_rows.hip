@@ -47,6 +47,7 @@ struct RowsArgs {
   int32_t m_tiles, c_tiles, s_blocks;
   int32_t wt, wchunks, xspan;
   int32_t units, units_per_slice, ks_count;
+  int32_t tiles, work;   // tiles per slice, tiles * ks_count
 };
 
 // kUnit: stride 1 and dilation 1 are compile-time (every LDS offset of the
@@ -64,9 +65,15 @@ __global__ __launch_bounds__(512, 1) void dense_rows_kernel(RowsArgs a) {
   const int half = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);
   const int lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
-  const int bid = blockIdx.x;
-  const int slice = bid % a.ks_count;
-  int tile = bid / a.ks_count;
+  // Work item w = slice * tiles + tile.  Workgroups are dispatched to the 8
+  // XCDs round-robin (block i on XCD i % 8); each XCD takes a contiguous run
+  // of items, so the tiles of one slice, which read the same dY rows and
+  // overlapping X rows, run on one XCD and share its L2.
+  const int per_xcd = (a.work + 7) >> 3;
+  const int w = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if ((int)(blockIdx.x >> 3) >= per_xcd || w >= a.work) return;
+  const int slice = w / a.tiles;
+  int tile = w % a.tiles;
   const int ct = tile % a.c_tiles;
   tile /= a.c_tiles;
   const int sb = tile % a.s_blocks;
@@ -148,36 +155,33 @@ __global__ __launch_bounds__(512, 1) void dense_rows_kernel(RowsArgs a) {
   const int b_kstep = 4 * stride * kPitch;
   const int b_tap = (kUnit ? 1 : a.dil) * kPitch;
 
+  // One unit's MFMAs: up to kMaxWt / 4 k-steps, fully unrolled so that every
+  // LDS offset is an immediate (no VALU work between the MFMAs).  Two operand
+  // sets alternate: the fragments of k-step k + 1 are read before the MFMAs of
+  // k-step k issue.
   auto compute_unit = [&](int npix) {
     const int nk = (npix + 3) >> 2;
-    // Two operand sets alternate: the fragments of k-step k + 1 are read
-    // before the MFMAs of k-step k issue.  The last read of an even count
-    // repeats a k-step in range and is not used.
-    float pa[4], pb[SB], qa[4], qb[SB];
-    auto read_k = [&](int k, float (&fa)[4], float (&fb)[SB]) {
+    float fa[2][4], fb[2][SB];
+    auto read_k = [&](int k, float (&ra_)[4], float (&rb_)[SB]) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = A[4 * k * kPitch + 16 * i];
+      for (int i = 0; i < 4; ++i) ra_[i] = A[4 * k * kPitch + 16 * i];
 #pragma unroll
-      for (int s = 0; s < SB; ++s) fb[s] = B[k * b_kstep + s * b_tap];
+      for (int s = 0; s < SB; ++s) rb_[s] = B[k * b_kstep + s * b_tap];
       // Keep the scheduler from hoisting the following MFMAs above the reads.
       __builtin_amdgcn_sched_barrier(0);
     };
-    auto mfma_k = [&](const float (&fa)[4], const float (&fb)[SB]) {
+    if (nk > 0) read_k(0, fa[0], fb[0]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int k = 0; k < kMaxWt / 4; ++k) {
+      if (k < nk) {
+        if (k + 1 < nk) read_k(k + 1, fa[(k + 1) & 1], fb[(k + 1) & 1]);
 #pragma unroll
-        for (int s = 0; s < SB; ++s)
-          acc[i][s] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[i], fb[s], acc[i][s], 0, 0, 0);
-    };
-    read_k(0, pa, pb);
-    int k = 0;
-    for (; k + 1 < nk; k += 2) {
-      read_k(k + 1, qa, qb);
-      mfma_k(pa, pb);
-      read_k(k + 2 < nk ? k + 2 : k + 1, pa, pb);
-      mfma_k(qa, qb);
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int s = 0; s < SB; ++s)
+            acc[i][s] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[k & 1][i], fb[k & 1][s], acc[i][s], 0, 0, 0);
+      }
     }
-    if (k < nk) mfma_k(pa, pb);
   };
 
   // Half h takes units h, h + 2, ... of the slice.  In phase p the half with
@@ -243,7 +247,8 @@ hipError_t launch_sb(const RowsArgs& args, int64_t grid, hipStream_t stream) {
       hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
   if (attr != hipSuccess) return attr;
   void* params[] = {const_cast<RowsArgs*>(&args)};
-  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(512), params, kLds, stream);
+  const int64_t xcd_grid = (grid + 7) / 8 * 8;   // whole rounds over the 8 XCDs
+  return launch_raw(fn, dim3((unsigned)xcd_grid), dim3(512), params, kLds, stream);
 }
 
 template <typename T, bool kUnit>
@@ -288,6 +293,8 @@ hipError_t launch_dense_rows(const Plan& plan, const void* x, const void* dy, St
   a.units = (int32_t)plan.pub.units;
   a.units_per_slice = (int32_t)plan.pub.units_per_slice;
   a.ks_count = plan.pub.ks_count;
+  a.tiles = (int32_t)plan.pub.tiles;
+  a.work = (int32_t)plan.pub.grid;
   switch (p.dtype) {
     case CONV_WGRAD_F32: return launch_t<float>(plan, a, stream);
     case CONV_WGRAD_BF16: return launch_t<Bf16>(plan, a, stream);

@@ -331,7 +331,7 @@ hipError_t launch_xl(const DwArgs& args, int64_t grid, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   void* params[] = {const_cast<DwArgs*>(&args)};
-  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), params, (size_t)L::kBytes, stream);
+  return launch_raw(fn, dim3((unsigned)grid), dim3(kThreads), params, (size_t)L::kBytes, stream);
 }
 
 template <bool kBf16, int RB, int SB>

@@ -14,12 +14,25 @@ struct Stage1Out {
   int64_t slab_stride;   // floats between slabs (0 when writing dw)
 };
 
+// Events the next stage-1 launch on this thread records its own start and end
+// in (the dispatch's timestamps, not the stream position around it); set by
+// the timed entry point, consumed by launch_raw.
+struct Stage1Events {
+  hipEvent_t begin = nullptr, end = nullptr;
+};
+Stage1Events& stage1_events();
+
+// Launch one kernel; with pending stage-1 events, hipExtLaunchKernel records
+// them at the kernel's start and end.  Returns the status of this launch only.
+hipError_t launch_raw(const void* fn, dim3 grid, dim3 block, void** params, size_t shmem,
+                      hipStream_t stream);
+
 // Launch `kernel(args)`; returns the status of this launch only.
 template <typename Args>
 inline hipError_t launch_kernel(void (*kernel)(Args), dim3 grid, dim3 block, const Args& args,
                                 hipStream_t stream) {
   void* params[] = {const_cast<Args*>(&args)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, params, 0, stream);
+  return launch_raw(reinterpret_cast<const void*>(kernel), grid, block, params, 0, stream);
 }
 
 hipError_t launch_dense(const Plan& plan, const void* x, const void* dy, Stage1Out out,

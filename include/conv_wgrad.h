@@ -161,10 +161,11 @@ conv_wgrad_status_t conv_wgrad_ex(const conv_wgrad_desc_t* desc, const void* x, 
 
 /*
  * Profiling variant of conv_wgrad: identical work on `stream`, and the caller's
- * HIP events (hipEvent_t, created by the caller; either may be NULL) are
- * recorded on `stream` immediately before and immediately after the stage-1
- * kernel, so the caller can time that kernel alone (the slab reduce, when
- * launched, follows the second event).  The events are only recorded, never
+ * HIP events (hipEvent_t, created by the caller; either may be NULL) take the
+ * start and end timestamps of the stage-1 kernel's own dispatch (the stage-1
+ * launch goes through hipExtLaunchKernel with them), so the caller can time
+ * that kernel alone, without the launch gaps around it; the slab reduce, when
+ * launched, is not included.  The events are only recorded, never
  * synchronised or destroyed.
  */
 conv_wgrad_status_t conv_wgrad_timed(const conv_wgrad_desc_t* desc, const void* x, const void* dy,
