@@ -103,7 +103,8 @@ conv_wgrad_status_t run(const conv_wgrad_desc_t* desc, const void* x, const void
   } guard(ev_begin, ev_end);
   switch (plan.pub.variant) {
     case cw::kDirectElem: err = cw::launch_direct(plan, x, dy, out, s); break;
-    case cw::kGrouped16: err = cw::launch_grouped16(plan, x, dy, out, s); break;
+    case cw::kGrouped16:
+    case cw::kGrouped16Rows: err = cw::launch_grouped16(plan, x, dy, out, s); break;
     case cw::kDepthwise: err = cw::launch_depthwise(plan, x, dy, out, s); break;
     case cw::kDenseRows: err = cw::launch_dense_rows(plan, x, dy, out, s); break;
     case cw::kDense1x1: err = cw::launch_dense_1x1(plan, x, dy, out, s); break;

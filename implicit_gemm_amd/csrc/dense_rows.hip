@@ -13,7 +13,8 @@
 //   * a unit's dY rows [wt][64] and X segment [xspan][64] are staged once in
 //     LDS (widened to fp32); within a wave, 4*SB independent
 //     v_mfma_f32_16x16x4_f32 accumulators (all 64 output channels x 16 input
-//     channels) are fed by 4 + SB LDS reads per 4 reduction rows;
+//     channels) are fed per 4 reduction rows by one 16-byte read of 4 dY
+//     channels and SB reads of X;
 //   * ping-pong: the workgroup has two halves of four waves (one wave of each
 //     per SIMD) that take alternate units of the slice, each with its own LDS
 //     buffer.  Phases separated by workgroup barriers alternate the roles, so
@@ -150,7 +151,10 @@ __global__ __launch_bounds__(512, 1) void dense_rows_kernel(RowsArgs a) {
     for (int j = 0; j < SB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int stride = kUnit ? 1 : a.stride;
-  const float* const A = buf + lg * kPitch + li;                       // + 4*kstep rows, + 16*mt
+  // Row li of M-block i is output channel m0 + 4*li + i, so a lane's four A
+  // fragments are the 4 consecutive channels 4*li .. 4*li + 3 of its pixel
+  // row: one 16-byte LDS read per k-step.
+  const float* const A = buf + lg * kPitch + 4 * li;                   // + 4*kstep rows
   const float* const B = buf + kMaxWt * kPitch + lg * stride * kPitch + 16 * wave + li;
   const int b_kstep = 4 * stride * kPitch;
   const int b_tap = (kUnit ? 1 : a.dil) * kPitch;
@@ -163,8 +167,8 @@ __global__ __launch_bounds__(512, 1) void dense_rows_kernel(RowsArgs a) {
     const int nk = (npix + 3) >> 2;
     float fa[2][4], fb[2][SB];
     auto read_k = [&](int k, float (&ra_)[4], float (&rb_)[SB]) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ra_[i] = A[4 * k * kPitch + 16 * i];
+      const float4 av = *reinterpret_cast<const float4*>(A + 4 * k * kPitch);
+      ra_[0] = av.x; ra_[1] = av.y; ra_[2] = av.z; ra_[3] = av.w;
 #pragma unroll
       for (int s = 0; s < SB; ++s) rb_[s] = B[k * b_kstep + s * b_tap];
       // Keep the scheduler from hoisting the following MFMAs above the reads.
@@ -231,7 +235,8 @@ __global__ __launch_bounds__(512, 1) void dense_rows_kernel(RowsArgs a) {
     for (int s = 0; s < SB; ++s)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int m = m0 + 16 * i + 4 * lg + v;
+        // acc[i][s][v] is D row 4*lg + v of M-block i: channel 4*(4*lg + v) + i.
+        const int m = m0 + 16 * lg + 4 * v + i;
         const int sa = s0 + s;
         if (m < a.Kg && c < a.Cg && sa < a.S)
           out[((int64_t)g * a.Kg + m) * a.cols + (r * a.S + sa) * a.Cg + c] = acc[i][s][v];

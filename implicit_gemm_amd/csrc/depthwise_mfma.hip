@@ -93,13 +93,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const unsigned char* 
                                            0x00020000);
 }
 
-// Workgroup barrier that waits for this wave's LDS accesses only (not for
-// its outstanding global loads); the memory clobber keeps the compiler from
-// moving LDS accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 // Pixels 2pp, 2pp + 1 x 8 channels per pass, as loaded (pixel-major).
 template <int NP>
 struct Item {

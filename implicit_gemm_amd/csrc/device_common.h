@@ -62,4 +62,11 @@ __device__ __forceinline__ void buf_load4(__amdgpu_buffer_rsrc_t r, int off, con
   out[0] = (float)v[0]; out[1] = (float)v[1]; out[2] = (float)v[2]; out[3] = (float)v[3];
 }
 
+// Workgroup barrier that waits for this wave's LDS accesses only (not for
+// its outstanding global loads); the memory clobber keeps the compiler from
+// moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 }  // namespace cw

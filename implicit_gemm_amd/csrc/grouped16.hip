@@ -315,6 +315,132 @@ __global__ __launch_bounds__(256, 3) void grouped16_win_kernel(G16Args a) {
   }
 }
 
+// Row-streaming path for stride 1, dilation 1, Wo <= 32 and a compile-time
+// R x S filter.  A workgroup owns 64 channels and a slice of output rows of
+// one image at a time.  Step h brings X row h (34 pixels with the padding
+// columns) and dY row h + pad into LDS (double-buffered, one barrier per
+// step) with 16-byte buffer loads that run kPf steps ahead; the buffer range
+// of a row supplies its zero padding, and rows outside the image or the
+// segment have an empty range.  The A operand of each dY row is read once and
+// kept in registers for the R steps that use it; X row h is read at its S
+// column offsets and multiplied with the A operands of output rows
+// h + pad - r, so every staged element is read from HBM once per slice.
+template <bool kBf16, int R, int S>
+__global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
+  constexpr int kXPixR = kWoT + S - 1;            // staged X pixels per row
+  constexpr int kPf = 8;                          // steps fetched ahead (even)
+  __shared__ __attribute__((aligned(16))) unsigned short s_x[2][kXPixR * kPitchE];
+  __shared__ __attribute__((aligned(16))) unsigned short s_dy[2][kWoT * kPitchE];
+  const unsigned char* __restrict__ xg = static_cast<const unsigned char*>(a.x);
+  const unsigned char* __restrict__ dyg = static_cast<const unsigned char*>(a.dy);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bid = blockIdx.x;
+  // Consecutive blocks take the channel blocks of one slice (they read the
+  // same pixel rows at the same time).
+  const int cb = bid % a.c_blocks;
+  const int slice = bid / a.c_blocks;
+  const int c0 = cb * kCh;
+  const int r_begin = slice * a.units_per_slice;
+  const int r_end = min(a.units, r_begin + a.units_per_slice);   // units are output rows
+
+  // Loader role: pixel slot ps (and ps + 32 for the X halo), 16-byte chunk q.
+  const int q = tid & 7, ps = tid >> 3;
+  const int x_row_bytes = (a.W * a.C - c0) * 2;
+  const int dy_row_bytes = (a.Wo * a.K - c0) * 2;
+  const int ox0 = ((ps - a.pad) * a.C + 8 * q) * 2;               // negative: zero (padding)
+  const int ox1 = ps + 32 < kXPixR ? ((ps + 32 - a.pad) * a.C + 8 * q) * 2 : 0x7fffffff;
+  const int ody = (ps * a.K + 8 * q) * 2;
+  struct Step {
+    uint4 x0, x1, d;
+  };
+  // Step t of a segment: X row ho0 - pad + t and dY row ho0 + t (t < steps).
+  int n = 0, ho0 = 0, ho_hi = 0, steps = 0;
+  auto fetch = [&](int t, Step& st) {
+    const int h = ho0 - a.pad + t;
+    const bool x_in = h >= 0 && h < a.H && t < steps;
+    const __amdgpu_buffer_rsrc_t rx =
+        buf_rsrc(xg + 2 * ((int64_t)n * a.x_img + (int64_t)(x_in ? h : 0) * a.W * a.C + c0),
+                 x_in ? x_row_bytes : 0);
+    st.x0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, ox0, 0, 0));
+    st.x1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, ox1, 0, 0));
+    const int ho = ho0 + t;
+    const bool d_in = ho < ho_hi;
+    const __amdgpu_buffer_rsrc_t rd =
+        buf_rsrc(dyg + 2 * (((int64_t)n * a.Ho + (d_in ? ho : ho0)) * a.Wo * a.K + c0),
+                 d_in ? dy_row_bytes : 0);
+    st.d = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rd, ody, 0, 0));
+  };
+  auto store = [&](int buf, const Step& st) {
+    *reinterpret_cast<uint4*>(&s_x[buf][ps * kPitchE + 8 * q]) = st.x0;
+    if (ps + 32 < kXPixR) *reinterpret_cast<uint4*>(&s_x[buf][(ps + 32) * kPitchE + 8 * q]) = st.x1;
+    *reinterpret_cast<uint4*>(&s_dy[buf][ps * kPitchE + 8 * q]) = st.d;
+  };
+
+  const int j = lane & 15, g = lane >> 4;
+  const int lane_off = (8 * g + (j >> 2)) * kPitchE + 16 * wave + 4 * (j & 3);
+  auto tr8 = [&](const unsigned short* p) {
+    return __builtin_shufflevector(tr_read(p), tr_read(p + 4 * kPitchE), 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+
+  f32x4 acc[R * S];
+#pragma unroll
+  for (int t = 0; t < R * S; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  Step pf[kPf];
+  int row = r_begin;
+  while (row < r_end) {
+    n = row / a.Ho;
+    ho0 = row % a.Ho;
+    const int seg = min(r_end - row, a.Ho - ho0);
+    ho_hi = ho0 + seg;
+    steps = seg + R - 1;
+    // A operands of dY rows ho0 + t - r, r = 0..R-1 (zero before the segment).
+    s16x8 fa[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) fa[r] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < kPf; ++k) fetch(k, pf[k]);
+    for (int t = 0; t < steps; t += kPf) {
+#pragma unroll
+      for (int k = 0; k < kPf; ++k) {
+        const int tk = t + k;
+        store(k & 1, pf[k]);
+        fetch(tk + kPf, pf[k]);
+        lds_barrier();
+        if (tk < steps) {
+#pragma unroll
+          for (int r = R - 1; r > 0; --r) fa[r] = fa[r - 1];
+          fa[0] = tr8(&s_dy[k & 1][lane_off]);
+          s16x8 fb[S];
+#pragma unroll
+          for (int s2 = 0; s2 < S; ++s2) fb[s2] = tr8(&s_x[k & 1][s2 * kPitchE + lane_off]);
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int s2 = 0; s2 < S; ++s2)
+              acc[r * S + s2] = mfma16<kBf16>(fa[r], fb[s2], acc[r * S + s2]);
+        }
+      }
+    }
+    // The next segment restarts at buffer 0; all waves finish this one first.
+    lds_barrier();
+    row += seg;
+  }
+
+  float* out = a.out + (int64_t)slice * a.slab_stride;
+  const int c = c0 + 16 * wave + j;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int k = c0 + 16 * wave + 4 * g + v;
+    if (k < a.K && c < a.C && k / a.Kg == c / a.Cg) {
+      float* o = out + (int64_t)k * (R * S) * a.Cg + (c % a.Cg);
+#pragma unroll
+      for (int t = 0; t < R * S; ++t) o[t * a.Cg] = acc[t][v];
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_grouped16(const Plan& plan, const void* x, const void* dy, Stage1Out out,
@@ -331,7 +457,7 @@ hipError_t launch_grouped16(const Plan& plan, const void* x, const void* dy, Sta
   a.pad = (int32_t)p.pad; a.dil = (int32_t)p.dil;
   a.Cg = (int32_t)p.Cg; a.Kg = (int32_t)p.Kg; a.taps = (int32_t)(p.R * p.S);
   a.ru = plan.ru;
-  a.hblocks = (int32_t)ceil_div(p.Ho, plan.ru);
+  a.hblocks = plan.ru > 0 ? (int32_t)ceil_div(p.Ho, plan.ru) : 0;   // unit-row kernels only
   a.wchunks = (int32_t)ceil_div(p.Wo, kWoT);
   a.xrows = plan.xrows;
   a.xpix = plan.xspan;
@@ -341,6 +467,13 @@ hipError_t launch_grouped16(const Plan& plan, const void* x, const void* dy, Sta
   a.ks_count = plan.pub.ks_count;
   const dim3 grid((unsigned)plan.pub.grid), block(256);
   const bool bf = p.dtype == CONV_WGRAD_BF16;
+  if (plan.pub.variant == kGrouped16Rows) {
+    if (p.R == 3)
+      return bf ? launch_kernel(grouped16_rows_kernel<true, 3, 3>, grid, block, a, stream)
+                : launch_kernel(grouped16_rows_kernel<false, 3, 3>, grid, block, a, stream);
+    return bf ? launch_kernel(grouped16_rows_kernel<true, 1, 1>, grid, block, a, stream)
+              : launch_kernel(grouped16_rows_kernel<false, 1, 1>, grid, block, a, stream);
+  }
   if (plan.ru == 4 && p.dil == 1 && p.R == 3 && p.S == 3)
     return bf ? launch_kernel(grouped16_win_kernel<true, 3, 3>, grid, block, a, stream)
               : launch_kernel(grouped16_win_kernel<false, 3, 3>, grid, block, a, stream);

@@ -194,6 +194,19 @@ bool plan_grouped16(const Problem& p, Plan* out) {
   return true;
 }
 
+// Row-streaming grouped kernel (grouped16.hip): as the block-diagonal kernel,
+// plus stride 1, no dilation, a 1x1 or 3x3 filter and output rows of at most
+// 32 pixels (one MFMA k-step); padding below the filter size.
+bool plan_grouped16_rows(const Problem& p, Plan* out) {
+  if (p.dtype == CONV_WGRAD_F32 || p.stride != 1 || p.dil != 1 || p.Cg != p.Kg || 16 % p.Cg != 0)
+    return false;
+  if (p.C % 16 != 0 || p.Wo > 32 || p.pad >= p.S || p.pad >= p.R) return false;
+  if (!((p.R == 3 && p.S == 3) || (p.R == 1 && p.S == 1))) return false;
+  if (p.W * p.C * 2 > kI32Max / 2 || p.Wo * p.K * 2 > kI32Max / 2) return false;
+  out->c_tiles = ceil_div(p.C, 64);
+  return true;
+}
+
 // Depthwise 4x4x4 kernel (depthwise_mfma.hip): 16-bit, one channel per group,
 // stride 1, no dilation, channels in whole 16-channel groups, filter up to
 // 8 x 8, rows of at most 120 columns staged as 8 mod 16 columns, padding up
@@ -248,6 +261,16 @@ conv_wgrad_status_t make_plan(const conv_wgrad_desc_t* desc, Plan* out) {
     // Four-wave workgroups, as many per CU as the LDS holds.
     const int64_t per_cu = kDwLdsMax / out->dw_lds;
     return choose_split(units, out->c_tiles, desc->split_k, 8, 256 * per_cu, 4, p, &pub);
+  }
+  if (small_groups && plan_grouped16_rows(p, out)) {
+    pub.path = CONV_WGRAD_PATH_DIRECT;
+    pub.variant = kGrouped16Rows;
+    pub.unit_rows = p.Wo;  // a unit is one output row
+    int64_t units;
+    if (!mul_ok(p.N, p.Ho, &units)) return CONV_WGRAD_ERR_UNSUPPORTED;
+    // Four-wave workgroups, about two per CU; slices of at least 8 rows keep
+    // the re-read X halo rows small.
+    return choose_split(units, out->c_tiles, desc->split_k, 8, 512, 4, p, &pub);
   }
   if (small_groups && plan_grouped16(p, out)) {
     pub.path = CONV_WGRAD_PATH_DIRECT;

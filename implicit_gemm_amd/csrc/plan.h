@@ -20,7 +20,8 @@ enum Variant : int32_t {
   kDense1x1 = 2,      // 1x1 stride-1 unpadded fp32: rows streamed into MFMA registers
   kDirectElem = 10,   // direct small-group kernel, one dW element per lane
   kGrouped16 = 11,    // 16-bit small groups: block-diagonal 16x16x32 MFMA, transposed LDS reads
-  kDepthwise = 12,    // 16-bit depthwise: batched 4x4x4 MFMA, one wave per 16 channels
+  kDepthwise = 12,    // 16-bit depthwise: batched 4x4x4 MFMA, 64 channels per workgroup
+  kGrouped16Rows = 13,  // 16-bit small groups, 1x1 / 3x3, Wo <= 32: row-streaming 16x16x32 MFMA
 };
 
 struct Problem {

@@ -115,7 +115,7 @@ def check_plan_invariants(d, p):
     assert p.E == d.K * d.R * d.S * (d.C // d.groups)
     if p.path == iga.PATH_DENSE and p.variant == 1:   # row units: (n, ho, chunk of Wo)
         assert p.units == d.N * Ho * -(-Wo // p.unit_rows)
-    elif p.variant == 12:                             # depthwise: one output row per unit
+    elif p.variant in (12, 13):                       # depthwise, row-streaming grouped: one output row per unit
         assert p.units == d.N * Ho and p.unit_rows == Wo
     elif p.variant == 11:                             # units of ru rows x 32 pixels
         ru = p.unit_rows // 32
@@ -130,7 +130,7 @@ def check_plan_invariants(d, p):
         assert ks <= d.split_k
         assert ups == -(-p.units // min(d.split_k, p.units))
     assert p.needs_reduce == (1 if ks > 1 else 0)
-    if p.variant == 12:   # depthwise: one workgroup per (slice, 64-channel quad)
+    if p.variant in (12, 13):   # one workgroup per (slice, 64-channel block)
         assert p.tiles == -(-d.C // 64)
     assert p.grid == p.tiles * ks
     assert p.slab_stride % 64 == 0 and p.slab_stride >= p.E
