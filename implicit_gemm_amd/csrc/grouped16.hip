@@ -317,20 +317,21 @@ __global__ __launch_bounds__(256, 3) void grouped16_win_kernel(G16Args a) {
 
 // Row-streaming path for stride 1, dilation 1, Wo <= 32 and a compile-time
 // R x S filter.  A workgroup owns 64 channels and a slice of output rows of
-// one image at a time.  Step h brings X row h (34 pixels with the padding
-// columns) and dY row h + pad into LDS (double-buffered, one barrier per
-// step) with 16-byte buffer loads that run kPf steps ahead; the buffer range
-// of a row supplies its zero padding, and rows outside the image or the
+// one image at a time.  Each step brings kRows X rows (34 pixels with the
+// padding columns) and kRows dY rows into LDS (double-buffered, one barrier
+// per step) with 16-byte buffer loads that run kPf steps ahead; the buffer
+// range of a row supplies its zero padding, and rows outside the image or the
 // segment have an empty range.  The A operand of each dY row is read once and
-// kept in registers for the R steps that use it; X row h is read at its S
+// kept in registers for the R rows that use it; X row h is read at its S
 // column offsets and multiplied with the A operands of output rows
 // h + pad - r, so every staged element is read from HBM once per slice.
 template <bool kBf16, int R, int S>
 __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
   constexpr int kXPixR = kWoT + S - 1;            // staged X pixels per row
-  constexpr int kPf = 8;                          // steps fetched ahead (even)
-  __shared__ __attribute__((aligned(16))) unsigned short s_x[2][kXPixR * kPitchE];
-  __shared__ __attribute__((aligned(16))) unsigned short s_dy[2][kWoT * kPitchE];
+  constexpr int kRows = 2;                        // rows per step (one barrier)
+  constexpr int kPf = 2;                          // steps fetched ahead (even)
+  __shared__ __attribute__((aligned(16))) unsigned short s_x[2][kRows][kXPixR * kPitchE];
+  __shared__ __attribute__((aligned(16))) unsigned short s_dy[2][kRows][kWoT * kPitchE];
   const unsigned char* __restrict__ xg = static_cast<const unsigned char*>(a.x);
   const unsigned char* __restrict__ dyg = static_cast<const unsigned char*>(a.dy);
 
@@ -351,30 +352,41 @@ __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
   const int ox0 = ((ps - a.pad) * a.C + 8 * q) * 2;               // negative: zero (padding)
   const int ox1 = ps + 32 < kXPixR ? ((ps + 32 - a.pad) * a.C + 8 * q) * 2 : 0x7fffffff;
   const int ody = (ps * a.K + 8 * q) * 2;
-  struct Step {
+  struct Row {
     uint4 x0, x1, d;
   };
-  // Step t of a segment: X row ho0 - pad + t and dY row ho0 + t (t < steps).
-  int n = 0, ho0 = 0, ho_hi = 0, steps = 0;
-  auto fetch = [&](int t, Step& st) {
-    const int h = ho0 - a.pad + t;
-    const bool x_in = h >= 0 && h < a.H && t < steps;
+  struct Step {
+    Row row[kRows];
+  };
+  // Row u of a segment: X row ho0 - pad + u and dY row ho0 + u (u < rows_x).
+  int n = 0, ho0 = 0, ho_hi = 0, rows_x = 0;
+  auto fetch_row = [&](int u, Row& st) {
+    const int h = ho0 - a.pad + u;
+    const bool x_in = h >= 0 && h < a.H && u < rows_x;
     const __amdgpu_buffer_rsrc_t rx =
         buf_rsrc(xg + 2 * ((int64_t)n * a.x_img + (int64_t)(x_in ? h : 0) * a.W * a.C + c0),
                  x_in ? x_row_bytes : 0);
     st.x0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, ox0, 0, 0));
     st.x1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, ox1, 0, 0));
-    const int ho = ho0 + t;
+    const int ho = ho0 + u;
     const bool d_in = ho < ho_hi;
     const __amdgpu_buffer_rsrc_t rd =
         buf_rsrc(dyg + 2 * (((int64_t)n * a.Ho + (d_in ? ho : ho0)) * a.Wo * a.K + c0),
                  d_in ? dy_row_bytes : 0);
     st.d = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rd, ody, 0, 0));
   };
+  auto fetch = [&](int t, Step& st) {
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) fetch_row(kRows * t + i, st.row[i]);
+  };
   auto store = [&](int buf, const Step& st) {
-    *reinterpret_cast<uint4*>(&s_x[buf][ps * kPitchE + 8 * q]) = st.x0;
-    if (ps + 32 < kXPixR) *reinterpret_cast<uint4*>(&s_x[buf][(ps + 32) * kPitchE + 8 * q]) = st.x1;
-    *reinterpret_cast<uint4*>(&s_dy[buf][ps * kPitchE + 8 * q]) = st.d;
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+      *reinterpret_cast<uint4*>(&s_x[buf][i][ps * kPitchE + 8 * q]) = st.row[i].x0;
+      if (ps + 32 < kXPixR)
+        *reinterpret_cast<uint4*>(&s_x[buf][i][(ps + 32) * kPitchE + 8 * q]) = st.row[i].x1;
+      *reinterpret_cast<uint4*>(&s_dy[buf][i][ps * kPitchE + 8 * q]) = st.row[i].d;
+    }
   };
 
   const int j = lane & 15, g = lane >> 4;
@@ -394,8 +406,9 @@ __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
     ho0 = row % a.Ho;
     const int seg = min(r_end - row, a.Ho - ho0);
     ho_hi = ho0 + seg;
-    steps = seg + R - 1;
-    // A operands of dY rows ho0 + t - r, r = 0..R-1 (zero before the segment).
+    rows_x = seg + R - 1;     // X rows ho0 - pad .. ho0 + seg - 1 - pad + R - 1
+    const int steps = (rows_x + kRows - 1) / kRows;
+    // A operands of dY rows ho0 + u - r, r = 0..R-1 (zero before the segment).
     s16x8 fa[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) fa[r] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
@@ -409,17 +422,21 @@ __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
         fetch(tk + kPf, pf[k]);
         lds_barrier();
         if (tk < steps) {
+          // Rows past the segment's X rows hold zero dY, so their products vanish.
 #pragma unroll
-          for (int r = R - 1; r > 0; --r) fa[r] = fa[r - 1];
-          fa[0] = tr8(&s_dy[k & 1][lane_off]);
-          s16x8 fb[S];
+          for (int i = 0; i < kRows; ++i) {
 #pragma unroll
-          for (int s2 = 0; s2 < S; ++s2) fb[s2] = tr8(&s_x[k & 1][s2 * kPitchE + lane_off]);
+            for (int r = R - 1; r > 0; --r) fa[r] = fa[r - 1];
+            fa[0] = tr8(&s_dy[k & 1][i][lane_off]);
+            s16x8 fb[S];
 #pragma unroll
-          for (int r = 0; r < R; ++r)
+            for (int s2 = 0; s2 < S; ++s2) fb[s2] = tr8(&s_x[k & 1][i][s2 * kPitchE + lane_off]);
 #pragma unroll
-            for (int s2 = 0; s2 < S; ++s2)
-              acc[r * S + s2] = mfma16<kBf16>(fa[r], fb[s2], acc[r * S + s2]);
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+              for (int s2 = 0; s2 < S; ++s2)
+                acc[r * S + s2] = mfma16<kBf16>(fa[r], fb[s2], acc[r * S + s2]);
+          }
         }
       }
     }

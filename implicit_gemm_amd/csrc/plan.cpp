@@ -79,9 +79,11 @@ conv_wgrad_status_t canonicalise(const conv_wgrad_desc_t* d, Problem* o) {
 
 conv_wgrad_status_t choose_split(int64_t units, int64_t tiles, int32_t requested, int64_t min_units,
                                  int64_t target_groups, int64_t traffic_div, const Problem& p,
-                                 conv_wgrad_plan_t* pub) {
+                                 conv_wgrad_plan_t* pub, int64_t forced_ups) {
   int64_t degree;
-  if (requested >= 1) {
+  if (forced_ups >= 1) {
+    degree = ceil_div(units, forced_ups < units ? forced_ups : units);
+  } else if (requested >= 1) {
     degree = requested;
   } else {
     degree = target_groups / tiles;
@@ -99,6 +101,9 @@ conv_wgrad_status_t choose_split(int64_t units, int64_t tiles, int32_t requested
   if (degree > kMaxSlices) degree = kMaxSlices;
   pub->units = units;
   pub->units_per_slice = ceil_div(units, degree);
+  // A forced slice length is kept as given (a later slice may be shorter).
+  if (forced_ups >= 1 && pub->units_per_slice < forced_ups && forced_ups <= units)
+    pub->units_per_slice = forced_ups;
   int64_t ks = ceil_div(units, pub->units_per_slice);
   if (ks > kI32Max) return CONV_WGRAD_ERR_UNSUPPORTED;
   pub->ks_count = (int32_t)ks;
@@ -268,9 +273,21 @@ conv_wgrad_status_t make_plan(const conv_wgrad_desc_t* desc, Plan* out) {
     pub.unit_rows = p.Wo;  // a unit is one output row
     int64_t units;
     if (!mul_ok(p.N, p.Ho, &units)) return CONV_WGRAD_ERR_UNSUPPORTED;
-    // Four-wave workgroups, about two per CU; slices of at least 8 rows keep
-    // the re-read X halo rows small.
-    return choose_split(units, out->c_tiles, desc->split_k, 8, 512, 4, p, &pub);
+    // Four-wave workgroups, about one per CU, each streaming long runs of rows.
+    if (desc->split_k >= 1) return choose_split(units, out->c_tiles, desc->split_k, 8, 256, 4, p, &pub);
+    // A slice that straddles two images restarts the row pipeline (and
+    // re-reads R - 1 halo rows), so the automatic slice length is rounded up
+    // to whole images, or to a divisor of an image's rows.
+    conv_wgrad_plan_t probe = pub;
+    st = choose_split(units, out->c_tiles, -1, 8, 256, 4, p, &probe);
+    if (st != CONV_WGRAD_OK) return st;
+    int64_t ups = probe.units_per_slice;
+    if (ups >= p.Ho) {
+      ups = ceil_div(ups, p.Ho) * p.Ho;
+    } else {
+      while (p.Ho % ups != 0) ++ups;
+    }
+    return choose_split(units, out->c_tiles, -1, 8, 256, 4, p, &pub, ups);
   }
   if (small_groups && plan_grouped16(p, out)) {
     pub.path = CONV_WGRAD_PATH_DIRECT;

@@ -73,9 +73,10 @@ conv_wgrad_status_t make_plan(const conv_wgrad_desc_t* desc, Plan* out);
 // Auto degree: floor(target_groups / tiles) slices (so the grid never exceeds
 // target_groups), at most units / min_units, and with the slab traffic
 // (each slab element written once and read once) at most the algorithmic
-// bytes divided by traffic_div.
+// bytes divided by traffic_div.  forced_ups >= 1 fixes the units per slice
+// instead (the degree follows from it).
 conv_wgrad_status_t choose_split(int64_t units, int64_t tiles, int32_t requested, int64_t min_units,
                                  int64_t target_groups, int64_t traffic_div, const Problem& p,
-                                 conv_wgrad_plan_t* pub);
+                                 conv_wgrad_plan_t* pub, int64_t forced_ups = 0);
 
 }  // namespace cw
