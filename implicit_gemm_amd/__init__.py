@@ -129,7 +129,7 @@ def conv_wgrad_ex(desc: Desc, x_ptr: int, dy_ptr: int, dw_ptr: int, ws_ptr: int,
 
 def conv_wgrad_timed(desc: Desc, x_ptr: int, dy_ptr: int, dw_ptr: int, ws_ptr: int, ws_bytes: int,
                      stream: int, ev_begin: int, ev_end: int) -> None:
-    """conv_wgrad with HIP events recorded around the stage-1 kernel."""
+    """conv_wgrad whose stage-1 dispatch stamps its start and end into two HIP events."""
     st = load().conv_wgrad_timed(ctypes.byref(desc), x_ptr, dy_ptr, dw_ptr, ws_ptr or None, ws_bytes,
                                  stream or None, ev_begin or None, ev_end or None)
     if st != 0:

@@ -172,6 +172,46 @@ def test_nonzero_result_stream_and_default_stream():
     assert int((a == 0).sum()) == 0
 
 
+def test_timed_entry_point_events_and_bits():
+    """conv_wgrad_timed gives conv_wgrad's bits, and its events bracket a stage-1 dispatch."""
+    import ctypes
+    import torch
+    import implicit_gemm_amd as iga
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    for name in ("c2_3x3_f32", "c4a_grp3x3_cpg4_f16"):
+        wl = wd.WORKLOADS[name]
+        s = wl.shape
+        log("timed entry point", name)
+        x, dy = wd.make_inputs(wl)
+        xd, dyd = to_device(x, wl.dtype), to_device(dy, wl.dtype)
+        ref = iga.wgrad(xd, dyd, s.R, s.S, s.pad, s.stride, s.dilation, s.groups)
+        d = iga.desc_for(xd, dyd, s.R, s.S, s.pad, s.stride, s.dilation, s.groups, -1)
+        plan = iga.get_plan(d)
+        dw = torch.full_like(ref, float("nan"))
+        ws = torch.empty(max(int(plan.ws_bytes), 16), dtype=torch.uint8, device=xd.device)
+        evs = [ctypes.c_void_p(), ctypes.c_void_p()]
+        for e in evs:
+            assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        sp = torch.cuda.current_stream().cuda_stream
+        iga.conv_wgrad_timed(d, xd.data_ptr(), dyd.data_ptr(), dw.data_ptr(), ws.data_ptr(),
+                             int(plan.ws_bytes), sp, evs[0].value, evs[1].value)
+        assert hip.hipEventSynchronize(evs[1]) == 0
+        ms = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), evs[0], evs[1]) == 0
+        torch.cuda.synchronize()
+        for e in evs:
+            hip.hipEventDestroy(e)
+        assert torch.equal(dw, ref)
+        assert 0.0 < ms.value < 1000.0
+        # A later launch on the thread does not record into the events again.
+        iga.wgrad(xd, dyd, s.R, s.S, s.pad, s.stride, s.dilation, s.groups)
+        torch.cuda.synchronize()
+
+
 SMALL_GROUP_CASES = [
     # depthwise on the 4x4x4 kernel: filter sizes 1..8, pads, widths, ragged rows
     (wd.ConvShape(2, 16, 9, 11, 16, 7, 7, pad=3, groups=16), "bf16", -1),
