@@ -6,9 +6,13 @@ plan has several slices) on inputs already resident in HBM.  The default
 workload is the 3x3 fp32 wgrad, N=32, C=K=64, H=W=56, pad 1.  Prints one
 JSON line:
 
-  value           TFLOP/s of the whole call over K back-to-back steps
-  roofline        the stage-1 kernel alone, timed with HIP events recorded on
-                  its own stream around each launch in the timed region,
+  value           TFLOP/s of the whole call over K back-to-back steps (after
+                  W warm-up steps and --prewarm-s seconds of untimed steps
+                  that bring the GPU to its clocks under load)
+  roofline        the stage-1 kernel alone, its duration taken from HIP events
+                  on its own dispatch in each of K further back-to-back steps
+                  right after the timed region (kept out of that region: a
+                  launch that carries events costs the call GPU time),
                   against the MI355X peak of its bound (f32 MFMA or HBM);
                   traffic = HBM bytes per launch from the FETCH_SIZE /
                   WRITE_SIZE counter table in profiles/hbm_traffic.md when
@@ -157,6 +161,8 @@ def main():
     ap.add_argument("--config", default=DEFAULT_CONFIG)
     ap.add_argument("--split-k", type=int, default=-1)
     ap.add_argument("--cold", type=int, default=20, help="cold-cache calls (0 = skip)")
+    ap.add_argument("--prewarm-s", type=float, default=0.3,
+                    help="seconds of untimed steps after the warm-up steps (clock ramp)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -222,15 +228,32 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # Clock warm-up: the GPU leaves its idle clocks only after some time under
+    # load, so untimed steps run until --prewarm-s seconds have passed.
+    t_pre = time.perf_counter()
+    prewarm_steps = 0
+    while time.perf_counter() - t_pre < args.prewarm_s:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+        prewarm_steps += 10
 
-    # Timed region: K back-to-back steps; events around every stage-1 launch.
-    evs = [(hip.event(), hip.event()) for _ in range(args.steps)]
+    # Timed region: K back-to-back steps, no per-call events (a launch that
+    # carries timing events costs the call several microseconds of GPU time).
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # Stage-1 kernel durations: the next K back-to-back steps, with HIP events
+    # that take the stage-1 dispatch's own start and end timestamps.
+    evs = [(hip.event(), hip.event()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
     for i in range(args.steps):
         step(*evs[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     k_ms = [hip.elapsed_ms(a, b) for a, b in evs]
     for a, b in evs:
         hip.destroy(a)
@@ -280,6 +303,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "prewarm_steps": prewarm_steps,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",

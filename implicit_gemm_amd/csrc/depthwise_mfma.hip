@@ -75,7 +75,8 @@ struct DwLayout {
   static constexpr int kDWave = 16 * kDs;
   static constexpr int kDBuf = 64 * kDs;          // bytes per dY buffer
   static constexpr int kDyBase = RING * kSlot;
-  static constexpr int kBytes = kDyBase + 2 * kDBuf;
+  static constexpr int kOut = kQuadCh * 64 * 4;   // output block of 64 channels, up to 8 x 8 taps
+  static constexpr int kBytes = kDyBase + 2 * kDBuf > kOut ? kDyBase + 2 * kDBuf : kOut;
 };
 
 template <bool kBf16>
@@ -299,20 +300,26 @@ __global__ __launch_bounds__(kThreads) void depthwise_mfma_kernel(DwArgs a) {
     row += seg;
   }
 
-  // acc[rb][sb][v] = dW[c0 + wave + 4b][4*rb + v][4*sb + q]
-  const int c = c0 + wave + 4 * b;
-  if (c < a.C) {
-    float* out = a.out + (int64_t)slice * a.slab_stride + (int64_t)c * a.R * a.S;
+  // acc[rb][sb][v] = dW[c0 + wave + 4b][4*rb + v][4*sb + q].  The outputs are
+  // gathered in LDS in the [c][r][s] order of the output (every wave has
+  // passed the last barrier above, after its last LDS access), so that the
+  // workgroup writes its min(64, C - c0) channels as whole 16-byte stores.
+  const int RS = a.R * a.S;
+  float* s_out = reinterpret_cast<float*>(lds);
+  const int cl = wave + 4 * b;
 #pragma unroll
-    for (int i = 0; i < RB; ++i)
+  for (int i = 0; i < RB; ++i)
 #pragma unroll
-      for (int j = 0; j < SB; ++j)
+    for (int j = 0; j < SB; ++j)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int r = 4 * i + v, s = 4 * j + q;
-          if (r < a.R && s < a.S) out[r * a.S + s] = acc[i][j][v];
-        }
-  }
+      for (int v = 0; v < 4; ++v) {
+        const int r = 4 * i + v, s = 4 * j + q;
+        if (r < a.R && s < a.S) s_out[cl * RS + r * a.S + s] = acc[i][j][v];
+      }
+  __syncthreads();
+  const int n4 = min(kQuadCh, a.C - c0) * RS / 4;   // C % 16 == 0
+  float4* out = reinterpret_cast<float4*>(a.out + (int64_t)slice * a.slab_stride + (int64_t)c0 * RS);
+  for (int i = tid; i < n4; i += kThreads) out[i] = reinterpret_cast<const float4*>(lds)[i];
 }
 
 template <bool kBf16, int RB, int SB, int XL>

@@ -330,17 +330,33 @@ __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
   constexpr int kXPixR = kWoT + S - 1;            // staged X pixels per row
   constexpr int kRows = 2;                        // rows per step (one barrier)
   constexpr int kPf = 2;                          // steps fetched ahead (even)
-  __shared__ __attribute__((aligned(16))) unsigned short s_x[2][kRows][kXPixR * kPitchE];
-  __shared__ __attribute__((aligned(16))) unsigned short s_dy[2][kRows][kWoT * kPitchE];
+  constexpr int kOut = kCh * R * S * 16;          // largest output block (16 channels per group)
+  // The row tiles, and after the last row the workgroup's output block.
+  union Smem {
+    struct {
+      unsigned short x[2][kRows][kXPixR * kPitchE];
+      unsigned short dy[2][kRows][kWoT * kPitchE];
+    } t;
+    float4 out[kOut / 4];
+  };
+  static_assert(sizeof(Smem) == sizeof(Smem::t), "the output block fits in the row tiles");
+  __shared__ __attribute__((aligned(16))) Smem sm;
+  auto& s_x = sm.t.x;
+  auto& s_dy = sm.t.dy;
   const unsigned char* __restrict__ xg = static_cast<const unsigned char*>(a.x);
   const unsigned char* __restrict__ dyg = static_cast<const unsigned char*>(a.dy);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int bid = blockIdx.x;
-  // Consecutive blocks take the channel blocks of one slice (they read the
-  // same pixel rows at the same time).
-  const int cb = bid % a.c_blocks;
-  const int slice = bid / a.c_blocks;
+  // Work item w = (slice, channel block), channel block fastest; the grid is
+  // a multiple of 8 and block b runs on XCD b % 8, so XCD x takes the items
+  // [x * per_xcd, (x + 1) * per_xcd): the channel blocks of a slice, which
+  // read the same pixel rows at the same time, share one L2.
+  const int work = a.c_blocks * a.ks_count;
+  const int per_xcd = (work + 7) >> 3;
+  const int w = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (w >= work) return;
+  const int cb = w % a.c_blocks;
+  const int slice = w / a.c_blocks;
   const int c0 = cb * kCh;
   const int r_begin = slice * a.units_per_slice;
   const int r_end = min(a.units, r_begin + a.units_per_slice);   // units are output rows
@@ -445,17 +461,26 @@ __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
     row += seg;
   }
 
-  float* out = a.out + (int64_t)slice * a.slab_stride;
-  const int c = c0 + 16 * wave + j;
+  // acc[t][v] = out[k = c0 + 16*wave + 4*g + v][c = c0 + 16*wave + j] for tap t;
+  // only same-group pairs are outputs.  They are gathered in LDS (every wave
+  // has passed the last barrier above, after its last tile read) in the
+  // [k][tap][c % Cg] order of the output, so that the workgroup writes its
+  // block of min(64, K - c0) output channels as whole 16-byte stores.
+  constexpr int kTaps = R * S;
+  const int Cg = a.Cg;
+  float* s_out = reinterpret_cast<float*>(sm.out);
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    const int k = c0 + 16 * wave + 4 * g + v;
-    if (k < a.K && c < a.C && k / a.Kg == c / a.Cg) {
-      float* o = out + (int64_t)k * (R * S) * a.Cg + (c % a.Cg);
+    const int kl = 16 * wave + 4 * g + v;
+    if ((4 * g + v) / Cg == j / Cg) {
 #pragma unroll
-      for (int t = 0; t < R * S; ++t) o[t * a.Cg] = acc[t][v];
+      for (int t = 0; t < kTaps; ++t) s_out[(kl * kTaps + t) * Cg + j % Cg] = acc[t][v];
     }
   }
+  __syncthreads();
+  const int n4 = min(kCh, a.K - c0) * kTaps * Cg / 4;
+  float4* out = reinterpret_cast<float4*>(a.out + (int64_t)slice * a.slab_stride + (int64_t)c0 * kTaps * Cg);
+  for (int i = tid; i < n4; i += 256) out[i] = sm.out[i];
 }
 
 }  // namespace
@@ -485,11 +510,12 @@ hipError_t launch_grouped16(const Plan& plan, const void* x, const void* dy, Sta
   const dim3 grid((unsigned)plan.pub.grid), block(256);
   const bool bf = p.dtype == CONV_WGRAD_BF16;
   if (plan.pub.variant == kGrouped16Rows) {
+    const dim3 xcd_grid((unsigned)(ceil_div(plan.pub.grid, 8) * 8));
     if (p.R == 3)
-      return bf ? launch_kernel(grouped16_rows_kernel<true, 3, 3>, grid, block, a, stream)
-                : launch_kernel(grouped16_rows_kernel<false, 3, 3>, grid, block, a, stream);
-    return bf ? launch_kernel(grouped16_rows_kernel<true, 1, 1>, grid, block, a, stream)
-              : launch_kernel(grouped16_rows_kernel<false, 1, 1>, grid, block, a, stream);
+      return bf ? launch_kernel(grouped16_rows_kernel<true, 3, 3>, xcd_grid, block, a, stream)
+                : launch_kernel(grouped16_rows_kernel<false, 3, 3>, xcd_grid, block, a, stream);
+    return bf ? launch_kernel(grouped16_rows_kernel<true, 1, 1>, xcd_grid, block, a, stream)
+              : launch_kernel(grouped16_rows_kernel<false, 1, 1>, xcd_grid, block, a, stream);
   }
   if (plan.ru == 4 && p.dil == 1 && p.R == 3 && p.S == 3)
     return bf ? launch_kernel(grouped16_win_kernel<true, 3, 3>, grid, block, a, stream)

@@ -57,23 +57,25 @@ __global__ __launch_bounds__(256) void slab_fold_kernel(FoldArgs a) {
   float4 acc = {0.f, 0.f, 0.f, 0.f};
   if (i < a.E && hi > lo) {
     const float* s = a.src + (int64_t)lo * a.src_step + i;
+    const int cnt = hi - lo;
     if (full) {
-      acc = *reinterpret_cast<const float4*>(s);
-      int j = lo + 1;
-      for (; j + kBatch <= hi; j += kBatch) {
+      // All loads of a batch are issued before its adds (a part is usually
+      // shorter than one batch, so its slabs cost one memory latency).
+      for (int j0 = 0; j0 < cnt; j0 += kBatch) {
         float4 v[kBatch];
 #pragma unroll
         for (int b = 0; b < kBatch; ++b)
-          v[b] = *reinterpret_cast<const float4*>(s + (int64_t)(j - lo + b) * a.src_step);
+          v[b] = j0 + b < cnt ? *reinterpret_cast<const float4*>(s + (int64_t)(j0 + b) * a.src_step)
+                              : float4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int b = 0; b < kBatch; ++b) acc = add4(acc, v[b]);
+        for (int b = 0; b < kBatch; ++b)
+          if (j0 + b < cnt) acc = j0 + b == 0 ? v[b] : add4(acc, v[b]);
       }
-      for (; j < hi; ++j) acc = add4(acc, *reinterpret_cast<const float4*>(s + (int64_t)(j - lo) * a.src_step));
     } else {
       float t[4] = {0.f, 0.f, 0.f, 0.f};
       for (int e = 0; e < 4 && i + e < a.E; ++e) {
         t[e] = s[e];
-        for (int j = lo + 1; j < hi; ++j) t[e] += s[(int64_t)(j - lo) * a.src_step + e];
+        for (int j = 1; j < cnt; ++j) t[e] += s[(int64_t)j * a.src_step + e];
       }
       acc = float4{t[0], t[1], t[2], t[3]};
     }
