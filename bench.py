@@ -20,7 +20,10 @@ JSON line:
   cold_cache      per-call event times with a 1 GiB cache flush before each call
   cpu_baseline    the CPU oracle (test infrastructure) timed on the host cores
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu] [--bias]
+
+With --bias every step is conv_wgrad_bias (the weight gradient and the fused
+bias gradient db = sum dY); value still counts the weight-gradient FLOPs.
 """
 from __future__ import annotations
 
@@ -164,6 +167,8 @@ def main():
     ap.add_argument("--prewarm-s", type=float, default=0.3,
                     help="seconds of untimed steps after the warm-up steps (clock ramp)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--bias", action="store_true",
+                    help="time conv_wgrad_bias (dW and the fused bias gradient db = sum dY)")
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run 3 device-to-device copies of 1 GiB (scale for HBM byte counters)")
@@ -221,9 +226,15 @@ def main():
     hip = Hip()
     torch.cuda.synchronize()
 
+    db = torch.empty((s.K,), dtype=torch.float32, device=dev)
+
     def step(ev0=0, ev1=0):
-        iga.conv_wgrad_timed(d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(),
-                             ws.data_ptr() if ws_bytes else 0, ws_bytes, sp, ev0, ev1)
+        if args.bias:
+            iga.conv_wgrad_bias_timed(d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(), db.data_ptr(),
+                                      ws.data_ptr() if ws_bytes else 0, ws_bytes, sp, ev0, ev1)
+        else:
+            iga.conv_wgrad_timed(d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(),
+                                 ws.data_ptr() if ws_bytes else 0, ws_bytes, sp, ev0, ev1)
 
     for _ in range(args.warmup):
         step()
@@ -290,7 +301,7 @@ def main():
     value = s.flops() / (wall / args.steps) / 1e12
     stage1_avg_s = statistics.mean(k_ms) * 1e-3
     roof = roofline_for(s, wl.dtype, stage1_avg_s,
-                        measured_traffic(wl.name, source_digest(plan.variant)))
+                        None if args.bias else measured_traffic(wl.name, source_digest(plan.variant)))
 
     cpu = None
     if not args.no_cpu:
@@ -314,6 +325,7 @@ def main():
                    "K": s.K, "R": s.R, "S": s.S, "pad": s.pad, "stride": s.stride,
                    "dilation": s.dilation, "groups": s.groups, "split_k": args.split_k,
                    "ks_count": int(plan.ks_count), "path": int(plan.path), "variant": int(plan.variant),
+                   "bias_gradient": bool(args.bias),
                    "parallelism": "single GPU"},
         "roofline": roof,
         "stage1_ms_mean": round(stage1_avg_s * 1e3, 5),

@@ -87,6 +87,13 @@ def load():
     lib.conv_wgrad_timed.argtypes = [P(Desc), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                      ctypes.c_void_p, ctypes.c_void_p]
+    lib.conv_wgrad_bias.restype = ctypes.c_int
+    lib.conv_wgrad_bias.argtypes = [P(Desc), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.conv_wgrad_bias_timed.restype = ctypes.c_int
+    lib.conv_wgrad_bias_timed.argtypes = [P(Desc), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     _lib = lib
     return lib
 
@@ -136,6 +143,25 @@ def conv_wgrad_timed(desc: Desc, x_ptr: int, dy_ptr: int, dw_ptr: int, ws_ptr: i
         raise ConvWgradError(st, "conv_wgrad_timed")
 
 
+def conv_wgrad_bias(desc: Desc, x_ptr: int, dy_ptr: int, dw_ptr: int, db_ptr: int, ws_ptr: int,
+                    ws_bytes: int, stream: int) -> None:
+    """Weight gradient into dw and bias gradient (sum of dy per channel) into db."""
+    st = load().conv_wgrad_bias(ctypes.byref(desc), x_ptr, dy_ptr, dw_ptr, db_ptr or None,
+                                ws_ptr or None, ws_bytes, stream or None)
+    if st != 0:
+        raise ConvWgradError(st, "conv_wgrad_bias")
+
+
+def conv_wgrad_bias_timed(desc: Desc, x_ptr: int, dy_ptr: int, dw_ptr: int, db_ptr: int, ws_ptr: int,
+                          ws_bytes: int, stream: int, ev_begin: int, ev_end: int) -> None:
+    """conv_wgrad_bias whose stage-1 dispatch stamps its start and end into two HIP events."""
+    st = load().conv_wgrad_bias_timed(ctypes.byref(desc), x_ptr, dy_ptr, dw_ptr, db_ptr or None,
+                                      ws_ptr or None, ws_bytes, stream or None, ev_begin or None,
+                                      ev_end or None)
+    if st != 0:
+        raise ConvWgradError(st, "conv_wgrad_bias_timed")
+
+
 def _dtype_code(t):
     import torch
     codes = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
@@ -156,8 +182,12 @@ def desc_for(x, dy, R, S, pad=0, stride=1, dilation=1, groups=1, split_k=-1) -> 
 
 
 def wgrad(x, dy, R, S, pad=0, stride=1, dilation=1, groups=1, split_k=-1, dw=None, workspace=None,
-          stream=None):
-    """Weight gradient dW [K, R, S, C/groups] (fp32) of NHWC x and dy on the current HIP stream."""
+          stream=None, bias=False, db=None):
+    """Weight gradient dW [K, R, S, C/groups] (fp32) of NHWC x and dy on the current HIP stream.
+
+    With bias=True, returns (dW, db) where db [K] (fp32) is the bias gradient,
+    the sum of dy over its N, Ho, Wo axes, from the same pass over dy.
+    """
     import torch
     d = desc_for(x, dy, R, S, pad, stride, dilation, groups, split_k)
     plan = get_plan(d)
@@ -178,8 +208,15 @@ def wgrad(x, dy, R, S, pad=0, stride=1, dilation=1, groups=1, split_k=-1, dw=Non
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
-    conv_wgrad_ex(d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(),
-                  workspace.data_ptr() if ws_bytes else 0,
-                  workspace.numel() * workspace.element_size() if ws_bytes else 0,
-                  stream.cuda_stream)
-    return dw
+    ws_ptr = workspace.data_ptr() if ws_bytes else 0
+    ws_len = workspace.numel() * workspace.element_size() if ws_bytes else 0
+    if not bias:
+        conv_wgrad_ex(d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(), ws_ptr, ws_len, stream.cuda_stream)
+        return dw
+    if db is None:
+        db = torch.empty((d.K,), dtype=torch.float32, device=x.device)
+    elif tuple(db.shape) != (d.K,) or db.dtype != torch.float32 or not db.is_contiguous():
+        raise ValueError("db must be a contiguous float32 tensor of shape (%d,)" % d.K)
+    conv_wgrad_bias(d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(), db.data_ptr(), ws_ptr, ws_len,
+                    stream.cuda_stream)
+    return dw, db

@@ -69,16 +69,17 @@ conv_wgrad_status_t get_plan(const conv_wgrad_desc_t* desc, cw::Plan* out) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// with_db: the bias gradient is requested (db must then be a valid pointer).
 conv_wgrad_status_t run(const conv_wgrad_desc_t* desc, const void* x, const void* dy, float* dw,
-                        void* workspace, bool check_ws, size_t ws_bytes, void* stream,
-                        void* ev_begin = nullptr, void* ev_end = nullptr) {
+                        bool with_db, float* db, void* workspace, bool check_ws, size_t ws_bytes,
+                        void* stream, void* ev_begin = nullptr, void* ev_end = nullptr) {
   cw::Plan plan;
   conv_wgrad_status_t st = get_plan(desc, &plan);
   if (st != CONV_WGRAD_OK) return st;
-  if (!x || !dy || !dw) return CONV_WGRAD_ERR_NULL_ARG;
+  if (!x || !dy || !dw || (with_db && !db)) return CONV_WGRAD_ERR_NULL_ARG;
   if (plan.pub.ws_bytes > 0 && !workspace) return CONV_WGRAD_ERR_NULL_ARG;
   if (check_ws && ws_bytes < plan.pub.ws_bytes) return CONV_WGRAD_ERR_WORKSPACE;
-  if (!aligned16(x) || !aligned16(dy) || !aligned16(dw) ||
+  if (!aligned16(x) || !aligned16(dy) || !aligned16(dw) || (with_db && !aligned16(db)) ||
       (plan.pub.ws_bytes > 0 && !aligned16(workspace)))
     return CONV_WGRAD_ERR_MISALIGNED;
 
@@ -87,9 +88,11 @@ conv_wgrad_status_t run(const conv_wgrad_desc_t* desc, const void* x, const void
   if (plan.pub.needs_reduce) {
     out.base = static_cast<float*>(workspace);
     out.slab_stride = plan.pub.slab_stride;
+    out.db = with_db ? out.base + cw::db_offset(plan.p) : nullptr;
   } else {
     out.base = dw;
     out.slab_stride = 0;
+    out.db = with_db ? db : nullptr;
   }
   hipError_t err;
   // The stage-1 launch takes the events (timestamps of its own dispatch); the
@@ -112,7 +115,7 @@ conv_wgrad_status_t run(const conv_wgrad_desc_t* desc, const void* x, const void
   }
   if (err != hipSuccess) return CONV_WGRAD_ERR_HIP;
   if (plan.pub.needs_reduce) {
-    err = cw::launch_slab_reduce(plan, static_cast<float*>(workspace), dw, s);
+    err = cw::launch_slab_reduce(plan, static_cast<float*>(workspace), dw, with_db ? db : nullptr, s);
     if (err != hipSuccess) return CONV_WGRAD_ERR_HIP;
   }
   return CONV_WGRAD_OK;
@@ -157,18 +160,33 @@ conv_wgrad_status_t conv_wgrad_workspace_size(const conv_wgrad_desc_t* desc, siz
 
 conv_wgrad_status_t conv_wgrad(const conv_wgrad_desc_t* desc, const void* x, const void* dy,
                                float* dw, void* workspace, void* stream) {
-  return run(desc, x, dy, dw, workspace, false, 0, stream);
+  return run(desc, x, dy, dw, false, nullptr, workspace, false, 0, stream);
 }
 
 conv_wgrad_status_t conv_wgrad_ex(const conv_wgrad_desc_t* desc, const void* x, const void* dy,
                                   float* dw, void* workspace, size_t ws_bytes, void* stream) {
-  return run(desc, x, dy, dw, workspace, true, ws_bytes, stream);
+  return run(desc, x, dy, dw, false, nullptr, workspace, true, ws_bytes, stream);
 }
 
 conv_wgrad_status_t conv_wgrad_timed(const conv_wgrad_desc_t* desc, const void* x, const void* dy,
                                      float* dw, void* workspace, size_t ws_bytes, void* stream,
                                      void* stage1_begin, void* stage1_end) {
-  return run(desc, x, dy, dw, workspace, true, ws_bytes, stream, stage1_begin, stage1_end);
+  return run(desc, x, dy, dw, false, nullptr, workspace, true, ws_bytes, stream, stage1_begin,
+             stage1_end);
+}
+
+conv_wgrad_status_t conv_wgrad_bias(const conv_wgrad_desc_t* desc, const void* x, const void* dy,
+                                    float* dw, float* db, void* workspace, size_t ws_bytes,
+                                    void* stream) {
+  return run(desc, x, dy, dw, true, db, workspace, true, ws_bytes, stream);
+}
+
+conv_wgrad_status_t conv_wgrad_bias_timed(const conv_wgrad_desc_t* desc, const void* x,
+                                          const void* dy, float* dw, float* db, void* workspace,
+                                          size_t ws_bytes, void* stream, void* stage1_begin,
+                                          void* stage1_end) {
+  return run(desc, x, dy, dw, true, db, workspace, true, ws_bytes, stream, stage1_begin,
+             stage1_end);
 }
 
 }  // extern "C"

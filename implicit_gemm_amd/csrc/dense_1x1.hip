@@ -36,6 +36,7 @@ struct OneByOneArgs {
   int64_t L;            // rows
   int64_t rows_per_slice;
   int32_t ks_count;
+  float* dbo;   // bias-gradient partial of slice 0 (slab_stride apart), or nullptr
 };
 
 template <int AV, int BV>
@@ -73,7 +74,9 @@ __device__ __forceinline__ void load_batch(const float* dyp, const float* xp, bo
   }
 }
 
-template <int AV, int BV>
+// kDb: the bias-gradient variant (a separate instantiation keeps the extra
+// registers and code out of the plain kernel's load pipeline).
+template <int AV, int BV, bool kDb>
 __global__ __launch_bounds__(64) void dense_1x1_kernel(OneByOneArgs a) {
   const int lane = threadIdx.x;
   const int li = lane & 15, lg = lane >> 4;
@@ -101,6 +104,14 @@ __global__ __launch_bounds__(64) void dense_1x1_kernel(OneByOneArgs a) {
 #pragma unroll
     for (int j = 0; j < BV; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Bias gradient: the first input-channel tile of each (group, output-channel
+  // tile) adds up the dY values it feeds to the MFMAs (rows past the slice
+  // load as zero); lane (i, g) sums rows = g mod 4 for channels m0 + AV*i ...
+  const bool want_db = kDb && ct == 0;
+  float dbp[AV];
+#pragma unroll
+  for (int i = 0; i < AV; ++i) dbp[i] = 0.f;
+
   float ra[kPf][AV], rb[kPf][BV];
 #pragma unroll
   for (int p = 0; p < kPf; ++p) {
@@ -116,9 +127,29 @@ __global__ __launch_bounds__(64) void dense_1x1_kernel(OneByOneArgs a) {
 #pragma unroll
           for (int j = 0; j < BV; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ra[p][i], rb[p][j], acc[i][j], 0, 0, 0);
+        if constexpr (kDb) {
+#pragma unroll
+          for (int i = 0; i < AV; ++i) dbp[i] += ra[p][i];
+        }
         load_batch<AV, BV>(dyp, xp, row < r_end, ra[p], rb[p]);
         dyp += dy_step; xp += x_step; row += 4;
       }
+    }
+  }
+
+  if (want_db) {
+    // Lanes i, i + 16, i + 32, i + 48 hold the same channels: a fixed pairwise tree.
+#pragma unroll
+    for (int i = 0; i < AV; ++i) {
+      float v = dbp[i];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      dbp[i] = v;
+    }
+    if (lg == 0) {
+      float* o = a.dbo + (int64_t)slice * a.slab_stride + (int64_t)g * a.Kg + m0 + AV * li;
+#pragma unroll
+      for (int i = 0; i < AV; ++i) o[i] = dbp[i];
     }
   }
 
@@ -138,7 +169,9 @@ __global__ __launch_bounds__(64) void dense_1x1_kernel(OneByOneArgs a) {
 
 template <int AV, int BV>
 hipError_t launch_ab(const OneByOneArgs& args, int64_t grid, hipStream_t stream) {
-  return launch_kernel(dense_1x1_kernel<AV, BV>, dim3((unsigned)grid), dim3(64), args, stream);
+  if (args.dbo)
+    return launch_kernel(dense_1x1_kernel<AV, BV, true>, dim3((unsigned)grid), dim3(64), args, stream);
+  return launch_kernel(dense_1x1_kernel<AV, BV, false>, dim3((unsigned)grid), dim3(64), args, stream);
 }
 
 }  // namespace
@@ -158,6 +191,7 @@ hipError_t launch_dense_1x1(const Plan& plan, const void* x, const void* dy, Sta
   a.L = p.L;
   a.rows_per_slice = plan.pub.units_per_slice * plan.pub.unit_rows;
   a.ks_count = plan.pub.ks_count;
+  a.dbo = out.db;
   const int64_t grid = plan.pub.grid;
   switch (plan.bv) {
     case 1: return launch_ab<4, 1>(a, grid, stream);

@@ -36,6 +36,7 @@ struct DenseArgs {
   int32_t Cg, Kg, cols;
   int32_t m_tiles, n_tiles;
   int32_t L, rows_per_slice, ks_count;
+  float* dbo;   // bias-gradient partial of slice 0 (slab_stride apart), or nullptr
 };
 
 // One thread's view of 4 consecutive GEMM columns (fixed for the whole kernel).
@@ -133,12 +134,21 @@ __global__ __launch_bounds__(256) void dense_lds_kernel(DenseArgs a) {
   const int wm = wave >> 1, wn = wave & 1;
   const int li = lane & 15, lg = lane >> 4;
 
+  // Bias gradient: the first column tile of each (group, output-channel
+  // tile) adds up the dY rows it stages (rows past the slice load as zero).
+  const bool want_db = a.dbo != nullptr && nt == 0;
+  float dbp[4] = {0.f, 0.f, 0.f, 0.f};
+
   load_step(l_begin);
   for (int l0 = l_begin; l0 < l_end; l0 += kBK) {
     __syncthreads();  // previous step's MFMA reads of LDS are done
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
       const int row = row0 + 16 * it;
+      if (want_db) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dbp[e] += ra[it][e];
+      }
       *reinterpret_cast<float4*>(&sA[row * kLdA + 4 * c4]) =
           float4{ra[it][0], ra[it][1], ra[it][2], ra[it][3]};
       *reinterpret_cast<float4*>(&sB[row * kLdB + 4 * c4]) =
@@ -159,6 +169,11 @@ __global__ __launch_bounds__(256) void dense_lds_kernel(DenseArgs a) {
       acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc[1][1], 0, 0, 0);
     }
   }
+
+  if (want_db)   // 16 loader rows per channel quad
+    block_sum64<16, 4>(sA, row0, 4 * c4, dbp,
+                       a.dbo + (int64_t)slice * a.slab_stride + (int64_t)g * a.Kg + m0,
+                       min(kBM, a.Kg - m0));
 
   // Each output element of this tile is written once, to dw or to slab `slice`.
   float* out = a.out + (int64_t)slice * a.slab_stride;
@@ -198,6 +213,7 @@ hipError_t launch_dense(const Plan& plan, const void* x, const void* dy, Stage1O
   a.dy = dy;
   a.out = out.base;
   a.slab_stride = out.slab_stride;
+  a.dbo = out.db;
   a.x_img = p.x_img;
   a.H = (int32_t)p.H; a.W = (int32_t)p.W; a.C = (int32_t)p.C; a.K = (int32_t)p.K;
   a.Ho = (int32_t)p.Ho; a.Wo = (int32_t)p.Wo;

@@ -49,6 +49,7 @@ struct RowsArgs {
   int32_t wt, wchunks, xspan;
   int32_t units, units_per_slice, ks_count;
   int32_t tiles, work;   // tiles per slice, tiles * ks_count
+  float* dbo;            // bias-gradient partial of slice 0 (slab_stride apart), or nullptr
 };
 
 // kUnit: stride 1 and dilation 1 are compile-time (every LDS offset of the
@@ -131,12 +132,23 @@ __global__ __launch_bounds__(512, 1) void dense_rows_kernel(RowsArgs a) {
     for (int i = 0; i < kMaxXSpan / 16; ++i) buf_load4(rs_b, ob[i] + wb, xp, rb[i]);
   };
 
+  // Bias gradient: the tile with the first filter row, tap block and input
+  // channel block of its (group, output-channel block) adds up the dY rows it
+  // stages (every output pixel of the slice once; pixels past a unit load as
+  // zero), per thread for its 4 channels.
+  const bool want_db = a.dbo != nullptr && r == 0 && sb == 0 && ct == 0;
+  float dbp[4] = {0.f, 0.f, 0.f, 0.f};
   float* const buf = smem + half * kBuf;
   auto store_unit = [&]() {
 #pragma unroll
-    for (int i = 0; i < kMaxWt / 16; ++i)
+    for (int i = 0; i < kMaxWt / 16; ++i) {
       *reinterpret_cast<float4*>(&buf[(p0 + 16 * i) * kPitch + 4 * q]) =
           float4{ra[i][0], ra[i][1], ra[i][2], ra[i][3]};
+      if (want_db) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dbp[j] += ra[i][j];
+      }
+    }
     float* xb = buf + kMaxWt * kPitch;
 #pragma unroll
     for (int i = 0; i < kMaxXSpan / 16; ++i)
@@ -206,6 +218,12 @@ __global__ __launch_bounds__(512, 1) void dense_rows_kernel(RowsArgs a) {
     compute_unit(comp ? npix_cur : 0);
     __syncthreads();
   }
+
+  // Bias partial: rows are the 16 loader rows of half 0, then those of half 1.
+  if (want_db)
+    block_sum64<32, 4>(smem, 16 * half + p0, 4 * q, dbp,
+                       a.dbo + (int64_t)slice * a.slab_stride + (int64_t)g * a.Kg + m0,
+                       min(64, a.Kg - m0));
 
   // Half 1 hands its accumulators to half 0 through LDS (both buffers are
   // free after the last barrier); half 0 adds them and writes the slab.
@@ -283,6 +301,7 @@ hipError_t launch_dense_rows(const Plan& plan, const void* x, const void* dy, St
   a.dy = dy;
   a.out = out.base;
   a.slab_stride = out.slab_stride;
+  a.dbo = out.db;
   a.x_img = p.x_img;
   a.H = (int32_t)p.H; a.W = (int32_t)p.W; a.C = (int32_t)p.C; a.K = (int32_t)p.K;
   a.Ho = (int32_t)p.Ho; a.Wo = (int32_t)p.Wo;

@@ -62,6 +62,7 @@ struct DwArgs {
   int32_t dy_off;          // column of dY element 0 in a staged dY row
   int32_t rows, rows_per_slice, ks_count;  // rows = N * Ho
   int32_t quads;           // ceil(C / 64)
+  float* dbo;              // bias-gradient partial of slice 0 (slab_stride apart), or nullptr
 };
 
 // LDS layout for staged rows of XL columns.
@@ -261,6 +262,8 @@ __global__ __launch_bounds__(kThreads) void depthwise_mfma_kernel(DwArgs a) {
   // issues the same loads (rows outside the image or the segment have an
   // empty range and read 0), so the load counters are static.
   const bool guard_ring = a.R + 1 > RING;
+  const bool want_db = a.dbo != nullptr;
+  float dbp[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // channels 8o .. 8o + 7
   Item<NP> qx[kPf], qd[kPf];
   int row = r_begin;
   while (row < r_end) {
@@ -286,6 +289,15 @@ __global__ __launch_bounds__(kThreads) void depthwise_mfma_kernel(DwArgs a) {
         const int tk = t + k;
         store_x((ho0 - a.pad + tk) & (RING - 1), qx[k]);
         store_dy(k & 1, qd[k]);
+        if (want_db) {
+          // Each dY row of the segment is staged by exactly one step; rows
+          // outside it and pixels past the row were loaded as zero.
+#pragma unroll
+          for (int p = 0; p < NP; ++p) {
+            add8<kBf16>(dbp, __builtin_bit_cast(uint4, qd[k].p[p][0]));
+            add8<kBf16>(dbp, __builtin_bit_cast(uint4, qd[k].p[p][1]));
+          }
+        }
         fetch_step(tk + kPf, qx[k], qd[k]);
         lds_barrier();
         if (tk >= a.R - 1 && tk < steps) {
@@ -299,6 +311,10 @@ __global__ __launch_bounds__(kThreads) void depthwise_mfma_kernel(DwArgs a) {
     lds_barrier();
     row += seg;
   }
+
+  if (want_db)   // sums of the 32 pixel-pair loaders, channels c0 .. c0 + 63 (LDS is free here)
+    block_sum64<32, 8>(reinterpret_cast<float*>(lds), pp, 8 * o, dbp,
+                       a.dbo + (int64_t)slice * a.slab_stride + c0, min(kQuadCh, a.C - c0));
 
   // acc[rb][sb][v] = dW[c0 + wave + 4b][4*rb + v][4*sb + q].  The outputs are
   // gathered in LDS in the [c][r][s] order of the output (every wave has
@@ -393,6 +409,7 @@ hipError_t launch_depthwise(const Plan& plan, const void* x, const void* dy, Sta
   a.rows_per_slice = (int32_t)plan.pub.units_per_slice;
   a.ks_count = plan.pub.ks_count;
   a.quads = (int32_t)ceil_div(p.C, 64);
+  a.dbo = out.db;
   if (p.dtype == CONV_WGRAD_BF16) return launch_b<true>(plan, a, stream);
   return launch_b<false>(plan, a, stream);
 }

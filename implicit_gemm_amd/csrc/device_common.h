@@ -62,6 +62,43 @@ __device__ __forceinline__ void buf_load4(__amdgpu_buffer_rsrc_t r, int off, con
   out[0] = (float)v[0]; out[1] = (float)v[1]; out[2] = (float)v[2]; out[3] = (float)v[3];
 }
 
+// Adds the 8 16-bit values of v (8 consecutive channels as loaded) to d.
+template <bool kBf16>
+__device__ __forceinline__ void add8(float (&d)[8], uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (kBf16) {
+      d[2 * i] += __uint_as_float(w[i] << 16);
+      d[2 * i + 1] += __uint_as_float(w[i] & 0xffff0000u);
+    } else {
+      d[2 * i] += (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] & 0xffffu));
+      d[2 * i + 1] += (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
+    }
+  }
+}
+
+// Bias-gradient partial of a 64-channel block: thread t holds NV per-thread
+// sums d[j] of channel ch0 + j for partial row `row` (ROWS rows, each channel
+// covered once per row).  The rows are added in ascending order through
+// `scratch` (ROWS * 64 floats of LDS) and out[c] = sum for c < nvalid.  Every
+// thread of the workgroup calls it (it has barriers before and after).
+template <int ROWS, int NV>
+__device__ __forceinline__ void block_sum64(float* scratch, int row, int ch0, const float (&d)[NV],
+                                            float* out, int nvalid) {
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < NV; ++j) scratch[row * 64 + ch0 + j] = d[j];
+  __syncthreads();
+  const int c = (int)threadIdx.x;
+  if (c < 64 && c < nvalid) {
+    float r = scratch[c];
+    for (int i = 1; i < ROWS; ++i) r += scratch[i * 64 + c];
+    out[c] = r;
+  }
+  __syncthreads();
+}
+
 // Workgroup barrier that waits for this wave's LDS accesses only (not for
 // its outstanding global loads); the memory clobber keeps the compiler from
 // moving LDS accesses across it.

@@ -25,6 +25,7 @@ struct DirectArgs {
   int32_t taps;  // R*S*Cg
   int32_t E;     // K*taps
   int32_t L, pix_per_slice, ks_count;
+  float* dbo;    // bias-gradient partial of slice 0 (slab_stride apart), or nullptr
 };
 
 template <typename T>
@@ -47,7 +48,10 @@ __global__ __launch_bounds__(256) void direct_elem_kernel(DirectArgs a) {
   int n = p_begin / HoWo;
   int rem = p_begin - n * HoWo;
   int ho = rem / a.Wo, wo = rem - ho * a.Wo;
-  float acc = 0.f;
+  // The lanes of tap column 0 (e < K) also sum dY[., k] over every pixel of
+  // the slice: the bias-gradient partial of channel k.
+  const bool db_lane = a.dbo != nullptr && t == 0;
+  float acc = 0.f, dbacc = 0.f;
   for (int pix = p_begin; pix < p_end; ++pix) {
     const int h = ho * a.stride + dh, w = wo * a.stride + dw;
     if (h >= 0 && h < a.H && w >= 0 && w < a.W) {
@@ -55,12 +59,14 @@ __global__ __launch_bounds__(256) void direct_elem_kernel(DirectArgs a) {
       const float xv = to_f32(x[(int64_t)n * a.x_img + ((int64_t)h * a.W + w) * a.C + ch]);
       acc = __builtin_fmaf(gy, xv, acc);
     }
+    if (db_lane) dbacc += to_f32(dy[(int64_t)pix * a.K + k]);
     if (++wo == a.Wo) {
       wo = 0;
       if (++ho == a.Ho) { ho = 0; ++n; }
     }
   }
   a.out[(int64_t)slice * a.slab_stride + (int64_t)k * a.taps + t] = acc;
+  if (db_lane) a.dbo[(int64_t)slice * a.slab_stride + k] = dbacc;
 }
 
 }  // namespace
@@ -84,6 +90,7 @@ hipError_t launch_direct(const Plan& plan, const void* x, const void* dy, Stage1
   a.L = (int32_t)p.L;
   a.pix_per_slice = (int32_t)(plan.pub.units_per_slice * plan.pub.unit_rows);
   a.ks_count = plan.pub.ks_count;
+  a.dbo = out.db;
   const dim3 grid((unsigned)plan.pub.grid), block(256);
   switch (p.dtype) {
     case CONV_WGRAD_F32: return launch_kernel(direct_elem_kernel<float>, grid, block, a, stream);

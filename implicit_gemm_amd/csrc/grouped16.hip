@@ -51,6 +51,7 @@ struct G16Args {
   int32_t H, W, C, K, Ho, Wo, R, S, pad, dil, Cg, Kg, taps;
   int32_t ru, hblocks, wchunks, xrows, xpix;
   int32_t c_blocks, units, units_per_slice, ks_count;
+  float* dbo;   // bias-gradient partial of slice 0 (slab_stride apart), or nullptr
 };
 
 __device__ __forceinline__ s16x4 tr_read(const unsigned short* p) {
@@ -120,10 +121,16 @@ __global__ __launch_bounds__(256, 2) void grouped16_kernel(G16Args a) {
             x + (int64_t)n * a.x_img + ((int64_t)h * a.W + w) * a.C + c0 + 8 * q);
     }
   };
+  // Bias-gradient partial of channels c0 + 8q .. + 7: every dY pixel of the
+  // slice is staged once (pixels outside the output were loaded as zero).
+  const bool want_db = a.dbo != nullptr;
+  float dbp[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   auto store_unit = [&]() {
 #pragma unroll
-    for (int i = 0; i < kDyPix / kLoaders; ++i)
+    for (int i = 0; i < kDyPix / kLoaders; ++i) {
       *reinterpret_cast<uint4*>(&s_dy[(pslot + kLoaders * i) * kPitchE + 8 * q]) = rdy[i];
+      if (want_db) add8<kBf16>(dbp, rdy[i]);
+    }
 #pragma unroll
     for (int i = 0; i < kXPix / kLoaders; ++i)
       *reinterpret_cast<uint4*>(&s_x[(pslot + kLoaders * i) * kPitchE + 8 * q]) = rx[i];
@@ -184,6 +191,10 @@ __global__ __launch_bounds__(256, 2) void grouped16_kernel(G16Args a) {
       }
     }
   }
+
+  if (want_db)
+    block_sum64<32, 8>(reinterpret_cast<float*>(s_dy), pslot, 8 * q, dbp,
+                       a.dbo + (int64_t)slice * a.slab_stride + c0, min(kCh, a.K - c0));
 
   // acc[t][v] = out[k = c0 + 16*wave + 4*g + v][c = c0 + 16*wave + j] for tap t;
   // only same-group pairs are outputs.
@@ -257,11 +268,15 @@ __global__ __launch_bounds__(256, 3) void grouped16_win_kernel(G16Args a) {
             x + (int64_t)n * a.x_img + ((int64_t)h * a.W + w) * a.C + c0 + 8 * q);
     }
   };
+  const bool want_db = a.dbo != nullptr;
+  float dbp[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // bias partial, channels c0 + 8q ..
   auto store_unit = [&]() {
 #pragma unroll
     for (int i = 0; i < kDyLoads; ++i)
-      if (pslot + kLoaders * i < kDy)
+      if (pslot + kLoaders * i < kDy) {
         *reinterpret_cast<uint4*>(&s_dy[(pslot + kLoaders * i) * kPitchE + 8 * q]) = rdy[i];
+        if (want_db) add8<kBf16>(dbp, rdy[i]);
+      }
 #pragma unroll
     for (int i = 0; i < kXLoads; ++i)
       if (pslot + kLoaders * i < kX)
@@ -301,6 +316,10 @@ __global__ __launch_bounds__(256, 3) void grouped16_win_kernel(G16Args a) {
       }
     }
   }
+
+  if (want_db)
+    block_sum64<32, 8>(reinterpret_cast<float*>(s_x), pslot, 8 * q, dbp,
+                       a.dbo + (int64_t)slice * a.slab_stride + c0, min(kCh, a.K - c0));
 
   float* out = a.out + (int64_t)slice * a.slab_stride;
   const int c = c0 + 16 * wave + j;
@@ -395,6 +414,11 @@ __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
 #pragma unroll
     for (int i = 0; i < kRows; ++i) fetch_row(kRows * t + i, st.row[i]);
   };
+  // Bias-gradient partial of channels c0 + 8q .. + 7: each dY row of a segment
+  // is fetched by exactly one step (rows outside it, and pixels past the row,
+  // load as zero).
+  const bool want_db = a.dbo != nullptr;
+  float dbp[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   auto store = [&](int buf, const Step& st) {
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
@@ -402,6 +426,7 @@ __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
       if (ps + 32 < kXPixR)
         *reinterpret_cast<uint4*>(&s_x[buf][i][(ps + 32) * kPitchE + 8 * q]) = st.row[i].x1;
       *reinterpret_cast<uint4*>(&s_dy[buf][i][ps * kPitchE + 8 * q]) = st.row[i].d;
+      if (want_db) add8<kBf16>(dbp, st.row[i].d);
     }
   };
 
@@ -461,6 +486,10 @@ __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
     row += seg;
   }
 
+  if (want_db)
+    block_sum64<32, 8>(reinterpret_cast<float*>(sm.out), ps, 8 * q, dbp,
+                       a.dbo + (int64_t)slice * a.slab_stride + c0, min(kCh, a.K - c0));
+
   // acc[t][v] = out[k = c0 + 16*wave + 4*g + v][c = c0 + 16*wave + j] for tap t;
   // only same-group pairs are outputs.  They are gathered in LDS (every wave
   // has passed the last barrier above, after its last tile read) in the
@@ -507,6 +536,7 @@ hipError_t launch_grouped16(const Plan& plan, const void* x, const void* dy, Sta
   a.units = (int32_t)plan.pub.units;
   a.units_per_slice = (int32_t)plan.pub.units_per_slice;
   a.ks_count = plan.pub.ks_count;
+  a.dbo = out.db;
   const dim3 grid((unsigned)plan.pub.grid), block(256);
   const bool bf = p.dtype == CONV_WGRAD_BF16;
   if (plan.pub.variant == kGrouped16Rows) {

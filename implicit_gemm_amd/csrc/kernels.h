@@ -8,10 +8,15 @@
 
 namespace cw {
 
-// Stage-1 output: dw itself (one slice) or the fp32 slab workspace.
+// Stage-1 output: dw itself (one slice) or the fp32 slab workspace.  When the
+// bias gradient is requested, db points at slice 0's bias partial (db itself
+// for one slice, else the slab's bias range) and the workgroups that own an
+// output-channel block of a slice write its sum of dY there; slices are
+// slab_stride floats apart as for the weight gradient.
 struct Stage1Out {
   float* base;           // dw or workspace
   int64_t slab_stride;   // floats between slabs (0 when writing dw)
+  float* db = nullptr;   // bias-gradient partial of slice 0, or nullptr
 };
 
 // Events the next stage-1 launch on this thread records its own start and end
@@ -47,6 +52,7 @@ hipError_t launch_depthwise(const Plan& plan, const void* x, const void* dy, Sta
                             hipStream_t stream);
 hipError_t launch_direct(const Plan& plan, const void* x, const void* dy, Stage1Out out,
                          hipStream_t stream);
-hipError_t launch_slab_reduce(const Plan& plan, float* ws, float* dw, hipStream_t stream);
+// Folds the slabs into dw and, when db is not null, into db.
+hipError_t launch_slab_reduce(const Plan& plan, float* ws, float* dw, float* db, hipStream_t stream);
 
 }  // namespace cw

@@ -112,7 +112,7 @@ conv_wgrad_status_t choose_split(int64_t units, int64_t tiles, int32_t requested
   int64_t grid;
   if (!mul_ok(tiles, ks, &grid) || grid > kI32Max) return CONV_WGRAD_ERR_UNSUPPORTED;
   pub->grid = grid;
-  pub->slab_stride = ceil_div(p.E, 64) * 64;
+  pub->slab_stride = ceil_div(db_offset(p) + p.K, 64) * 64;   // dW partial, then db partial
   int64_t ws_elems;
   if (ks > 1) {
     if (!mul_ok(pub->slab_stride, ks, &ws_elems) || ws_elems > INT64_MAX / 4)

@@ -56,6 +56,10 @@ struct Plan {
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// A slab holds the weight-gradient partial in elements [0, E) and the
+// bias-gradient partial (K elements) from this 16-byte aligned offset on.
+inline int64_t db_offset(const Problem& p) { return ceil_div(p.E, 4) * 4; }
+
 // Validate and canonicalise desc.  Returns CONV_WGRAD_OK or the error code.
 conv_wgrad_status_t canonicalise(const conv_wgrad_desc_t* desc, Problem* out);
 

@@ -5,6 +5,10 @@
 // two-stage split-K of rocm-libraries PR #14393, sections "Two-stage split-K"
 // and "Review follow-ups").
 //
+// A slab holds the weight-gradient partial (E elements) and, from element
+// db_offset on, the bias-gradient partial (K elements) when one is requested;
+// both ranges are folded the same way.
+//
 // One fold pass sums, for every output group o, the input slabs
 // [o*G, min(n, (o+1)*G)).  A workgroup owns 16 element chunks (4 floats
 // each) of one group; the group's slabs are cut into kParts consecutive
@@ -33,9 +37,16 @@ struct FoldArgs {
   int64_t src_step;   // floats between consecutive input slabs
   int32_t n;          // input slabs
   int32_t group;      // input slabs per output
-  float* dst;         // output 0
   int64_t dst_step;   // floats between outputs
-  int64_t E;          // elements per slab
+  // Two element ranges of a slab are folded: [0, E) into dst (the weight
+  // gradient) and, when E2 > 0, [off2, off2 + E2) into dst2 (the bias
+  // gradient).  Blocks [0, nb1) take the first range, the rest the second.
+  float* dst;
+  int64_t E;
+  int32_t nb1;
+  int64_t off2;
+  int64_t E2;
+  float* dst2;
 };
 
 __device__ __forceinline__ float4 add4(float4 a, float4 b) {
@@ -46,17 +57,22 @@ __global__ __launch_bounds__(256) void slab_fold_kernel(FoldArgs a) {
   __shared__ float4 part_sum[kParts][kChunks];
   __shared__ int part_len[kParts];
   const int c = threadIdx.x % kChunks, p = threadIdx.x / kChunks;
-  const int64_t i = ((int64_t)blockIdx.x * kChunks + c) * 4;  // first element of the chunk
+  const bool second = (int)blockIdx.x >= a.nb1;
+  const int blk = second ? (int)blockIdx.x - a.nb1 : (int)blockIdx.x;
+  const int64_t E = second ? a.E2 : a.E;
+  const float* const src = a.src + (second ? a.off2 : 0);
+  float* const dst = second ? a.dst2 : a.dst;
+  const int64_t i = ((int64_t)blk * kChunks + c) * 4;  // first element of the chunk
   const int o = blockIdx.y;
   const int first = o * a.group;
   const int len = min(a.group, a.n - first);
   const int lo = first + (int)((int64_t)p * len / kParts);
   const int hi = first + (int)((int64_t)(p + 1) * len / kParts);
   if (c == 0) part_len[p] = hi - lo;
-  const bool full = i + 4 <= a.E;
+  const bool full = i + 4 <= E;
   float4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (i < a.E && hi > lo) {
-    const float* s = a.src + (int64_t)lo * a.src_step + i;
+  if (i < E && hi > lo) {
+    const float* s = src + (int64_t)lo * a.src_step + i;
     const int cnt = hi - lo;
     if (full) {
       // All loads of a batch are issued before its adds (a part is usually
@@ -73,7 +89,7 @@ __global__ __launch_bounds__(256) void slab_fold_kernel(FoldArgs a) {
       }
     } else {
       float t[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int e = 0; e < 4 && i + e < a.E; ++e) {
+      for (int e = 0; e < 4 && i + e < E; ++e) {
         t[e] = s[e];
         for (int j = 1; j < cnt; ++j) t[e] += s[(int64_t)j * a.src_step + e];
       }
@@ -82,40 +98,45 @@ __global__ __launch_bounds__(256) void slab_fold_kernel(FoldArgs a) {
   }
   part_sum[p][c] = acc;
   __syncthreads();  // every read of this group's slabs is done before the in-place store below
-  if (p == 0 && i < a.E) {
+  if (p == 0 && i < E) {
     int q = 0;
     while (part_len[q] == 0) ++q;  // the group has >= 1 slab, so some part is non-empty
     float4 r = part_sum[q][c];
     for (++q; q < kParts; ++q)
       if (part_len[q] > 0) r = add4(r, part_sum[q][c]);
-    float* d = a.dst + (int64_t)o * a.dst_step + i;
+    float* d = dst + (int64_t)o * a.dst_step + i;
     if (full) {
       *reinterpret_cast<float4*>(d) = r;  // dw and the slabs are 16-byte aligned
     } else {
       const float rv[4] = {r.x, r.y, r.z, r.w};
-      for (int e = 0; e < 4 && i + e < a.E; ++e) d[e] = rv[e];
+      for (int e = 0; e < 4 && i + e < E; ++e) d[e] = rv[e];
     }
   }
 }
 
-hipError_t fold(const FoldArgs& a, int outputs, hipStream_t stream) {
-  const int64_t chunks = (a.E + 3) / 4;
-  const dim3 grid((unsigned)((chunks + kChunks - 1) / kChunks), (unsigned)outputs);
+hipError_t fold(FoldArgs a, int outputs, hipStream_t stream) {
+  const int64_t per_block = 4 * kChunks;
+  a.nb1 = (int32_t)ceil_div(a.E, per_block);
+  const int64_t nb2 = a.E2 > 0 ? ceil_div(a.E2, per_block) : 0;
+  const dim3 grid((unsigned)(a.nb1 + nb2), (unsigned)outputs);
   return launch_kernel(slab_fold_kernel, grid, dim3(256), a, stream);
 }
 
 }  // namespace
 
-hipError_t launch_slab_reduce(const Plan& plan, float* ws, float* dw, hipStream_t stream) {
+hipError_t launch_slab_reduce(const Plan& plan, float* ws, float* dw, float* db, hipStream_t stream) {
   const int64_t E = plan.p.E, stride = plan.pub.slab_stride;
+  const int64_t off2 = db_offset(plan.p), E2 = db ? plan.p.K : 0;
   const int32_t ks = plan.pub.ks_count;
-  if (ks <= kMaxSinglePass) return fold(FoldArgs{ws, stride, ks, ks, dw, 0, E}, 1, stream);
+  if (ks <= kMaxSinglePass)
+    return fold(FoldArgs{ws, stride, ks, ks, 0, dw, E, 0, off2, E2, db}, 1, stream);
   // Pass 1: run r of kRun slabs -> slab r*kRun (each workgroup reads all of
   // its run before writing that run's first slab).
   const int32_t runs = (ks + kRun - 1) / kRun;
-  hipError_t err = fold(FoldArgs{ws, stride, ks, kRun, ws, stride * kRun, E}, runs, stream);
+  hipError_t err = fold(FoldArgs{ws, stride, ks, kRun, stride * kRun, ws, E, 0, off2, E2, ws + off2},
+                        runs, stream);
   if (err != hipSuccess) return err;
-  return fold(FoldArgs{ws, stride * kRun, runs, runs, dw, 0, E}, 1, stream);
+  return fold(FoldArgs{ws, stride * kRun, runs, runs, 0, dw, E, 0, off2, E2, db}, 1, stream);
 }
 
 }  // namespace cw

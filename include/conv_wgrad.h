@@ -127,8 +127,9 @@ typedef struct conv_wgrad_plan {
 const char* conv_wgrad_status_string(conv_wgrad_status_t status);
 
 /*
- * Workspace bytes conv_wgrad needs for desc (0 when the plan has one slice).
- * Pure host function.  Errors: NULL_ARG (desc or bytes NULL), BAD_*, UNSUPPORTED.
+ * Workspace bytes conv_wgrad and conv_wgrad_bias need for desc (0 when the plan
+ * has one slice).  Pure host function.  Errors: NULL_ARG (desc or bytes NULL),
+ * BAD_*, UNSUPPORTED.
  */
 conv_wgrad_status_t conv_wgrad_workspace_size(const conv_wgrad_desc_t* desc, size_t* bytes);
 
@@ -171,6 +172,30 @@ conv_wgrad_status_t conv_wgrad_ex(const conv_wgrad_desc_t* desc, const void* x, 
 conv_wgrad_status_t conv_wgrad_timed(const conv_wgrad_desc_t* desc, const void* x, const void* dy,
                                      float* dw, void* workspace, size_t ws_bytes, void* stream,
                                      void* stage1_begin, void* stage1_end);
+
+/*
+ * Weight gradient and bias gradient in one pass over dy.  The bias gradient of
+ * a convolution is the sum of the output gradient over every output pixel
+ * (rocm-libraries PR #11188, section Motivation, checks bias.grad beside
+ * weight.grad of nn.Conv2d):
+ *   db[k] = sum over n, ho, wo of dy[n][ho][wo][k]
+ *   db        : device pointer, fp32 [K], 16-byte aligned; overwritten
+ * The stage-1 kernels add up the dy values they already stage, per slice;
+ * db is folded with the slabs in the same fixed order as dw (fp32 adds), so
+ * the result is bit-identical from run to run at a fixed split, and dw is
+ * bit-identical to what conv_wgrad_ex writes for the same desc.  The other
+ * arguments, the workspace size and the errors are those of conv_wgrad_ex
+ * (NULL_ARG also for a NULL db, MISALIGNED for a misaligned one).
+ */
+conv_wgrad_status_t conv_wgrad_bias(const conv_wgrad_desc_t* desc, const void* x, const void* dy,
+                                    float* dw, float* db, void* workspace, size_t ws_bytes,
+                                    void* stream);
+
+/* Profiling variant of conv_wgrad_bias, with stage-1 events as in conv_wgrad_timed. */
+conv_wgrad_status_t conv_wgrad_bias_timed(const conv_wgrad_desc_t* desc, const void* x,
+                                          const void* dy, float* dw, float* db, void* workspace,
+                                          size_t ws_bytes, void* stream, void* stage1_begin,
+                                          void* stage1_end);
 
 #ifdef __cplusplus
 }

@@ -56,6 +56,8 @@ def load(path: str | None = None):
         lib.oracle_out_size.argtypes = [i64] * 5
         lib.oracle_wgrad_accumulate.restype = ctypes.c_int
         lib.oracle_wgrad_accumulate.argtypes = [i64] * 11 + [ctypes.c_void_p] * 4 + [ctypes.c_int]
+        lib.oracle_bgrad_accumulate.restype = ctypes.c_int
+        lib.oracle_bgrad_accumulate.argtypes = [i64] * 4 + [ctypes.c_void_p] * 3
         lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         if path is None:
@@ -135,6 +137,21 @@ def wgrad_ref(x, dy, R, S, pad=0, stride=1, dilation=1, groups=1, nthreads=None,
     acc = WgradAccumulator(C, H, W, K, R, S, pad, stride, dilation, groups, nthreads, lib)
     acc.add(x, dy)
     return acc.dw, acc.den
+
+
+def bgrad_ref(dy, lib=None):
+    """Bias gradient db (fp64, [K]) of NHWC dy, and its error denominator max_k sum |dy[..., k]|."""
+    dy = np.ascontiguousarray(dy, dtype=np.float32)
+    if dy.ndim != 4:
+        raise ValueError("dy must be [N, Ho, Wo, K]")
+    n, ho, wo, k = dy.shape
+    db = np.zeros(k, np.float64)
+    ab = np.zeros(k, np.float64)
+    rc = (lib or load()).oracle_bgrad_accumulate(n, ho, wo, k, dy.ctypes.data, db.ctypes.data,
+                                                 ab.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("oracle_bgrad_accumulate failed: %d" % rc)
+    return db, float(ab.max()) if ab.size else 0.0
 
 
 def normalised_error(dw_test, dw_ref, den) -> float:

@@ -119,6 +119,32 @@ int oracle_wgrad_accumulate(int64_t nc, int64_t C, int64_t H, int64_t W, int64_t
   return 0;
 }
 
+/*
+ * Bias gradient (the "bias.grad" beside weight.grad of nn.Conv2d in
+ * rocm-libraries PR #11188, section Motivation): the output gradient summed
+ * over every output pixel,
+ *
+ *   db[k] = sum over n, ho, wo of dY[n, ho, wo, k],
+ *
+ * added for nc images into db and, as its error denominator, the sum of
+ * |dY[n, ho, wo, k]| into absacc (both [K], fp64).  dy is [nc][Ho][Wo][K]
+ * fp32; the sum runs in pixel order, in fp64.  Returns 0, or -1 on invalid
+ * arguments.
+ */
+int oracle_bgrad_accumulate(int64_t nc, int64_t Ho, int64_t Wo, int64_t K, const float* dy,
+                            double* db, double* absacc) {
+  if (nc < 0 || Ho < 1 || Wo < 1 || K < 1) return -1;
+  const int64_t pixels = nc * Ho * Wo;
+  for (int64_t l = 0; l < pixels; ++l) {
+    const float* g = dy + l * K;
+    for (int64_t k = 0; k < K; ++k) {
+      db[k] += (double)g[k];
+      absacc[k] += fabs((double)g[k]);
+    }
+  }
+  return 0;
+}
+
 /* Number of threads the OpenMP runtime would give a parallel region. */
 int oracle_max_threads(void) {
 #ifdef _OPENMP

@@ -183,6 +183,45 @@ def pin_bias_gradient(lib, seed=14):
         assert np.allclose(got[:, 0, 0, c], db, rtol=0, atol=1e-12), (c, got[:, 0, 0, c], db)
 
 
+def _bgrad(lib, dy):
+    return oracle.bgrad_ref(dy, lib=lib)
+
+
+def pin_bgrad(lib, seed=21):
+    """The bias-gradient oracle db[k] = sum dY[..., k] against: integer hand values
+    (exact), the weight-gradient oracle at X == 1 with a 1x1 filter (another code
+    path), numpy's float64 sum and torch's conv2d bias gradient (library routines),
+    and its denominator against numpy's sum of |dY|."""
+    # Hand-worked: pixel values 1..6 and 10..60 in two channels -> 21 and 210.
+    dy = np.array([[[[1, 10], [2, 20], [3, 30]], [[4, 40], [5, 50], [6, 60]]]], np.float32)
+    db, den = _bgrad(lib, dy)
+    assert np.array_equal(db, [21.0, 210.0]), db
+    assert den == 210.0, den
+    dy = -dy
+    db, den = _bgrad(lib, dy)
+    assert np.array_equal(db, [-21.0, -210.0]) and den == 210.0, (db, den)
+    rng = np.random.default_rng(seed)
+    import torch
+    for (N, Ho, Wo, K) in [(2, 5, 7, 3), (1, 1, 1, 4), (3, 4, 2, 9)]:
+        dy = rng.uniform(-1, 1, (N, Ho, Wo, K)).astype(np.float32)
+        db, den = _bgrad(lib, dy)
+        assert db.shape == (K,)
+        want = dy.astype(np.float64).sum(axis=(0, 1, 2))
+        assert np.max(np.abs(db - want)) <= 1e-13 * den, (N, Ho, Wo, K)
+        assert abs(den - np.abs(dy.astype(np.float64)).sum(axis=(0, 1, 2)).max()) <= 1e-13 * den
+        # X == 1, 1x1, stride 1, pad 0: every dW[k, 0, 0, c] is db[k].
+        dw, _ = _ref(lib, np.ones((N, Ho, Wo, 3), np.float32), dy, 1, 1)
+        for c in range(3):
+            assert np.max(np.abs(dw[:, 0, 0, c] - db)) <= 1e-13 * den, c
+        # torch: the gradient of a conv2d bias is the sum of the output gradient.
+        xt = torch.zeros((N, 2, Ho + 2, Wo + 2), dtype=torch.float64)
+        wt = torch.zeros((K, 2, 3, 3), dtype=torch.float64)
+        bt = torch.zeros((K,), dtype=torch.float64, requires_grad=True)
+        y = torch.nn.functional.conv2d(xt, wt, bt)
+        y.backward(torch.from_numpy(dy.astype(np.float64)).permute(0, 3, 1, 2))
+        assert np.max(np.abs(db - bt.grad.numpy())) <= 1e-13 * den, (N, Ho, Wo, K)
+
+
 def pin_box_sum(lib, seed=15):
     """X == 1, stride 1: dW[k,r,s,c] = sum of dY over the output window where the tap is inside."""
     rng = np.random.default_rng(seed)
@@ -290,4 +329,4 @@ def pin_denominator(lib, seed=20):
 
 ALL_PINS = [pin_hand_examples, pin_finite_differences, pin_torch_autograd, pin_closed_form_1x1,
             pin_bias_gradient, pin_box_sum, pin_depthwise_correlate, pin_grouped_is_dense_per_group,
-            pin_bilinear, pin_split_invariance, pin_denominator]
+            pin_bilinear, pin_split_invariance, pin_denominator, pin_bgrad]

@@ -26,7 +26,8 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = iga.load()
     names = declared_functions()
     assert set(names) == {"conv_wgrad", "conv_wgrad_ex", "conv_wgrad_get_plan", "conv_wgrad_timed",
-                          "conv_wgrad_status_string", "conv_wgrad_workspace_size"}
+                          "conv_wgrad_status_string", "conv_wgrad_workspace_size",
+                          "conv_wgrad_bias", "conv_wgrad_bias_timed"}
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", iga.LIB_PATH], capture_output=True,
@@ -92,6 +93,12 @@ def test_null_arguments():
     d = D(N=8, H=32, W=32, split_k=4)
     assert iga.get_plan(d).ks_count > 1
     assert lib.conv_wgrad(ctypes.byref(d), 16, 16, 16, None, None) == 1
+    # The bias entry point: db is required; the rest as conv_wgrad_ex.
+    ws = iga.workspace_size(d)
+    assert lib.conv_wgrad_bias(ctypes.byref(d), 16, 16, 16, None, 16, ws, None) == 1
+    assert lib.conv_wgrad_bias(ctypes.byref(d), 16, 16, None, 16, 16, ws, None) == 1
+    assert lib.conv_wgrad_bias(ctypes.byref(d), 16, 16, 16, 16, None, ws, None) == 1
+    assert lib.conv_wgrad_bias_timed(ctypes.byref(d), 16, 16, 16, None, 16, ws, None, None, None) == 1
 
 
 def test_misaligned_and_small_workspace():
@@ -104,6 +111,8 @@ def test_misaligned_and_small_workspace():
     assert lib.conv_wgrad(ctypes.byref(d), 16, 16, 24, 16, None) == 6
     assert lib.conv_wgrad(ctypes.byref(d), 16, 16, 16, 8, None) == 6
     assert lib.conv_wgrad_ex(ctypes.byref(d), 16, 16, 16, 16, ws - 1, None) == 7
+    assert lib.conv_wgrad_bias(ctypes.byref(d), 16, 16, 16, 40, 16, ws, None) == 6
+    assert lib.conv_wgrad_bias(ctypes.byref(d), 16, 16, 16, 16, 16, ws - 1, None) == 7
 
 
 def check_plan_invariants(d, p):
@@ -133,7 +142,8 @@ def check_plan_invariants(d, p):
     if p.variant in (12, 13):   # one workgroup per (slice, 64-channel block)
         assert p.tiles == -(-d.C // 64)
     assert p.grid == p.tiles * ks
-    assert p.slab_stride % 64 == 0 and p.slab_stride >= p.E
+    # a slab: the dW partial, then the db partial from the next 16-byte boundary
+    assert p.slab_stride % 64 == 0 and p.slab_stride >= -(-p.E // 4) * 4 + d.K
     assert p.ws_bytes == (ks * p.slab_stride * 4 if ks > 1 else 0)
     esz = 4 if d.dtype == iga.F32 else 2
     assert p.x_bytes == d.N * d.H * d.W * d.C * esz

@@ -228,6 +228,7 @@ SMALL_GROUP_CASES = [
     (wd.ConvShape(2, 64, 8, 64, 64, 5, 5, pad=2, groups=64), "bf16", -1),     # even pad, 72-column rows
     (wd.ConvShape(3, 16, 4, 33, 16, 6, 2, pad=1, groups=16), "f16", 4),       # odd Wo
     (wd.ConvShape(3, 384, 14, 14, 384, 7, 7, pad=3, groups=384), "bf16", 5),  # slices across images
+    (wd.ConvShape(2, 16, 6, 10, 16, 3, 3, pad=12, groups=16), "f16", 3),      # pad 12: zero X rows > R - 1
     # grouped 16-bit, row-streaming path (stride 1, 1x1 / 3x3, Wo <= 32)
     (wd.ConvShape(3, 64, 9, 32, 64, 3, 3, pad=1, groups=16), "f16", -1),      # Wo = 32, cpg4
     (wd.ConvShape(2, 48, 7, 13, 48, 3, 3, pad=0, groups=6), "bf16", 3),       # cpg8, pad 0, partial block

@@ -25,6 +25,11 @@ MUTANTS = {
     "last_row_dropped": ("if (h < 0 || h >= H) continue", "if (h < 0 || h >= H - 1) continue"),
     "out_size_off_by_one": ("return span / stride + 1;", "return span / stride;"),
     "single_thread_copy_only": ("for (int t = 0; t < nthreads; ++t) {", "for (int t = 0; t < 1; ++t) {"),
+    "bgrad_last_pixel_dropped": ("for (int64_t l = 0; l < pixels; ++l) {",
+                                 "for (int64_t l = 0; l < pixels - 1; ++l) {"),
+    "bgrad_abs_summed": ("db[k] += (double)g[k];", "db[k] += fabs((double)g[k]);"),
+    "bgrad_signed_denominator": ("absacc[k] += fabs((double)g[k]);", "absacc[k] += (double)g[k];"),
+    "bgrad_channel_stride": ("const float* g = dy + l * K;", "const float* g = dy + (l / K) * K;"),
 }
 
 
