@@ -344,7 +344,9 @@ __global__ __launch_bounds__(256, 3) void grouped16_win_kernel(G16Args a) {
 // kept in registers for the R rows that use it; X row h is read at its S
 // column offsets and multiplied with the A operands of output rows
 // h + pad - r, so every staged element is read from HBM once per slice.
-template <bool kBf16, int R, int S>
+// kDb: also the bias gradient (a separate instantiation keeps the plain
+// kernel's MFMA loop unchanged).
+template <bool kBf16, int R, int S, bool kDb>
 __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
   constexpr int kXPixR = kWoT + S - 1;            // staged X pixels per row
   constexpr int kRows = 2;                        // rows per step (one barrier)
@@ -414,11 +416,6 @@ __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
 #pragma unroll
     for (int i = 0; i < kRows; ++i) fetch_row(kRows * t + i, st.row[i]);
   };
-  // Bias-gradient partial of channels c0 + 8q .. + 7: each dY row of a segment
-  // is fetched by exactly one step (rows outside it, and pixels past the row,
-  // load as zero).
-  const bool want_db = a.dbo != nullptr;
-  float dbp[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   auto store = [&](int buf, const Step& st) {
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
@@ -426,7 +423,6 @@ __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
       if (ps + 32 < kXPixR)
         *reinterpret_cast<uint4*>(&s_x[buf][i][(ps + 32) * kPitchE + 8 * q]) = st.row[i].x1;
       *reinterpret_cast<uint4*>(&s_dy[buf][i][ps * kPitchE + 8 * q]) = st.row[i].d;
-      if (want_db) add8<kBf16>(dbp, st.row[i].d);
     }
   };
 
@@ -439,6 +435,13 @@ __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
   f32x4 acc[R * S];
 #pragma unroll
   for (int t = 0; t < R * S; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Bias gradient: each dY row's A operand (fa[0] when the row enters) times a
+  // B operand of ones gives, in every column, the row's sum per output
+  // channel; every dY row of a segment enters once (rows outside it are zero).
+  f32x4 acc_db = f32x4{0.f, 0.f, 0.f, 0.f};
+  const unsigned short one = kBf16 ? 0x3f80 : 0x3c00;
+  const s16x8 ones{(short)one, (short)one, (short)one, (short)one,
+                   (short)one, (short)one, (short)one, (short)one};
 
   Step pf[kPf];
   int row = r_begin;
@@ -469,6 +472,7 @@ __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
 #pragma unroll
             for (int r = R - 1; r > 0; --r) fa[r] = fa[r - 1];
             fa[0] = tr8(&s_dy[k & 1][i][lane_off]);
+            if constexpr (kDb) acc_db = mfma16<kBf16>(fa[0], ones, acc_db);
             s16x8 fb[S];
 #pragma unroll
             for (int s2 = 0; s2 < S; ++s2) fb[s2] = tr8(&s_x[k & 1][i][s2 * kPitchE + lane_off]);
@@ -486,9 +490,17 @@ __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
     row += seg;
   }
 
-  if (want_db)
-    block_sum64<32, 8>(reinterpret_cast<float*>(sm.out), ps, 8 * q, dbp,
-                       a.dbo + (int64_t)slice * a.slab_stride + c0, min(kCh, a.K - c0));
+  if constexpr (kDb) {
+    // acc_db[v] = db partial of channel c0 + 16*wave + 4*g + v (the same in every column j).
+    if (j == 0) {
+      float* o = a.dbo + (int64_t)slice * a.slab_stride;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int k = c0 + 16 * wave + 4 * g + v;
+        if (k < a.K) o[k] = acc_db[v];
+      }
+    }
+  }
 
   // acc[t][v] = out[k = c0 + 16*wave + 4*g + v][c = c0 + 16*wave + j] for tap t;
   // only same-group pairs are outputs.  They are gathered in LDS (every wave
@@ -541,11 +553,19 @@ hipError_t launch_grouped16(const Plan& plan, const void* x, const void* dy, Sta
   const bool bf = p.dtype == CONV_WGRAD_BF16;
   if (plan.pub.variant == kGrouped16Rows) {
     const dim3 xcd_grid((unsigned)(ceil_div(plan.pub.grid, 8) * 8));
-    if (p.R == 3)
-      return bf ? launch_kernel(grouped16_rows_kernel<true, 3, 3>, xcd_grid, block, a, stream)
-                : launch_kernel(grouped16_rows_kernel<false, 3, 3>, xcd_grid, block, a, stream);
-    return bf ? launch_kernel(grouped16_rows_kernel<true, 1, 1>, xcd_grid, block, a, stream)
-              : launch_kernel(grouped16_rows_kernel<false, 1, 1>, xcd_grid, block, a, stream);
+    const bool db = a.dbo != nullptr;
+    if (p.R == 3) {
+      if (db)
+        return bf ? launch_kernel(grouped16_rows_kernel<true, 3, 3, true>, xcd_grid, block, a, stream)
+                  : launch_kernel(grouped16_rows_kernel<false, 3, 3, true>, xcd_grid, block, a, stream);
+      return bf ? launch_kernel(grouped16_rows_kernel<true, 3, 3, false>, xcd_grid, block, a, stream)
+                : launch_kernel(grouped16_rows_kernel<false, 3, 3, false>, xcd_grid, block, a, stream);
+    }
+    if (db)
+      return bf ? launch_kernel(grouped16_rows_kernel<true, 1, 1, true>, xcd_grid, block, a, stream)
+                : launch_kernel(grouped16_rows_kernel<false, 1, 1, true>, xcd_grid, block, a, stream);
+    return bf ? launch_kernel(grouped16_rows_kernel<true, 1, 1, false>, xcd_grid, block, a, stream)
+              : launch_kernel(grouped16_rows_kernel<false, 1, 1, false>, xcd_grid, block, a, stream);
   }
   if (plan.ru == 4 && p.dil == 1 && p.R == 3 && p.S == 3)
     return bf ? launch_kernel(grouped16_win_kernel<true, 3, 3>, grid, block, a, stream)
