@@ -51,7 +51,8 @@ VARIANT_SOURCE = {0: "dense_lds.hip", 1: "dense_rows.hip", 2: "dense_1x1.hip", 1
                   11: "grouped16.hip", 12: "depthwise_mfma.hip", 13: "grouped16.hip"}
 SHARED_SOURCES = ("device_common.h", "kernels.h", "plan.h", "plan.cpp")
 TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
-CPU_SAMPLE_FLOPS = 1.0e12   # at most ~20 s of oracle work on 16 host cores
+CPU_SAMPLE_FLOPS = 1.0e12   # at most ~20 s of oracle work on 16 host cores per run
+CPU_SAMPLE_SECONDS = 10.0   # runs repeat until about this much oracle time
 
 
 def source_digest(variant):
@@ -143,11 +144,13 @@ def cpu_baseline(wl, x, dy, reps):
     per_image = s.flops() / s.N
     n_s = int(max(1, min(s.N, CPU_SAMPLE_FLOPS // per_image)))
     xs, dys = x[:n_s], dy[:n_s]
+    # At least `reps` runs, and more until about CPU_SAMPLE_SECONDS of oracle work.
     times = []
-    for _ in range(reps):
+    while len(times) < reps or (sum(times) < CPU_SAMPLE_SECONDS and len(times) < 200):
         t0 = time.perf_counter()
         oracle.wgrad_ref(xs, dys, s.R, s.S, s.pad, s.stride, s.dilation, s.groups, nthreads=threads)
         times.append(time.perf_counter() - t0)
+    reps = len(times)
     t = statistics.median(times)
     what = "whole workload" if n_s == s.N else "first %d of %d images" % (n_s, s.N)
     return {"value": round(per_image * n_s / t / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
