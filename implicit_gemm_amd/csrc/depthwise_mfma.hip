@@ -66,7 +66,12 @@ struct DwArgs {
 };
 
 // LDS layout for staged rows of XL columns.
-template <int XL, int RING>
+// Ring rows for RB row blocks: R + 1 rows (the rows of one output row plus the
+// row being staged) rounded up to a power of two.
+template <int RB>
+constexpr int dw_ring() { return RB == 1 ? 4 : RB == 2 ? 8 : 16; }
+
+template <int XL, int RING, int TAPS>
 struct DwLayout {
   static constexpr int kCs = 2 * XL;              // bytes per X channel row
   static constexpr int kXWave = 16 * kCs;         // bytes per wave in a ring slot
@@ -76,7 +81,7 @@ struct DwLayout {
   static constexpr int kDWave = 16 * kDs;
   static constexpr int kDBuf = 64 * kDs;          // bytes per dY buffer
   static constexpr int kDyBase = RING * kSlot;
-  static constexpr int kOut = kQuadCh * 64 * 4;   // output block of 64 channels, up to 8 x 8 taps
+  static constexpr int kOut = kQuadCh * TAPS * 4;  // output block: 64 channels x up to TAPS taps
   static constexpr int kBytes = kDyBase + 2 * kDBuf > kOut ? kDyBase + 2 * kDBuf : kOut;
 };
 
@@ -105,9 +110,9 @@ template <bool kBf16, int RB, int SB, int XL>
 __global__ __launch_bounds__(kThreads) void depthwise_mfma_kernel(DwArgs a) {
   constexpr int NP = XL > 64 ? 2 : 1;   // pixel-pair passes per row
   constexpr int kPf = NP == 1 ? 4 : 2;  // steps fetched ahead (even: dY buffer parity is static)
-  constexpr int RING = RB == 1 ? 4 : 8;
+  constexpr int RING = dw_ring<RB>();
   constexpr int NPAIRS = XL / 8;
-  using L = DwLayout<XL, RING>;
+  using L = DwLayout<XL, RING, 16 * RB * SB>;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const unsigned char* __restrict__ xg = static_cast<const unsigned char*>(a.x);
   const unsigned char* __restrict__ dyg = static_cast<const unsigned char*>(a.dy);
@@ -213,6 +218,8 @@ __global__ __launch_bounds__(kThreads) void depthwise_mfma_kernel(DwArgs a) {
     u32x2 qprev = blk(bp - 8);    // block of step -4
     u32x2 qcur = blk(bp);         // block of step 0
     s16x4 b1 = window(qprev, qcur);                           // s-block 1 of step 0
+    // s-block 2 of step 0 is the s-block-0 window of step -8 (SB = 3 only).
+    s16x4 b2 = SB > 2 ? window(blk(bp - 16), qprev) : b1;
     // Operands of pair pr + 1 are read before the MFMAs of pair pr; the empty
     // asm between pairs also keeps the block reads of different pairs from
     // being merged into ds_read2_b64.
@@ -235,7 +242,9 @@ __global__ __launch_bounds__(kThreads) void depthwise_mfma_kernel(DwArgs a) {
         const s16x4 av = __builtin_bit_cast(s16x4, u32x2{fa[pr][i].x, fa[pr][i].y});
         acc[i][0] = mfma4<kBf16>(av, b0, acc[i][0]);
         if (SB > 1) acc[i][1] = mfma4<kBf16>(av, b1, acc[i][1]);
+        if (SB > 2) acc[i][2] = mfma4<kBf16>(av, b2, acc[i][2]);
       }
+      b2 = b1;
       b1 = b0;
       b0 = window(q1[pr], q2[pr]);
 #pragma unroll
@@ -243,7 +252,9 @@ __global__ __launch_bounds__(kThreads) void depthwise_mfma_kernel(DwArgs a) {
         const s16x4 av = __builtin_bit_cast(s16x4, u32x2{fa[pr][i].z, fa[pr][i].w});
         acc[i][0] = mfma4<kBf16>(av, b0, acc[i][0]);
         if (SB > 1) acc[i][1] = mfma4<kBf16>(av, b1, acc[i][1]);
+        if (SB > 2) acc[i][2] = mfma4<kBf16>(av, b2, acc[i][2]);
       }
+      b2 = b1;
       b1 = b0;
       qcur = q2[pr];
     }
@@ -340,7 +351,7 @@ __global__ __launch_bounds__(kThreads) void depthwise_mfma_kernel(DwArgs a) {
 
 template <bool kBf16, int RB, int SB, int XL>
 hipError_t launch_xl(const DwArgs& args, int64_t grid, hipStream_t stream) {
-  using L = DwLayout<XL, RB == 1 ? 4 : 8>;
+  using L = DwLayout<XL, dw_ring<RB>(), 16 * RB * SB>;
   const void* fn = reinterpret_cast<const void*>(depthwise_mfma_kernel<kBf16, RB, SB, XL>);
   if (L::kBytes > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, L::kBytes);
@@ -369,6 +380,7 @@ template <bool kBf16>
 hipError_t launch_b(const Plan& plan, const DwArgs& a, hipStream_t stream) {
   const int64_t grid = plan.pub.grid;
   const int xl = plan.dw_xl;
+  if (a.R > 8 || a.S > 8) return launch_rs<kBf16, 3, 3>(xl, a, grid, stream);
   const bool r2 = a.R > 4, s2 = a.S > 4;
   if (r2 && s2) return launch_rs<kBf16, 2, 2>(xl, a, grid, stream);
   if (r2) return launch_rs<kBf16, 2, 1>(xl, a, grid, stream);
@@ -378,12 +390,20 @@ hipError_t launch_b(const Plan& plan, const DwArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-// LDS bytes the depthwise kernel uses for a staged row length (0 if unsupported).
-int32_t depthwise_lds_bytes(int32_t xl, int32_t R) {
-  const bool big = R > 4;
+// LDS bytes the depthwise kernel uses for a staged row length and filter size
+// (0 if unsupported).
+int32_t depthwise_lds_bytes(int32_t xl, int32_t R, int32_t S) {
+  const int rb = R > 8 || S > 8 ? 3 : R > 4 ? 2 : 1;
+  const int sb = R > 8 || S > 8 ? 3 : S > 4 ? 2 : 1;
   switch (xl) {
-#define CW_DW_CASE(V) \
-  case V: return big ? DwLayout<V, 8>::kBytes : DwLayout<V, 4>::kBytes;
+#define CW_DW_CASE(V)                                                           \
+  case V:                                                                       \
+    if (rb == 3) return DwLayout<V, dw_ring<3>(), 144>::kBytes;                 \
+    if (rb == 2)                                                                \
+      return sb == 2 ? DwLayout<V, dw_ring<2>(), 64>::kBytes                    \
+                     : DwLayout<V, dw_ring<2>(), 32>::kBytes;                   \
+    return sb == 2 ? DwLayout<V, dw_ring<1>(), 32>::kBytes                      \
+                   : DwLayout<V, dw_ring<1>(), 16>::kBytes;
     CW_DW_CASE(8) CW_DW_CASE(24) CW_DW_CASE(40) CW_DW_CASE(56)
     CW_DW_CASE(72) CW_DW_CASE(88) CW_DW_CASE(104) CW_DW_CASE(120)
 #undef CW_DW_CASE

@@ -214,21 +214,24 @@ bool plan_grouped16_rows(const Problem& p, Plan* out) {
 
 // Depthwise 4x4x4 kernel (depthwise_mfma.hip): 16-bit, one channel per group,
 // stride 1, no dilation, channels in whole 16-channel groups, filter up to
-// 8 x 8, rows of at most 120 columns staged as 8 mod 16 columns, padding up
+// 12 x 12 (blocks of 4 filter rows / columns: 1 or 2 each up to 8 x 8, 3 x 3
+// above), rows of at most 120 columns staged as 8 mod 16 columns, padding up
 // to 12.  A staged dY row holds element 0 at an even column off with
-// 7 <= pad + off <= 12, so every lane's window blocks, from one column step
-// before column 0 to one past the row, lie in the xl + 16 staged columns.
+// 4 * (SB - 1) + 3 <= pad + off <= 12, so every lane's window blocks, from
+// SB - 1 column steps before column 0 to one past the row, lie in the xl + 16
+// staged columns.
 bool plan_depthwise(const Problem& p, Plan* out) {
   if (p.dtype == CONV_WGRAD_F32 || p.Cg != 1 || p.Kg != 1 || p.stride != 1 || p.dil != 1) return false;
-  if (p.C % 16 != 0 || p.C > (1 << 20) || p.R > 8 || p.S > 8 || p.pad > 12) return false;
+  if (p.C % 16 != 0 || p.C > (1 << 20) || p.R > 12 || p.S > 12 || p.pad > 12) return false;
   if (p.W > 120 || p.Wo > 128 || p.W * p.C * 2 > kI32Max) return false;
   int64_t xl = 8;
   while (xl < p.W) xl += 16;
   const int64_t np = xl > 64 ? 2 : 1;
-  int64_t off = (8 - p.pad) & ~(int64_t)1;
+  const bool blocks3 = p.R > 8 || p.S > 8;        // 3 x 3 filter blocks
+  int64_t off = ((blocks3 ? 12 : 8) - p.pad) & ~(int64_t)1;
   if (off < 0) off = 0;
   if (p.Wo > 64 * np || 2 * ceil_div(p.Wo, 2) + off > xl + 16) return false;
-  const int32_t lds = depthwise_lds_bytes((int32_t)xl, (int32_t)p.R);
+  const int32_t lds = depthwise_lds_bytes((int32_t)xl, (int32_t)p.R, (int32_t)p.S);
   if (lds <= 0 || lds > kDwLdsMax) return false;
   out->dw_xl = (int32_t)xl;
   out->dw_lds = lds;

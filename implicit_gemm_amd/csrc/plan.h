@@ -63,9 +63,9 @@ inline int64_t db_offset(const Problem& p) { return ceil_div(p.E, 4) * 4; }
 // Validate and canonicalise desc.  Returns CONV_WGRAD_OK or the error code.
 conv_wgrad_status_t canonicalise(const conv_wgrad_desc_t* desc, Problem* out);
 
-// LDS bytes of the depthwise kernel for staged rows of xl columns and R filter
-// rows (0 if xl is not a supported length); defined with the kernel.
-int32_t depthwise_lds_bytes(int32_t xl, int32_t R);
+// LDS bytes of the depthwise kernel for staged rows of xl columns and an R x S
+// filter (0 if xl is not a supported length); defined with the kernel.
+int32_t depthwise_lds_bytes(int32_t xl, int32_t R, int32_t S);
 
 // Build the full plan (calls canonicalise).
 conv_wgrad_status_t make_plan(const conv_wgrad_desc_t* desc, Plan* out);

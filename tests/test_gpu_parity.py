@@ -229,6 +229,15 @@ SMALL_GROUP_CASES = [
     (wd.ConvShape(3, 16, 4, 33, 16, 6, 2, pad=1, groups=16), "f16", 4),       # odd Wo
     (wd.ConvShape(3, 384, 14, 14, 384, 7, 7, pad=3, groups=384), "bf16", 5),  # slices across images
     (wd.ConvShape(2, 16, 6, 10, 16, 3, 3, pad=12, groups=16), "f16", 3),      # pad 12: zero X rows > R - 1
+    # depthwise with 3 x 3 blocks of filter rows / columns (R or S above 8)
+    (wd.ConvShape(2, 16, 12, 20, 16, 9, 9, pad=4, groups=16), "bf16", 3),
+    (wd.ConvShape(2, 32, 14, 40, 32, 11, 11, pad=5, groups=32), "f16", -1),
+    (wd.ConvShape(3, 16, 9, 11, 16, 12, 12, pad=6, groups=16), "bf16", 2),
+    (wd.ConvShape(2, 16, 9, 30, 16, 11, 3, pad=5, groups=16), "f16", 2),     # R > 8 only
+    (wd.ConvShape(2, 16, 9, 30, 16, 3, 11, pad=5, groups=16), "bf16", -1),   # S > 8 only
+    (wd.ConvShape(2, 16, 6, 8, 16, 10, 10, pad=12, groups=16), "f16", 1),    # Ho, Wo > H, W
+    (wd.ConvShape(2, 48, 12, 12, 48, 9, 9, pad=0, groups=48), "bf16", -1),   # Ho = Wo = 4, 3 blocks of 16
+    (wd.ConvShape(3, 64, 20, 50, 64, 11, 11, pad=5, groups=64), "bf16", 4),  # 56-column rows
     # grouped 16-bit, row-streaming path (stride 1, 1x1 / 3x3, Wo <= 32)
     (wd.ConvShape(3, 64, 9, 32, 64, 3, 3, pad=1, groups=16), "f16", -1),      # Wo = 32, cpg4
     (wd.ConvShape(2, 48, 7, 13, 48, 3, 3, pad=0, groups=6), "bf16", 3),       # cpg8, pad 0, partial block
