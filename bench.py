@@ -47,7 +47,8 @@ DEFAULT_CONFIG = "c2_3x3_f32"
 # Stage-1 kernel source of each plan variant; with the shared headers and the
 # planner it identifies the code a counter measurement was taken on.
 CSRC = os.path.join(ROOT, "implicit_gemm_amd", "csrc")
-VARIANT_SOURCE = {0: "dense_lds.hip", 1: "dense_rows.hip", 2: "dense_1x1.hip", 10: "direct_elem.hip",
+VARIANT_SOURCE = {0: "dense_lds.hip", 1: "dense_rows.hip", 2: "dense_1x1.hip", 3: "dense16_rows.hip",
+                  10: "direct_elem.hip",
                   11: "grouped16.hip", 12: "depthwise_mfma.hip", 13: "grouped16.hip"}
 SHARED_SOURCES = ("device_common.h", "kernels.h", "plan.h", "plan.cpp")
 TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "hbm_traffic.md")

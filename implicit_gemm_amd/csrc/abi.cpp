@@ -111,6 +111,7 @@ conv_wgrad_status_t run(const conv_wgrad_desc_t* desc, const void* x, const void
     case cw::kDepthwise: err = cw::launch_depthwise(plan, x, dy, out, s); break;
     case cw::kDenseRows: err = cw::launch_dense_rows(plan, x, dy, out, s); break;
     case cw::kDense1x1: err = cw::launch_dense_1x1(plan, x, dy, out, s); break;
+    case cw::kDense16Rows: err = cw::launch_dense16_rows(plan, x, dy, out, s); break;
     default: err = cw::launch_dense(plan, x, dy, out, s); break;
   }
   if (err != hipSuccess) return CONV_WGRAD_ERR_HIP;

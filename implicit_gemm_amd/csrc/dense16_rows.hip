@@ -1,0 +1,275 @@
+// Dense implicit-GEMM weight gradient for 16-bit inputs on 16x16x32 MFMA (gfx950).
+//
+// The GEMM of the dense kernels (per group: M = Kg output channels,
+// N = R*S*Cg columns, reduction over the output pixels), with bf16 / fp16
+// operands on v_mfma_f32_16x16x32_{bf16,f16} and fp32 accumulation, for
+// stride 1 and dilation 1:
+//
+//   * a reduction unit is a run of up to 64 output pixels of one output row;
+//     a workgroup tile is (group, 64 output channels, filter row r, SB
+//     consecutive taps, 64 input channels), as in the fp32 row kernel;
+//   * the unit's 64 dY pixels and the 68 X pixels the taps need are staged in
+//     LDS in their NHWC order (64 channels per pixel, 160-byte pixel pitch)
+//     by 16-byte buffer loads whose range supplies the zero padding;
+//   * the MFMA operands hold 8 consecutive pixels of one channel per lane, a
+//     transpose of that layout, which ds_read_b64_tr_b16 does on the read:
+//     within a 16-lane group lane j points at 4 channels of pixel j / 4 and
+//     lane i receives channel i of 4 consecutive pixels.  Tap s's B operand is
+//     the X segment read s pixels further on: an address offset;
+//   * wave w owns input channels 16w .. 16w + 15 of the tile and all 64 output
+//     channels: 4 A operands (dY) and SB B operands (X) per 32 pixels feed
+//     4 * SB accumulators;
+//   * two LDS buffers alternate: a unit is staged while the previous one is
+//     computed, one barrier per unit.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace cw {
+
+namespace {
+
+constexpr int kPitchE = 80;      // 16-bit elements per staged pixel (64 channels + pad)
+constexpr int kWt = 64;          // dY pixels staged per unit (two 32-pixel k-steps)
+constexpr int kXs = 68;          // X pixels staged per unit (64 + up to 3 tap shifts, all rows initialised)
+constexpr int kDyChunks = kWt * 8 / 256;                  // 16-byte loads per lane for dY
+constexpr int kXChunks = (kXs * 8 + 255) / 256;           // and for X
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+struct R16Args {
+  const void* x;
+  const void* dy;
+  float* out;
+  int64_t slab_stride;
+  int64_t x_img;   // H*W*C
+  int32_t H, W, C, K, Ho, Wo, R, S, pad;
+  int32_t Cg, Kg, cols;
+  int32_t m_tiles, c_tiles, s_blocks;
+  int32_t wt, wchunks;
+  int32_t units, units_per_slice, ks_count;
+  int32_t tiles, work;
+  float* dbo;      // bias-gradient partial of slice 0 (slab_stride apart), or nullptr
+};
+
+__device__ __forceinline__ s16x4 tr_read(const unsigned short* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
+
+template <bool kBf16>
+__device__ __forceinline__ f32x4 mfma16(s16x8 a, s16x8 b, f32x4 c) {
+  if constexpr (kBf16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// kDb: also the bias gradient (a separate instantiation).
+template <bool kBf16, int SB, bool kDb>
+__global__ __launch_bounds__(256) void dense16_rows_kernel(R16Args a) {
+  __shared__ __attribute__((aligned(16))) unsigned short s_dy[2][kWt * kPitchE];
+  __shared__ __attribute__((aligned(16))) unsigned short s_x[2][kXs * kPitchE];
+  const unsigned char* __restrict__ xg = static_cast<const unsigned char*>(a.x);
+  const unsigned char* __restrict__ dyg = static_cast<const unsigned char*>(a.dy);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Work item w = slice * tiles + tile; XCD x (block b runs on XCD b % 8)
+  // takes a contiguous run of items, so the tiles of a slice share one L2.
+  const int per_xcd = (a.work + 7) >> 3;
+  const int w = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if ((int)(blockIdx.x >> 3) >= per_xcd || w >= a.work) return;
+  const int slice = w / a.tiles;
+  int tile = w % a.tiles;
+  const int ct = tile % a.c_tiles;
+  tile /= a.c_tiles;
+  const int sb = tile % a.s_blocks;
+  tile /= a.s_blocks;
+  const int r = tile % a.R;
+  tile /= a.R;
+  const int mt = tile % a.m_tiles;
+  const int g = tile / a.m_tiles;
+  const int m0 = mt * 64, c0 = ct * 64, s0 = sb * SB;
+  const int u_begin = slice * a.units_per_slice;
+  const int u_end = min(a.units, u_begin + a.units_per_slice);
+
+  // Loader role: chunk t + 256 i = (pixel (t + 256 i) / 8, 8 channels at 8 * (t % 8)).
+  const int q8 = tid & 7, px0 = tid >> 3;
+  const int dy_col0 = g * a.Kg + m0;
+  const int x_col0 = g * a.Cg + c0;
+  const int x_row_bytes = (a.W * a.C - x_col0) * 2;
+  uint4 rdy[kDyChunks], rx[kXChunks];
+  int npix_next = 0;
+  auto load_unit = [&](int u) {
+    const int wc = u % a.wchunks;
+    const int t = u / a.wchunks;
+    const int ho = t % a.Ho, n = t / a.Ho;
+    const int wo0 = wc * a.wt;
+    const int npix = min(a.wt, a.Wo - wo0);
+    npix_next = npix;
+    const unsigned char* dyp = dyg + 2 * (((int64_t)(n * a.Ho + ho) * a.Wo + wo0) * a.K + dy_col0);
+    const __amdgpu_buffer_rsrc_t rd = buf_rsrc(dyp, (npix * a.K - dy_col0) * 2);
+#pragma unroll
+    for (int i = 0; i < kDyChunks; ++i)
+      rdy[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             rd, ((px0 + 32 * i) * a.K + 8 * q8) * 2, 0, 0));
+    const int h = ho + r - a.pad;
+    const bool row_ok = h >= 0 && h < a.H;
+    const unsigned char* xp = xg + 2 * ((int64_t)n * a.x_img + (int64_t)(row_ok ? h : 0) * a.W * a.C + x_col0);
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(xp, row_ok ? x_row_bytes : 0);
+    const int w0 = wo0 - a.pad + s0;   // first staged X column (negative: padding, reads zero)
+#pragma unroll
+    for (int i = 0; i < kXChunks; ++i)
+      rx[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rs, ((w0 + px0 + 32 * i) * a.C + 8 * q8) * 2, 0, 0));
+  };
+  auto store_unit = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kDyChunks; ++i)
+      *reinterpret_cast<uint4*>(&s_dy[buf][(px0 + 32 * i) * kPitchE + 8 * q8]) = rdy[i];
+#pragma unroll
+    for (int i = 0; i < kXChunks; ++i)
+      if (px0 + 32 * i < kXs)
+        *reinterpret_cast<uint4*>(&s_x[buf][(px0 + 32 * i) * kPitchE + 8 * q8]) = rx[i];
+  };
+
+  // Transposed-read addressing: in 16-lane group gq, lane j points at pixel
+  // 8 gq + j / 4 (+ 4 for the upper half of the k-step) and 4 channels at 4 (j % 4).
+  const int j = lane & 15, gq = lane >> 4;
+  const int lane_off = (8 * gq + (j >> 2)) * kPitchE + 4 * (j & 3);
+  auto tr8 = [&](const unsigned short* p) {
+    return __builtin_shufflevector(tr_read(p), tr_read(p + 4 * kPitchE), 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+
+  f32x4 acc[4][SB];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int s = 0; s < SB; ++s) acc[i][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Bias gradient: in the tile with the first filter row, tap block and input
+  // channel block, wave 0 multiplies each A operand by ones (every column of
+  // the product is the per-channel sum of the operand's 32 pixels).
+  const bool db_wave = kDb && r == 0 && sb == 0 && ct == 0 && wave == 0;
+  f32x4 acc_db[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc_db[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const unsigned short one = kBf16 ? 0x3f80 : 0x3c00;
+  const s16x8 ones{(short)one, (short)one, (short)one, (short)one,
+                   (short)one, (short)one, (short)one, (short)one};
+
+  auto compute_unit = [&](int buf, int npix) {
+    const unsigned short* ad = s_dy[buf] + lane_off;
+    const unsigned short* bx = s_x[buf] + lane_off + 16 * wave;
+#pragma unroll
+    for (int ks = 0; ks < kWt / 32; ++ks) {
+      if (32 * ks < npix) {
+        s16x8 fa[4], fb[SB];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[i] = tr8(ad + 32 * ks * kPitchE + 16 * i);
+#pragma unroll
+        for (int s = 0; s < SB; ++s) fb[s] = tr8(bx + (32 * ks + s) * kPitchE);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int s = 0; s < SB; ++s) acc[i][s] = mfma16<kBf16>(fa[i], fb[s], acc[i][s]);
+        if constexpr (kDb) {
+          if (db_wave) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc_db[i] = mfma16<kBf16>(fa[i], ones, acc_db[i]);
+          }
+        }
+      }
+    }
+  };
+
+  if (u_begin < u_end) load_unit(u_begin);
+  for (int u = u_begin; u < u_end; ++u) {
+    const int buf = (u - u_begin) & 1;
+    const int npix = npix_next;
+    store_unit(buf);
+    if (u + 1 < u_end) load_unit(u + 1);
+    __syncthreads();   // the unit is staged; every wave is done with the other buffer
+    compute_unit(buf, npix);
+  }
+
+  // acc[i][s][v] = dW[g*Kg + m0 + 16 i + 4 gq + v][(r*S + s0 + s)*Cg + c0 + 16 wave + j].
+  float* out = a.out + (int64_t)slice * a.slab_stride;
+  const int c = c0 + 16 * wave + j;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = m0 + 16 * i + 4 * gq + v;
+      if (m < a.Kg && c < a.Cg) {
+        float* o = out + ((int64_t)g * a.Kg + m) * a.cols + (int64_t)(r * a.S + s0) * a.Cg + c;
+#pragma unroll
+        for (int s = 0; s < SB; ++s)
+          if (s0 + s < a.S) o[(int64_t)s * a.Cg] = acc[i][s][v];
+      }
+    }
+  if (db_wave && j == 0) {
+    float* o = a.dbo + (int64_t)slice * a.slab_stride + (int64_t)g * a.Kg;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = m0 + 16 * i + 4 * gq + v;
+        if (m < a.Kg) o[m] = acc_db[i][v];
+      }
+  }
+}
+
+template <bool kBf16, int SB>
+hipError_t launch_sb(const R16Args& args, int64_t grid, hipStream_t stream) {
+  const dim3 xcd_grid((unsigned)((grid + 7) / 8 * 8)), block(256);   // whole rounds over the 8 XCDs
+  if (args.dbo) return launch_kernel(dense16_rows_kernel<kBf16, SB, true>, xcd_grid, block, args, stream);
+  return launch_kernel(dense16_rows_kernel<kBf16, SB, false>, xcd_grid, block, args, stream);
+}
+
+template <bool kBf16>
+hipError_t launch_b(const Plan& plan, const R16Args& args, hipStream_t stream) {
+  const int64_t grid = plan.pub.grid;
+  switch (plan.sb) {
+    case 1: return launch_sb<kBf16, 1>(args, grid, stream);
+    case 2: return launch_sb<kBf16, 2>(args, grid, stream);
+    case 3: return launch_sb<kBf16, 3>(args, grid, stream);
+    default: return launch_sb<kBf16, 4>(args, grid, stream);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_dense16_rows(const Plan& plan, const void* x, const void* dy, Stage1Out out,
+                               hipStream_t stream) {
+  const Problem& p = plan.p;
+  R16Args a;
+  a.x = x;
+  a.dy = dy;
+  a.out = out.base;
+  a.slab_stride = out.slab_stride;
+  a.dbo = out.db;
+  a.x_img = p.x_img;
+  a.H = (int32_t)p.H; a.W = (int32_t)p.W; a.C = (int32_t)p.C; a.K = (int32_t)p.K;
+  a.Ho = (int32_t)p.Ho; a.Wo = (int32_t)p.Wo;
+  a.R = (int32_t)p.R; a.S = (int32_t)p.S; a.pad = (int32_t)p.pad;
+  a.Cg = (int32_t)p.Cg; a.Kg = (int32_t)p.Kg; a.cols = (int32_t)p.cols;
+  a.m_tiles = (int32_t)plan.m_tiles;
+  a.c_tiles = (int32_t)plan.c_tiles;
+  a.s_blocks = (int32_t)plan.s_blocks;
+  a.wt = plan.wt;
+  a.wchunks = (int32_t)plan.wchunks;
+  a.units = (int32_t)plan.pub.units;
+  a.units_per_slice = (int32_t)plan.pub.units_per_slice;
+  a.ks_count = plan.pub.ks_count;
+  a.tiles = (int32_t)plan.pub.tiles;
+  a.work = (int32_t)(plan.pub.tiles * plan.pub.ks_count);
+  if (p.dtype == CONV_WGRAD_BF16) return launch_b<true>(plan, a, stream);
+  return launch_b<false>(plan, a, stream);
+}
+
+}  // namespace cw

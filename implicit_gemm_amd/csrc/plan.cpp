@@ -79,7 +79,7 @@ conv_wgrad_status_t canonicalise(const conv_wgrad_desc_t* d, Problem* o) {
 
 conv_wgrad_status_t choose_split(int64_t units, int64_t tiles, int32_t requested, int64_t min_units,
                                  int64_t target_groups, int64_t traffic_div, const Problem& p,
-                                 conv_wgrad_plan_t* pub, int64_t forced_ups) {
+                                 conv_wgrad_plan_t* pub, int64_t forced_ups, int64_t traffic_mul) {
   int64_t degree;
   if (forced_ups >= 1) {
     degree = ceil_div(units, forced_ups < units ? forced_ups : units);
@@ -92,7 +92,7 @@ conv_wgrad_status_t choose_split(int64_t units, int64_t tiles, int32_t requested
     if (degree > by_depth) degree = by_depth;
     uint64_t alg = p.x_bytes + p.dy_bytes + p.dw_bytes;
     uint64_t slab = (uint64_t)p.E * 8u;  // 4 bytes written + 4 bytes read per slab element
-    int64_t by_traffic = (int64_t)(alg / ((uint64_t)traffic_div * slab));
+    int64_t by_traffic = (int64_t)(alg * (uint64_t)traffic_mul / ((uint64_t)traffic_div * slab));
     if (by_traffic < 1) by_traffic = 1;
     if (degree > by_traffic) degree = by_traffic;
     if (degree < 1) degree = 1;
@@ -212,6 +212,22 @@ bool plan_grouped16_rows(const Problem& p, Plan* out) {
   return true;
 }
 
+// 16-bit dense row kernel (dense16_rows.hip): stride 1, dilation 1, channel
+// counts in whole 16-byte chunks (8 channels); units of up to 64 output pixels
+// (32 when the output row is that short), up to 4 taps per tile.
+bool plan_dense16_rows(const Problem& p, Plan* out) {
+  if (p.dtype == CONV_WGRAD_F32 || p.stride != 1 || p.dil != 1) return false;
+  if (p.C % 8 != 0 || p.K % 8 != 0 || p.Cg % 8 != 0 || p.Kg % 8 != 0) return false;
+  if (p.W * p.C * 2 > kI32Max / 2 || p.Wo * p.K * 2 > kI32Max / 2) return false;
+  out->sb = (int32_t)(p.S < 4 ? p.S : 4);
+  out->wt = p.Wo > 32 ? 64 : 32;
+  out->s_blocks = ceil_div(p.S, out->sb);
+  out->c_tiles = ceil_div(p.Cg, 64);
+  out->m_tiles = ceil_div(p.Kg, 64);
+  out->wchunks = ceil_div(p.Wo, out->wt);
+  return true;
+}
+
 // Depthwise 4x4x4 kernel (depthwise_mfma.hip): 16-bit, one channel per group,
 // stride 1, no dilation, channels in whole 16-channel groups, filter up to
 // 12 x 12 (blocks of 4 filter rows / columns: 1 or 2 each up to 8 x 8, 3 x 3
@@ -320,6 +336,19 @@ conv_wgrad_status_t make_plan(const conv_wgrad_desc_t* desc, Plan* out) {
     if (!mul3(p.groups, out->m_tiles, out->c_tiles, &tiles)) return CONV_WGRAD_ERR_UNSUPPORTED;
     // One-wave workgroups, about eight per CU.
     return choose_split(ceil_div(p.L, 64), tiles, desc->split_k, 4, 2048, 4, p, &pub);
+  }
+  if (plan_dense16_rows(p, out)) {
+    pub.variant = kDense16Rows;
+    pub.unit_rows = out->wt;
+    int64_t units, tiles;
+    if (!mul3(p.N, p.Ho, out->wchunks, &units)) return CONV_WGRAD_ERR_UNSUPPORTED;
+    if (!mul4(p.groups, out->m_tiles, p.R, out->s_blocks, &tiles) ||
+        !mul_ok(tiles, out->c_tiles, &tiles))
+      return CONV_WGRAD_ERR_UNSUPPORTED;
+    // Three 256-lane workgroups fit per CU (42 KB of LDS each), two per CU
+    // are targeted.  A unit costs the same time whatever the MFMA work, so
+    // slices are worth up to 4x the algorithmic bytes in slab traffic.
+    return choose_split(units, tiles, desc->split_k, 2, 512, 1, p, &pub, 0, 4);
   }
   if (plan_dense_rows(p, out)) {
     pub.variant = kDenseRows;

@@ -18,6 +18,7 @@ enum Variant : int32_t {
   kDenseLds = 0,      // dense implicit GEMM, LDS-staged tiles, f32 MFMA 16x16x4 (any geometry)
   kDenseRows = 1,     // dense implicit GEMM over output-row units, per-filter-row tiles
   kDense1x1 = 2,      // 1x1 stride-1 unpadded fp32: rows streamed into MFMA registers
+  kDense16Rows = 3,   // 16-bit dense, stride 1, dilation 1: row units on 16x16x32 bf16/fp16 MFMA
   kDirectElem = 10,   // direct small-group kernel, one dW element per lane
   kGrouped16 = 11,    // 16-bit small groups: block-diagonal 16x16x32 MFMA, transposed LDS reads
   kDepthwise = 12,    // 16-bit depthwise: batched 4x4x4 MFMA, 64 channels per workgroup
@@ -77,10 +78,11 @@ conv_wgrad_status_t make_plan(const conv_wgrad_desc_t* desc, Plan* out);
 // Auto degree: floor(target_groups / tiles) slices (so the grid never exceeds
 // target_groups), at most units / min_units, and with the slab traffic
 // (each slab element written once and read once) at most the algorithmic
-// bytes divided by traffic_div.  forced_ups >= 1 fixes the units per slice
-// instead (the degree follows from it).
+// bytes times traffic_mul / traffic_div.  forced_ups >= 1 fixes the units per
+// slice instead (the degree follows from it).
 conv_wgrad_status_t choose_split(int64_t units, int64_t tiles, int32_t requested, int64_t min_units,
                                  int64_t target_groups, int64_t traffic_div, const Problem& p,
-                                 conv_wgrad_plan_t* pub, int64_t forced_ups = 0);
+                                 conv_wgrad_plan_t* pub, int64_t forced_ups = 0,
+                                 int64_t traffic_mul = 1);
 
 }  // namespace cw
