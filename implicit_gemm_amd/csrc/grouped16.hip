@@ -351,16 +351,19 @@ __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
   constexpr int kXPixR = kWoT + S - 1;            // staged X pixels per row
   constexpr int kRows = 2;                        // rows per step (one barrier)
   constexpr int kPf = 2;                          // steps fetched ahead (even)
-  constexpr int kOut = kCh * R * S * 16;          // largest output block (16 channels per group)
-  // The row tiles, and after the last row the workgroup's output block.
-  union Smem {
-    struct {
-      unsigned short x[2][kRows][kXPixR * kPitchE];
-      unsigned short dy[2][kRows][kWoT * kPitchE];
-    } t;
-    float4 out[kOut / 4];
+  // The output block (16 channels per group at most) is gathered in LDS when
+  // it fits in the row tiles (1x1, 3x3); larger filters store it directly.
+  struct Tiles {
+    unsigned short x[2][kRows][kXPixR * kPitchE];
+    unsigned short dy[2][kRows][kWoT * kPitchE];
   };
-  static_assert(sizeof(Smem) == sizeof(Smem::t), "the output block fits in the row tiles");
+  constexpr int kOut = kCh * R * S * 16;
+  constexpr bool kStageOut = kOut * 4 <= (int)sizeof(Tiles);
+  union Smem {
+    Tiles t;
+    float4 out[kStageOut ? kOut / 4 : 1];
+  };
+  static_assert(sizeof(Smem) == sizeof(Tiles), "the output block fits in the row tiles");
   __shared__ __attribute__((aligned(16))) Smem sm;
   auto& s_x = sm.t.x;
   auto& s_dy = sm.t.dy;
@@ -509,6 +512,21 @@ __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
   // block of min(64, K - c0) output channels as whole 16-byte stores.
   constexpr int kTaps = R * S;
   const int Cg = a.Cg;
+  if constexpr (!kStageOut) {
+    float* out = a.out + (int64_t)slice * a.slab_stride;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int k = c0 + 16 * wave + 4 * g + v;
+      const int c = c0 + 16 * wave + j;
+      if (k < a.K && (4 * g + v) / Cg == j / Cg) {
+        float* o = out + (int64_t)k * kTaps * Cg + j % Cg;
+#pragma unroll
+        for (int t = 0; t < kTaps; ++t) o[t * Cg] = acc[t][v];
+      }
+      (void)c;
+    }
+    return;
+  }
   float* s_out = reinterpret_cast<float*>(sm.out);
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
@@ -554,6 +572,17 @@ hipError_t launch_grouped16(const Plan& plan, const void* x, const void* dy, Sta
   if (plan.pub.variant == kGrouped16Rows) {
     const dim3 xcd_grid((unsigned)(ceil_div(plan.pub.grid, 8) * 8));
     const bool db = a.dbo != nullptr;
+#define CW_G16R(RR)                                                                              \
+    if (p.R == RR) {                                                                             \
+      if (db)                                                                                    \
+        return bf ? launch_kernel(grouped16_rows_kernel<true, RR, RR, true>, xcd_grid, block, a, stream) \
+                  : launch_kernel(grouped16_rows_kernel<false, RR, RR, true>, xcd_grid, block, a, stream); \
+      return bf ? launch_kernel(grouped16_rows_kernel<true, RR, RR, false>, xcd_grid, block, a, stream)   \
+                : launch_kernel(grouped16_rows_kernel<false, RR, RR, false>, xcd_grid, block, a, stream); \
+    }
+    CW_G16R(5)
+    CW_G16R(7)
+#undef CW_G16R
     if (p.R == 3) {
       if (db)
         return bf ? launch_kernel(grouped16_rows_kernel<true, 3, 3, true>, xcd_grid, block, a, stream)

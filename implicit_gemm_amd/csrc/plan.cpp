@@ -200,13 +200,13 @@ bool plan_grouped16(const Problem& p, Plan* out) {
 }
 
 // Row-streaming grouped kernel (grouped16.hip): as the block-diagonal kernel,
-// plus stride 1, no dilation, a 1x1 or 3x3 filter and output rows of at most
+// plus stride 1, no dilation, a 1x1, 3x3, 5x5 or 7x7 filter and output rows of at most
 // 32 pixels (one MFMA k-step); padding below the filter size.
 bool plan_grouped16_rows(const Problem& p, Plan* out) {
   if (p.dtype == CONV_WGRAD_F32 || p.stride != 1 || p.dil != 1 || p.Cg != p.Kg || 16 % p.Cg != 0)
     return false;
   if (p.C % 16 != 0 || p.Wo > 32 || p.pad >= p.S || p.pad >= p.R) return false;
-  if (!((p.R == 3 && p.S == 3) || (p.R == 1 && p.S == 1))) return false;
+  if (p.R != p.S || !(p.R == 1 || p.R == 3 || p.R == 5 || p.R == 7)) return false;
   if (p.W * p.C * 2 > kI32Max / 2 || p.Wo * p.K * 2 > kI32Max / 2) return false;
   out->c_tiles = ceil_div(p.C, 64);
   return true;
@@ -293,20 +293,22 @@ conv_wgrad_status_t make_plan(const conv_wgrad_desc_t* desc, Plan* out) {
     int64_t units;
     if (!mul_ok(p.N, p.Ho, &units)) return CONV_WGRAD_ERR_UNSUPPORTED;
     // Four-wave workgroups, about one per CU, each streaming long runs of rows.
-    if (desc->split_k >= 1) return choose_split(units, out->c_tiles, desc->split_k, 8, 256, 4, p, &pub);
+    // Slabs may cost up to half the algorithmic bytes (the larger filters
+    // have large slabs, and a half-empty device costs more).
+    if (desc->split_k >= 1) return choose_split(units, out->c_tiles, desc->split_k, 8, 256, 2, p, &pub);
     // A slice that straddles two images restarts the row pipeline (and
-    // re-reads R - 1 halo rows), so the automatic slice length is rounded up
-    // to whole images, or to a divisor of an image's rows.
+    // re-reads R - 1 halo rows), so the automatic slice length is rounded to
+    // the nearest whole number of images, or up to a divisor of an image's rows.
     conv_wgrad_plan_t probe = pub;
-    st = choose_split(units, out->c_tiles, -1, 8, 256, 4, p, &probe);
+    st = choose_split(units, out->c_tiles, -1, 8, 256, 2, p, &probe);
     if (st != CONV_WGRAD_OK) return st;
     int64_t ups = probe.units_per_slice;
     if (ups >= p.Ho) {
-      ups = ceil_div(ups, p.Ho) * p.Ho;
+      ups = (ups + p.Ho / 2) / p.Ho * p.Ho;
     } else {
       while (p.Ho % ups != 0) ++ups;
     }
-    return choose_split(units, out->c_tiles, -1, 8, 256, 4, p, &pub, ups);
+    return choose_split(units, out->c_tiles, -1, 8, 256, 2, p, &pub, ups);
   }
   if (small_groups && plan_grouped16(p, out)) {
     pub.path = CONV_WGRAD_PATH_DIRECT;

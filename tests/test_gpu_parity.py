@@ -244,6 +244,10 @@ SMALL_GROUP_CASES = [
     (wd.ConvShape(4, 128, 5, 1, 128, 3, 3, pad=1, groups=128), "f16", 5),     # cpg1, one column
     (wd.ConvShape(2, 64, 6, 20, 64, 1, 1, pad=0, groups=4), "bf16", -1),      # cpg16, 1x1
     (wd.ConvShape(5, 32, 3, 7, 32, 3, 3, pad=1, groups=16), "bf16", 4),       # cpg2, slices across images
+    (wd.ConvShape(3, 64, 12, 28, 64, 5, 5, pad=2, groups=16), "f16", -1),     # 5x5 cpg4
+    (wd.ConvShape(2, 128, 9, 32, 128, 5, 5, pad=4, groups=16), "bf16", 3),    # 5x5 cpg8, pad R - 1
+    (wd.ConvShape(3, 64, 10, 20, 64, 7, 7, pad=3, groups=4), "bf16", 2),      # 7x7 cpg16
+    (wd.ConvShape(2, 48, 7, 13, 48, 7, 7, pad=0, groups=12), "f16", -1),      # 7x7 cpg4, pad 0, partial block
     # grouped 16-bit: windowed 3x3 / 1x1 paths and the generic path (dilation, 2x2)
     (wd.ConvShape(3, 64, 10, 37, 64, 3, 3, pad=1, groups=16), "f16", -1),
     (wd.ConvShape(2, 128, 9, 9, 128, 1, 1, pad=0, groups=16), "bf16", 3),
