@@ -190,9 +190,9 @@ def main():
     import wgrad_data as wd
 
     if args.digest:
-        s = wd.WORKLOADS[args.config].shape
+        s = wd.workload(args.config).shape
         d = iga.make_desc(s.N, s.C, s.H, s.W, s.K, s.R, s.S, s.pad, s.stride, s.dilation, s.groups,
-                          {"f32": 0, "bf16": 1, "f16": 2}[wd.WORKLOADS[args.config].dtype], args.split_k)
+                          {"f32": 0, "bf16": 1, "f16": 2}[wd.workload(args.config).dtype], args.split_k)
         v = int(iga.get_plan(d).variant)
         print(json.dumps({"workload": args.config, "variant": v, "source": VARIANT_SOURCE[v],
                           "digest": source_digest(v)}))
@@ -209,7 +209,7 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": src.numel() * 4, "copies": 3}))
         return 0
-    wl = wd.WORKLOADS[args.config]
+    wl = wd.workload(args.config)
     s = wl.shape
     if s.N > 64 and wl.n_sweep:
         s = s.with_n(64)

@@ -59,6 +59,7 @@ struct DwArgs {
   int64_t slab_stride;
   int64_t x_img, dy_img;   // elements per image
   int32_t H, W, C, Ho, Wo, R, S, pad;
+  int32_t stride;          // 1 or 2 (both axes)
   int32_t dy_off;          // column of dY element 0 in a staged dY row
   int32_t rows, rows_per_slice, ks_count;  // rows = N * Ho
   int32_t quads;           // ceil(C / 64)
@@ -165,10 +166,23 @@ __global__ __launch_bounds__(kThreads) void depthwise_mfma_kernel(DwArgs a) {
       }
     }
   };
+  // Stride 2 stages each dY row upsampled (element wo at column 2 wo, zeros
+  // between), so that the column-step windows below are those of stride 1.
+  unsigned char* const dw2 = lds + L::kDyBase + 2 * o * L::kDs + 2 * a.dy_off + 8 * pp;
   auto store_dy = [&](int buf, const Item<NP>& it) {
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       if (2 * (pp + 32 * p) < a.Wo) {
+        if (a.stride == 2) {
+          unsigned char* d = dw2 + buf * L::kDBuf + 256 * p;
+#pragma unroll
+          for (int cc = 0; cc < 8; ++cc) {
+            const uint32_t v = chan(it.p[p][0], it.p[p][1], cc);
+            *reinterpret_cast<u32x2*>(d + (cc & 3) * L::kDWave + (cc >> 2) * L::kDs) =
+                u32x2{v & 0xffffu, v >> 16};
+          }
+          continue;
+        }
         unsigned char* d = dw0 + buf * L::kDBuf + 128 * p;
 #pragma unroll
         for (int cc = 0; cc < 8; ++cc)
@@ -211,7 +225,7 @@ __global__ __launch_bounds__(kThreads) void depthwise_mfma_kernel(DwArgs a) {
   auto compute_row = [&](int ho, int buf) {
     const unsigned char* ap[RB];
 #pragma unroll
-    for (int i = 0; i < RB; ++i) ap[i] = xr + ((ho - a.pad + 4 * i + q) & (RING - 1)) * L::kSlot;
+    for (int i = 0; i < RB; ++i) ap[i] = xr + ((a.stride * ho - a.pad + 4 * i + q) & (RING - 1)) * L::kSlot;
     lds_cu8* bp = bq + buf * L::kDBuf;
     lds_cu8* bp4 = bq4 + buf * L::kDBuf;
     auto blk = [](lds_cu8* ptr) { return *reinterpret_cast<__attribute__((address_space(3))) const u32x2*>(ptr); };
@@ -280,15 +294,19 @@ __global__ __launch_bounds__(kThreads) void depthwise_mfma_kernel(DwArgs a) {
   while (row < r_end) {
     const int n = row / a.Ho, ho0 = row % a.Ho;
     const int seg = min(r_end - row, a.Ho - ho0);
-    const int steps = seg + a.R - 1;
+    const int steps = a.stride * (seg - 1) + a.R;  // X rows of the segment
     const int last = ho0 + seg;                    // first output row past the segment
+    const int h0 = a.stride * ho0 - a.pad;         // X row of step 0
+    // Step t stages X row h0 + t and, when u = t - (R - 1) is a non-negative
+    // multiple of the stride, dY row ho0 + u / stride, which it then computes.
     auto fetch_step = [&](int t, Item<NP>& ix, Item<NP>& id) {
-      const int h = ho0 - a.pad + t;
+      const int h = h0 + t;
       const bool x_in = h >= 0 && h < a.H && t < steps;
       const int64_t ex = (int64_t)n * a.x_img + (int64_t)(x_in ? h : 0) * a.W * a.C + c0;
       fetch(row_rsrc(xg + 2 * ex, x_in ? row_bytes_x : 0), ix);
-      const int ho = ho0 + t - (a.R - 1);
-      const bool d_in = ho >= ho0 && ho < last;
+      const int u = t - (a.R - 1);
+      const int ho = ho0 + (a.stride == 2 ? u >> 1 : u);
+      const bool d_in = u >= 0 && (u & (a.stride - 1)) == 0 && ho < last;
       const int64_t ed = (int64_t)n * a.dy_img + (int64_t)(d_in ? ho : ho0) * a.Wo * a.C + c0;
       fetch(row_rsrc(dyg + 2 * ed, d_in ? row_bytes_dy : 0), id);
     };
@@ -298,7 +316,7 @@ __global__ __launch_bounds__(kThreads) void depthwise_mfma_kernel(DwArgs a) {
 #pragma unroll
       for (int k = 0; k < kPf; ++k) {
         const int tk = t + k;
-        store_x((ho0 - a.pad + tk) & (RING - 1), qx[k]);
+        store_x((h0 + tk) & (RING - 1), qx[k]);
         store_dy(k & 1, qd[k]);
         if (want_db) {
           // Each dY row of the segment is staged by exactly one step; rows
@@ -311,8 +329,9 @@ __global__ __launch_bounds__(kThreads) void depthwise_mfma_kernel(DwArgs a) {
         }
         fetch_step(tk + kPf, qx[k], qd[k]);
         lds_barrier();
-        if (tk >= a.R - 1 && tk < steps) {
-          compute_row(ho0 + tk - (a.R - 1), k & 1);
+        const int u = tk - (a.R - 1);
+        if (u >= 0 && (u & (a.stride - 1)) == 0 && tk < steps) {
+          compute_row(ho0 + (a.stride == 2 ? u >> 1 : u), k & 1);
           if (guard_ring) lds_barrier();
         }
       }
@@ -424,6 +443,7 @@ hipError_t launch_depthwise(const Plan& plan, const void* x, const void* dy, Sta
   a.H = (int32_t)p.H; a.W = (int32_t)p.W; a.C = (int32_t)p.C;
   a.Ho = (int32_t)p.Ho; a.Wo = (int32_t)p.Wo;
   a.R = (int32_t)p.R; a.S = (int32_t)p.S; a.pad = (int32_t)p.pad;
+  a.stride = (int32_t)p.stride;
   a.dy_off = plan.dw_off;
   a.rows = (int32_t)(p.N * p.Ho);
   a.rows_per_slice = (int32_t)plan.pub.units_per_slice;

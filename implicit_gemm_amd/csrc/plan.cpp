@@ -236,17 +236,32 @@ bool plan_dense16_rows(const Problem& p, Plan* out) {
 // 4 * (SB - 1) + 3 <= pad + off <= 12, so every lane's window blocks, from
 // SB - 1 column steps before column 0 to one past the row, lie in the xl + 16
 // staged columns.
+//
+// Stride 2 (filters up to 8 x 8) stages each dY row upsampled, element wo at
+// column off + 2 wo with zeros between, so the column windows are those of
+// stride 1 on an output row twice as long; off is then a multiple of 4 (the
+// stores of a pixel pair are 8-byte aligned).  X rows advance two per output
+// row.
 bool plan_depthwise(const Problem& p, Plan* out) {
-  if (p.dtype == CONV_WGRAD_F32 || p.Cg != 1 || p.Kg != 1 || p.stride != 1 || p.dil != 1) return false;
+  if (p.dtype == CONV_WGRAD_F32 || p.Cg != 1 || p.Kg != 1 || p.dil != 1) return false;
+  if (p.stride != 1 && p.stride != 2) return false;
   if (p.C % 16 != 0 || p.C > (1 << 20) || p.R > 12 || p.S > 12 || p.pad > 12) return false;
   if (p.W > 120 || p.Wo > 128 || p.W * p.C * 2 > kI32Max) return false;
   int64_t xl = 8;
   while (xl < p.W) xl += 16;
   const int64_t np = xl > 64 ? 2 : 1;
   const bool blocks3 = p.R > 8 || p.S > 8;        // 3 x 3 filter blocks
-  int64_t off = ((blocks3 ? 12 : 8) - p.pad) & ~(int64_t)1;
-  if (off < 0) off = 0;
-  if (p.Wo > 64 * np || 2 * ceil_div(p.Wo, 2) + off > xl + 16) return false;
+  if (p.stride == 2 && blocks3) return false;
+  int64_t off;
+  if (p.stride == 2) {
+    off = 0;
+    while (p.pad + off < 7) off += 4;
+  } else {
+    off = ((blocks3 ? 12 : 8) - p.pad) & ~(int64_t)1;
+    if (off < 0) off = 0;
+  }
+  const int64_t staged = p.stride * 2 * ceil_div(p.Wo, 2);   // dY columns the pixel pairs cover
+  if (p.Wo > 64 * np || staged + off > xl + 16) return false;
   const int32_t lds = depthwise_lds_bytes((int32_t)xl, (int32_t)p.R, (int32_t)p.S);
   if (lds <= 0 || lds > kDwLdsMax) return false;
   out->dw_xl = (int32_t)xl;

@@ -35,6 +35,7 @@ BIAS_CASES = [
     (wd.ConvShape(3, 384, 14, 14, 384, 7, 7, pad=3, groups=384), "bf16", 3),  # depthwise, 6 channel blocks
     (wd.ConvShape(2, 80, 6, 120, 80, 3, 3, pad=1, groups=80), "f16", 1),       # depthwise, 2 pixel passes
     (wd.ConvShape(2, 32, 14, 40, 32, 11, 11, pad=5, groups=32), "bf16", 3),    # depthwise, 3 x 3 filter blocks
+    (wd.ConvShape(2, 48, 23, 100, 48, 7, 7, pad=3, stride=2, groups=48), "f16", 2),  # depthwise stride 2
     (wd.ConvShape(3, 64, 9, 32, 64, 3, 3, pad=1, groups=16), "f16", -1),       # grouped rows
     (wd.ConvShape(2, 48, 7, 13, 48, 3, 3, pad=0, groups=6), "bf16", 3),        # grouped rows, partial block
     (wd.ConvShape(3, 64, 10, 20, 64, 7, 7, pad=3, groups=16), "f16", 2),       # grouped rows 7x7

@@ -229,6 +229,13 @@ SMALL_GROUP_CASES = [
     (wd.ConvShape(3, 16, 4, 33, 16, 6, 2, pad=1, groups=16), "f16", 4),       # odd Wo
     (wd.ConvShape(3, 384, 14, 14, 384, 7, 7, pad=3, groups=384), "bf16", 5),  # slices across images
     (wd.ConvShape(2, 16, 6, 10, 16, 3, 3, pad=12, groups=16), "f16", 3),      # pad 12: zero X rows > R - 1
+    # depthwise stride 2 (dY rows staged upsampled; X rows advance two per output row)
+    (wd.ConvShape(2, 16, 9, 11, 16, 3, 3, pad=1, stride=2, groups=16), "bf16", 2),
+    (wd.ConvShape(2, 32, 20, 40, 32, 5, 5, pad=2, stride=2, groups=32), "f16", -1),
+    (wd.ConvShape(3, 16, 15, 17, 16, 8, 8, pad=4, stride=2, groups=16), "bf16", 1),   # R = 8: ring guard
+    (wd.ConvShape(2, 48, 23, 100, 48, 7, 7, pad=3, stride=2, groups=48), "bf16", 3),  # two pixel passes
+    (wd.ConvShape(2, 16, 12, 13, 16, 4, 2, pad=0, stride=2, groups=16), "f16", -1),   # even R, pad 0, odd W
+    (wd.ConvShape(4, 64, 7, 7, 64, 3, 3, pad=1, stride=2, groups=64), "bf16", 3),     # slices across images
     # depthwise with 3 x 3 blocks of filter rows / columns (R or S above 8)
     (wd.ConvShape(2, 16, 12, 20, 16, 9, 9, pad=4, groups=16), "bf16", 3),
     (wd.ConvShape(2, 32, 14, 40, 32, 11, 11, pad=5, groups=32), "f16", -1),

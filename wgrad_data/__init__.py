@@ -177,4 +177,43 @@ WORKLOADS = {
         note="1x1 fp32, C=96 K=64 H=W=512, N swept", n_sweep=(43, 64, 96, 128, 192)),
 }
 
+# Geometry variants of the same operation (stride, dilation, larger depthwise
+# and grouped filters, 16-bit dense), measured beside the five workloads.
+def _geo(name, shape, dtype, seed, note):
+    return Workload(name, shape, dtype, Dist("normal", 1.0), Dist("normal", 0.1), seed=seed, note=note)
+
+
+GEOMETRY = {w.name: w for w in [
+    _geo("g_dw3x3_bf16", ConvShape(64, 384, 56, 56, 384, 3, 3, pad=1, groups=384), "bf16", 101,
+         "depthwise 3x3 bf16, N=64 C=384 56x56 pad 1"),
+    _geo("g_dw5x5_bf16", ConvShape(64, 384, 56, 56, 384, 5, 5, pad=2, groups=384), "bf16", 102,
+         "depthwise 5x5 bf16, N=64 C=384 56x56 pad 2"),
+    _geo("g_dw11x11_bf16", ConvShape(64, 384, 56, 56, 384, 11, 11, pad=5, groups=384), "bf16", 103,
+         "depthwise 11x11 bf16, N=64 C=384 56x56 pad 5"),
+    _geo("g_dw7x7_s2_bf16", ConvShape(16, 384, 112, 112, 384, 7, 7, pad=3, stride=2, groups=384), "bf16", 104,
+         "depthwise 7x7 stride 2 bf16, N=16 C=384 112x112 pad 3"),
+    _geo("g_3x3_s2_f32", ConvShape(32, 64, 112, 112, 64, 3, 3, pad=1, stride=2), "f32", 105,
+         "3x3 stride 2 fp32, N=32 C=K=64 112x112 pad 1"),
+    _geo("g_3x3_d2_f32", ConvShape(32, 64, 56, 56, 64, 3, 3, pad=2, dilation=2), "f32", 106,
+         "3x3 dilation 2 fp32, N=32 C=K=64 56x56 pad 2"),
+    _geo("g_3x3_bf16", ConvShape(32, 64, 56, 56, 64, 3, 3, pad=1), "bf16", 107,
+         "3x3 bf16, N=32 C=K=64 56x56 pad 1"),
+    _geo("g_3x3_c256_bf16", ConvShape(64, 256, 14, 14, 256, 3, 3, pad=1), "bf16", 108,
+         "3x3 bf16, N=64 C=K=256 14x14 pad 1"),
+    _geo("g_grp5x5_cpg4_f16", ConvShape(64, 256, 28, 28, 256, 5, 5, pad=2, groups=64), "f16", 109,
+         "grouped 5x5 fp16, 4 ch/group, N=64 C=K=256 28x28 pad 2"),
+    _geo("g_grp3x3_cpg4_56_f16", ConvShape(32, 256, 56, 56, 256, 3, 3, pad=1, groups=64), "f16", 110,
+         "grouped 3x3 fp16, 4 ch/group, N=32 C=K=256 56x56 pad 1"),
+    _geo("g_grp3x3_s2_f16", ConvShape(64, 256, 56, 56, 256, 3, 3, pad=1, stride=2, groups=64), "f16", 111,
+         "grouped 3x3 stride 2 fp16, 4 ch/group, N=64 C=K=256 56x56 pad 1"),
+]}
+
+
+def workload(name: str) -> Workload:
+    """A workload of the study or a geometry variant, by name."""
+    if name in WORKLOADS:
+        return WORKLOADS[name]
+    return GEOMETRY[name]
+
+
 IN_BYTES = {"f32": 4, "bf16": 2, "f16": 2}
