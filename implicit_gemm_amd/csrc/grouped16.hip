@@ -334,6 +334,59 @@ __global__ __launch_bounds__(256, 3) void grouped16_win_kernel(G16Args a) {
   }
 }
 
+// Epilogue of the row-streaming grouped kernels: the bias partial (kDb) and the
+// block-diagonal outputs.  acc[t][v] = out[k = c0 + 16*wave + 4*g + v]
+// [c = c0 + 16*wave + j] for tap t; only same-group pairs are outputs.  With
+// kStageOut they are gathered in `scratch` (LDS, free: every wave has passed
+// the last barrier after its last tile read) in the [k][tap][c % Cg] order of
+// the output, so that the workgroup writes its block of min(64, K - c0)
+// output channels as whole 16-byte stores; otherwise they are stored directly.
+template <int kTaps, bool kDb, bool kStageOut>
+__device__ __forceinline__ void rows_epilogue(const G16Args& a, const f32x4 (&acc)[kTaps], f32x4 acc_db,
+                                              int slice, int c0, float4* scratch) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j = lane & 15, g = lane >> 4;
+  if constexpr (kDb) {
+    // acc_db[v] = db partial of channel c0 + 16*wave + 4*g + v (the same in every column j).
+    if (j == 0) {
+      float* o = a.dbo + (int64_t)slice * a.slab_stride;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int k = c0 + 16 * wave + 4 * g + v;
+        if (k < a.K) o[k] = acc_db[v];
+      }
+    }
+  }
+
+  const int Cg = a.Cg;
+  if constexpr (!kStageOut) {
+    float* out = a.out + (int64_t)slice * a.slab_stride;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int k = c0 + 16 * wave + 4 * g + v;
+      if (k < a.K && (4 * g + v) / Cg == j / Cg) {
+        float* o = out + (int64_t)k * kTaps * Cg + j % Cg;
+#pragma unroll
+        for (int t = 0; t < kTaps; ++t) o[t * Cg] = acc[t][v];
+      }
+    }
+    return;
+  }
+  float* s_out = reinterpret_cast<float*>(scratch);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int kl = 16 * wave + 4 * g + v;
+    if ((4 * g + v) / Cg == j / Cg) {
+#pragma unroll
+      for (int t = 0; t < kTaps; ++t) s_out[(kl * kTaps + t) * Cg + j % Cg] = acc[t][v];
+    }
+  }
+  __syncthreads();
+  const int n4 = min(kCh, a.K - c0) * kTaps * Cg / 4;
+  float4* out = reinterpret_cast<float4*>(a.out + (int64_t)slice * a.slab_stride + (int64_t)c0 * kTaps * Cg);
+  for (int i = tid; i < n4; i += 256) out[i] = scratch[i];
+}
+
 // Row-streaming path for stride 1, dilation 1, Wo <= 32 and a compile-time
 // R x S filter.  A workgroup owns 64 channels and a slice of output rows of
 // one image at a time.  Each step brings kRows X rows (34 pixels with the
@@ -493,53 +546,155 @@ __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
     row += seg;
   }
 
-  if constexpr (kDb) {
-    // acc_db[v] = db partial of channel c0 + 16*wave + 4*g + v (the same in every column j).
-    if (j == 0) {
-      float* o = a.dbo + (int64_t)slice * a.slab_stride;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int k = c0 + 16 * wave + 4 * g + v;
-        if (k < a.K) o[k] = acc_db[v];
-      }
-    }
-  }
-
-  // acc[t][v] = out[k = c0 + 16*wave + 4*g + v][c = c0 + 16*wave + j] for tap t;
-  // only same-group pairs are outputs.  They are gathered in LDS (every wave
-  // has passed the last barrier above, after its last tile read) in the
-  // [k][tap][c % Cg] order of the output, so that the workgroup writes its
-  // block of min(64, K - c0) output channels as whole 16-byte stores.
   constexpr int kTaps = R * S;
-  const int Cg = a.Cg;
-  if constexpr (!kStageOut) {
-    float* out = a.out + (int64_t)slice * a.slab_stride;
+  rows_epilogue<kTaps, kDb, kStageOut>(a, acc, acc_db, slice, c0, reinterpret_cast<float4*>(&sm));
+}
+
+
+// Row-streaming path for stride 2 (dilation 1, Wo <= 32, compile-time R x S).
+// Output row ho reads X rows 2 ho - pad + r, so each step brings two X rows
+// and one dY row: X row 2t + i (i = 0, 1) of the segment meets the filter
+// rows r with r = i mod 2, whose dY rows t - (r - i) / 2 have A operands in a
+// shift register of (R + 1) / 2 rows.  Tap s reads X column 2 wo - pad + s:
+// the X rows are staged de-interleaved (even and odd staged columns in two
+// regions), so that the 32 pixels of one tap are consecutive in one region
+// and the transposed reads work as for stride 1.
+template <bool kBf16, int R, int S, bool kDb>
+__global__ __launch_bounds__(256) void grouped16_rows_s2_kernel(G16Args a) {
+  constexpr int kReg = kWoT + (S - 1) / 2;        // pixels per parity region
+  constexpr int kXCols = 2 * kReg;                // staged X columns -pad .. -pad + kXCols - 1
+  constexpr int kPf = 2;
+  constexpr int kNA = (R + 1) / 2;                // dY rows in flight per X row pair
+  struct Tiles {
+    unsigned short x[2][2][kXCols * kPitchE];     // [buffer][row of the pair][region * kReg + index]
+    unsigned short dy[2][kWoT * kPitchE];
+  };
+  constexpr int kOut = kCh * R * S * 16;
+  constexpr bool kStageOut = kOut * 4 <= (int)sizeof(Tiles);
+  __shared__ __attribute__((aligned(16))) Tiles sm;
+  auto& s_x = sm.x;
+  auto& s_dy = sm.dy;
+  const unsigned char* __restrict__ xg = static_cast<const unsigned char*>(a.x);
+  const unsigned char* __restrict__ dyg = static_cast<const unsigned char*>(a.dy);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int work = a.c_blocks * a.ks_count;
+  const int per_xcd = (work + 7) >> 3;
+  const int w = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (w >= work) return;
+  const int cb = w % a.c_blocks;
+  const int slice = w / a.c_blocks;
+  const int c0 = cb * kCh;
+  const int r_begin = slice * a.units_per_slice;
+  const int r_end = min(a.units, r_begin + a.units_per_slice);   // units are output rows
+
+  // Loader role: staged columns ps, ps + 32, ps + 64, 16-byte chunk q.
+  const int q = tid & 7, ps = tid >> 3;
+  const int x_row_bytes = (a.W * a.C - c0) * 2;
+  const int dy_row_bytes = (a.Wo * a.K - c0) * 2;
+  int ox[3];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int k = c0 + 16 * wave + 4 * g + v;
-      const int c = c0 + 16 * wave + j;
-      if (k < a.K && (4 * g + v) / Cg == j / Cg) {
-        float* o = out + (int64_t)k * kTaps * Cg + j % Cg;
+  for (int i = 0; i < 3; ++i)
+    ox[i] = ps + 32 * i < kXCols ? ((ps + 32 * i - a.pad) * a.C + 8 * q) * 2 : 0x7fffffff;
+  const int ody = (ps * a.K + 8 * q) * 2;
+  struct Step {
+    uint4 x[2][3], d;
+  };
+  int n = 0, ho0 = 0, ho_hi = 0, rows_x = 0;
+  // Step t: X rows 2 ho0 - pad + 2t + i of the segment, dY row ho0 + t.
+  auto fetch = [&](int t, Step& st) {
 #pragma unroll
-        for (int t = 0; t < kTaps; ++t) o[t * Cg] = acc[t][v];
+    for (int i = 0; i < 2; ++i) {
+      const int u = 2 * t + i;
+      const int h = 2 * ho0 - a.pad + u;
+      const bool x_in = h >= 0 && h < a.H && u < rows_x;
+      const __amdgpu_buffer_rsrc_t rx =
+          buf_rsrc(xg + 2 * ((int64_t)n * a.x_img + (int64_t)(x_in ? h : 0) * a.W * a.C + c0),
+                   x_in ? x_row_bytes : 0);
+#pragma unroll
+      for (int k = 0; k < 3; ++k)
+        st.x[i][k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, ox[k], 0, 0));
+    }
+    const int ho = ho0 + t;
+    const bool d_in = ho < ho_hi;
+    const __amdgpu_buffer_rsrc_t rd =
+        buf_rsrc(dyg + 2 * (((int64_t)n * a.Ho + (d_in ? ho : ho0)) * a.Wo * a.K + c0),
+                 d_in ? dy_row_bytes : 0);
+    st.d = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rd, ody, 0, 0));
+  };
+  auto store = [&](int buf, const Step& st) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const int col = ps + 32 * k;   // staged column: region col & 1, index col >> 1
+        if (col < kXCols)
+          *reinterpret_cast<uint4*>(&s_x[buf][i][((col & 1) * kReg + (col >> 1)) * kPitchE + 8 * q]) =
+              st.x[i][k];
       }
-      (void)c;
-    }
-    return;
-  }
-  float* s_out = reinterpret_cast<float*>(sm.out);
+    *reinterpret_cast<uint4*>(&s_dy[buf][ps * kPitchE + 8 * q]) = st.d;
+  };
+
+  const int j = lane & 15, g = lane >> 4;
+  const int lane_off = (8 * g + (j >> 2)) * kPitchE + 16 * wave + 4 * (j & 3);
+  auto tr8 = [&](const unsigned short* p) {
+    return __builtin_shufflevector(tr_read(p), tr_read(p + 4 * kPitchE), 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+
+  f32x4 acc[R * S];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int kl = 16 * wave + 4 * g + v;
-    if ((4 * g + v) / Cg == j / Cg) {
+  for (int t = 0; t < R * S; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 acc_db = f32x4{0.f, 0.f, 0.f, 0.f};
+  const unsigned short one = kBf16 ? 0x3f80 : 0x3c00;
+  const s16x8 ones{(short)one, (short)one, (short)one, (short)one,
+                   (short)one, (short)one, (short)one, (short)one};
+
+  Step pf[kPf];
+  int row = r_begin;
+  while (row < r_end) {
+    n = row / a.Ho;
+    ho0 = row % a.Ho;
+    const int seg = min(r_end - row, a.Ho - ho0);
+    ho_hi = ho0 + seg;
+    rows_x = 2 * (seg - 1) + R;   // X rows 2 ho0 - pad .. 2 (ho0 + seg - 1) - pad + R - 1
+    const int steps = (rows_x + 1) / 2;
+    // fa[m] = A operand of dY row ho0 + t - m (zero before the segment).
+    s16x8 fa[kNA];
 #pragma unroll
-      for (int t = 0; t < kTaps; ++t) s_out[(kl * kTaps + t) * Cg + j % Cg] = acc[t][v];
+    for (int m = 0; m < kNA; ++m) fa[m] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < kPf; ++k) fetch(k, pf[k]);
+    for (int t = 0; t < steps; t += kPf) {
+#pragma unroll
+      for (int k = 0; k < kPf; ++k) {
+        const int tk = t + k;
+        store(k & 1, pf[k]);
+        fetch(tk + kPf, pf[k]);
+        lds_barrier();
+        if (tk < steps) {
+#pragma unroll
+          for (int m = kNA - 1; m > 0; --m) fa[m] = fa[m - 1];
+          fa[0] = tr8(&s_dy[k & 1][lane_off]);
+          if constexpr (kDb) acc_db = mfma16<kBf16>(fa[0], ones, acc_db);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            s16x8 fb[S];
+#pragma unroll
+            for (int s2 = 0; s2 < S; ++s2)
+              fb[s2] = tr8(&s_x[k & 1][i][((s2 & 1) * kReg + (s2 >> 1)) * kPitchE + lane_off]);
+#pragma unroll
+            for (int r = i; r < R; r += 2)
+#pragma unroll
+              for (int s2 = 0; s2 < S; ++s2)
+                acc[r * S + s2] = mfma16<kBf16>(fa[(r - i) / 2], fb[s2], acc[r * S + s2]);
+          }
+        }
+      }
     }
+    lds_barrier();
+    row += seg;
   }
-  __syncthreads();
-  const int n4 = min(kCh, a.K - c0) * kTaps * Cg / 4;
-  float4* out = reinterpret_cast<float4*>(a.out + (int64_t)slice * a.slab_stride + (int64_t)c0 * kTaps * Cg);
-  for (int i = tid; i < n4; i += 256) out[i] = sm.out[i];
+  rows_epilogue<R * S, kDb, kStageOut>(a, acc, acc_db, slice, c0, reinterpret_cast<float4*>(&sm));
 }
 
 }  // namespace
@@ -572,6 +727,22 @@ hipError_t launch_grouped16(const Plan& plan, const void* x, const void* dy, Sta
   if (plan.pub.variant == kGrouped16Rows) {
     const dim3 xcd_grid((unsigned)(ceil_div(plan.pub.grid, 8) * 8));
     const bool db = a.dbo != nullptr;
+    if (p.stride == 2) {
+#define CW_G16S2(RR)                                                                                \
+      if (p.R == RR) {                                                                              \
+        if (db)                                                                                     \
+          return bf ? launch_kernel(grouped16_rows_s2_kernel<true, RR, RR, true>, xcd_grid, block, a, stream)  \
+                    : launch_kernel(grouped16_rows_s2_kernel<false, RR, RR, true>, xcd_grid, block, a, stream); \
+        return bf ? launch_kernel(grouped16_rows_s2_kernel<true, RR, RR, false>, xcd_grid, block, a, stream)    \
+                  : launch_kernel(grouped16_rows_s2_kernel<false, RR, RR, false>, xcd_grid, block, a, stream);  \
+      }
+      CW_G16S2(1)
+      CW_G16S2(3)
+      CW_G16S2(5)
+      CW_G16S2(7)
+#undef CW_G16S2
+      return hipErrorInvalidValue;
+    }
 #define CW_G16R(RR)                                                                              \
     if (p.R == RR) {                                                                             \
       if (db)                                                                                    \

@@ -200,10 +200,11 @@ bool plan_grouped16(const Problem& p, Plan* out) {
 }
 
 // Row-streaming grouped kernel (grouped16.hip): as the block-diagonal kernel,
-// plus stride 1, no dilation, a 1x1, 3x3, 5x5 or 7x7 filter and output rows of at most
+// plus stride 1 or 2, no dilation, a 1x1, 3x3, 5x5 or 7x7 filter and output rows of at most
 // 32 pixels (one MFMA k-step); padding below the filter size.
 bool plan_grouped16_rows(const Problem& p, Plan* out) {
-  if (p.dtype == CONV_WGRAD_F32 || p.stride != 1 || p.dil != 1 || p.Cg != p.Kg || 16 % p.Cg != 0)
+  if (p.dtype == CONV_WGRAD_F32 || (p.stride != 1 && p.stride != 2) || p.dil != 1 || p.Cg != p.Kg ||
+      16 % p.Cg != 0)
     return false;
   if (p.C % 16 != 0 || p.Wo > 32 || p.pad >= p.S || p.pad >= p.R) return false;
   if (p.R != p.S || !(p.R == 1 || p.R == 3 || p.R == 5 || p.R == 7)) return false;

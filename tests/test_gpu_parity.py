@@ -252,6 +252,13 @@ SMALL_GROUP_CASES = [
     (wd.ConvShape(2, 64, 6, 20, 64, 1, 1, pad=0, groups=4), "bf16", -1),      # cpg16, 1x1
     (wd.ConvShape(5, 32, 3, 7, 32, 3, 3, pad=1, groups=16), "bf16", 4),       # cpg2, slices across images
     (wd.ConvShape(3, 64, 12, 28, 64, 5, 5, pad=2, groups=16), "f16", -1),     # 5x5 cpg4
+    # grouped, stride 2 (X rows staged de-interleaved, two X rows per dY row)
+    (wd.ConvShape(2, 64, 13, 29, 64, 3, 3, pad=1, stride=2, groups=16), "f16", 2),     # cpg4
+    (wd.ConvShape(3, 128, 16, 64, 128, 3, 3, pad=1, stride=2, groups=16), "bf16", -1), # cpg8, Wo = 32
+    (wd.ConvShape(2, 48, 11, 21, 48, 1, 1, pad=0, stride=2, groups=12), "bf16", 3),    # 1x1, partial block
+    (wd.ConvShape(2, 64, 14, 30, 64, 5, 5, pad=2, stride=2, groups=64), "f16", -1),    # 5x5 cpg1
+    (wd.ConvShape(3, 32, 9, 17, 32, 7, 7, pad=3, stride=2, groups=8), "bf16", 2),      # 7x7 cpg4
+    (wd.ConvShape(4, 64, 6, 10, 64, 3, 3, pad=0, stride=2, groups=16), "f16", 3),      # pad 0, slices across images
     (wd.ConvShape(2, 128, 9, 32, 128, 5, 5, pad=4, groups=16), "bf16", 3),    # 5x5 cpg8, pad R - 1
     (wd.ConvShape(3, 64, 10, 20, 64, 7, 7, pad=3, groups=4), "bf16", 2),      # 7x7 cpg16
     (wd.ConvShape(2, 48, 7, 13, 48, 7, 7, pad=0, groups=12), "f16", -1),      # 7x7 cpg4, pad 0, partial block
