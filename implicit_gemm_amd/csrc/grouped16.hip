@@ -387,7 +387,7 @@ __device__ __forceinline__ void rows_epilogue(const G16Args& a, const f32x4 (&ac
   for (int i = tid; i < n4; i += 256) out[i] = scratch[i];
 }
 
-// Row-streaming path for stride 1, dilation 1, Wo <= 32 and a compile-time
+// Row-streaming path for stride 1, dilation 1, Wo <= 64 and a compile-time
 // R x S filter.  A workgroup owns 64 channels and a slice of output rows of
 // one image at a time.  Each step brings kRows X rows (34 pixels with the
 // padding columns) and kRows dY rows into LDS (double-buffered, one barrier
@@ -399,16 +399,17 @@ __device__ __forceinline__ void rows_epilogue(const G16Args& a, const f32x4 (&ac
 // h + pad - r, so every staged element is read from HBM once per slice.
 // kDb: also the bias gradient (a separate instantiation keeps the plain
 // kernel's MFMA loop unchanged).
-template <bool kBf16, int R, int S, bool kDb>
+template <bool kBf16, int R, int S, bool kDb, int WT>
 __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
-  constexpr int kXPixR = kWoT + S - 1;            // staged X pixels per row
+  constexpr int kXPixR = WT + S - 1;              // staged X pixels per row
+  constexpr int kKs = WT / 32;                    // 32-pixel MFMA k-steps per row
   constexpr int kRows = 2;                        // rows per step (one barrier)
   constexpr int kPf = 2;                          // steps fetched ahead (even)
   // The output block (16 channels per group at most) is gathered in LDS when
   // it fits in the row tiles (1x1, 3x3); larger filters store it directly.
   struct Tiles {
     unsigned short x[2][kRows][kXPixR * kPitchE];
-    unsigned short dy[2][kRows][kWoT * kPitchE];
+    unsigned short dy[2][kRows][WT * kPitchE];
   };
   constexpr int kOut = kCh * R * S * 16;
   constexpr bool kStageOut = kOut * 4 <= (int)sizeof(Tiles);
@@ -438,15 +439,20 @@ __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
   const int r_begin = slice * a.units_per_slice;
   const int r_end = min(a.units, r_begin + a.units_per_slice);   // units are output rows
 
-  // Loader role: pixel slot ps (and ps + 32 for the X halo), 16-byte chunk q.
+  // Loader role: pixel slots ps + 32 i (X: kNX passes with the halo; dY:
+  // kKs passes), 16-byte chunk q.
+  constexpr int kNX = (kXPixR + 31) / 32;
   const int q = tid & 7, ps = tid >> 3;
   const int x_row_bytes = (a.W * a.C - c0) * 2;
   const int dy_row_bytes = (a.Wo * a.K - c0) * 2;
-  const int ox0 = ((ps - a.pad) * a.C + 8 * q) * 2;               // negative: zero (padding)
-  const int ox1 = ps + 32 < kXPixR ? ((ps + 32 - a.pad) * a.C + 8 * q) * 2 : 0x7fffffff;
-  const int ody = (ps * a.K + 8 * q) * 2;
+  int ox[kNX], ody[kKs];
+#pragma unroll
+  for (int i = 0; i < kNX; ++i)   // negative offsets (padding) and offsets past the range read zero
+    ox[i] = ps + 32 * i < kXPixR ? ((ps + 32 * i - a.pad) * a.C + 8 * q) * 2 : 0x7fffffff;
+#pragma unroll
+  for (int i = 0; i < kKs; ++i) ody[i] = ((ps + 32 * i) * a.K + 8 * q) * 2;
   struct Row {
-    uint4 x0, x1, d;
+    uint4 x[kNX], d[kKs];
   };
   struct Step {
     Row row[kRows];
@@ -459,14 +465,17 @@ __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
     const __amdgpu_buffer_rsrc_t rx =
         buf_rsrc(xg + 2 * ((int64_t)n * a.x_img + (int64_t)(x_in ? h : 0) * a.W * a.C + c0),
                  x_in ? x_row_bytes : 0);
-    st.x0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, ox0, 0, 0));
-    st.x1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, ox1, 0, 0));
+#pragma unroll
+    for (int i = 0; i < kNX; ++i)
+      st.x[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, ox[i], 0, 0));
     const int ho = ho0 + u;
     const bool d_in = ho < ho_hi;
     const __amdgpu_buffer_rsrc_t rd =
         buf_rsrc(dyg + 2 * (((int64_t)n * a.Ho + (d_in ? ho : ho0)) * a.Wo * a.K + c0),
                  d_in ? dy_row_bytes : 0);
-    st.d = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rd, ody, 0, 0));
+#pragma unroll
+    for (int i = 0; i < kKs; ++i)
+      st.d[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rd, ody[i], 0, 0));
   };
   auto fetch = [&](int t, Step& st) {
 #pragma unroll
@@ -475,10 +484,13 @@ __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
   auto store = [&](int buf, const Step& st) {
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
-      *reinterpret_cast<uint4*>(&s_x[buf][i][ps * kPitchE + 8 * q]) = st.row[i].x0;
-      if (ps + 32 < kXPixR)
-        *reinterpret_cast<uint4*>(&s_x[buf][i][(ps + 32) * kPitchE + 8 * q]) = st.row[i].x1;
-      *reinterpret_cast<uint4*>(&s_dy[buf][i][ps * kPitchE + 8 * q]) = st.row[i].d;
+#pragma unroll
+      for (int x = 0; x < kNX; ++x)
+        if (ps + 32 * x < kXPixR)
+          *reinterpret_cast<uint4*>(&s_x[buf][i][(ps + 32 * x) * kPitchE + 8 * q]) = st.row[i].x[x];
+#pragma unroll
+      for (int x = 0; x < kKs; ++x)
+        *reinterpret_cast<uint4*>(&s_dy[buf][i][(ps + 32 * x) * kPitchE + 8 * q]) = st.row[i].d[x];
     }
   };
 
@@ -508,10 +520,12 @@ __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
     ho_hi = ho0 + seg;
     rows_x = seg + R - 1;     // X rows ho0 - pad .. ho0 + seg - 1 - pad + R - 1
     const int steps = (rows_x + kRows - 1) / kRows;
-    // A operands of dY rows ho0 + u - r, r = 0..R-1 (zero before the segment).
-    s16x8 fa[R];
+    // A operands of dY rows ho0 + u - r, r = 0..R-1, per k-step (zero before the segment).
+    s16x8 fa[R][kKs];
 #pragma unroll
-    for (int r = 0; r < R; ++r) fa[r] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int kk = 0; kk < kKs; ++kk) fa[r][kk] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int k = 0; k < kPf; ++k) fetch(k, pf[k]);
     for (int t = 0; t < steps; t += kPf) {
@@ -526,17 +540,23 @@ __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
 #pragma unroll
           for (int i = 0; i < kRows; ++i) {
 #pragma unroll
-            for (int r = R - 1; r > 0; --r) fa[r] = fa[r - 1];
-            fa[0] = tr8(&s_dy[k & 1][i][lane_off]);
-            if constexpr (kDb) acc_db = mfma16<kBf16>(fa[0], ones, acc_db);
-            s16x8 fb[S];
+            for (int r = R - 1; r > 0; --r)
 #pragma unroll
-            for (int s2 = 0; s2 < S; ++s2) fb[s2] = tr8(&s_x[k & 1][i][s2 * kPitchE + lane_off]);
+              for (int kk = 0; kk < kKs; ++kk) fa[r][kk] = fa[r - 1][kk];
 #pragma unroll
-            for (int r = 0; r < R; ++r)
+            for (int kk = 0; kk < kKs; ++kk) {
+              fa[0][kk] = tr8(&s_dy[k & 1][i][32 * kk * kPitchE + lane_off]);
+              if constexpr (kDb) acc_db = mfma16<kBf16>(fa[0][kk], ones, acc_db);
+              s16x8 fb[S];
 #pragma unroll
               for (int s2 = 0; s2 < S; ++s2)
-                acc[r * S + s2] = mfma16<kBf16>(fa[r], fb[s2], acc[r * S + s2]);
+                fb[s2] = tr8(&s_x[k & 1][i][(32 * kk + s2) * kPitchE + lane_off]);
+#pragma unroll
+              for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int s2 = 0; s2 < S; ++s2)
+                  acc[r * S + s2] = mfma16<kBf16>(fa[r][kk], fb[s2], acc[r * S + s2]);
+            }
           }
         }
       }
@@ -743,29 +763,23 @@ hipError_t launch_grouped16(const Plan& plan, const void* x, const void* dy, Sta
 #undef CW_G16S2
       return hipErrorInvalidValue;
     }
-#define CW_G16R(RR)                                                                              \
-    if (p.R == RR) {                                                                             \
+#define CW_G16R_W(RR, WW)                                                                         \
+    if (p.R == RR && wt == WW) {                                                                 \
       if (db)                                                                                    \
-        return bf ? launch_kernel(grouped16_rows_kernel<true, RR, RR, true>, xcd_grid, block, a, stream) \
-                  : launch_kernel(grouped16_rows_kernel<false, RR, RR, true>, xcd_grid, block, a, stream); \
-      return bf ? launch_kernel(grouped16_rows_kernel<true, RR, RR, false>, xcd_grid, block, a, stream)   \
-                : launch_kernel(grouped16_rows_kernel<false, RR, RR, false>, xcd_grid, block, a, stream); \
+        return bf ? launch_kernel(grouped16_rows_kernel<true, RR, RR, true, WW>, xcd_grid, block, a, stream) \
+                  : launch_kernel(grouped16_rows_kernel<false, RR, RR, true, WW>, xcd_grid, block, a, stream); \
+      return bf ? launch_kernel(grouped16_rows_kernel<true, RR, RR, false, WW>, xcd_grid, block, a, stream)   \
+                : launch_kernel(grouped16_rows_kernel<false, RR, RR, false, WW>, xcd_grid, block, a, stream); \
     }
+#define CW_G16R(RR) CW_G16R_W(RR, 32) CW_G16R_W(RR, 64)
+    const int wt = p.Wo > 32 ? 64 : 32;
+    CW_G16R(1)
+    CW_G16R(3)
     CW_G16R(5)
     CW_G16R(7)
 #undef CW_G16R
-    if (p.R == 3) {
-      if (db)
-        return bf ? launch_kernel(grouped16_rows_kernel<true, 3, 3, true>, xcd_grid, block, a, stream)
-                  : launch_kernel(grouped16_rows_kernel<false, 3, 3, true>, xcd_grid, block, a, stream);
-      return bf ? launch_kernel(grouped16_rows_kernel<true, 3, 3, false>, xcd_grid, block, a, stream)
-                : launch_kernel(grouped16_rows_kernel<false, 3, 3, false>, xcd_grid, block, a, stream);
-    }
-    if (db)
-      return bf ? launch_kernel(grouped16_rows_kernel<true, 1, 1, true>, xcd_grid, block, a, stream)
-                : launch_kernel(grouped16_rows_kernel<false, 1, 1, true>, xcd_grid, block, a, stream);
-    return bf ? launch_kernel(grouped16_rows_kernel<true, 1, 1, false>, xcd_grid, block, a, stream)
-              : launch_kernel(grouped16_rows_kernel<false, 1, 1, false>, xcd_grid, block, a, stream);
+#undef CW_G16R_W
+    return hipErrorInvalidValue;
   }
   if (plan.ru == 4 && p.dil == 1 && p.R == 3 && p.S == 3)
     return bf ? launch_kernel(grouped16_win_kernel<true, 3, 3>, grid, block, a, stream)

@@ -200,13 +200,15 @@ bool plan_grouped16(const Problem& p, Plan* out) {
 }
 
 // Row-streaming grouped kernel (grouped16.hip): as the block-diagonal kernel,
-// plus stride 1 or 2, no dilation, a 1x1, 3x3, 5x5 or 7x7 filter and output rows of at most
-// 32 pixels (one MFMA k-step); padding below the filter size.
+// plus stride 1 or 2, no dilation, a 1x1, 3x3, 5x5 or 7x7 filter, output rows
+// of at most 64 pixels at stride 1 (two MFMA k-steps) or 32 at stride 2, and
+// padding below the filter size.
 bool plan_grouped16_rows(const Problem& p, Plan* out) {
   if (p.dtype == CONV_WGRAD_F32 || (p.stride != 1 && p.stride != 2) || p.dil != 1 || p.Cg != p.Kg ||
       16 % p.Cg != 0)
     return false;
-  if (p.C % 16 != 0 || p.Wo > 32 || p.pad >= p.S || p.pad >= p.R) return false;
+  // Rows of up to 64 output pixels at stride 1 (two MFMA k-steps), 32 at stride 2.
+  if (p.C % 16 != 0 || p.Wo > (p.stride == 1 ? 64 : 32) || p.pad >= p.S || p.pad >= p.R) return false;
   if (p.R != p.S || !(p.R == 1 || p.R == 3 || p.R == 5 || p.R == 7)) return false;
   if (p.W * p.C * 2 > kI32Max / 2 || p.Wo * p.K * 2 > kI32Max / 2) return false;
   out->c_tiles = ceil_div(p.C, 64);

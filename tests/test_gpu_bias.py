@@ -40,6 +40,7 @@ BIAS_CASES = [
     (wd.ConvShape(2, 48, 7, 13, 48, 3, 3, pad=0, groups=6), "bf16", 3),        # grouped rows, partial block
     (wd.ConvShape(3, 64, 10, 20, 64, 7, 7, pad=3, groups=16), "f16", 2),       # grouped rows 7x7
     (wd.ConvShape(2, 64, 13, 29, 64, 3, 3, pad=1, stride=2, groups=16), "bf16", 2),  # grouped rows stride 2
+    (wd.ConvShape(2, 64, 9, 56, 64, 3, 3, pad=1, groups=16), "f16", 2),        # grouped rows, 64-pixel rows
     (wd.ConvShape(3, 64, 10, 37, 64, 3, 3, pad=1, groups=16), "f16", -1),      # grouped window kernel
     (wd.ConvShape(2, 48, 11, 12, 48, 3, 3, pad=2, dilation=2, groups=6), "bf16", 2),  # grouped generic
     (wd.ConvShape(8, 16, 40, 40, 16, 3, 3, pad=1), "f32", 320),                # > 256 slices: two fold passes

@@ -252,6 +252,12 @@ SMALL_GROUP_CASES = [
     (wd.ConvShape(2, 64, 6, 20, 64, 1, 1, pad=0, groups=4), "bf16", -1),      # cpg16, 1x1
     (wd.ConvShape(5, 32, 3, 7, 32, 3, 3, pad=1, groups=16), "bf16", 4),       # cpg2, slices across images
     (wd.ConvShape(3, 64, 12, 28, 64, 5, 5, pad=2, groups=16), "f16", -1),     # 5x5 cpg4
+    # grouped row kernel with two 32-pixel k-steps per row (32 < Wo <= 64)
+    (wd.ConvShape(2, 64, 9, 56, 64, 3, 3, pad=1, groups=16), "f16", -1),      # Wo = 56
+    (wd.ConvShape(3, 128, 7, 64, 128, 3, 3, pad=1, groups=16), "bf16", 3),    # Wo = 64, cpg8
+    (wd.ConvShape(2, 48, 8, 33, 48, 1, 1, pad=0, groups=12), "f16", 2),       # Wo = 33, 1x1, partial block
+    (wd.ConvShape(2, 64, 10, 45, 64, 7, 7, pad=3, groups=16), "bf16", -1),    # 7x7, Wo = 45
+    (wd.ConvShape(3, 32, 6, 40, 32, 5, 5, pad=1, groups=32), "f16", 4),       # 5x5 cpg1, pad < R - 1
     # grouped, stride 2 (X rows staged de-interleaved, two X rows per dY row)
     (wd.ConvShape(2, 64, 13, 29, 64, 3, 3, pad=1, stride=2, groups=16), "f16", 2),     # cpg4
     (wd.ConvShape(3, 128, 16, 64, 128, 3, 3, pad=1, stride=2, groups=16), "bf16", -1), # cpg8, Wo = 32
