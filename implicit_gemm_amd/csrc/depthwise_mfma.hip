@@ -27,8 +27,9 @@
 //    bytes and the slot pitch 64 mod 256 bytes, so the A reads (one 16-byte
 //    read gives the operands of two column steps) are free of bank conflicts.
 //  * dY rows alternate between two buffers.  A lane's B window starts at a
-//    column that depends on its filter column j; it is cut out of two aligned
-//    8-byte blocks with three selects and two v_perm_b32 (per-lane choices).
+//    column that depends on its filter column j; it is cut out of two
+//    4-byte-aligned dword pairs (ds_read2_b32, starting at the window's column
+//    rounded down to even) with two v_perm_b32 whose selector is per lane.
 //    The B operand of s-block 1 at column step w0 equals the s-block-0
 //    operand of step w0 - 4, so it is carried in registers.
 // The staged row length is a template parameter: every LDS offset is an
@@ -195,21 +196,18 @@ __global__ __launch_bounds__(kThreads) void depthwise_mfma_kernel(DwArgs a) {
   // MFMA operand addressing.  Lane = 4*b + q: block b = channel c0 + wave + 4b.
   const int b = lane >> 2, q = lane & 3;
   // The s-block-0 window of lane q at column step w0 starts at dY element
-  // w0 + pad - q, staged at column w0 + d with d = dy_off + pad - q >= 4: it is
-  // elements u..u+3 (u = d mod 4) of the aligned blocks at columns w0 + 4m and
-  // w0 + 4m + 4 (m = d / 4).
+  // w0 + pad - q, staged at column w0 + d with d = dy_off + pad - q: it is
+  // elements u..u+3 (u = d mod 2) of the dword pairs at columns w0 + 2m and
+  // w0 + 2m + 4 (m = d / 2).
   const int d0 = a.dy_off + a.pad - q;
-  const bool bhi = (d0 & 2) != 0;                                 // u >= 2: start in the second dword
   const uint32_t bsel = (d0 & 1) ? 0x05040302u : 0x03020100u;     // u odd: shift by one element
-  lds_cu8* const bq = (lds_cu8*)lds + L::kDyBase + wave * L::kDWave + b * L::kDs + 2 * (d0 & ~3);
-  // Separate base registers keep the two block reads of a pair from being
-  // merged into one ds_read2_b64, which is slower than two ds_read_b64.
+  lds_cu8* const bq = (lds_cu8*)lds + L::kDyBase + wave * L::kDWave + b * L::kDs + 2 * (d0 & ~1);
+  // Separate base registers keep the two dword-pair reads of a column-step
+  // pair as separate instructions.
   lds_cu8* bq4 = bq + 8;
   asm volatile("" : "+v"(bq4));
   auto window = [&](u32x2 q0, u32x2 q1) {
-    const uint32_t lo = bhi ? q0.y : q0.x;
-    const uint32_t mid = bhi ? q1.x : q0.y;
-    const uint32_t hi = bhi ? q1.y : q1.x;
+    const uint32_t lo = q0.x, mid = q0.y, hi = q1.x;
     const u32x2 v{__builtin_amdgcn_perm(mid, lo, bsel), __builtin_amdgcn_perm(hi, mid, bsel)};
     return __builtin_bit_cast(s16x4, v);
   };
@@ -228,7 +226,7 @@ __global__ __launch_bounds__(kThreads) void depthwise_mfma_kernel(DwArgs a) {
     for (int i = 0; i < RB; ++i) ap[i] = xr + ((a.stride * ho - a.pad + 4 * i + q) & (RING - 1)) * L::kSlot;
     lds_cu8* bp = bq + buf * L::kDBuf;
     lds_cu8* bp4 = bq4 + buf * L::kDBuf;
-    auto blk = [](lds_cu8* ptr) { return *reinterpret_cast<__attribute__((address_space(3))) const u32x2*>(ptr); };
+    auto blk = [](lds_cu8* ptr) { const auto* w = reinterpret_cast<__attribute__((address_space(3))) const uint32_t*>(ptr); return u32x2{w[0], w[1]}; };
     u32x2 qprev = blk(bp - 8);    // block of step -4
     u32x2 qcur = blk(bp);         // block of step 0
     s16x4 b1 = window(qprev, qcur);                           // s-block 1 of step 0
