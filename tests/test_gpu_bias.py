@@ -33,6 +33,7 @@ BIAS_CASES = [
     (wd.ConvShape(3, 12, 7, 7, 24, 3, 3, pad=1, groups=3), "f32", 4),         # direct, Cg 4 / Kg 8
     (wd.ConvShape(3, 48, 7, 7, 48, 3, 3, pad=1, groups=48), "bf16", 5),        # depthwise
     (wd.ConvShape(3, 384, 14, 14, 384, 7, 7, pad=3, groups=384), "bf16", 3),  # depthwise, 6 channel blocks
+    (wd.ConvShape(2, 96, 9, 33, 96, 5, 5, pad=2, groups=96), "f16", 2),        # depthwise, partial second quad
     (wd.ConvShape(2, 80, 6, 120, 80, 3, 3, pad=1, groups=80), "f16", 1),       # depthwise, 2 pixel passes
     (wd.ConvShape(2, 32, 14, 40, 32, 11, 11, pad=5, groups=32), "bf16", 3),    # depthwise, 3 x 3 filter blocks
     (wd.ConvShape(2, 48, 23, 100, 48, 7, 7, pad=3, stride=2, groups=48), "f16", 2),  # depthwise stride 2

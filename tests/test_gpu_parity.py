@@ -229,6 +229,10 @@ SMALL_GROUP_CASES = [
     (wd.ConvShape(3, 16, 4, 33, 16, 6, 2, pad=1, groups=16), "f16", 4),       # odd Wo
     (wd.ConvShape(3, 384, 14, 14, 384, 7, 7, pad=3, groups=384), "bf16", 5),  # slices across images
     (wd.ConvShape(2, 16, 6, 10, 16, 3, 3, pad=12, groups=16), "f16", 3),      # pad 12: zero X rows > R - 1
+    # depthwise, two channel quads (a partial one), slices across images, stride 2
+    (wd.ConvShape(2, 96, 9, 33, 96, 5, 5, pad=2, groups=96), "f16", -1),      # partial second quad
+    (wd.ConvShape(3, 128, 12, 56, 128, 7, 7, pad=3, groups=128), "bf16", 5),  # slices across images
+    (wd.ConvShape(2, 128, 20, 40, 128, 5, 5, pad=2, stride=2, groups=128), "bf16", 2),  # stride 2
     # depthwise stride 2 (dY rows staged upsampled; X rows advance two per output row)
     (wd.ConvShape(2, 16, 9, 11, 16, 3, 3, pad=1, stride=2, groups=16), "bf16", 2),
     (wd.ConvShape(2, 32, 20, 40, 32, 5, 5, pad=2, stride=2, groups=32), "f16", -1),
@@ -252,6 +256,8 @@ SMALL_GROUP_CASES = [
     (wd.ConvShape(2, 64, 6, 20, 64, 1, 1, pad=0, groups=4), "bf16", -1),      # cpg16, 1x1
     (wd.ConvShape(5, 32, 3, 7, 32, 3, 3, pad=1, groups=16), "bf16", 4),       # cpg2, slices across images
     (wd.ConvShape(3, 64, 12, 28, 64, 5, 5, pad=2, groups=16), "f16", -1),     # 5x5 cpg4
+    (wd.ConvShape(3, 32, 1, 24, 32, 3, 3, pad=1, groups=8), "f16", -1),       # Ho = 1: second half idle
+    (wd.ConvShape(4, 64, 2, 17, 64, 3, 3, pad=1, groups=16), "bf16", 3),      # Ho = 2, slices across images
     # grouped row kernel with two 32-pixel k-steps per row (32 < Wo <= 64)
     (wd.ConvShape(2, 64, 9, 56, 64, 3, 3, pad=1, groups=16), "f16", -1),      # Wo = 56
     (wd.ConvShape(3, 128, 7, 64, 128, 3, 3, pad=1, groups=16), "bf16", 3),    # Wo = 64, cpg8
