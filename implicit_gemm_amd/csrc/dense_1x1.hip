@@ -39,39 +39,30 @@ struct OneByOneArgs {
   float* dbo;   // bias-gradient partial of slice 0 (slab_stride apart), or nullptr
 };
 
+// One 4-row batch: lane (i, g) loads row g of the batch, AV channels of dY at
+// byte offset ody and BV channels of X at byte offset ox, from buffer
+// resources whose ranges end at the slice's last row (rows past it read 0).
 template <int AV, int BV>
-__device__ __forceinline__ void load_batch(const float* dyp, const float* xp, bool ok,
+__device__ __forceinline__ void load_batch(__amdgpu_buffer_rsrc_t rdy, int ody, __amdgpu_buffer_rsrc_t rx, int ox,
                                            float (&a)[AV], float (&b)[BV]) {
-  if (ok) {
-    if (AV == 4) {
-      const float4 v = *reinterpret_cast<const float4*>(dyp);
-      a[0] = v.x; a[1] = v.y; a[2] = v.z; a[3] = v.w;
-    } else {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  static_assert(AV == 4, "four output channels per lane");
+  const f4 va = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rdy, ody, 0, 0));
+  a[0] = va[0]; a[1] = va[1]; a[2] = va[2]; a[3] = va[3];
+  int j = 0;
 #pragma unroll
-      for (int j = 0; j < AV; ++j) a[j] = dyp[j];
-    }
-    if (BV % 4 == 0) {
-#pragma unroll
-      for (int j = 0; j < BV; j += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(xp + j);
-        b[j] = v.x; b[j + 1] = v.y; b[j + 2] = v.z; b[j + 3] = v.w;
-      }
-    } else if (BV % 2 == 0) {
-#pragma unroll
-      for (int j = 0; j < BV; j += 2) {
-        const float2 v = *reinterpret_cast<const float2*>(xp + j);
-        b[j] = v.x; b[j + 1] = v.y;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < BV; ++j) b[j] = xp[j];
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < AV; ++j) a[j] = 0.f;
-#pragma unroll
-    for (int j = 0; j < BV; ++j) b[j] = 0.f;
+  for (; j + 4 <= BV; j += 4) {
+    const f4 v = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rx, ox + 4 * j, 0, 0));
+    b[j] = v[0]; b[j + 1] = v[1]; b[j + 2] = v[2]; b[j + 3] = v[3];
   }
+  if constexpr (BV % 4 >= 2) {
+    const f2 v = __builtin_bit_cast(f2, __builtin_amdgcn_raw_buffer_load_b64(rx, ox + 4 * j, 0, 0));
+    b[j] = v[0]; b[j + 1] = v[1];
+    j += 2;
+  }
+  if constexpr (BV % 2 == 1)
+    b[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rx, ox + 4 * j, 0, 0));
 }
 
 // kDb: the bias-gradient variant (a separate instantiation keeps the extra
@@ -91,12 +82,25 @@ __global__ __launch_bounds__(64) void dense_1x1_kernel(OneByOneArgs a) {
 
   const int64_t r_begin = (int64_t)slice * a.rows_per_slice;
   const int64_t r_end = min(a.L, r_begin + a.rows_per_slice);
-  const int64_t nb = (r_end - r_begin + 3) >> 2;  // 4-row batches
+  // 4-row batches, rounded up to whole rings so that the loop body has no
+  // branches (the load counters stay exact and the ring never drains); the
+  // extra batches read zeros.
+  const int64_t nb = (r_end - r_begin + 4 * kPf - 1) / (4 * kPf) * kPf;
 
-  const float* dyp = a.dy + (r_begin + lg) * a.K + (int64_t)g * a.Kg + m0 + AV * li;
-  const float* xp = a.x + (r_begin + lg) * a.C + (int64_t)g * a.Cg + c0 + BV * li;
-  const int64_t dy_step = 4 * (int64_t)a.K, x_step = 4 * (int64_t)a.C;
-  int64_t row = r_begin + lg;
+  // Batch t reads rows r_begin + 4t .. + 3 from uniform 64-bit bases; the
+  // buffer range of a batch ends at the slice's last row.
+  const int cdy = g * a.Kg + m0, cx = g * a.Cg + c0;          // first channel of the tile
+  const unsigned char* const dy0 = reinterpret_cast<const unsigned char*>(a.dy + r_begin * a.K + cdy);
+  const unsigned char* const x0 = reinterpret_cast<const unsigned char*>(a.x + r_begin * a.C + cx);
+  const int ody = (lg * a.K + AV * li) * 4, ox = (lg * a.C + BV * li) * 4;
+  auto load = [&](int64_t t, float (&ra)[AV], float (&rb)[BV]) {
+    const int64_t left = r_end - r_begin - 4 * t;              // rows of the slice from this batch on
+    const int rows = left < 0 ? 0 : left > 4 ? 4 : (int)left;
+    const __amdgpu_buffer_rsrc_t rdy =
+        buf_rsrc(dy0 + 16 * t * a.K, rows > 0 ? (rows * a.K - cdy) * 4 : 0);
+    const __amdgpu_buffer_rsrc_t rx = buf_rsrc(x0 + 16 * t * a.C, rows > 0 ? (rows * a.C - cx) * 4 : 0);
+    load_batch<AV, BV>(rdy, ody, rx, ox, ra, rb);
+  };
 
   f32x4 acc[AV][BV];
 #pragma unroll
@@ -112,28 +116,27 @@ __global__ __launch_bounds__(64) void dense_1x1_kernel(OneByOneArgs a) {
 #pragma unroll
   for (int i = 0; i < AV; ++i) dbp[i] = 0.f;
 
+  // The prologue issues the ring in the order the loop consumes it (pinned by
+  // scheduling barriers), so the wait at the loop head is for one batch only.
   float ra[kPf][AV], rb[kPf][BV];
 #pragma unroll
   for (int p = 0; p < kPf; ++p) {
-    load_batch<AV, BV>(dyp, xp, row < r_end, ra[p], rb[p]);
-    dyp += dy_step; xp += x_step; row += 4;
+    load(p, ra[p], rb[p]);
+    __builtin_amdgcn_sched_barrier(0);
   }
   for (int64_t b = 0; b < nb; b += kPf) {
 #pragma unroll
     for (int p = 0; p < kPf; ++p) {
-      if (b + p < nb) {
 #pragma unroll
-        for (int i = 0; i < AV; ++i)
+      for (int i = 0; i < AV; ++i)
 #pragma unroll
-          for (int j = 0; j < BV; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ra[p][i], rb[p][j], acc[i][j], 0, 0, 0);
-        if constexpr (kDb) {
+        for (int j = 0; j < BV; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ra[p][i], rb[p][j], acc[i][j], 0, 0, 0);
+      if constexpr (kDb) {
 #pragma unroll
-          for (int i = 0; i < AV; ++i) dbp[i] += ra[p][i];
-        }
-        load_batch<AV, BV>(dyp, xp, row < r_end, ra[p], rb[p]);
-        dyp += dy_step; xp += x_step; row += 4;
+        for (int i = 0; i < AV; ++i) dbp[i] += ra[p][i];
       }
+      load(b + p + kPf, ra[p], rb[p]);
     }
   }
 

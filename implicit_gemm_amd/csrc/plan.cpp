@@ -163,6 +163,8 @@ bool plan_dense_rows(const Problem& p, Plan* out) {
 bool plan_dense_1x1(const Problem& p, Plan* out) {
   if (p.dtype != CONV_WGRAD_F32 || p.R != 1 || p.S != 1 || p.pad != 0 || p.stride != 1) return false;
   if (p.Kg % 64 != 0 || p.Cg % 16 != 0) return false;
+  // A batch's buffer range (4 rows) and the lane offsets are 32-bit.
+  if (p.C > (1 << 26) || p.K > (1 << 26)) return false;
   const int64_t q = p.Cg / 16;
   int32_t bv = 1;
   for (int32_t cand = 8; cand >= 1; --cand) {
