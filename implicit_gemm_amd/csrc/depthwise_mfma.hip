@@ -120,10 +120,17 @@ __global__ __launch_bounds__(kThreads) void depthwise_mfma_kernel(DwArgs a) {
   const unsigned char* __restrict__ dyg = static_cast<const unsigned char*>(a.dy);
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  // Consecutive blocks take the channel quads of one slice: the workgroups
-  // that read the same pixel rows run together.
-  const int quad = blockIdx.x % a.quads;
-  const int slice = blockIdx.x / a.quads;
+  // Work item w = (slice, channel quad), quad fastest.  Block b runs on XCD
+  // b % 8 (round-robin dispatch) and XCD x takes the items
+  // [x * per_xcd, (x + 1) * per_xcd), so the quads of a slice, which read
+  // the same pixel records at the same time, share one L2 and reach DRAM
+  // together; the grid is a multiple of 8 and the blocks past the items exit.
+  const int work = a.quads * a.ks_count;
+  const int per_xcd = (work + 7) >> 3;
+  const int w = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if ((int)(blockIdx.x >> 3) >= per_xcd || w >= work) return;
+  const int quad = w % a.quads;
+  const int slice = w / a.quads;
   const int c0 = quad * kQuadCh;
   const int r_begin = slice * a.rows_per_slice;
   const int r_end = min(a.rows, r_begin + a.rows_per_slice);
@@ -375,7 +382,8 @@ hipError_t launch_xl(const DwArgs& args, int64_t grid, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   void* params[] = {const_cast<DwArgs*>(&args)};
-  return launch_raw(fn, dim3((unsigned)grid), dim3(kThreads), params, (size_t)L::kBytes, stream);
+  const int64_t xcd_grid = (grid + 7) / 8 * 8;   // whole rounds over the 8 XCDs
+  return launch_raw(fn, dim3((unsigned)xcd_grid), dim3(kThreads), params, (size_t)L::kBytes, stream);
 }
 
 template <bool kBf16, int RB, int SB>
