@@ -17,7 +17,8 @@ JSON line:
                   traffic = HBM bytes per launch from the FETCH_SIZE /
                   WRITE_SIZE counter table in profiles/hbm_traffic.md when
                   it was taken on the current kernel source, else null
-  cold_cache      per-call event times with a 1 GiB cache flush before each call
+  cold_cache      per-call event times with a cache flush before each call (a
+                  read of a clean 1 GiB buffer)
   cpu_baseline    the CPU oracle (test infrastructure) timed on the host cores
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu] [--bias]
@@ -274,14 +275,19 @@ def main():
         hip.destroy(a)
         hip.destroy(b)
 
-    # Cold-cache calls (outside the timed region): a 1 GiB write before each.
+    # Cold-cache calls (outside the timed region): before each, a read of a
+    # 1 GiB buffer (written once beforehand) evicts the inputs from the L2s and
+    # the 256 MB MALL and leaves clean lines, so the call neither hits the
+    # caches nor competes with the write-back of a flush's dirty lines.
     cold = None
     if args.cold > 0:
-        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        probe = torch.empty((), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
         e0, e1, e2 = hip.event(), hip.event(), hip.event()
         whole, stage1 = [], []
         for _ in range(args.cold):
-            flush.fill_(1.0)
+            torch.amax(flush, dim=0, out=probe)   # queued just before the call: no idle gap
             hip.record(e0, sp)
             step(e1, e2)
             e3 = hip.event()
@@ -294,7 +300,7 @@ def main():
                 "call_ms_p90": round(whole[int(0.9 * (len(whole) - 1))], 5),
                 "stage1_ms_median": round(statistics.median(stage1), 5),
                 "tflops_median": round(s.flops() / (statistics.median(whole) * 1e-3) / 1e12, 3)}
-        del flush
+        del flush, probe
 
     torch.cuda.synchronize()
     dw_h = dw.cpu().numpy()
