@@ -20,7 +20,13 @@
 //     channels: 4 A operands (dY) and SB B operands (X) per 32 pixels feed
 //     4 * SB accumulators;
 //   * two LDS buffers alternate: a unit is staged while the previous one is
-//     computed, one barrier per unit.
+//     computed, one barrier per unit;
+//   * short rows (Wo + SB - 1 <= 32): a unit is ru = 64 / P consecutive output
+//     rows staged at a pitch of P = Wo + SB - 1 pixels -- dY row j in slots
+//     j*P .. j*P + Wo - 1 followed by zeros, its X segment in slots
+//     j*P .. j*P + P - 1 -- so tap s is still the shift by s slots (a product
+//     that crosses into the next row's segment meets a zero dY column), and a
+//     14-pixel row no longer occupies a whole 64-pixel unit.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -49,6 +55,7 @@ struct R16Args {
   int32_t Cg, Kg, cols;
   int32_t m_tiles, c_tiles, s_blocks;
   int32_t wt, wchunks;
+  int32_t ru, pitch, hblocks;   // output rows per unit, staging pitch, ceil(Ho / ru)
   int32_t units, units_per_slice, ks_count;
   int32_t tiles, work;
   float* dbo;      // bias-gradient partial of slice 0 (slab_stride apart), or nullptr
@@ -105,7 +112,48 @@ __global__ __launch_bounds__(256) void dense16_rows_kernel(R16Args a) {
   const int x_row_bytes = (a.W * a.C - x_col0) * 2;
   uint4 rdy[kDyChunks], rx[kXChunks];
   int npix_next = 0;
+  // Multi-row units: slot p of a loader chunk is row p / pitch, column p % pitch.
+  int dj[kDyChunks], dcol[kDyChunks], xj[kXChunks], xcol[kXChunks];
+  if (a.ru > 1) {
+#pragma unroll
+    for (int i = 0; i < kDyChunks; ++i) { dj[i] = (px0 + 32 * i) / a.pitch; dcol[i] = (px0 + 32 * i) % a.pitch; }
+#pragma unroll
+    for (int i = 0; i < kXChunks; ++i) { xj[i] = (px0 + 32 * i) / a.pitch; xcol[i] = (px0 + 32 * i) % a.pitch; }
+  }
+  auto load_rows = [&](int u) {
+    const int n = u / a.hblocks, ho0 = (u % a.hblocks) * a.ru;
+    const int rows = min(a.ru, a.Ho - ho0);
+    npix_next = a.ru * a.pitch;
+    // dY rows ho0 .. ho0 + rows - 1 are contiguous; columns past Wo and rows
+    // past the unit read zero.
+    const unsigned char* dyp = dyg + 2 * (((int64_t)(n * a.Ho + ho0) * a.Wo) * a.K + dy_col0);
+    const __amdgpu_buffer_rsrc_t rd = buf_rsrc(dyp, (rows * a.Wo * a.K - dy_col0) * 2);
+#pragma unroll
+    for (int i = 0; i < kDyChunks; ++i) {
+      const bool ok = dcol[i] < a.Wo && dj[i] < rows;
+      rdy[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             rd, ok ? ((dj[i] * a.Wo + dcol[i]) * a.K + 8 * q8) * 2 : 0x7fffffff, 0, 0));
+    }
+    // X rows h0 + j of the unit (filter row r), columns w0 .. w0 + pitch - 1;
+    // rows and columns outside the image read zero.
+    const int h0 = ho0 + r - a.pad;
+    const int hb = max(h0, 0), he = min(h0 + rows, a.H);
+    const int w0 = s0 - a.pad;
+    const unsigned char* xp = xg + 2 * ((int64_t)n * a.x_img + (int64_t)hb * a.W * a.C + x_col0);
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(xp, he > hb ? ((he - hb) * a.W * a.C - x_col0) * 2 : 0);
+#pragma unroll
+    for (int i = 0; i < kXChunks; ++i) {
+      const int h = h0 + xj[i], w = w0 + xcol[i];
+      const bool ok = xj[i] < rows && h >= hb && h < he && w >= 0 && w < a.W;
+      rx[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rs, ok ? (((h - hb) * a.W + w) * a.C + 8 * q8) * 2 : 0x7fffffff, 0, 0));
+    }
+  };
   auto load_unit = [&](int u) {
+    if (a.ru > 1) {
+      load_rows(u);
+      return;
+    }
     const int wc = u % a.wchunks;
     const int t = u / a.wchunks;
     const int ho = t % a.Ho, n = t / a.Ho;
@@ -263,6 +311,9 @@ hipError_t launch_dense16_rows(const Plan& plan, const void* x, const void* dy, 
   a.s_blocks = (int32_t)plan.s_blocks;
   a.wt = plan.wt;
   a.wchunks = (int32_t)plan.wchunks;
+  a.ru = plan.ru > 1 ? plan.ru : 1;
+  a.pitch = (int32_t)(p.Wo + plan.sb - 1);
+  a.hblocks = (int32_t)ceil_div(p.Ho, a.ru);
   a.units = (int32_t)plan.pub.units;
   a.units_per_slice = (int32_t)plan.pub.units_per_slice;
   a.ks_count = plan.pub.ks_count;

@@ -230,6 +230,16 @@ bool plan_dense16_rows(const Problem& p, Plan* out) {
   out->c_tiles = ceil_div(p.Cg, 64);
   out->m_tiles = ceil_div(p.Kg, 64);
   out->wchunks = ceil_div(p.Wo, out->wt);
+  // Short rows: units of ru output rows staged at a pitch of Wo + SB - 1
+  // pixels in the 64 slots of a unit (ru >= 2).
+  const int64_t pitch = p.Wo + out->sb - 1;
+  out->ru = pitch <= 32 ? (int32_t)(64 / pitch) : 1;
+  // A unit's rows are one buffer range each for X and dY (32-bit).
+  if (out->ru > 1 && (out->ru * p.W * p.C * 2 > kI32Max || out->ru * p.Wo * p.K * 2 > kI32Max)) out->ru = 1;
+  if (out->ru > 1) {
+    out->wt = 64;
+    out->wchunks = 1;
+  }
   return true;
 }
 
@@ -361,9 +371,14 @@ conv_wgrad_status_t make_plan(const conv_wgrad_desc_t* desc, Plan* out) {
   }
   if (plan_dense16_rows(p, out)) {
     pub.variant = kDense16Rows;
-    pub.unit_rows = out->wt;
     int64_t units, tiles;
-    if (!mul3(p.N, p.Ho, out->wchunks, &units)) return CONV_WGRAD_ERR_UNSUPPORTED;
+    if (out->ru > 1) {
+      pub.unit_rows = out->ru * p.Wo;   // a unit is ru whole output rows
+      if (!mul_ok(p.N, ceil_div(p.Ho, out->ru), &units)) return CONV_WGRAD_ERR_UNSUPPORTED;
+    } else {
+      pub.unit_rows = out->wt;
+      if (!mul3(p.N, p.Ho, out->wchunks, &units)) return CONV_WGRAD_ERR_UNSUPPORTED;
+    }
     if (!mul4(p.groups, out->m_tiles, p.R, out->s_blocks, &tiles) ||
         !mul_ok(tiles, out->c_tiles, &tiles))
       return CONV_WGRAD_ERR_UNSUPPORTED;

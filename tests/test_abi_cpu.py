@@ -122,7 +122,11 @@ def check_plan_invariants(d, p):
     assert (p.Ho, p.Wo) == (Ho, Wo)
     assert p.L == d.N * Ho * Wo
     assert p.E == d.K * d.R * d.S * (d.C // d.groups)
-    if p.path == iga.PATH_DENSE and p.variant in (1, 3):   # row units: (n, ho, chunk of Wo)
+    if p.path == iga.PATH_DENSE and p.variant == 3 and p.unit_rows > Wo:   # units of ru whole rows
+        ru = p.unit_rows // Wo
+        assert p.unit_rows == ru * Wo and ru >= 2 and ru * (Wo + min(d.S, 4) - 1) <= 64
+        assert p.units == d.N * -(-Ho // ru)
+    elif p.path == iga.PATH_DENSE and p.variant in (1, 3):   # row units: (n, ho, chunk of Wo)
         assert p.units == d.N * Ho * -(-Wo // p.unit_rows)
     elif p.variant in (12, 13):                       # depthwise, row-streaming grouped: one output row per unit
         assert p.units == d.N * Ho and p.unit_rows == Wo

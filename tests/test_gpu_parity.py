@@ -294,3 +294,33 @@ def test_small_group_kernels(idx):
     x, dy = wd.random_inputs(shp, dtype, seed=500 + idx, x_dist=wd.Dist("normal", 1.0),
                              dy_dist=wd.Dist("normal", 0.1))
     check_against_oracle(x, dy, shp, dtype, split_k=split_k)
+
+
+# 16-bit dense kernel with units of several short output rows (Wo + SB - 1 <= 32):
+# row pitch Wo + SB - 1 inside the 64-slot unit, Ho not a multiple of the rows
+# per unit, padding 0..2, two tap blocks (S = 5), partial channel tiles, slices.
+DENSE16_ROW_CASES = [
+    (wd.ConvShape(3, 64, 14, 14, 64, 3, 3, pad=1), "bf16", -1),       # 4 rows per unit, last unit 2 rows
+    (wd.ConvShape(2, 72, 7, 7, 40, 3, 3, pad=1), "f16", 2),           # 7 rows per unit, partial tiles
+    (wd.ConvShape(2, 64, 30, 30, 64, 3, 3, pad=0), "bf16", 3),        # Wo = 28, 2 rows per unit
+    (wd.ConvShape(2, 64, 30, 30, 64, 3, 3, pad=1), "f16", -1),        # Wo = 30, pitch 32
+    (wd.ConvShape(3, 32, 9, 1, 32, 1, 1), "bf16", 2),                 # Wo = 1: 64 rows per unit
+    (wd.ConvShape(2, 64, 12, 12, 136, 5, 5, pad=2), "f16", 4),        # S = 5: two tap blocks, 3 M tiles
+    (wd.ConvShape(4, 128, 10, 13, 64, 3, 3, pad=2), "bf16", -1),      # pad 2: Ho, Wo > H - 2
+    (wd.ConvShape(2, 64, 16, 16, 64, 3, 3, pad=1, groups=2), "f16", 3),  # two groups of 32 channels
+]
+
+
+@pytest.mark.parametrize("idx", range(len(DENSE16_ROW_CASES)))
+def test_dense16_multirow_units(idx):
+    import implicit_gemm_amd as iga
+    shp, dtype, split_k = DENSE16_ROW_CASES[idx]
+    d = iga.make_desc(shp.N, shp.C, shp.H, shp.W, shp.K, shp.R, shp.S, shp.pad, shp.stride,
+                      shp.dilation, shp.groups, {"f32": 0, "bf16": 1, "f16": 2}[dtype], split_k)
+    plan = iga.get_plan(d)
+    log("dense16 rows", idx, shp, dtype, "split", split_k, "variant", plan.variant,
+        "unit_rows", plan.unit_rows, "ks", plan.ks_count)
+    assert plan.variant == 3 and plan.unit_rows > plan.Wo   # several rows per unit
+    x, dy = wd.random_inputs(shp, dtype, seed=700 + idx, x_dist=wd.Dist("normal", 1.0),
+                             dy_dist=wd.Dist("normal", 0.1))
+    check_against_oracle(x, dy, shp, dtype, split_k=split_k)
