@@ -384,7 +384,10 @@ conv_wgrad_status_t make_plan(const conv_wgrad_desc_t* desc, Plan* out) {
       return CONV_WGRAD_ERR_UNSUPPORTED;
     // Three 256-lane workgroups fit per CU (42 KB of LDS each), two per CU
     // are targeted.  A unit costs the same time whatever the MFMA work, so
-    // slices are worth up to 4x the algorithmic bytes in slab traffic.
+    // slices are worth up to 4x the algorithmic bytes in slab traffic.  Units
+    // of several short rows carry ~4x the MFMA work of a single short row:
+    // three per CU, and slab traffic up to 8x (it overlaps the MFMAs).
+    if (out->ru > 1) return choose_split(units, tiles, desc->split_k, 2, 768, 1, p, &pub, 0, 8);
     return choose_split(units, tiles, desc->split_k, 2, 512, 1, p, &pub, 0, 4);
   }
   if (plan_dense_rows(p, out)) {
