@@ -21,7 +21,7 @@ JSON line:
                   read of a clean 1 GiB buffer)
   cpu_baseline    the CPU oracle (test infrastructure) timed on the host cores
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu] [--bias]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--n N] [--no-cpu] [--bias]
 
 With --bias every step is conv_wgrad_bias (the weight gradient and the fused
 bias gradient db = sum dY); value still counts the weight-gradient FLOPs.
@@ -168,6 +168,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=DEFAULT_CONFIG)
     ap.add_argument("--split-k", type=int, default=-1)
+    ap.add_argument("--n", type=int, default=0, help="batch of an N-swept workload (default 64)")
     ap.add_argument("--cold", type=int, default=20, help="cold-cache calls (0 = skip)")
     ap.add_argument("--prewarm-s", type=float, default=0.3,
                     help="seconds of untimed steps after the warm-up steps (clock ramp)")
@@ -212,9 +213,17 @@ def main():
         return 0
     wl = wd.workload(args.config)
     s = wl.shape
-    if s.N > 64 and wl.n_sweep:
-        s = s.with_n(64)
+    if wl.n_sweep:
+        # N-swept workload: N = 64 unless --n picks another point of the sweep.
+        n = args.n if args.n else 64
+        if n not in wl.n_sweep:
+            print("--n must be one of %s for %s" % (wl.n_sweep, wl.name), file=sys.stderr)
+            return 2
+        s = s.with_n(n)
         wl = wd.Workload(wl.name, s, wl.dtype, wl.x_dist, wl.dy_dist, wl.seed, wl.note)
+    elif args.n:
+        print("--n applies only to an N-swept workload", file=sys.stderr)
+        return 2
     log("workload", wl.name, s, wl.dtype)
     x_h, dy_h = wd.make_inputs(wl)
     dev = torch.device("cuda:0")
