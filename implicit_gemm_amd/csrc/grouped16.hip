@@ -398,11 +398,15 @@ __device__ __forceinline__ void rows_epilogue(const G16Args& a, const f32x4 (&ac
 // column offsets and multiplied with the A operands of output rows
 // h + pad - r, so every staged element is read from HBM once per slice.
 // kDb: also the bias gradient (a separate instantiation keeps the plain
-// kernel's MFMA loop unchanged).
-template <bool kBf16, int R, int S, bool kDb, int WT>
+// kernel's MFMA loop unchanged).  Only the W image pixels of an X row are
+// loaded (one 16-byte chunk per lane, kNXL passes of 32 pixels, kWide when
+// W > WT); they land at slot pad + w and the padding slots are zeroed once,
+// so no load instruction is spent on padding columns.
+template <bool kBf16, int R, int S, bool kDb, int WT, bool kWide>
 __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
   constexpr int kXPixR = WT + S - 1;              // staged X pixels per row
   constexpr int kKs = WT / 32;                    // 32-pixel MFMA k-steps per row
+  constexpr int kNXL = WT / 32 + (kWide ? 1 : 0); // X load passes per row (W <= 32 * kNXL)
   constexpr int kRows = 2;                        // rows per step (one barrier)
   constexpr int kPf = 2;                          // steps fetched ahead (even)
   // The output block (16 channels per group at most) is gathered in LDS when
@@ -439,24 +443,31 @@ __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
   const int r_begin = slice * a.units_per_slice;
   const int r_end = min(a.units, r_begin + a.units_per_slice);   // units are output rows
 
-  // Loader role: pixel slots ps + 32 i (X: kNX passes with the halo; dY:
-  // kKs passes), 16-byte chunk q.
-  constexpr int kNX = (kXPixR + 31) / 32;
+  // Loader role: image pixels ps + 32 i of an X row (kNXL passes), dY pixels
+  // ps + 32 i (kKs passes), 16-byte chunk q.
   const int q = tid & 7, ps = tid >> 3;
   const int x_row_bytes = (a.W * a.C - c0) * 2;
   const int dy_row_bytes = (a.Wo * a.K - c0) * 2;
-  int ox[kNX], ody[kKs];
+  int ox[kNXL], ody[kKs];
 #pragma unroll
-  for (int i = 0; i < kNX; ++i)   // negative offsets (padding) and offsets past the range read zero
-    ox[i] = ps + 32 * i < kXPixR ? ((ps + 32 * i - a.pad) * a.C + 8 * q) * 2 : 0x7fffffff;
+  for (int i = 0; i < kNXL; ++i)   // offsets past the range read zero
+    ox[i] = ps + 32 * i < a.W ? ((ps + 32 * i) * a.C + 8 * q) * 2 : 0x7fffffff;
 #pragma unroll
   for (int i = 0; i < kKs; ++i) ody[i] = ((ps + 32 * i) * a.K + 8 * q) * 2;
   struct Row {
-    uint4 x[kNX], d[kKs];
+    uint4 x[kNXL], d[kKs];
   };
   struct Step {
     Row row[kRows];
   };
+  // X slots [0, pad) and [pad + W, kXPixR) of every row buffer hold the zero
+  // padding; the stores below never touch them.
+  for (int e = tid; e < 2 * kRows * kXPixR * 8; e += 256) {
+    const int slot = (e >> 3) % kXPixR;
+    if (slot < a.pad || slot >= a.pad + a.W)
+      *reinterpret_cast<uint4*>(&s_x[e / (8 * kRows * kXPixR)][(e / (8 * kXPixR)) % kRows][slot * kPitchE + 8 * (e & 7)]) =
+          uint4{0u, 0u, 0u, 0u};
+  }
   // Row u of a segment: X row ho0 - pad + u and dY row ho0 + u (u < rows_x).
   int n = 0, ho0 = 0, ho_hi = 0, rows_x = 0;
   auto fetch_row = [&](int u, Row& st) {
@@ -466,7 +477,7 @@ __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
         buf_rsrc(xg + 2 * ((int64_t)n * a.x_img + (int64_t)(x_in ? h : 0) * a.W * a.C + c0),
                  x_in ? x_row_bytes : 0);
 #pragma unroll
-    for (int i = 0; i < kNX; ++i)
+    for (int i = 0; i < kNXL; ++i)
       st.x[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, ox[i], 0, 0));
     const int ho = ho0 + u;
     const bool d_in = ho < ho_hi;
@@ -485,9 +496,9 @@ __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
 #pragma unroll
-      for (int x = 0; x < kNX; ++x)
-        if (ps + 32 * x < kXPixR)
-          *reinterpret_cast<uint4*>(&s_x[buf][i][(ps + 32 * x) * kPitchE + 8 * q]) = st.row[i].x[x];
+      for (int x = 0; x < kNXL; ++x)
+        if (ps + 32 * x < a.W)
+          *reinterpret_cast<uint4*>(&s_x[buf][i][(ps + 32 * x + a.pad) * kPitchE + 8 * q]) = st.row[i].x[x];
 #pragma unroll
       for (int x = 0; x < kKs; ++x)
         *reinterpret_cast<uint4*>(&s_dy[buf][i][(ps + 32 * x) * kPitchE + 8 * q]) = st.row[i].d[x];
@@ -763,16 +774,17 @@ hipError_t launch_grouped16(const Plan& plan, const void* x, const void* dy, Sta
 #undef CW_G16S2
       return hipErrorInvalidValue;
     }
-#define CW_G16R_W(RR, WW)                                                                         \
-    if (p.R == RR && wt == WW) {                                                                 \
+#define CW_G16R_W(RR, WW, XW)                                                                     \
+    if (p.R == RR && wt == WW && wide == XW) {                                                   \
       if (db)                                                                                    \
-        return bf ? launch_kernel(grouped16_rows_kernel<true, RR, RR, true, WW>, xcd_grid, block, a, stream) \
-                  : launch_kernel(grouped16_rows_kernel<false, RR, RR, true, WW>, xcd_grid, block, a, stream); \
-      return bf ? launch_kernel(grouped16_rows_kernel<true, RR, RR, false, WW>, xcd_grid, block, a, stream)   \
-                : launch_kernel(grouped16_rows_kernel<false, RR, RR, false, WW>, xcd_grid, block, a, stream); \
+        return bf ? launch_kernel(grouped16_rows_kernel<true, RR, RR, true, WW, XW>, xcd_grid, block, a, stream) \
+                  : launch_kernel(grouped16_rows_kernel<false, RR, RR, true, WW, XW>, xcd_grid, block, a, stream); \
+      return bf ? launch_kernel(grouped16_rows_kernel<true, RR, RR, false, WW, XW>, xcd_grid, block, a, stream)   \
+                : launch_kernel(grouped16_rows_kernel<false, RR, RR, false, WW, XW>, xcd_grid, block, a, stream); \
     }
-#define CW_G16R(RR) CW_G16R_W(RR, 32) CW_G16R_W(RR, 64)
+#define CW_G16R(RR) CW_G16R_W(RR, 32, false) CW_G16R_W(RR, 64, false) CW_G16R_W(RR, 32, true) CW_G16R_W(RR, 64, true)
     const int wt = p.Wo > 32 ? 64 : 32;
+    const bool wide = p.W > wt;   // a row has more image pixels than one pass per k-step
     CW_G16R(1)
     CW_G16R(3)
     CW_G16R(5)
