@@ -111,7 +111,7 @@ struct Item {
 template <bool kBf16, int RB, int SB, int XL>
 __global__ __launch_bounds__(kThreads) void depthwise_mfma_kernel(DwArgs a) {
   constexpr int NP = XL > 64 ? 2 : 1;   // pixel-pair passes per row
-  constexpr int kPf = NP == 1 ? 4 : 2;  // steps fetched ahead (even: dY buffer parity is static)
+  constexpr int kPf = 2;                // steps fetched ahead (even: dY buffer parity is static)
   constexpr int RING = dw_ring<RB>();
   constexpr int NPAIRS = XL / 8;
   using L = DwLayout<XL, RING, 16 * RB * SB>;
