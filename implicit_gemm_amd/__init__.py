@@ -69,6 +69,12 @@ def load():
     if not os.path.exists(LIB_PATH):
         raise ImportError("libconvwgrad.so is not built (%s); run `python -m implicit_gemm_amd.build`"
                           % LIB_PATH)
+    # torch ships its own HIP runtime under the same soname as ROCm's but asks
+    # for it by another name; loaded after this library it would be a second
+    # runtime in the process, to which torch's streams belong and this
+    # library's launches do not.  Loading torch first makes the library bind
+    # to torch's runtime: one runtime, shared streams.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER
     lib.conv_wgrad_status_string.restype = ctypes.c_char_p

@@ -3,6 +3,7 @@ planner (pure host integer code reached through conv_wgrad_get_plan)."""
 import ctypes
 import json
 import os
+import sys
 import re
 import subprocess
 
@@ -215,3 +216,24 @@ def test_split_pinning_and_auto():
     assert p.ks_count == p.units
     pa = iga.get_plan(D(N=32, C=64, H=56, W=56, K=64, split_k=-1))
     assert pa.ks_count >= 1 and 128 <= pa.grid <= 256  # about one workgroup per CU
+
+
+def test_one_hip_runtime_when_the_library_loads_first():
+    """Loading the library before torch must not leave two HIP runtimes in the process.
+
+    torch's bundled runtime and ROCm's share a soname but torch asks for it by
+    another name; if the library pulled in ROCm's copy first, torch would load a
+    second one and its streams would be foreign to the library's launches.
+    """
+    import subprocess
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "import implicit_gemm_amd as iga\n"
+        "iga.load()\n"
+        "import torch\n"
+        "maps = open('/proc/self/maps').read().split('\\n')\n"
+        "paths = sorted({l.split()[-1] for l in maps if 'libamdhip64' in l})\n"
+        "print(len(paths), paths)\n" % ROOT)
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.split()[0] == "1", out.stdout
