@@ -401,7 +401,11 @@ __device__ __forceinline__ void rows_epilogue(const G16Args& a, const f32x4 (&ac
 // kernel's MFMA loop unchanged).  Only the W image pixels of an X row are
 // loaded (one 16-byte chunk per lane, kNXL passes of 32 pixels, kWide when
 // W > WT); they land at slot pad + w and the padding slots are zeroed once,
-// so no load instruction is spent on padding columns.
+// so no load instruction is spent on padding columns.  Padding rows are not
+// staged either: the steps cover only the X rows inside the image, and the
+// up to R - 1 dY rows that pair with the padding rows above the first one
+// are fetched with the segment's first loads and enter the A-operand shift
+// register before its first step.
 template <bool kBf16, int R, int S, bool kDb, int WT, bool kWide>
 __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
   constexpr int kXPixR = WT + S - 1;              // staged X pixels per row
@@ -411,9 +415,11 @@ __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
   constexpr int kPf = 2;                          // steps fetched ahead (even)
   // The output block (16 channels per group at most) is gathered in LDS when
   // it fits in the row tiles (1x1, 3x3); larger filters store it directly.
+  constexpr int kPre = R - 1;                     // dY rows that enter before the first step
   struct Tiles {
     unsigned short x[2][kRows][kXPixR * kPitchE];
     unsigned short dy[2][kRows][WT * kPitchE];
+    unsigned short pre[kPre > 0 ? kPre : 1][kPre > 0 ? WT * kPitchE : 8];
   };
   constexpr int kOut = kCh * R * S * 16;
   constexpr bool kStageOut = kOut * 4 <= (int)sizeof(Tiles);
@@ -425,6 +431,7 @@ __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
   __shared__ __attribute__((aligned(16))) Smem sm;
   auto& s_x = sm.t.x;
   auto& s_dy = sm.t.dy;
+  auto& s_pre = sm.t.pre;
   const unsigned char* __restrict__ xg = static_cast<const unsigned char*>(a.x);
   const unsigned char* __restrict__ dyg = static_cast<const unsigned char*>(a.dy);
 
@@ -460,26 +467,23 @@ __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
   struct Step {
     Row row[kRows];
   };
-  // X slots [0, pad) and [pad + W, kXPixR) of every row buffer hold the zero
-  // padding; the stores below never touch them.
-  for (int e = tid; e < 2 * kRows * kXPixR * 8; e += 256) {
-    const int slot = (e >> 3) % kXPixR;
-    if (slot < a.pad || slot >= a.pad + a.W)
-      *reinterpret_cast<uint4*>(&s_x[e / (8 * kRows * kXPixR)][(e / (8 * kXPixR)) % kRows][slot * kPitchE + 8 * (e & 7)]) =
-          uint4{0u, 0u, 0u, 0u};
-  }
-  // Row u of a segment: X row ho0 - pad + u and dY row ho0 + u (u < rows_x).
-  int n = 0, ho0 = 0, ho_hi = 0, rows_x = 0;
+  // Segment: output rows [ho0, ho_hi) of image n.  Its X rows inside the
+  // image are hx0 .. hx0 + ev - 1; row u of the segment is X row hx0 + u
+  // (u < ev) and dY row hx0 + pad + u (the row that meets X row hx0 + u at
+  // filter row 0; zero from ho_hi on).  Row ho = h + pad - r meets X row h at
+  // filter row r, so the X rows below hx0 and from hx0 + ev on meet only
+  // zero padding or rows outside the segment.
+  int n = 0, ho0 = 0, ho_hi = 0, hx0 = 0, ev = 0;
   auto fetch_row = [&](int u, Row& st) {
-    const int h = ho0 - a.pad + u;
-    const bool x_in = h >= 0 && h < a.H && u < rows_x;
+    const int h = hx0 + u;
+    const bool x_in = u < ev;
     const __amdgpu_buffer_rsrc_t rx =
         buf_rsrc(xg + 2 * ((int64_t)n * a.x_img + (int64_t)(x_in ? h : 0) * a.W * a.C + c0),
                  x_in ? x_row_bytes : 0);
 #pragma unroll
     for (int i = 0; i < kNXL; ++i)
       st.x[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, ox[i], 0, 0));
-    const int ho = ho0 + u;
+    const int ho = hx0 + a.pad + u;
     const bool d_in = ho < ho_hi;
     const __amdgpu_buffer_rsrc_t rd =
         buf_rsrc(dyg + 2 * (((int64_t)n * a.Ho + (d_in ? ho : ho0)) * a.Wo * a.K + c0),
@@ -487,6 +491,22 @@ __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
 #pragma unroll
     for (int i = 0; i < kKs; ++i)
       st.d[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rd, ody[i], 0, 0));
+  };
+  // dY rows hx0 + pad - 1 - i (i < R - 1): the rows that the shift register
+  // holds at row 0 in its places 1 + i (zero outside the segment).
+  uint4 pre[kPre > 0 ? kPre : 1][kKs];
+  auto fetch_pre = [&]() {
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) {
+      const int ho = hx0 + a.pad - 1 - i;
+      const bool d_in = ho >= ho0 && ho < ho_hi;
+      const __amdgpu_buffer_rsrc_t rd =
+          buf_rsrc(dyg + 2 * (((int64_t)n * a.Ho + (d_in ? ho : ho0)) * a.Wo * a.K + c0),
+                   d_in ? dy_row_bytes : 0);
+#pragma unroll
+      for (int k = 0; k < kKs; ++k)
+        pre[i][k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rd, ody[k], 0, 0));
+    }
   };
   auto fetch = [&](int t, Step& st) {
 #pragma unroll
@@ -516,29 +536,63 @@ __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
   for (int t = 0; t < R * S; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   // Bias gradient: each dY row's A operand (fa[0] when the row enters) times a
   // B operand of ones gives, in every column, the row's sum per output
-  // channel; every dY row of a segment enters once (rows outside it are zero).
+  // channel; every dY row of a segment enters once, before the first step or
+  // at its row (rows outside the segment are zero).
   f32x4 acc_db = f32x4{0.f, 0.f, 0.f, 0.f};
   const unsigned short one = kBf16 ? 0x3f80 : 0x3c00;
   const s16x8 ones{(short)one, (short)one, (short)one, (short)one,
                    (short)one, (short)one, (short)one, (short)one};
 
   Step pf[kPf];
-  int row = r_begin;
-  while (row < r_end) {
+  int row = r_begin, seg = 0, steps = 0;
+  // Sets up the segment that starts at output row `row` and issues its first
+  // loads: the rows before its first step, then kPf steps.
+  auto begin_segment = [&]() {
     n = row / a.Ho;
     ho0 = row % a.Ho;
-    const int seg = min(r_end - row, a.Ho - ho0);
+    seg = min(r_end - row, a.Ho - ho0);
     ho_hi = ho0 + seg;
-    rows_x = seg + R - 1;     // X rows ho0 - pad .. ho0 + seg - 1 - pad + R - 1
-    const int steps = (rows_x + kRows - 1) / kRows;
-    // A operands of dY rows ho0 + u - r, r = 0..R-1, per k-step (zero before the segment).
+    hx0 = max(0, ho0 - a.pad);
+    ev = min(a.H, ho_hi + R - 1 - a.pad) - hx0;   // >= 1 (pad < R, ho0 < Ho)
+    steps = (ev + kRows - 1) / kRows;
+    fetch_pre();
+#pragma unroll
+    for (int k = 0; k < kPf; ++k) fetch(k, pf[k]);
+  };
+  if (row < r_end) begin_segment();
+  // X slots [0, pad) and [pad + W, kXPixR) of every row buffer hold the zero
+  // padding; the stores below never touch them.  (Written while the first
+  // loads are in flight; the barrier before the first step orders them.)
+  for (int e = tid; e < 2 * kRows * kXPixR * 8; e += 256) {
+    const int slot = (e >> 3) % kXPixR;
+    if (slot < a.pad || slot >= a.pad + a.W)
+      *reinterpret_cast<uint4*>(&s_x[e / (8 * kRows * kXPixR)][(e / (8 * kXPixR)) % kRows][slot * kPitchE + 8 * (e & 7)]) =
+          uint4{0u, 0u, 0u, 0u};
+  }
+  while (row < r_end) {
+    // A operands of dY rows hx0 + pad + u - r, r = 0..R-1, per k-step at row u.
+    // Each row shifts the register up one place before its new row enters in
+    // place 0, so the rows before the first step start in places 0..R-2.
     s16x8 fa[R][kKs];
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int kk = 0; kk < kKs; ++kk) fa[r][kk] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    if constexpr (kPre > 0) {
 #pragma unroll
-    for (int k = 0; k < kPf; ++k) fetch(k, pf[k]);
+      for (int i = 0; i < kPre; ++i)
+#pragma unroll
+        for (int x = 0; x < kKs; ++x)
+          *reinterpret_cast<uint4*>(&s_pre[i][(ps + 32 * x) * kPitchE + 8 * q]) = pre[i][x];
+      lds_barrier();
+#pragma unroll
+      for (int i = 0; i < kPre; ++i)
+#pragma unroll
+        for (int kk = 0; kk < kKs; ++kk) {
+          fa[i][kk] = tr8(&s_pre[i][32 * kk * kPitchE + lane_off]);
+          if constexpr (kDb) acc_db = mfma16<kBf16>(fa[i][kk], ones, acc_db);
+        }
+    }
     for (int t = 0; t < steps; t += kPf) {
 #pragma unroll
       for (int k = 0; k < kPf; ++k) {
@@ -547,7 +601,7 @@ __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
         fetch(tk + kPf, pf[k]);
         lds_barrier();
         if (tk < steps) {
-          // Rows past the segment's X rows hold zero dY, so their products vanish.
+          // Rows past the segment's ev rows hold zero X and dY.
 #pragma unroll
           for (int i = 0; i < kRows; ++i) {
 #pragma unroll
@@ -575,6 +629,7 @@ __global__ __launch_bounds__(256) void grouped16_rows_kernel(G16Args a) {
     // The next segment restarts at buffer 0; all waves finish this one first.
     lds_barrier();
     row += seg;
+    if (row < r_end) begin_segment();
   }
 
   constexpr int kTaps = R * S;
