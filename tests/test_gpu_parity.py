@@ -296,6 +296,41 @@ def test_small_group_kernels(idx):
     check_against_oracle(x, dy, shp, dtype, split_k=split_k)
 
 
+# Grouped row kernel with slices of one to three output rows, so that segments
+# start at every row of the top padding band and below it: the dY rows that
+# pair with padding rows above the image enter before the first step (only
+# those inside the segment), and the bias gradient counts each dY row once.
+GROUPED_SHORT_SLICE_CASES = [
+    (wd.ConvShape(1, 64, 9, 20, 64, 7, 7, pad=3, groups=16), "bf16", 9),     # one row per slice
+    (wd.ConvShape(2, 64, 8, 24, 64, 5, 5, pad=2, groups=16), "f16", 8),      # two rows per slice
+    (wd.ConvShape(1, 32, 11, 17, 32, 7, 7, pad=2, groups=8), "f16", 4),      # three rows, pad < R / 2
+    (wd.ConvShape(2, 64, 7, 40, 64, 5, 5, pad=4, groups=16), "bf16", 11),    # pad R - 1, Wo = 44
+]
+
+
+@pytest.mark.parametrize("idx", range(len(GROUPED_SHORT_SLICE_CASES)))
+def test_grouped_rows_short_slices(idx):
+    import torch
+    import implicit_gemm_amd as iga
+    shp, dtype, split_k = GROUPED_SHORT_SLICE_CASES[idx]
+    d = iga.make_desc(shp.N, shp.C, shp.H, shp.W, shp.K, shp.R, shp.S, shp.pad, shp.stride,
+                      shp.dilation, shp.groups, {"f32": 0, "bf16": 1, "f16": 2}[dtype], split_k)
+    plan = iga.get_plan(d)
+    log("grouped short slices", idx, shp, dtype, "split", split_k, "variant", plan.variant,
+        "rows per slice", plan.units_per_slice, "ks", plan.ks_count)
+    assert plan.variant == 13 and plan.units_per_slice <= 3
+    x, dy = wd.random_inputs(shp, dtype, seed=800 + idx, x_dist=wd.Dist("normal", 1.0),
+                             dy_dist=wd.Dist("normal", 0.1))
+    dw, db = iga.wgrad(to_device(x, dtype), to_device(dy, dtype), shp.R, shp.S, shp.pad, shp.stride,
+                       shp.dilation, shp.groups, split_k=split_k, bias=True)
+    torch.cuda.synchronize()
+    check_against_oracle(x, dy, shp, dtype, split_k=split_k, dw_gpu=dw.cpu().numpy().astype(np.float64))
+    dyf = dy.astype(np.float64).reshape(-1, shp.K)
+    db_err = float(np.abs(db.cpu().numpy().astype(np.float64) - dyf.sum(0)).max()
+                   / max(np.abs(dyf).sum(0).max(), 1e-300))
+    assert db_err <= oracle.TOL[dtype], db_err
+
+
 # 16-bit dense kernel with units of several short output rows (Wo + SB - 1 <= 32):
 # row pitch Wo + SB - 1 inside the 64-slot unit, Ho not a multiple of the rows
 # per unit, padding 0..2, two tap blocks (S = 5), partial channel tiles, slices.
