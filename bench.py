@@ -19,7 +19,13 @@ JSON line:
                   it was taken on the current kernel source, else null
   cold_cache      per-call event times with a cache flush before each call (a
                   read of a clean 1 GiB buffer)
-  cpu_baseline    the CPU oracle (test infrastructure) timed on the host cores
+  cpu_baseline    the CPU oracle (test infrastructure) timed on the host cores,
+                  with the host CPU model; for 1x1 workloads also numpy's
+                  float64 BLAS closed form dW = dY^T X on the same images
+
+  python bench.py --peaks   achievable streaming-read bandwidth (buffers of the
+                  workloads' input sizes, hot and cold) and MFMA rates, beside
+                  the published peaks; one JSON line
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--n N] [--no-cpu] [--bias]
 
@@ -118,6 +124,62 @@ class Hip:
         self.lib.hipEventDestroy(ev)
 
 
+def measure_peaks(hip):
+    """Achievable peaks beside the published ones: a 16-byte streaming read of
+    buffers the size of the workloads' inputs (hot: back to back; cold: after
+    a read of 1 GiB of other data), and loops of independent MFMA chains.
+    Each figure is the median of 10 dispatch-stamped launches at the best of
+    several grid sizes."""
+    import torch
+    import implicit_gemm_amd as iga
+    stream = torch.cuda.current_stream().cuda_stream
+    e0, e1 = hip.event(), hip.event()
+
+    def timed(launch, reps=10, before=None):
+        for _ in range(3):
+            launch(None, None)
+        ms = []
+        for _ in range(reps):
+            if before:
+                before()
+            launch(e0, e1)
+            ms.append(hip.elapsed_ms(e0, e1))
+        return statistics.median(ms)
+
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    probe = torch.empty((), dtype=torch.float32, device="cuda")
+    sink = torch.empty(65536 * 256, dtype=torch.float32, device="cuda")
+    reads = []
+    for nbytes in (51417088, 308356608, 1 << 30, 10737418240):
+        buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        for cold in ((False, True) if nbytes <= (1 << 30) else (False,)):
+            best = None
+            for blocks in (512, 1024, 2048, 4096):
+                ms = timed(lambda a, b: iga.peak_read(buf.data_ptr(), nbytes, blocks, sink.data_ptr(), stream, a, b),
+                           before=(lambda: torch.amax(flush, dim=0, out=probe)) if cold else None)
+                if best is None or ms < best[1]:
+                    best = (blocks, ms)
+            reads.append({"bytes": nbytes, "cold": cold, "blocks": best[0], "us": round(best[1] * 1e3, 2),
+                          "gbs": round(nbytes / (best[1] * 1e-3) / 1e9, 1),
+                          "frac_of_published": round(nbytes / (best[1] * 1e-3) / 1e9 / PEAK["hbm_gbs"], 4)})
+        del buf
+    mfma = []
+    for name, code, iters, per_round in (("f32", 0, 5000, 16384), ("bf16", 1, 10000, 131072),
+                                         ("f16", 2, 10000, 131072)):
+        best = None
+        for blocks in (1024, 2048):
+            ms = timed(lambda a, b: iga.peak_mfma(code, iters, blocks, sink.data_ptr(), stream, a, b), reps=5)
+            tf = blocks * 4 * iters * per_round / (ms * 1e-3) / 1e12
+            if best is None or tf > best[1]:
+                best = (blocks, tf)
+        mfma.append({"dtype": name, "blocks": best[0], "tflops": round(best[1], 1),
+                     "frac_of_published": round(best[1] / PEAK["mfma_tflops"][name], 4)})
+    torch.cuda.synchronize()
+    hip.destroy(e0)
+    hip.destroy(e1)
+    return {"read": reads, "mfma": mfma, "published": PEAK}
+
+
 def roofline_for(shape, dtype, seconds, traffic=None):
     import wgrad_data as wd
     flops = shape.flops()
@@ -155,10 +217,35 @@ def cpu_baseline(wl, x, dy, reps):
     reps = len(times)
     t = statistics.median(times)
     what = "whole workload" if n_s == s.N else "first %d of %d images" % (n_s, s.N)
-    return {"value": round(per_image * n_s / t / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
-            "sample": "%s (%s), median of %d runs, fp64 C oracle, %.2f s per run"
-                      % (what, wl.name, reps, t)}
+    out = {"value": round(per_image * n_s / t / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
+           "kind": "oracle",
+           "sample": "%s (%s), median of %d runs, fp64 C oracle, %.2f s per run"
+                     % (what, wl.name, reps, t),
+           "cpu_model": cpu_model()}
+    if s.R == 1 and s.S == 1 and s.stride == 1 and s.pad == 0 and s.groups == 1:
+        # A 1x1 weight gradient is one product, dW = dY^T X over all pixels:
+        # numpy's float64 BLAS on the same images, one image at a time.
+        import numpy as np
+        t0 = time.perf_counter()
+        acc = np.zeros((s.K, s.C))
+        for i in range(n_s):
+            acc += dys[i].reshape(-1, s.K).astype(np.float64).T @ xs[i].reshape(-1, s.C).astype(np.float64)
+        tb = time.perf_counter() - t0
+        out["blas_closed_form"] = {"value": round(per_image * n_s / tb / 1e12, 5), "unit": "TFLOP/s",
+                                   "sample": "%s, numpy float64 dY^T X per image (widening included), "
+                                             "one run, %.2f s" % (what, tb)}
+    return out
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -176,6 +263,8 @@ def main():
     ap.add_argument("--bias", action="store_true",
                     help="time conv_wgrad_bias (dW and the fused bias gradient db = sum dY)")
     ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--peaks", action="store_true",
+                    help="measure the achievable streaming-read bandwidth and MFMA rates and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run 3 device-to-device copies of 1 GiB (scale for HBM byte counters)")
     ap.add_argument("--digest", action="store_true",
@@ -203,6 +292,9 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         return 1
+    if args.peaks:
+        print(json.dumps({"peaks": measure_peaks(Hip())}))
+        return 0
     if args.calibrate_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)

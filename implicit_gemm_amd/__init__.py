@@ -100,8 +100,30 @@ def load():
     lib.conv_wgrad_bias_timed.argtypes = [P(Desc), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.conv_wgrad_peak_read.restype = ctypes.c_int
+    lib.conv_wgrad_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.conv_wgrad_peak_mfma.restype = ctypes.c_int
+    lib.conv_wgrad_peak_mfma.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     _lib = lib
     return lib
+
+
+def peak_read(src_ptr: int, nbytes: int, blocks: int, sink_ptr: int, stream: int, begin=None,
+              end=None) -> None:
+    """Achievable-read probe (conv_wgrad_peak_read): device pointers as integers."""
+    st = load().conv_wgrad_peak_read(src_ptr, nbytes, blocks, sink_ptr, stream or None, begin, end)
+    if st != 0:
+        raise ConvWgradError(st, "peak_read")
+
+
+def peak_mfma(dtype: int, iters: int, blocks: int, sink_ptr: int, stream: int, begin=None,
+              end=None) -> None:
+    """Achievable-MFMA probe (conv_wgrad_peak_mfma): sink holds blocks * 256 floats."""
+    st = load().conv_wgrad_peak_mfma(dtype, iters, blocks, sink_ptr, stream or None, begin, end)
+    if st != 0:
+        raise ConvWgradError(st, "peak_mfma")
 
 
 def make_desc(N, C, H, W, K, R, S, pad=0, stride=1, dilation=1, groups=1, dtype=F32,

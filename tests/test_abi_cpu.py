@@ -1,6 +1,7 @@
 """The C-ABI library without a GPU: exported symbols, validation errors and the
 planner (pure host integer code reached through conv_wgrad_get_plan)."""
 import ctypes
+import glob
 import json
 import os
 import sys
@@ -14,21 +15,26 @@ import implicit_gemm_amd as iga
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "conv_wgrad.h")
+PEAKS_HEADER = os.path.join(ROOT, "include", "conv_wgrad_peaks.h")
 GOLDEN = os.path.join(ROOT, "tests", "golden")
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(conv_wgrad\w*)\s*\(", text)))
 
 
 def test_library_loads_and_exports_every_declared_symbol():
     lib = iga.load()
-    names = declared_functions()
-    assert set(names) == {"conv_wgrad", "conv_wgrad_ex", "conv_wgrad_get_plan", "conv_wgrad_timed",
-                          "conv_wgrad_status_string", "conv_wgrad_workspace_size",
-                          "conv_wgrad_bias", "conv_wgrad_bias_timed"}
+    headers = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
+    assert headers == [HEADER, PEAKS_HEADER]
+    assert set(declared_functions()) == {"conv_wgrad", "conv_wgrad_ex", "conv_wgrad_get_plan",
+                                         "conv_wgrad_timed", "conv_wgrad_status_string",
+                                         "conv_wgrad_workspace_size", "conv_wgrad_bias",
+                                         "conv_wgrad_bias_timed"}
+    assert set(declared_functions(PEAKS_HEADER)) == {"conv_wgrad_peak_read", "conv_wgrad_peak_mfma"}
+    names = sorted(set(n for h in headers for n in declared_functions(h)))
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", iga.LIB_PATH], capture_output=True,
@@ -41,6 +47,22 @@ def test_struct_sizes_match_header_layout():
     # 11 int64 + 2 int32; plan: see conv_wgrad_plan_t field order.
     assert ctypes.sizeof(iga.Desc) == 11 * 8 + 2 * 4
     assert ctypes.sizeof(iga.Plan) == 8 + 8 * 7 + 4 + 4 + 8 * 3 + 8 * 4 + 8
+
+
+def test_peak_probe_argument_errors():
+    # Validation happens before any launch, so no GPU is needed.
+    lib = iga.load()
+    fake = ctypes.c_void_p(0x10000)
+    assert lib.conv_wgrad_peak_read(None, 16, 1, fake, None, None, None) == 1          # NULL_ARG
+    assert lib.conv_wgrad_peak_read(fake, 16, 1, None, None, None, None) == 1
+    for nbytes, blocks in ((0, 1), (-16, 1), (24, 1), (16, 0), (16, 65537)):
+        assert lib.conv_wgrad_peak_read(fake, nbytes, blocks, fake, None, None, None) == 2  # BAD_SHAPE
+    assert lib.conv_wgrad_peak_read(ctypes.c_void_p(0x10008), 16, 1, fake, None, None, None) == 6
+    assert lib.conv_wgrad_peak_mfma(0, 1, 1, None, None, None, None) == 1
+    for dtype in (3, -1):
+        assert lib.conv_wgrad_peak_mfma(dtype, 1, 1, fake, None, None, None) == 3       # BAD_DTYPE
+    for iters, blocks in ((0, 1), (1 << 31, 1), (1, 0), (1, 65537)):
+        assert lib.conv_wgrad_peak_mfma(0, iters, blocks, fake, None, None, None) == 2
 
 
 def test_status_strings():
