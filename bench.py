@@ -17,6 +17,8 @@ JSON line:
                   traffic = HBM bytes per launch from the FETCH_SIZE /
                   WRITE_SIZE counter table in profiles/hbm_traffic.md when
                   it was taken on the current kernel source, else null
+  whole_call_roofline_frac  the same roofline fraction for the whole call
+                  (stage 1 + the slab reduce, the time behind value)
   cold_cache      per-call event times with a cache flush before each call (a
                   read of a clean 1 GiB buffer)
   cpu_baseline    the CPU oracle (test infrastructure) timed on the host cores,
@@ -439,6 +441,7 @@ def main():
                    "bias_gradient": bool(args.bias),
                    "parallelism": "single GPU"},
         "roofline": roof,
+        "whole_call_roofline_frac": roofline_for(s, wl.dtype, ms_per_step * 1e-3)["frac"],
         "stage1_ms_mean": round(stage1_avg_s * 1e3, 5),
         "cold_cache": cold,
         "cpu_baseline": cpu,
