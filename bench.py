@@ -133,7 +133,7 @@ def measure_peaks(hip):
     Each figure is the median of 10 dispatch-stamped launches at the best of
     several grid sizes."""
     import torch
-    import implicit_gemm_amd as iga
+    from implicit_gemm_amd import probes
     stream = torch.cuda.current_stream().cuda_stream
     e0, e1 = hip.event(), hip.event()
 
@@ -157,7 +157,7 @@ def measure_peaks(hip):
         for cold in ((False, True) if nbytes <= (1 << 30) else (False,)):
             best = None
             for blocks in (512, 1024, 2048, 4096):
-                ms = timed(lambda a, b: iga.peak_read(buf.data_ptr(), nbytes, blocks, sink.data_ptr(), stream, a, b),
+                ms = timed(lambda a, b: probes.peak_read(buf.data_ptr(), nbytes, blocks, sink.data_ptr(), stream, a, b),
                            before=(lambda: torch.amax(flush, dim=0, out=probe)) if cold else None)
                 if best is None or ms < best[1]:
                     best = (blocks, ms)
@@ -170,7 +170,7 @@ def measure_peaks(hip):
                                          ("f16", 2, 10000, 131072)):
         best = None
         for blocks in (1024, 2048):
-            ms = timed(lambda a, b: iga.peak_mfma(code, iters, blocks, sink.data_ptr(), stream, a, b), reps=5)
+            ms = timed(lambda a, b: probes.peak_mfma(code, iters, blocks, sink.data_ptr(), stream, a, b), reps=5)
             tf = blocks * 4 * iters * per_round / (ms * 1e-3) / 1e12
             if best is None or tf > best[1]:
                 best = (blocks, tf)

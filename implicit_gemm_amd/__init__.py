@@ -100,30 +100,8 @@ def load():
     lib.conv_wgrad_bias_timed.argtypes = [P(Desc), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
-    lib.conv_wgrad_peak_read.restype = ctypes.c_int
-    lib.conv_wgrad_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
-                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
-    lib.conv_wgrad_peak_mfma.restype = ctypes.c_int
-    lib.conv_wgrad_peak_mfma.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
-                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     _lib = lib
     return lib
-
-
-def peak_read(src_ptr: int, nbytes: int, blocks: int, sink_ptr: int, stream: int, begin=None,
-              end=None) -> None:
-    """Achievable-read probe (conv_wgrad_peak_read): device pointers as integers."""
-    st = load().conv_wgrad_peak_read(src_ptr, nbytes, blocks, sink_ptr, stream or None, begin, end)
-    if st != 0:
-        raise ConvWgradError(st, "peak_read")
-
-
-def peak_mfma(dtype: int, iters: int, blocks: int, sink_ptr: int, stream: int, begin=None,
-              end=None) -> None:
-    """Achievable-MFMA probe (conv_wgrad_peak_mfma): sink holds blocks * 256 floats."""
-    st = load().conv_wgrad_peak_mfma(dtype, iters, blocks, sink_ptr, stream or None, begin, end)
-    if st != 0:
-        raise ConvWgradError(st, "peak_mfma")
 
 
 def make_desc(N, C, H, W, K, R, S, pad=0, stride=1, dilation=1, groups=1, dtype=F32,
@@ -227,24 +205,29 @@ def wgrad(x, dy, R, S, pad=0, stride=1, dilation=1, groups=1, split_k=-1, dw=Non
     if not (x.is_contiguous() and dy.is_contiguous()):
         raise ValueError("x and dy must be contiguous NHWC")
     shape = (d.K, d.R, d.S, d.C // d.groups)
-    if dw is None:
-        dw = torch.empty(shape, dtype=torch.float32, device=x.device)
-    elif tuple(dw.shape) != shape or dw.dtype != torch.float32 or not dw.is_contiguous():
+    if dw is not None and (tuple(dw.shape) != shape or dw.dtype != torch.float32 or not dw.is_contiguous()):
         raise ValueError("dw must be a contiguous float32 tensor of shape %s" % (shape,))
-    ws_bytes = plan.ws_bytes
-    if ws_bytes and workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    if bias and db is not None and (tuple(db.shape) != (d.K,) or db.dtype != torch.float32
+                                    or not db.is_contiguous()):
+        raise ValueError("db must be a contiguous float32 tensor of shape (%d,)" % d.K)
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
+    ws_bytes = plan.ws_bytes
+    # Buffers allocated here belong to the stream the work is enqueued on, so
+    # the caching allocator does not hand the workspace (dropped on return,
+    # while the kernels may still be queued) to another stream's allocation.
+    with torch.cuda.stream(stream):
+        if dw is None:
+            dw = torch.empty(shape, dtype=torch.float32, device=x.device)
+        if bias and db is None:
+            db = torch.empty((d.K,), dtype=torch.float32, device=x.device)
+        if ws_bytes and workspace is None:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
     ws_ptr = workspace.data_ptr() if ws_bytes else 0
     ws_len = workspace.numel() * workspace.element_size() if ws_bytes else 0
     if not bias:
         conv_wgrad_ex(d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(), ws_ptr, ws_len, stream.cuda_stream)
         return dw
-    if db is None:
-        db = torch.empty((d.K,), dtype=torch.float32, device=x.device)
-    elif tuple(db.shape) != (d.K,) or db.dtype != torch.float32 or not db.is_contiguous():
-        raise ValueError("db must be a contiguous float32 tensor of shape (%d,)" % d.K)
     conv_wgrad_bias(d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(), db.data_ptr(), ws_ptr, ws_len,
                     stream.cuda_stream)
     return dw, db

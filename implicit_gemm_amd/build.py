@@ -1,4 +1,5 @@
-"""Compile the gfx950 weight-gradient library (libconvwgrad.so) in-tree with hipcc.
+"""Compile the gfx950 weight-gradient library (libconvwgrad.so) in-tree with hipcc,
+and beside it the measurement probes (libcwprobes.so, not part of the C ABI).
 
     python -m implicit_gemm_amd.build
 """
@@ -13,6 +14,8 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libconvwgrad.so")
+PROBES_DIR = os.path.join(HERE, "probes")
+PROBES_LIB = os.path.join(PROBES_DIR, "libcwprobes.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
@@ -37,20 +40,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libconvwgrad.so; returns the library path."""
-    os.makedirs(OBJ_DIR, exist_ok=True)
-    srcs = sources()
-    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, out):
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed:\n%s%s" % (res.stdout, res.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source, link libconvwgrad.so and libcwprobes.so; returns the library path."""
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    srcs = sources()
+    probe_srcs = sorted(glob.glob(os.path.join(PROBES_DIR, "*.hip")))
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(probe_srcs))) as ex:
+        objs = list(ex.map(_compile, srcs + probe_srcs))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], PROBES_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBES_LIB)
     return LIB
 
 

@@ -36,6 +36,11 @@ constexpr int64_t kMaxRows = kI32Max - 65536;
 constexpr int64_t kDwLdsMax = 160 * 1024;  // LDS per CU
 // Upper bound on the split degree (the slab fold launches one workgroup row per run).
 constexpr int64_t kMaxSlices = 65536;
+// Launch geometry limits: lanes per launch, the widest stage-1 workgroup, and
+// the slab fold's workgroup (256 lanes folding 64 consecutive elements).
+constexpr int64_t kLaunchLanes = (int64_t)1 << 32;
+constexpr int64_t kMaxBlock = 512;
+constexpr int64_t kFoldBlock = 256, kFoldElemsPerBlock = 64;
 
 }  // namespace
 
@@ -111,6 +116,13 @@ conv_wgrad_status_t choose_split(int64_t units, int64_t tiles, int32_t requested
   pub->tiles = tiles;
   int64_t grid;
   if (!mul_ok(tiles, ks, &grid) || grid > kI32Max) return CONV_WGRAD_ERR_UNSUPPORTED;
+  // A launch's lanes (workgroups x lanes per workgroup) must stay below 2^32:
+  // stage 1 (at most kMaxBlock lanes per workgroup, plus the up to 7
+  // workgroups the XCD-ordered grids round up by) and the slab fold.
+  if ((grid + 8) * kMaxBlock >= kLaunchLanes) return CONV_WGRAD_ERR_UNSUPPORTED;
+  if (ks > 1 && (ceil_div(p.E, kFoldElemsPerBlock) + ceil_div(p.K, kFoldElemsPerBlock)) * kFoldBlock >=
+                    kLaunchLanes)
+    return CONV_WGRAD_ERR_UNSUPPORTED;
   pub->grid = grid;
   pub->slab_stride = ceil_div(db_offset(p) + p.K, 64) * 64;   // dW partial, then db partial
   int64_t ws_elems;
@@ -135,8 +147,15 @@ constexpr int kRowsMaxWt = 64, kRowsMaxXSpan = 80;
 // segment of at most 80 pixels for at least 16 output pixels per unit.
 bool plan_dense_rows(const Problem& p, Plan* out) {
   if (p.Kg % 4 != 0 || p.Cg % 4 != 0) return false;
-  // Buffer loads address one X or dY row with 32-bit byte offsets.
+  // Buffer loads address one X or dY row with 32-bit byte offsets: a lane's
+  // offsets reach 64 dY pixels past the unit's first one, and X columns from
+  // -pad to past the image by up to the staged span plus the filter's reach.
   if (p.W * p.C * p.esize > kI32Max / 2 || p.Wo * p.K * p.esize > kI32Max / 2) return false;
+  int64_t dy_reach, x_cols, x_reach;
+  if (!mul3(kRowsMaxWt, p.K, p.esize, &dy_reach) || dy_reach > kI32Max / 2) return false;
+  if (!mul_ok(p.S, p.dil, &x_cols) || x_cols > kI32Max) return false;
+  x_cols += p.W + 2 * p.pad + kRowsMaxXSpan;
+  if (!mul3(x_cols, p.C, p.esize, &x_reach) || x_reach > kI32Max / 2) return false;
   const int64_t sb = p.S < 4 ? p.S : 4;
   int64_t wt = 0;
   for (int64_t cand = kRowsMaxWt; cand >= 16; cand -= 16) {
@@ -224,6 +243,11 @@ bool plan_dense16_rows(const Problem& p, Plan* out) {
   if (p.dtype == CONV_WGRAD_F32 || p.stride != 1 || p.dil != 1) return false;
   if (p.C % 8 != 0 || p.K % 8 != 0 || p.Cg % 8 != 0 || p.Kg % 8 != 0) return false;
   if (p.W * p.C * 2 > kI32Max / 2 || p.Wo * p.K * 2 > kI32Max / 2) return false;
+  // Lane offsets reach 64 dY pixels into a unit and X columns from -pad to
+  // past the image by the staged 96 pixels plus the filter's reach.
+  int64_t dy_reach, x_reach;
+  if (!mul3(64, p.K, 2, &dy_reach) || dy_reach > kI32Max / 2) return false;
+  if (!mul3(p.W + 2 * p.pad + p.S + 96, p.C, 2, &x_reach) || x_reach > kI32Max / 2) return false;
   out->sb = (int32_t)(p.S < 4 ? p.S : 4);
   out->wt = p.Wo > 32 ? 64 : 32;
   out->s_blocks = ceil_div(p.S, out->sb);

@@ -8,8 +8,8 @@
 
 #include <type_traits>
 
-#include "../../include/conv_wgrad_peaks.h"
-#include "device_common.h"
+#include "probes.h"
+#include "../csrc/device_common.h"
 
 namespace cw {
 
@@ -102,7 +102,7 @@ conv_wgrad_status_t launch(const void* fn, int32_t blocks, void** params, void* 
 
 }  // namespace cw
 
-extern "C" conv_wgrad_status_t conv_wgrad_peak_read(const void* src, int64_t nbytes, int32_t blocks,
+extern "C" conv_wgrad_status_t cwprobe_read(const void* src, int64_t nbytes, int32_t blocks,
                                                     uint32_t* sink, void* stream, void* begin, void* end) {
   if (!src || !sink) return CONV_WGRAD_ERR_NULL_ARG;
   if (nbytes <= 0 || nbytes % 16 != 0 || blocks < 1 || blocks > 65536) return CONV_WGRAD_ERR_BAD_SHAPE;
@@ -113,7 +113,7 @@ extern "C" conv_wgrad_status_t conv_wgrad_peak_read(const void* src, int64_t nby
   return cw::launch(reinterpret_cast<const void*>(cw::peak_read_kernel), blocks, params, stream, begin, end);
 }
 
-extern "C" conv_wgrad_status_t conv_wgrad_peak_mfma(int32_t dtype, int64_t iters, int32_t blocks, float* sink,
+extern "C" conv_wgrad_status_t cwprobe_mfma(int32_t dtype, int64_t iters, int32_t blocks, float* sink,
                                                     void* stream, void* begin, void* end) {
   if (!sink) return CONV_WGRAD_ERR_NULL_ARG;
   if (dtype != CONV_WGRAD_F32 && dtype != CONV_WGRAD_BF16 && dtype != CONV_WGRAD_F16)

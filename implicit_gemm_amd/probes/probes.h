@@ -1,5 +1,6 @@
 /*
- * Achievable-peak probes of libconvwgrad.so (gfx950).
+ * Achievable-peak probes (gfx950), built as libcwprobes.so beside the weight-gradient
+ * library and used only to measure the chip (not part of its C ABI).
  *
  * The weight-gradient kernels are priced against the chip's nominal HBM
  * bandwidth (8 TB/s) and dense MFMA rates (f32 157.3 TFLOP/s, bf16 / fp16
@@ -14,12 +15,12 @@
  * own start and end (hipExtLaunchKernel), so hipEventElapsedTime(begin, end)
  * is the kernel's duration.  Status codes are those of conv_wgrad.h.
  */
-#ifndef CONV_WGRAD_PEAKS_H_
-#define CONV_WGRAD_PEAKS_H_
+#ifndef CWPROBES_H_
+#define CWPROBES_H_
 
 #include <stdint.h>
 
-#include "conv_wgrad.h"
+#include "../../include/conv_wgrad.h"
 
 #ifdef __cplusplus
 extern "C" {
@@ -38,7 +39,7 @@ extern "C" {
  *            meaningless (stored to only for one specific folded value)
  * NULL src or sink is NULL_ARG; a launch failure is ERR_HIP.
  */
-conv_wgrad_status_t conv_wgrad_peak_read(const void* src, int64_t nbytes, int32_t blocks,
+conv_wgrad_status_t cwprobe_read(const void* src, int64_t nbytes, int32_t blocks,
                                          uint32_t* sink, void* stream, void* begin, void* end);
 
 /*
@@ -58,11 +59,11 @@ conv_wgrad_status_t conv_wgrad_peak_read(const void* src, int64_t nbytes, int32_
  * FLOPs per call: blocks * 4 * iters * (16384 for f32, 131072 for bf16 / f16).
  * NULL sink is NULL_ARG; a launch failure is ERR_HIP.
  */
-conv_wgrad_status_t conv_wgrad_peak_mfma(int32_t dtype, int64_t iters, int32_t blocks, float* sink,
+conv_wgrad_status_t cwprobe_mfma(int32_t dtype, int64_t iters, int32_t blocks, float* sink,
                                          void* stream, void* begin, void* end);
 
 #ifdef __cplusplus
 }
 #endif
 
-#endif /* CONV_WGRAD_PEAKS_H_ */
+#endif /* CWPROBES_H_ */

@@ -123,19 +123,39 @@ typedef struct conv_wgrad_plan {
                               tensors span (diagnostic; one launch covers them all) */
 } conv_wgrad_plan_t;
 
-/* Human-readable name of a status code (static storage; never NULL). */
+/*
+ * Human-readable name of a status code (static storage; never NULL; "unknown
+ * status" for a value outside the enum).  Every failure is reported as one of
+ * these codes rather than as a silently wrong dW: a weight gradient that came
+ * back all zeros with no error is the failure rocm-libraries PR #11188
+ * ("fix silent zero wgrad", section Motivation) fixed.
+ */
 const char* conv_wgrad_status_string(conv_wgrad_status_t status);
 
 /*
- * Workspace bytes conv_wgrad and conv_wgrad_bias need for desc (0 when the plan
- * has one slice).  Pure host function.  Errors: NULL_ARG (desc or bytes NULL),
- * BAD_*, UNSUPPORTED.
+ * Workspace bytes conv_wgrad and conv_wgrad_bias need for desc: ks_count fp32
+ * slabs (each holding one slice's partial dW, then its partial db), or 0 when
+ * the plan has one slice.  The workspace is the split-K slab buffer of
+ * rocm-libraries PR #14393 (section "Two-stage split-K": every workgroup stores
+ * an fp32 partial tile into its slab; section "ABI, AOT and runtime": the
+ * split-K form takes a workspace argument).
+ *   desc  : read only
+ *   bytes : host pointer, written on success only
+ * Pure host function (no HIP call).  Errors: NULL_ARG (desc or bytes NULL),
+ * BAD_SHAPE / BAD_DTYPE / BAD_SPLIT as for conv_wgrad, UNSUPPORTED.
  */
 conv_wgrad_status_t conv_wgrad_workspace_size(const conv_wgrad_desc_t* desc, size_t* bytes);
 
 /*
- * Fill *plan with the plan for desc.  Pure host function (no HIP call); the
- * same validation as conv_wgrad.
+ * Fill *plan with the plan for desc: the stage-1 kernel, the reduction units,
+ * the split degree (split_k = -1 resolves it automatically, n >= 1 pins it, as
+ * in rocm-libraries PR #14393, section "Auto-deduced degree (split_k = -1)";
+ * the slices come from exact integer ceiling divisions, the form whose
+ * truncating variant under-counted the batch split in rocm-libraries
+ * PR #11188, section Technical Details), the grid and the workspace size.
+ *   desc : read only;  plan : host pointer, written on success only
+ * Pure host function (no HIP call); the same validation and errors as
+ * conv_wgrad (NULL_ARG for a NULL desc or plan).
  */
 conv_wgrad_status_t conv_wgrad_get_plan(const conv_wgrad_desc_t* desc, conv_wgrad_plan_t* plan);
 

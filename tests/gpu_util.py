@@ -44,3 +44,12 @@ def check_against_oracle(x, dy, shape: wd.ConvShape, dtype: str, split_k=-1, tol
     assert dw_gpu.shape == ref.shape, (dw_gpu.shape, ref.shape)
     assert err <= tol, "normalised error %.3e > %.1e for %s %s split_k=%s" % (err, tol, shape, dtype, split_k)
     return err
+
+
+def check_bias_against_oracle(dy, db_gpu, dtype: str, tol=None):
+    """Bias gradient db [K] from the GPU against the oracle's db = sum of dy per channel."""
+    ref, den = oracle.bgrad_ref(dy)
+    err = oracle.normalised_error(np.asarray(db_gpu, np.float64), ref, den)
+    tol = oracle.TOL[dtype] if tol is None else tol
+    assert err <= tol, "bias-gradient normalised error %.3e > %.1e (%s)" % (err, tol, dtype)
+    return err

@@ -15,32 +15,49 @@ import implicit_gemm_amd as iga
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "conv_wgrad.h")
-PEAKS_HEADER = os.path.join(ROOT, "include", "conv_wgrad_peaks.h")
+PROBES_HEADER = os.path.join(ROOT, "implicit_gemm_amd", "probes", "probes.h")
 GOLDEN = os.path.join(ROOT, "tests", "golden")
 
 
-def declared_functions(header=HEADER):
+PUBLIC_FUNCTIONS = {"conv_wgrad", "conv_wgrad_ex", "conv_wgrad_get_plan", "conv_wgrad_timed",
+                    "conv_wgrad_status_string", "conv_wgrad_workspace_size", "conv_wgrad_bias",
+                    "conv_wgrad_bias_timed"}
+
+
+def declared_functions(header=HEADER, prefix="conv_wgrad"):
     text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(conv_wgrad\w*)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(%s\w*)\s*\(" % prefix, text)))
+
+
+def exported_symbols(path):
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    return set(re.findall(r"\s[TW]\s(\w+)$", out, flags=re.M))
 
 
 def test_library_loads_and_exports_every_declared_symbol():
     lib = iga.load()
     headers = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
-    assert headers == [HEADER, PEAKS_HEADER]
-    assert set(declared_functions()) == {"conv_wgrad", "conv_wgrad_ex", "conv_wgrad_get_plan",
-                                         "conv_wgrad_timed", "conv_wgrad_status_string",
-                                         "conv_wgrad_workspace_size", "conv_wgrad_bias",
-                                         "conv_wgrad_bias_timed"}
-    assert set(declared_functions(PEAKS_HEADER)) == {"conv_wgrad_peak_read", "conv_wgrad_peak_mfma"}
-    names = sorted(set(n for h in headers for n in declared_functions(h)))
+    assert headers == [HEADER]
+    names = declared_functions()
+    assert set(names) == PUBLIC_FUNCTIONS
     for n in names:
         assert hasattr(lib, n), n
-    out = subprocess.run(["nm", "-D", "--defined-only", iga.LIB_PATH], capture_output=True,
-                         text=True, check=True).stdout
-    exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
+    exported = exported_symbols(iga.LIB_PATH)
     assert set(names) <= exported
+    # The measurement probes live in their own library, not in the product's ABI.
+    assert not any("probe" in n or "peak" in n for n in exported if n.startswith("conv_wgrad"))
+
+
+def test_probe_library_exports_its_declared_symbols():
+    from implicit_gemm_amd import probes
+    lib = probes.load()
+    names = declared_functions(PROBES_HEADER, prefix="cwprobe")
+    assert set(names) == {"cwprobe_read", "cwprobe_mfma"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) <= exported_symbols(probes.LIB_PATH)
 
 
 def test_struct_sizes_match_header_layout():
@@ -51,18 +68,19 @@ def test_struct_sizes_match_header_layout():
 
 def test_peak_probe_argument_errors():
     # Validation happens before any launch, so no GPU is needed.
-    lib = iga.load()
+    from implicit_gemm_amd import probes
+    lib = probes.load()
     fake = ctypes.c_void_p(0x10000)
-    assert lib.conv_wgrad_peak_read(None, 16, 1, fake, None, None, None) == 1          # NULL_ARG
-    assert lib.conv_wgrad_peak_read(fake, 16, 1, None, None, None, None) == 1
+    assert lib.cwprobe_read(None, 16, 1, fake, None, None, None) == 1          # NULL_ARG
+    assert lib.cwprobe_read(fake, 16, 1, None, None, None, None) == 1
     for nbytes, blocks in ((0, 1), (-16, 1), (24, 1), (16, 0), (16, 65537)):
-        assert lib.conv_wgrad_peak_read(fake, nbytes, blocks, fake, None, None, None) == 2  # BAD_SHAPE
-    assert lib.conv_wgrad_peak_read(ctypes.c_void_p(0x10008), 16, 1, fake, None, None, None) == 6
-    assert lib.conv_wgrad_peak_mfma(0, 1, 1, None, None, None, None) == 1
+        assert lib.cwprobe_read(fake, nbytes, blocks, fake, None, None, None) == 2  # BAD_SHAPE
+    assert lib.cwprobe_read(ctypes.c_void_p(0x10008), 16, 1, fake, None, None, None) == 6
+    assert lib.cwprobe_mfma(0, 1, 1, None, None, None, None) == 1
     for dtype in (3, -1):
-        assert lib.conv_wgrad_peak_mfma(dtype, 1, 1, fake, None, None, None) == 3       # BAD_DTYPE
+        assert lib.cwprobe_mfma(dtype, 1, 1, fake, None, None, None) == 3       # BAD_DTYPE
     for iters, blocks in ((0, 1), (1 << 31, 1), (1, 0), (1, 65537)):
-        assert lib.conv_wgrad_peak_mfma(0, iters, blocks, fake, None, None, None) == 2
+        assert lib.cwprobe_mfma(0, iters, blocks, fake, None, None, None) == 2
 
 
 def test_status_strings():
@@ -259,3 +277,38 @@ def test_one_hip_runtime_when_the_library_loads_first():
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.split()[0] == "1", out.stdout
+
+
+def test_launch_lane_limits_are_rejected_before_launch():
+    """A launch holds fewer than 2^32 lanes: a plan whose slab fold would need more
+    (E = 12288 * 9 * 12288 dW elements folded by 256-lane workgroups of 64
+    elements) is UNSUPPORTED, while the same problem with one slice (no fold) plans."""
+    lib = iga.load()
+    big = dict(N=1, C=12288, H=8, W=8, K=12288, R=3, S=3, pad=1)
+    p = iga.get_plan(D(split_k=1, **big))
+    assert p.ks_count == 1 and p.E == 12288 * 9 * 12288
+    d = D(split_k=2, **big)
+    assert (p.E // 64) * 256 >= 1 << 32
+    plan = iga.Plan()
+    assert lib.conv_wgrad_get_plan(ctypes.byref(d), ctypes.byref(plan)) == 5
+    n = ctypes.c_size_t(0)
+    assert lib.conv_wgrad_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 5
+    assert lib.conv_wgrad(ctypes.byref(d), 16, 16, 16, 16, None) == 5
+
+
+def test_row_kernel_lane_offsets_stay_32_bit():
+    """The row-unit kernels address a unit's 64 dY pixels with 32-bit lane offsets:
+    a channel count that would carry the last pixel's offset past 2^30 bytes must not
+    reach them (the general kernel, 64-bit addressed, takes the shape instead)."""
+    ok = iga.get_plan(D(N=1, C=4, H=1, W=1, K=4194300, R=1, S=1, pad=0))
+    assert ok.variant == 1                     # 64 * K * 4 < 2^30: the row kernel
+    over = iga.get_plan(D(N=1, C=4, H=1, W=1, K=4194308, R=1, S=1, pad=0))
+    assert 64 * 4194308 * 4 > (1 << 30) - 1
+    assert over.variant == 0                   # the general LDS kernel
+    # 16-bit: X columns reach (W + 2 pad + S + 96) pixels of C channels
+    ok16 = iga.get_plan(D(N=1, C=8, H=1, W=1, K=8, R=1, S=1, pad=0, dtype=iga.BF16))
+    assert ok16.variant == 3
+    c_over = -(-((1 << 30)) // (2 * (1 + 1 + 96))) + 8
+    c_over += (-c_over) % 8
+    over16 = iga.get_plan(D(N=1, C=c_over, H=1, W=1, K=8, R=1, S=1, pad=0, dtype=iga.BF16))
+    assert over16.variant != 3

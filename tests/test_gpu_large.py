@@ -5,12 +5,10 @@ returned an all-zero weight gradient once the batch pushed X past ~4 GB.  The
 inputs are generated once for N=192 (per-image seeded streams, so every
 smaller N is a prefix) and stay on the GPU; each N is one call on a prefix.
 
-At these sizes the oracle computes a sampled block of dW (a subset of output
-and input channels, which for a dense 1x1 filter is exactly the matching block
-of the full result), streamed image by image.  Properties that hold at any
-size check every element: the row and column sums of dW equal
-dY^T (X 1) and (dY 1)^T X in fp64, and no element is exactly zero or
-non-finite.
+The oracle streams every image through its fp64 loops (one image per worker
+thread, the per-image partials added in image order) and computes the whole
+[64, 96] result, so every dW element is compared with it at every N.  No
+element may be exactly zero or non-finite.
 """
 import numpy as np
 import pytest
@@ -21,29 +19,14 @@ from gpu_util import log
 
 pytestmark = pytest.mark.gpu
 
-K_IDX = np.array([0, 5, 17, 31, 32, 47, 58, 63])
-C_IDX = np.array([0, 3, 11, 24, 40, 51, 63, 64, 70, 81, 90, 95])
 CHUNK = 16
-ROWS = 16384
 
 
 def _image_terms(X, Y):
-    """fp64 contributions of one image: the oracle's sampled block and the row/column sums."""
-    acc = oracle.WgradAccumulator(len(C_IDX), X.shape[0], X.shape[1], len(K_IDX), 1, 1, nthreads=1)
-    acc.add(np.ascontiguousarray(X[None][..., C_IDX]), np.ascontiguousarray(Y[None][..., K_IDX]))
-    Xf = X.reshape(-1, X.shape[-1])
-    Yf = Y.reshape(-1, Y.shape[-1])
-    row = np.zeros(Yf.shape[1]); col = np.zeros(Xf.shape[1])
-    row_abs = np.zeros(Yf.shape[1]); col_abs = np.zeros(Xf.shape[1])
-    for i0 in range(0, Xf.shape[0], ROWS):
-        xb = Xf[i0:i0 + ROWS].astype(np.float64)
-        yb = Yf[i0:i0 + ROWS].astype(np.float64)
-        row += yb.T @ xb.sum(axis=1)
-        col += xb.T @ yb.sum(axis=1)
-        ax, ay = np.abs(xb), np.abs(yb)
-        row_abs += ay.T @ ax.sum(axis=1)
-        col_abs += ax.T @ ay.sum(axis=1)
-    return acc.dw[:, 0, 0, :], acc.abs_sum[:, 0, 0, :], row, col, row_abs, col_abs
+    """fp64 oracle contribution of one image: dW [K, C] and the |dY||X| sums [K, C]."""
+    acc = oracle.WgradAccumulator(X.shape[-1], X.shape[0], X.shape[1], Y.shape[-1], 1, 1, nthreads=1)
+    acc.add(X[None], Y[None])
+    return acc.dw[:, 0, 0, :], acc.abs_sum[:, 0, 0, :]
 
 
 @pytest.mark.timeout(900)
@@ -101,18 +84,13 @@ def test_large_1x1_sweep_past_4gb():
         dw = iga.wgrad(x[:N], dy[:N], 1, 1)
         torch.cuda.synchronize()
         g = dw.cpu().numpy()[:, 0, 0, :].astype(np.float64)
-        ref, ref_abs, r, c, ra, ca = snap[N]
         assert np.all(np.isfinite(g)), N
         assert int((g == 0).sum()) == 0, "exact zeros at N=%d" % N
-        blk = g[np.ix_(K_IDX, C_IDX)]
-        err = np.max(np.abs(blk - ref)) / ref_abs.max()
-        log("  sampled block normalised error %.3e" % err)
+        ref, ref_abs = snap[N]
+        err = oracle.normalised_error(g, ref, float(ref_abs.max()))
+        log("  full dW [%d x %d] normalised error %.3e (max |diff| %.3e, den %.3e)"
+            % (g.shape[0], g.shape[1], err, float(np.max(np.abs(g - ref))), float(ref_abs.max())))
         assert err <= oracle.TOL["f32"], (N, err)
-        # Row / column sums cover every element of dW.
-        e_row = np.max(np.abs(g.sum(axis=1) - r) / ra)
-        e_col = np.max(np.abs(g.sum(axis=0) - c) / ca)
-        log("  row-sum error %.3e, column-sum error %.3e" % (e_row, e_col))
-        assert e_row <= oracle.TOL["f32"] and e_col <= oracle.TOL["f32"], (N, e_row, e_col)
 
 
 @pytest.mark.parametrize("N", [1, 3])

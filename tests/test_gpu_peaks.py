@@ -1,4 +1,4 @@
-"""The achievable-peak probes through the C ABI (they compute nothing of the
+"""The achievable-peak probes of libcwprobes.so (they compute nothing of the
 gradient; these tests check that they run, stay in their buffers and time)."""
 import ctypes
 
@@ -15,8 +15,8 @@ def _cuda():
     import torch
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    import implicit_gemm_amd as iga
-    iga.load()
+    from implicit_gemm_amd import probes
+    probes.load()
 
 
 def _events():
@@ -31,13 +31,13 @@ def _events():
 
 def test_peak_read_leaves_sink_and_times():
     import torch
-    import implicit_gemm_amd as iga
+    from implicit_gemm_amd import probes
     hip, (e0, e1) = _events()
     buf = torch.ones(1 << 18, dtype=torch.float32, device="cuda")      # 1 MiB: every lane's XOR is 0
     sink = torch.full((64 + 1,), 7, dtype=torch.int32, device="cuda")   # one guard word past the blocks
     stream = torch.cuda.current_stream().cuda_stream
     for blocks in (1, 7, 64):
-        iga.peak_read(buf.data_ptr(), buf.numel() * 4, blocks, sink.data_ptr(), stream, e0, e1)
+        probes.peak_read(buf.data_ptr(), buf.numel() * 4, blocks, sink.data_ptr(), stream, e0, e1)
         assert hip.hipEventSynchronize(e1) == 0
         ms = ctypes.c_float()
         assert hip.hipEventElapsedTime(ctypes.byref(ms), e0, e1) == 0
@@ -50,14 +50,14 @@ def test_peak_read_leaves_sink_and_times():
 @pytest.mark.parametrize("dtype", [0, 1, 2])
 def test_peak_mfma_writes_finite_repeatable_sums(dtype):
     import torch
-    import implicit_gemm_amd as iga
+    from implicit_gemm_amd import probes
     blocks = 3
     sink = torch.full((blocks * 256 + 64,), -1.0, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
-    iga.peak_mfma(dtype, 5, blocks, sink.data_ptr(), stream)
+    probes.peak_mfma(dtype, 5, blocks, sink.data_ptr(), stream)
     torch.cuda.synchronize()
     a = sink.cpu().numpy().copy()
-    iga.peak_mfma(dtype, 5, blocks, sink.data_ptr(), stream)
+    probes.peak_mfma(dtype, 5, blocks, sink.data_ptr(), stream)
     torch.cuda.synchronize()
     b = sink.cpu().numpy()
     assert np.isfinite(a[:blocks * 256]).all() and (a[:blocks * 256] > 0).all()
