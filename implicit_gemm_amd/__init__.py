@@ -16,6 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libconvwgrad.so")
 
 F32, BF16, F16 = 0, 1, 2
+NOALLOC_SCRATCH_BYTES = 64 << 20   # CONV_WGRAD_NOALLOC_SCRATCH_BYTES
 PATH_DENSE, PATH_DIRECT = 0, 1
 
 STATUS = {
@@ -100,6 +101,9 @@ def load():
     lib.conv_wgrad_bias_timed.argtypes = [P(Desc), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.conv_wgrad_noalloc.restype = ctypes.c_int
+    lib.conv_wgrad_noalloc.argtypes = [P(Desc), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p]
     _lib = lib
     return lib
 
@@ -166,6 +170,14 @@ def conv_wgrad_bias_timed(desc: Desc, x_ptr: int, dy_ptr: int, dw_ptr: int, db_p
                                       ev_end or None)
     if st != 0:
         raise ConvWgradError(st, "conv_wgrad_bias_timed")
+
+
+def conv_wgrad_noalloc(desc: Desc, x_ptr: int, dy_ptr: int, dw_ptr: int, db_ptr: int, stream: int) -> None:
+    """Weight gradient (and the bias gradient when db_ptr is non-zero) with the
+    library-owned workspace of NOALLOC_SCRATCH_BYTES per GPU: no allocation."""
+    st = load().conv_wgrad_noalloc(ctypes.byref(desc), x_ptr, dy_ptr, dw_ptr, db_ptr or None, stream or None)
+    if st != 0:
+        raise ConvWgradError(st, "conv_wgrad_noalloc")
 
 
 def _dtype_code(t):

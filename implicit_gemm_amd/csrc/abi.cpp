@@ -190,4 +190,16 @@ conv_wgrad_status_t conv_wgrad_bias_timed(const conv_wgrad_desc_t* desc, const v
              stage1_end);
 }
 
+conv_wgrad_status_t conv_wgrad_noalloc(const conv_wgrad_desc_t* desc, const void* x, const void* dy,
+                                       float* dw, float* db, void* stream) {
+  cw::Plan plan;
+  conv_wgrad_status_t st = get_plan(desc, &plan);
+  if (st != CONV_WGRAD_OK) return st;
+  if (!x || !dy || !dw) return CONV_WGRAD_ERR_NULL_ARG;
+  if (plan.pub.ws_bytes > cw::kNoallocScratchBytes) return CONV_WGRAD_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (plan.pub.ws_bytes > 0 && cw::noalloc_scratch(&ws) != hipSuccess) return CONV_WGRAD_ERR_HIP;
+  return run(desc, x, dy, dw, db != nullptr, db, ws, true, cw::kNoallocScratchBytes, stream);
+}
+
 }  // extern "C"

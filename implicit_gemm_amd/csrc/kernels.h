@@ -54,6 +54,11 @@ hipError_t launch_depthwise(const Plan& plan, const void* x, const void* dy, Sta
                             hipStream_t stream);
 hipError_t launch_direct(const Plan& plan, const void* x, const void* dy, Stage1Out out,
                          hipStream_t stream);
+// Library-owned workspace of conv_wgrad_noalloc: the device address of this
+// process's copy on the current device (looked up once per device).
+constexpr size_t kNoallocScratchBytes = CONV_WGRAD_NOALLOC_SCRATCH_BYTES;
+hipError_t noalloc_scratch(void** ptr);
+
 // Folds the slabs into dw and, when db is not null, into db.
 hipError_t launch_slab_reduce(const Plan& plan, float* ws, float* dw, float* db, hipStream_t stream);
 

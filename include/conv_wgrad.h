@@ -217,6 +217,29 @@ conv_wgrad_status_t conv_wgrad_bias_timed(const conv_wgrad_desc_t* desc, const v
                                           size_t ws_bytes, void* stream, void* stage1_begin,
                                           void* stage1_end);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): conv_wgrad_bias
+ * without the workspace argument.  The slabs live in a library-owned device
+ * array of CONV_WGRAD_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, held until the
+ * process ends; its device address is looked up (hipGetSymbolAddress) on the
+ * first call on each device, with that device current.  No call allocates or
+ * frees memory (no hipMalloc / hipFree, no allocating library routine).
+ *   db : NULL for the weight gradient only (dw then equals conv_wgrad's), or
+ *        an fp32 [K] buffer for the bias gradient as in conv_wgrad_bias
+ * The other arguments, the results and the errors are those of conv_wgrad_bias,
+ * plus CONV_WGRAD_ERR_WORKSPACE when conv_wgrad_workspace_size(desc) exceeds
+ * CONV_WGRAD_NOALLOC_SCRATCH_BYTES (pin a smaller split_k to fit) and
+ * CONV_WGRAD_ERR_HIP when the address lookup fails; errors are returned
+ * before anything is enqueued.  The current device must be the stream's.
+ * Every call on one GPU shares that GPU's array (nothing in it needs clearing:
+ * each slab element is written before the fold reads it), so calls that
+ * overlap in time on one GPU (other streams, other host threads) race.
+ */
+#define CONV_WGRAD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+conv_wgrad_status_t conv_wgrad_noalloc(const conv_wgrad_desc_t* desc, const void* x, const void* dy,
+                                       float* dw, float* db, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

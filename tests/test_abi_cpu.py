@@ -21,7 +21,7 @@ GOLDEN = os.path.join(ROOT, "tests", "golden")
 
 PUBLIC_FUNCTIONS = {"conv_wgrad", "conv_wgrad_ex", "conv_wgrad_get_plan", "conv_wgrad_timed",
                     "conv_wgrad_status_string", "conv_wgrad_workspace_size", "conv_wgrad_bias",
-                    "conv_wgrad_bias_timed"}
+                    "conv_wgrad_bias_timed", "conv_wgrad_noalloc"}
 
 
 def declared_functions(header=HEADER, prefix="conv_wgrad"):
@@ -140,6 +140,9 @@ def test_null_arguments():
     assert lib.conv_wgrad_bias(ctypes.byref(d), 16, 16, None, 16, 16, ws, None) == 1
     assert lib.conv_wgrad_bias(ctypes.byref(d), 16, 16, 16, 16, None, ws, None) == 1
     assert lib.conv_wgrad_bias_timed(ctypes.byref(d), 16, 16, 16, None, 16, ws, None, None, None) == 1
+    assert lib.conv_wgrad_noalloc(ctypes.byref(d), None, 16, 16, None, None) == 1
+    assert lib.conv_wgrad_noalloc(ctypes.byref(d), 16, 16, None, 16, None) == 1
+    assert lib.conv_wgrad_noalloc(None, 16, 16, 16, None, None) == 1
 
 
 def test_misaligned_and_small_workspace():
