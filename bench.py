@@ -1,37 +1,40 @@
 #!/usr/bin/env python3
 """Benchmark of the MI355X convolution weight gradient (one GPU).
 
-A step is one full weight-gradient call (stage 1 + the slab reduce when the
-plan has several slices) on inputs already resident in HBM.  The default
-workload is the 3x3 fp32 wgrad, N=32, C=K=64, H=W=56, pad 1.  Prints one
-JSON line:
+A step is one full weight-gradient call (stage 1 + the slab fold when the
+plan has several slices) on inputs already resident in HBM.  With no
+--config, one run measures every workload of the study and prints ONE JSON
+line whose headline is the largest single-GPU workload, the 1x1 fp32 wgrad
+C=96 K=64 512x512 at N=192 (32.2 GB of X and dY, so every step reads its
+inputs from HBM; no cache holds them):
 
-  value           TFLOP/s of the whole call over K back-to-back steps (after
-                  W warm-up steps and --prewarm-s seconds of untimed steps
-                  that bring the GPU to its clocks under load)
-  roofline        the stage-1 kernel alone, its duration taken from HIP events
-                  on its own dispatch in each of K further back-to-back steps
-                  right after the timed region (kept out of that region: a
-                  launch that carries events costs the call GPU time),
-                  against the MI355X peak of its bound (f32 MFMA or HBM);
-                  traffic = HBM bytes per launch from the FETCH_SIZE /
-                  WRITE_SIZE counter table in profiles/hbm_traffic.md when
-                  it was taken on the current kernel source, else null
-  whole_call_roofline_frac  the same roofline fraction for the whole call
-                  (stage 1 + the slab reduce, the time behind value)
-  cold_cache      per-call event times with a cache flush before each call (a
-                  read of a clean 1 GiB buffer)
-  cpu_baseline    the CPU oracle (test infrastructure) timed on the host cores,
-                  with the host CPU model; for 1x1 workloads also numpy's
-                  float64 BLAS closed form dW = dY^T X on the same images
+  value, ms_per_step  whole-call TFLOP/s over K back-to-back steps between
+                  synchronisations (after W warm-up steps and --prewarm-s
+                  seconds of untimed steps that bring the GPU to its clocks)
+  roofline        the dominant (stage-1) kernel: algorithmic bytes or FLOPs
+                  per launch / its mean duration from HIP events stamped by
+                  its own dispatch in K further steps, against the MI355X
+                  peak of its bound; traffic = HBM bytes per launch from the
+                  FETCH_SIZE / WRITE_SIZE counter table (profiles/
+                  hbm_traffic.md) when it was taken on the current source
+  whole_call_roofline_frac  the same fraction for the whole call (value)
+  cpu_baseline    the CPU oracle (test infrastructure) on the host cores, on a
+                  bounded sample of the workload, with the host CPU model
+  configs         one record per workload (the five of the study, the 1x1
+                  case at N=64 and N=192): the cold whole call -- each call
+                  after a read of a clean 1 GiB buffer that evicts the inputs
+                  from the L2s and the 256 MB MALL, HIP events on the stream
+                  around stage 1 + fold, median / min / p90 of --cold calls --
+                  with its roofline fraction; the stage-1 kernel alone, cold
+                  and hot (dispatch-stamped events, in calls of their own);
+                  the hot back-to-back call; counter traffic; cpu_baseline
 
-  python bench.py --peaks   achievable streaming-read bandwidth (buffers of the
-                  workloads' input sizes, hot and cold) and MFMA rates, beside
-                  the published peaks; one JSON line
+  python bench.py --config NAME [--n N]   only that workload (its record is
+                  the headline; value is then the hot back-to-back figure)
+  python bench.py --peaks   achievable streaming-read bandwidth and MFMA
+                  rates beside the published peaks; one JSON line
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--n N] [--no-cpu] [--bias]
-
-With --bias every step is conv_wgrad_bias (the weight gradient and the fused
+With --bias every call is conv_wgrad_bias (the weight gradient and the fused
 bias gradient db = sum dY); value still counts the weight-gradient FLOPs.
 """
 from __future__ import annotations
@@ -75,8 +78,11 @@ def source_digest(variant):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, digest):
-    """HBM bytes per stage-1 launch from the counter table, if taken on this source."""
+def measured_traffic(workload, digest, n):
+    """HBM bytes per stage-1 launch from the counter table, if taken on this source.
+
+    Table rows: | workload | N | kernel | source digest | dispatches | FETCH_SIZE KiB |
+    WRITE_SIZE KiB | fetch scale | write scale | traffic bytes | algorithmic bytes |"""
     try:
         with open(TRAFFIC_TABLE) as f:
             lines = f.read().splitlines()
@@ -84,9 +90,9 @@ def measured_traffic(workload, digest):
         return None
     for line in lines:
         cells = [c.strip() for c in line.strip().strip("|").split("|")]
-        if len(cells) >= 9 and cells[0] == workload and cells[2] == digest:
+        if len(cells) >= 11 and cells[0] == workload and cells[1] == str(n) and cells[3] == digest:
             try:
-                return int(cells[8].replace(",", ""))
+                return int(cells[9].replace(",", ""))
             except ValueError:
                 return None
     return None
@@ -201,28 +207,93 @@ def roofline_for(shape, dtype, seconds, traffic=None):
             "frac": round(achieved / PEAK["hbm_gbs"], 4), "traffic": traffic}
 
 
-def cpu_baseline(wl, x, dy, reps):
-    """The fp64 oracle on the host cores, on the first images of the workload
-    (all of them unless that exceeds CPU_SAMPLE_FLOPS), in TFLOP/s."""
-    import oracle
+ALL_RECORDS = [("c1_1x1_tiny_f32", None), ("c2_3x3_f32", None), ("c3_dw7x7_bf16", None),
+               ("c4a_grp3x3_cpg4_f16", None), ("c4b_grp3x3_cpg8_f16", None), ("c5_1x1_big_f32", 64)]
+HEADLINE = ("c5_1x1_big_f32", 192)
+FAMILY = {0: "dense_lds", 1: "dense_rows", 2: "dense_1x1", 3: "dense16_rows", 10: "direct_elem",
+          11: "grouped16", 12: "depthwise_mfma", 13: "grouped16_rows"}
+
+
+def resolve(name, n):
+    """Workload and shape for a configuration name (N-swept workloads at batch n, default 64)."""
+    import wgrad_data as wd
+    wl = wd.workload(name)
     s = wl.shape
+    if wl.n_sweep:
+        n = n or 64
+        if n not in wl.n_sweep:
+            raise SystemExit("--n must be one of %s for %s" % (wl.n_sweep, wl.name))
+        s = s.with_n(n)
+        wl = wd.Workload(wl.name, s, wl.dtype, wl.x_dist, wl.dy_dist, wl.seed, wl.note, wl.n_sweep)
+    elif n:
+        raise SystemExit("--n applies only to an N-swept workload")
+    return wl, s
+
+
+def device_inputs(wl, s, dev):
+    """x, dy on the device (the seeded per-image draws of wgrad_data), filled in
+    chunks of images through pinned host staging so host memory stays bounded."""
+    import os as _os
+    from concurrent.futures import ThreadPoolExecutor
+    import torch
+    import wgrad_data as wd
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[wl.dtype]
+    x = torch.empty((s.N, s.H, s.W, s.C), dtype=tdt, device=dev)
+    dy = torch.empty((s.N, s.Ho, s.Wo, s.K), dtype=tdt, device=dev)
+    per_img = (s.H * s.W * s.C + s.Ho * s.Wo * s.K) * 4
+    chunk = max(1, min(s.N, (1 << 31) // per_img))
+    if chunk >= s.N:
+        xh, dyh = wd.make_inputs(wl)
+        x.copy_(torch.from_numpy(xh).to(tdt))
+        dy.copy_(torch.from_numpy(dyh).to(tdt))
+        return x, dy
+    xs = torch.empty((chunk, s.H, s.W, s.C), dtype=torch.float32, pin_memory=True)
+    dys = torch.empty((chunk, s.Ho, s.Wo, s.K), dtype=torch.float32, pin_memory=True)
+    xa, dya = xs.numpy(), dys.numpy()
+    threads = min(16, max(1, len(_os.sched_getaffinity(0))))
+
+    def fill(i, n):
+        wd.draw_images(wl.seed, wd.X_ID, n, 1, s.H, s.W, s.C, wl.x_dist, out=xa[i:i + 1], threads=1)
+        wd.draw_images(wl.seed, wd.DY_ID, n, 1, s.Ho, s.Wo, s.K, wl.dy_dist, out=dya[i:i + 1], threads=1)
+
+    with ThreadPoolExecutor(threads) as ex:
+        for n0 in range(0, s.N, chunk):
+            cnt = min(chunk, s.N - n0)
+            list(ex.map(lambda i: fill(i, n0 + i), range(cnt)))
+            if wl.dtype != "f32":
+                raise SystemExit("chunked staging is for fp32 workloads")
+            x[n0:n0 + cnt].copy_(xs[:cnt], non_blocking=True)
+            dy[n0:n0 + cnt].copy_(dys[:cnt], non_blocking=True)
+            torch.cuda.synchronize()   # the staging buffers are refilled by the next chunk
+    return x, dy
+
+
+def cpu_baseline(wl, s, seconds):
+    """The fp64 oracle on the host cores, on the first images of the workload
+    (as many as fit about seconds / 3 of oracle time per run; at least three
+    runs and about `seconds` in all), in TFLOP/s."""
+    import oracle
+    import wgrad_data as wd
     threads = oracle.default_threads()
     per_image = s.flops() / s.N
-    n_s = int(max(1, min(s.N, CPU_SAMPLE_FLOPS // per_image)))
-    xs, dys = x[:n_s], dy[:n_s]
-    # At least `reps` runs, and more until about CPU_SAMPLE_SECONDS of oracle work.
+    # Size the sample from one timed image.
+    x1, dy1 = wd.make_inputs(wl, 0, 1)
+    t0 = time.perf_counter()
+    oracle.wgrad_ref(x1, dy1, s.R, s.S, s.pad, s.stride, s.dilation, s.groups, nthreads=threads)
+    t_img = max(time.perf_counter() - t0, 1e-6)
+    n_s = int(max(1, min(s.N, (seconds / 3.0) / t_img)))
+    xs, dys = wd.make_inputs(wl, 0, n_s)
     times = []
-    while len(times) < reps or (sum(times) < CPU_SAMPLE_SECONDS and len(times) < 200):
+    while len(times) < 3 or (sum(times) < seconds and len(times) < 200):
         t0 = time.perf_counter()
         oracle.wgrad_ref(xs, dys, s.R, s.S, s.pad, s.stride, s.dilation, s.groups, nthreads=threads)
         times.append(time.perf_counter() - t0)
-    reps = len(times)
     t = statistics.median(times)
     what = "whole workload" if n_s == s.N else "first %d of %d images" % (n_s, s.N)
     out = {"value": round(per_image * n_s / t / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
            "kind": "oracle",
-           "sample": "%s (%s), median of %d runs, fp64 C oracle, %.2f s per run"
-                     % (what, wl.name, reps, t),
+           "sample": "%s of %s, median of %d runs, fp64 C oracle, %.2f s per run"
+                     % (what, wl.name, len(times), t),
            "cpu_model": cpu_model()}
     if s.R == 1 and s.S == 1 and s.stride == 1 and s.pad == 0 and s.groups == 1:
         # A 1x1 weight gradient is one product, dW = dY^T X over all pixels:
@@ -250,21 +321,135 @@ def cpu_model():
     return "unknown"
 
 
+def _pct(vals, q):
+    v = sorted(vals)
+    return v[int(q * (len(v) - 1))]
+
+
+def measure(wl, s, x, dy, args, hip, cold_reps, bias=False):
+    """Time one workload on resident inputs; returns (record, hot wall seconds per step,
+    hot stage-1 mean seconds)."""
+    import numpy as np
+    import torch
+    import implicit_gemm_amd as iga
+    import wgrad_data as wd
+    dev = x.device
+    d = iga.desc_for(x, dy, s.R, s.S, s.pad, s.stride, s.dilation, s.groups, args.split_k)
+    plan = iga.get_plan(d)
+    dw = torch.empty((s.K, s.R, s.S, s.Cg), dtype=torch.float32, device=dev)
+    db = torch.empty((s.K,), dtype=torch.float32, device=dev)
+    ws_bytes = int(plan.ws_bytes)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    sp = torch.cuda.current_stream(dev).cuda_stream
+    wsp = ws.data_ptr() if ws_bytes else 0
+
+    def step(ev0=0, ev1=0):
+        if bias:
+            iga.conv_wgrad_bias_timed(d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(), db.data_ptr(), wsp,
+                                      ws_bytes, sp, ev0, ev1)
+        elif ev0 or ev1:
+            iga.conv_wgrad_timed(d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(), wsp, ws_bytes, sp, ev0, ev1)
+        else:
+            iga.conv_wgrad_ex(d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(), wsp, ws_bytes, sp)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # Clock warm-up: the GPU leaves its idle clocks only after some time under load.
+    t_pre = time.perf_counter()
+    while time.perf_counter() - t_pre < args.prewarm_s:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+
+    # Timed region: K back-to-back plain steps between synchronisations.
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+
+    # Stage-1 durations: K further steps whose stage-1 dispatch stamps its own
+    # start and end into HIP events (the dominant kernel's launch duration).
+    evs = [(hip.event(), hip.event()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        step(a, b)
+    torch.cuda.synchronize()
+    k_ms = [hip.elapsed_ms(a, b) for a, b in evs]
+    for a, b in evs:
+        hip.destroy(a)
+        hip.destroy(b)
+
+    # Cold calls: before each, a read of a clean 1 GiB buffer evicts the inputs
+    # from the L2s and the MALL (queued just before the call, so the GPU never
+    # idles).  Series 1: events on the stream around the plain call (stage 1 +
+    # fold together, no dispatch events).  Series 2: the stage-1 dispatch alone.
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    probe = torch.empty((), dtype=torch.float32, device=dev)
+    e0, e1, e2, e3 = hip.event(), hip.event(), hip.event(), hip.event()
+    torch.cuda.synchronize()
+    whole, stage1 = [], []
+    for _ in range(cold_reps):
+        torch.amax(flush, dim=0, out=probe)
+        hip.record(e0, sp)
+        step()
+        hip.record(e1, sp)
+        whole.append(hip.elapsed_ms(e0, e1))
+    for _ in range(cold_reps):
+        torch.amax(flush, dim=0, out=probe)
+        step(e2, e3)
+        stage1.append(hip.elapsed_ms(e2, e3))
+    for e in (e0, e1, e2, e3):
+        hip.destroy(e)
+    del flush, probe
+    torch.cuda.synchronize()
+    dw_h = dw.cpu().numpy()
+
+    cold_med = statistics.median(whole) * 1e-3
+    digest = source_digest(plan.variant)
+    traffic = None if bias else measured_traffic(wl.name, digest, s.N)
+    rec = {
+        "workload": wl.name, "note": wl.note, "dtype": wl.dtype,
+        "N": s.N, "C": s.C, "H": s.H, "W": s.W, "K": s.K, "R": s.R, "S": s.S, "pad": s.pad,
+        "stride": s.stride, "dilation": s.dilation, "groups": s.groups,
+        "kernel": FAMILY.get(int(plan.variant), str(plan.variant)), "variant": int(plan.variant),
+        "ks_count": int(plan.ks_count), "split_k": args.split_k, "bias_gradient": bool(bias),
+        "flops": s.flops(), "algorithmic_bytes": s.algorithmic_bytes(wd.IN_BYTES[wl.dtype]),
+        "cold_call_us": {"median": round(cold_med * 1e6, 2), "min": round(min(whole) * 1e3, 2),
+                         "p90": round(_pct(whole, 0.9) * 1e3, 2), "calls": cold_reps},
+        "tflops": round(s.flops() / cold_med / 1e12, 3),
+        "roofline": roofline_for(s, wl.dtype, cold_med, traffic),
+        "stage1_cold_us": round(statistics.median(stage1) * 1e3, 2),
+        "stage1_cold_frac": roofline_for(s, wl.dtype, statistics.median(stage1) * 1e-3)["frac"],
+        "hot_call_us": round(wall * 1e6, 2),
+        "hot_stage1_us": round(statistics.mean(k_ms) * 1e3, 2),
+        "hot_stage1_frac": roofline_for(s, wl.dtype, statistics.mean(k_ms) * 1e-3)["frac"],
+        "source_digest": digest,
+        "check": {"zeros": int((dw_h == 0).sum()), "finite": bool(np.isfinite(dw_h).all())},
+    }
+    if s.flops() < 1e6:
+        rec["roofline"]["note"] = "launch-latency bound (roofline time ~1 ns): the call time is its latency"
+    return rec, wall, statistics.mean(k_ms) * 1e-3
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default=DEFAULT_CONFIG)
+    ap.add_argument("--config", default=None, help="only this workload (default: all, headline 1x1 N=192)")
     ap.add_argument("--split-k", type=int, default=-1)
     ap.add_argument("--n", type=int, default=0, help="batch of an N-swept workload (default 64)")
-    ap.add_argument("--cold", type=int, default=20, help="cold-cache calls (0 = skip)")
+    ap.add_argument("--cold", type=int, default=50, help="cold-cache calls per series (1x1 512x512: 5)")
     ap.add_argument("--prewarm-s", type=float, default=0.3,
                     help="seconds of untimed steps after the warm-up steps (clock ramp)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="oracle seconds for the headline cpu_baseline (3 s per other record)")
     ap.add_argument("--bias", action="store_true",
                     help="time conv_wgrad_bias (dW and the fused bias gradient db = sum dY)")
-    ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--peaks", action="store_true",
                     help="measure the achievable streaming-read bandwidth and MFMA rates and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -277,23 +462,22 @@ def main():
               "(--gpus %d is not supported)" % args.gpus, file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
     import implicit_gemm_amd as iga
-    import wgrad_data as wd
 
     if args.digest:
-        s = wd.workload(args.config).shape
+        wl, s = resolve(args.config, args.n) if args.config else resolve(*HEADLINE)
         d = iga.make_desc(s.N, s.C, s.H, s.W, s.K, s.R, s.S, s.pad, s.stride, s.dilation, s.groups,
-                          {"f32": 0, "bf16": 1, "f16": 2}[wd.workload(args.config).dtype], args.split_k)
+                          {"f32": 0, "bf16": 1, "f16": 2}[wl.dtype], args.split_k)
         v = int(iga.get_plan(d).variant)
-        print(json.dumps({"workload": args.config, "variant": v, "source": VARIANT_SOURCE[v],
+        print(json.dumps({"workload": wl.name, "N": s.N, "variant": v, "source": VARIANT_SOURCE[v],
                           "digest": source_digest(v)}))
         return 0
 
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         return 1
+    iga.load()
     if args.peaks:
         print(json.dumps({"peaks": measure_peaks(Hip())}))
         return 0
@@ -305,147 +489,73 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": src.numel() * 4, "copies": 3}))
         return 0
-    wl = wd.workload(args.config)
-    s = wl.shape
-    if wl.n_sweep:
-        # N-swept workload: N = 64 unless --n picks another point of the sweep.
-        n = args.n if args.n else 64
-        if n not in wl.n_sweep:
-            print("--n must be one of %s for %s" % (wl.n_sweep, wl.name), file=sys.stderr)
-            return 2
-        s = s.with_n(n)
-        wl = wd.Workload(wl.name, s, wl.dtype, wl.x_dist, wl.dy_dist, wl.seed, wl.note)
-    elif args.n:
-        print("--n applies only to an N-swept workload", file=sys.stderr)
-        return 2
-    log("workload", wl.name, s, wl.dtype)
-    x_h, dy_h = wd.make_inputs(wl)
+
     dev = torch.device("cuda:0")
-    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[wl.dtype]
-    x = torch.from_numpy(x_h).to(tdt).to(dev)
-    dy = torch.from_numpy(dy_h).to(tdt).to(dev)
-    d = iga.desc_for(x, dy, s.R, s.S, s.pad, s.stride, s.dilation, s.groups, args.split_k)
-    plan = iga.get_plan(d)
-    dw = torch.empty((s.K, s.R, s.S, s.Cg), dtype=torch.float32, device=dev)
-    ws_bytes = int(plan.ws_bytes)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
-    sp = stream.cuda_stream
     hip = Hip()
-    torch.cuda.synchronize()
+    records = []
+    if args.config:
+        plan_runs = []
+        head_name, head_n = args.config, args.n
+    else:
+        plan_runs = ALL_RECORDS
+        head_name, head_n = HEADLINE
 
-    db = torch.empty((s.K,), dtype=torch.float32, device=dev)
+    def cold_reps_for(s):
+        return 5 if s.flops() > 1e11 else args.cold
 
-    def step(ev0=0, ev1=0):
-        if args.bias:
-            iga.conv_wgrad_bias_timed(d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(), db.data_ptr(),
-                                      ws.data_ptr() if ws_bytes else 0, ws_bytes, sp, ev0, ev1)
+    big = None   # device inputs of the N-swept workload at the headline batch, shared by its records
+    hwl, hs = resolve(head_name, head_n)
+    for name, n in plan_runs:
+        wl, s = resolve(name, n)
+        log("record", wl.name, s, wl.dtype)
+        if wl.n_sweep and hwl.name == wl.name and s.N <= hs.N:
+            if big is None:
+                big = device_inputs(hwl, hs, dev)
+            x, dy = big[0][:s.N], big[1][:s.N]
         else:
-            iga.conv_wgrad_timed(d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(),
-                                 ws.data_ptr() if ws_bytes else 0, ws_bytes, sp, ev0, ev1)
+            x, dy = device_inputs(wl, s, dev)
+        rec, _, _ = measure(wl, s, x, dy, args, hip, cold_reps_for(s), args.bias)
+        if not args.no_cpu:
+            rec["cpu_baseline"] = cpu_baseline(wl, s, 3.0)
+        records.append(rec)
+        log(json.dumps(rec))
+        del x, dy
+        torch.cuda.empty_cache()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    # Clock warm-up: the GPU leaves its idle clocks only after some time under
-    # load, so untimed steps run until --prewarm-s seconds have passed.
-    t_pre = time.perf_counter()
-    prewarm_steps = 0
-    while time.perf_counter() - t_pre < args.prewarm_s:
-        for _ in range(10):
-            step()
-        torch.cuda.synchronize()
-        prewarm_steps += 10
-
-    # Timed region: K back-to-back steps, no per-call events (a launch that
-    # carries timing events costs the call several microseconds of GPU time).
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    # Stage-1 kernel durations: the next K back-to-back steps, with HIP events
-    # that take the stage-1 dispatch's own start and end timestamps.
-    evs = [(hip.event(), hip.event()) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(*evs[i])
-    torch.cuda.synchronize()
-    k_ms = [hip.elapsed_ms(a, b) for a, b in evs]
-    for a, b in evs:
-        hip.destroy(a)
-        hip.destroy(b)
-
-    # Cold-cache calls (outside the timed region): before each, a read of a
-    # 1 GiB buffer (written once beforehand) evicts the inputs from the L2s and
-    # the 256 MB MALL and leaves clean lines, so the call neither hits the
-    # caches nor competes with the write-back of a flush's dirty lines.
-    cold = None
-    if args.cold > 0:
-        flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-        probe = torch.empty((), dtype=torch.float32, device=dev)
-        torch.cuda.synchronize()
-        e0, e1, e2 = hip.event(), hip.event(), hip.event()
-        whole, stage1 = [], []
-        for _ in range(args.cold):
-            torch.amax(flush, dim=0, out=probe)   # queued just before the call: no idle gap
-            hip.record(e0, sp)
-            step(e1, e2)
-            e3 = hip.event()
-            hip.record(e3, sp)
-            whole.append(hip.elapsed_ms(e0, e3))
-            stage1.append(hip.elapsed_ms(e1, e2))
-            hip.destroy(e3)
-        whole.sort()
-        cold = {"call_ms_median": round(statistics.median(whole), 5), "call_ms_min": round(whole[0], 5),
-                "call_ms_p90": round(whole[int(0.9 * (len(whole) - 1))], 5),
-                "stage1_ms_median": round(statistics.median(stage1), 5),
-                "tflops_median": round(s.flops() / (statistics.median(whole) * 1e-3) / 1e12, 3)}
-        del flush, probe
-
-    torch.cuda.synchronize()
-    dw_h = dw.cpu().numpy()
-    zeros = int((dw_h == 0).sum())
-    finite = bool(np.isfinite(dw_h).all())
-
-    ms_per_step = wall / args.steps * 1e3
-    value = s.flops() / (wall / args.steps) / 1e12
-    stage1_avg_s = statistics.mean(k_ms) * 1e-3
-    roof = roofline_for(s, wl.dtype, stage1_avg_s,
-                        None if args.bias else measured_traffic(wl.name, source_digest(plan.variant)))
-
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline(wl, x_h, dy_h, args.cpu_reps)
-
+    log("headline", hwl.name, hs, hwl.dtype)
+    if big is None:
+        big = device_inputs(hwl, hs, dev)
+    rec, wall, stage1_s = measure(hwl, hs, big[0], big[1], args, hip, cold_reps_for(hs), args.bias)
+    cpu = None if args.no_cpu else cpu_baseline(hwl, hs, args.cpu_seconds)
+    if cpu:
+        rec["cpu_baseline"] = cpu
+    records.append(rec)
+    log(json.dumps(rec))
+    roof = roofline_for(hs, hwl.dtype, stage1_s, rec["roofline"]["traffic"])
     out = {
         "metric": "wgrad TFLOP/s and % of MFMA-or-HBM roofline per conv shape, 1xMI355X",
-        "value": round(value, 3),
+        "value": round(hs.flops() / wall / 1e12, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "prewarm_steps": prewarm_steps,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(wall * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wl.dtype,
+        "dtype": hwl.dtype,
         "data": "synthetic (seeded PCG64 per image)",
-        "config": {"workload": wl.name, "note": wl.note, "N": s.N, "C": s.C, "H": s.H, "W": s.W,
-                   "K": s.K, "R": s.R, "S": s.S, "pad": s.pad, "stride": s.stride,
-                   "dilation": s.dilation, "groups": s.groups, "split_k": args.split_k,
-                   "ks_count": int(plan.ks_count), "path": int(plan.path), "variant": int(plan.variant),
-                   "bias_gradient": bool(args.bias),
+        "config": {"workload": hwl.name, "note": hwl.note, "N": hs.N, "C": hs.C, "H": hs.H, "W": hs.W,
+                   "K": hs.K, "R": hs.R, "S": hs.S, "pad": hs.pad, "stride": hs.stride,
+                   "dilation": hs.dilation, "groups": hs.groups, "split_k": args.split_k,
+                   "ks_count": rec["ks_count"], "kernel": rec["kernel"], "bias_gradient": bool(args.bias),
                    "parallelism": "single GPU"},
         "roofline": roof,
-        "whole_call_roofline_frac": roofline_for(s, wl.dtype, ms_per_step * 1e-3)["frac"],
-        "stage1_ms_mean": round(stage1_avg_s * 1e3, 5),
-        "cold_cache": cold,
+        "whole_call_roofline_frac": roofline_for(hs, hwl.dtype, wall)["frac"],
+        "stage1_ms_mean": round(stage1_s * 1e3, 5),
         "cpu_baseline": cpu,
-        "check": {"zeros": zeros, "finite": finite},
+        "check": rec["check"],
+        "configs": records,
     }
     print(json.dumps(out), flush=True)
     return 0
