@@ -56,6 +56,8 @@ def load(path: str | None = None):
         lib.oracle_out_size.argtypes = [i64] * 5
         lib.oracle_wgrad_accumulate.restype = ctypes.c_int
         lib.oracle_wgrad_accumulate.argtypes = [i64] * 11 + [ctypes.c_void_p] * 4 + [ctypes.c_int]
+        lib.oracle_wgrad2_accumulate.restype = ctypes.c_int
+        lib.oracle_wgrad2_accumulate.argtypes = [i64] * 14 + [ctypes.c_void_p] * 4 + [ctypes.c_int]
         lib.oracle_bgrad_accumulate.restype = ctypes.c_int
         lib.oracle_bgrad_accumulate.argtypes = [i64] * 4 + [ctypes.c_void_p] * 3
         lib.oracle_max_threads.restype = ctypes.c_int
@@ -74,11 +76,21 @@ def out_size(n_in: int, k: int, pad: int, stride: int, dil: int, lib=None) -> in
     return int((lib or load()).oracle_out_size(n_in, k, pad, stride, dil))
 
 
+def pair(v):
+    """(row, column) value of a geometry argument given as one int or an (h, w) pair."""
+    if isinstance(v, (tuple, list)):
+        if len(v) != 2:
+            raise ValueError("expected an int or an (h, w) pair, got %r" % (v,))
+        return int(v[0]), int(v[1])
+    return int(v), int(v)
+
+
 class WgradAccumulator:
     """Streams images through the oracle: dW and the |dY||X| sums in fp64.
 
-    ``add(x, dy)`` adds the contribution of a chunk of images; ``dw`` and
-    ``den`` give the fp64 result [K, R, S, Cg] and max of the |dY|*|X| sums.
+    ``pad``, ``stride`` and ``dilation`` are one int (both axes) or an (h, w)
+    pair.  ``add(x, dy)`` adds the contribution of a chunk of images; ``dw``
+    and ``den`` give the fp64 result [K, R, S, Cg] and max of the |dY|*|X| sums.
     """
 
     def __init__(self, C, H, W, K, R, S, pad=0, stride=1, dilation=1, groups=1,
@@ -86,12 +98,12 @@ class WgradAccumulator:
         self.lib = lib or load()
         self.C, self.H, self.W, self.K = C, H, W, K
         self.R, self.S = R, S
-        self.pad, self.stride, self.dilation, self.groups = pad, stride, dilation, groups
+        self.pad, self.stride, self.dilation, self.groups = pair(pad), pair(stride), pair(dilation), groups
         if C % groups or K % groups:
             raise ValueError("C and K must be divisible by groups")
         self.Cg = C // groups
-        self.Ho = out_size(H, R, pad, stride, dilation, self.lib)
-        self.Wo = out_size(W, S, pad, stride, dilation, self.lib)
+        self.Ho = out_size(H, R, self.pad[0], self.stride[0], self.dilation[0], self.lib)
+        self.Wo = out_size(W, S, self.pad[1], self.stride[1], self.dilation[1], self.lib)
         if self.Ho < 1 or self.Wo < 1:
             raise ValueError("empty output")
         self.nthreads = nthreads or default_threads()
@@ -107,12 +119,12 @@ class WgradAccumulator:
             raise ValueError("x shape %r" % (x.shape,))
         if dy.shape != (nc, self.Ho, self.Wo, self.K):
             raise ValueError("dy shape %r, expected %r" % (dy.shape, (nc, self.Ho, self.Wo, self.K)))
-        rc = self.lib.oracle_wgrad_accumulate(
-            nc, self.C, self.H, self.W, self.K, self.R, self.S, self.pad, self.stride,
-            self.dilation, self.groups, x.ctypes.data, dy.ctypes.data, self._dw.ctypes.data,
-            self._abs.ctypes.data, self.nthreads)
+        rc = self.lib.oracle_wgrad2_accumulate(
+            nc, self.C, self.H, self.W, self.K, self.R, self.S, self.pad[0], self.pad[1],
+            self.stride[0], self.stride[1], self.dilation[0], self.dilation[1], self.groups,
+            x.ctypes.data, dy.ctypes.data, self._dw.ctypes.data, self._abs.ctypes.data, self.nthreads)
         if rc != 0:
-            raise RuntimeError("oracle_wgrad_accumulate failed: %d" % rc)
+            raise RuntimeError("oracle_wgrad2_accumulate failed: %d" % rc)
         self.images += nc
 
     @property
@@ -129,7 +141,9 @@ class WgradAccumulator:
 
 
 def wgrad_ref(x, dy, R, S, pad=0, stride=1, dilation=1, groups=1, nthreads=None, lib=None):
-    """dW (fp64, [K, R, S, C/groups]) and the error denominator for NHWC x, dy."""
+    """dW (fp64, [K, R, S, C/groups]) and the error denominator for NHWC x, dy.
+
+    pad, stride and dilation: one int for both axes or an (h, w) pair."""
     x = np.asarray(x)
     dy = np.asarray(dy)
     _, H, W, C = x.shape

@@ -48,18 +48,30 @@ int64_t oracle_out_size(int64_t in, int64_t k, int64_t pad, int64_t stride, int6
 
 /*
  * Add the contribution of nc images to dw and absacc (both [K][R][S][Cg],
- * fp64, row-major).  x is [nc][H][W][C], dy is [nc][Ho][Wo][K], both fp32.
+ * fp64, row-major) for per-axis geometry: rows use (pad_h, stride_h, dil_h),
+ * columns (pad_w, stride_w, dil_w), i.e.
+ *
+ *   dW[k, r, s, c] += dY[n, ho, wo, k]
+ *                     * Xpad[n, ho*stride_h + r*dil_h - pad_h, wo*stride_w + s*dil_w - pad_w, g(k)*Cg + c]
+ *
+ * with Ho from (H, R, pad_h, stride_h, dil_h) and Wo from (W, S, pad_w,
+ * stride_w, dil_w).  Per-axis padding is the pad_w of rocm-libraries PR
+ * #14393's embedded depthwise-dgrad PR #14386 (section "Per-axis padding"),
+ * where the column padding may differ from the row padding and Wo uses it.
+ * x is [nc][H][W][C], dy is [nc][Ho][Wo][K], both fp32.
  * Returns 0 on success, -1 on invalid arguments, -2 on allocation failure.
  */
-int oracle_wgrad_accumulate(int64_t nc, int64_t C, int64_t H, int64_t W, int64_t K,
-                            int64_t R, int64_t S, int64_t pad, int64_t stride, int64_t dil,
-                            int64_t groups, const float* x, const float* dy, double* dw,
-                            double* absacc, int nthreads) {
-  if (nc < 0 || C < 1 || H < 1 || W < 1 || K < 1 || R < 1 || S < 1 || pad < 0 ||
-      stride < 1 || dil < 1 || groups < 1 || C % groups != 0 || K % groups != 0)
+int oracle_wgrad2_accumulate(int64_t nc, int64_t C, int64_t H, int64_t W, int64_t K,
+                             int64_t R, int64_t S, int64_t pad_h, int64_t pad_w, int64_t stride_h,
+                             int64_t stride_w, int64_t dil_h, int64_t dil_w, int64_t groups,
+                             const float* x, const float* dy, double* dw, double* absacc,
+                             int nthreads) {
+  if (nc < 0 || C < 1 || H < 1 || W < 1 || K < 1 || R < 1 || S < 1 || pad_h < 0 || pad_w < 0 ||
+      stride_h < 1 || stride_w < 1 || dil_h < 1 || dil_w < 1 || groups < 1 || C % groups != 0 ||
+      K % groups != 0)
     return -1;
-  const int64_t Ho = oracle_out_size(H, R, pad, stride, dil);
-  const int64_t Wo = oracle_out_size(W, S, pad, stride, dil);
+  const int64_t Ho = oracle_out_size(H, R, pad_h, stride_h, dil_h);
+  const int64_t Wo = oracle_out_size(W, S, pad_w, stride_w, dil_w);
   if (Ho < 1 || Wo < 1) return -1;
   const int64_t Cg = C / groups, Kg = K / groups;
   const int64_t E = K * R * S * Cg;
@@ -88,10 +100,10 @@ int oracle_wgrad_accumulate(int64_t nc, int64_t C, int64_t H, int64_t W, int64_t
           const double g = (double)dy_px[k];
           const int64_t grp = k / Kg;
           for (int64_t r = 0; r < R; ++r) {
-            const int64_t h = ho * stride + r * dil - pad;
+            const int64_t h = ho * stride_h + r * dil_h - pad_h;
             if (h < 0 || h >= H) continue; /* zero padding */
             for (int64_t s = 0; s < S; ++s) {
-              const int64_t w = wo * stride + s * dil - pad;
+              const int64_t w = wo * stride_w + s * dil_w - pad_w;
               if (w < 0 || w >= W) continue; /* zero padding */
               const float* x_px = x + ((n * H + h) * W + w) * C + grp * Cg;
               double* d = my_dw + ((k * R + r) * S + s) * Cg;
@@ -117,6 +129,15 @@ int oracle_wgrad_accumulate(int64_t nc, int64_t C, int64_t H, int64_t W, int64_t
   }
   free(priv);
   return 0;
+}
+
+/* The same geometry on both axes (one pad, stride and dilation). */
+int oracle_wgrad_accumulate(int64_t nc, int64_t C, int64_t H, int64_t W, int64_t K,
+                            int64_t R, int64_t S, int64_t pad, int64_t stride, int64_t dil,
+                            int64_t groups, const float* x, const float* dy, double* dw,
+                            double* absacc, int nthreads) {
+  return oracle_wgrad2_accumulate(nc, C, H, W, K, R, S, pad, pad, stride, stride, dil, dil, groups,
+                                  x, dy, dw, absacc, nthreads);
 }
 
 /*

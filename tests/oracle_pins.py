@@ -38,22 +38,28 @@ def _extent(n, k, pad, stride, dil):
     return span // stride + 1 if span >= 0 else 0
 
 
+def _pair(v):
+    return (int(v[0]), int(v[1])) if isinstance(v, (tuple, list)) else (int(v), int(v))
+
+
 def forward_conv_numpy(x, w, pad, stride, dil, groups):
     """Forward convolution, NHWC x [N,H,W,C], KRSC w [K,R,S,Cg] -> [N,Ho,Wo,K] (fp64).
 
-    Built from np.pad and strided slices: every filter tap (r, s) selects the
-    strided window of the padded input that it multiplies.
+    pad, stride, dil: one int or an (h, w) pair.  Built from np.pad and strided
+    slices: every filter tap (r, s) selects the strided window of the padded
+    input that it multiplies.
     """
     N, H, W, C = x.shape
     K, R, S, Cg = w.shape
     Kg = K // groups
-    Ho, Wo = _extent(H, R, pad, stride, dil), _extent(W, S, pad, stride, dil)
-    xp = np.pad(x.astype(np.float64), ((0, 0), (pad, pad), (pad, pad), (0, 0)))
+    (ph, pw), (sh, sw), (dh, dw) = _pair(pad), _pair(stride), _pair(dil)
+    Ho, Wo = _extent(H, R, ph, sh, dh), _extent(W, S, pw, sw, dw)
+    xp = np.pad(x.astype(np.float64), ((0, 0), (ph, ph), (pw, pw), (0, 0)))
     y = np.zeros((N, Ho, Wo, K), np.float64)
     for r in range(R):
         for s in range(S):
-            win = xp[:, r * dil: r * dil + (Ho - 1) * stride + 1: stride,
-                     s * dil: s * dil + (Wo - 1) * stride + 1: stride, :]
+            win = xp[:, r * dh: r * dh + (Ho - 1) * sh + 1: sh,
+                     s * dw: s * dw + (Wo - 1) * sw + 1: sw, :]
             for g in range(groups):
                 xs = win[..., g * Cg:(g + 1) * Cg].reshape(-1, Cg)
                 ws = w[g * Kg:(g + 1) * Kg, r, s, :].astype(np.float64)
@@ -327,6 +333,80 @@ def pin_denominator(lib, seed=20):
     assert np.all(np.abs(acc.dw) <= acc.abs_sum)
 
 
+def _per_axis_shapes(rng, count):
+    """Tiny shapes whose row and column geometry differ."""
+    shapes = []
+    while len(shapes) < count:
+        N = int(rng.integers(1, 3))
+        groups = int(rng.choice([1, 1, 2]))
+        C, K = groups * int(rng.integers(1, 4)), groups * int(rng.integers(1, 4))
+        H, W = int(rng.integers(1, 8)), int(rng.integers(1, 8))
+        R, S = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        pad = (int(rng.integers(0, 3)), int(rng.integers(0, 3)))
+        stride = (int(rng.integers(1, 4)), int(rng.integers(1, 4)))
+        dil = (int(rng.integers(1, 3)), int(rng.integers(1, 3)))
+        if pad[0] == pad[1] and stride[0] == stride[1] and dil[0] == dil[1]:
+            continue
+        if _extent(H, R, pad[0], stride[0], dil[0]) < 1 or _extent(W, S, pad[1], stride[1], dil[1]) < 1:
+            continue
+        shapes.append((N, C, H, W, K, R, S, pad, stride, dil, groups))
+    return shapes
+
+
+def pin_per_axis_finite_differences(lib, count=40, seed=22):
+    """Per-axis pad / stride / dilation: every dW element against central
+    differences of the independent numpy forward convolution."""
+    rng = np.random.default_rng(seed)
+    for shape in _per_axis_shapes(rng, count):
+        N, C, H, W, K, R, S, pad, stride, dil, groups = shape
+        Ho, Wo = _extent(H, R, pad[0], stride[0], dil[0]), _extent(W, S, pad[1], stride[1], dil[1])
+        x = rng.uniform(-1, 1, (N, H, W, C)).astype(np.float32)
+        dy = rng.uniform(-1, 1, (N, Ho, Wo, K)).astype(np.float32)
+        got, den = _ref(lib, x, dy, R, S, pad, stride, dil, groups)
+        want = fd_wgrad(x, dy, R, S, pad, stride, dil, groups, rng)
+        err = np.max(np.abs(got - want)) / max(den, 1e-30)
+        assert err <= 1e-12, (shape, err)
+
+
+def pin_per_axis_torch(lib, count=30, seed=23):
+    """Per-axis geometry against torch's fp64 conv2d autograd with padding=(ph, pw),
+    stride=(sh, sw), dilation=(dh, dw) (a library routine)."""
+    import torch
+    rng = np.random.default_rng(seed)
+    for shape in _per_axis_shapes(rng, count) + [(2, 6, 9, 14, 4, 3, 5, (1, 2), (2, 1), (1, 2), 2),
+                                                  (1, 4, 16, 12, 8, 7, 1, (3, 0), (1, 1), (1, 1), 1)]:
+        N, C, H, W, K, R, S, pad, stride, dil, groups = shape
+        Ho, Wo = _extent(H, R, pad[0], stride[0], dil[0]), _extent(W, S, pad[1], stride[1], dil[1])
+        x = rng.standard_normal((N, H, W, C)).astype(np.float32)
+        dy = rng.standard_normal((N, Ho, Wo, K)).astype(np.float32)
+        xt = torch.from_numpy(x.astype(np.float64)).permute(0, 3, 1, 2)
+        wt = torch.zeros((K, C // groups, R, S), dtype=torch.float64, requires_grad=True)
+        y = torch.nn.functional.conv2d(xt, wt, None, stride, pad, dil, groups)
+        assert tuple(y.shape) == (N, K, Ho, Wo), (shape, tuple(y.shape))
+        y.backward(torch.from_numpy(dy.astype(np.float64)).permute(0, 3, 1, 2))
+        want = wt.grad.permute(0, 2, 3, 1).numpy()
+        got, den = _ref(lib, x, dy, R, S, pad, stride, dil, groups)
+        err = np.max(np.abs(got - want)) / max(den, 1e-30)
+        assert err <= 1e-12, (shape, err)
+
+
+def pin_axis_swap(lib, seed=24):
+    """Transposing the images (H <-> W) with the row and column geometry swapped
+    transposes the filter taps: dW'[k, s, r, c] = dW[k, r, s, c], exactly
+    (integer inputs, exact sums)."""
+    rng = np.random.default_rng(seed)
+    for (N, C, H, W, K, R, S, pad, stride, dil, groups) in [(2, 3, 7, 5, 2, 3, 2, (1, 0), (2, 1), (1, 2), 1),
+                                                            (1, 4, 6, 9, 4, 2, 3, (0, 2), (1, 3), (2, 1), 2)]:
+        x, dy = _int_inputs(rng, (N, C, H, W, K, R, S, 0, 1, 1, groups), lo=-4, hi=5)
+        Ho, Wo = _extent(H, R, pad[0], stride[0], dil[0]), _extent(W, S, pad[1], stride[1], dil[1])
+        dy = rng.integers(-4, 5, (N, Ho, Wo, K)).astype(np.float32)
+        a, _ = _ref(lib, x, dy, R, S, pad, stride, dil, groups)
+        b, _ = _ref(lib, np.ascontiguousarray(x.transpose(0, 2, 1, 3)), np.ascontiguousarray(dy.transpose(0, 2, 1, 3)),
+                    S, R, pad[::-1], stride[::-1], dil[::-1], groups)
+        assert np.array_equal(b, a.transpose(0, 2, 1, 3)), (N, C, H, W, K, R, S)
+
+
 ALL_PINS = [pin_hand_examples, pin_finite_differences, pin_torch_autograd, pin_closed_form_1x1,
             pin_bias_gradient, pin_box_sum, pin_depthwise_correlate, pin_grouped_is_dense_per_group,
-            pin_bilinear, pin_split_invariance, pin_denominator, pin_bgrad]
+            pin_bilinear, pin_split_invariance, pin_denominator, pin_bgrad,
+            pin_per_axis_finite_differences, pin_per_axis_torch, pin_axis_swap]

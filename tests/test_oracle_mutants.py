@@ -14,10 +14,16 @@ import oracle_pins as P
 SRC = os.path.join(os.path.dirname(oracle.__file__), "wgrad_ref.c")
 
 MUTANTS = {
-    "pad_sign_h": ("ho * stride + r * dil - pad", "ho * stride + r * dil + pad"),
-    "r_for_s_in_w": ("wo * stride + s * dil - pad", "wo * stride + r * dil - pad"),
-    "no_stride_w": ("wo * stride + s * dil - pad", "wo + s * dil - pad"),
-    "no_dilation_w": ("wo * stride + s * dil - pad", "wo * stride + s - pad"),
+    "pad_sign_h": ("ho * stride_h + r * dil_h - pad_h", "ho * stride_h + r * dil_h + pad_h"),
+    "r_for_s_in_w": ("wo * stride_w + s * dil_w - pad_w", "wo * stride_w + r * dil_w - pad_w"),
+    "no_stride_w": ("wo * stride_w + s * dil_w - pad_w", "wo + s * dil_w - pad_w"),
+    "no_dilation_w": ("wo * stride_w + s * dil_w - pad_w", "wo * stride_w + s - pad_w"),
+    "row_pad_on_columns": ("wo * stride_w + s * dil_w - pad_w", "wo * stride_w + s * dil_w - pad_h"),
+    "row_stride_on_columns": ("wo * stride_w + s * dil_w - pad_w", "wo * stride_h + s * dil_w - pad_w"),
+    "row_dilation_on_columns": ("wo * stride_w + s * dil_w - pad_w", "wo * stride_w + s * dil_h - pad_w"),
+    "column_pad_on_rows": ("ho * stride_h + r * dil_h - pad_h", "ho * stride_h + r * dil_h - pad_w"),
+    "wo_from_row_geometry": ("oracle_out_size(W, S, pad_w, stride_w, dil_w)",
+                             "oracle_out_size(W, S, pad_h, stride_h, dil_h)"),
     "dropped_group_offset": ("* C + grp * Cg;", "* C;"),
     "transposed_taps": ("((k * R + r) * S + s) * Cg;\n              double* a",
                         "((k * S + s) * R + r) * Cg;\n              double* a"),
@@ -46,7 +52,7 @@ def test_mutant_is_caught(name, tmp_path):
     for pin in P.ALL_PINS:
         try:
             pin(lib)
-        except (AssertionError, ValueError):
+        except (AssertionError, ValueError, RuntimeError):
             return  # caught
     pytest.fail("mutant %s passed every pin" % name)
 
