@@ -47,6 +47,23 @@ class Plan(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_}
 
 
+class Desc2(ctypes.Structure):
+    """conv_wgrad_desc2_t: per-axis geometry, math mode and width fold."""
+    _fields_ = [(n, ctypes.c_int64) for n in
+                ("N", "C", "H", "W", "K", "R", "S", "pad_h", "pad_w", "stride_h", "stride_w",
+                 "dil_h", "dil_w", "groups")] + \
+               [(n, ctypes.c_int32) for n in ("dtype", "split_k", "math", "fold_width")]
+
+
+class Plan2(ctypes.Structure):
+    """conv_wgrad_plan2_t."""
+    _fields_ = [("base", Plan), ("math", ctypes.c_int32), ("fold_width", ctypes.c_int32)]
+
+
+MATH = {"exact": 0, "bf16x3": 1}
+VARIANT_DENSE_BF16X3 = 4
+
+
 class ConvWgradError(RuntimeError):
     def __init__(self, status: int, what: str = ""):
         self.status = status
@@ -101,6 +118,13 @@ def load():
     lib.conv_wgrad_bias_timed.argtypes = [P(Desc), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.conv_wgrad2_workspace_size.restype = ctypes.c_int
+    lib.conv_wgrad2_workspace_size.argtypes = [P(Desc2), P(ctypes.c_size_t)]
+    lib.conv_wgrad2_get_plan.restype = ctypes.c_int
+    lib.conv_wgrad2_get_plan.argtypes = [P(Desc2), P(Plan2)]
+    lib.conv_wgrad2.restype = ctypes.c_int
+    lib.conv_wgrad2.argtypes = [P(Desc2), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.conv_wgrad_noalloc.restype = ctypes.c_int
     lib.conv_wgrad_noalloc.argtypes = [P(Desc), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p]
@@ -111,6 +135,39 @@ def load():
 def make_desc(N, C, H, W, K, R, S, pad=0, stride=1, dilation=1, groups=1, dtype=F32,
               split_k=-1) -> Desc:
     return Desc(N, C, H, W, K, R, S, pad, stride, dilation, groups, dtype, split_k)
+
+
+def _pair(v):
+    if isinstance(v, (tuple, list)):
+        if len(v) != 2:
+            raise ValueError("expected an int or an (h, w) pair, got %r" % (v,))
+        return int(v[0]), int(v[1])
+    return int(v), int(v)
+
+
+def make_desc2(N, C, H, W, K, R, S, pad=0, stride=1, dilation=1, groups=1, dtype=F32, split_k=-1,
+               math="exact", fold_width=-1) -> Desc2:
+    """Extended descriptor; pad, stride and dilation are one int or an (h, w) pair."""
+    (ph, pw), (sh, sw), (dh, dw) = _pair(pad), _pair(stride), _pair(dilation)
+    m = MATH[math] if isinstance(math, str) else int(math)
+    return Desc2(N, C, H, W, K, R, S, ph, pw, sh, sw, dh, dw, groups, dtype, split_k, m, fold_width)
+
+
+def get_plan2(desc: Desc2) -> Plan2:
+    p = Plan2()
+    st = load().conv_wgrad2_get_plan(ctypes.byref(desc), ctypes.byref(p))
+    if st != 0:
+        raise ConvWgradError(st, "get_plan2")
+    return p
+
+
+def conv_wgrad2(desc: Desc2, x_ptr: int, dy_ptr: int, dw_ptr: int, db_ptr: int, ws_ptr: int, ws_bytes: int,
+                stream: int) -> None:
+    """Raw extended call (db_ptr 0 for the weight gradient only)."""
+    st = load().conv_wgrad2(ctypes.byref(desc), x_ptr, dy_ptr, dw_ptr, db_ptr or None, ws_ptr or None,
+                            ws_bytes, stream or None)
+    if st != 0:
+        raise ConvWgradError(st, "conv_wgrad2")
 
 
 def get_plan(desc: Desc) -> Plan:
@@ -199,16 +256,32 @@ def desc_for(x, dy, R, S, pad=0, stride=1, dilation=1, groups=1, split_k=-1) -> 
     return make_desc(N, C, H, W, K, R, S, pad, stride, dilation, groups, _dtype_code(x), split_k)
 
 
+def desc2_for(x, dy, R, S, pad=0, stride=1, dilation=1, groups=1, split_k=-1, math="exact",
+              fold_width=-1) -> Desc2:
+    """Extended descriptor for NHWC torch tensors x [N,H,W,C] and dy [N,Ho,Wo,K]."""
+    if x.dim() != 4 or dy.dim() != 4:
+        raise ValueError("x and dy must be 4-D NHWC tensors")
+    if x.dtype != dy.dtype:
+        raise TypeError("x and dy must have the same dtype")
+    N, H, W, C = x.shape
+    K = dy.shape[3]
+    return make_desc2(N, C, H, W, K, R, S, pad, stride, dilation, groups, _dtype_code(x), split_k, math,
+                      fold_width)
+
+
 def wgrad(x, dy, R, S, pad=0, stride=1, dilation=1, groups=1, split_k=-1, dw=None, workspace=None,
-          stream=None, bias=False, db=None):
+          stream=None, bias=False, db=None, math="exact", fold_width=-1):
     """Weight gradient dW [K, R, S, C/groups] (fp32) of NHWC x and dy on the current HIP stream.
 
+    pad, stride and dilation are one int or an (h, w) pair.  math="bf16x3"
+    allows BF16x3 emulation for fp32 inputs where a kernel covers the shape;
+    fold_width is the width fold (-1 automatic, 0/1 off, f >= 2 fold by f).
     With bias=True, returns (dW, db) where db [K] (fp32) is the bias gradient,
     the sum of dy over its N, Ho, Wo axes, from the same pass over dy.
     """
     import torch
-    d = desc_for(x, dy, R, S, pad, stride, dilation, groups, split_k)
-    plan = get_plan(d)
+    d = desc2_for(x, dy, R, S, pad, stride, dilation, groups, split_k, math, fold_width)
+    plan = get_plan2(d).base
     if tuple(dy.shape) != (d.N, plan.Ho, plan.Wo, d.K):
         raise ValueError("dy shape %s does not match [N, Ho, Wo, K] = %s"
                          % (tuple(dy.shape), (d.N, plan.Ho, plan.Wo, d.K)))
@@ -216,7 +289,7 @@ def wgrad(x, dy, R, S, pad=0, stride=1, dilation=1, groups=1, split_k=-1, dw=Non
         raise ValueError("x and dy must be on the same GPU")
     if not (x.is_contiguous() and dy.is_contiguous()):
         raise ValueError("x and dy must be contiguous NHWC")
-    shape = (d.K, d.R, d.S, d.C // d.groups)
+    shape = (d.K, d.R, d.S, d.C // d.groups)   # the unfolded layout (a fold keeps the bytes)
     if dw is not None and (tuple(dw.shape) != shape or dw.dtype != torch.float32 or not dw.is_contiguous()):
         raise ValueError("dw must be a contiguous float32 tensor of shape %s" % (shape,))
     if bias and db is not None and (tuple(db.shape) != (d.K,) or db.dtype != torch.float32
@@ -237,9 +310,6 @@ def wgrad(x, dy, R, S, pad=0, stride=1, dilation=1, groups=1, split_k=-1, dw=Non
             workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
     ws_ptr = workspace.data_ptr() if ws_bytes else 0
     ws_len = workspace.numel() * workspace.element_size() if ws_bytes else 0
-    if not bias:
-        conv_wgrad_ex(d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(), ws_ptr, ws_len, stream.cuda_stream)
-        return dw
-    conv_wgrad_bias(d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(), db.data_ptr(), ws_ptr, ws_len,
-                    stream.cuda_stream)
-    return dw, db
+    conv_wgrad2(d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(), db.data_ptr() if bias else 0, ws_ptr, ws_len,
+                stream.cuda_stream)
+    return (dw, db) if bias else dw

@@ -45,7 +45,7 @@ namespace {
 std::mutex g_mutex;
 std::unordered_map<std::string, cw::Plan>* g_plans = nullptr;
 
-conv_wgrad_status_t get_plan(const conv_wgrad_desc_t* desc, cw::Plan* out) {
+conv_wgrad_status_t get_plan(const conv_wgrad_desc2_t* desc, cw::Plan* out) {
   if (!desc) return CONV_WGRAD_ERR_NULL_ARG;
   const std::string key(reinterpret_cast<const char*>(desc), sizeof(*desc));
   {
@@ -69,8 +69,20 @@ conv_wgrad_status_t get_plan(const conv_wgrad_desc_t* desc, cw::Plan* out) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The plain descriptor as an extended one (NULL stays NULL).
+struct Desc2 {
+  conv_wgrad_desc2_t d;
+  const conv_wgrad_desc2_t* ptr;
+  explicit Desc2(const conv_wgrad_desc_t* p) : ptr(nullptr) {
+    if (p) {
+      d = cw::to_desc2(*p);
+      ptr = &d;
+    }
+  }
+};
+
 // with_db: the bias gradient is requested (db must then be a valid pointer).
-conv_wgrad_status_t run(const conv_wgrad_desc_t* desc, const void* x, const void* dy, float* dw,
+conv_wgrad_status_t run(const conv_wgrad_desc2_t* desc, const void* x, const void* dy, float* dw,
                         bool with_db, float* db, void* workspace, bool check_ws, size_t ws_bytes,
                         void* stream, void* ev_begin = nullptr, void* ev_end = nullptr) {
   cw::Plan plan;
@@ -111,7 +123,8 @@ conv_wgrad_status_t run(const conv_wgrad_desc_t* desc, const void* x, const void
     case cw::kDepthwise: err = cw::launch_depthwise(plan, x, dy, out, s); break;
     case cw::kDenseRows: err = cw::launch_dense_rows(plan, x, dy, out, s); break;
     case cw::kDense1x1: err = cw::launch_dense_1x1(plan, x, dy, out, s); break;
-    case cw::kDense16Rows: err = cw::launch_dense16_rows(plan, x, dy, out, s); break;
+    case cw::kDense16Rows:
+    case cw::kDense16RowsX3: err = cw::launch_dense16_rows(plan, x, dy, out, s); break;
     default: err = cw::launch_dense(plan, x, dy, out, s); break;
   }
   if (err != hipSuccess) return CONV_WGRAD_ERR_HIP;
@@ -144,7 +157,7 @@ const char* conv_wgrad_status_string(conv_wgrad_status_t status) {
 conv_wgrad_status_t conv_wgrad_get_plan(const conv_wgrad_desc_t* desc, conv_wgrad_plan_t* plan) {
   if (!desc || !plan) return CONV_WGRAD_ERR_NULL_ARG;
   cw::Plan p;
-  conv_wgrad_status_t st = get_plan(desc, &p);
+  conv_wgrad_status_t st = get_plan(Desc2(desc).ptr, &p);
   if (st != CONV_WGRAD_OK) return st;
   *plan = p.pub;
   return CONV_WGRAD_OK;
@@ -153,7 +166,7 @@ conv_wgrad_status_t conv_wgrad_get_plan(const conv_wgrad_desc_t* desc, conv_wgra
 conv_wgrad_status_t conv_wgrad_workspace_size(const conv_wgrad_desc_t* desc, size_t* bytes) {
   if (!desc || !bytes) return CONV_WGRAD_ERR_NULL_ARG;
   cw::Plan p;
-  conv_wgrad_status_t st = get_plan(desc, &p);
+  conv_wgrad_status_t st = get_plan(Desc2(desc).ptr, &p);
   if (st != CONV_WGRAD_OK) return st;
   *bytes = (size_t)p.pub.ws_bytes;
   return CONV_WGRAD_OK;
@@ -161,45 +174,71 @@ conv_wgrad_status_t conv_wgrad_workspace_size(const conv_wgrad_desc_t* desc, siz
 
 conv_wgrad_status_t conv_wgrad(const conv_wgrad_desc_t* desc, const void* x, const void* dy,
                                float* dw, void* workspace, void* stream) {
-  return run(desc, x, dy, dw, false, nullptr, workspace, false, 0, stream);
+  return run(Desc2(desc).ptr, x, dy, dw, false, nullptr, workspace, false, 0, stream);
 }
 
 conv_wgrad_status_t conv_wgrad_ex(const conv_wgrad_desc_t* desc, const void* x, const void* dy,
                                   float* dw, void* workspace, size_t ws_bytes, void* stream) {
-  return run(desc, x, dy, dw, false, nullptr, workspace, true, ws_bytes, stream);
+  return run(Desc2(desc).ptr, x, dy, dw, false, nullptr, workspace, true, ws_bytes, stream);
 }
 
 conv_wgrad_status_t conv_wgrad_timed(const conv_wgrad_desc_t* desc, const void* x, const void* dy,
                                      float* dw, void* workspace, size_t ws_bytes, void* stream,
                                      void* stage1_begin, void* stage1_end) {
-  return run(desc, x, dy, dw, false, nullptr, workspace, true, ws_bytes, stream, stage1_begin,
+  return run(Desc2(desc).ptr, x, dy, dw, false, nullptr, workspace, true, ws_bytes, stream, stage1_begin,
              stage1_end);
 }
 
 conv_wgrad_status_t conv_wgrad_bias(const conv_wgrad_desc_t* desc, const void* x, const void* dy,
                                     float* dw, float* db, void* workspace, size_t ws_bytes,
                                     void* stream) {
-  return run(desc, x, dy, dw, true, db, workspace, true, ws_bytes, stream);
+  return run(Desc2(desc).ptr, x, dy, dw, true, db, workspace, true, ws_bytes, stream);
 }
 
 conv_wgrad_status_t conv_wgrad_bias_timed(const conv_wgrad_desc_t* desc, const void* x,
                                           const void* dy, float* dw, float* db, void* workspace,
                                           size_t ws_bytes, void* stream, void* stage1_begin,
                                           void* stage1_end) {
-  return run(desc, x, dy, dw, true, db, workspace, true, ws_bytes, stream, stage1_begin,
+  return run(Desc2(desc).ptr, x, dy, dw, true, db, workspace, true, ws_bytes, stream, stage1_begin,
              stage1_end);
 }
 
 conv_wgrad_status_t conv_wgrad_noalloc(const conv_wgrad_desc_t* desc, const void* x, const void* dy,
                                        float* dw, float* db, void* stream) {
   cw::Plan plan;
-  conv_wgrad_status_t st = get_plan(desc, &plan);
+  const Desc2 d2(desc);
+  conv_wgrad_status_t st = get_plan(d2.ptr, &plan);
   if (st != CONV_WGRAD_OK) return st;
   if (!x || !dy || !dw) return CONV_WGRAD_ERR_NULL_ARG;
   if (plan.pub.ws_bytes > cw::kNoallocScratchBytes) return CONV_WGRAD_ERR_WORKSPACE;
   void* ws = nullptr;
   if (plan.pub.ws_bytes > 0 && cw::noalloc_scratch(&ws) != hipSuccess) return CONV_WGRAD_ERR_HIP;
-  return run(desc, x, dy, dw, db != nullptr, db, ws, true, cw::kNoallocScratchBytes, stream);
+  return run(d2.ptr, x, dy, dw, db != nullptr, db, ws, true, cw::kNoallocScratchBytes, stream);
+}
+
+conv_wgrad_status_t conv_wgrad2_workspace_size(const conv_wgrad_desc2_t* desc, size_t* bytes) {
+  if (!desc || !bytes) return CONV_WGRAD_ERR_NULL_ARG;
+  cw::Plan p;
+  conv_wgrad_status_t st = get_plan(desc, &p);
+  if (st != CONV_WGRAD_OK) return st;
+  *bytes = (size_t)p.pub.ws_bytes;
+  return CONV_WGRAD_OK;
+}
+
+conv_wgrad_status_t conv_wgrad2_get_plan(const conv_wgrad_desc2_t* desc, conv_wgrad_plan2_t* plan) {
+  if (!desc || !plan) return CONV_WGRAD_ERR_NULL_ARG;
+  cw::Plan p;
+  conv_wgrad_status_t st = get_plan(desc, &p);
+  if (st != CONV_WGRAD_OK) return st;
+  plan->base = p.pub;
+  plan->math = p.pub.variant == CONV_WGRAD_VARIANT_DENSE_BF16X3 ? CONV_WGRAD_MATH_BF16X3 : CONV_WGRAD_MATH_EXACT;
+  plan->fold_width = p.p.fold;
+  return CONV_WGRAD_OK;
+}
+
+conv_wgrad_status_t conv_wgrad2(const conv_wgrad_desc2_t* desc, const void* x, const void* dy,
+                                float* dw, float* db, void* workspace, size_t ws_bytes, void* stream) {
+  return run(desc, x, dy, dw, db != nullptr, db, workspace, true, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -27,6 +27,14 @@
 //     j*P .. j*P + P - 1 -- so tap s is still the shift by s slots (a product
 //     that crosses into the next row's segment meets a zero dY column), and a
 //     14-pixel row no longer occupies a whole 64-pixel unit.
+//
+// BF16x3 mode (fp32 inputs, math = BF16X3; the gfx950 form of fp32 matrix
+// work in rocm-libraries PR #14393, timeline, the TF32 entry): the loaders
+// read fp32 and split every value v at staging into hi = bf16(v) and
+// lo = bf16(v - hi) (both round-to-nearest-even, v - hi exact in fp32), kept
+// in two LDS planes; each product is a_hi*b_hi + a_hi*b_lo + a_lo*b_hi, three
+// bf16 MFMAs into the same fp32 accumulator.  The bias gradient is then summed
+// from the fp32 values at staging (exact fp32 adds), not through the MFMA.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -51,7 +59,7 @@ struct R16Args {
   float* out;
   int64_t slab_stride;
   int64_t x_img;   // H*W*C
-  int32_t H, W, C, K, Ho, Wo, R, S, pad;
+  int32_t H, W, C, K, Ho, Wo, R, S, pad_h, pad_w;
   int32_t Cg, Kg, cols;
   int32_t m_tiles, c_tiles, s_blocks;
   int32_t wt, wchunks;
@@ -76,11 +84,32 @@ __device__ __forceinline__ f32x4 mfma16(s16x8 a, s16x8 b, f32x4 c) {
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// kDb: also the bias gradient (a separate instantiation).
-template <bool kBf16, int SB, bool kDb>
+// Split of 8 fp32 values into 8 bf16 high parts and 8 bf16 low parts
+// (round-to-nearest-even; v - hi is exact in fp32).
+__device__ __forceinline__ void split_bf16x8(uint4 v0, uint4 v1, uint4& hi, uint4& lo) {
+  const float f[8] = {__uint_as_float(v0.x), __uint_as_float(v0.y), __uint_as_float(v0.z), __uint_as_float(v0.w),
+                      __uint_as_float(v1.x), __uint_as_float(v1.y), __uint_as_float(v1.z), __uint_as_float(v1.w)};
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const __bf16 h0 = (__bf16)f[2 * i], h1 = (__bf16)f[2 * i + 1];
+    const __bf16 l0 = (__bf16)(f[2 * i] - (float)h0), l1 = (__bf16)(f[2 * i + 1] - (float)h1);
+    h[i] = (uint32_t)__builtin_bit_cast(unsigned short, h0) | ((uint32_t)__builtin_bit_cast(unsigned short, h1) << 16);
+    l[i] = (uint32_t)__builtin_bit_cast(unsigned short, l0) | ((uint32_t)__builtin_bit_cast(unsigned short, l1) << 16);
+  }
+  hi = uint4{h[0], h[1], h[2], h[3]};
+  lo = uint4{l[0], l[1], l[2], l[3]};
+}
+
+// kDb: also the bias gradient (a separate instantiation).  kX3: fp32 inputs
+// by BF16x3 (kBf16 is then true).
+template <bool kBf16, int SB, bool kDb, bool kX3>
 __global__ __launch_bounds__(256) void dense16_rows_kernel(R16Args a) {
-  __shared__ __attribute__((aligned(16))) unsigned short s_dy[2][kWt * kPitchE];
-  __shared__ __attribute__((aligned(16))) unsigned short s_x[2][kXs * kPitchE];
+  constexpr int kEs = kX3 ? 4 : 2;          // bytes per input element
+  constexpr int kLd = kX3 ? 2 : 1;          // 16-byte loads per 8-channel chunk
+  constexpr int kPlanes = kX3 ? 2 : 1;      // hi (and lo) planes
+  __shared__ __attribute__((aligned(16))) unsigned short s_dy[kPlanes][2][kWt * kPitchE];
+  __shared__ __attribute__((aligned(16))) unsigned short s_x[kPlanes][2][kXs * kPitchE];
   const unsigned char* __restrict__ xg = static_cast<const unsigned char*>(a.x);
   const unsigned char* __restrict__ dyg = static_cast<const unsigned char*>(a.dy);
 
@@ -109,8 +138,8 @@ __global__ __launch_bounds__(256) void dense16_rows_kernel(R16Args a) {
   const int q8 = tid & 7, px0 = tid >> 3;
   const int dy_col0 = g * a.Kg + m0;
   const int x_col0 = g * a.Cg + c0;
-  const int x_row_bytes = (a.W * a.C - x_col0) * 2;
-  uint4 rdy[kDyChunks], rx[kXChunks];
+  const int x_row_bytes = (a.W * a.C - x_col0) * kEs;
+  uint4 rdy[kDyChunks][kLd], rx[kXChunks][kLd];
   int npix_next = 0;
   // Multi-row units: slot p of a loader chunk is row p / pitch, column p % pitch.
   int dj[kDyChunks], dcol[kDyChunks], xj[kXChunks], xcol[kXChunks];
@@ -126,27 +155,31 @@ __global__ __launch_bounds__(256) void dense16_rows_kernel(R16Args a) {
     npix_next = a.ru * a.pitch;
     // dY rows ho0 .. ho0 + rows - 1 are contiguous; columns past Wo and rows
     // past the unit read zero.
-    const unsigned char* dyp = dyg + 2 * (((int64_t)(n * a.Ho + ho0) * a.Wo) * a.K + dy_col0);
-    const __amdgpu_buffer_rsrc_t rd = buf_rsrc(dyp, (rows * a.Wo * a.K - dy_col0) * 2);
+    const unsigned char* dyp = dyg + kEs * (((int64_t)(n * a.Ho + ho0) * a.Wo) * a.K + dy_col0);
+    const __amdgpu_buffer_rsrc_t rd = buf_rsrc(dyp, (rows * a.Wo * a.K - dy_col0) * kEs);
 #pragma unroll
     for (int i = 0; i < kDyChunks; ++i) {
       const bool ok = dcol[i] < a.Wo && dj[i] < rows;
-      rdy[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                             rd, ok ? ((dj[i] * a.Wo + dcol[i]) * a.K + 8 * q8) * 2 : 0x7fffffff, 0, 0));
+      const int off = ok ? ((dj[i] * a.Wo + dcol[i]) * a.K + 8 * q8) * kEs : 0x7fffffe0;
+#pragma unroll
+      for (int h = 0; h < kLd; ++h)
+        rdy[i][h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rd, off + 16 * h, 0, 0));
     }
     // X rows h0 + j of the unit (filter row r), columns w0 .. w0 + pitch - 1;
     // rows and columns outside the image read zero.
-    const int h0 = ho0 + r - a.pad;
+    const int h0 = ho0 + r - a.pad_h;
     const int hb = max(h0, 0), he = min(h0 + rows, a.H);
-    const int w0 = s0 - a.pad;
-    const unsigned char* xp = xg + 2 * ((int64_t)n * a.x_img + (int64_t)hb * a.W * a.C + x_col0);
-    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(xp, he > hb ? ((he - hb) * a.W * a.C - x_col0) * 2 : 0);
+    const int w0 = s0 - a.pad_w;
+    const unsigned char* xp = xg + kEs * ((int64_t)n * a.x_img + (int64_t)hb * a.W * a.C + x_col0);
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(xp, he > hb ? ((he - hb) * a.W * a.C - x_col0) * kEs : 0);
 #pragma unroll
     for (int i = 0; i < kXChunks; ++i) {
       const int h = h0 + xj[i], w = w0 + xcol[i];
       const bool ok = xj[i] < rows && h >= hb && h < he && w >= 0 && w < a.W;
-      rx[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            rs, ok ? (((h - hb) * a.W + w) * a.C + 8 * q8) * 2 : 0x7fffffff, 0, 0));
+      const int off = ok ? (((h - hb) * a.W + w) * a.C + 8 * q8) * kEs : 0x7fffffe0;
+#pragma unroll
+      for (int hh = 0; hh < kLd; ++hh)
+        rx[i][hh] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16 * hh, 0, 0));
     }
   };
   auto load_unit = [&](int u) {
@@ -160,30 +193,62 @@ __global__ __launch_bounds__(256) void dense16_rows_kernel(R16Args a) {
     const int wo0 = wc * a.wt;
     const int npix = min(a.wt, a.Wo - wo0);
     npix_next = npix;
-    const unsigned char* dyp = dyg + 2 * (((int64_t)(n * a.Ho + ho) * a.Wo + wo0) * a.K + dy_col0);
-    const __amdgpu_buffer_rsrc_t rd = buf_rsrc(dyp, (npix * a.K - dy_col0) * 2);
+    const unsigned char* dyp = dyg + kEs * (((int64_t)(n * a.Ho + ho) * a.Wo + wo0) * a.K + dy_col0);
+    const __amdgpu_buffer_rsrc_t rd = buf_rsrc(dyp, (npix * a.K - dy_col0) * kEs);
 #pragma unroll
     for (int i = 0; i < kDyChunks; ++i)
-      rdy[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                             rd, ((px0 + 32 * i) * a.K + 8 * q8) * 2, 0, 0));
-    const int h = ho + r - a.pad;
+#pragma unroll
+      for (int h = 0; h < kLd; ++h)
+        rdy[i][h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rd, ((px0 + 32 * i) * a.K + 8 * q8) * kEs + 16 * h, 0, 0));
+    const int h = ho + r - a.pad_h;
     const bool row_ok = h >= 0 && h < a.H;
-    const unsigned char* xp = xg + 2 * ((int64_t)n * a.x_img + (int64_t)(row_ok ? h : 0) * a.W * a.C + x_col0);
+    const unsigned char* xp = xg + kEs * ((int64_t)n * a.x_img + (int64_t)(row_ok ? h : 0) * a.W * a.C + x_col0);
     const __amdgpu_buffer_rsrc_t rs = buf_rsrc(xp, row_ok ? x_row_bytes : 0);
-    const int w0 = wo0 - a.pad + s0;   // first staged X column (negative: padding, reads zero)
+    const int w0 = wo0 - a.pad_w + s0;   // first staged X column (negative: padding, reads zero)
 #pragma unroll
     for (int i = 0; i < kXChunks; ++i)
-      rx[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            rs, ((w0 + px0 + 32 * i) * a.C + 8 * q8) * 2, 0, 0));
+#pragma unroll
+      for (int hh = 0; hh < kLd; ++hh)
+        rx[i][hh] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rs, ((w0 + px0 + 32 * i) * a.C + 8 * q8) * kEs + 16 * hh, 0, 0));
   };
+  // BF16x3: per-thread fp32 sums of the staged dY values (8 channels at 8 q8
+  // for every loader pixel row), for the bias gradient.
+  const bool db_x3 = kX3 && kDb && r == 0 && sb == 0 && ct == 0;
+  float dbp[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   auto store_unit = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < kDyChunks; ++i)
-      *reinterpret_cast<uint4*>(&s_dy[buf][(px0 + 32 * i) * kPitchE + 8 * q8]) = rdy[i];
+    for (int i = 0; i < kDyChunks; ++i) {
+      unsigned short* d = &s_dy[0][buf][(px0 + 32 * i) * kPitchE + 8 * q8];
+      if constexpr (kX3) {
+        uint4 hi, lo;
+        split_bf16x8(rdy[i][0], rdy[i][kLd - 1], hi, lo);
+        *reinterpret_cast<uint4*>(d) = hi;
+        *reinterpret_cast<uint4*>(&s_dy[kPlanes - 1][buf][(px0 + 32 * i) * kPitchE + 8 * q8]) = lo;
+        if (db_x3) {
+          const uint32_t w[8] = {rdy[i][0].x, rdy[i][0].y, rdy[i][0].z, rdy[i][0].w,
+                                 rdy[i][kLd - 1].x, rdy[i][kLd - 1].y, rdy[i][kLd - 1].z, rdy[i][kLd - 1].w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dbp[e] += __uint_as_float(w[e]);
+        }
+      } else {
+        *reinterpret_cast<uint4*>(d) = rdy[i][0];
+      }
+    }
 #pragma unroll
     for (int i = 0; i < kXChunks; ++i)
-      if (px0 + 32 * i < kXs)
-        *reinterpret_cast<uint4*>(&s_x[buf][(px0 + 32 * i) * kPitchE + 8 * q8]) = rx[i];
+      if (px0 + 32 * i < kXs) {
+        unsigned short* d = &s_x[0][buf][(px0 + 32 * i) * kPitchE + 8 * q8];
+        if constexpr (kX3) {
+          uint4 hi, lo;
+          split_bf16x8(rx[i][0], rx[i][kLd - 1], hi, lo);
+          *reinterpret_cast<uint4*>(d) = hi;
+          *reinterpret_cast<uint4*>(&s_x[kPlanes - 1][buf][(px0 + 32 * i) * kPitchE + 8 * q8]) = lo;
+        } else {
+          *reinterpret_cast<uint4*>(d) = rx[i][0];
+        }
+      }
   };
 
   // Transposed-read addressing: in 16-lane group gq, lane j points at pixel
@@ -202,7 +267,7 @@ __global__ __launch_bounds__(256) void dense16_rows_kernel(R16Args a) {
   // Bias gradient: in the tile with the first filter row, tap block and input
   // channel block, wave 0 multiplies each A operand by ones (every column of
   // the product is the per-channel sum of the operand's 32 pixels).
-  const bool db_wave = kDb && r == 0 && sb == 0 && ct == 0 && wave == 0;
+  const bool db_wave = kDb && !kX3 && r == 0 && sb == 0 && ct == 0 && wave == 0;
   f32x4 acc_db[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc_db[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -211,8 +276,10 @@ __global__ __launch_bounds__(256) void dense16_rows_kernel(R16Args a) {
                    (short)one, (short)one, (short)one, (short)one};
 
   auto compute_unit = [&](int buf, int npix) {
-    const unsigned short* ad = s_dy[buf] + lane_off;
-    const unsigned short* bx = s_x[buf] + lane_off + 16 * wave;
+    const unsigned short* ad = s_dy[0][buf] + lane_off;
+    const unsigned short* bx = s_x[0][buf] + lane_off + 16 * wave;
+    const unsigned short* ad_lo = s_dy[kPlanes - 1][buf] + lane_off;
+    const unsigned short* bx_lo = s_x[kPlanes - 1][buf] + lane_off + 16 * wave;
 #pragma unroll
     for (int ks = 0; ks < kWt / 32; ++ks) {
       if (32 * ks < npix) {
@@ -221,11 +288,26 @@ __global__ __launch_bounds__(256) void dense16_rows_kernel(R16Args a) {
         for (int i = 0; i < 4; ++i) fa[i] = tr8(ad + 32 * ks * kPitchE + 16 * i);
 #pragma unroll
         for (int s = 0; s < SB; ++s) fb[s] = tr8(bx + (32 * ks + s) * kPitchE);
+        if constexpr (kX3) {
+          // The two cross terms first (small), then hi * hi.
+          s16x8 fa_lo[4], fb_lo[SB];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) fa_lo[i] = tr8(ad_lo + 32 * ks * kPitchE + 16 * i);
+#pragma unroll
+          for (int s = 0; s < SB; ++s) fb_lo[s] = tr8(bx_lo + (32 * ks + s) * kPitchE);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int s = 0; s < SB; ++s) {
+              acc[i][s] = mfma16<true>(fa_lo[i], fb[s], acc[i][s]);
+              acc[i][s] = mfma16<true>(fa[i], fb_lo[s], acc[i][s]);
+            }
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int s = 0; s < SB; ++s) acc[i][s] = mfma16<kBf16>(fa[i], fb[s], acc[i][s]);
-        if constexpr (kDb) {
+        if constexpr (kDb && !kX3) {
           if (db_wave) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc_db[i] = mfma16<kBf16>(fa[i], ones, acc_db[i]);
@@ -260,6 +342,14 @@ __global__ __launch_bounds__(256) void dense16_rows_kernel(R16Args a) {
           if (s0 + s < a.S) o[(int64_t)s * a.Cg] = acc[i][s][v];
       }
     }
+  if constexpr (kX3 && kDb) {
+    // 32 loader rows (px0) x 64 channels of per-thread sums, added in
+    // ascending row order through LDS (the staging buffers are free now).
+    if (db_x3)   // workgroup-uniform; block_sum64 has its own barriers
+      block_sum64<32, 8>(reinterpret_cast<float*>(&s_x[0][0][0]), px0, 8 * q8, dbp,
+                         a.dbo + (int64_t)slice * a.slab_stride + (int64_t)g * a.Kg + m0,
+                         min(64, a.Kg - m0));
+  }
   if (db_wave && j == 0) {
     float* o = a.dbo + (int64_t)slice * a.slab_stride + (int64_t)g * a.Kg;
 #pragma unroll
@@ -272,21 +362,21 @@ __global__ __launch_bounds__(256) void dense16_rows_kernel(R16Args a) {
   }
 }
 
-template <bool kBf16, int SB>
+template <bool kBf16, int SB, bool kX3>
 hipError_t launch_sb(const R16Args& args, int64_t grid, hipStream_t stream) {
   const dim3 xcd_grid((unsigned)((grid + 7) / 8 * 8)), block(256);   // whole rounds over the 8 XCDs
-  if (args.dbo) return launch_kernel(dense16_rows_kernel<kBf16, SB, true>, xcd_grid, block, args, stream);
-  return launch_kernel(dense16_rows_kernel<kBf16, SB, false>, xcd_grid, block, args, stream);
+  if (args.dbo) return launch_kernel(dense16_rows_kernel<kBf16, SB, true, kX3>, xcd_grid, block, args, stream);
+  return launch_kernel(dense16_rows_kernel<kBf16, SB, false, kX3>, xcd_grid, block, args, stream);
 }
 
-template <bool kBf16>
+template <bool kBf16, bool kX3>
 hipError_t launch_b(const Plan& plan, const R16Args& args, hipStream_t stream) {
   const int64_t grid = plan.pub.grid;
   switch (plan.sb) {
-    case 1: return launch_sb<kBf16, 1>(args, grid, stream);
-    case 2: return launch_sb<kBf16, 2>(args, grid, stream);
-    case 3: return launch_sb<kBf16, 3>(args, grid, stream);
-    default: return launch_sb<kBf16, 4>(args, grid, stream);
+    case 1: return launch_sb<kBf16, 1, kX3>(args, grid, stream);
+    case 2: return launch_sb<kBf16, 2, kX3>(args, grid, stream);
+    case 3: return launch_sb<kBf16, 3, kX3>(args, grid, stream);
+    default: return launch_sb<kBf16, 4, kX3>(args, grid, stream);
   }
 }
 
@@ -304,7 +394,8 @@ hipError_t launch_dense16_rows(const Plan& plan, const void* x, const void* dy, 
   a.x_img = p.x_img;
   a.H = (int32_t)p.H; a.W = (int32_t)p.W; a.C = (int32_t)p.C; a.K = (int32_t)p.K;
   a.Ho = (int32_t)p.Ho; a.Wo = (int32_t)p.Wo;
-  a.R = (int32_t)p.R; a.S = (int32_t)p.S; a.pad = (int32_t)p.pad;
+  a.R = (int32_t)p.R; a.S = (int32_t)p.S;
+  a.pad_h = (int32_t)p.pad_h; a.pad_w = (int32_t)p.pad_w;
   a.Cg = (int32_t)p.Cg; a.Kg = (int32_t)p.Kg; a.cols = (int32_t)p.cols;
   a.m_tiles = (int32_t)plan.m_tiles;
   a.c_tiles = (int32_t)plan.c_tiles;
@@ -319,8 +410,9 @@ hipError_t launch_dense16_rows(const Plan& plan, const void* x, const void* dy, 
   a.ks_count = plan.pub.ks_count;
   a.tiles = (int32_t)plan.pub.tiles;
   a.work = (int32_t)(plan.pub.tiles * plan.pub.ks_count);
-  if (p.dtype == CONV_WGRAD_BF16) return launch_b<true>(plan, a, stream);
-  return launch_b<false>(plan, a, stream);
+  if (p.dtype == CONV_WGRAD_F32) return launch_b<true, true>(plan, a, stream);   // BF16x3
+  if (p.dtype == CONV_WGRAD_BF16) return launch_b<true, false>(plan, a, stream);
+  return launch_b<false, false>(plan, a, stream);
 }
 
 }  // namespace cw

@@ -32,7 +32,7 @@ struct DenseArgs {
   int64_t slab_stride;
   int64_t x_img;  // H*W*C
   int32_t H, W, C, K, Ho, Wo;
-  int32_t R, S, pad, stride, dil;
+  int32_t R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w;
   int32_t Cg, Kg, cols;
   int32_t m_tiles, n_tiles;
   int32_t L, rows_per_slice, ks_count;
@@ -75,8 +75,8 @@ __global__ __launch_bounds__(256) void dense_lds_kernel(DenseArgs a) {
     const int jj = ci.valid[e] ? j : 0;
     const int c = jj % a.Cg, rs = jj / a.Cg;
     const int s = rs % a.S, r = rs / a.S;
-    ci.dh[e] = r * a.dil - a.pad;
-    ci.dw[e] = s * a.dil - a.pad;
+    ci.dh[e] = r * a.dil_h - a.pad_h;
+    ci.dw[e] = s * a.dil_w - a.pad_w;
     ci.ch[e] = g * a.Cg + c;
   }
   const int HoWo = a.Ho * a.Wo;
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void dense_lds_kernel(DenseArgs a) {
       const int ho = rem / a.Wo, wo = rem - (rem / a.Wo) * a.Wo;
       const T* xn = x + (int64_t)n * a.x_img;
       if (VB == 4) {
-        const int h = ho * a.stride + ci.dh[0], w = wo * a.stride + ci.dw[0];
+        const int h = ho * a.stride_h + ci.dh[0], w = wo * a.stride_w + ci.dw[0];
         if (lv && ci.valid[0] && h >= 0 && h < a.H && w >= 0 && w < a.W) {
           load4(xn + ((int64_t)h * a.W + w) * a.C + ci.ch[0], rb[it]);
         } else {
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256) void dense_lds_kernel(DenseArgs a) {
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int h = ho * a.stride + ci.dh[e], w = wo * a.stride + ci.dw[e];
+          const int h = ho * a.stride_h + ci.dh[e], w = wo * a.stride_w + ci.dw[e];
           rb[it][e] = (lv && ci.valid[e] && h >= 0 && h < a.H && w >= 0 && w < a.W)
                           ? to_f32(xn[((int64_t)h * a.W + w) * a.C + ci.ch[e]])
                           : 0.f;
@@ -217,8 +217,10 @@ hipError_t launch_dense(const Plan& plan, const void* x, const void* dy, Stage1O
   a.x_img = p.x_img;
   a.H = (int32_t)p.H; a.W = (int32_t)p.W; a.C = (int32_t)p.C; a.K = (int32_t)p.K;
   a.Ho = (int32_t)p.Ho; a.Wo = (int32_t)p.Wo;
-  a.R = (int32_t)p.R; a.S = (int32_t)p.S; a.pad = (int32_t)p.pad;
-  a.stride = (int32_t)p.stride; a.dil = (int32_t)p.dil;
+  a.R = (int32_t)p.R; a.S = (int32_t)p.S;
+  a.pad_h = (int32_t)p.pad_h; a.pad_w = (int32_t)p.pad_w;
+  a.stride_h = (int32_t)p.stride_h; a.stride_w = (int32_t)p.stride_w;
+  a.dil_h = (int32_t)p.dil_h; a.dil_w = (int32_t)p.dil_w;
   a.Cg = (int32_t)p.Cg; a.Kg = (int32_t)p.Kg; a.cols = (int32_t)p.cols;
   a.m_tiles = (int32_t)plan.m_tiles; a.n_tiles = (int32_t)plan.n_tiles;
   a.L = (int32_t)p.L;

@@ -43,7 +43,7 @@ struct RowsArgs {
   int64_t slab_stride;
   int64_t x_img;  // H*W*C
   int32_t H, W, C, K, Ho, Wo;
-  int32_t R, S, pad, stride, dil;
+  int32_t R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w;
   int32_t Cg, Kg, cols;
   int32_t m_tiles, c_tiles, s_blocks;
   int32_t wt, wchunks, xspan;
@@ -52,7 +52,7 @@ struct RowsArgs {
   float* dbo;            // bias-gradient partial of slice 0 (slab_stride apart), or nullptr
 };
 
-// kUnit: stride 1 and dilation 1 are compile-time (every LDS offset of the
+// kUnit: column stride 1 and column dilation 1 are compile-time (every LDS offset of the
 // MFMA loop is an immediate); otherwise they are read from the arguments.
 template <typename T, int SB, bool kUnit>
 __global__ __launch_bounds__(512, 1) void dense_rows_kernel(RowsArgs a) {
@@ -97,8 +97,8 @@ __global__ __launch_bounds__(512, 1) void dense_rows_kernel(RowsArgs a) {
   const int q = tid & 15, p0 = tid >> 4;
   const int dy_col0 = g * a.Kg + m0;         // first output channel of the tile
   const int x_col0 = g * a.Cg + c0;          // first input channel of the tile
-  const int dh = r * a.dil - a.pad;
-  const int xw_off = s0 * a.dil - a.pad;
+  const int dh = r * a.dil_h - a.pad_h;
+  const int xw_off = s0 * a.dil_w - a.pad_w;
   int oa[kMaxWt / 16], ob[kMaxXSpan / 16];
 #pragma unroll
   for (int i = 0; i < kMaxWt / 16; ++i) oa[i] = ((p0 + 16 * i) * a.K + 4 * q) * kEs;
@@ -122,9 +122,9 @@ __global__ __launch_bounds__(512, 1) void dense_rows_kernel(RowsArgs a) {
     const __amdgpu_buffer_rsrc_t rs_a = buf_rsrc(dyp, (npix * a.K - dy_col0) * kEs);
 #pragma unroll
     for (int i = 0; i < kMaxWt / 16; ++i) buf_load4(rs_a, oa[i], dyp, ra[i]);
-    const int h = ho * a.stride + dh;
+    const int h = ho * a.stride_h + dh;
     const bool row_ok = h >= 0 && h < a.H;
-    const int w0 = wo0 * a.stride + xw_off;
+    const int w0 = wo0 * a.stride_w + xw_off;
     const T* xp = x + (int64_t)n * a.x_img + (int64_t)(row_ok ? h : 0) * a.W * a.C + x_col0;
     const __amdgpu_buffer_rsrc_t rs_b = buf_rsrc(xp, row_ok ? x_row_bytes : 0);
     const int wb = w0 * a.C * kEs;
@@ -162,14 +162,14 @@ __global__ __launch_bounds__(512, 1) void dense_rows_kernel(RowsArgs a) {
 #pragma unroll
     for (int j = 0; j < SB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int stride = kUnit ? 1 : a.stride;
+  const int stride = kUnit ? 1 : a.stride_w;
   // Row li of M-block i is output channel m0 + 4*li + i, so a lane's four A
   // fragments are the 4 consecutive channels 4*li .. 4*li + 3 of its pixel
   // row: one 16-byte LDS read per k-step.
   const float* const A = buf + lg * kPitch + 4 * li;                   // + 4*kstep rows
   const float* const B = buf + kMaxWt * kPitch + lg * stride * kPitch + 16 * wave + li;
   const int b_kstep = 4 * stride * kPitch;
-  const int b_tap = (kUnit ? 1 : a.dil) * kPitch;
+  const int b_tap = (kUnit ? 1 : a.dil_w) * kPitch;
 
   // One unit's MFMAs: up to kMaxWt / 4 k-steps, fully unrolled so that every
   // LDS offset is an immediate (no VALU work between the MFMAs).  Two operand
@@ -287,7 +287,7 @@ hipError_t launch_u(const Plan& plan, const RowsArgs& args, hipStream_t stream) 
 
 template <typename T>
 hipError_t launch_t(const Plan& plan, const RowsArgs& args, hipStream_t stream) {
-  if (args.stride == 1 && args.dil == 1) return launch_u<T, true>(plan, args, stream);
+  if (args.stride_w == 1 && args.dil_w == 1) return launch_u<T, true>(plan, args, stream);
   return launch_u<T, false>(plan, args, stream);
 }
 
@@ -305,8 +305,10 @@ hipError_t launch_dense_rows(const Plan& plan, const void* x, const void* dy, St
   a.x_img = p.x_img;
   a.H = (int32_t)p.H; a.W = (int32_t)p.W; a.C = (int32_t)p.C; a.K = (int32_t)p.K;
   a.Ho = (int32_t)p.Ho; a.Wo = (int32_t)p.Wo;
-  a.R = (int32_t)p.R; a.S = (int32_t)p.S; a.pad = (int32_t)p.pad;
-  a.stride = (int32_t)p.stride; a.dil = (int32_t)p.dil;
+  a.R = (int32_t)p.R; a.S = (int32_t)p.S;
+  a.pad_h = (int32_t)p.pad_h; a.pad_w = (int32_t)p.pad_w;
+  a.stride_h = (int32_t)p.stride_h; a.stride_w = (int32_t)p.stride_w;
+  a.dil_h = (int32_t)p.dil_h; a.dil_w = (int32_t)p.dil_w;
   a.Cg = (int32_t)p.Cg; a.Kg = (int32_t)p.Kg; a.cols = (int32_t)p.cols;
   a.m_tiles = (int32_t)plan.m_tiles;
   a.c_tiles = (int32_t)plan.c_tiles;

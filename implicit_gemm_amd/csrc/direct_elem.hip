@@ -21,7 +21,7 @@ struct DirectArgs {
   int64_t slab_stride;
   int64_t x_img;
   int32_t H, W, C, K, Ho, Wo;
-  int32_t R, S, pad, stride, dil, Cg, Kg;
+  int32_t R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w, Cg, Kg;
   int32_t taps;  // R*S*Cg
   int32_t E;     // K*taps
   int32_t L, pix_per_slice, ks_count;
@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void direct_elem_kernel(DirectArgs a) {
   const int c = t % a.Cg, rs = t / a.Cg;
   const int s = rs % a.S, r = rs / a.S;
   const int ch = (k / a.Kg) * a.Cg + c;
-  const int dh = r * a.dil - a.pad, dw = s * a.dil - a.pad;
+  const int dh = r * a.dil_h - a.pad_h, dw = s * a.dil_w - a.pad_w;
   const int p_begin = slice * a.pix_per_slice;
   const int p_end = min(a.L, p_begin + a.pix_per_slice);
   const int HoWo = a.Ho * a.Wo;
@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256) void direct_elem_kernel(DirectArgs a) {
   const bool db_lane = a.dbo != nullptr && t == 0;
   float acc = 0.f, dbacc = 0.f;
   for (int pix = p_begin; pix < p_end; ++pix) {
-    const int h = ho * a.stride + dh, w = wo * a.stride + dw;
+    const int h = ho * a.stride_h + dh, w = wo * a.stride_w + dw;
     if (h >= 0 && h < a.H && w >= 0 && w < a.W) {
       const float gy = to_f32(dy[(int64_t)pix * a.K + k]);
       const float xv = to_f32(x[(int64_t)n * a.x_img + ((int64_t)h * a.W + w) * a.C + ch]);
@@ -82,8 +82,10 @@ hipError_t launch_direct(const Plan& plan, const void* x, const void* dy, Stage1
   a.x_img = p.x_img;
   a.H = (int32_t)p.H; a.W = (int32_t)p.W; a.C = (int32_t)p.C; a.K = (int32_t)p.K;
   a.Ho = (int32_t)p.Ho; a.Wo = (int32_t)p.Wo;
-  a.R = (int32_t)p.R; a.S = (int32_t)p.S; a.pad = (int32_t)p.pad;
-  a.stride = (int32_t)p.stride; a.dil = (int32_t)p.dil;
+  a.R = (int32_t)p.R; a.S = (int32_t)p.S;
+  a.pad_h = (int32_t)p.pad_h; a.pad_w = (int32_t)p.pad_w;
+  a.stride_h = (int32_t)p.stride_h; a.stride_w = (int32_t)p.stride_w;
+  a.dil_h = (int32_t)p.dil_h; a.dil_w = (int32_t)p.dil_w;
   a.Cg = (int32_t)p.Cg; a.Kg = (int32_t)p.Kg;
   a.taps = (int32_t)p.cols;
   a.E = (int32_t)p.E;

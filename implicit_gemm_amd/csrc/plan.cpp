@@ -44,22 +44,70 @@ constexpr int64_t kFoldBlock = 256, kFoldElemsPerBlock = 64;
 
 }  // namespace
 
-conv_wgrad_status_t canonicalise(const conv_wgrad_desc_t* d, Problem* o) {
+conv_wgrad_desc2_t to_desc2(const conv_wgrad_desc_t& d) {
+  conv_wgrad_desc2_t e;
+  memset(&e, 0, sizeof(e));
+  e.N = d.N; e.C = d.C; e.H = d.H; e.W = d.W; e.K = d.K; e.R = d.R; e.S = d.S;
+  e.pad_h = e.pad_w = d.pad;
+  e.stride_h = e.stride_w = d.stride;
+  e.dil_h = e.dil_w = d.dilation;
+  e.groups = d.groups;
+  e.dtype = d.dtype;
+  e.split_k = d.split_k;
+  e.math = CONV_WGRAD_MATH_EXACT;
+  e.fold_width = -1;
+  return e;
+}
+
+namespace {
+
+int64_t gcd64(int64_t a, int64_t b) {
+  while (b != 0) {
+    const int64_t t = a % b;
+    a = b;
+    b = t;
+  }
+  return a;
+}
+
+// Width fold by f (the caller has checked that f divides S, stride_w, W and
+// pad_w, with dil_w == 1 and one group): X [N][H][W][C] read as
+// [N][H][W/f][f*C], the filter [K][R][S][C] as [K][R][S/f][f*C].  Wo, the
+// tensor sizes and the dW layout do not change.
+void apply_fold(Problem* o, int64_t f) {
+  o->W /= f;
+  o->S /= f;
+  o->stride_w /= f;
+  o->pad_w /= f;
+  o->C *= f;
+  o->fold = (int32_t)f;
+}
+
+}  // namespace
+
+conv_wgrad_status_t canonicalise(const conv_wgrad_desc2_t* d, Problem* o) {
   if (!d || !o) return CONV_WGRAD_ERR_NULL_ARG;
   memset(o, 0, sizeof(*o));
   if (d->dtype != CONV_WGRAD_F32 && d->dtype != CONV_WGRAD_BF16 && d->dtype != CONV_WGRAD_F16)
     return CONV_WGRAD_ERR_BAD_DTYPE;
+  if (d->math != CONV_WGRAD_MATH_EXACT && d->math != CONV_WGRAD_MATH_BF16X3) return CONV_WGRAD_ERR_BAD_DTYPE;
   if (d->split_k == 0 || d->split_k < -1) return CONV_WGRAD_ERR_BAD_SPLIT;
   if (d->N < 1 || d->C < 1 || d->H < 1 || d->W < 1 || d->K < 1 || d->R < 1 || d->S < 1 ||
-      d->pad < 0 || d->stride < 1 || d->dilation < 1 || d->groups < 1)
+      d->pad_h < 0 || d->pad_w < 0 || d->stride_h < 1 || d->stride_w < 1 || d->dil_h < 1 ||
+      d->dil_w < 1 || d->groups < 1 || d->fold_width < -1)
     return CONV_WGRAD_ERR_BAD_SHAPE;
   if (d->C % d->groups != 0 || d->K % d->groups != 0) return CONV_WGRAD_ERR_BAD_SHAPE;
   o->N = d->N; o->C = d->C; o->H = d->H; o->W = d->W; o->K = d->K; o->R = d->R; o->S = d->S;
-  o->pad = d->pad; o->stride = d->stride; o->dil = d->dilation; o->groups = d->groups;
+  o->pad_h = d->pad_h; o->pad_w = d->pad_w;
+  o->stride_h = d->stride_h; o->stride_w = d->stride_w;
+  o->dil_h = d->dil_h; o->dil_w = d->dil_w;
+  o->groups = d->groups;
   o->dtype = d->dtype;
+  o->math = d->dtype == CONV_WGRAD_F32 ? d->math : CONV_WGRAD_MATH_EXACT;
+  o->fold = 1;
   o->esize = d->dtype == CONV_WGRAD_F32 ? 4 : 2;
-  o->Ho = extent(d->H, d->R, d->pad, d->stride, d->dilation);
-  o->Wo = extent(d->W, d->S, d->pad, d->stride, d->dilation);
+  o->Ho = extent(d->H, d->R, d->pad_h, d->stride_h, d->dil_h);
+  o->Wo = extent(d->W, d->S, d->pad_w, d->stride_w, d->dil_w);
   if (o->Ho < 1 || o->Wo < 1) return CONV_WGRAD_ERR_BAD_SHAPE;
   o->Cg = d->C / d->groups;
   o->Kg = d->K / d->groups;
@@ -76,9 +124,31 @@ conv_wgrad_status_t canonicalise(const conv_wgrad_desc_t* d, Problem* o) {
   // Documented limits: offsets inside one image, the reduction index and the
   // dW index are 32-bit in the kernels; bases of images are 64-bit.
   if (o->x_img > kI32Max || o->dy_img > kI32Max || o->L > kMaxRows || o->E > kI32Max ||
-      o->H > kI32Max / 2 || o->W > kI32Max / 2 || o->pad > kI32Max / 4 ||
-      o->stride > kI32Max / 4 || o->dil > kI32Max / 4 || o->R > kI32Max / 4 || o->S > kI32Max / 4)
+      o->H > kI32Max / 2 || o->W > kI32Max / 2 || o->pad_h > kI32Max / 4 || o->pad_w > kI32Max / 4 ||
+      o->stride_h > kI32Max / 4 || o->stride_w > kI32Max / 4 || o->dil_h > kI32Max / 4 ||
+      o->dil_w > kI32Max / 4 || o->R > kI32Max / 4 || o->S > kI32Max / 4)
     return CONV_WGRAD_ERR_UNSUPPORTED;
+
+  // Width fold (the foldable f all divide S, stride_w, W and pad_w).
+  const bool foldable = o->groups == 1 && o->dil_w == 1;
+  const int64_t fmax = foldable ? gcd64(gcd64(o->S, o->stride_w), gcd64(o->W, o->pad_w)) : 1;
+  if (d->fold_width >= 2) {
+    if (!foldable || fmax % d->fold_width != 0) return CONV_WGRAD_ERR_BAD_SHAPE;
+    int64_t fc;
+    if (!mul_ok(o->C, d->fold_width, &fc) || fc > kI32Max) return CONV_WGRAD_ERR_UNSUPPORTED;
+    apply_fold(o, d->fold_width);
+  } else if (d->fold_width == -1 && fmax >= 2 && o->Cg % 4 != 0 && (o->Cg * fmax) % 4 == 0 &&
+             o->C * fmax <= kI32Max) {
+    apply_fold(o, fmax);
+  }
+  if (o->fold > 1) {
+    o->Cg = o->C;   // one group
+    o->cols = o->R * o->S * o->Cg;
+  }
+  o->uniform = o->pad_h == o->pad_w && o->stride_h == o->stride_w && o->dil_h == o->dil_w;
+  o->pad = o->pad_h;
+  o->stride = o->stride_h;
+  o->dil = o->dil_h;
   return CONV_WGRAD_OK;
 }
 
@@ -153,13 +223,13 @@ bool plan_dense_rows(const Problem& p, Plan* out) {
   if (p.W * p.C * p.esize > kI32Max / 2 || p.Wo * p.K * p.esize > kI32Max / 2) return false;
   int64_t dy_reach, x_cols, x_reach;
   if (!mul3(kRowsMaxWt, p.K, p.esize, &dy_reach) || dy_reach > kI32Max / 2) return false;
-  if (!mul_ok(p.S, p.dil, &x_cols) || x_cols > kI32Max) return false;
-  x_cols += p.W + 2 * p.pad + kRowsMaxXSpan;
+  if (!mul_ok(p.S, p.dil_w, &x_cols) || x_cols > kI32Max) return false;
+  x_cols += p.W + 2 * p.pad_w + kRowsMaxXSpan;
   if (!mul3(x_cols, p.C, p.esize, &x_reach) || x_reach > kI32Max / 2) return false;
   const int64_t sb = p.S < 4 ? p.S : 4;
   int64_t wt = 0;
   for (int64_t cand = kRowsMaxWt; cand >= 16; cand -= 16) {
-    if ((cand - 1) * p.stride + (sb - 1) * p.dil + 1 <= kRowsMaxXSpan) {
+    if ((cand - 1) * p.stride_w + (sb - 1) * p.dil_w + 1 <= kRowsMaxXSpan) {
       wt = cand;
       break;
     }
@@ -169,7 +239,7 @@ bool plan_dense_rows(const Problem& p, Plan* out) {
   if (wt > wo16) wt = wo16;
   out->sb = (int32_t)sb;
   out->wt = (int32_t)wt;
-  out->xspan = (int32_t)((wt - 1) * p.stride + (sb - 1) * p.dil + 1);
+  out->xspan = (int32_t)((wt - 1) * p.stride_w + (sb - 1) * p.dil_w + 1);
   out->s_blocks = ceil_div(p.S, sb);
   out->c_tiles = ceil_div(p.Cg, 64);
   out->m_tiles = ceil_div(p.Kg, 64);
@@ -180,7 +250,9 @@ bool plan_dense_rows(const Problem& p, Plan* out) {
 // 1x1 streaming kernel: fp32, unpadded stride-1 1x1 filter, output channels in
 // whole 64-channel tiles and input channels in 16-channel lane groups.
 bool plan_dense_1x1(const Problem& p, Plan* out) {
-  if (p.dtype != CONV_WGRAD_F32 || p.R != 1 || p.S != 1 || p.pad != 0 || p.stride != 1) return false;
+  if (p.dtype != CONV_WGRAD_F32 || p.R != 1 || p.S != 1 || p.pad_h != 0 || p.pad_w != 0 ||
+      p.stride_h != 1 || p.stride_w != 1)
+    return false;
   if (p.Kg % 64 != 0 || p.Cg % 16 != 0) return false;
   // A batch's buffer range (4 rows) and the lane offsets are 32-bit.
   if (p.C > (1 << 26) || p.K > (1 << 26)) return false;
@@ -202,7 +274,7 @@ bool plan_dense_1x1(const Problem& p, Plan* out) {
 // group dividing 16, channel count in 16-channel super-groups, at most 9 taps,
 // and a staged tile of at most 8 X rows x 40 X pixels.
 bool plan_grouped16(const Problem& p, Plan* out) {
-  if (p.dtype == CONV_WGRAD_F32 || p.stride != 1 || p.Cg != p.Kg || 16 % p.Cg != 0) return false;
+  if (!p.uniform || p.dtype == CONV_WGRAD_F32 || p.stride != 1 || p.Cg != p.Kg || 16 % p.Cg != 0) return false;
   if (p.C % 16 != 0 || p.R * p.S > 9 || (p.S - 1) * p.dil + 32 > 40) return false;
   int32_t ru = 0;
   for (int32_t cand = 4; cand >= 1; cand /= 2) {
@@ -225,7 +297,7 @@ bool plan_grouped16(const Problem& p, Plan* out) {
 // of at most 64 pixels at stride 1 (two MFMA k-steps) or 32 at stride 2, and
 // padding below the filter size.
 bool plan_grouped16_rows(const Problem& p, Plan* out) {
-  if (p.dtype == CONV_WGRAD_F32 || (p.stride != 1 && p.stride != 2) || p.dil != 1 || p.Cg != p.Kg ||
+  if (!p.uniform || p.dtype == CONV_WGRAD_F32 || (p.stride != 1 && p.stride != 2) || p.dil != 1 || p.Cg != p.Kg ||
       16 % p.Cg != 0)
     return false;
   // Rows of up to 64 output pixels at stride 1 (two MFMA k-steps), 32 at stride 2.
@@ -240,14 +312,18 @@ bool plan_grouped16_rows(const Problem& p, Plan* out) {
 // counts in whole 16-byte chunks (8 channels); units of up to 64 output pixels
 // (32 when the output row is that short), up to 4 taps per tile.
 bool plan_dense16_rows(const Problem& p, Plan* out) {
-  if (p.dtype == CONV_WGRAD_F32 || p.stride != 1 || p.dil != 1) return false;
+  // 16-bit inputs, or fp32 inputs under BF16x3 (split into two bf16 planes at staging).
+  const bool x3 = p.dtype == CONV_WGRAD_F32 && p.math == CONV_WGRAD_MATH_BF16X3;
+  if ((p.dtype == CONV_WGRAD_F32 && !x3) || p.stride_h != 1 || p.stride_w != 1 || p.dil_h != 1 || p.dil_w != 1)
+    return false;
   if (p.C % 8 != 0 || p.K % 8 != 0 || p.Cg % 8 != 0 || p.Kg % 8 != 0) return false;
-  if (p.W * p.C * 2 > kI32Max / 2 || p.Wo * p.K * 2 > kI32Max / 2) return false;
+  const int64_t es = p.esize;
+  if (p.W * p.C * es > kI32Max / 2 || p.Wo * p.K * es > kI32Max / 2) return false;
   // Lane offsets reach 64 dY pixels into a unit and X columns from -pad to
   // past the image by the staged 96 pixels plus the filter's reach.
   int64_t dy_reach, x_reach;
-  if (!mul3(64, p.K, 2, &dy_reach) || dy_reach > kI32Max / 2) return false;
-  if (!mul3(p.W + 2 * p.pad + p.S + 96, p.C, 2, &x_reach) || x_reach > kI32Max / 2) return false;
+  if (!mul3(64, p.K, es, &dy_reach) || dy_reach > kI32Max / 2) return false;
+  if (!mul3(p.W + 2 * p.pad_w + p.S + 96, p.C, es, &x_reach) || x_reach > kI32Max / 2) return false;
   out->sb = (int32_t)(p.S < 4 ? p.S : 4);
   out->wt = p.Wo > 32 ? 64 : 32;
   out->s_blocks = ceil_div(p.S, out->sb);
@@ -259,7 +335,10 @@ bool plan_dense16_rows(const Problem& p, Plan* out) {
   const int64_t pitch = p.Wo + out->sb - 1;
   out->ru = pitch <= 32 ? (int32_t)(64 / pitch) : 1;
   // A unit's rows are one buffer range each for X and dY (32-bit).
-  if (out->ru > 1 && (out->ru * p.W * p.C * 2 > kI32Max || out->ru * p.Wo * p.K * 2 > kI32Max)) out->ru = 1;
+  // (Below 2^30, so the out-of-range offset the loaders use for empty slots
+  // lies past every range.)
+  if (out->ru > 1 && (out->ru * p.W * p.C * es > kI32Max / 2 || out->ru * p.Wo * p.K * es > kI32Max / 2))
+    out->ru = 1;
   if (out->ru > 1) {
     out->wt = 64;
     out->wchunks = 1;
@@ -282,7 +361,7 @@ bool plan_dense16_rows(const Problem& p, Plan* out) {
 // stores of a pixel pair are 8-byte aligned).  X rows advance two per output
 // row.
 bool plan_depthwise(const Problem& p, Plan* out) {
-  if (p.dtype == CONV_WGRAD_F32 || p.Cg != 1 || p.Kg != 1 || p.dil != 1) return false;
+  if (!p.uniform || p.dtype == CONV_WGRAD_F32 || p.Cg != 1 || p.Kg != 1 || p.dil != 1) return false;
   if (p.stride != 1 && p.stride != 2) return false;
   if (p.C % 16 != 0 || p.C > (1 << 20) || p.R > 12 || p.S > 12 || p.pad > 12) return false;
   if (p.W > 120 || p.Wo > 128 || p.W * p.C * 2 > kI32Max) return false;
@@ -312,7 +391,7 @@ bool plan_depthwise(const Problem& p, Plan* out) {
 
 }  // namespace
 
-conv_wgrad_status_t make_plan(const conv_wgrad_desc_t* desc, Plan* out) {
+conv_wgrad_status_t make_plan(const conv_wgrad_desc2_t* desc, Plan* out) {
   if (!desc || !out) return CONV_WGRAD_ERR_NULL_ARG;
   memset(out, 0, sizeof(*out));
   Problem& p = out->p;
@@ -394,7 +473,8 @@ conv_wgrad_status_t make_plan(const conv_wgrad_desc_t* desc, Plan* out) {
     return choose_split(ceil_div(p.L, 64), tiles, desc->split_k, 4, 2048, 4, p, &pub);
   }
   if (plan_dense16_rows(p, out)) {
-    pub.variant = kDense16Rows;
+    const bool x3 = p.dtype == CONV_WGRAD_F32;   // BF16x3 (the planner only allows it then)
+    pub.variant = x3 ? kDense16RowsX3 : kDense16Rows;
     int64_t units, tiles;
     if (out->ru > 1) {
       pub.unit_rows = out->ru * p.Wo;   // a unit is ru whole output rows
@@ -411,6 +491,8 @@ conv_wgrad_status_t make_plan(const conv_wgrad_desc_t* desc, Plan* out) {
     // slices are worth up to 4x the algorithmic bytes in slab traffic.  Units
     // of several short rows carry ~4x the MFMA work of a single short row:
     // three per CU, and slab traffic up to 8x (it overlaps the MFMAs).
+    // BF16x3 holds two planes (82.5 KB of LDS): one workgroup per CU.
+    if (x3) return choose_split(units, tiles, desc->split_k, 2, 256, 1, p, &pub, 0, 4);
     if (out->ru > 1) return choose_split(units, tiles, desc->split_k, 2, 768, 1, p, &pub, 0, 8);
     return choose_split(units, tiles, desc->split_k, 2, 512, 1, p, &pub, 0, 4);
   }

@@ -19,6 +19,7 @@ enum Variant : int32_t {
   kDenseRows = 1,     // dense implicit GEMM over output-row units, per-filter-row tiles
   kDense1x1 = 2,      // 1x1 stride-1 unpadded fp32: rows streamed into MFMA registers
   kDense16Rows = 3,   // 16-bit dense, stride 1, dilation 1: row units on 16x16x32 bf16/fp16 MFMA
+  kDense16RowsX3 = 4, // fp32 dense by BF16x3 emulation on the 16-bit row kernel (math = BF16X3)
   kDirectElem = 10,   // direct small-group kernel, one dW element per lane
   kGrouped16 = 11,    // 16-bit small groups: block-diagonal 16x16x32 MFMA, transposed LDS reads
   kDepthwise = 12,    // 16-bit depthwise: batched 4x4x4 MFMA, 64 channels per workgroup
@@ -26,7 +27,15 @@ enum Variant : int32_t {
 };
 
 struct Problem {
-  int64_t N, C, H, W, K, R, S, pad, stride, dil, groups;
+  int64_t N, C, H, W, K, R, S, groups;
+  // Per-axis geometry: rows (h) and columns (w).
+  int64_t pad_h, pad_w, stride_h, stride_w, dil_h, dil_w;
+  // The row values, for the kernels the planner gives only problems whose
+  // two axes agree (uniform).
+  int64_t pad, stride, dil;
+  bool uniform;
+  int32_t math;          // CONV_WGRAD_MATH_*
+  int32_t fold;          // width fold applied (1 = none): C, W, S, stride_w, pad_w are the folded ones
   int32_t dtype;
   int32_t esize;         // bytes per x / dy element
   int64_t Ho, Wo, Cg, Kg;
@@ -61,15 +70,19 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // bias-gradient partial (K elements) from this 16-byte aligned offset on.
 inline int64_t db_offset(const Problem& p) { return ceil_div(p.E, 4) * 4; }
 
-// Validate and canonicalise desc.  Returns CONV_WGRAD_OK or the error code.
-conv_wgrad_status_t canonicalise(const conv_wgrad_desc_t* desc, Problem* out);
+// The extended descriptor of a plain one (equal axes, exact math, automatic fold).
+conv_wgrad_desc2_t to_desc2(const conv_wgrad_desc_t& d);
+
+// Validate and canonicalise desc (and apply the width fold it asks for or
+// allows).  Returns CONV_WGRAD_OK or the error code.
+conv_wgrad_status_t canonicalise(const conv_wgrad_desc2_t* desc, Problem* out);
 
 // LDS bytes of the depthwise kernel for staged rows of xl columns and an R x S
 // filter (0 if xl is not a supported length); defined with the kernel.
 int32_t depthwise_lds_bytes(int32_t xl, int32_t R, int32_t S);
 
 // Build the full plan (calls canonicalise).
-conv_wgrad_status_t make_plan(const conv_wgrad_desc_t* desc, Plan* out);
+conv_wgrad_status_t make_plan(const conv_wgrad_desc2_t* desc, Plan* out);
 
 // Split policy shared by all paths.  `units` reduction units, `tiles` output
 // tiles per slice, `requested` the descriptor's split_k (-1 = auto).  Fills

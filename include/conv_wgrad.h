@@ -218,6 +218,92 @@ conv_wgrad_status_t conv_wgrad_bias_timed(const conv_wgrad_desc_t* desc, const v
                                           void* stage1_end);
 
 /*
+ * Extended problem descriptor: per-axis geometry, an arithmetic mode for fp32
+ * inputs and the width fold.  conv_wgrad_desc_t is this with equal axes,
+ * math = CONV_WGRAD_MATH_EXACT and fold_width = -1.
+ *
+ * Per-axis geometry (the column padding pad_w beside the row padding of
+ * rocm-libraries PR #14393's embedded depthwise-dgrad PR #14386, section
+ * "Per-axis padding"; stride and dilation the same way):
+ *   dW[k, r, s, c] = sum_{n, ho, wo} dY[n, ho, wo, k]
+ *       * X[n, ho*stride_h + r*dil_h - pad_h, wo*stride_w + s*dil_w - pad_w, g(k)*Cg + c]
+ *   Ho = (H + 2*pad_h - dil_h*(R-1) - 1) / stride_h + 1,
+ *   Wo = (W + 2*pad_w - dil_w*(S-1) - 1) / stride_w + 1.
+ *   pad_h, pad_w >= 0; stride_h, stride_w, dil_h, dil_w >= 1 (BAD_SHAPE otherwise).
+ *
+ * math (fp32 inputs; ignored for bf16 / fp16, which always use their own MFMA):
+ *   CONV_WGRAD_MATH_EXACT  (0): fp32 products on f32 MFMA (the default).
+ *   CONV_WGRAD_MATH_BF16X3 (1): BF16x3 emulation, the form the pages give for
+ *       fp32 ("TF32") matrix work on gfx950 (rocm-libraries PR #14393,
+ *       timeline, the TF32 entry: native XF32 on gfx942, BF16x3 on gfx950):
+ *       each fp32 value v = hi + lo with hi = bf16(v), lo = bf16(v - hi), and
+ *       a*b ~ a_hi*b_hi + a_hi*b_lo + a_lo*b_hi on bf16 MFMA with fp32
+ *       accumulation.  Each product carries a relative error of at most about
+ *       3 * 2^-16 (the dropped a_lo*b_lo term and the two splits' residuals),
+ *       so the normalised error is bounded by ~4.6e-5 in the worst case and is
+ *       ~1e-7 for inputs of random sign.  It is a permission, never a silent
+ *       downgrade of other shapes: the plan uses it only where a BF16x3 kernel
+ *       covers the shape (plan variant CONV_WGRAD_VARIANT_DENSE_BF16X3) and the
+ *       exact fp32 path elsewhere.  Any other value is BAD_DTYPE.
+ * fold_width (rocm-libraries PR #14393, commit bodies, the fold_width
+ * paragraph: f adjacent W positions folded into the channels when f divides
+ * the filter width, the W stride, the input width and the W padding; the
+ * identity holds in every direction, so it is a view of the same tensors):
+ *   -1: fold by the largest such f when the shape gains from it (input
+ *       channels per group not a multiple of 4, a multiple after folding);
+ *    0 or 1: never fold;  f >= 2: fold by f (BAD_SHAPE if f does not divide
+ *       S, stride_w, W and pad_w, or if dil_w != 1 or groups != 1).
+ *   Folding changes only the kernel and the summation order, never the
+ *   layouts: X [N][H][W][C] is read as [N][H][W/f][f*C], dY is unchanged, and
+ *   dW [K][R][S][Cg] is written as [K][R][S/f][f*Cg] -- the same bytes.
+ */
+typedef struct conv_wgrad_desc2 {
+  int64_t N, C, H, W, K, R, S;
+  int64_t pad_h, pad_w, stride_h, stride_w, dil_h, dil_w;
+  int64_t groups;
+  int32_t dtype;       /* conv_wgrad_dtype_t of x and dy */
+  int32_t split_k;     /* as in conv_wgrad_desc_t */
+  int32_t math;        /* CONV_WGRAD_MATH_* */
+  int32_t fold_width;  /* -1 auto, 0 / 1 off, f >= 2 fold by f */
+} conv_wgrad_desc2_t;
+
+#define CONV_WGRAD_MATH_EXACT 0
+#define CONV_WGRAD_MATH_BF16X3 1
+
+/* conv_wgrad_plan_t::variant of the BF16x3 dense kernel. */
+#define CONV_WGRAD_VARIANT_DENSE_BF16X3 4
+
+/* The plan of an extended descriptor: the base plan (of the problem the kernels
+ * run, i.e. after a width fold) and what was applied. */
+typedef struct conv_wgrad_plan2 {
+  conv_wgrad_plan_t base;
+  int32_t math;        /* CONV_WGRAD_MATH_* the kernels use */
+  int32_t fold_width;  /* applied fold (1 = none) */
+} conv_wgrad_plan2_t;
+
+/*
+ * conv_wgrad_workspace_size for an extended descriptor: the workspace bytes
+ * conv_wgrad2 needs (0 when the plan has one slice).  Pure host function;
+ * errors: NULL_ARG (desc or bytes NULL), BAD_SHAPE, BAD_DTYPE (also a math
+ * value outside CONV_WGRAD_MATH_*), BAD_SPLIT, UNSUPPORTED.
+ */
+conv_wgrad_status_t conv_wgrad2_workspace_size(const conv_wgrad_desc2_t* desc, size_t* bytes);
+
+/* conv_wgrad_get_plan for an extended descriptor (same validation and errors). */
+conv_wgrad_status_t conv_wgrad2_get_plan(const conv_wgrad_desc2_t* desc, conv_wgrad_plan2_t* plan);
+
+/*
+ * The weight gradient (and, when db is not NULL, the bias gradient db[k] =
+ * sum of dy over n, ho, wo) for an extended descriptor, enqueued on `stream`.
+ * Layouts, ownership, workspace rules (at least conv_wgrad2_workspace_size
+ * bytes, WORKSPACE otherwise; NULL allowed when that is 0), alignment,
+ * determinism at a fixed split and errors are those of conv_wgrad_bias; dw
+ * and db are overwritten.
+ */
+conv_wgrad_status_t conv_wgrad2(const conv_wgrad_desc2_t* desc, const void* x, const void* dy,
+                                float* dw, float* db, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): conv_wgrad_bias
  * without the workspace argument.  The slabs live in a library-owned device

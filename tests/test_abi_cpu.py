@@ -21,7 +21,8 @@ GOLDEN = os.path.join(ROOT, "tests", "golden")
 
 PUBLIC_FUNCTIONS = {"conv_wgrad", "conv_wgrad_ex", "conv_wgrad_get_plan", "conv_wgrad_timed",
                     "conv_wgrad_status_string", "conv_wgrad_workspace_size", "conv_wgrad_bias",
-                    "conv_wgrad_bias_timed", "conv_wgrad_noalloc"}
+                    "conv_wgrad_bias_timed", "conv_wgrad_noalloc", "conv_wgrad2_workspace_size",
+                    "conv_wgrad2_get_plan", "conv_wgrad2"}
 
 
 def declared_functions(header=HEADER, prefix="conv_wgrad"):
@@ -64,6 +65,9 @@ def test_struct_sizes_match_header_layout():
     # 11 int64 + 2 int32; plan: see conv_wgrad_plan_t field order.
     assert ctypes.sizeof(iga.Desc) == 11 * 8 + 2 * 4
     assert ctypes.sizeof(iga.Plan) == 8 + 8 * 7 + 4 + 4 + 8 * 3 + 8 * 4 + 8
+    # desc2: 14 int64 + 4 int32; plan2: plan + 2 int32
+    assert ctypes.sizeof(iga.Desc2) == 14 * 8 + 4 * 4
+    assert ctypes.sizeof(iga.Plan2) == ctypes.sizeof(iga.Plan) + 8
 
 
 def test_peak_probe_argument_errors():
@@ -315,3 +319,142 @@ def test_row_kernel_lane_offsets_stay_32_bit():
     c_over += (-c_over) % 8
     over16 = iga.get_plan(D(N=1, C=c_over, H=1, W=1, K=8, R=1, S=1, pad=0, dtype=iga.BF16))
     assert over16.variant != 3
+
+
+def D2(**kw):
+    base = dict(N=2, C=8, H=8, W=8, K=4, R=3, S=3, pad=1, stride=1, dilation=1, groups=1,
+                dtype=iga.F32, split_k=-1, math="exact", fold_width=-1)
+    base.update(kw)
+    return iga.make_desc2(**base)
+
+
+def _status2(d):
+    plan = iga.Plan2()
+    return iga.load().conv_wgrad2_get_plan(ctypes.byref(d), ctypes.byref(plan))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(pad=(-1, 0)), 2), (dict(pad=(0, -1)), 2), (dict(stride=(0, 1)), 2), (dict(stride=(1, 0)), 2),
+    (dict(dilation=(1, 0)), 2), (dict(dilation=(0, 1)), 2),
+    (dict(W=2, S=3, pad=(1, 0)), 2),                 # Wo < 1 from the column geometry
+    (dict(H=2, R=3, pad=(0, 1)), 2),                 # Ho < 1 from the row geometry
+    (dict(math=2), 3), (dict(math=-1), 3),
+    (dict(fold_width=-2), 2),
+    (dict(fold_width=2, S=3), 2),                    # 2 does not divide S
+    (dict(fold_width=2, S=2, pad=0, stride=2, groups=2), 2),     # groups
+    (dict(fold_width=2, S=2, pad=0, stride=2, dilation=(1, 2)), 2),  # column dilation
+    (dict(fold_width=2, S=2, pad=(0, 1), stride=2), 2),  # 2 does not divide pad_w
+    (dict(fold_width=2, S=2, pad=0, stride=2, W=7), 2),  # 2 does not divide W
+    (dict(split_k=0), 4),
+])
+def test_desc2_invalid_is_rejected(kw, code):
+    lib = iga.load()
+    d = D2(**kw)
+    assert _status2(d) == code
+    n = ctypes.c_size_t(0)
+    assert lib.conv_wgrad2_workspace_size(ctypes.byref(d), ctypes.byref(n)) == code
+    assert lib.conv_wgrad2(ctypes.byref(d), 16, 16, 16, None, 16, 1 << 30, None) == code
+
+
+def test_desc2_null_arguments():
+    lib = iga.load()
+    d = D2()
+    ws = iga.get_plan2(d).base.ws_bytes
+    assert lib.conv_wgrad2(None, 16, 16, 16, None, 16, ws, None) == 1
+    assert lib.conv_wgrad2(ctypes.byref(d), None, 16, 16, None, 16, ws, None) == 1
+    assert lib.conv_wgrad2(ctypes.byref(d), 16, None, 16, None, 16, ws, None) == 1
+    assert lib.conv_wgrad2(ctypes.byref(d), 16, 16, None, None, 16, ws, None) == 1
+    assert lib.conv_wgrad2_get_plan(ctypes.byref(d), None) == 1
+    assert lib.conv_wgrad2_workspace_size(ctypes.byref(d), None) == 1
+
+
+def test_desc2_equal_axes_plan_equals_plain_plan():
+    """An extended descriptor with equal axes, exact math and the automatic fold
+    plans exactly as the plain descriptor."""
+    rng = np.random.default_rng(5)
+    fields = [n for n, _ in iga.Plan._fields_]
+    for _ in range(400):
+        groups = int(rng.choice([1, 2, 4, 16]))
+        C, K = groups * int(rng.integers(1, 9)), groups * int(rng.integers(1, 9))
+        H, W = int(rng.integers(3, 40)), int(rng.integers(3, 40))
+        R, S = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        pad, stride, dil = int(rng.integers(0, 2)), int(rng.integers(1, 3)), int(rng.integers(1, 3))
+        if H + 2 * pad - dil * (R - 1) - 1 < 0 or W + 2 * pad - dil * (S - 1) - 1 < 0:
+            continue
+        dt, sk = int(rng.integers(0, 3)), int(rng.choice([-1, 1, 3]))
+        N = int(rng.integers(1, 9))
+        a = iga.get_plan(iga.make_desc(N, C, H, W, K, R, S, pad, stride, dil, groups, dt, sk))
+        b = iga.get_plan2(iga.make_desc2(N, C, H, W, K, R, S, pad, stride, dil, groups, dt, sk))
+        assert [getattr(a, f) for f in fields] == [getattr(b.base, f) for f in fields]
+
+
+def test_per_axis_plans_route_to_per_axis_kernels():
+    """Unequal axes reach only the kernels that take per-axis geometry (dense rows,
+    16-bit dense rows, the general dense kernel, the element kernel), and the plan's
+    extents follow the row and column geometry."""
+    rng = np.random.default_rng(9)
+    per_axis_variants = {0, 1, 3, 4, 10}
+    seen = set()
+    for _ in range(1500):
+        groups = int(rng.choice([1, 1, 2, 8, 32]))
+        C, K = groups * int(rng.integers(1, 9)), groups * int(rng.integers(1, 9))
+        H, W = int(rng.integers(1, 60)), int(rng.integers(1, 60))
+        R, S = int(rng.integers(1, 6)), int(rng.integers(1, 6))
+        ph, pw = int(rng.integers(0, 3)), int(rng.integers(0, 3))
+        sh, sw = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        dh, dw = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+        Ho = (H + 2 * ph - dh * (R - 1) - 1)
+        Wo = (W + 2 * pw - dw * (S - 1) - 1)
+        if Ho < 0 or Wo < 0 or (ph == pw and sh == sw and dh == dw):
+            continue
+        d = iga.make_desc2(int(rng.integers(1, 9)), C, H, W, K, R, S, (ph, pw), (sh, sw), (dh, dw), groups,
+                           int(rng.integers(0, 3)), int(rng.choice([-1, 2])), "exact", 0)
+        p = iga.get_plan2(d)
+        assert p.fold_width == 1
+        assert p.base.variant in per_axis_variants, (d.pad_h, d.pad_w, p.base.variant)
+        assert (p.base.Ho, p.base.Wo) == (Ho // sh + 1, Wo // sw + 1)
+        seen.add(p.base.variant)
+    assert {0, 1, 10} <= seen
+    # per-axis padding alone keeps the 16-bit row kernel (and BF16x3 for fp32)
+    p = iga.get_plan2(iga.make_desc2(4, 64, 20, 24, 64, 3, 5, (1, 2), 1, 1, 1, iga.BF16))
+    assert p.base.variant == 3 and (p.base.Ho, p.base.Wo) == (20, 24)
+    p = iga.get_plan2(iga.make_desc2(4, 64, 20, 24, 64, 3, 5, (1, 2), 1, 1, 1, iga.F32, -1, "bf16x3"))
+    assert p.base.variant == iga.VARIANT_DENSE_BF16X3
+
+
+def test_width_fold_plans():
+    """The width fold: automatic for a 16x16 stride-16 patch embedding with C = 3
+    (f = 16: 48 channels, one filter column), off on request, explicit f checked;
+    the folded plan keeps the tensor sizes and dW elements of the original."""
+    base = dict(N=2, C=3, H=224, W=224, K=768, R=16, S=16, pad=0, stride=16)
+    auto = iga.get_plan2(D2(**base))
+    off = iga.get_plan2(D2(fold_width=0, **base))
+    f4 = iga.get_plan2(D2(fold_width=4, **base))
+    assert auto.fold_width == 16 and off.fold_width == 1 and f4.fold_width == 4
+    for p in (auto, off, f4):
+        assert p.base.E == 768 * 16 * 16 * 3 and (p.base.Ho, p.base.Wo) == (14, 14)
+        assert p.base.x_bytes == 2 * 224 * 224 * 3 * 4 and p.base.dy_bytes == 2 * 14 * 14 * 768 * 4
+    assert off.base.variant == 0 and auto.base.variant == 1   # C = 3 takes the general kernel unfolded
+    # 2x2 stride 2, C = 6: f = 2 makes 12 channels
+    p = iga.get_plan2(D2(N=2, C=6, H=32, W=32, K=16, R=2, S=2, pad=0, stride=2))
+    assert p.fold_width == 2
+    # channels already in quads: no automatic fold
+    assert iga.get_plan2(D2(N=2, C=8, H=32, W=32, K=16, R=2, S=2, pad=0, stride=2)).fold_width == 1
+    # per-axis padding divisible by f: 5x4 filter, stride (1, 4), pad (2, 4), W = 36
+    p = iga.get_plan2(D2(N=1, C=3, H=10, W=36, K=8, R=5, S=4, pad=(2, 4), stride=(1, 4)))
+    assert p.fold_width == 4 and p.base.Wo == (36 + 8 - 4) // 4 + 1
+
+
+def test_bf16x3_plan_selection():
+    """math = BF16X3 takes the BF16x3 kernel where the 16-bit row kernel covers the
+    shape (fp32, stride 1, dilation 1, channels in eights) and the exact path
+    elsewhere; it never applies to 16-bit inputs."""
+    c2 = dict(N=32, C=64, H=56, W=56, K=64, R=3, S=3, pad=1)
+    p = iga.get_plan2(D2(math="bf16x3", **c2))
+    assert p.math == 1 and p.base.variant == iga.VARIANT_DENSE_BF16X3
+    assert iga.get_plan2(D2(**c2)).base.variant == 1 and iga.get_plan2(D2(**c2)).math == 0
+    for kw in (dict(stride=2), dict(dilation=2), dict(C=60), dict(groups=32, C=64, K=64)):
+        q = iga.get_plan2(D2(math="bf16x3", **dict(c2, **kw)))
+        assert q.math == 0 and q.base.variant != iga.VARIANT_DENSE_BF16X3, kw
+    q = iga.get_plan2(D2(math="bf16x3", dtype=iga.BF16, **c2))
+    assert q.math == 0 and q.base.variant == 3
