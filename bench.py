@@ -60,6 +60,7 @@ DEFAULT_CONFIG = "c2_3x3_f32"
 # planner it identifies the code a counter measurement was taken on.
 CSRC = os.path.join(ROOT, "implicit_gemm_amd", "csrc")
 VARIANT_SOURCE = {0: "dense_lds.hip", 1: "dense_rows.hip", 2: "dense_1x1.hip", 3: "dense16_rows.hip",
+                  4: "dense16_rows.hip",
                   10: "direct_elem.hip",
                   11: "grouped16.hip", 12: "depthwise_mfma.hip", 13: "grouped16.hip"}
 SHARED_SOURCES = ("device_common.h", "kernels.h", "plan.h", "plan.cpp")
@@ -188,30 +189,42 @@ def measure_peaks(hip):
     return {"read": reads, "mfma": mfma, "published": PEAK}
 
 
-def roofline_for(shape, dtype, seconds, traffic=None):
+def roofline_for(shape, dtype, seconds, traffic=None, math="exact"):
+    """Roofline of one call: algorithmic FLOPs against the MFMA peak of the dtype the
+    products run in, algorithmic bytes against HBM, whichever takes longer.  BF16x3
+    runs three bf16 products per fp32 product, so its MFMA work is 3x the FLOPs at
+    the bf16 peak."""
     import wgrad_data as wd
     flops = shape.flops()
     nbytes = shape.algorithmic_bytes(wd.IN_BYTES[dtype])
-    t_mfma = flops / (PEAK["mfma_tflops"][dtype] * 1e12)
+    mfma_dtype, mult = ("bf16", 3) if math == "bf16x3" else (dtype, 1)
+    peak_mfma = PEAK["mfma_tflops"][mfma_dtype]
+    t_mfma = mult * flops / (peak_mfma * 1e12)
     t_hbm = nbytes / (PEAK["hbm_gbs"] * 1e9)
     bound = "mfma" if t_mfma >= t_hbm else "hbm"
     if shape.groups > 1 and shape.Cg <= 8:
         bound = "hbm"  # direct small-group path: its metric is achieved HBM bandwidth
     if bound == "mfma":
-        achieved = flops / seconds / 1e12
-        return {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK["mfma_tflops"][dtype],
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK["mfma_tflops"][dtype], 4),
-                "traffic": traffic}
+        achieved = mult * flops / seconds / 1e12
+        out = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_mfma,
+               "unit": "TFLOP/s", "frac": round(achieved / peak_mfma, 4), "traffic": traffic}
+        if mult > 1:
+            out["note"] = "BF16x3: MFMA work is three bf16 products per fp32 product"
+        return out
     achieved = nbytes / seconds / 1e9
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm_gbs"], "unit": "GB/s",
             "frac": round(achieved / PEAK["hbm_gbs"], 4), "traffic": traffic}
 
 
-ALL_RECORDS = [("c1_1x1_tiny_f32", None), ("c2_3x3_f32", None), ("c3_dw7x7_bf16", None),
-               ("c4a_grp3x3_cpg4_f16", None), ("c4b_grp3x3_cpg8_f16", None), ("c5_1x1_big_f32", 64)]
-HEADLINE = ("c5_1x1_big_f32", 192)
-FAMILY = {0: "dense_lds", 1: "dense_rows", 2: "dense_1x1", 3: "dense16_rows", 10: "direct_elem",
-          11: "grouped16", 12: "depthwise_mfma", 13: "grouped16_rows"}
+# (workload, batch of an N-swept workload, extended-descriptor options)
+ALL_RECORDS = [("c1_1x1_tiny_f32", None, {}), ("c2_3x3_f32", None, {}), ("c3_dw7x7_bf16", None, {}),
+               ("c4a_grp3x3_cpg4_f16", None, {}), ("c4b_grp3x3_cpg8_f16", None, {}),
+               ("c5_1x1_big_f32", 64, {}),
+               ("c2_3x3_f32", None, {"math": "bf16x3"}),
+               ("g_patch16_f32", None, {}), ("g_patch16_f32", None, {"fold_width": 0})]
+HEADLINE = ("c5_1x1_big_f32", 192, {})
+FAMILY = {0: "dense_lds", 1: "dense_rows", 2: "dense_1x1", 3: "dense16_rows", 4: "dense16_rows_bf16x3",
+          10: "direct_elem", 11: "grouped16", 12: "depthwise_mfma", 13: "grouped16_rows"}
 
 
 def resolve(name, n):
@@ -326,16 +339,20 @@ def _pct(vals, q):
     return v[int(q * (len(v) - 1))]
 
 
-def measure(wl, s, x, dy, args, hip, cold_reps, bias=False):
-    """Time one workload on resident inputs; returns (record, hot wall seconds per step,
-    hot stage-1 mean seconds)."""
+def measure(wl, s, x, dy, args, hip, cold_reps, bias=False, opts=None):
+    """Time one workload on resident inputs (extended-descriptor options opts: math,
+    fold_width); returns (record, hot wall seconds per step, hot stage-1 mean seconds)."""
     import numpy as np
     import torch
     import implicit_gemm_amd as iga
     import wgrad_data as wd
+    opts = opts or {}
+    math = opts.get("math", "exact")
     dev = x.device
-    d = iga.desc_for(x, dy, s.R, s.S, s.pad, s.stride, s.dilation, s.groups, args.split_k)
-    plan = iga.get_plan(d)
+    d = iga.desc2_for(x, dy, s.R, s.S, s.pad, s.stride, s.dilation, s.groups, args.split_k, math,
+                      opts.get("fold_width", -1))
+    plan2 = iga.get_plan2(d)
+    plan = plan2.base
     dw = torch.empty((s.K, s.R, s.S, s.Cg), dtype=torch.float32, device=dev)
     db = torch.empty((s.K,), dtype=torch.float32, device=dev)
     ws_bytes = int(plan.ws_bytes)
@@ -343,14 +360,13 @@ def measure(wl, s, x, dy, args, hip, cold_reps, bias=False):
     sp = torch.cuda.current_stream(dev).cuda_stream
     wsp = ws.data_ptr() if ws_bytes else 0
 
+    dbp = db.data_ptr() if bias else 0
+
     def step(ev0=0, ev1=0):
-        if bias:
-            iga.conv_wgrad_bias_timed(d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(), db.data_ptr(), wsp,
-                                      ws_bytes, sp, ev0, ev1)
-        elif ev0 or ev1:
-            iga.conv_wgrad_timed(d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(), wsp, ws_bytes, sp, ev0, ev1)
+        if ev0 or ev1:
+            iga.conv_wgrad2_timed(d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(), dbp, wsp, ws_bytes, sp, ev0, ev1)
         else:
-            iga.conv_wgrad_ex(d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(), wsp, ws_bytes, sp)
+            iga.conv_wgrad2(d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(), dbp, wsp, ws_bytes, sp)
 
     for _ in range(args.warmup):
         step()
@@ -409,23 +425,27 @@ def measure(wl, s, x, dy, args, hip, cold_reps, bias=False):
 
     cold_med = statistics.median(whole) * 1e-3
     digest = source_digest(plan.variant)
-    traffic = None if bias else measured_traffic(wl.name, digest, s.N)
+    used_math = "bf16x3" if int(plan2.math) == 1 else "exact"
+    tag = wl.name + ("+bf16x3" if used_math == "bf16x3" else "") + \
+        ("+nofold" if opts.get("fold_width", -1) in (0, 1) and wl.name.startswith("g_patch") else "")
+    traffic = None if bias else measured_traffic(tag, digest, s.N)
     rec = {
         "workload": wl.name, "note": wl.note, "dtype": wl.dtype,
         "N": s.N, "C": s.C, "H": s.H, "W": s.W, "K": s.K, "R": s.R, "S": s.S, "pad": s.pad,
         "stride": s.stride, "dilation": s.dilation, "groups": s.groups,
         "kernel": FAMILY.get(int(plan.variant), str(plan.variant)), "variant": int(plan.variant),
         "ks_count": int(plan.ks_count), "split_k": args.split_k, "bias_gradient": bool(bias),
+        "math": used_math, "fold_width": int(plan2.fold_width), "record": tag,
         "flops": s.flops(), "algorithmic_bytes": s.algorithmic_bytes(wd.IN_BYTES[wl.dtype]),
         "cold_call_us": {"median": round(cold_med * 1e6, 2), "min": round(min(whole) * 1e3, 2),
                          "p90": round(_pct(whole, 0.9) * 1e3, 2), "calls": cold_reps},
         "tflops": round(s.flops() / cold_med / 1e12, 3),
-        "roofline": roofline_for(s, wl.dtype, cold_med, traffic),
+        "roofline": roofline_for(s, wl.dtype, cold_med, traffic, used_math),
         "stage1_cold_us": round(statistics.median(stage1) * 1e3, 2),
-        "stage1_cold_frac": roofline_for(s, wl.dtype, statistics.median(stage1) * 1e-3)["frac"],
+        "stage1_cold_frac": roofline_for(s, wl.dtype, statistics.median(stage1) * 1e-3, None, used_math)["frac"],
         "hot_call_us": round(wall * 1e6, 2),
         "hot_stage1_us": round(statistics.mean(k_ms) * 1e3, 2),
-        "hot_stage1_frac": roofline_for(s, wl.dtype, statistics.mean(k_ms) * 1e-3)["frac"],
+        "hot_stage1_frac": roofline_for(s, wl.dtype, statistics.mean(k_ms) * 1e-3, None, used_math)["frac"],
         "source_digest": digest,
         "check": {"zeros": int((dw_h == 0).sum()), "finite": bool(np.isfinite(dw_h).all())},
     }
@@ -448,6 +468,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="oracle seconds for the headline cpu_baseline (3 s per other record)")
+    ap.add_argument("--math", default="exact", choices=["exact", "bf16x3"],
+                    help="with --config: arithmetic for fp32 inputs (bf16x3 where a kernel covers the shape)")
+    ap.add_argument("--fold-width", type=int, default=-1, help="with --config: width fold (-1 auto, 0 off)")
     ap.add_argument("--bias", action="store_true",
                     help="time conv_wgrad_bias (dW and the fused bias gradient db = sum dY)")
     ap.add_argument("--peaks", action="store_true",
@@ -466,7 +489,7 @@ def main():
     import implicit_gemm_amd as iga
 
     if args.digest:
-        wl, s = resolve(args.config, args.n) if args.config else resolve(*HEADLINE)
+        wl, s = resolve(args.config, args.n) if args.config else resolve(*HEADLINE[:2])
         d = iga.make_desc(s.N, s.C, s.H, s.W, s.K, s.R, s.S, s.pad, s.stride, s.dilation, s.groups,
                           {"f32": 0, "bf16": 1, "f16": 2}[wl.dtype], args.split_k)
         v = int(iga.get_plan(d).variant)
@@ -496,25 +519,30 @@ def main():
     if args.config:
         plan_runs = []
         head_name, head_n = args.config, args.n
+        head_opts = {}
+        if args.math != "exact":
+            head_opts["math"] = args.math
+        if args.fold_width != -1:
+            head_opts["fold_width"] = args.fold_width
     else:
         plan_runs = ALL_RECORDS
-        head_name, head_n = HEADLINE
+        head_name, head_n, head_opts = HEADLINE
 
     def cold_reps_for(s):
         return 5 if s.flops() > 1e11 else args.cold
 
     big = None   # device inputs of the N-swept workload at the headline batch, shared by its records
     hwl, hs = resolve(head_name, head_n)
-    for name, n in plan_runs:
+    for name, n, opts in plan_runs:
         wl, s = resolve(name, n)
-        log("record", wl.name, s, wl.dtype)
+        log("record", wl.name, s, wl.dtype, opts)
         if wl.n_sweep and hwl.name == wl.name and s.N <= hs.N:
             if big is None:
                 big = device_inputs(hwl, hs, dev)
             x, dy = big[0][:s.N], big[1][:s.N]
         else:
             x, dy = device_inputs(wl, s, dev)
-        rec, _, _ = measure(wl, s, x, dy, args, hip, cold_reps_for(s), args.bias)
+        rec, _, _ = measure(wl, s, x, dy, args, hip, cold_reps_for(s), args.bias, opts)
         if not args.no_cpu:
             rec["cpu_baseline"] = cpu_baseline(wl, s, 3.0)
         records.append(rec)
@@ -525,13 +553,13 @@ def main():
     log("headline", hwl.name, hs, hwl.dtype)
     if big is None:
         big = device_inputs(hwl, hs, dev)
-    rec, wall, stage1_s = measure(hwl, hs, big[0], big[1], args, hip, cold_reps_for(hs), args.bias)
+    rec, wall, stage1_s = measure(hwl, hs, big[0], big[1], args, hip, cold_reps_for(hs), args.bias, head_opts)
     cpu = None if args.no_cpu else cpu_baseline(hwl, hs, args.cpu_seconds)
     if cpu:
         rec["cpu_baseline"] = cpu
     records.append(rec)
     log(json.dumps(rec))
-    roof = roofline_for(hs, hwl.dtype, stage1_s, rec["roofline"]["traffic"])
+    roof = roofline_for(hs, hwl.dtype, stage1_s, rec["roofline"]["traffic"], rec["math"])
     out = {
         "metric": "wgrad TFLOP/s and % of MFMA-or-HBM roofline per conv shape, 1xMI355X",
         "value": round(hs.flops() / wall / 1e12, 3),
@@ -549,9 +577,10 @@ def main():
                    "K": hs.K, "R": hs.R, "S": hs.S, "pad": hs.pad, "stride": hs.stride,
                    "dilation": hs.dilation, "groups": hs.groups, "split_k": args.split_k,
                    "ks_count": rec["ks_count"], "kernel": rec["kernel"], "bias_gradient": bool(args.bias),
+                   "math": rec["math"], "fold_width": rec["fold_width"],
                    "parallelism": "single GPU"},
         "roofline": roof,
-        "whole_call_roofline_frac": roofline_for(hs, hwl.dtype, wall)["frac"],
+        "whole_call_roofline_frac": roofline_for(hs, hwl.dtype, wall, None, rec["math"])["frac"],
         "stage1_ms_mean": round(stage1_s * 1e3, 5),
         "cpu_baseline": cpu,
         "check": rec["check"],

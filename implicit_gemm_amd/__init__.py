@@ -125,6 +125,10 @@ def load():
     lib.conv_wgrad2.restype = ctypes.c_int
     lib.conv_wgrad2.argtypes = [P(Desc2), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                 ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.conv_wgrad2_timed.restype = ctypes.c_int
+    lib.conv_wgrad2_timed.argtypes = [P(Desc2), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p]
     lib.conv_wgrad_noalloc.restype = ctypes.c_int
     lib.conv_wgrad_noalloc.argtypes = [P(Desc), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p]
@@ -168,6 +172,15 @@ def conv_wgrad2(desc: Desc2, x_ptr: int, dy_ptr: int, dw_ptr: int, db_ptr: int, 
                             ws_bytes, stream or None)
     if st != 0:
         raise ConvWgradError(st, "conv_wgrad2")
+
+
+def conv_wgrad2_timed(desc: Desc2, x_ptr: int, dy_ptr: int, dw_ptr: int, db_ptr: int, ws_ptr: int,
+                      ws_bytes: int, stream: int, ev_begin: int, ev_end: int) -> None:
+    """conv_wgrad2 whose stage-1 dispatch stamps its start and end into two HIP events."""
+    st = load().conv_wgrad2_timed(ctypes.byref(desc), x_ptr, dy_ptr, dw_ptr, db_ptr or None, ws_ptr or None,
+                                  ws_bytes, stream or None, ev_begin or None, ev_end or None)
+    if st != 0:
+        raise ConvWgradError(st, "conv_wgrad2_timed")
 
 
 def get_plan(desc: Desc) -> Plan:

@@ -241,4 +241,11 @@ conv_wgrad_status_t conv_wgrad2(const conv_wgrad_desc2_t* desc, const void* x, c
   return run(desc, x, dy, dw, db != nullptr, db, workspace, true, ws_bytes, stream);
 }
 
+conv_wgrad_status_t conv_wgrad2_timed(const conv_wgrad_desc2_t* desc, const void* x, const void* dy,
+                                      float* dw, float* db, void* workspace, size_t ws_bytes,
+                                      void* stream, void* stage1_begin, void* stage1_end) {
+  return run(desc, x, dy, dw, db != nullptr, db, workspace, true, ws_bytes, stream, stage1_begin,
+             stage1_end);
+}
+
 }  // extern "C"

@@ -496,7 +496,12 @@ conv_wgrad_status_t make_plan(const conv_wgrad_desc2_t* desc, Plan* out) {
     if (out->ru > 1) return choose_split(units, tiles, desc->split_k, 2, 768, 1, p, &pub, 0, 8);
     return choose_split(units, tiles, desc->split_k, 2, 512, 1, p, &pub, 0, 4);
   }
-  if (plan_dense_rows(p, out)) {
+  // A width fold exists to give the general kernel 4-wide input-channel loads
+  // (three input channels become 48 for a 16x16 patch); the row kernel would
+  // take the folded problem's few-pixel output rows one unit each (a 16x16
+  // stride-16 patch embedding of 224x224 images ran at 644 us folded on the
+  // row kernel against 329 us unfolded on the general kernel).
+  if (p.fold == 1 && plan_dense_rows(p, out)) {
     pub.variant = kDenseRows;
     pub.unit_rows = out->wt;
     int64_t units, tiles;

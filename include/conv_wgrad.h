@@ -303,6 +303,11 @@ conv_wgrad_status_t conv_wgrad2_get_plan(const conv_wgrad_desc2_t* desc, conv_wg
 conv_wgrad_status_t conv_wgrad2(const conv_wgrad_desc2_t* desc, const void* x, const void* dy,
                                 float* dw, float* db, void* workspace, size_t ws_bytes, void* stream);
 
+/* Profiling variant of conv_wgrad2, with stage-1 events as in conv_wgrad_timed. */
+conv_wgrad_status_t conv_wgrad2_timed(const conv_wgrad_desc2_t* desc, const void* x, const void* dy,
+                                      float* dw, float* db, void* workspace, size_t ws_bytes,
+                                      void* stream, void* stage1_begin, void* stage1_end);
+
 /*
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): conv_wgrad_bias

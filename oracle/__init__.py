@@ -58,6 +58,10 @@ def load(path: str | None = None):
         lib.oracle_wgrad_accumulate.argtypes = [i64] * 11 + [ctypes.c_void_p] * 4 + [ctypes.c_int]
         lib.oracle_wgrad2_accumulate.restype = ctypes.c_int
         lib.oracle_wgrad2_accumulate.argtypes = [i64] * 14 + [ctypes.c_void_p] * 4 + [ctypes.c_int]
+        lib.oracle_fwd.restype = ctypes.c_int
+        lib.oracle_fwd.argtypes = [i64] * 14 + [ctypes.c_void_p] * 4 + [ctypes.c_int]
+        lib.oracle_dgrad.restype = ctypes.c_int
+        lib.oracle_dgrad.argtypes = [i64] * 14 + [ctypes.c_void_p] * 4 + [ctypes.c_int]
         lib.oracle_bgrad_accumulate.restype = ctypes.c_int
         lib.oracle_bgrad_accumulate.argtypes = [i64] * 4 + [ctypes.c_void_p] * 3
         lib.oracle_max_threads.restype = ctypes.c_int
@@ -166,6 +170,54 @@ def bgrad_ref(dy, lib=None):
     if rc != 0:
         raise RuntimeError("oracle_bgrad_accumulate failed: %d" % rc)
     return db, float(ab.max()) if ab.size else 0.0
+
+
+def fwd_ref(x, w, pad=0, stride=1, dilation=1, groups=1, nthreads=None, lib=None):
+    """Forward convolution Y (fp64, [N, Ho, Wo, K]) of NHWC x [N,H,W,C] and the
+    filter w [K,R,S,C/groups], and its error denominator max over Y of sum |X||W|.
+    pad, stride and dilation: one int or an (h, w) pair."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, H, W, C = x.shape
+    K, R, S, Cg = w.shape
+    (ph, pw), (sh, sw), (dh, dw) = pair(pad), pair(stride), pair(dilation)
+    if Cg * groups != C:
+        raise ValueError("filter has %d channels per group, expected %d" % (Cg, C // groups))
+    lib = lib or load()
+    Ho, Wo = out_size(H, R, ph, sh, dh, lib), out_size(W, S, pw, sw, dw, lib)
+    if Ho < 1 or Wo < 1:
+        raise ValueError("empty output")
+    y = np.empty((N, Ho, Wo, K), np.float64)
+    a = np.empty((N, Ho, Wo, K), np.float64)
+    rc = lib.oracle_fwd(N, C, H, W, K, R, S, ph, pw, sh, sw, dh, dw, groups, x.ctypes.data, w.ctypes.data,
+                        y.ctypes.data, a.ctypes.data, nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError("oracle_fwd failed: %d" % rc)
+    return y, float(a.max())
+
+
+def dgrad_ref(dy, w, H, W, pad=0, stride=1, dilation=1, groups=1, nthreads=None, lib=None):
+    """Data gradient dX (fp64, [N, H, W, C]) of NHWC dy [N,Ho,Wo,K] and the filter
+    w [K,R,S,C/groups] for H x W images, and its error denominator max over dX of
+    sum |dY||W|.  pad, stride and dilation: one int or an (h, w) pair."""
+    dy = np.ascontiguousarray(dy, dtype=np.float32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, Ho, Wo, K = dy.shape
+    Kw, R, S, Cg = w.shape
+    if Kw != K:
+        raise ValueError("filter has %d output channels, dy has %d" % (Kw, K))
+    (ph, pw), (sh, sw), (dh, dw) = pair(pad), pair(stride), pair(dilation)
+    lib = lib or load()
+    if (out_size(H, R, ph, sh, dh, lib), out_size(W, S, pw, sw, dw, lib)) != (Ho, Wo):
+        raise ValueError("dy extents do not match the geometry")
+    C = Cg * groups
+    dx = np.empty((N, H, W, C), np.float64)
+    a = np.empty((N, H, W, C), np.float64)
+    rc = lib.oracle_dgrad(N, C, H, W, K, R, S, ph, pw, sh, sw, dh, dw, groups, dy.ctypes.data, w.ctypes.data,
+                          dx.ctypes.data, a.ctypes.data, nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError("oracle_dgrad failed: %d" % rc)
+    return dx, float(a.max())
 
 
 def normalised_error(dw_test, dw_ref, den) -> float:

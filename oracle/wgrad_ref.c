@@ -166,6 +166,131 @@ int oracle_bgrad_accumulate(int64_t nc, int64_t Ho, int64_t Wo, int64_t K, const
   return 0;
 }
 
+/*
+ * Forward convolution (the other direction on the same implicit-GEMM and
+ * split-K machinery, rocm-libraries PR #14393 "split-K forward implicit-GEMM
+ * convolution on gfx1250", section Summary), per-axis geometry:
+ *
+ *   Y[n, ho, wo, k] = sum over r, s, c of
+ *       Xpad[n, ho*stride_h + r*dil_h - pad_h, wo*stride_w + s*dil_w - pad_w, g(k)*Cg + c]
+ *       * Wt[k, r, s, c]
+ *
+ * x is [N][H][W][C], w is [K][R][S][Cg] (fp32 values), y and absacc are
+ * [N][Ho][Wo][K] fp64 (overwritten); absacc holds the same sum of |Xpad|*|Wt|,
+ * whose largest element is the normalised-error denominator.  Output rows
+ * (n, ho) are split over threads; every output element is one thread's own
+ * fp64 sum in (r, s, c) order.  Returns 0, or -1 on invalid arguments.
+ */
+int oracle_fwd(int64_t N, int64_t C, int64_t H, int64_t W, int64_t K, int64_t R, int64_t S,
+               int64_t pad_h, int64_t pad_w, int64_t stride_h, int64_t stride_w, int64_t dil_h,
+               int64_t dil_w, int64_t groups, const float* x, const float* w, double* y,
+               double* absacc, int nthreads) {
+  if (N < 1 || C < 1 || H < 1 || W < 1 || K < 1 || R < 1 || S < 1 || pad_h < 0 || pad_w < 0 ||
+      stride_h < 1 || stride_w < 1 || dil_h < 1 || dil_w < 1 || groups < 1 || C % groups != 0 ||
+      K % groups != 0)
+    return -1;
+  const int64_t Ho = oracle_out_size(H, R, pad_h, stride_h, dil_h);
+  const int64_t Wo = oracle_out_size(W, S, pad_w, stride_w, dil_w);
+  if (Ho < 1 || Wo < 1) return -1;
+  const int64_t Cg = C / groups, Kg = K / groups;
+  if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+  for (int64_t row = 0; row < N * Ho; ++row) {
+    const int64_t n = row / Ho, ho = row % Ho;
+    for (int64_t wo = 0; wo < Wo; ++wo) {
+      for (int64_t k = 0; k < K; ++k) {
+        const int64_t grp = k / Kg;
+        double acc = 0.0, aacc = 0.0;
+        for (int64_t r = 0; r < R; ++r) {
+          const int64_t h = ho * stride_h + r * dil_h - pad_h;
+          if (h < 0 || h >= H) continue; /* zero padding */
+          for (int64_t s = 0; s < S; ++s) {
+            const int64_t ww = wo * stride_w + s * dil_w - pad_w;
+            if (ww < 0 || ww >= W) continue; /* zero padding */
+            const float* xp = x + ((n * H + h) * W + ww) * C + grp * Cg;
+            const float* wp = w + ((k * R + r) * S + s) * Cg;
+            for (int64_t c = 0; c < Cg; ++c) {
+              acc += (double)xp[c] * (double)wp[c];
+              aacc += fabs((double)xp[c]) * fabs((double)wp[c]);
+            }
+          }
+        }
+        y[((n * Ho + ho) * Wo + wo) * K + k] = acc;
+        absacc[((n * Ho + ho) * Wo + wo) * K + k] = aacc;
+      }
+    }
+  }
+  return 0;
+}
+
+/*
+ * Data gradient (dgrad, the input gradient of the same convolution; the
+ * pages' third direction beside wgrad and forward, rocm-libraries PR #14393,
+ * section "Auto-deduced degree": "as it does for wgrad and dgrad"), written as
+ * the scatter that transposes the forward sum: every term of
+ *   Y[n, ho, wo, k] += Xpad[n, h, w, g(k)*Cg + c] * Wt[k, r, s, c]
+ * (h = ho*stride_h + r*dil_h - pad_h, w = wo*stride_w + s*dil_w - pad_w, inside
+ * the image) sends dY[n, ho, wo, k] * Wt[k, r, s, c] to dX[n, h, w, g(k)*Cg + c]:
+ *
+ *   dX[n, h, w, g*Cg + c] = sum over (k in group g, r, s, ho, wo) with
+ *       ho*stride_h + r*dil_h - pad_h == h and wo*stride_w + s*dil_w - pad_w == w
+ *       of dY[n, ho, wo, k] * Wt[k, r, s, c].
+ *
+ * dy is [N][Ho][Wo][K], w is [K][R][S][Cg] (fp32 values); dx and absacc are
+ * [N][H][W][C] fp64 (overwritten; absacc is the sum of |dY|*|Wt|).  Images are
+ * split over threads (each image's dX is written by one thread), and within an
+ * image the terms are added in (ho, wo, k, r, s, c) order.  Returns 0, or -1
+ * on invalid arguments.
+ */
+int oracle_dgrad(int64_t N, int64_t C, int64_t H, int64_t W, int64_t K, int64_t R, int64_t S,
+                 int64_t pad_h, int64_t pad_w, int64_t stride_h, int64_t stride_w, int64_t dil_h,
+                 int64_t dil_w, int64_t groups, const float* dy, const float* w, double* dx,
+                 double* absacc, int nthreads) {
+  if (N < 1 || C < 1 || H < 1 || W < 1 || K < 1 || R < 1 || S < 1 || pad_h < 0 || pad_w < 0 ||
+      stride_h < 1 || stride_w < 1 || dil_h < 1 || dil_w < 1 || groups < 1 || C % groups != 0 ||
+      K % groups != 0)
+    return -1;
+  const int64_t Ho = oracle_out_size(H, R, pad_h, stride_h, dil_h);
+  const int64_t Wo = oracle_out_size(W, S, pad_w, stride_w, dil_w);
+  if (Ho < 1 || Wo < 1) return -1;
+  const int64_t Cg = C / groups, Kg = K / groups;
+  if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    double* dxn = dx + n * H * W * C;
+    double* an = absacc + n * H * W * C;
+    for (int64_t i = 0; i < H * W * C; ++i) {
+      dxn[i] = 0.0;
+      an[i] = 0.0;
+    }
+    for (int64_t ho = 0; ho < Ho; ++ho) {
+      for (int64_t wo = 0; wo < Wo; ++wo) {
+        const float* g = dy + ((n * Ho + ho) * Wo + wo) * K;
+        for (int64_t k = 0; k < K; ++k) {
+          const double gv = (double)g[k];
+          const int64_t grp = k / Kg;
+          for (int64_t r = 0; r < R; ++r) {
+            const int64_t hi = ho * stride_h + r * dil_h - pad_h;
+            if (hi < 0 || hi >= H) continue; /* the term multiplies a padding zero */
+            for (int64_t s = 0; s < S; ++s) {
+              const int64_t wi = wo * stride_w + s * dil_w - pad_w;
+              if (wi < 0 || wi >= W) continue;
+              const float* wq = w + ((k * R + r) * S + s) * Cg;
+              double* d = dxn + (hi * W + wi) * C + grp * Cg;
+              double* a = an + (hi * W + wi) * C + grp * Cg;
+              for (int64_t c = 0; c < Cg; ++c) {
+                d[c] += gv * (double)wq[c];
+                a[c] += fabs(gv) * fabs((double)wq[c]);
+              }
+            }
+          }
+        }
+      }
+    }
+  }
+  return 0;
+}
+
 /* Number of threads the OpenMP runtime would give a parallel region. */
 int oracle_max_threads(void) {
 #ifdef _OPENMP

@@ -406,7 +406,164 @@ def pin_axis_swap(lib, seed=24):
         assert np.array_equal(b, a.transpose(0, 2, 1, 3)), (N, C, H, W, K, R, S)
 
 
+def _fwd(lib, x, w, pad, stride, dil, groups):
+    return oracle.fwd_ref(x, w, pad, stride, dil, groups, nthreads=3, lib=lib)
+
+
+def _dgrad(lib, dy, w, H, W, pad, stride, dil, groups):
+    return oracle.dgrad_ref(dy, w, H, W, pad, stride, dil, groups, nthreads=3, lib=lib)
+
+
+def _mixed_shapes(rng, count):
+    """Tiny shapes with equal or per-axis geometry (forward / data-gradient pins)."""
+    out = []
+    for sh in tiny_shapes(rng, count // 2):
+        N, C, H, W, K, R, S, pad, stride, dil, groups = sh
+        out.append((N, C, H, W, K, R, S, (pad, pad), (stride, stride), (dil, dil), groups))
+    return out + _per_axis_shapes(rng, count - len(out))
+
+
+def pin_fwd_hand(lib):
+    """Forward on the hand-worked cases: 2x2 filter [[1, 0], [0, 2]] over X = 1..9 (3x3),
+    no padding: Y[ho, wo] = X[ho, wo] + 2 X[ho+1, wo+1] = [[11, 14], [20, 23]];
+    and with pad (1, 0), stride (1, 2) on X = [[1, 2, 3, 4], [5, 6, 7, 8]] and a
+    2x1 filter [3, -1]: Y[ho, wo] = 3 Xpad[ho-1, 2wo] - Xpad[ho, 2wo]
+    = [[-1, -3], [3 - 5, 9 - 7], [15, 21]] = [[-1, -3], [-2, 2], [15, 21]]."""
+    x = np.arange(1, 10, dtype=np.float32).reshape(1, 3, 3, 1)
+    w = np.array([1, 0, 0, 2], np.float32).reshape(1, 2, 2, 1)
+    y, _ = _fwd(lib, x, w, 0, 1, 1, 1)
+    assert np.array_equal(y[0, :, :, 0], [[11, 14], [20, 23]]), y[0, :, :, 0]
+    x = np.arange(1, 9, dtype=np.float32).reshape(1, 2, 4, 1)
+    w = np.array([3, -1], np.float32).reshape(1, 2, 1, 1)
+    y, _ = _fwd(lib, x, w, (1, 0), (1, 2), 1, 1)
+    assert np.array_equal(y[0, :, :, 0], [[-1, -3], [-2, 2], [15, 21]]), y[0, :, :, 0]
+
+
+def pin_fwd_library_routines(lib, count=40, seed=30):
+    """Forward against torch's fp64 conv2d and the numpy strided-slice forward."""
+    import torch
+    rng = np.random.default_rng(seed)
+    for shape in _mixed_shapes(rng, count):
+        N, C, H, W, K, R, S, pad, stride, dil, groups = shape
+        x = rng.standard_normal((N, H, W, C)).astype(np.float32)
+        w = rng.standard_normal((K, R, S, C // groups)).astype(np.float32)
+        got, den = _fwd(lib, x, w, pad, stride, dil, groups)
+        want = torch.nn.functional.conv2d(torch.from_numpy(x.astype(np.float64)).permute(0, 3, 1, 2),
+                                          torch.from_numpy(w.astype(np.float64)).permute(0, 3, 1, 2),
+                                          None, stride, pad, dil, groups).permute(0, 2, 3, 1).numpy()
+        assert got.shape == want.shape, (shape, got.shape, want.shape)
+        assert np.max(np.abs(got - want)) <= 1e-12 * max(den, 1e-30), shape
+        want2 = forward_conv_numpy(x, w, pad, stride, dil, groups)
+        assert np.max(np.abs(got - want2)) <= 1e-12 * max(den, 1e-30), shape
+
+
+def pin_fwd_closed_form_1x1(lib, seed=31):
+    """1x1 stride 1 forward per group: Y = X W^T on the [N*H*W, .] matrices."""
+    rng = np.random.default_rng(seed)
+    for (N, C, H, W, K, groups) in [(2, 6, 5, 7, 4, 1), (1, 8, 3, 4, 6, 2)]:
+        x = rng.uniform(-1, 1, (N, H, W, C)).astype(np.float32)
+        w = rng.uniform(-1, 1, (K, 1, 1, C // groups)).astype(np.float32)
+        got, den = _fwd(lib, x, w, 0, 1, 1, groups)
+        Cg, Kg = C // groups, K // groups
+        for g in range(groups):
+            xs = x[..., g * Cg:(g + 1) * Cg].reshape(-1, Cg).astype(np.float64)
+            ws = w[g * Kg:(g + 1) * Kg, 0, 0, :].astype(np.float64)
+            want = (xs @ ws.T).reshape(N, H, W, Kg)
+            assert np.max(np.abs(got[..., g * Kg:(g + 1) * Kg] - want)) <= 1e-13 * den, g
+
+
+def pin_dgrad_library_routines(lib, count=40, seed=32):
+    """Data gradient against torch's fp64 conv2d autograd (the input gradient)."""
+    import torch
+    rng = np.random.default_rng(seed)
+    for shape in _mixed_shapes(rng, count):
+        N, C, H, W, K, R, S, pad, stride, dil, groups = shape
+        Ho, Wo = _extent(H, R, pad[0], stride[0], dil[0]), _extent(W, S, pad[1], stride[1], dil[1])
+        dy = rng.standard_normal((N, Ho, Wo, K)).astype(np.float32)
+        w = rng.standard_normal((K, R, S, C // groups)).astype(np.float32)
+        xt = torch.zeros((N, C, H, W), dtype=torch.float64, requires_grad=True)
+        y = torch.nn.functional.conv2d(xt, torch.from_numpy(w.astype(np.float64)).permute(0, 3, 1, 2),
+                                       None, stride, pad, dil, groups)
+        y.backward(torch.from_numpy(dy.astype(np.float64)).permute(0, 3, 1, 2))
+        want = xt.grad.permute(0, 2, 3, 1).numpy()
+        got, den = _dgrad(lib, dy, w, H, W, pad, stride, dil, groups)
+        assert got.shape == want.shape, shape
+        assert np.max(np.abs(got - want)) <= 1e-12 * max(den, 1e-30), shape
+
+
+def pin_dgrad_finite_differences(lib, count=16, seed=33):
+    """Every dX element against central differences (step 1, exact for the linear
+    loss <dY, conv(X, W)>) of the independent numpy forward."""
+    rng = np.random.default_rng(seed)
+    for shape in _mixed_shapes(rng, count):
+        N, C, H, W, K, R, S, pad, stride, dil, groups = shape
+        Ho, Wo = _extent(H, R, pad[0], stride[0], dil[0]), _extent(W, S, pad[1], stride[1], dil[1])
+        dy = rng.uniform(-1, 1, (N, Ho, Wo, K)).astype(np.float32)
+        w = rng.uniform(-1, 1, (K, R, S, C // groups)).astype(np.float32)
+        x0 = rng.standard_normal((N, H, W, C))
+        want = np.zeros((N, H, W, C))
+        dyd = dy.astype(np.float64)
+        for idx in np.ndindex(N, H, W, C):
+            xp, xm = x0.copy(), x0.copy()
+            xp[idx] += 1.0
+            xm[idx] -= 1.0
+            want[idx] = (np.sum(forward_conv_numpy(xp, w, pad, stride, dil, groups) * dyd)
+                         - np.sum(forward_conv_numpy(xm, w, pad, stride, dil, groups) * dyd)) / 2.0
+        got, den = _dgrad(lib, dy, w, H, W, pad, stride, dil, groups)
+        assert np.max(np.abs(got - want)) <= 1e-11 * max(den, 1e-30), shape
+
+
+def pin_adjoint_identity(lib, seed=34):
+    """<dY, fwd(X, W)> = <dgrad(dY, W), X> = <wgrad(X, dY), W>, exactly on integer
+    inputs (every sum is exact in fp64): the three oracles are one bilinear form."""
+    rng = np.random.default_rng(seed)
+    for (N, C, H, W, K, R, S, pad, stride, dil, groups) in [
+            (2, 4, 7, 6, 6, 3, 2, (1, 0), (2, 1), (1, 2), 2), (1, 3, 9, 8, 2, 3, 3, 1, 1, 1, 1),
+            (2, 8, 6, 9, 8, 2, 4, (0, 2), (1, 3), (2, 1), 8)]:
+        (ph, pw), (sh, sw), (dh, dw) = P_pair(pad), P_pair(stride), P_pair(dil)
+        Ho, Wo = _extent(H, R, ph, sh, dh), _extent(W, S, pw, sw, dw)
+        x = rng.integers(-5, 6, (N, H, W, C)).astype(np.float32)
+        dy = rng.integers(-5, 6, (N, Ho, Wo, K)).astype(np.float32)
+        w = rng.integers(-5, 6, (K, R, S, C // groups)).astype(np.float32)
+        y, _ = _fwd(lib, x, w, pad, stride, dil, groups)
+        dx, _ = _dgrad(lib, dy, w, H, W, pad, stride, dil, groups)
+        dw_, _ = _ref(lib, x, dy, R, S, pad, stride, dil, groups)
+        a = float(np.sum(y * dy.astype(np.float64)))
+        b = float(np.sum(dx * x.astype(np.float64)))
+        c = float(np.sum(dw_ * w.astype(np.float64)))
+        assert a == b == c, (a, b, c)
+
+
+def pin_fwd_dgrad_denominators(lib, seed=35):
+    """With non-negative inputs the |.| sums equal the results; with mixed signs
+    they bound them."""
+    rng = np.random.default_rng(seed)
+    N, C, H, W, K, R, S, pad, stride, dil, groups = 2, 4, 6, 7, 6, 3, 2, (1, 0), (1, 2), 1, 2
+    Ho, Wo = _extent(H, R, 1, 1, 1), _extent(W, S, 0, 2, 1)
+    x = rng.integers(0, 4, (N, H, W, C)).astype(np.float32)
+    w = rng.integers(0, 4, (K, R, S, C // groups)).astype(np.float32)
+    dy = rng.integers(0, 4, (N, Ho, Wo, K)).astype(np.float32)
+    y, den = _fwd(lib, x, w, pad, stride, dil, groups)
+    assert den == y.max()
+    dx, den = _dgrad(lib, dy, w, H, W, pad, stride, dil, groups)
+    assert den == dx.max()
+    # mixed signs: the denominators are the results of |X|, |W| (and |dY|), which bound |Y| and |dX|
+    xm, wm, dym = x - 2, w - 2, dy - 2
+    y, den = _fwd(lib, xm, wm, pad, stride, dil, groups)
+    ya, _ = _fwd(lib, np.abs(xm), np.abs(wm), pad, stride, dil, groups)
+    assert den == ya.max() and np.abs(y).max() <= den, (den, ya.max())
+    dx, den = _dgrad(lib, dym, wm, H, W, pad, stride, dil, groups)
+    dxa, _ = _dgrad(lib, np.abs(dym), np.abs(wm), H, W, pad, stride, dil, groups)
+    assert den == dxa.max() and np.abs(dx).max() <= den, (den, dxa.max())
+
+
+def P_pair(v):
+    return _pair(v)
+
+
 ALL_PINS = [pin_hand_examples, pin_finite_differences, pin_torch_autograd, pin_closed_form_1x1,
             pin_bias_gradient, pin_box_sum, pin_depthwise_correlate, pin_grouped_is_dense_per_group,
             pin_bilinear, pin_split_invariance, pin_denominator, pin_bgrad,
-            pin_per_axis_finite_differences, pin_per_axis_torch, pin_axis_swap]
+            pin_per_axis_finite_differences, pin_per_axis_torch, pin_axis_swap,
+            pin_fwd_hand, pin_fwd_library_routines, pin_fwd_closed_form_1x1, pin_dgrad_library_routines,
+            pin_dgrad_finite_differences, pin_adjoint_identity, pin_fwd_dgrad_denominators]

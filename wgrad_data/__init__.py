@@ -206,6 +206,8 @@ GEOMETRY = {w.name: w for w in [
          "grouped 3x3 fp16, 4 ch/group, N=32 C=K=256 56x56 pad 1"),
     _geo("g_grp3x3_s2_f16", ConvShape(64, 256, 56, 56, 256, 3, 3, pad=1, stride=2, groups=64), "f16", 111,
          "grouped 3x3 stride 2 fp16, 4 ch/group, N=64 C=K=256 56x56 pad 1"),
+    _geo("g_patch16_f32", ConvShape(64, 3, 224, 224, 768, 16, 16, stride=16), "f32", 112,
+         "patch embedding 16x16 stride 16 fp32, N=64 C=3 K=768 224x224"),
 ]}
 
 
