@@ -61,6 +61,8 @@ class Plan2(ctypes.Structure):
 
 
 MATH = {"exact": 0, "bf16x3": 1}
+DIRECTION_WGRAD, DIRECTION_FWD, DIRECTION_DGRAD = 0, 1, 2
+VARIANT_FWD, VARIANT_DGRAD = 20, 21
 VARIANT_DENSE_BF16X3 = 4
 
 
@@ -129,6 +131,15 @@ def load():
     lib.conv_wgrad2_timed.argtypes = [P(Desc2), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_void_p]
+    lib.conv_igemm_get_plan.restype = ctypes.c_int
+    lib.conv_igemm_get_plan.argtypes = [P(Desc2), ctypes.c_int32, P(Plan2)]
+    lib.conv_igemm_workspace_size.restype = ctypes.c_int
+    lib.conv_igemm_workspace_size.argtypes = [P(Desc2), ctypes.c_int32, P(ctypes.c_size_t)]
+    for name in ("conv_fwd", "conv_dgrad"):
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [P(Desc2), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                      ctypes.c_size_t, ctypes.c_void_p]
     lib.conv_wgrad_noalloc.restype = ctypes.c_int
     lib.conv_wgrad_noalloc.argtypes = [P(Desc), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p]
@@ -248,6 +259,83 @@ def conv_wgrad_noalloc(desc: Desc, x_ptr: int, dy_ptr: int, dw_ptr: int, db_ptr:
     st = load().conv_wgrad_noalloc(ctypes.byref(desc), x_ptr, dy_ptr, dw_ptr, db_ptr or None, stream or None)
     if st != 0:
         raise ConvWgradError(st, "conv_wgrad_noalloc")
+
+
+def get_igemm_plan(desc: Desc2, direction: int) -> Plan2:
+    """Plan of the forward (DIRECTION_FWD) or data-gradient (DIRECTION_DGRAD) implicit GEMM."""
+    p = Plan2()
+    st = load().conv_igemm_get_plan(ctypes.byref(desc), direction, ctypes.byref(p))
+    if st != 0:
+        raise ConvWgradError(st, "conv_igemm_get_plan")
+    return p
+
+
+def conv_fwd(desc: Desc2, x_ptr: int, w_ptr: int, y_ptr: int, ws_ptr: int, ws_bytes: int, stream: int) -> None:
+    st = load().conv_fwd(ctypes.byref(desc), x_ptr, w_ptr, y_ptr, ws_ptr or None, ws_bytes, stream or None)
+    if st != 0:
+        raise ConvWgradError(st, "conv_fwd")
+
+
+def conv_dgrad(desc: Desc2, dy_ptr: int, w_ptr: int, dx_ptr: int, ws_ptr: int, ws_bytes: int,
+               stream: int) -> None:
+    st = load().conv_dgrad(ctypes.byref(desc), dy_ptr, w_ptr, dx_ptr, ws_ptr or None, ws_bytes, stream or None)
+    if st != 0:
+        raise ConvWgradError(st, "conv_dgrad")
+
+
+def _igemm_call(direction, src, w, out_shape, desc, split_k, stream, out):
+    import torch
+    plan = get_igemm_plan(desc, direction).base
+    if stream is None:
+        stream = torch.cuda.current_stream(src.device)
+    with torch.cuda.stream(stream):
+        if out is None:
+            out = torch.empty(out_shape, dtype=torch.float32, device=src.device)
+        ws = torch.empty(max(int(plan.ws_bytes), 16), dtype=torch.uint8, device=src.device)
+    if tuple(out.shape) != tuple(out_shape) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("output must be a contiguous float32 tensor of shape %s" % (tuple(out_shape),))
+    f = conv_fwd if direction == DIRECTION_FWD else conv_dgrad
+    f(desc, src.data_ptr(), w.data_ptr(), out.data_ptr(), ws.data_ptr() if plan.ws_bytes else 0,
+      int(plan.ws_bytes), stream.cuda_stream)
+    return out
+
+
+def fwd(x, w, pad=0, stride=1, dilation=1, groups=1, split_k=-1, fold_width=-1, y=None, stream=None):
+    """Forward convolution y [N, Ho, Wo, K] (fp32) of NHWC x [N,H,W,C] and the filter
+    w [K,R,S,C/groups] (same dtype as x)."""
+    if x.dim() != 4 or w.dim() != 4 or x.dtype != w.dtype or x.device != w.device:
+        raise ValueError("x [N,H,W,C] and w [K,R,S,Cg] must be 4-D, same dtype and device")
+    if not (x.is_contiguous() and w.is_contiguous()):
+        raise ValueError("x and w must be contiguous")
+    N, H, W, C = x.shape
+    K, R, S, Cg = w.shape
+    if Cg * groups != C:
+        raise ValueError("w has %d channels per group, expected %d" % (Cg, C // groups))
+    d = make_desc2(N, C, H, W, K, R, S, pad, stride, dilation, groups, _dtype_code(x), split_k, "exact",
+                   fold_width)
+    plan = get_igemm_plan(d, DIRECTION_FWD).base
+    return _igemm_call(DIRECTION_FWD, x, w, (N, plan.Ho, plan.Wo, K), d, split_k, stream, y)
+
+
+def dgrad(dy, w, H, W, pad=0, stride=1, dilation=1, groups=1, split_k=-1, fold_width=-1, dx=None,
+          stream=None):
+    """Data gradient dx [N, H, W, C] (fp32) of NHWC dy [N,Ho,Wo,K] and the filter
+    w [K,R,S,C/groups] (same dtype as dy) for H x W input images."""
+    if dy.dim() != 4 or w.dim() != 4 or dy.dtype != w.dtype or dy.device != w.device:
+        raise ValueError("dy [N,Ho,Wo,K] and w [K,R,S,Cg] must be 4-D, same dtype and device")
+    if not (dy.is_contiguous() and w.is_contiguous()):
+        raise ValueError("dy and w must be contiguous")
+    N, Ho, Wo, K = dy.shape
+    Kw, R, S, Cg = w.shape
+    if Kw != K:
+        raise ValueError("w has %d output channels, dy has %d" % (Kw, K))
+    C = Cg * groups
+    d = make_desc2(N, C, H, W, K, R, S, pad, stride, dilation, groups, _dtype_code(dy), split_k, "exact",
+                   fold_width)
+    plan = get_igemm_plan(d, DIRECTION_DGRAD).base
+    if (plan.Ho, plan.Wo) != (Ho, Wo):
+        raise ValueError("dy extents %s do not match the geometry (%d, %d)" % ((Ho, Wo), plan.Ho, plan.Wo))
+    return _igemm_call(DIRECTION_DGRAD, dy, w, (N, H, W, C), d, split_k, stream, dx)
 
 
 def _dtype_code(t):

@@ -45,9 +45,11 @@ namespace {
 std::mutex g_mutex;
 std::unordered_map<std::string, cw::Plan>* g_plans = nullptr;
 
-conv_wgrad_status_t get_plan(const conv_wgrad_desc2_t* desc, cw::Plan* out) {
+conv_wgrad_status_t get_plan(const conv_wgrad_desc2_t* desc, cw::Plan* out,
+                             int32_t direction = CONV_DIRECTION_WGRAD) {
   if (!desc) return CONV_WGRAD_ERR_NULL_ARG;
-  const std::string key(reinterpret_cast<const char*>(desc), sizeof(*desc));
+  std::string key(reinterpret_cast<const char*>(desc), sizeof(*desc));
+  key.push_back(static_cast<char>(direction));
   {
     std::lock_guard<std::mutex> lock(g_mutex);
     if (g_plans) {
@@ -58,7 +60,8 @@ conv_wgrad_status_t get_plan(const conv_wgrad_desc2_t* desc, cw::Plan* out) {
       }
     }
   }
-  conv_wgrad_status_t st = cw::make_plan(desc, out);
+  conv_wgrad_status_t st = direction == CONV_DIRECTION_WGRAD ? cw::make_plan(desc, out)
+                                                             : cw::make_igemm_plan(desc, direction, out);
   if (st != CONV_WGRAD_OK) return st;
   std::lock_guard<std::mutex> lock(g_mutex);
   if (!g_plans) g_plans = new std::unordered_map<std::string, cw::Plan>();
@@ -132,6 +135,35 @@ conv_wgrad_status_t run(const conv_wgrad_desc2_t* desc, const void* x, const voi
     err = cw::launch_slab_reduce(plan, static_cast<float*>(workspace), dw, with_db ? db : nullptr, s);
     if (err != hipSuccess) return CONV_WGRAD_ERR_HIP;
   }
+  return CONV_WGRAD_OK;
+}
+
+// Forward / data gradient: validate, stage 1 (the implicit GEMM) and, with
+// several slices, the slab fold into the output, on the caller's stream.
+conv_wgrad_status_t run_igemm(const conv_wgrad_desc2_t* desc, int32_t direction, const void* a_src,
+                              const void* w, float* out, void* workspace, size_t ws_bytes, void* stream) {
+  cw::Plan plan;
+  conv_wgrad_status_t st = get_plan(desc, &plan, direction);
+  if (st != CONV_WGRAD_OK) return st;
+  if (!a_src || !w || !out) return CONV_WGRAD_ERR_NULL_ARG;
+  if (plan.pub.ws_bytes > 0 && !workspace) return CONV_WGRAD_ERR_NULL_ARG;
+  if (ws_bytes < plan.pub.ws_bytes) return CONV_WGRAD_ERR_WORKSPACE;
+  if (!aligned16(a_src) || !aligned16(w) || !aligned16(out) ||
+      (plan.pub.ws_bytes > 0 && !aligned16(workspace)))
+    return CONV_WGRAD_ERR_MISALIGNED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  cw::Stage1Out o;
+  if (plan.pub.needs_reduce) {
+    o.base = static_cast<float*>(workspace);
+    o.slab_stride = plan.pub.slab_stride;
+  } else {
+    o.base = out;
+    o.slab_stride = 0;
+  }
+  if (cw::launch_igemm(plan, a_src, w, o, s) != hipSuccess) return CONV_WGRAD_ERR_HIP;
+  if (plan.pub.needs_reduce &&
+      cw::launch_slab_reduce(plan, static_cast<float*>(workspace), out, nullptr, s) != hipSuccess)
+    return CONV_WGRAD_ERR_HIP;
   return CONV_WGRAD_OK;
 }
 
@@ -246,6 +278,40 @@ conv_wgrad_status_t conv_wgrad2_timed(const conv_wgrad_desc2_t* desc, const void
                                       void* stream, void* stage1_begin, void* stage1_end) {
   return run(desc, x, dy, dw, db != nullptr, db, workspace, true, ws_bytes, stream, stage1_begin,
              stage1_end);
+}
+
+conv_wgrad_status_t conv_igemm_get_plan(const conv_wgrad_desc2_t* desc, int32_t direction,
+                                        conv_wgrad_plan2_t* plan) {
+  if (!desc || !plan) return CONV_WGRAD_ERR_NULL_ARG;
+  if (direction == CONV_DIRECTION_WGRAD) return conv_wgrad2_get_plan(desc, plan);
+  cw::Plan p;
+  conv_wgrad_status_t st = get_plan(desc, &p, direction);
+  if (st != CONV_WGRAD_OK) return st;
+  plan->base = p.pub;
+  plan->math = CONV_WGRAD_MATH_EXACT;
+  plan->fold_width = p.p.fold;
+  return CONV_WGRAD_OK;
+}
+
+conv_wgrad_status_t conv_igemm_workspace_size(const conv_wgrad_desc2_t* desc, int32_t direction,
+                                              size_t* bytes) {
+  if (!desc || !bytes) return CONV_WGRAD_ERR_NULL_ARG;
+  if (direction == CONV_DIRECTION_WGRAD) return conv_wgrad2_workspace_size(desc, bytes);
+  cw::Plan p;
+  conv_wgrad_status_t st = get_plan(desc, &p, direction);
+  if (st != CONV_WGRAD_OK) return st;
+  *bytes = (size_t)p.pub.ws_bytes;
+  return CONV_WGRAD_OK;
+}
+
+conv_wgrad_status_t conv_fwd(const conv_wgrad_desc2_t* desc, const void* x, const void* w, float* y,
+                             void* workspace, size_t ws_bytes, void* stream) {
+  return run_igemm(desc, CONV_DIRECTION_FWD, x, w, y, workspace, ws_bytes, stream);
+}
+
+conv_wgrad_status_t conv_dgrad(const conv_wgrad_desc2_t* desc, const void* dy, const void* w, float* dx,
+                               void* workspace, size_t ws_bytes, void* stream) {
+  return run_igemm(desc, CONV_DIRECTION_DGRAD, dy, w, dx, workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -54,6 +54,10 @@ hipError_t launch_depthwise(const Plan& plan, const void* x, const void* dy, Sta
                             hipStream_t stream);
 hipError_t launch_direct(const Plan& plan, const void* x, const void* dy, Stage1Out out,
                          hipStream_t stream);
+// Forward or data-gradient implicit GEMM (plan variant kFwdIgemm / kDgradIgemm):
+// a_src is x (forward) or dy (dgrad), w the filter; out.base the output or slab 0.
+hipError_t launch_igemm(const Plan& plan, const void* a_src, const void* w, Stage1Out out, hipStream_t stream);
+
 // Library-owned workspace of conv_wgrad_noalloc: the device address of this
 // process's copy on the current device (looked up once per device).
 constexpr size_t kNoallocScratchBytes = CONV_WGRAD_NOALLOC_SCRATCH_BYTES;

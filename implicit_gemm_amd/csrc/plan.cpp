@@ -528,4 +528,88 @@ conv_wgrad_status_t make_plan(const conv_wgrad_desc2_t* desc, Plan* out) {
   return choose_split(units, tiles, desc->split_k, 8, 1024, 4, p, &pub);
 }
 
+conv_wgrad_status_t make_igemm_plan(const conv_wgrad_desc2_t* desc, int32_t direction, Plan* out) {
+  if (!desc || !out) return CONV_WGRAD_ERR_NULL_ARG;
+  if (direction != CONV_DIRECTION_FWD && direction != CONV_DIRECTION_DGRAD) return CONV_WGRAD_ERR_BAD_DTYPE;
+  memset(out, 0, sizeof(*out));
+  Problem& p = out->p;
+  conv_wgrad_status_t st = canonicalise(desc, &p);
+  if (st != CONV_WGRAD_OK) return st;
+  p.math = CONV_WGRAD_MATH_EXACT;   // no BF16x3 kernel for these directions
+  const bool fwd = direction == CONV_DIRECTION_FWD;
+  conv_wgrad_plan_t& pub = out->pub;
+  pub.path = CONV_WGRAD_PATH_DENSE;
+  pub.variant = fwd ? kFwdIgemm : kDgradIgemm;
+  pub.Ho = p.Ho;
+  pub.Wo = p.Wo;
+  pub.x_bytes = p.x_bytes;
+  pub.dy_bytes = p.dy_bytes;
+  pub.dw_bytes = p.dw_bytes;   // the filter (read by these directions)
+  // Output pixels, channels and the per-group reduction length.
+  int64_t M, Q, E;
+  if (fwd) {
+    M = p.L;
+    if (!mul3(p.R, p.S, p.Cg, &Q)) return CONV_WGRAD_ERR_UNSUPPORTED;
+  } else {
+    if (!mul3(p.N, p.H, p.W, &M)) return CONV_WGRAD_ERR_UNSUPPORTED;
+    if (!mul3(p.R, p.S, p.Kg, &Q)) return CONV_WGRAD_ERR_UNSUPPORTED;
+  }
+  const int64_t NT = fwd ? p.K : p.C, Ng = fwd ? p.Kg : p.Cg;
+  if (!mul_ok(M, NT, &E)) return CONV_WGRAD_ERR_UNSUPPORTED;
+  // Pixel and reduction indices are 32-bit in the kernel; the output index is 64-bit.
+  if (M > kMaxRows || Q > kI32Max - 64) return CONV_WGRAD_ERR_UNSUPPORTED;
+  const uint64_t out_bytes = (uint64_t)E * 4u;
+  const uint64_t big = p.x_bytes > out_bytes ? p.x_bytes : out_bytes;
+  pub.windows_4g = (int64_t)((big + ((uint64_t)1 << 32) - 1) >> 32);
+  pub.L = M;
+  pub.E = E;
+  p.E = E;   // the slab fold covers the output
+  out->m_tiles = ceil_div(M, 64);
+  out->n_tiles = ceil_div(Ng, 64);
+  // 16-byte loads along the contiguous axis: the gathered tensor's channels
+  // of a group (c forward, k dgrad); the filter along q (forward, whole rows)
+  // or along c (dgrad).
+  out->vec_a = (fwd ? p.Cg : p.Kg) % 4 == 0 ? 4 : 1;
+  out->vec_b = fwd ? (Q % 4 == 0 ? 4 : 1) : (p.Cg % 4 == 0 ? 4 : 1);
+  int64_t tiles;
+  if (!mul3(p.groups, out->m_tiles, out->n_tiles, &tiles)) return CONV_WGRAD_ERR_UNSUPPORTED;
+  pub.unit_rows = 32;
+  const int64_t units = ceil_div(Q, 32);
+  int64_t degree;
+  if (desc->split_k >= 1) {
+    degree = desc->split_k;
+  } else {
+    // Split only a grid under 4 workgroups per CU over a reduction at least
+    // 512 deep; a power of two toward that target, at most 32, with at least
+    // two reduction tiles per slice.
+    constexpr int64_t kTarget = 4 * 256;
+    degree = 1;
+    if (tiles < kTarget && Q >= 512) {
+      const int64_t want = ceil_div(kTarget, tiles);
+      while (degree * 2 <= want && degree * 2 <= 32 && units / (degree * 2) >= 2) degree *= 2;
+    }
+  }
+  if (degree > units) degree = units;
+  if (degree > kMaxSlices) degree = kMaxSlices;
+  pub.units = units;
+  pub.units_per_slice = ceil_div(units, degree);
+  const int64_t ks = ceil_div(units, pub.units_per_slice);
+  pub.ks_count = (int32_t)ks;
+  pub.needs_reduce = ks > 1 ? 1 : 0;
+  pub.tiles = tiles;
+  int64_t grid;
+  if (!mul_ok(tiles, ks, &grid) || grid > kI32Max || grid * 256 >= kLaunchLanes) return CONV_WGRAD_ERR_UNSUPPORTED;
+  if (ks > 1 && ceil_div(E, kFoldElemsPerBlock) * kFoldBlock >= kLaunchLanes) return CONV_WGRAD_ERR_UNSUPPORTED;
+  pub.grid = grid;
+  pub.slab_stride = ceil_div(E, 64) * 64;
+  if (ks > 1) {
+    int64_t ws_elems;
+    if (!mul_ok(pub.slab_stride, ks, &ws_elems) || ws_elems > INT64_MAX / 4) return CONV_WGRAD_ERR_UNSUPPORTED;
+    pub.ws_bytes = (uint64_t)ws_elems * 4u;
+  } else {
+    pub.ws_bytes = 0;
+  }
+  return CONV_WGRAD_OK;
+}
+
 }  // namespace cw

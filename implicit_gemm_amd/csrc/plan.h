@@ -24,6 +24,8 @@ enum Variant : int32_t {
   kGrouped16 = 11,    // 16-bit small groups: block-diagonal 16x16x32 MFMA, transposed LDS reads
   kDepthwise = 12,    // 16-bit depthwise: batched 4x4x4 MFMA, 64 channels per workgroup
   kGrouped16Rows = 13,  // 16-bit small groups, 1x1 / 3x3, Wo <= 32: row-streaming 16x16x32 MFMA
+  kFwdIgemm = 20,     // forward convolution: implicit GEMM over (r, s, c), split-K slabs
+  kDgradIgemm = 21,   // data gradient: implicit GEMM over (r, s, k), split-K slabs
 };
 
 struct Problem {
@@ -83,6 +85,13 @@ int32_t depthwise_lds_bytes(int32_t xl, int32_t R, int32_t S);
 
 // Build the full plan (calls canonicalise).
 conv_wgrad_status_t make_plan(const conv_wgrad_desc2_t* desc, Plan* out);
+
+// Plan of the forward (CONV_DIRECTION_FWD) or data-gradient
+// (CONV_DIRECTION_DGRAD) implicit GEMM of the same convolution.  In these
+// plans pub.L is the output pixel count (N*Ho*Wo forward, N*H*W dgrad), pub.E
+// and p.E the output elements the slab fold covers, a unit is 32 reduction
+// entries (r, s, c) or (r, s, k), and tiles are 64 pixels x 64 channels.
+conv_wgrad_status_t make_igemm_plan(const conv_wgrad_desc2_t* desc, int32_t direction, Plan* out);
 
 // Split policy shared by all paths.  `units` reduction units, `tiles` output
 // tiles per slice, `requested` the descriptor's split_k (-1 = auto).  Fills

@@ -309,6 +309,56 @@ conv_wgrad_status_t conv_wgrad2_timed(const conv_wgrad_desc2_t* desc, const void
                                       void* stream, void* stage1_begin, void* stage1_end);
 
 /*
+ * Forward convolution and data gradient on the same implicit-GEMM, split-K
+ * slab and fold machinery (rocm-libraries PR #14393 "split-K forward
+ * implicit-GEMM convolution on gfx1250": sections Summary, "Two-stage
+ * split-K" -- every workgroup stores an fp32 partial tile into its slab, a
+ * second kernel folds the slabs, no workspace clearing, deterministic -- and
+ * "Auto-deduced degree (split_k = -1)", whose policy is refitted here for 256
+ * CUs: split only a grid under 4 workgroups per CU (1024) over a reduction at
+ * least 512 deep, by a power of two toward that target, at most 32, with at
+ * least two 32-entry reduction tiles per slice).
+ *
+ *   forward: y[n][ho][wo][k] = sum_{r,s,c} x[n][ho*stride_h + r*dil_h - pad_h]
+ *                                            [wo*stride_w + s*dil_w - pad_w][g(k)*Cg + c]
+ *                                          * w[k][r][s][c]
+ *   dgrad:   dx[n][h][w][g*Cg + c] = sum over k of group g and r, s with
+ *              ho*stride_h = h + pad_h - r*dil_h, wo*stride_w = w + pad_w - s*dil_w
+ *              (exactly, 0 <= ho < Ho, 0 <= wo < Wo) of dy[n][ho][wo][k] * w[k][r][s][c]
+ *
+ * The descriptor is conv_wgrad_desc2_t (per-axis geometry, groups, dtype,
+ * split_k, fold_width; math is read as in conv_wgrad2 and only the exact path
+ * exists for these directions).  Layouts: x [N][H][W][C] and dy [N][Ho][Wo][K]
+ * and the filter w [K][R][S][Cg] in desc->dtype; y [N][Ho][Wo][K] and dx
+ * [N][H][W][C] are fp32 (fp32 accumulation for every dtype), overwritten.
+ * Workspace, alignment (16 bytes), ownership, determinism at a fixed split and
+ * errors are those of conv_wgrad_ex; the workspace holds ks_count slabs of the
+ * whole output.
+ */
+#define CONV_DIRECTION_WGRAD 0
+#define CONV_DIRECTION_FWD 1
+#define CONV_DIRECTION_DGRAD 2
+
+/* Plan of a direction (CONV_DIRECTION_*; WGRAD gives conv_wgrad2_get_plan's).
+ * For FWD / DGRAD: base.L is the output pixel count, base.E the output
+ * elements, base.unit_rows 32 reduction entries, base.variant 20 / 21.
+ * Unknown direction: BAD_DTYPE.  Pure host function. */
+conv_wgrad_status_t conv_igemm_get_plan(const conv_wgrad_desc2_t* desc, int32_t direction,
+                                        conv_wgrad_plan2_t* plan);
+
+/* Workspace bytes of conv_fwd (direction FWD) or conv_dgrad (DGRAD). */
+conv_wgrad_status_t conv_igemm_workspace_size(const conv_wgrad_desc2_t* desc, int32_t direction,
+                                              size_t* bytes);
+
+/* Forward convolution: y (fp32) from x and w, enqueued on stream. */
+conv_wgrad_status_t conv_fwd(const conv_wgrad_desc2_t* desc, const void* x, const void* w, float* y,
+                             void* workspace, size_t ws_bytes, void* stream);
+
+/* Data gradient: dx (fp32) from dy and w, enqueued on stream. */
+conv_wgrad_status_t conv_dgrad(const conv_wgrad_desc2_t* desc, const void* dy, const void* w, float* dx,
+                               void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): conv_wgrad_bias
  * without the workspace argument.  The slabs live in a library-owned device

@@ -22,10 +22,11 @@ GOLDEN = os.path.join(ROOT, "tests", "golden")
 PUBLIC_FUNCTIONS = {"conv_wgrad", "conv_wgrad_ex", "conv_wgrad_get_plan", "conv_wgrad_timed",
                     "conv_wgrad_status_string", "conv_wgrad_workspace_size", "conv_wgrad_bias",
                     "conv_wgrad_bias_timed", "conv_wgrad_noalloc", "conv_wgrad2_workspace_size",
-                    "conv_wgrad2_get_plan", "conv_wgrad2", "conv_wgrad2_timed"}
+                    "conv_wgrad2_get_plan", "conv_wgrad2", "conv_wgrad2_timed", "conv_igemm_get_plan",
+                    "conv_igemm_workspace_size", "conv_fwd", "conv_dgrad"}
 
 
-def declared_functions(header=HEADER, prefix="conv_wgrad"):
+def declared_functions(header=HEADER, prefix="conv_"):
     text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(%s\w*)\s*\(" % prefix, text)))
@@ -48,7 +49,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     exported = exported_symbols(iga.LIB_PATH)
     assert set(names) <= exported
     # The measurement probes live in their own library, not in the product's ABI.
-    assert not any("probe" in n or "peak" in n for n in exported if n.startswith("conv_wgrad"))
+    assert not any("probe" in n or "peak" in n for n in exported if n.startswith("conv_"))
 
 
 def test_probe_library_exports_its_declared_symbols():
@@ -459,3 +460,47 @@ def test_bf16x3_plan_selection():
         assert q.math == 0 and q.base.variant != iga.VARIANT_DENSE_BF16X3, kw
     q = iga.get_plan2(D2(math="bf16x3", dtype=iga.BF16, **c2))
     assert q.math == 0 and q.base.variant == 3
+
+
+def test_igemm_plans_and_errors():
+    """Forward / data-gradient plans: output sizes, exact ceil-division slices, the
+    refitted auto degree (split only grids under 1024 workgroups over a reduction
+    of at least 512, a power of two, at most 32, at least two reduction tiles per
+    slice), and validation before any launch."""
+    lib = iga.load()
+    # A small-M layer: 1568 output pixels, reduction 4608.
+    d = D2(N=8, C=512, H=14, W=14, K=512, R=3, S=3, pad=1)
+    for direction in (iga.DIRECTION_FWD, iga.DIRECTION_DGRAD):
+        p = iga.get_igemm_plan(d, direction).base
+        assert p.variant == (20 if direction == iga.DIRECTION_FWD else 21)
+        assert p.L == 8 * 14 * 14 and p.E == p.L * 512
+        assert p.units == 4608 // 32 and p.tiles == 25 * 8
+        assert p.ks_count == 4 and p.grid == 800 and p.needs_reduce == 1     # 1024 / 200 -> 4
+        assert p.ws_bytes == 4 * (-(-p.E // 64) * 64) * 4
+    # Large grids and shallow reductions are not split.
+    assert iga.get_igemm_plan(D2(N=32, C=64, H=56, W=56, K=64, R=3, S=3, pad=1), 1).base.ks_count == 1
+    assert iga.get_igemm_plan(D2(N=1, C=32, H=4, W=4, K=32, R=3, S=3, pad=1), 1).base.ks_count == 1
+    # Degree caps: at most 32, at least two reduction tiles per slice.
+    p = iga.get_igemm_plan(D2(N=1, C=2048, H=4, W=4, K=64, R=3, S=3, pad=1), 1).base
+    assert p.ks_count == 32 and p.units_per_slice >= 2
+    # Q = 576: 18 reduction tiles; degree 8 (18 / 16 < 2), i.e. 3 tiles per slice, 6 slices
+    p = iga.get_igemm_plan(D2(N=1, C=64, H=4, W=4, K=64, R=3, S=3, pad=1), 1).base
+    assert p.units_per_slice == 3 and p.ks_count == 6
+    # Pinned degrees keep every slice non-empty.
+    for sk in (1, 3, 7, 100):
+        p = iga.get_igemm_plan(D2(N=2, C=64, H=9, W=9, K=32, R=3, S=3, pad=1, split_k=sk), 2).base
+        assert p.ks_count <= sk and (p.ks_count - 1) * p.units_per_slice < p.units <= p.ks_count * p.units_per_slice
+    # Width fold applies to these directions too.
+    assert iga.get_igemm_plan(D2(N=2, C=3, H=64, W=64, K=96, R=16, S=16, pad=0, stride=16), 1).fold_width == 16
+    # Errors before any launch.
+    plan = iga.Plan2()
+    assert lib.conv_igemm_get_plan(ctypes.byref(d), 3, ctypes.byref(plan)) == 3
+    assert lib.conv_igemm_get_plan(ctypes.byref(D2(split_k=0)), 1, ctypes.byref(plan)) == 4
+    ws = iga.get_igemm_plan(d, 1).base.ws_bytes
+    assert lib.conv_fwd(ctypes.byref(d), None, 16, 16, 16, ws, None) == 1
+    assert lib.conv_fwd(ctypes.byref(d), 16, 16, 16, None, ws, None) == 1
+    assert lib.conv_fwd(ctypes.byref(d), 16, 16, 16, 16, ws - 1, None) == 7
+    assert lib.conv_dgrad(ctypes.byref(d), 16, 24, 16, 16, ws, None) == 6
+    assert lib.conv_dgrad(None, 16, 16, 16, 16, ws, None) == 1
+    n = ctypes.c_size_t(0)
+    assert lib.conv_igemm_workspace_size(ctypes.byref(d), 2, ctypes.byref(n)) == 0 and n.value == ws

@@ -5,7 +5,8 @@ and rounds them to the input dtype.  Both the GPU path and the oracle receive
 exactly the arrays produced here.
 
 Recipe: one numpy PCG64 stream per (seed, tensor, image), seeded with
-``SeedSequence([seed, tensor_id, n])`` (tensor_id 0 for X, 1 for dY), filled
+``SeedSequence([seed, tensor_id, n])`` (tensor_id 0 for X, 1 for dY, 2 for a
+filter W, whose "images" are its output channels), filled
 in NHWC order in float32.  Uniform draws are ``2*U[0,1) - 1``; normal draws are
 ``sigma * standard_normal``.  For 16-bit configurations the float32 draw is
 rounded to bf16 / fp16 with round-to-nearest-even, and the rounded values are
@@ -20,7 +21,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-X_ID, DY_ID = 0, 1
+X_ID, DY_ID, W_ID = 0, 1, 2
 
 
 def _extent(n_in, k, pad, stride, dil):
@@ -119,6 +120,12 @@ def draw_images(seed, tensor_id, n0, count, h, w, c, dist: Dist, out=None, threa
         with ThreadPoolExecutor(min(threads, count)) as ex:
             list(ex.map(lambda i: _fill_image(seed, tensor_id, n0 + i, flat[i], dist), range(count)))
     return out
+
+
+def draw_filter(seed, K, R, S, Cg, dist: Dist, dtype="f32") -> np.ndarray:
+    """float32 [K, R, S, Cg] filter (one stream per output channel, tensor id 2),
+    rounded to dtype like the activations."""
+    return round_to(draw_images(seed, W_ID, 0, K, R, S, Cg, dist), dtype)
 
 
 def round_to(a: np.ndarray, dtype: str) -> np.ndarray:
