@@ -221,7 +221,10 @@ ALL_RECORDS = [("c1_1x1_tiny_f32", None, {}), ("c2_3x3_f32", None, {}), ("c3_dw7
                ("c4a_grp3x3_cpg4_f16", None, {}), ("c4b_grp3x3_cpg8_f16", None, {}),
                ("c5_1x1_big_f32", 64, {}),
                ("c2_3x3_f32", None, {"math": "bf16x3"}),
-               ("g_patch16_f32", None, {}), ("g_patch16_f32", None, {"fold_width": 0})]
+               ("g_patch16_f32", None, {}), ("g_patch16_f32", None, {"fold_width": 0}),
+               ("l_3x3_c512_f32", None, {"direction": "fwd"}), ("l_3x3_c512_f32", None, {"direction": "fwd", "split_k": 1}),
+               ("l_3x3_c512_f32", None, {"direction": "dgrad"}), ("l_3x3_c512_bf16", None, {"direction": "fwd"}),
+               ("l_3x3_c512_bf16", None, {"direction": "dgrad"})]
 HEADLINE = ("c5_1x1_big_f32", 192, {})
 FAMILY = {0: "dense_lds", 1: "dense_rows", 2: "dense_1x1", 3: "dense16_rows", 4: "dense16_rows_bf16x3",
           10: "direct_elem", 11: "grouped16", 12: "depthwise_mfma", 13: "grouped16_rows"}
@@ -454,6 +457,102 @@ def measure(wl, s, x, dy, args, hip, cold_reps, bias=False, opts=None):
     return rec, wall, statistics.mean(k_ms) * 1e-3
 
 
+def measure_igemm(wl, s, args, hip, cold_reps, opts):
+    """Time the forward convolution or the data gradient (conv_fwd / conv_dgrad) of a
+    workload's shape: hot back-to-back calls and cold calls (stream events around
+    the implicit GEMM + fold after a 1 GiB clean read)."""
+    import numpy as np
+    import torch
+    import implicit_gemm_amd as iga
+    import wgrad_data as wd
+    direction = iga.DIRECTION_FWD if opts["direction"] == "fwd" else iga.DIRECTION_DGRAD
+    dev = torch.device("cuda:0")
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[wl.dtype]
+    x, dy = wd.make_inputs(wl)
+    w = wd.draw_filter(wl.seed, s.K, s.R, s.S, s.Cg, wd.Dist("normal", 0.05), wl.dtype)
+    src = torch.from_numpy(x if direction == iga.DIRECTION_FWD else dy).to(tdt).to(dev)
+    wt = torch.from_numpy(w).to(tdt).to(dev)
+    split_k = opts.get("split_k", args.split_k)
+    d = iga.make_desc2(s.N, s.C, s.H, s.W, s.K, s.R, s.S, s.pad, s.stride, s.dilation, s.groups,
+                       {"f32": 0, "bf16": 1, "f16": 2}[wl.dtype], split_k)
+    plan2 = iga.get_igemm_plan(d, direction)
+    plan = plan2.base
+    out = torch.empty(int(plan.E), dtype=torch.float32, device=dev)
+    ws_bytes = int(plan.ws_bytes)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    sp = torch.cuda.current_stream(dev).cuda_stream
+    f = iga.conv_fwd if direction == iga.DIRECTION_FWD else iga.conv_dgrad
+
+    def step():
+        f(d, src.data_ptr(), wt.data_ptr(), out.data_ptr(), ws.data_ptr() if ws_bytes else 0, ws_bytes, sp)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_pre = time.perf_counter()
+    while time.perf_counter() - t_pre < args.prewarm_s:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    probe = torch.empty((), dtype=torch.float32, device=dev)
+    e0, e1 = hip.event(), hip.event()
+    whole = []
+    for _ in range(cold_reps):
+        torch.amax(flush, dim=0, out=probe)
+        hip.record(e0, sp)
+        step()
+        hip.record(e1, sp)
+        whole.append(hip.elapsed_ms(e0, e1))
+    hip.destroy(e0)
+    hip.destroy(e1)
+    del flush, probe
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    cold_med = statistics.median(whole) * 1e-3
+    esz = wd.IN_BYTES[wl.dtype]
+    w_bytes = s.K * s.R * s.S * s.Cg * esz
+    if direction == iga.DIRECTION_FWD:
+        nbytes = s.N * s.H * s.W * s.C * esz + w_bytes + s.N * s.Ho * s.Wo * s.K * 4
+    else:
+        nbytes = s.N * s.Ho * s.Wo * s.K * esz + w_bytes + s.N * s.H * s.W * s.C * 4
+    flops = s.flops()
+    peak_mfma = PEAK["mfma_tflops"]["f32"]   # the kernel's products run on f32 MFMA for every dtype
+    t_roof = max(flops / (peak_mfma * 1e12), nbytes / (PEAK["hbm_gbs"] * 1e9))
+    bound = "mfma" if flops / (peak_mfma * 1e12) >= nbytes / (PEAK["hbm_gbs"] * 1e9) else "hbm"
+
+    def roof(t):
+        if bound == "mfma":
+            a = flops / t / 1e12
+            return {"bound": "mfma", "achieved": round(a, 2), "peak": peak_mfma, "unit": "TFLOP/s",
+                    "frac": round(a / peak_mfma, 4), "traffic": None,
+                    "note": "16-bit inputs are widened and multiplied on f32 MFMA"}
+        a = nbytes / t / 1e9
+        return {"bound": "hbm", "achieved": round(a, 1), "peak": PEAK["hbm_gbs"], "unit": "GB/s",
+                "frac": round(a / PEAK["hbm_gbs"], 4), "traffic": None}
+
+    tag = "%s+%s%s" % (wl.name, opts["direction"], "+split%d" % split_k if split_k >= 1 else "")
+    return {
+        "workload": wl.name, "record": tag, "direction": opts["direction"], "note": wl.note, "dtype": wl.dtype,
+        "N": s.N, "C": s.C, "H": s.H, "W": s.W, "K": s.K, "R": s.R, "S": s.S, "pad": s.pad,
+        "stride": s.stride, "dilation": s.dilation, "groups": s.groups,
+        "kernel": "igemm_" + opts["direction"], "variant": int(plan.variant), "ks_count": int(plan.ks_count),
+        "split_k": split_k, "fold_width": int(plan2.fold_width), "flops": flops, "algorithmic_bytes": nbytes,
+        "cold_call_us": {"median": round(cold_med * 1e6, 2), "min": round(min(whole) * 1e3, 2),
+                         "p90": round(_pct(whole, 0.9) * 1e3, 2), "calls": cold_reps},
+        "tflops": round(flops / cold_med / 1e12, 3),
+        "roofline": roof(cold_med),
+        "hot_call_us": round(wall * 1e6, 2), "hot_frac": roof(wall)["frac"], "hot_roofline": roof(wall),
+        "roofline_time_us": round(t_roof * 1e6, 2),
+        "check": {"zeros": int((o == 0).sum()), "finite": bool(np.isfinite(o).all())},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -471,6 +570,8 @@ def main():
     ap.add_argument("--math", default="exact", choices=["exact", "bf16x3"],
                     help="with --config: arithmetic for fp32 inputs (bf16x3 where a kernel covers the shape)")
     ap.add_argument("--fold-width", type=int, default=-1, help="with --config: width fold (-1 auto, 0 off)")
+    ap.add_argument("--direction", default="wgrad", choices=["wgrad", "fwd", "dgrad"],
+                    help="with --config: time the forward convolution or the data gradient instead")
     ap.add_argument("--bias", action="store_true",
                     help="time conv_wgrad_bias (dW and the fused bias gradient db = sum dY)")
     ap.add_argument("--peaks", action="store_true",
@@ -536,6 +637,12 @@ def main():
     for name, n, opts in plan_runs:
         wl, s = resolve(name, n)
         log("record", wl.name, s, wl.dtype, opts)
+        if "direction" in opts:
+            rec = measure_igemm(wl, s, args, hip, args.cold, opts)
+            records.append(rec)
+            log(json.dumps(rec))
+            torch.cuda.empty_cache()
+            continue
         if wl.n_sweep and hwl.name == wl.name and s.N <= hs.N:
             if big is None:
                 big = device_inputs(hwl, hs, dev)
@@ -549,6 +656,24 @@ def main():
         log(json.dumps(rec))
         del x, dy
         torch.cuda.empty_cache()
+
+    if args.config and args.direction != "wgrad":
+        opts = {"direction": args.direction}
+        rec = measure_igemm(hwl, hs, args, hip, args.cold, opts)
+        wall = rec["hot_call_us"] * 1e-6
+        print(json.dumps({
+            "metric": "wgrad TFLOP/s and % of MFMA-or-HBM roofline per conv shape, 1xMI355X",
+            "value": round(hs.flops() / wall / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": hwl.dtype,
+            "data": "synthetic (seeded PCG64 per image)",
+            "config": {"workload": hwl.name, "direction": args.direction, "N": hs.N, "C": hs.C, "H": hs.H,
+                       "W": hs.W, "K": hs.K, "R": hs.R, "S": hs.S, "pad": hs.pad, "stride": hs.stride,
+                       "split_k": args.split_k, "ks_count": rec["ks_count"], "kernel": rec["kernel"],
+                       "parallelism": "single GPU"},
+            "roofline": rec["hot_roofline"], "cpu_baseline": None, "check": rec["check"], "configs": [rec]}),
+            flush=True)
+        return 0
 
     log("headline", hwl.name, hs, hwl.dtype)
     if big is None:

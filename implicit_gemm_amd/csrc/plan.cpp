@@ -579,14 +579,16 @@ conv_wgrad_status_t make_igemm_plan(const conv_wgrad_desc2_t* desc, int32_t dire
   if (desc->split_k >= 1) {
     degree = desc->split_k;
   } else {
-    // Split only a grid under 4 workgroups per CU over a reduction at least
-    // 512 deep; a power of two toward that target, at most 32, with at least
-    // two reduction tiles per slice.
-    constexpr int64_t kTarget = 4 * 256;
+    // Split only a grid under half of 8 workgroups per CU (the kernel keeps
+    // 6-7 resident per CU) over a reduction at least 512 deep, by the
+    // smallest power of two that reaches 8 workgroups per CU, at most 32, with
+    // at least two reduction tiles per slice.  Measured on the 3x3 C=K=512
+    // 14x14 N=8 forward (200 tiles): 1 / 2 / 4 / 8 / 16 / 32 slices took
+    // 151 / 124 / 108 / 95 / 91 / 97 us.
+    constexpr int64_t kThreshold = 4 * 256, kTarget = 8 * 256;
     degree = 1;
-    if (tiles < kTarget && Q >= 512) {
-      const int64_t want = ceil_div(kTarget, tiles);
-      while (degree * 2 <= want && degree * 2 <= 32 && units / (degree * 2) >= 2) degree *= 2;
+    if (tiles < kThreshold && Q >= 512) {
+      while (tiles * degree < kTarget && degree * 2 <= 32 && units / (degree * 2) >= 2) degree *= 2;
     }
   }
   if (degree > units) degree = units;

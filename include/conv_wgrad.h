@@ -316,8 +316,9 @@ conv_wgrad_status_t conv_wgrad2_timed(const conv_wgrad_desc2_t* desc, const void
  * second kernel folds the slabs, no workspace clearing, deterministic -- and
  * "Auto-deduced degree (split_k = -1)", whose policy is refitted here for 256
  * CUs: split only a grid under 4 workgroups per CU (1024) over a reduction at
- * least 512 deep, by a power of two toward that target, at most 32, with at
- * least two 32-entry reduction tiles per slice).
+ * least 512 deep, by the smallest power of two that brings the grid to 8
+ * workgroups per CU (2048), at most 32, with at least two 32-entry reduction
+ * tiles per slice).
  *
  *   forward: y[n][ho][wo][k] = sum_{r,s,c} x[n][ho*stride_h + r*dil_h - pad_h]
  *                                            [wo*stride_w + s*dil_w - pad_w][g(k)*Cg + c]

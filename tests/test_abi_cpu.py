@@ -465,8 +465,8 @@ def test_bf16x3_plan_selection():
 def test_igemm_plans_and_errors():
     """Forward / data-gradient plans: output sizes, exact ceil-division slices, the
     refitted auto degree (split only grids under 1024 workgroups over a reduction
-    of at least 512, a power of two, at most 32, at least two reduction tiles per
-    slice), and validation before any launch."""
+    of at least 512, the smallest power of two reaching 2048 workgroups, at most
+    32, at least two reduction tiles per slice), and validation before any launch."""
     lib = iga.load()
     # A small-M layer: 1568 output pixels, reduction 4608.
     d = D2(N=8, C=512, H=14, W=14, K=512, R=3, S=3, pad=1)
@@ -475,8 +475,8 @@ def test_igemm_plans_and_errors():
         assert p.variant == (20 if direction == iga.DIRECTION_FWD else 21)
         assert p.L == 8 * 14 * 14 and p.E == p.L * 512
         assert p.units == 4608 // 32 and p.tiles == 25 * 8
-        assert p.ks_count == 4 and p.grid == 800 and p.needs_reduce == 1     # 1024 / 200 -> 4
-        assert p.ws_bytes == 4 * (-(-p.E // 64) * 64) * 4
+        assert p.ks_count == 16 and p.grid == 3200 and p.needs_reduce == 1   # 200 tiles x 16 >= 2048
+        assert p.ws_bytes == 16 * (-(-p.E // 64) * 64) * 4
     # Large grids and shallow reductions are not split.
     assert iga.get_igemm_plan(D2(N=32, C=64, H=56, W=56, K=64, R=3, S=3, pad=1), 1).base.ks_count == 1
     assert iga.get_igemm_plan(D2(N=1, C=32, H=4, W=4, K=32, R=3, S=3, pad=1), 1).base.ks_count == 1

@@ -215,6 +215,10 @@ GEOMETRY = {w.name: w for w in [
          "grouped 3x3 stride 2 fp16, 4 ch/group, N=64 C=K=256 56x56 pad 1"),
     _geo("g_patch16_f32", ConvShape(64, 3, 224, 224, 768, 16, 16, stride=16), "f32", 112,
          "patch embedding 16x16 stride 16 fp32, N=64 C=3 K=768 224x224"),
+    _geo("l_3x3_c512_f32", ConvShape(8, 512, 14, 14, 512, 3, 3, pad=1), "f32", 113,
+         "small-M 3x3 fp32 layer, N=8 C=K=512 14x14 pad 1 (1568 output pixels, reduction 4608)"),
+    _geo("l_3x3_c512_bf16", ConvShape(8, 512, 14, 14, 512, 3, 3, pad=1), "bf16", 114,
+         "small-M 3x3 bf16 layer, N=8 C=K=512 14x14 pad 1"),
 ]}
 
 
