@@ -44,9 +44,10 @@ namespace {
 
 constexpr int kPitchE = 80;      // 16-bit elements per staged pixel (64 channels + pad)
 constexpr int kWt = 64;          // dY pixels staged per unit (two 32-pixel k-steps)
-constexpr int kXs = 68;          // X pixels staged per unit (64 + up to 3 tap shifts, all rows initialised)
+constexpr int kXUse = 68;        // X pixels a unit's MFMAs read (64 + up to 3 tap shifts)
 constexpr int kDyChunks = kWt * 8 / 256;                  // 16-byte loads per lane for dY
-constexpr int kXChunks = (kXs * 8 + 255) / 256;           // and for X
+constexpr int kXChunks = (kXUse * 8 + 255) / 256;         // and for X
+constexpr int kXs = kXChunks * 32;                        // X pixel rows staged: every loader chunk has one
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -102,8 +103,13 @@ __device__ __forceinline__ void split_bf16x8(uint4 v0, uint4 v1, uint4& hi, uint
 }
 
 // kDb: also the bias gradient (a separate instantiation).  kX3: fp32 inputs
-// by BF16x3 (kBf16 is then true).
-template <bool kBf16, int SB, bool kDb, bool kX3>
+// by BF16x3 (kBf16 is then true).  kMulti: units of several short rows.
+// kSets: register sets of unit loads in flight.  The loop runs whole rounds
+// of kSets units, each set with its own registers (no copies between sets),
+// and every load is issued unconditionally -- units past the slice have empty
+// buffer ranges and read zero, their MFMAs are skipped -- so the waits at a
+// set's staging count only that set's loads.
+template <bool kBf16, int SB, bool kDb, bool kX3, bool kMulti, int kSets>
 __global__ __launch_bounds__(256) void dense16_rows_kernel(R16Args a) {
   constexpr int kEs = kX3 ? 4 : 2;          // bytes per input element
   constexpr int kLd = kX3 ? 2 : 1;          // 16-byte loads per 8-channel chunk
@@ -139,116 +145,146 @@ __global__ __launch_bounds__(256) void dense16_rows_kernel(R16Args a) {
   const int dy_col0 = g * a.Kg + m0;
   const int x_col0 = g * a.Cg + c0;
   const int x_row_bytes = (a.W * a.C - x_col0) * kEs;
-  uint4 rdy[kDyChunks][kLd], rx[kXChunks][kLd];
-  int npix_next = 0;
+  struct Set {
+    uint4 dy[kDyChunks][kLd], x[kXChunks][kLd];
+    int npix;   // output pixel slots the unit fills (0 past the slice)
+  };
   // Multi-row units: slot p of a loader chunk is row p / pitch, column p % pitch.
   int dj[kDyChunks], dcol[kDyChunks], xj[kXChunks], xcol[kXChunks];
-  if (a.ru > 1) {
+  if constexpr (kMulti) {
 #pragma unroll
     for (int i = 0; i < kDyChunks; ++i) { dj[i] = (px0 + 32 * i) / a.pitch; dcol[i] = (px0 + 32 * i) % a.pitch; }
 #pragma unroll
     for (int i = 0; i < kXChunks; ++i) { xj[i] = (px0 + 32 * i) / a.pitch; xcol[i] = (px0 + 32 * i) % a.pitch; }
   }
-  auto load_rows = [&](int u) {
-    const int n = u / a.hblocks, ho0 = (u % a.hblocks) * a.ru;
-    const int rows = min(a.ru, a.Ho - ho0);
-    npix_next = a.ru * a.pitch;
-    // dY rows ho0 .. ho0 + rows - 1 are contiguous; columns past Wo and rows
-    // past the unit read zero.
-    const unsigned char* dyp = dyg + kEs * (((int64_t)(n * a.Ho + ho0) * a.Wo) * a.K + dy_col0);
-    const __amdgpu_buffer_rsrc_t rd = buf_rsrc(dyp, (rows * a.Wo * a.K - dy_col0) * kEs);
-#pragma unroll
-    for (int i = 0; i < kDyChunks; ++i) {
-      const bool ok = dcol[i] < a.Wo && dj[i] < rows;
-      const int off = ok ? ((dj[i] * a.Wo + dcol[i]) * a.K + 8 * q8) * kEs : 0x7fffffe0;
-#pragma unroll
-      for (int h = 0; h < kLd; ++h)
-        rdy[i][h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rd, off + 16 * h, 0, 0));
-    }
-    // X rows h0 + j of the unit (filter row r), columns w0 .. w0 + pitch - 1;
-    // rows and columns outside the image read zero.
-    const int h0 = ho0 + r - a.pad_h;
-    const int hb = max(h0, 0), he = min(h0 + rows, a.H);
-    const int w0 = s0 - a.pad_w;
-    const unsigned char* xp = xg + kEs * ((int64_t)n * a.x_img + (int64_t)hb * a.W * a.C + x_col0);
-    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(xp, he > hb ? ((he - hb) * a.W * a.C - x_col0) * kEs : 0);
-#pragma unroll
-    for (int i = 0; i < kXChunks; ++i) {
-      const int h = h0 + xj[i], w = w0 + xcol[i];
-      const bool ok = xj[i] < rows && h >= hb && h < he && w >= 0 && w < a.W;
-      const int off = ok ? (((h - hb) * a.W + w) * a.C + 8 * q8) * kEs : 0x7fffffe0;
-#pragma unroll
-      for (int hh = 0; hh < kLd; ++hh)
-        rx[i][hh] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16 * hh, 0, 0));
+  // The loads take the slice's units in order, so the next unit's coordinates
+  // are a cursor advanced by one per load (no divisions in the loop):
+  // multi-row units (n, row block cb), single-row units (n, ho, chunk wc).
+  int cur_n, cur_ho = 0, cur_w = 0;
+  if constexpr (kMulti) {
+    cur_n = u_begin / a.hblocks;
+    cur_ho = u_begin % a.hblocks;
+  } else {
+    cur_w = u_begin % a.wchunks;
+    const int t0 = u_begin / a.wchunks;
+    cur_ho = t0 % a.Ho;
+    cur_n = t0 / a.Ho;
+  }
+  const int n_first = cur_n, ho_first = cur_ho, w_first = cur_w;
+  auto advance = [&]() {
+    if constexpr (kMulti) {
+      if (++cur_ho == a.hblocks) { cur_ho = 0; ++cur_n; }
+    } else {
+      if (++cur_w == a.wchunks) {
+        cur_w = 0;
+        if (++cur_ho == a.Ho) { cur_ho = 0; ++cur_n; }
+      }
     }
   };
-  auto load_unit = [&](int u) {
-    if (a.ru > 1) {
-      load_rows(u);
-      return;
+  // Unit u of the slice (the cursor's) into set st; a unit past the slice
+  // (u >= u_end) addresses the slice's first unit with empty ranges, so it
+  // reads zero.
+  auto load_unit = [&](int u, Set& st) {
+    const bool live = u < u_end;
+    const int un = live ? cur_n : n_first, uho = live ? cur_ho : ho_first, uw = live ? cur_w : w_first;
+    if (live) advance();
+    if constexpr (kMulti) {
+      const int n = un, ho0 = uho * a.ru;
+      const int rows = live ? min(a.ru, a.Ho - ho0) : 0;
+      st.npix = live ? a.ru * a.pitch : 0;
+      // dY rows ho0 .. ho0 + rows - 1 are contiguous; columns past Wo and rows
+      // past the unit read zero.
+      const unsigned char* dyp = dyg + kEs * (((int64_t)(n * a.Ho + ho0) * a.Wo) * a.K + dy_col0);
+      const __amdgpu_buffer_rsrc_t rd = buf_rsrc(dyp, rows > 0 ? (rows * a.Wo * a.K - dy_col0) * kEs : 0);
+#pragma unroll
+      for (int i = 0; i < kDyChunks; ++i) {
+        const bool ok = dcol[i] < a.Wo && dj[i] < rows;
+        const int off = ok ? ((dj[i] * a.Wo + dcol[i]) * a.K + 8 * q8) * kEs : 0x7fffffe0;
+#pragma unroll
+        for (int h = 0; h < kLd; ++h)
+          st.dy[i][h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rd, off + 16 * h, 0, 0));
+      }
+      // X rows h0 + j of the unit (filter row r), columns w0 .. w0 + pitch - 1;
+      // rows and columns outside the image read zero.
+      const int h0 = ho0 + r - a.pad_h;
+      const int hb = max(h0, 0), he = min(h0 + rows, a.H);
+      const int w0 = s0 - a.pad_w;
+      const unsigned char* xp = xg + kEs * ((int64_t)n * a.x_img + (int64_t)hb * a.W * a.C + x_col0);
+      const __amdgpu_buffer_rsrc_t rs = buf_rsrc(xp, he > hb ? ((he - hb) * a.W * a.C - x_col0) * kEs : 0);
+#pragma unroll
+      for (int i = 0; i < kXChunks; ++i) {
+        const int h = h0 + xj[i], w = w0 + xcol[i];
+        const bool ok = xj[i] < rows && h >= hb && h < he && w >= 0 && w < a.W;
+        const int off = ok ? (((h - hb) * a.W + w) * a.C + 8 * q8) * kEs : 0x7fffffe0;
+#pragma unroll
+        for (int hh = 0; hh < kLd; ++hh)
+          st.x[i][hh] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16 * hh, 0, 0));
+      }
+    } else {
+      const int wc = uw, ho = uho, n = un;
+      const int wo0 = wc * a.wt;
+      const int npix = live ? min(a.wt, a.Wo - wo0) : 0;
+      st.npix = npix;
+      const unsigned char* dyp = dyg + kEs * (((int64_t)(n * a.Ho + ho) * a.Wo + wo0) * a.K + dy_col0);
+      const __amdgpu_buffer_rsrc_t rd = buf_rsrc(dyp, npix > 0 ? (npix * a.K - dy_col0) * kEs : 0);
+#pragma unroll
+      for (int i = 0; i < kDyChunks; ++i)
+#pragma unroll
+        for (int h = 0; h < kLd; ++h)
+          st.dy[i][h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      rd, ((px0 + 32 * i) * a.K + 8 * q8) * kEs + 16 * h, 0, 0));
+      const int h = ho + r - a.pad_h;
+      const bool row_ok = live && h >= 0 && h < a.H;
+      const unsigned char* xp = xg + kEs * ((int64_t)n * a.x_img + (int64_t)(row_ok ? h : 0) * a.W * a.C + x_col0);
+      const int w0 = wo0 - a.pad_w + s0;   // first staged X column (negative: padding, reads zero)
+      // The MFMAs use X columns up to w0 + npix + SB - 2; the loader chunks
+      // past them (the rest of 96 staged slots) read zero instead of memory.
+      const int x_used = (w0 + npix + SB - 1) * a.C * kEs;
+      const __amdgpu_buffer_rsrc_t rs = buf_rsrc(xp, row_ok ? max(0, min(x_row_bytes, x_used)) : 0);
+#pragma unroll
+      for (int i = 0; i < kXChunks; ++i)
+#pragma unroll
+        for (int hh = 0; hh < kLd; ++hh)
+          st.x[i][hh] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      rs, ((w0 + px0 + 32 * i) * a.C + 8 * q8) * kEs + 16 * hh, 0, 0));
     }
-    const int wc = u % a.wchunks;
-    const int t = u / a.wchunks;
-    const int ho = t % a.Ho, n = t / a.Ho;
-    const int wo0 = wc * a.wt;
-    const int npix = min(a.wt, a.Wo - wo0);
-    npix_next = npix;
-    const unsigned char* dyp = dyg + kEs * (((int64_t)(n * a.Ho + ho) * a.Wo + wo0) * a.K + dy_col0);
-    const __amdgpu_buffer_rsrc_t rd = buf_rsrc(dyp, (npix * a.K - dy_col0) * kEs);
-#pragma unroll
-    for (int i = 0; i < kDyChunks; ++i)
-#pragma unroll
-      for (int h = 0; h < kLd; ++h)
-        rdy[i][h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                  rd, ((px0 + 32 * i) * a.K + 8 * q8) * kEs + 16 * h, 0, 0));
-    const int h = ho + r - a.pad_h;
-    const bool row_ok = h >= 0 && h < a.H;
-    const unsigned char* xp = xg + kEs * ((int64_t)n * a.x_img + (int64_t)(row_ok ? h : 0) * a.W * a.C + x_col0);
-    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(xp, row_ok ? x_row_bytes : 0);
-    const int w0 = wo0 - a.pad_w + s0;   // first staged X column (negative: padding, reads zero)
-#pragma unroll
-    for (int i = 0; i < kXChunks; ++i)
-#pragma unroll
-      for (int hh = 0; hh < kLd; ++hh)
-        rx[i][hh] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                  rs, ((w0 + px0 + 32 * i) * a.C + 8 * q8) * kEs + 16 * hh, 0, 0));
   };
   // BF16x3: per-thread fp32 sums of the staged dY values (8 channels at 8 q8
   // for every loader pixel row), for the bias gradient.
   const bool db_x3 = kX3 && kDb && r == 0 && sb == 0 && ct == 0;
   float dbp[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  auto store_unit = [&](int buf) {
+  auto store_unit = [&](int buf, const Set& st) {
 #pragma unroll
     for (int i = 0; i < kDyChunks; ++i) {
       unsigned short* d = &s_dy[0][buf][(px0 + 32 * i) * kPitchE + 8 * q8];
       if constexpr (kX3) {
         uint4 hi, lo;
-        split_bf16x8(rdy[i][0], rdy[i][kLd - 1], hi, lo);
+        split_bf16x8(st.dy[i][0], st.dy[i][kLd - 1], hi, lo);
         *reinterpret_cast<uint4*>(d) = hi;
         *reinterpret_cast<uint4*>(&s_dy[kPlanes - 1][buf][(px0 + 32 * i) * kPitchE + 8 * q8]) = lo;
         if (db_x3) {
-          const uint32_t w[8] = {rdy[i][0].x, rdy[i][0].y, rdy[i][0].z, rdy[i][0].w,
-                                 rdy[i][kLd - 1].x, rdy[i][kLd - 1].y, rdy[i][kLd - 1].z, rdy[i][kLd - 1].w};
+          const uint32_t w[8] = {st.dy[i][0].x, st.dy[i][0].y, st.dy[i][0].z, st.dy[i][0].w,
+                                 st.dy[i][kLd - 1].x, st.dy[i][kLd - 1].y, st.dy[i][kLd - 1].z,
+                                 st.dy[i][kLd - 1].w};
 #pragma unroll
           for (int e = 0; e < 8; ++e) dbp[e] += __uint_as_float(w[e]);
         }
       } else {
-        *reinterpret_cast<uint4*>(d) = rdy[i][0];
+        *reinterpret_cast<uint4*>(d) = st.dy[i][0];
       }
     }
 #pragma unroll
-    for (int i = 0; i < kXChunks; ++i)
-      if (px0 + 32 * i < kXs) {
-        unsigned short* d = &s_x[0][buf][(px0 + 32 * i) * kPitchE + 8 * q8];
-        if constexpr (kX3) {
-          uint4 hi, lo;
-          split_bf16x8(rx[i][0], rx[i][kLd - 1], hi, lo);
-          *reinterpret_cast<uint4*>(d) = hi;
-          *reinterpret_cast<uint4*>(&s_x[kPlanes - 1][buf][(px0 + 32 * i) * kPitchE + 8 * q8]) = lo;
-        } else {
-          *reinterpret_cast<uint4*>(d) = rx[i][0];
-        }
+    for (int i = 0; i < kXChunks; ++i) {
+      unsigned short* d = &s_x[0][buf][(px0 + 32 * i) * kPitchE + 8 * q8];
+      if constexpr (kX3) {
+        uint4 hi, lo;
+        split_bf16x8(st.x[i][0], st.x[i][kLd - 1], hi, lo);
+        *reinterpret_cast<uint4*>(d) = hi;
+        *reinterpret_cast<uint4*>(&s_x[kPlanes - 1][buf][(px0 + 32 * i) * kPitchE + 8 * q8]) = lo;
+      } else {
+        *reinterpret_cast<uint4*>(d) = st.x[i][0];
       }
+    }
   };
 
   // Transposed-read addressing: in 16-lane group gq, lane j points at pixel
@@ -275,6 +311,10 @@ __global__ __launch_bounds__(256) void dense16_rows_kernel(R16Args a) {
   const s16x8 ones{(short)one, (short)one, (short)one, (short)one,
                    (short)one, (short)one, (short)one, (short)one};
 
+  // One unit's MFMAs: per 32-pixel k-step, the A and B operands by
+  // transposed LDS reads, then 4 * SB MFMAs (with BF16x3 the two cross terms,
+  // small, before hi * hi).  npix is workgroup-uniform, so a unit of at most
+  // 32 pixel slots skips the second k-step and a unit past the slice both.
   auto compute_unit = [&](int buf, int npix) {
     const unsigned short* ad = s_dy[0][buf] + lane_off;
     const unsigned short* bx = s_x[0][buf] + lane_off + 16 * wave;
@@ -289,7 +329,6 @@ __global__ __launch_bounds__(256) void dense16_rows_kernel(R16Args a) {
 #pragma unroll
         for (int s = 0; s < SB; ++s) fb[s] = tr8(bx + (32 * ks + s) * kPitchE);
         if constexpr (kX3) {
-          // The two cross terms first (small), then hi * hi.
           s16x8 fa_lo[4], fb_lo[SB];
 #pragma unroll
           for (int i = 0; i < 4; ++i) fa_lo[i] = tr8(ad_lo + 32 * ks * kPitchE + 16 * i);
@@ -317,14 +356,26 @@ __global__ __launch_bounds__(256) void dense16_rows_kernel(R16Args a) {
     }
   };
 
-  if (u_begin < u_end) load_unit(u_begin);
-  for (int u = u_begin; u < u_end; ++u) {
-    const int buf = (u - u_begin) & 1;
-    const int npix = npix_next;
-    store_unit(buf);
-    if (u + 1 < u_end) load_unit(u + 1);
-    __syncthreads();   // the unit is staged; every wave is done with the other buffer
-    compute_unit(buf, npix);
+  // Whole rounds of kSets units; the prologue issues the sets in the order
+  // the loop consumes them (pinned by scheduling barriers).
+  const int rounds = (u_end - u_begin + kSets - 1) / kSets;
+  Set sets[kSets];
+#pragma unroll
+  for (int p = 0; p < kSets; ++p) {
+    load_unit(u_begin + p, sets[p]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int it = 0; it < rounds; ++it) {
+#pragma unroll
+    for (int p = 0; p < kSets; ++p) {
+      const int u = u_begin + it * kSets + p;
+      const int buf = (it * kSets + p) & 1;
+      const int npix = sets[p].npix;
+      store_unit(buf, sets[p]);
+      load_unit(u + kSets, sets[p]);
+      __syncthreads();   // the unit is staged; every wave is done with the other buffer
+      compute_unit(buf, npix);
+    }
   }
 
   // acc[i][s][v] = dW[g*Kg + m0 + 16 i + 4 gq + v][(r*S + s0 + s)*Cg + c0 + 16 wave + j].
@@ -362,11 +413,18 @@ __global__ __launch_bounds__(256) void dense16_rows_kernel(R16Args a) {
   }
 }
 
+constexpr int kSetsDefault = 2;
+
 template <bool kBf16, int SB, bool kX3>
 hipError_t launch_sb(const R16Args& args, int64_t grid, hipStream_t stream) {
   const dim3 xcd_grid((unsigned)((grid + 7) / 8 * 8)), block(256);   // whole rounds over the 8 XCDs
-  if (args.dbo) return launch_kernel(dense16_rows_kernel<kBf16, SB, true, kX3>, xcd_grid, block, args, stream);
-  return launch_kernel(dense16_rows_kernel<kBf16, SB, false, kX3>, xcd_grid, block, args, stream);
+  constexpr int kS = kSetsDefault;
+  if (args.ru > 1) {
+    if (args.dbo) return launch_kernel(dense16_rows_kernel<kBf16, SB, true, kX3, true, kS>, xcd_grid, block, args, stream);
+    return launch_kernel(dense16_rows_kernel<kBf16, SB, false, kX3, true, kS>, xcd_grid, block, args, stream);
+  }
+  if (args.dbo) return launch_kernel(dense16_rows_kernel<kBf16, SB, true, kX3, false, kS>, xcd_grid, block, args, stream);
+  return launch_kernel(dense16_rows_kernel<kBf16, SB, false, kX3, false, kS>, xcd_grid, block, args, stream);
 }
 
 template <bool kBf16, bool kX3>
