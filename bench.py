@@ -365,8 +365,11 @@ def measure(wl, s, x, dy, args, hip, cold_reps, bias=False, opts=None):
 
     dbp = db.data_ptr() if bias else 0
 
-    def step(ev0=0, ev1=0):
-        if ev0 or ev1:
+    def step(ev0=0, ev1=0, whole=False):
+        if whole:
+            iga.conv_wgrad2_call_timed(d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(), dbp, wsp, ws_bytes, sp,
+                                       ev0, ev1)
+        elif ev0 or ev1:
             iga.conv_wgrad2_timed(d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(), dbp, wsp, ws_bytes, sp, ev0, ev1)
         else:
             iga.conv_wgrad2(d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(), dbp, wsp, ws_bytes, sp)
@@ -403,19 +406,32 @@ def measure(wl, s, x, dy, args, hip, cold_reps, bias=False, opts=None):
 
     # Cold calls: before each, a read of a clean 1 GiB buffer evicts the inputs
     # from the L2s and the MALL (queued just before the call, so the GPU never
-    # idles).  Series 1: events on the stream around the plain call (stage 1 +
-    # fold together, no dispatch events).  Series 2: the stage-1 dispatch alone.
+    # idles).  Series 1 (the cold figure): the whole call, from the start of
+    # its first kernel to the end of its last (stage 1 + fold + the gap
+    # between them), stamped by the dispatches themselves.  Series 2: events
+    # on the stream around the plain call (they add their own marker time,
+    # reported beside it as the floor of two markers with nothing between).
+    # Series 3: the stage-1 dispatch alone.
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     probe = torch.empty((), dtype=torch.float32, device=dev)
     e0, e1, e2, e3 = hip.event(), hip.event(), hip.event(), hip.event()
     torch.cuda.synchronize()
-    whole, stage1 = [], []
+    whole, stream_ev, floor, stage1 = [], [], [], []
+    for _ in range(cold_reps):
+        torch.amax(flush, dim=0, out=probe)
+        step(e0, e1, whole=True)
+        whole.append(hip.elapsed_ms(e0, e1))
     for _ in range(cold_reps):
         torch.amax(flush, dim=0, out=probe)
         hip.record(e0, sp)
         step()
         hip.record(e1, sp)
-        whole.append(hip.elapsed_ms(e0, e1))
+        stream_ev.append(hip.elapsed_ms(e0, e1))
+    for _ in range(min(cold_reps, 20)):
+        torch.amax(flush, dim=0, out=probe)
+        hip.record(e0, sp)
+        hip.record(e1, sp)
+        floor.append(hip.elapsed_ms(e0, e1))
     for _ in range(cold_reps):
         torch.amax(flush, dim=0, out=probe)
         step(e2, e3)
@@ -443,7 +459,10 @@ def measure(wl, s, x, dy, args, hip, cold_reps, bias=False, opts=None):
         "math": used_math, "fold_width": int(plan2.fold_width), "record": tag,
         "flops": s.flops(), "algorithmic_bytes": s.algorithmic_bytes(wd.IN_BYTES[wl.dtype]),
         "cold_call_us": {"median": round(cold_med * 1e6, 2), "min": round(min(whole) * 1e3, 2),
-                         "p90": round(_pct(whole, 0.9) * 1e3, 2), "calls": cold_reps},
+                         "p90": round(_pct(whole, 0.9) * 1e3, 2), "calls": cold_reps,
+                         "timing": "first kernel start to last kernel end, dispatch-stamped events"},
+        "cold_call_stream_events_us": round(statistics.median(stream_ev) * 1e3, 2) if stream_ev else None,
+        "stream_event_floor_us": round(statistics.median(floor) * 1e3, 2) if floor else None,
         "tflops": round(s.flops() / cold_med / 1e12, 3),
         "roofline": roofline_for(s, wl.dtype, cold_med, traffic, used_math),
         "stage1_cold_us": round(statistics.median(stage1) * 1e3, 2),

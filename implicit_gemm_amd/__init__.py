@@ -140,6 +140,8 @@ def load():
         f.restype = ctypes.c_int
         f.argtypes = [P(Desc2), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                       ctypes.c_size_t, ctypes.c_void_p]
+    lib.conv_wgrad2_call_timed.restype = ctypes.c_int
+    lib.conv_wgrad2_call_timed.argtypes = lib.conv_wgrad2_timed.argtypes
     lib.conv_wgrad_noalloc.restype = ctypes.c_int
     lib.conv_wgrad_noalloc.argtypes = [P(Desc), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p]
@@ -192,6 +194,15 @@ def conv_wgrad2_timed(desc: Desc2, x_ptr: int, dy_ptr: int, dw_ptr: int, db_ptr:
                                   ws_bytes, stream or None, ev_begin or None, ev_end or None)
     if st != 0:
         raise ConvWgradError(st, "conv_wgrad2_timed")
+
+
+def conv_wgrad2_call_timed(desc: Desc2, x_ptr: int, dy_ptr: int, dw_ptr: int, db_ptr: int, ws_ptr: int,
+                           ws_bytes: int, stream: int, ev_begin: int, ev_end: int) -> None:
+    """conv_wgrad2 whose first kernel stamps its start and last kernel its end into two HIP events."""
+    st = load().conv_wgrad2_call_timed(ctypes.byref(desc), x_ptr, dy_ptr, dw_ptr, db_ptr or None,
+                                       ws_ptr or None, ws_bytes, stream or None, ev_begin or None, ev_end or None)
+    if st != 0:
+        raise ConvWgradError(st, "conv_wgrad2_call_timed")
 
 
 def get_plan(desc: Desc) -> Plan:

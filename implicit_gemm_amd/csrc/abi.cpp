@@ -30,6 +30,14 @@ Stage1Events& stage1_events() {
 hipError_t launch_raw(const void* fn, dim3 grid, dim3 block, void** params, size_t shmem,
                       hipStream_t stream) {
   Stage1Events& ev = stage1_events();
+  if (ev.end_on_last) {
+    const hipEvent_t b = ev.begin;
+    const hipEvent_t e = --ev.launches_left == 0 ? ev.end : nullptr;
+    ev.begin = nullptr;
+    if (ev.launches_left <= 0) ev = Stage1Events{};
+    if (b || e) return hipExtLaunchKernel(fn, grid, block, params, shmem, stream, b, e, 0);
+    return hipLaunchKernel(fn, grid, block, params, shmem, stream);
+  }
   if (ev.begin || ev.end) {
     const Stage1Events use = ev;
     ev = Stage1Events{};
@@ -87,7 +95,8 @@ struct Desc2 {
 // with_db: the bias gradient is requested (db must then be a valid pointer).
 conv_wgrad_status_t run(const conv_wgrad_desc2_t* desc, const void* x, const void* dy, float* dw,
                         bool with_db, float* db, void* workspace, bool check_ws, size_t ws_bytes,
-                        void* stream, void* ev_begin = nullptr, void* ev_end = nullptr) {
+                        void* stream, void* ev_begin = nullptr, void* ev_end = nullptr,
+                        bool whole_call = false) {
   cw::Plan plan;
   conv_wgrad_status_t st = get_plan(desc, &plan);
   if (st != CONV_WGRAD_OK) return st;
@@ -112,13 +121,18 @@ conv_wgrad_status_t run(const conv_wgrad_desc2_t* desc, const void* x, const voi
   hipError_t err;
   // The stage-1 launch takes the events (timestamps of its own dispatch); the
   // guard clears them again whatever happens, so no later launch records them.
+  // Launches of this call: stage 1, then one fold pass (two beyond 256 slabs).
+  const int launches = 1 + (plan.pub.needs_reduce ? (plan.pub.ks_count > 256 ? 2 : 1) : 0);
   struct EventsGuard {
-    EventsGuard(void* b, void* e) {
-      cw::stage1_events().begin = static_cast<hipEvent_t>(b);
-      cw::stage1_events().end = static_cast<hipEvent_t>(e);
+    EventsGuard(void* b, void* e, bool whole, int launches) {
+      cw::Stage1Events& ev = cw::stage1_events();
+      ev.begin = static_cast<hipEvent_t>(b);
+      ev.end = static_cast<hipEvent_t>(e);
+      ev.end_on_last = whole && (b || e);
+      ev.launches_left = launches;
     }
     ~EventsGuard() { cw::stage1_events() = cw::Stage1Events{}; }
-  } guard(ev_begin, ev_end);
+  } guard(ev_begin, ev_end, whole_call, launches);
   switch (plan.pub.variant) {
     case cw::kDirectElem: err = cw::launch_direct(plan, x, dy, out, s); break;
     case cw::kGrouped16:
@@ -278,6 +292,13 @@ conv_wgrad_status_t conv_wgrad2_timed(const conv_wgrad_desc2_t* desc, const void
                                       void* stream, void* stage1_begin, void* stage1_end) {
   return run(desc, x, dy, dw, db != nullptr, db, workspace, true, ws_bytes, stream, stage1_begin,
              stage1_end);
+}
+
+conv_wgrad_status_t conv_wgrad2_call_timed(const conv_wgrad_desc2_t* desc, const void* x, const void* dy,
+                                           float* dw, float* db, void* workspace, size_t ws_bytes,
+                                           void* stream, void* call_begin, void* call_end) {
+  return run(desc, x, dy, dw, db != nullptr, db, workspace, true, ws_bytes, stream, call_begin, call_end,
+             true);
 }
 
 conv_wgrad_status_t conv_igemm_get_plan(const conv_wgrad_desc2_t* desc, int32_t direction,

@@ -19,11 +19,15 @@ struct Stage1Out {
   float* db = nullptr;   // bias-gradient partial of slice 0, or nullptr
 };
 
-// Events the next stage-1 launch on this thread records its own start and end
-// in (the dispatch's timestamps, not the stream position around it); set by
-// the timed entry point, consumed by launch_raw.
+// Events the launches of one call on this thread record in (the dispatches'
+// own timestamps, not the stream position around them); set by the timed
+// entry points, consumed by launch_raw.  Stage-1 timing: begin and end on the
+// first launch.  Call timing (end_on_last): begin at the start of the first
+// launch, end at the end of the launch that leaves launches_left at zero.
 struct Stage1Events {
   hipEvent_t begin = nullptr, end = nullptr;
+  bool end_on_last = false;
+  int launches_left = 0;
 };
 Stage1Events& stage1_events();
 

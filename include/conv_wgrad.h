@@ -308,6 +308,16 @@ conv_wgrad_status_t conv_wgrad2_timed(const conv_wgrad_desc2_t* desc, const void
                                       float* dw, float* db, void* workspace, size_t ws_bytes,
                                       void* stream, void* stage1_begin, void* stage1_end);
 
+/* Profiling variant of conv_wgrad2 that times the whole call on the GPU: the
+ * caller's events (hipEvent_t, either may be NULL) take the start timestamp of
+ * the call's first kernel (stage 1) and the end timestamp of its last kernel
+ * (the slab fold, or stage 1 with one slice), through hipExtLaunchKernel, so
+ * hipEventElapsedTime gives stage 1 + fold + the gap between them without any
+ * marker of its own.  Only recorded, never synchronised or destroyed. */
+conv_wgrad_status_t conv_wgrad2_call_timed(const conv_wgrad_desc2_t* desc, const void* x, const void* dy,
+                                           float* dw, float* db, void* workspace, size_t ws_bytes,
+                                           void* stream, void* call_begin, void* call_end);
+
 /*
  * Forward convolution and data gradient on the same implicit-GEMM, split-K
  * slab and fold machinery (rocm-libraries PR #14393 "split-K forward
