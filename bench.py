@@ -60,7 +60,7 @@ DEFAULT_CONFIG = "c2_3x3_f32"
 # planner it identifies the code a counter measurement was taken on.
 CSRC = os.path.join(ROOT, "implicit_gemm_amd", "csrc")
 VARIANT_SOURCE = {0: "dense_lds.hip", 1: "dense_rows.hip", 2: "dense_1x1.hip", 3: "dense16_rows.hip",
-                  4: "dense16_rows.hip",
+                  4: "dense16_rows.hip", 20: "conv_igemm.hip", 21: "conv_igemm.hip",
                   10: "direct_elem.hip",
                   11: "grouped16.hip", 12: "depthwise_mfma.hip", 13: "grouped16.hip"}
 SHARED_SOURCES = ("device_common.h", "kernels.h", "plan.h", "plan.cpp")
@@ -478,6 +478,38 @@ def measure(wl, s, x, dy, args, hip, cold_reps, bias=False, opts=None):
     return rec, wall, statistics.mean(k_ms) * 1e-3
 
 
+def cpu_baseline_igemm(wl, s, direction, seconds):
+    """The fp64 forward or data-gradient oracle on the host cores, on the first
+    images of the workload (as many as fit about seconds / 3 per run; at least
+    three runs and about `seconds` in all), in TFLOP/s."""
+    import oracle
+    import wgrad_data as wd
+    threads = oracle.default_threads()
+    w = wd.draw_filter(wl.seed, s.K, s.R, s.S, s.Cg, wd.Dist("normal", 0.05), wl.dtype)
+
+    def run(n):
+        x, dy = wd.make_inputs(wl, 0, n)
+        t0 = time.perf_counter()
+        if direction == "fwd":
+            oracle.fwd_ref(x, w, s.pad, s.stride, s.dilation, s.groups, nthreads=threads)
+        else:
+            oracle.dgrad_ref(dy, w, s.H, s.W, s.pad, s.stride, s.dilation, s.groups, nthreads=threads)
+        return time.perf_counter() - t0
+
+    t_img = max(run(1), 1e-6)
+    n_s = int(max(1, min(s.N, (seconds / 3.0) / t_img)))
+    times = []
+    while len(times) < 3 or (sum(times) < seconds and len(times) < 200):
+        times.append(run(n_s))
+    t = statistics.median(times)
+    per_image = s.flops() / s.N
+    what = "whole workload" if n_s == s.N else "first %d of %d images" % (n_s, s.N)
+    return {"value": round(per_image * n_s / t / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%s of %s (%s), median of %d runs, fp64 C oracle, %.2f s per run"
+                      % (what, wl.name, direction, len(times), t),
+            "cpu_model": cpu_model()}
+
+
 def measure_igemm(wl, s, args, hip, cold_reps, opts):
     """Time the forward convolution or the data gradient (conv_fwd / conv_dgrad) of a
     workload's shape: hot back-to-back calls and cold calls (stream events around
@@ -504,8 +536,12 @@ def measure_igemm(wl, s, args, hip, cold_reps, opts):
     sp = torch.cuda.current_stream(dev).cuda_stream
     f = iga.conv_fwd if direction == iga.DIRECTION_FWD else iga.conv_dgrad
 
-    def step():
-        f(d, src.data_ptr(), wt.data_ptr(), out.data_ptr(), ws.data_ptr() if ws_bytes else 0, ws_bytes, sp)
+    def step(ev0=0, ev1=0):
+        if ev0 or ev1:
+            iga.conv_igemm_call_timed(d, direction, src.data_ptr(), wt.data_ptr(), out.data_ptr(),
+                                      ws.data_ptr() if ws_bytes else 0, ws_bytes, sp, ev0, ev1)
+        else:
+            f(d, src.data_ptr(), wt.data_ptr(), out.data_ptr(), ws.data_ptr() if ws_bytes else 0, ws_bytes, sp)
 
     for _ in range(args.warmup):
         step()
@@ -520,15 +556,24 @@ def measure_igemm(wl, s, args, hip, cold_reps, opts):
         step()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
+    # Hot whole calls stamped by their own dispatches (GPU time of K calls).
+    evs = [(hip.event(), hip.event()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        step(a, b)
+    torch.cuda.synchronize()
+    k_ms = [hip.elapsed_ms(a, b) for a, b in evs]
+    for a, b in evs:
+        hip.destroy(a)
+        hip.destroy(b)
+    # Cold calls after a clean 1 GiB read, stamped the same way.
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     probe = torch.empty((), dtype=torch.float32, device=dev)
     e0, e1 = hip.event(), hip.event()
     whole = []
     for _ in range(cold_reps):
         torch.amax(flush, dim=0, out=probe)
-        hip.record(e0, sp)
-        step()
-        hip.record(e1, sp)
+        step(e0, e1)
         whole.append(hip.elapsed_ms(e0, e1))
     hip.destroy(e0)
     hip.destroy(e1)
@@ -536,8 +581,9 @@ def measure_igemm(wl, s, args, hip, cold_reps, opts):
     torch.cuda.synchronize()
     o = out.cpu().numpy()
     if not whole:   # --cold 0 (profiling runs): the hot figure stands in
-        whole = [wall * 1e3]
+        whole = k_ms
     cold_med = statistics.median(whole) * 1e-3
+    hot = statistics.mean(k_ms) * 1e-3
     esz = wd.IN_BYTES[wl.dtype]
     w_bytes = s.K * s.R * s.S * s.Cg * esz
     if direction == iga.DIRECTION_FWD:
@@ -549,17 +595,20 @@ def measure_igemm(wl, s, args, hip, cold_reps, opts):
     t_roof = max(flops / (peak_mfma * 1e12), nbytes / (PEAK["hbm_gbs"] * 1e9))
     bound = "mfma" if flops / (peak_mfma * 1e12) >= nbytes / (PEAK["hbm_gbs"] * 1e9) else "hbm"
 
+    tag = "%s+%s%s" % (wl.name, opts["direction"], "+split%d" % split_k if split_k >= 1 else "")
+    digest = source_digest(int(plan.variant))
+    traffic = measured_traffic(tag, digest, s.N)
+
     def roof(t):
         if bound == "mfma":
             a = flops / t / 1e12
             return {"bound": "mfma", "achieved": round(a, 2), "peak": peak_mfma, "unit": "TFLOP/s",
-                    "frac": round(a / peak_mfma, 4), "traffic": None,
+                    "frac": round(a / peak_mfma, 4), "traffic": traffic,
                     "note": "16-bit inputs are widened and multiplied on f32 MFMA"}
         a = nbytes / t / 1e9
         return {"bound": "hbm", "achieved": round(a, 1), "peak": PEAK["hbm_gbs"], "unit": "GB/s",
-                "frac": round(a / PEAK["hbm_gbs"], 4), "traffic": None}
+                "frac": round(a / PEAK["hbm_gbs"], 4), "traffic": traffic}
 
-    tag = "%s+%s%s" % (wl.name, opts["direction"], "+split%d" % split_k if split_k >= 1 else "")
     return {
         "workload": wl.name, "record": tag, "direction": opts["direction"], "note": wl.note, "dtype": wl.dtype,
         "N": s.N, "C": s.C, "H": s.H, "W": s.W, "K": s.K, "R": s.R, "S": s.S, "pad": s.pad,
@@ -567,11 +616,14 @@ def measure_igemm(wl, s, args, hip, cold_reps, opts):
         "kernel": "igemm_" + opts["direction"], "variant": int(plan.variant), "ks_count": int(plan.ks_count),
         "split_k": split_k, "fold_width": int(plan2.fold_width), "flops": flops, "algorithmic_bytes": nbytes,
         "cold_call_us": {"median": round(cold_med * 1e6, 2), "min": round(min(whole) * 1e3, 2),
-                         "p90": round(_pct(whole, 0.9) * 1e3, 2), "calls": cold_reps},
+                         "p90": round(_pct(whole, 0.9) * 1e3, 2), "calls": cold_reps,
+                         "timing": "first kernel start to last kernel end, dispatch-stamped events"},
         "tflops": round(flops / cold_med / 1e12, 3),
         "roofline": roof(cold_med),
-        "hot_call_us": round(wall * 1e6, 2), "hot_frac": roof(wall)["frac"], "hot_roofline": roof(wall),
+        "hot_call_us": round(hot * 1e6, 2), "hot_frac": roof(hot)["frac"], "hot_roofline": roof(hot),
+        "hot_wall_us": round(wall * 1e6, 2),
         "roofline_time_us": round(t_roof * 1e6, 2),
+        "source_digest": digest,
         "check": {"zeros": int((o == 0).sum()), "finite": bool(np.isfinite(o).all())},
     }
 
@@ -614,9 +666,13 @@ def main():
 
     if args.digest:
         wl, s = resolve(args.config, args.n) if args.config else resolve(*HEADLINE[:2])
-        d = iga.make_desc(s.N, s.C, s.H, s.W, s.K, s.R, s.S, s.pad, s.stride, s.dilation, s.groups,
-                          {"f32": 0, "bf16": 1, "f16": 2}[wl.dtype], args.split_k)
-        v = int(iga.get_plan(d).variant)
+        d = iga.make_desc2(s.N, s.C, s.H, s.W, s.K, s.R, s.S, s.pad, s.stride, s.dilation, s.groups,
+                           {"f32": 0, "bf16": 1, "f16": 2}[wl.dtype], args.split_k, args.math, args.fold_width)
+        if args.direction == "wgrad":
+            v = int(iga.get_plan2(d).base.variant)
+        else:
+            dirn = iga.DIRECTION_FWD if args.direction == "fwd" else iga.DIRECTION_DGRAD
+            v = int(iga.get_igemm_plan(d, dirn).base.variant)
         print(json.dumps({"workload": wl.name, "N": s.N, "variant": v, "source": VARIANT_SOURCE[v],
                           "digest": source_digest(v)}))
         return 0
@@ -662,6 +718,8 @@ def main():
         log("record", wl.name, s, wl.dtype, opts)
         if "direction" in opts:
             rec = measure_igemm(wl, s, args, hip, args.cold, opts)
+            if not args.no_cpu:
+                rec["cpu_baseline"] = cpu_baseline_igemm(wl, s, opts["direction"], 3.0)
             records.append(rec)
             log(json.dumps(rec))
             torch.cuda.empty_cache()

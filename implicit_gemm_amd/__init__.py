@@ -142,6 +142,10 @@ def load():
                       ctypes.c_size_t, ctypes.c_void_p]
     lib.conv_wgrad2_call_timed.restype = ctypes.c_int
     lib.conv_wgrad2_call_timed.argtypes = lib.conv_wgrad2_timed.argtypes
+    lib.conv_igemm_call_timed.restype = ctypes.c_int
+    lib.conv_igemm_call_timed.argtypes = [P(Desc2), ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p]
     lib.conv_wgrad_noalloc.restype = ctypes.c_int
     lib.conv_wgrad_noalloc.argtypes = [P(Desc), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p]
@@ -292,6 +296,15 @@ def conv_dgrad(desc: Desc2, dy_ptr: int, w_ptr: int, dx_ptr: int, ws_ptr: int, w
     st = load().conv_dgrad(ctypes.byref(desc), dy_ptr, w_ptr, dx_ptr, ws_ptr or None, ws_bytes, stream or None)
     if st != 0:
         raise ConvWgradError(st, "conv_dgrad")
+
+
+def conv_igemm_call_timed(desc: Desc2, direction: int, src_ptr: int, w_ptr: int, out_ptr: int, ws_ptr: int,
+                          ws_bytes: int, stream: int, ev_begin: int, ev_end: int) -> None:
+    """conv_fwd / conv_dgrad with the whole call's GPU time in two hipEvent_t handles."""
+    st = load().conv_igemm_call_timed(ctypes.byref(desc), direction, src_ptr, w_ptr, out_ptr, ws_ptr or None,
+                                      ws_bytes, stream or None, ev_begin or None, ev_end or None)
+    if st != 0:
+        raise ConvWgradError(st, "conv_igemm_call_timed")
 
 
 def _igemm_call(direction, src, w, out_shape, desc, split_k, stream, out):

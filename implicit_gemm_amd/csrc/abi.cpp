@@ -92,6 +92,26 @@ struct Desc2 {
   }
 };
 
+// Launches of one call: stage 1, then one fold pass (two beyond 256 slabs).
+int launches_of(const cw::Plan& plan) {
+  return 1 + (plan.pub.needs_reduce ? (plan.pub.ks_count > 256 ? 2 : 1) : 0);
+}
+
+// Timing events for the launches of one call: the stage-1 launch takes them
+// (timestamps of its own dispatch), or with `whole` the first launch takes the
+// begin event and the last the end event.  The destructor clears them again
+// whatever happens, so no later launch records them.
+struct EventsGuard {
+  EventsGuard(void* b, void* e, bool whole, int launches) {
+    cw::Stage1Events& ev = cw::stage1_events();
+    ev.begin = static_cast<hipEvent_t>(b);
+    ev.end = static_cast<hipEvent_t>(e);
+    ev.end_on_last = whole && (b || e);
+    ev.launches_left = launches;
+  }
+  ~EventsGuard() { cw::stage1_events() = cw::Stage1Events{}; }
+};
+
 // with_db: the bias gradient is requested (db must then be a valid pointer).
 conv_wgrad_status_t run(const conv_wgrad_desc2_t* desc, const void* x, const void* dy, float* dw,
                         bool with_db, float* db, void* workspace, bool check_ws, size_t ws_bytes,
@@ -119,20 +139,7 @@ conv_wgrad_status_t run(const conv_wgrad_desc2_t* desc, const void* x, const voi
     out.db = with_db ? db : nullptr;
   }
   hipError_t err;
-  // The stage-1 launch takes the events (timestamps of its own dispatch); the
-  // guard clears them again whatever happens, so no later launch records them.
-  // Launches of this call: stage 1, then one fold pass (two beyond 256 slabs).
-  const int launches = 1 + (plan.pub.needs_reduce ? (plan.pub.ks_count > 256 ? 2 : 1) : 0);
-  struct EventsGuard {
-    EventsGuard(void* b, void* e, bool whole, int launches) {
-      cw::Stage1Events& ev = cw::stage1_events();
-      ev.begin = static_cast<hipEvent_t>(b);
-      ev.end = static_cast<hipEvent_t>(e);
-      ev.end_on_last = whole && (b || e);
-      ev.launches_left = launches;
-    }
-    ~EventsGuard() { cw::stage1_events() = cw::Stage1Events{}; }
-  } guard(ev_begin, ev_end, whole_call, launches);
+  EventsGuard guard(ev_begin, ev_end, whole_call, launches_of(plan));
   switch (plan.pub.variant) {
     case cw::kDirectElem: err = cw::launch_direct(plan, x, dy, out, s); break;
     case cw::kGrouped16:
@@ -155,7 +162,8 @@ conv_wgrad_status_t run(const conv_wgrad_desc2_t* desc, const void* x, const voi
 // Forward / data gradient: validate, stage 1 (the implicit GEMM) and, with
 // several slices, the slab fold into the output, on the caller's stream.
 conv_wgrad_status_t run_igemm(const conv_wgrad_desc2_t* desc, int32_t direction, const void* a_src,
-                              const void* w, float* out, void* workspace, size_t ws_bytes, void* stream) {
+                              const void* w, float* out, void* workspace, size_t ws_bytes, void* stream,
+                              void* ev_begin = nullptr, void* ev_end = nullptr) {
   cw::Plan plan;
   conv_wgrad_status_t st = get_plan(desc, &plan, direction);
   if (st != CONV_WGRAD_OK) return st;
@@ -174,6 +182,7 @@ conv_wgrad_status_t run_igemm(const conv_wgrad_desc2_t* desc, int32_t direction,
     o.base = out;
     o.slab_stride = 0;
   }
+  EventsGuard guard(ev_begin, ev_end, true, launches_of(plan));
   if (cw::launch_igemm(plan, a_src, w, o, s) != hipSuccess) return CONV_WGRAD_ERR_HIP;
   if (plan.pub.needs_reduce &&
       cw::launch_slab_reduce(plan, static_cast<float*>(workspace), out, nullptr, s) != hipSuccess)
@@ -333,6 +342,14 @@ conv_wgrad_status_t conv_fwd(const conv_wgrad_desc2_t* desc, const void* x, cons
 conv_wgrad_status_t conv_dgrad(const conv_wgrad_desc2_t* desc, const void* dy, const void* w, float* dx,
                                void* workspace, size_t ws_bytes, void* stream) {
   return run_igemm(desc, CONV_DIRECTION_DGRAD, dy, w, dx, workspace, ws_bytes, stream);
+}
+
+conv_wgrad_status_t conv_igemm_call_timed(const conv_wgrad_desc2_t* desc, int32_t direction,
+                                          const void* src, const void* w, float* out, void* workspace,
+                                          size_t ws_bytes, void* stream, void* call_begin,
+                                          void* call_end) {
+  if (direction != CONV_DIRECTION_FWD && direction != CONV_DIRECTION_DGRAD) return CONV_WGRAD_ERR_BAD_DTYPE;
+  return run_igemm(desc, direction, src, w, out, workspace, ws_bytes, stream, call_begin, call_end);
 }
 
 }  // extern "C"

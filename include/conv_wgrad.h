@@ -369,6 +369,16 @@ conv_wgrad_status_t conv_fwd(const conv_wgrad_desc2_t* desc, const void* x, cons
 conv_wgrad_status_t conv_dgrad(const conv_wgrad_desc2_t* desc, const void* dy, const void* w, float* dx,
                                void* workspace, size_t ws_bytes, void* stream);
 
+/* Profiling variant of conv_fwd (direction FWD: src = x, out = y) and
+ * conv_dgrad (DGRAD: src = dy, out = dx) that times the whole call on the
+ * GPU as conv_wgrad2_call_timed does: call_begin takes the start timestamp of
+ * the implicit GEMM's dispatch, call_end the end timestamp of the call's last
+ * kernel (either may be NULL; only recorded).  Another direction: BAD_DTYPE. */
+conv_wgrad_status_t conv_igemm_call_timed(const conv_wgrad_desc2_t* desc, int32_t direction,
+                                          const void* src, const void* w, float* out, void* workspace,
+                                          size_t ws_bytes, void* stream, void* call_begin,
+                                          void* call_end);
+
 /*
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): conv_wgrad_bias

@@ -23,7 +23,7 @@ PUBLIC_FUNCTIONS = {"conv_wgrad", "conv_wgrad_ex", "conv_wgrad_get_plan", "conv_
                     "conv_wgrad_status_string", "conv_wgrad_workspace_size", "conv_wgrad_bias",
                     "conv_wgrad_bias_timed", "conv_wgrad_noalloc", "conv_wgrad2_workspace_size",
                     "conv_wgrad2_get_plan", "conv_wgrad2", "conv_wgrad2_timed", "conv_wgrad2_call_timed", "conv_igemm_get_plan",
-                    "conv_igemm_workspace_size", "conv_fwd", "conv_dgrad"}
+                    "conv_igemm_workspace_size", "conv_fwd", "conv_dgrad", "conv_igemm_call_timed"}
 
 
 def declared_functions(header=HEADER, prefix="conv_"):
