@@ -636,7 +636,7 @@ def main():
     ap.add_argument("--config", default=None, help="only this workload (default: all, headline 1x1 N=192)")
     ap.add_argument("--split-k", type=int, default=-1)
     ap.add_argument("--n", type=int, default=0, help="batch of an N-swept workload (default 64)")
-    ap.add_argument("--cold", type=int, default=50, help="cold-cache calls per series (1x1 512x512: 5)")
+    ap.add_argument("--cold", type=int, default=50, help="cold-cache calls per series (1x1 512x512: at most 15)")
     ap.add_argument("--prewarm-s", type=float, default=0.3,
                     help="seconds of untimed steps after the warm-up steps (clock ramp)")
     ap.add_argument("--no-cpu", action="store_true")
@@ -709,7 +709,7 @@ def main():
         head_name, head_n, head_opts = HEADLINE
 
     def cold_reps_for(s):
-        return 5 if s.flops() > 1e11 else args.cold
+        return min(args.cold, 15) if s.flops() > 1e11 else args.cold
 
     big = None   # device inputs of the N-swept workload at the headline batch, shared by its records
     hwl, hs = resolve(head_name, head_n)

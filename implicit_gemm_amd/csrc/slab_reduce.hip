@@ -10,15 +10,19 @@
 // both ranges are folded the same way.
 //
 // One fold pass sums, for every output group o, the input slabs
-// [o*G, min(n, (o+1)*G)).  A workgroup owns 16 element chunks (4 floats
-// each) of one group; the group's slabs are cut into kParts consecutive
-// parts, lane (chunk, part) sums its part left to right with all its loads in
-// flight, and part sums are then added in ascending part order through LDS:
+// [o*G, min(n, (o+1)*G)).  The group's slabs are cut into P consecutive parts
+// (P = 1 for G <= 16, 4 for G <= 32, else 16); a workgroup owns 256 / P
+// element chunks (4 floats each), lane (chunk, part) sums its part left to
+// right with its loads in flight, and part sums are then added in ascending
+// part order through LDS:
 //   out = ((sum(part 0) + sum(part 1)) + sum(part 2)) + ...
-// With at most 256 slabs a single pass writes dw; with more, a first pass
-// folds runs of 32 slabs into the first slab of each run and a second pass
-// folds those run sums.  The order depends only on the slab count, so the
-// result is bit-identical from run to run.
+// Few slabs thus take one part and 1024 elements per workgroup: a fold of a
+// large output over a handful of slabs is not split into tens of thousands
+// of workgroups that each read a few lines.  With at most 256 slabs a single
+// pass writes dw; with more, a first pass folds runs of 32 slabs into the
+// first slab of each run and a second pass folds those run sums.  The order
+// depends only on the slab count, so the result is bit-identical from run to
+// run.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -26,11 +30,10 @@ namespace cw {
 
 namespace {
 
-constexpr int kParts = 16;        // lanes sharing one element chunk
-constexpr int kChunks = 16;       // element chunks per workgroup (256 lanes)
+constexpr int kLanes = 256;
 constexpr int kRun = 32;          // slabs per run in the first of two passes
 constexpr int kMaxSinglePass = 256;
-constexpr int kBatch = 8;         // loads issued before their adds
+
 
 struct FoldArgs {
   const float* src;   // input slab 0
@@ -53,7 +56,11 @@ __device__ __forceinline__ float4 add4(float4 a, float4 b) {
   return float4{a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w};
 }
 
-__global__ __launch_bounds__(256) void slab_fold_kernel(FoldArgs a) {
+// kParts lanes share one element chunk; kLanes / kParts chunks per workgroup.
+template <int kParts>
+__global__ __launch_bounds__(kLanes) void slab_fold_kernel(FoldArgs a) {
+  constexpr int kChunks = kLanes / kParts;
+  constexpr int kBatch = kParts == 1 ? 16 : 8;   // loads issued before their adds
   __shared__ float4 part_sum[kParts][kChunks];
   __shared__ int part_len[kParts];
   const int c = threadIdx.x % kChunks, p = threadIdx.x / kChunks;
@@ -96,14 +103,20 @@ __global__ __launch_bounds__(256) void slab_fold_kernel(FoldArgs a) {
       acc = float4{t[0], t[1], t[2], t[3]};
     }
   }
-  part_sum[p][c] = acc;
-  __syncthreads();  // every read of this group's slabs is done before the in-place store below
+  float4 r = acc;
+  if constexpr (kParts > 1) {
+    part_sum[p][c] = acc;
+    __syncthreads();  // every read of this group's slabs is done before the in-place store below
+    if (p == 0 && i < E) {
+      int q = 0;
+      while (part_len[q] == 0) ++q;  // the group has >= 1 slab, so some part is non-empty
+      r = part_sum[q][c];
+      for (++q; q < kParts; ++q)
+        if (part_len[q] > 0) r = add4(r, part_sum[q][c]);
+    }
+  }
+  // One part: the lane's own sum is the result (it has read all its slabs).
   if (p == 0 && i < E) {
-    int q = 0;
-    while (part_len[q] == 0) ++q;  // the group has >= 1 slab, so some part is non-empty
-    float4 r = part_sum[q][c];
-    for (++q; q < kParts; ++q)
-      if (part_len[q] > 0) r = add4(r, part_sum[q][c]);
     float* d = dst + (int64_t)o * a.dst_step + i;
     if (full) {
       *reinterpret_cast<float4*>(d) = r;  // dw and the slabs are 16-byte aligned
@@ -114,12 +127,19 @@ __global__ __launch_bounds__(256) void slab_fold_kernel(FoldArgs a) {
   }
 }
 
-hipError_t fold(FoldArgs a, int outputs, hipStream_t stream) {
-  const int64_t per_block = 4 * kChunks;
+template <int kParts>
+hipError_t fold_p(FoldArgs a, int outputs, hipStream_t stream) {
+  const int64_t per_block = 4 * (kLanes / kParts);
   a.nb1 = (int32_t)ceil_div(a.E, per_block);
   const int64_t nb2 = a.E2 > 0 ? ceil_div(a.E2, per_block) : 0;
   const dim3 grid((unsigned)(a.nb1 + nb2), (unsigned)outputs);
-  return launch_kernel(slab_fold_kernel, grid, dim3(256), a, stream);
+  return launch_kernel(slab_fold_kernel<kParts>, grid, dim3(kLanes), a, stream);
+}
+
+hipError_t fold(FoldArgs a, int outputs, hipStream_t stream) {
+  if (a.group <= 16) return fold_p<1>(a, outputs, stream);
+  if (a.group <= 32) return fold_p<4>(a, outputs, stream);
+  return fold_p<16>(a, outputs, stream);
 }
 
 }  // namespace
