@@ -15,13 +15,20 @@
 //     v_mfma_f32_16x16x4_f32 accumulators (all 64 output channels x 16 input
 //     channels) are fed per 4 reduction rows by one 16-byte read of 4 dY
 //     channels and SB reads of X;
-//   * ping-pong: the workgroup has two halves of four waves (one wave of each
-//     per SIMD) that take alternate units of the slice, each with its own LDS
-//     buffer.  Phases separated by workgroup barriers alternate the roles, so
-//     while one half stages its next unit (global loads issued two phases
-//     ahead, fp32 widening, LDS stores) the other half's MFMAs run on the same
-//     SIMDs.  At the end the halves' accumulators are added (half 1 into
-//     half 0, a fixed order) and half 0 writes the slab.
+//   * two workgroup shapes keep the MFMA pipe busy while units are staged:
+//     - 256 lanes (four waves, the planner's choice when the split gives at
+//       least 1.5 workgroups per CU): two workgroups share a CU, each stages
+//       a unit (the loads of the next one are issued right after), waits at a
+//       barrier, computes it and waits again; the CU interleaves the two
+//       workgroups, so one's staging and barriers overlap the other's MFMAs
+//       and the two waves per SIMD hide each other's LDS reads;
+//     - 512 lanes (one workgroup per CU): two halves of four waves (one wave
+//       of each per SIMD) take alternate units of the slice, each with its own
+//       LDS buffer.  Phases separated by workgroup barriers alternate the
+//       roles, so while one half stages its next unit (global loads issued two
+//       phases ahead, fp32 widening, LDS stores) the other half's MFMAs run on
+//       the same SIMDs.  At the end the halves' accumulators are added (half 1
+//       into half 0, a fixed order) and half 0 writes the slab.
 //
 // Rows of the LDS tiles are 80 floats apart (16 mod 32 and 16 mod 64 banks),
 // so the 4 pixel rows a wave reads per MFMA fall in disjoint bank groups.
@@ -54,8 +61,9 @@ struct RowsArgs {
 
 // kUnit: column stride 1 and column dilation 1 are compile-time (every LDS offset of the
 // MFMA loop is an immediate); otherwise they are read from the arguments.
-template <typename T, int SB, bool kUnit>
-__global__ __launch_bounds__(512, 1) void dense_rows_kernel(RowsArgs a) {
+// kSolo: the 256-lane form (no halves); otherwise 512 lanes in two halves.
+template <typename T, int SB, bool kUnit, bool kSolo>
+__global__ __launch_bounds__(kSolo ? 256 : 512, kSolo ? 2 : 1) void dense_rows_kernel(RowsArgs a) {
   extern __shared__ float smem[];
   constexpr int kBuf = (kMaxWt + kMaxXSpan) * kPitch;  // floats per half's buffer
   const T* __restrict__ x = static_cast<const T*>(a.x);
@@ -64,7 +72,7 @@ __global__ __launch_bounds__(512, 1) void dense_rows_kernel(RowsArgs a) {
   // The half index is wave-uniform; readfirstlane lets the compiler keep the
   // values derived from it (unit indices, buffer resources) in SGPRs.
   const int tid = threadIdx.x & 255;
-  const int half = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);
+  const int half = kSolo ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);
   const int lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
   // Work item w = slice * tiles + tile.  Workgroups are dispatched to the 8
@@ -200,50 +208,69 @@ __global__ __launch_bounds__(512, 1) void dense_rows_kernel(RowsArgs a) {
     }
   };
 
-  // Half h takes units h, h + 2, ... of the slice.  In phase p the half with
-  // parity p stages unit p and the other half computes unit p - 1; a
-  // workgroup barrier ends every phase.
-  if (half < nu) load_unit(u_begin + half);
-  int npix_cur = 0;
-  for (int p = 0; p <= nu; ++p) {
-    const bool stage = (p & 1) == half && p < nu;
-    const bool comp = (p & 1) != half && p >= 1;
-    if (stage) {
-      npix_cur = npix_reg;
+  if constexpr (kSolo) {
+    // Unit by unit: stage it (its loads were issued one unit earlier), issue
+    // the next unit's loads, compute it; the second barrier keeps the next
+    // staging off the buffer until every wave has read it.
+    if (nu > 0) load_unit(u_begin);
+    for (int p = 0; p < nu; ++p) {
+      const int npix = npix_reg;
       store_unit();
-      if (p + 2 < nu) load_unit(u_begin + p + 2);
+      if (p + 1 < nu) load_unit(u_begin + p + 1);
+      __syncthreads();
+      compute_unit(npix);
+      __syncthreads();
     }
-    // Called on every phase (with no pixels when staging) so that the
-    // accumulators take one path through the loop.
-    compute_unit(comp ? npix_cur : 0);
+    if (want_db)   // 16 loader rows per channel quad
+      block_sum64<16, 4>(smem, p0, 4 * q, dbp,
+                         a.dbo + (int64_t)slice * a.slab_stride + (int64_t)g * a.Kg + m0,
+                         min(64, a.Kg - m0));
+  } else {
+    // Half h takes units h, h + 2, ... of the slice.  In phase p the half with
+    // parity p stages unit p and the other half computes unit p - 1; a
+    // workgroup barrier ends every phase.
+    if (half < nu) load_unit(u_begin + half);
+    int npix_cur = 0;
+    for (int p = 0; p <= nu; ++p) {
+      const bool stage = (p & 1) == half && p < nu;
+      const bool comp = (p & 1) != half && p >= 1;
+      if (stage) {
+        npix_cur = npix_reg;
+        store_unit();
+        if (p + 2 < nu) load_unit(u_begin + p + 2);
+      }
+      // Called on every phase (with no pixels when staging) so that the
+      // accumulators take one path through the loop.
+      compute_unit(comp ? npix_cur : 0);
+      __syncthreads();
+    }
+
+    // Bias partial: rows are the 16 loader rows of half 0, then those of half 1.
+    if (want_db)
+      block_sum64<32, 4>(smem, 16 * half + p0, 4 * q, dbp,
+                         a.dbo + (int64_t)slice * a.slab_stride + (int64_t)g * a.Kg + m0,
+                         min(64, a.Kg - m0));
+
+    // Half 1 hands its accumulators to half 0 through LDS (both buffers are
+    // free after the last barrier); half 0 adds them and writes the slab.
+    float* xfer = smem + tid;
+    if (half == 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int s = 0; s < SB; ++s)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) xfer[((i * SB + s) * 4 + v) * 256] = acc[i][s][v];
+    }
     __syncthreads();
-  }
-
-  // Bias partial: rows are the 16 loader rows of half 0, then those of half 1.
-  if (want_db)
-    block_sum64<32, 4>(smem, 16 * half + p0, 4 * q, dbp,
-                       a.dbo + (int64_t)slice * a.slab_stride + (int64_t)g * a.Kg + m0,
-                       min(64, a.Kg - m0));
-
-  // Half 1 hands its accumulators to half 0 through LDS (both buffers are
-  // free after the last barrier); half 0 adds them and writes the slab.
-  float* xfer = smem + tid;
-  if (half == 1) {
+    if (half == 1) return;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int s = 0; s < SB; ++s)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) xfer[((i * SB + s) * 4 + v) * 256] = acc[i][s][v];
+        for (int v = 0; v < 4; ++v) acc[i][s][v] += xfer[((i * SB + s) * 4 + v) * 256];
   }
-  __syncthreads();
-  if (half == 1) return;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int s = 0; s < SB; ++s)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc[i][s][v] += xfer[((i * SB + s) * 4 + v) * 256];
 
   float* out = a.out + (int64_t)slice * a.slab_stride;
   const int c = c0 + 16 * wave + li;
@@ -261,28 +288,37 @@ __global__ __launch_bounds__(512, 1) void dense_rows_kernel(RowsArgs a) {
       }
 }
 
-template <typename T, int SB, bool kUnit>
+template <typename T, int SB, bool kUnit, bool kSolo>
 hipError_t launch_sb(const RowsArgs& args, int64_t grid, hipStream_t stream) {
-  constexpr size_t kLds = 2 * (kMaxWt + kMaxXSpan) * kPitch * sizeof(float);
-  const void* fn = reinterpret_cast<const void*>(dense_rows_kernel<T, SB, kUnit>);
+  // One staging buffer (256 lanes) or one per half (512 lanes).
+  constexpr size_t kLds = (kSolo ? 1 : 2) * (kMaxWt + kMaxXSpan) * kPitch * sizeof(float);
+  const void* fn = reinterpret_cast<const void*>(dense_rows_kernel<T, SB, kUnit, kSolo>);
   // More than 64 KB of dynamic LDS must be enabled per kernel (once).
-  static const hipError_t attr =
-      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
-  if (attr != hipSuccess) return attr;
+  if (kLds > 64 * 1024) {
+    static const hipError_t attr =
+        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+    if (attr != hipSuccess) return attr;
+  }
   void* params[] = {const_cast<RowsArgs*>(&args)};
   const int64_t xcd_grid = (grid + 7) / 8 * 8;   // whole rounds over the 8 XCDs
-  return launch_raw(fn, dim3((unsigned)xcd_grid), dim3(512), params, kLds, stream);
+  return launch_raw(fn, dim3((unsigned)xcd_grid), dim3(kSolo ? 256 : 512), params, kLds, stream);
+}
+
+template <typename T, bool kUnit, bool kSolo>
+hipError_t launch_s(const Plan& plan, const RowsArgs& args, hipStream_t stream) {
+  const int64_t grid = plan.pub.grid;
+  switch (plan.sb) {
+    case 1: return launch_sb<T, 1, kUnit, kSolo>(args, grid, stream);
+    case 2: return launch_sb<T, 2, kUnit, kSolo>(args, grid, stream);
+    case 3: return launch_sb<T, 3, kUnit, kSolo>(args, grid, stream);
+    default: return launch_sb<T, 4, kUnit, kSolo>(args, grid, stream);
+  }
 }
 
 template <typename T, bool kUnit>
 hipError_t launch_u(const Plan& plan, const RowsArgs& args, hipStream_t stream) {
-  const int64_t grid = plan.pub.grid;
-  switch (plan.sb) {
-    case 1: return launch_sb<T, 1, kUnit>(args, grid, stream);
-    case 2: return launch_sb<T, 2, kUnit>(args, grid, stream);
-    case 3: return launch_sb<T, 3, kUnit>(args, grid, stream);
-    default: return launch_sb<T, 4, kUnit>(args, grid, stream);
-  }
+  if (plan.threads == 256) return launch_s<T, kUnit, true>(plan, args, stream);
+  return launch_s<T, kUnit, false>(plan, args, stream);
 }
 
 template <typename T>

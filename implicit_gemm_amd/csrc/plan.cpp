@@ -509,8 +509,24 @@ conv_wgrad_status_t make_plan(const conv_wgrad_desc2_t* desc, Plan* out) {
     if (!mul4(p.groups, out->m_tiles, p.R, out->s_blocks, &tiles) ||
         !mul_ok(tiles, out->c_tiles, &tiles))
       return CONV_WGRAD_ERR_UNSUPPORTED;
-    // One 256-lane workgroup per CU (256 CUs); slabs may cost up to the
-    // algorithmic bytes, since this kernel is MFMA-bound on the shapes it takes.
+    // Two workgroup shapes (Plan::threads).  256 lanes, two workgroups per
+    // CU, each staging and computing its own units: the CU interleaves the
+    // two, so one's staging and barriers overlap the other's MFMAs and two
+    // waves per SIMD keep the MFMA pipe fed (3x3 fp32 C=K=64 56x56 N=32: 75.6
+    // -> 71.9 us), taken when the split gives at least 1.5 workgroups per CU.
+    // Otherwise 512 lanes, one workgroup per CU, whose two halves ping-pong
+    // (one stages while the other computes): with few units the 256-lane form
+    // would leave half of each CU idle (3x3 C=K=512 14x14 N=8, 192 tiles and
+    // one slice: 126 us ping-pong, 158 us with 256 lanes).  Slabs may cost up
+    // to the algorithmic bytes, since this kernel is MFMA-bound on the shapes
+    // it takes.
+    conv_wgrad_status_t st = choose_split(units, tiles, desc->split_k, 2, 512, 1, p, &pub);
+    if (st != CONV_WGRAD_OK) return st;
+    if (pub.grid >= 384) {
+      out->threads = 256;
+      return CONV_WGRAD_OK;
+    }
+    out->threads = 512;
     return choose_split(units, tiles, desc->split_k, 2, 256, 1, p, &pub);
   }
   pub.variant = kDenseLds;

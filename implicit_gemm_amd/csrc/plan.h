@@ -62,8 +62,10 @@ struct Plan {
   int32_t ru, xrows;       // grouped16: output rows per unit, staged X rows
   // Depthwise: staged X row length (elements), LDS bytes, column of dY element 0.
   int32_t dw_xl, dw_lds, dw_off;
-  // Direct path.
-  int32_t threads;         // lanes per workgroup
+  // Direct path: lanes per workgroup.  Row-unit dense kernel: 256 (two
+  // workgroups per CU, each stages and computes its own units) or 512 (one
+  // workgroup per CU in two ping-pong halves).
+  int32_t threads;
 };
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -262,8 +262,12 @@ def test_split_pinning_and_auto():
     # More slices than units: every slice keeps at least one unit.
     p = iga.get_plan(D(N=1, H=2, W=2, R=1, S=1, pad=0, split_k=1000))
     assert p.ks_count == p.units
+    # Auto: the row kernel's 256-lane form (two workgroups per CU) when the
+    # split reaches 1.5 workgroups per CU, else the 512-lane form (one per CU).
     pa = iga.get_plan(D(N=32, C=64, H=56, W=56, K=64, split_k=-1))
-    assert pa.ks_count >= 1 and 128 <= pa.grid <= 256  # about one workgroup per CU
+    assert pa.variant == 1 and 384 <= pa.grid <= 512
+    pb = iga.get_plan(D(N=8, C=512, H=14, W=14, K=512, split_k=-1))
+    assert pb.variant == 1 and pb.grid < 384 and pb.grid <= 256
 
 
 def test_one_hip_runtime_when_the_library_loads_first():
