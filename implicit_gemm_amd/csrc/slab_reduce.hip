@@ -11,7 +11,7 @@
 //
 // One fold pass sums, for every output group o, the input slabs
 // [o*G, min(n, (o+1)*G)).  The group's slabs are cut into P consecutive parts
-// (P = 1 for G <= 16, 4 for G <= 32, else 16); a workgroup owns 256 / P
+// (P = 1 for G <= 16, 4 for G <= 32, else 8); a workgroup owns 256 / P
 // element chunks (4 floats each), lane (chunk, part) sums its part left to
 // right with its loads in flight, and part sums are then added in ascending
 // part order through LDS:
@@ -60,7 +60,7 @@ __device__ __forceinline__ float4 add4(float4 a, float4 b) {
 template <int kParts>
 __global__ __launch_bounds__(kLanes) void slab_fold_kernel(FoldArgs a) {
   constexpr int kChunks = kLanes / kParts;
-  constexpr int kBatch = kParts == 1 ? 16 : 8;   // loads issued before their adds
+  constexpr int kBatch = kParts == 4 ? 8 : 16;   // loads issued before their adds
   __shared__ float4 part_sum[kParts][kChunks];
   __shared__ int part_len[kParts];
   const int c = threadIdx.x % kChunks, p = threadIdx.x / kChunks;
@@ -139,7 +139,7 @@ hipError_t fold_p(FoldArgs a, int outputs, hipStream_t stream) {
 hipError_t fold(FoldArgs a, int outputs, hipStream_t stream) {
   if (a.group <= 16) return fold_p<1>(a, outputs, stream);
   if (a.group <= 32) return fold_p<4>(a, outputs, stream);
-  return fold_p<16>(a, outputs, stream);
+  return fold_p<8>(a, outputs, stream);
 }
 
 }  // namespace
