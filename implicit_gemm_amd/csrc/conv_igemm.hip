@@ -111,11 +111,41 @@ __global__ __launch_bounds__(256) void igemm_kernel(IgemmArgs a) {
       const int hn = py[i] + a.pad_h - r * a.dil_h;
       const int wn = px[i] + a.pad_w - s * a.dil_w;
       if (hn < 0 || wn < 0) return -1;
-      const int ho = hn / a.stride_h, wo = wn / a.stride_w;
-      if (ho * a.stride_h != hn || wo * a.stride_w != wn || ho >= a.Ho || wo >= a.Wo) return -1;
+      // Unit strides (a workgroup-uniform test) skip the two divisions.
+      int ho = hn, wo = wn;
+      if (a.stride_h != 1 || a.stride_w != 1) {
+        ho = hn / a.stride_h;
+        wo = wn / a.stride_w;
+        if (ho * a.stride_h != hn || wo * a.stride_w != wn) return -1;
+      }
+      if (ho >= a.Ho || wo >= a.Wo) return -1;
       return (ho * a.Wo + wo) * stride_src + ch_base + ch;
     }
   };
+
+  // Reduction cursors: the steps visit q0 = q_begin, q_begin + 32, ... in
+  // order, so the (channel, tap) of a thread's entries advance by 32 channels
+  // per step with carries instead of two divisions per step (the VALU work of
+  // the divisions does not overlap the MFMAs).
+  // A (VA == 4): entry q_begin + 4*q4 as (ca, sa, ra_) = (channel, s, r).
+  int ca = 0, sa = 0, ra_ = 0;
+  if (VA == 4) {
+    const int q = q_begin + 4 * q4;
+    ca = q % ch_per;
+    const int rs = q / ch_per;
+    sa = rs % a.S;
+    ra_ = rs / a.S;
+  }
+  // dgrad B: entries q_begin + ql + 16*i as (k, r*S + s).
+  int kb[2] = {0, 0}, rsb[2] = {0, 0};
+  if constexpr (!kFwd) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = q_begin + (tid >> 4) + 16 * i;
+      kb[i] = q % a.Kg;
+      rsb[i] = q / a.Kg;
+    }
+  }
 
   auto load_step = [&](int q0) {
     // A: entries q .. q + 3 of the two rows.
@@ -123,9 +153,15 @@ __global__ __launch_bounds__(256) void igemm_kernel(IgemmArgs a) {
     if (VA == 4) {
       // ch_per % 4 == 0: the four entries share one tap.
       const bool qv = q < q_end;
-      const int qq = qv ? q : 0;
-      const int ch = qq % ch_per, rs = qq / ch_per;
-      const int s = rs % a.S, r = rs / a.S;
+      const int ch = ca, s = sa, r = ra_;
+      ca += kBK;
+      while (ca >= ch_per) {
+        ca -= ch_per;
+        if (++sa == a.S) {
+          sa = 0;
+          ++ra_;
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int off = qv ? a_offset(i, r, s, ch) : -1;
@@ -178,9 +214,13 @@ __global__ __launch_bounds__(256) void igemm_kernel(IgemmArgs a) {
       for (int i = 0; i < 2; ++i) {
         const int qe = q0 + ql + 16 * i;
         const bool qv = qe < q_end;
-        const int qq = qv ? qe : 0;
-        const int k = qq % a.Kg, rs = qq / a.Kg;     // q = (r, s, k): W[g*Kg + k][r][s][.]
-        const T* wr = wt + ((int64_t)(g * a.Kg + k) * a.R * a.S + rs) * a.Cg;
+        const int k = kb[i], rs = rsb[i];     // q = (r, s, k): W[g*Kg + k][r][s][.]
+        kb[i] += kBK;
+        while (kb[i] >= a.Kg) {
+          kb[i] -= a.Kg;
+          ++rsb[i];
+        }
+        const T* wr = wt + ((int64_t)(g * a.Kg + (qv ? k : 0)) * a.R * a.S + (qv ? rs : 0)) * a.Cg;
         if (VB == 4) {
           if (qv && n < a.Cg) {
             load4(wr + n, rb[i]);
