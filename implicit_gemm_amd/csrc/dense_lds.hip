@@ -80,6 +80,18 @@ __global__ __launch_bounds__(256) void dense_lds_kernel(DenseArgs a) {
     ci.ch[e] = g * a.Cg + c;
   }
   const int HoWo = a.Ho * a.Wo;
+  // Pixel cursors of the thread's two rows: the steps visit l0 = l_begin,
+  // l_begin + 32, ... in order, so (n, ho, wo) advance by 32 pixels per step
+  // with carries instead of two divisions per row and step.
+  int cn[2], cho[2], cwo[2];
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int l = l_begin + row0 + 16 * it;
+    cn[it] = l / HoWo;
+    const int rem = l - cn[it] * HoWo;
+    cho[it] = rem / a.Wo;
+    cwo[it] = rem - cho[it] * a.Wo;
+  }
 
   float ra[2][4], rb[2][4];
   auto load_step = [&](int l0) {
@@ -87,6 +99,15 @@ __global__ __launch_bounds__(256) void dense_lds_kernel(DenseArgs a) {
     for (int it = 0; it < 2; ++it) {
       const int l = l0 + row0 + 16 * it;
       const bool lv = l < l_end;
+      const int n_c = cn[it], ho_c = cho[it], wo_c = cwo[it];
+      cwo[it] += kBK;
+      while (cwo[it] >= a.Wo) {
+        cwo[it] -= a.Wo;
+        if (++cho[it] == a.Ho) {
+          cho[it] = 0;
+          ++cn[it];
+        }
+      }
       // dY row l, output channels a_col .. a_col+3 of group g.
       const T* dyp = dy + (int64_t)l * a.K + (int64_t)g * a.Kg + a_col;
       if (VA == 4) {
@@ -101,9 +122,8 @@ __global__ __launch_bounds__(256) void dense_lds_kernel(DenseArgs a) {
         for (int e = 0; e < 4; ++e) ra[it][e] = (lv && a_col + e < a.Kg) ? to_f32(dyp[e]) : 0.f;
       }
       // im2col(X) row l, columns n0 + 4*c4 .. +3.
-      const int n = lv ? l / HoWo : 0;
-      const int rem = lv ? l - n * HoWo : 0;
-      const int ho = rem / a.Wo, wo = rem - (rem / a.Wo) * a.Wo;
+      const int n = lv ? n_c : 0;
+      const int ho = lv ? ho_c : 0, wo = lv ? wo_c : 0;
       const T* xn = x + (int64_t)n * a.x_img;
       if (VB == 4) {
         const int h = ho * a.stride_h + ci.dh[0], w = wo * a.stride_w + ci.dw[0];
