@@ -464,7 +464,12 @@ conv_wgrad_status_t make_plan(const conv_wgrad_desc2_t* desc, Plan* out) {
   }
   // Dense implicit GEMM per group.
   pub.path = CONV_WGRAD_PATH_DENSE;
-  if (plan_dense_1x1(p, out)) {
+  // Launch-bound problems (at most 2^20 FLOP with an automatic split: the
+  // whole reduction takes a few microseconds on one workgroup) run in one
+  // launch on the general kernel; a split would add a dependent fold launch
+  // to a call that is nothing but launch latency.
+  const bool tiny = desc->split_k < 1 && p.L <= (1 << 20) && p.E <= (1 << 20) && 2 * p.L * p.E <= (1 << 20);
+  if (!tiny && plan_dense_1x1(p, out)) {
     pub.variant = kDense1x1;
     pub.unit_rows = 64;
     int64_t tiles;
@@ -472,7 +477,7 @@ conv_wgrad_status_t make_plan(const conv_wgrad_desc2_t* desc, Plan* out) {
     // One-wave workgroups, about eight per CU.
     return choose_split(ceil_div(p.L, 64), tiles, desc->split_k, 4, 2048, 4, p, &pub);
   }
-  if (plan_dense16_rows(p, out)) {
+  if (!tiny && plan_dense16_rows(p, out)) {
     const bool x3 = p.dtype == CONV_WGRAD_F32;   // BF16x3 (the planner only allows it then)
     pub.variant = x3 ? kDense16RowsX3 : kDense16Rows;
     int64_t units, tiles;
@@ -501,7 +506,7 @@ conv_wgrad_status_t make_plan(const conv_wgrad_desc2_t* desc, Plan* out) {
   // take the folded problem's few-pixel output rows one unit each (a 16x16
   // stride-16 patch embedding of 224x224 images ran at 644 us folded on the
   // row kernel against 329 us unfolded on the general kernel).
-  if (p.fold == 1 && plan_dense_rows(p, out)) {
+  if (!tiny && p.fold == 1 && plan_dense_rows(p, out)) {
     pub.variant = kDenseRows;
     pub.unit_rows = out->wt;
     int64_t units, tiles;
@@ -541,7 +546,7 @@ conv_wgrad_status_t make_plan(const conv_wgrad_desc2_t* desc, Plan* out) {
   int64_t units = ceil_div(p.L, pub.unit_rows);
   int64_t tiles;
   if (!mul3(p.groups, out->m_tiles, out->n_tiles, &tiles)) return CONV_WGRAD_ERR_UNSUPPORTED;
-  return choose_split(units, tiles, desc->split_k, 8, 1024, 4, p, &pub);
+  return choose_split(units, tiles, tiny ? 1 : desc->split_k, 8, 1024, 4, p, &pub);
 }
 
 conv_wgrad_status_t make_igemm_plan(const conv_wgrad_desc2_t* desc, int32_t direction, Plan* out) {

@@ -268,6 +268,15 @@ def test_split_pinning_and_auto():
     assert pa.variant == 1 and 384 <= pa.grid <= 512
     pb = iga.get_plan(D(N=8, C=512, H=14, W=14, K=512, split_k=-1))
     assert pb.variant == 1 and pb.grid < 384 and pb.grid <= 256
+    # Launch-bound (2 * L * E <= 2^20 FLOP, automatic split): one launch on the
+    # general kernel, no fold, no workspace; a pinned split is honoured.
+    tiny = D(N=2, C=8, H=8, W=8, K=4, R=1, S=1, pad=0, split_k=-1)
+    pt = iga.get_plan(tiny)
+    assert (pt.variant, pt.ks_count, pt.needs_reduce, pt.ws_bytes, pt.grid) == (0, 1, 0, 0, 1)
+    assert iga.get_plan(D(N=2, C=8, H=8, W=8, K=4, R=1, S=1, pad=0, split_k=4)).ks_count == 4
+    # just past the bound: the automatic split is back
+    big = iga.get_plan(D(N=8, C=64, H=8, W=8, K=64, R=3, S=3, pad=1, split_k=-1))
+    assert 2 * big.L * big.E > (1 << 20) and big.variant == 1
 
 
 def test_one_hip_runtime_when_the_library_loads_first():
@@ -317,12 +326,13 @@ def test_row_kernel_lane_offsets_stay_32_bit():
     over = iga.get_plan(D(N=1, C=4, H=1, W=1, K=4194308, R=1, S=1, pad=0))
     assert 64 * 4194308 * 4 > (1 << 30) - 1
     assert over.variant == 0                   # the general LDS kernel
-    # 16-bit: X columns reach (W + 2 pad + S + 96) pixels of C channels
-    ok16 = iga.get_plan(D(N=1, C=8, H=1, W=1, K=8, R=1, S=1, pad=0, dtype=iga.BF16))
+    # 16-bit: X columns reach (W + 2 pad + S + 96) pixels of C channels (a pinned
+    # split: with an automatic one this tiny problem runs unsplit on the general kernel)
+    ok16 = iga.get_plan(D(N=1, C=8, H=1, W=1, K=8, R=1, S=1, pad=0, dtype=iga.BF16, split_k=1))
     assert ok16.variant == 3
     c_over = -(-((1 << 30)) // (2 * (1 + 1 + 96))) + 8
     c_over += (-c_over) % 8
-    over16 = iga.get_plan(D(N=1, C=c_over, H=1, W=1, K=8, R=1, S=1, pad=0, dtype=iga.BF16))
+    over16 = iga.get_plan(D(N=1, C=c_over, H=1, W=1, K=8, R=1, S=1, pad=0, dtype=iga.BF16, split_k=1))
     assert over16.variant != 3
 
 

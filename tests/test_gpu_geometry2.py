@@ -162,7 +162,7 @@ X3_CASES = [
     (2, 64, 12, 12, 136, 5, 5, (2, 2), 4, True),     # two tap blocks, three M tiles
     (4, 128, 10, 70, 40, 1, 1, (0, 0), 3, False),    # 1x1 with two 64-pixel chunks per row
     (2, 64, 16, 16, 64, 3, 3, (1, 1), 1, True),      # one slice (writes dw directly)
-    (1, 8, 5, 9, 8, 3, 2, (0, 1), -1, True),         # 8 channels
+    (1, 8, 5, 9, 8, 3, 2, (0, 1), 2, True),          # 8 channels (pinned split: automatic would run it unsplit, exact)
 ]
 
 
@@ -189,3 +189,8 @@ def test_bf16x3_positive_inputs_and_fallback():
     err2, plan2 = _check(x2, dy2, 3, 3, 1, 2, 1, 1, "f32", math="bf16x3")
     assert plan2.math == 0 and plan2.base.variant != 4
     log("bf16x3 request on stride 2: exact path, error %.3e" % err2)
+    # A launch-bound problem with an automatic split runs unsplit on the exact general kernel.
+    x3, dy3 = _inputs(1, 8, 5, 9, 8, 3, 2, (0, 1), (1, 1), (1, 1), "f32", 992)
+    err3, plan3 = _check(x3, dy3, 3, 2, (0, 1), 1, 1, 1, "f32", math="bf16x3")
+    assert plan3.math == 0 and plan3.base.variant == 0 and plan3.base.ks_count == 1
+    log("bf16x3 request on a launch-bound problem: exact, one launch, error %.3e" % err3)

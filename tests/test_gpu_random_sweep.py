@@ -5,7 +5,7 @@ Each sweep draws a few hundred small shapes aimed at one family of kernels
 channel counts, 16-bit dense with short and long rows, row-streaming and
 windowed grouped kernels at stride 1 and 2, depthwise, the element fallback,
 the 1x1 streaming kernel), with random split degrees and, on some cases, the
-fused bias gradient (db checked against a float64 sum of dY).
+fused bias gradient (db checked against the bias oracle).
 """
 from __future__ import annotations
 
