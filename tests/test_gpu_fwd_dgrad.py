@@ -77,6 +77,9 @@ CASES = [
     (2, 64, 8, 8, 64, 3, 3, 1, 1, 1, 64, "bf16", -1),              # depthwise
     (1, 40, 7, 9, 72, 1, 1, 0, 1, 1, 1, "f16", 1),                 # 1x1, one slice
     (2, 128, 6, 6, 130, 3, 3, 1, 1, 1, 1, "f32", 40),              # pinned deep split, partial tiles
+    (2, 136, 12, 12, 144, 3, 3, 1, 2, 1, 1, "f32", -1),            # dgrad at stride 2, partial tiles
+    (2, 256, 10, 9, 256, 3, 3, (1, 0), 1, 1, 2, "bf16", 3),        # two groups of 128, per-axis pad
+    (3, 132, 11, 13, 260, 3, 3, 1, 1, 1, 1, "f16", -1),            # partial tiles in M and N
 ]
 
 
