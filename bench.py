@@ -60,7 +60,8 @@ DEFAULT_CONFIG = "c2_3x3_f32"
 # planner it identifies the code a counter measurement was taken on.
 CSRC = os.path.join(ROOT, "implicit_gemm_amd", "csrc")
 VARIANT_SOURCE = {0: "dense_lds.hip", 1: "dense_rows.hip", 2: "dense_1x1.hip", 3: "dense16_rows.hip",
-                  4: "dense16_rows.hip", 20: "conv_igemm.hip", 21: "conv_igemm.hip",
+                  4: "dense16_rows.hip", 5: "dense16_taps.hip", 6: "dense16_taps.hip",
+                  20: "conv_igemm.hip", 21: "conv_igemm.hip",
                   10: "direct_elem.hip",
                   11: "grouped16.hip", 12: "depthwise_mfma.hip", 13: "grouped16.hip"}
 SHARED_SOURCES = ("device_common.h", "kernels.h", "plan.h", "plan.cpp")

@@ -64,6 +64,8 @@ MATH = {"exact": 0, "bf16x3": 1}
 DIRECTION_WGRAD, DIRECTION_FWD, DIRECTION_DGRAD = 0, 1, 2
 VARIANT_FWD, VARIANT_DGRAD = 20, 21
 VARIANT_DENSE_BF16X3 = 4
+VARIANT_DENSE16_TAPS, VARIANT_DENSE_BF16X3_TAPS = 5, 6
+VARIANTS_BF16X3 = (VARIANT_DENSE_BF16X3, VARIANT_DENSE_BF16X3_TAPS)
 
 
 class ConvWgradError(RuntimeError):

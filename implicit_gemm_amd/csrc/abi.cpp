@@ -149,6 +149,8 @@ conv_wgrad_status_t run(const conv_wgrad_desc2_t* desc, const void* x, const voi
     case cw::kDense1x1: err = cw::launch_dense_1x1(plan, x, dy, out, s); break;
     case cw::kDense16Rows:
     case cw::kDense16RowsX3: err = cw::launch_dense16_rows(plan, x, dy, out, s); break;
+    case cw::kDense16Taps:
+    case cw::kDense16TapsX3: err = cw::launch_dense16_taps(plan, x, dy, out, s); break;
     default: err = cw::launch_dense(plan, x, dy, out, s); break;
   }
   if (err != hipSuccess) return CONV_WGRAD_ERR_HIP;
@@ -286,7 +288,9 @@ conv_wgrad_status_t conv_wgrad2_get_plan(const conv_wgrad_desc2_t* desc, conv_wg
   conv_wgrad_status_t st = get_plan(desc, &p);
   if (st != CONV_WGRAD_OK) return st;
   plan->base = p.pub;
-  plan->math = p.pub.variant == CONV_WGRAD_VARIANT_DENSE_BF16X3 ? CONV_WGRAD_MATH_BF16X3 : CONV_WGRAD_MATH_EXACT;
+  plan->math = p.pub.variant == CONV_WGRAD_VARIANT_DENSE_BF16X3 || p.pub.variant == CONV_WGRAD_VARIANT_DENSE_BF16X3_TAPS
+                   ? CONV_WGRAD_MATH_BF16X3
+                   : CONV_WGRAD_MATH_EXACT;
   plan->fold_width = p.p.fold;
   return CONV_WGRAD_OK;
 }

@@ -373,7 +373,10 @@ __global__ __launch_bounds__(256) void dense16_rows_kernel(R16Args a) {
       const int npix = sets[p].npix;
       store_unit(buf, sets[p]);
       load_unit(u + kSets, sets[p]);
-      __syncthreads();   // the unit is staged; every wave is done with the other buffer
+      // The unit is staged and every wave is done with the other buffer.  An
+      // LDS-only barrier: the loads just issued stay in flight over the MFMAs
+      // (__syncthreads would also wait for them).
+      lds_barrier();
       compute_unit(buf, npix);
     }
   }

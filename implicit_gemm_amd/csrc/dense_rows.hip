@@ -217,9 +217,11 @@ __global__ __launch_bounds__(kSolo ? 256 : 512, kSolo ? 2 : 1) void dense_rows_k
       const int npix = npix_reg;
       store_unit();
       if (p + 1 < nu) load_unit(u_begin + p + 1);
-      __syncthreads();
+      // LDS-only barriers: the next unit's loads stay in flight over the
+      // MFMAs (__syncthreads would also wait for them).
+      lds_barrier();
       compute_unit(npix);
-      __syncthreads();
+      lds_barrier();
     }
     if (want_db)   // 16 loader rows per channel quad
       block_sum64<16, 4>(smem, p0, 4 * q, dbp,
@@ -242,7 +244,7 @@ __global__ __launch_bounds__(kSolo ? 256 : 512, kSolo ? 2 : 1) void dense_rows_k
       // Called on every phase (with no pixels when staging) so that the
       // accumulators take one path through the loop.
       compute_unit(comp ? npix_cur : 0);
-      __syncthreads();
+      lds_barrier();   // LDS only: the loads issued two phases ahead stay in flight
     }
 
     // Bias partial: rows are the 16 loader rows of half 0, then those of half 1.

@@ -50,6 +50,8 @@ hipError_t launch_dense_rows(const Plan& plan, const void* x, const void* dy, St
                              hipStream_t stream);
 hipError_t launch_dense16_rows(const Plan& plan, const void* x, const void* dy, Stage1Out out,
                                hipStream_t stream);
+hipError_t launch_dense16_taps(const Plan& plan, const void* x, const void* dy, Stage1Out out,
+                               hipStream_t stream);
 hipError_t launch_dense_1x1(const Plan& plan, const void* x, const void* dy, Stage1Out out,
                             hipStream_t stream);
 hipError_t launch_grouped16(const Plan& plan, const void* x, const void* dy, Stage1Out out,

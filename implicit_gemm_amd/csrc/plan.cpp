@@ -346,6 +346,42 @@ bool plan_dense16_rows(const Problem& p, Plan* out) {
   return true;
 }
 
+// 16-bit dense kernel with all taps per tile (dense16_taps.hip): 3 x 3
+// filters, stride 1, dilation 1, channel counts in whole 8-channel chunks,
+// output rows short enough that one padded row (P = Wo + 2 slots) fits a
+// 64-slot unit and the unit's X rows fit 192 staged slots (P <= 63).
+bool plan_dense16_taps(const Problem& p, Plan* out) {
+  const bool x3 = p.dtype == CONV_WGRAD_F32 && p.math == CONV_WGRAD_MATH_BF16X3;
+  if ((p.dtype == CONV_WGRAD_F32 && !x3) || p.stride_h != 1 || p.stride_w != 1 || p.dil_h != 1 || p.dil_w != 1)
+    return false;
+  if (p.R != 3 || p.S != 3) return false;
+  if (p.C % 8 != 0 || p.K % 8 != 0 || p.Cg % 8 != 0 || p.Kg % 8 != 0) return false;
+  // 16-bit groups of at most 64 x 64 channels keep the row kernel (3 x 3 C = K
+  // = 64 56x56: 29.3 us there, 31.3 us here, whose one tile per slice holds
+  // the whole gradient and doubles the slab bytes per workgroup).
+  if (!x3 && p.Kg <= 64 && p.Cg <= 64) return false;
+  const int64_t pitch = p.Wo + p.S - 1;
+  const int64_t need = 64 + (p.R - 1) * pitch + p.S - 1;   // X slots the MFMAs of a unit read
+  if (pitch > 64 || need > 192) return false;
+  const int64_t ru = 64 / pitch;
+  // Buffer ranges of a unit's dY rows and X rows, and every lane offset in
+  // them, below 2^30 (the out-of-range offset the loaders use lies past them).
+  const int64_t es = p.esize;
+  int64_t dy_bytes, x_bytes;
+  if (!mul3(ru * p.Wo, p.K, es, &dy_bytes) || dy_bytes > kI32Max / 2) return false;
+  if (!mul3((ru + p.R) * p.W, p.C, es, &x_bytes) || x_bytes > kI32Max / 2) return false;
+  out->ru = (int32_t)ru;
+  out->sb = (int32_t)p.S;
+  out->xspan = need <= 128 ? 128 : need <= 160 ? 160 : 192;
+  // 16-bit: 32 output channels per tile (two workgroups fit a CU); BF16x3
+  // (one workgroup per CU, 160 KB of LDS at most): 64, which halves the B
+  // operand reads per MFMA of its three products.
+  out->bm = x3 && p.Kg > 32 ? 64 : 32;
+  out->m_tiles = ceil_div(p.Kg, out->bm);
+  out->c_tiles = ceil_div(p.Cg, 64);
+  return true;
+}
+
 // Depthwise 4x4x4 kernel (depthwise_mfma.hip): 16-bit, one channel per group,
 // stride 1, no dilation, channels in whole 16-channel groups, filter up to
 // 12 x 12 (blocks of 4 filter rows / columns: 1 or 2 each up to 8 x 8, 3 x 3
@@ -476,6 +512,20 @@ conv_wgrad_status_t make_plan(const conv_wgrad_desc2_t* desc, Plan* out) {
     if (!mul3(p.groups, out->m_tiles, out->c_tiles, &tiles)) return CONV_WGRAD_ERR_UNSUPPORTED;
     // One-wave workgroups, about eight per CU.
     return choose_split(ceil_div(p.L, 64), tiles, desc->split_k, 4, 2048, 4, p, &pub);
+  }
+  if (!tiny && plan_dense16_taps(p, out)) {
+    pub.variant = p.dtype == CONV_WGRAD_F32 ? kDense16TapsX3 : kDense16Taps;
+    pub.unit_rows = out->ru * p.Wo;   // a unit is ru whole output rows
+    int64_t units, tiles;
+    if (!mul_ok(p.N, ceil_div(p.Ho, out->ru), &units) || !mul3(p.groups, out->m_tiles, out->c_tiles, &tiles))
+      return CONV_WGRAD_ERR_UNSUPPORTED;
+    // Measured on 3x3 shapes of 14x14 to 56x56: the call time is set by the
+    // units per workgroup (a unit costs ~1 us whatever its MFMA work) and the
+    // slab bytes, and is lowest at 14-16 units per slice with up to two
+    // workgroups per CU (16-bit) or about 7 with one (BF16x3); slab traffic
+    // up to 8x the algorithmic bytes pays off there.
+    if (pub.variant == kDense16TapsX3) return choose_split(units, tiles, desc->split_k, 7, 256, 1, p, &pub, 0, 8);
+    return choose_split(units, tiles, desc->split_k, 14, 512, 1, p, &pub, 0, 8);
   }
   if (!tiny && plan_dense16_rows(p, out)) {
     const bool x3 = p.dtype == CONV_WGRAD_F32;   // BF16x3 (the planner only allows it then)

@@ -20,6 +20,8 @@ enum Variant : int32_t {
   kDense1x1 = 2,      // 1x1 stride-1 unpadded fp32: rows streamed into MFMA registers
   kDense16Rows = 3,   // 16-bit dense, stride 1, dilation 1: row units on 16x16x32 bf16/fp16 MFMA
   kDense16RowsX3 = 4, // fp32 dense by BF16x3 emulation on the 16-bit row kernel (math = BF16X3)
+  kDense16Taps = 5,   // 16-bit dense 3x3, stride 1, short rows: all taps per tile, packed row units
+  kDense16TapsX3 = 6, // fp32 dense 3x3 by BF16x3 on the all-taps kernel (math = BF16X3)
   kDirectElem = 10,   // direct small-group kernel, one dW element per lane
   kGrouped16 = 11,    // 16-bit small groups: block-diagonal 16x16x32 MFMA, transposed LDS reads
   kDepthwise = 12,    // 16-bit depthwise: batched 4x4x4 MFMA, 64 channels per workgroup

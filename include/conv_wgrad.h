@@ -243,8 +243,9 @@ conv_wgrad_status_t conv_wgrad_bias_timed(const conv_wgrad_desc_t* desc, const v
  *       so the normalised error is bounded by ~4.6e-5 in the worst case and is
  *       ~1e-7 for inputs of random sign.  It is a permission, never a silent
  *       downgrade of other shapes: the plan uses it only where a BF16x3 kernel
- *       covers the shape (plan variant CONV_WGRAD_VARIANT_DENSE_BF16X3) and the
- *       exact fp32 path elsewhere.  Any other value is BAD_DTYPE.
+ *       covers the shape (plan variant CONV_WGRAD_VARIANT_DENSE_BF16X3 or
+ *       CONV_WGRAD_VARIANT_DENSE_BF16X3_TAPS) and the exact fp32 path
+ *       elsewhere.  Any other value is BAD_DTYPE.
  * fold_width (rocm-libraries PR #14393, commit bodies, the fold_width
  * paragraph: f adjacent W positions folded into the channels when f divides
  * the filter width, the W stride, the input width and the W padding; the
@@ -270,8 +271,11 @@ typedef struct conv_wgrad_desc2 {
 #define CONV_WGRAD_MATH_EXACT 0
 #define CONV_WGRAD_MATH_BF16X3 1
 
-/* conv_wgrad_plan_t::variant of the BF16x3 dense kernel. */
+/* conv_wgrad_plan_t::variant of the BF16x3 dense kernels: the row kernel
+ * (one filter row per tile) and the all-taps kernel (3 x 3 filters, output
+ * rows of at most 61 pixels). */
 #define CONV_WGRAD_VARIANT_DENSE_BF16X3 4
+#define CONV_WGRAD_VARIANT_DENSE_BF16X3_TAPS 6
 
 /* The plan of an extended descriptor: the base plan (of the problem the kernels
  * run, i.e. after a width fold) and what was applied. */

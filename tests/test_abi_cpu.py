@@ -175,6 +175,10 @@ def check_plan_invariants(d, p):
         ru = p.unit_rows // Wo
         assert p.unit_rows == ru * Wo and ru >= 2 and ru * (Wo + min(d.S, 4) - 1) <= 64
         assert p.units == d.N * -(-Ho // ru)
+    elif p.path == iga.PATH_DENSE and p.variant in (5, 6):   # all-taps kernel: ru whole rows, ru = 64 // (Wo + 2)
+        ru = 64 // (Wo + 2)
+        assert d.R == d.S == 3 and d.stride == d.dilation == 1 and ru >= 1
+        assert p.unit_rows == ru * Wo and p.units == d.N * -(-Ho // ru)
     elif p.path == iga.PATH_DENSE and p.variant in (1, 3):   # row units: (n, ho, chunk of Wo)
         assert p.units == d.N * Ho * -(-Wo // p.unit_rows)
     elif p.variant in (12, 13):                       # depthwise, row-streaming grouped: one output row per unit
@@ -408,7 +412,7 @@ def test_per_axis_plans_route_to_per_axis_kernels():
     16-bit dense rows, the general dense kernel, the element kernel), and the plan's
     extents follow the row and column geometry."""
     rng = np.random.default_rng(9)
-    per_axis_variants = {0, 1, 3, 4, 10}
+    per_axis_variants = {0, 1, 3, 4, 5, 6, 10}
     seen = set()
     for _ in range(1500):
         groups = int(rng.choice([1, 1, 2, 8, 32]))
@@ -467,13 +471,45 @@ def test_bf16x3_plan_selection():
     elsewhere; it never applies to 16-bit inputs."""
     c2 = dict(N=32, C=64, H=56, W=56, K=64, R=3, S=3, pad=1)
     p = iga.get_plan2(D2(math="bf16x3", **c2))
-    assert p.math == 1 and p.base.variant == iga.VARIANT_DENSE_BF16X3
+    assert p.math == 1 and p.base.variant == iga.VARIANT_DENSE_BF16X3_TAPS
     assert iga.get_plan2(D2(**c2)).base.variant == 1 and iga.get_plan2(D2(**c2)).math == 0
+    # 5x5: the row kernel's BF16x3 form
+    p5 = iga.get_plan2(D2(math="bf16x3", **dict(c2, R=5, S=5, pad=2)))
+    assert p5.math == 1 and p5.base.variant == iga.VARIANT_DENSE_BF16X3
     for kw in (dict(stride=2), dict(dilation=2), dict(C=60), dict(groups=32, C=64, K=64)):
         q = iga.get_plan2(D2(math="bf16x3", **dict(c2, **kw)))
-        assert q.math == 0 and q.base.variant != iga.VARIANT_DENSE_BF16X3, kw
+        assert q.math == 0 and q.base.variant not in iga.VARIANTS_BF16X3, kw
     q = iga.get_plan2(D2(math="bf16x3", dtype=iga.BF16, **c2))
     assert q.math == 0 and q.base.variant == 3
+
+
+def test_all_taps_plan_selection():
+    """16-bit 3x3 stride-1 dense shapes with more than 64 input or output channels
+    per group, whose padded output row fits 64 slots and whose unit's X rows fit
+    192 slots (Wo + 2 <= 63), take the all-taps kernel, with units of
+    64 // (Wo + 2) whole rows and tiles of 32 output x 64 input channels; longer
+    rows, other filters, strides, dilations and groups of at most 64 x 64
+    channels keep the row kernel.  BF16x3 takes it at any channel count, with
+    64 output channels per tile."""
+    def plan(**kw):
+        base = dict(N=4, C=128, H=30, W=30, K=64, R=3, S=3, pad=1, dtype=iga.BF16, split_k=2)
+        return iga.get_plan2(D2(**dict(base, **kw))).base
+    for W, ru in ((14, 4), (28, 2), (30, 2), (31, 1), (56, 1), (61, 1)):
+        p = plan(H=W, W=W)
+        assert p.variant == iga.VARIANT_DENSE16_TAPS and p.unit_rows == ru * W, (W, p.variant)
+        assert p.units == 4 * -(-W // ru) and p.tiles == 2 * 2
+    assert plan(C=64).variant == 3 and plan(C=64, K=72).variant == iga.VARIANT_DENSE16_TAPS
+    x3 = plan(C=64, dtype=iga.F32, math="bf16x3")
+    assert x3.variant == iga.VARIANT_DENSE_BF16X3_TAPS and x3.tiles == 1
+    assert plan(C=24, K=40, dtype=iga.F32, math="bf16x3").tiles == 1
+    assert plan(H=62, W=62).variant == 3            # 64 + 2 * 64 + 2 X slots: over 192
+    assert plan(R=5, S=5, pad=2).variant == 3
+    assert plan(stride=2).variant != iga.VARIANT_DENSE16_TAPS
+    assert plan(dilation=2).variant != iga.VARIANT_DENSE16_TAPS
+    assert plan(dtype=iga.F16).variant == iga.VARIANT_DENSE16_TAPS
+    assert plan(C=256, K=96, groups=2).tiles == 2 * 2 * 2   # per group: 48 output channels, 128 inputs
+    assert plan(pad=(0, 2)).Wo == 32 and plan(pad=(0, 2)).variant == iga.VARIANT_DENSE16_TAPS
+    assert plan(C=60).variant not in (iga.VARIANT_DENSE16_TAPS, 3)
 
 
 def test_igemm_plans_and_errors():

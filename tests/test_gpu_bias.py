@@ -17,14 +17,18 @@ from gpu_util import check_against_oracle, log, to_device
 
 pytestmark = pytest.mark.gpu
 
-VARIANT = {0: "dense_lds", 1: "dense_rows", 2: "dense_1x1", 3: "dense16_rows", 10: "direct_elem", 11: "grouped16",
+VARIANT = {0: "dense_lds", 1: "dense_rows", 2: "dense_1x1", 3: "dense16_rows", 5: "dense16_taps", 10: "direct_elem",
+           11: "grouped16",
            12: "depthwise", 13: "grouped16_rows"}
 
 BIAS_CASES = [
     (wd.ConvShape(4, 64, 56, 56, 64, 3, 3, pad=1), "f32", -1),                 # dense rows, 3x3
     (wd.ConvShape(4, 64, 56, 56, 64, 3, 3, pad=1), "f32", 1),                  # one slice: db written directly
-    (wd.ConvShape(2, 64, 12, 12, 64, 3, 3, pad=1), "bf16", 3),                 # 16-bit dense rows (16x16x32 MFMA)
-    (wd.ConvShape(3, 136, 9, 45, 72, 3, 3, pad=1), "f16", -1),                 # 16-bit dense rows, 2 M / 3 C tiles
+    (wd.ConvShape(2, 64, 12, 12, 96, 3, 3, pad=1), "bf16", 3),                 # 16-bit all-taps (16x16x32 MFMA)
+    (wd.ConvShape(2, 64, 12, 12, 64, 3, 3, pad=1), "bf16", 3),                 # 16-bit dense rows, 3x3
+    (wd.ConvShape(3, 136, 9, 45, 72, 3, 3, pad=1), "f16", -1),                 # 16-bit all-taps, 3 M / 3 C tiles
+    (wd.ConvShape(2, 64, 12, 12, 64, 5, 5, pad=2), "bf16", 3),                 # 16-bit dense rows, 5x5
+    (wd.ConvShape(2, 72, 5, 70, 40, 3, 3, pad=1), "f16", 2),                   # 16-bit dense rows, 70-pixel rows
     (wd.ConvShape(2, 6, 9, 9, 10, 3, 3, pad=1), "f32", 3),                    # general dense (Kg % 4 != 0)
     (wd.ConvShape(2, 40, 11, 13, 70, 3, 2, pad=1, stride=2), "f16", 4),        # general dense, stride 2, 2 M tiles
     (wd.ConvShape(2, 40, 11, 13, 72, 3, 2, pad=1, stride=2), "bf16", 4),       # dense rows, stride 2

@@ -143,7 +143,7 @@ def test_bf16x3_full_size_3x3():
     s = wl.shape
     x, dy = wd.make_inputs(wl)
     got, db, plan = _run(x, dy, s.R, s.S, s.pad, s.stride, s.dilation, s.groups, "f32", math="bf16x3", bias=True)
-    assert plan.base.variant == 4 and plan.math == 1
+    assert plan.base.variant == 6 and plan.math == 1   # the all-taps kernel's BF16x3 form
     ref, den = oracle.wgrad_ref(x, dy, s.R, s.S, s.pad, s.stride, s.dilation, s.groups)
     err = oracle.normalised_error(got, ref, den)
     db_err = check_bias_against_oracle(dy, db, "f32")
@@ -163,6 +163,7 @@ X3_CASES = [
     (4, 128, 10, 70, 40, 1, 1, (0, 0), 3, False),    # 1x1 with two 64-pixel chunks per row
     (2, 64, 16, 16, 64, 3, 3, (1, 1), 1, True),      # one slice (writes dw directly)
     (1, 8, 5, 9, 8, 3, 2, (0, 1), 2, True),          # 8 channels (pinned split: automatic would run it unsplit, exact)
+    (2, 64, 6, 70, 64, 3, 3, (1, 1), 2, True),       # 3x3 with 70-pixel rows: the row kernel
 ]
 
 
@@ -172,7 +173,8 @@ def test_bf16x3_shapes(idx):
     x, dy = _inputs(N, C, H, W, K, R, S, pad, (1, 1), (1, 1), "f32", 950 + idx)
     err, plan = _check(x, dy, R, S, pad, 1, 1, 1, "f32", split_k=sk, math="bf16x3", bias=bias)
     log("bf16x3", X3_CASES[idx], "ks", plan.base.ks_count, "error %.3e" % err)
-    assert plan.base.variant == 4
+    # 3x3 rows of at most 61 pixels: the all-taps kernel; otherwise the row kernel
+    assert plan.base.variant == (6 if (R, S) == (3, 3) and W + 2 * pad[1] - 2 <= 61 else 4)
 
 
 def test_bf16x3_positive_inputs_and_fallback():
@@ -184,10 +186,10 @@ def test_bf16x3_positive_inputs_and_fallback():
     x, dy = np.abs(x), np.abs(dy)
     err, plan = _check(x, dy, 3, 3, 1, 1, 1, 1, "f32", math="bf16x3")
     log("bf16x3 positive inputs: error %.3e" % err)
-    assert plan.base.variant == 4
+    assert plan.base.variant == 6
     x2, dy2 = _inputs(2, 64, 20, 20, 64, 3, 3, (1, 1), (2, 2), (1, 1), "f32", 991)
     err2, plan2 = _check(x2, dy2, 3, 3, 1, 2, 1, 1, "f32", math="bf16x3")
-    assert plan2.math == 0 and plan2.base.variant != 4
+    assert plan2.math == 0 and plan2.base.variant not in (4, 6)
     log("bf16x3 request on stride 2: exact path, error %.3e" % err2)
     # A launch-bound problem with an automatic split runs unsplit on the exact general kernel.
     x3, dy3 = _inputs(1, 8, 5, 9, 8, 3, 2, (0, 1), (1, 1), (1, 1), "f32", 992)

@@ -355,9 +355,10 @@ def test_grouped_rows_short_slices(idx):
     check_bias_against_oracle(dy, db.cpu().numpy(), dtype)
 
 
-# 16-bit dense kernel with units of several short output rows (Wo + SB - 1 <= 32):
-# row pitch Wo + SB - 1 inside the 64-slot unit, Ho not a multiple of the rows
-# per unit, padding 0..2, two tap blocks (S = 5), partial channel tiles, slices.
+# 16-bit dense kernels with units of several short output rows (the row kernel for
+# Wo + SB - 1 <= 32, the all-taps kernel for 3x3 filters): row pitch inside the
+# 64-slot unit, Ho not a multiple of the rows per unit, padding 0..3, two tap
+# blocks (S = 5, 7), partial channel tiles, slices.
 DENSE16_ROW_CASES = [
     (wd.ConvShape(3, 64, 14, 14, 64, 3, 3, pad=1), "bf16", -1),       # 4 rows per unit, last unit 2 rows
     (wd.ConvShape(2, 72, 7, 7, 40, 3, 3, pad=1), "f16", 2),           # 7 rows per unit, partial tiles
@@ -367,6 +368,8 @@ DENSE16_ROW_CASES = [
     (wd.ConvShape(2, 64, 12, 12, 136, 5, 5, pad=2), "f16", 4),        # S = 5: two tap blocks, 3 M tiles
     (wd.ConvShape(4, 128, 10, 13, 64, 3, 3, pad=2), "bf16", -1),      # pad 2: Ho, Wo > H - 2
     (wd.ConvShape(2, 64, 16, 16, 64, 3, 3, pad=1, groups=2), "f16", 3),  # two groups of 32 channels
+    (wd.ConvShape(3, 64, 14, 14, 64, 5, 5, pad=2), "bf16", -1),       # 5x5, 3 rows of pitch 17 per unit
+    (wd.ConvShape(2, 40, 12, 12, 48, 7, 7, pad=3), "f16", 3),         # 7x7: two tap blocks, 4 rows per unit
 ]
 
 
@@ -379,7 +382,10 @@ def test_dense16_multirow_units(idx):
     plan = iga.get_plan(d)
     log("dense16 rows", idx, shp, dtype, "split", split_k, "variant", plan.variant,
         "unit_rows", plan.unit_rows, "ks", plan.ks_count)
-    assert plan.variant == 3 and plan.unit_rows > plan.Wo   # several rows per unit
+    # several rows per unit: the row kernel, or the all-taps kernel for 3x3
+    # filters with more than 64 input or output channels per group
+    taps = (shp.R, shp.S) == (3, 3) and max(shp.C, shp.K) // shp.groups > 64
+    assert plan.variant == (5 if taps else 3) and plan.unit_rows > plan.Wo
     x, dy = wd.random_inputs(shp, dtype, seed=700 + idx, x_dist=wd.Dist("normal", 1.0),
                              dy_dist=wd.Dist("normal", 0.1))
     check_against_oracle(x, dy, shp, dtype, split_k=split_k)
