@@ -139,18 +139,31 @@ __global__ __launch_bounds__(256) void dense16_taps_kernel(TapsArgs a) {
   const int P = a.pitch;
   const int d_slot = tid / kDq, dq = tid % kDq;
   const int xs0 = tid >> 3, xq = tid & 7;
-  int dj[kDyChunks], dcol[kDyChunks];
+  // Per-lane parts of the loader offsets that are the same for every unit:
+  // byte offset within the unit's rows and whether the slot's column lies
+  // inside the output row (dY) or the image (X).  A load that must read zero
+  // gets an offset of at least kOob, past every buffer range.
+  constexpr int kOob = 0x7fffffe0;
+  int d_row[kDyChunks], d_part[kDyChunks];
+  bool d_colok[kDyChunks];
 #pragma unroll
   for (int i = 0; i < kDyChunks; ++i) {
-    dj[i] = (d_slot + (256 / kDq) * i) / P;
-    dcol[i] = (d_slot + (256 / kDq) * i) % P;
+    const int slot = d_slot + (256 / kDq) * i;
+    d_row[i] = slot / P;
+    const int col = slot % P;
+    d_colok[i] = col < a.Wo;
+    d_part[i] = ((d_row[i] * a.Wo + col) * a.K + 8 * dq) * kEs;
   }
-  int xj[kXChunks], xcol[kXChunks];
+  int x_row[kXChunks], x_part[kXChunks];
+  bool x_colok[kXChunks];
 #pragma unroll
   for (int i = 0; i < kXChunks; ++i) {
-    xj[i] = (xs0 + 32 * i) / P;
-    xcol[i] = (xs0 + 32 * i) % P;
+    x_row[i] = (xs0 + 32 * i) / P;
+    const int wc = (xs0 + 32 * i) % P - a.pad_w;
+    x_colok[i] = wc >= 0 && wc < a.W;
+    x_part[i] = (wc * a.C + 8 * xq) * kEs;
   }
+  const unsigned x_row_bytes = (unsigned)(a.W * a.C * kEs);
   const int dy_col0 = g * a.Kg + m0;   // first output channel of the tile
   const int x_col0 = g * a.Cg + c0;    // first input channel of the tile
 
@@ -159,7 +172,8 @@ __global__ __launch_bounds__(256) void dense16_taps_kernel(TapsArgs a) {
     int nslots;   // slots up to the last filled dY slot (0 past the slice)
   };
   // The loads take the slice's units in order: the unit's (image, row block)
-  // is a cursor advanced by one per load.
+  // is a cursor advanced by one per load.  The offsets are selected without
+  // branches, so the loads can be scheduled among the MFMAs of a unit.
   int cur_n = u_begin / a.hblocks, cur_b = u_begin % a.hblocks;
   const int n_first = cur_n, b_first = cur_b;
   auto load_unit = [&](int u, Set& st) {
@@ -177,22 +191,25 @@ __global__ __launch_bounds__(256) void dense16_taps_kernel(TapsArgs a) {
     const __amdgpu_buffer_rsrc_t rd = buf_rsrc(dyp, rows > 0 ? (rows * a.Wo * a.K - dy_col0) * kEs : 0);
 #pragma unroll
     for (int i = 0; i < kDyChunks; ++i) {
-      const int doff = dcol[i] < a.Wo && dj[i] < rows ? ((dj[i] * a.Wo + dcol[i]) * a.K + 8 * dq) * kEs : 0x7fffffe0;
+      const int doff = d_part[i] | (d_colok[i] && d_row[i] < rows ? 0 : kOob);
 #pragma unroll
       for (int h = 0; h < kLd; ++h)
         st.dy[i][h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rd, doff + 16 * h, 0, 0));
     }
     // X rows h0 .. h0 + rows + R - 2 (those inside the image), columns
     // -pad_w .. P - 1 - pad_w (those inside the image); the rest read zero.
+    // Row i of a lane's slot is image row hlo + x_row[i] + (h0 - hlo).
     const int h0 = ho0 - a.pad_h;
     const int hlo = max(h0, 0), hhi = rows > 0 ? min(h0 + rows + R - 1, a.H) : hlo;
+    const int rdelta = h0 - hlo, rspan = hhi - hlo;
     const unsigned char* xp = xg + kEs * ((int64_t)n * a.x_img + (int64_t)hlo * a.W * a.C + x_col0);
-    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(xp, hhi > hlo ? ((hhi - hlo) * a.W * a.C - x_col0) * kEs : 0);
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(xp, rspan > 0 ? (rspan * a.W * a.C - x_col0) * kEs : 0);
 #pragma unroll
     for (int i = 0; i < kXChunks; ++i) {
-      const int h = h0 + xj[i], wc = xcol[i] - a.pad_w;
-      const bool ok = h >= hlo && h < hhi && wc >= 0 && wc < a.W;
-      const int off = ok ? (((h - hlo) * a.W + wc) * a.C + 8 * xq) * kEs : 0x7fffffe0;
+      const int ri = x_row[i] + rdelta;
+      const bool ok = x_colok[i] && ri >= 0 && ri < rspan;
+      // Unsigned: the offset of a slot outside the rows may wrap; it is then replaced.
+      const int off = (int)(((unsigned)ri * x_row_bytes + (unsigned)x_part[i]) | (ok ? 0u : (unsigned)kOob));
 #pragma unroll
       for (int hh = 0; hh < kLd; ++hh)
         st.x[i][hh] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16 * hh, 0, 0));
@@ -262,8 +279,7 @@ __global__ __launch_bounds__(256) void dense16_taps_kernel(TapsArgs a) {
 
   // One unit's MFMAs: per 32-slot k-step the MB A operands, then per filter
   // row r and tap s the B operand read r*P + s slots further on and its MB
-  // MFMAs (with BF16x3 the two cross terms, small, before hi * hi).  nslots is
-  // workgroup-uniform: a unit of at most 32 slots skips the second k-step.
+  // MFMAs (with BF16x3 the two cross terms, small, before hi * hi).
   auto compute_unit = [&](int buf, int nslots) {
     const unsigned short* ad = s_dy[0][buf] + lane_off;
     const unsigned short* bx = s_x[0][buf] + lane_off + 16 * wave;
@@ -271,7 +287,12 @@ __global__ __launch_bounds__(256) void dense16_taps_kernel(TapsArgs a) {
     const unsigned short* bx_lo = s_x[kPlanes - 1][buf] + lane_off + 16 * wave;
 #pragma unroll
     for (int ks = 0; ks < kSlots / 32; ++ks) {
-      if (32 * ks < nslots) {
+      // 16-bit without the bias gradient: both k-steps run for every unit
+      // (empty slots and units past the slice staged zeros, whose products
+      // add nothing), so the loads issued before them are scheduled among
+      // the MFMAs.  The other forms skip empty k-steps: with more registers
+      // live, one region would move the accumulators in and out of AGPRs.
+      if ((!kX3 && !kDb) || 32 * ks < nslots) {
         s16x8 fa[MB], fa_lo[MB];
 #pragma unroll
         for (int i = 0; i < MB; ++i) fa[i] = tr8(ad + 32 * ks * kPitchE + 16 * i);
@@ -323,11 +344,11 @@ __global__ __launch_bounds__(256) void dense16_taps_kernel(TapsArgs a) {
       const int buf = (it * kSets + p) & 1;
       const int nslots = sets[p].nslots;
       store_unit(buf, sets[p]);
-      load_unit(u + kSets, sets[p]);
-      // The unit is staged and every wave is done with the other buffer.  An
-      // LDS-only barrier: the loads just issued stay in flight over the MFMAs
-      // (__syncthreads would also wait for them).
+      // The unit is staged and every wave is done with the other buffer (an
+      // LDS-only barrier: earlier loads stay in flight).  The next loads into
+      // this set are then issued among the unit's MFMAs.
       lds_barrier();
+      load_unit(u + kSets, sets[p]);
       compute_unit(buf, nslots);
     }
   }
@@ -388,7 +409,9 @@ hipError_t launch_mb(const Plan& plan, const TapsArgs& args, hipStream_t stream)
 
 template <bool kBf16, bool kX3>
 hipError_t launch_b(const Plan& plan, const TapsArgs& args, hipStream_t stream) {
-  if (plan.bm == 64) return launch_mb<kBf16, 4, kX3>(plan, args, stream);
+  if constexpr (kX3) {
+    if (plan.bm == 64) return launch_mb<kBf16, 4, kX3>(plan, args, stream);
+  }
   return launch_mb<kBf16, 2, kX3>(plan, args, stream);
 }
 
