@@ -50,9 +50,11 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK = {  # MI355X published peaks
+PEAK = {  # MI355X published peaks (and the unit counts the probes normalise by)
     "hbm_gbs": 8000.0,
     "mfma_tflops": {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6},
+    "cus": 256,
+    "clock_ghz": 2.4,
 }
 DEFAULT_CONFIG = "c2_3x3_f32"
 
@@ -184,10 +186,25 @@ def measure_peaks(hip):
                 best = (blocks, tf)
         mfma.append({"dtype": name, "blocks": best[0], "tflops": round(best[1], 1),
                      "frac_of_published": round(best[1] / PEAK["mfma_tflops"][name], 4)})
+    best = None
+    for blocks in (1024, 2048):   # the 16x16x32 bf16 form of the 16-bit kernels
+        ms = timed(lambda a, b: probes.peak_mfma16(10000, blocks, sink.data_ptr(), stream, a, b), reps=5)
+        tf = blocks * 4 * 10000 * 131072 / (ms * 1e-3) / 1e12
+        if best is None or tf > best[1]:
+            best = (blocks, tf)
+    mfma.append({"dtype": "bf16 (16x16x32)", "blocks": best[0], "tflops": round(best[1], 1),
+                 "frac_of_published": round(best[1] / PEAK["mfma_tflops"]["bf16"], 4)})
+    lds = []
+    for mode, name, width in ((0, "ds_read_b64_tr_b16", 8), (1, "ds_read_b64", 8), (2, "ds_read_b128", 16)):
+        for blocks in (256, 512, 1024):   # 1, 2 and 4 workgroups per CU
+            ms = timed(lambda a, b: probes.peak_lds(mode, 4000, blocks, sink.data_ptr(), stream, a, b), reps=5)
+            nbytes = blocks * 256 * 4000 * 8 * width
+            lds.append({"read": name, "workgroups_per_cu": blocks // PEAK["cus"],
+                        "bytes_per_clk_per_cu": round(nbytes / (ms * 1e-3) / (PEAK["clock_ghz"] * 1e9) / PEAK["cus"], 1)})
     torch.cuda.synchronize()
     hip.destroy(e0)
     hip.destroy(e1)
-    return {"read": reads, "mfma": mfma, "published": PEAK}
+    return {"read": reads, "mfma": mfma, "lds": lds, "published": PEAK}
 
 
 def roofline_for(shape, dtype, seconds, traffic=None, math="exact"):

@@ -26,6 +26,12 @@ def load():
     lib.cwprobe_mfma.restype = ctypes.c_int
     lib.cwprobe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.cwprobe_mfma16.restype = ctypes.c_int
+    lib.cwprobe_mfma16.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+    lib.cwprobe_lds.restype = ctypes.c_int
+    lib.cwprobe_lds.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     _lib = lib
     return lib
 
@@ -46,3 +52,13 @@ def peak_mfma(dtype: int, iters: int, blocks: int, sink_ptr: int, stream: int, b
               end=None) -> None:
     """MFMA-loop probe (cwprobe_mfma): sink holds blocks * 256 floats."""
     _check(load().cwprobe_mfma(dtype, iters, blocks, sink_ptr, stream or None, begin, end), "peak_mfma")
+
+
+def peak_mfma16(iters: int, blocks: int, sink_ptr: int, stream: int, begin=None, end=None) -> None:
+    """16x16x32 bf16 MFMA-loop probe (cwprobe_mfma16): sink holds blocks * 256 floats."""
+    _check(load().cwprobe_mfma16(iters, blocks, sink_ptr, stream or None, begin, end), "peak_mfma16")
+
+
+def peak_lds(mode: int, iters: int, blocks: int, sink_ptr: int, stream: int, begin=None, end=None) -> None:
+    """LDS-read probe (cwprobe_lds): mode 0 transposed 8-byte, 1 plain 8-byte, 2 plain 16-byte reads."""
+    _check(load().cwprobe_lds(mode, iters, blocks, sink_ptr, stream or None, begin, end), "peak_lds")

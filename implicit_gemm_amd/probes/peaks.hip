@@ -1,7 +1,8 @@
-// Achievable-peak probes (gfx950): a streaming read of a device buffer and a
-// loop of independent MFMA chains.  They measure what the chip sustains on
-// the two resources the weight-gradient kernels are priced against (HBM
-// bandwidth, dense MFMA rate); they compute nothing of the gradient.
+// Achievable-peak probes (gfx950): a streaming read of a device buffer, loops
+// of independent MFMA chains and loops of LDS reads.  They measure what the
+// chip sustains on the resources the weight-gradient kernels are priced
+// against (HBM bandwidth, dense MFMA rate) or bound by (LDS operand reads);
+// they compute nothing of the gradient.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -90,6 +91,64 @@ __global__ __launch_bounds__(256) void peak_mfma_kernel(int64_t iters, float* __
   sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// iters rounds of 8 independent chains of v_mfma_f32_16x16x32_bf16 (the form
+// the 16-bit kernels use), as peak_mfma_kernel.
+__global__ __launch_bounds__(256) void peak_mfma16_kernel(int64_t iters, float* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)(1.0e-3f * (float)(1 + (lane & 15)));
+    b[e] = (__bf16)(1.0e-3f * (float)(1 + (lane >> 4)));
+  }
+  f32x4 acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = f32x4{(float)c, (float)lane, 0.f, 0.f};
+  for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+  sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+// LDS reads of 256-lane workgroups (32 KB of LDS each): iters rounds of 8
+// reads per lane at the addressing of the 16-bit kernels' operand reads (16
+// pixel rows of 64 channels at a 160-byte pitch), folded into registers.
+// kMode 0: ds_read_b64_tr_b16 (the transposed 8-byte read), 1: ds_read_b64,
+// 2: ds_read_b128.  Every address lies inside the 32 KB array.
+template <int kMode>
+__global__ __launch_bounds__(256) void peak_lds_kernel(int64_t iters, uint32_t* __restrict__ sink) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  __shared__ __attribute__((aligned(16))) unsigned short s[16384];
+  for (int i = threadIdx.x; i < 16384; i += 256) s[i] = (unsigned short)(i * 7);
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = lane & 15, gq = lane >> 4;
+  const int off = (8 * gq + (j >> 2)) * 80 + 4 * (j & 3) + 16 * wave;   // < 2300
+  uint32_t x0 = 0, x1 = 0, x2 = 0, x3 = 0;
+  for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int o = off + (int)((it * 8 + k) & 31) * 80;   // < 2300 + 31 * 80 + 8 < 16384
+      if constexpr (kMode == 0) {
+        const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(s + o));
+        x0 ^= (uint32_t)v[0]; x1 ^= (uint32_t)v[1]; x2 ^= (uint32_t)v[2]; x3 ^= (uint32_t)v[3];
+      } else if constexpr (kMode == 1) {
+        const uint2 v = *reinterpret_cast<const uint2*>(s + o);
+        x0 ^= v.x; x1 ^= v.y;
+      } else {
+        const uint4 v = *reinterpret_cast<const uint4*>(s + (o & ~7));
+        x0 ^= v.x; x1 ^= v.y; x2 ^= v.z; x3 ^= v.w;
+      }
+    }
+  }
+  if ((x0 ^ x1 ^ x2 ^ x3) == kNever) sink[blockIdx.x] = threadIdx.x;
+}
+
 conv_wgrad_status_t launch(const void* fn, int32_t blocks, void** params, void* stream, void* begin,
                            void* end) {
   const hipError_t e = hipExtLaunchKernel(fn, dim3((unsigned)blocks), dim3(256), params, 0,
@@ -123,5 +182,25 @@ extern "C" conv_wgrad_status_t cwprobe_mfma(int32_t dtype, int64_t iters, int32_
   const void* fn = dtype == CONV_WGRAD_F32    ? reinterpret_cast<const void*>(cw::peak_mfma_kernel<0>)
                    : dtype == CONV_WGRAD_BF16 ? reinterpret_cast<const void*>(cw::peak_mfma_kernel<1>)
                                               : reinterpret_cast<const void*>(cw::peak_mfma_kernel<2>);
+  return cw::launch(fn, blocks, params, stream, begin, end);
+}
+
+extern "C" conv_wgrad_status_t cwprobe_mfma16(int64_t iters, int32_t blocks, float* sink, void* stream, void* begin,
+                                              void* end) {
+  if (!sink) return CONV_WGRAD_ERR_NULL_ARG;
+  if (iters < 1 || iters > INT32_MAX || blocks < 1 || blocks > 65536) return CONV_WGRAD_ERR_BAD_SHAPE;
+  void* params[] = {&iters, &sink};
+  return cw::launch(reinterpret_cast<const void*>(cw::peak_mfma16_kernel), blocks, params, stream, begin, end);
+}
+
+extern "C" conv_wgrad_status_t cwprobe_lds(int32_t mode, int64_t iters, int32_t blocks, uint32_t* sink,
+                                           void* stream, void* begin, void* end) {
+  if (!sink) return CONV_WGRAD_ERR_NULL_ARG;
+  if (mode < 0 || mode > 2 || iters < 1 || iters > INT32_MAX || blocks < 1 || blocks > 65536)
+    return CONV_WGRAD_ERR_BAD_SHAPE;
+  void* params[] = {&iters, &sink};
+  const void* fn = mode == 0   ? reinterpret_cast<const void*>(cw::peak_lds_kernel<0>)
+                   : mode == 1 ? reinterpret_cast<const void*>(cw::peak_lds_kernel<1>)
+                               : reinterpret_cast<const void*>(cw::peak_lds_kernel<2>);
   return cw::launch(fn, blocks, params, stream, begin, end);
 }

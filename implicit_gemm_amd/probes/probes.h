@@ -62,6 +62,27 @@ conv_wgrad_status_t cwprobe_read(const void* src, int64_t nbytes, int32_t blocks
 conv_wgrad_status_t cwprobe_mfma(int32_t dtype, int64_t iters, int32_t blocks, float* sink,
                                          void* stream, void* begin, void* end);
 
+/* cwprobe_mfma16: as cwprobe_mfma for bf16, with 8 independent chains of
+ * v_mfma_f32_16x16x32_bf16 (16384 FLOP each, 131072 per round and wave), the
+ * form the 16-bit weight-gradient kernels issue.  FLOPs per call:
+ * blocks * 4 * iters * 131072.  Same argument checks and errors. */
+conv_wgrad_status_t cwprobe_mfma16(int64_t iters, int32_t blocks, float* sink, void* stream, void* begin,
+                                   void* end);
+
+/* cwprobe_lds: LDS read rate.  `blocks` workgroups of 256 lanes, each with a
+ * 32 KB LDS array, run `iters` rounds of 8 reads per lane at the addressing
+ * of the 16-bit kernels' operand reads (16 pixel rows of 64 channels at a
+ * 160-byte pitch per wave), every read folded into registers:
+ *   mode 0: ds_read_b64_tr_b16 (8 bytes per lane), 1: ds_read_b64 (8 bytes),
+ *   2: ds_read_b128 (16 bytes); anything else is BAD_SHAPE
+ *   iters  : 1 .. 2^31 - 1, blocks: 1 .. 65536 (BAD_SHAPE otherwise)
+ *   sink   : device pointer to blocks uint32 (written only if the folded
+ *            value hits a fixed constant)
+ * LDS bytes read per call: blocks * 256 * iters * 8 * (8, 8 or 16).  NULL
+ * sink is NULL_ARG; a launch failure is ERR_HIP. */
+conv_wgrad_status_t cwprobe_lds(int32_t mode, int64_t iters, int32_t blocks, uint32_t* sink, void* stream,
+                                void* begin, void* end);
+
 #ifdef __cplusplus
 }
 #endif

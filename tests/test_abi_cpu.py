@@ -56,7 +56,7 @@ def test_probe_library_exports_its_declared_symbols():
     from implicit_gemm_amd import probes
     lib = probes.load()
     names = declared_functions(PROBES_HEADER, prefix="cwprobe")
-    assert set(names) == {"cwprobe_read", "cwprobe_mfma"}
+    assert set(names) == {"cwprobe_read", "cwprobe_mfma", "cwprobe_mfma16", "cwprobe_lds"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) <= exported_symbols(probes.LIB_PATH)
@@ -86,6 +86,12 @@ def test_peak_probe_argument_errors():
         assert lib.cwprobe_mfma(dtype, 1, 1, fake, None, None, None) == 3       # BAD_DTYPE
     for iters, blocks in ((0, 1), (1 << 31, 1), (1, 0), (1, 65537)):
         assert lib.cwprobe_mfma(0, iters, blocks, fake, None, None, None) == 2
+        assert lib.cwprobe_mfma16(iters, blocks, fake, None, None, None) == 2
+        assert lib.cwprobe_lds(0, iters, blocks, fake, None, None, None) == 2
+    assert lib.cwprobe_mfma16(1, 1, None, None, None, None) == 1
+    assert lib.cwprobe_lds(1, 1, 1, None, None, None, None) == 1
+    for mode in (-1, 3):
+        assert lib.cwprobe_lds(mode, 1, 1, fake, None, None, None) == 2
 
 
 def test_status_strings():
