@@ -245,6 +245,7 @@ ALL_RECORDS = [("c1_1x1_tiny_f32", None, {}), ("c2_3x3_f32", None, {}), ("c3_dw7
                ("l_3x3_c512_bf16", None, {"direction": "dgrad"})]
 HEADLINE = ("c5_1x1_big_f32", 192, {})
 FAMILY = {0: "dense_lds", 1: "dense_rows", 2: "dense_1x1", 3: "dense16_rows", 4: "dense16_rows_bf16x3",
+          5: "dense16_taps", 6: "dense16_taps_bf16x3",
           10: "direct_elem", 11: "grouped16", 12: "depthwise_mfma", 13: "grouped16_rows"}
 
 
