@@ -30,8 +30,19 @@
 //       the same SIMDs.  At the end the halves' accumulators are added (half 1
 //       into half 0, a fixed order) and half 0 writes the slab.
 //
-// Rows of the LDS tiles are 80 floats apart (16 mod 32 and 16 mod 64 banks),
-// so the 4 pixel rows a wave reads per MFMA fall in disjoint bank groups.
+// Two assignments of reduction rows to the MFMA k index:
+//   * interleaved: lane group lg (lanes 16lg .. 16lg + 15) takes pixel 4k + lg
+//     in k-step k, so each k-step reads SB X values (one per tap);
+//   * quarters (stride 1, dilation 1, one unit per output row, 256 lanes):
+//     lane group lg takes the contiguous pixels lg*Q .. lg*Q + Q - 1,
+//     Q = ceil(Wo / 4), pixel lg*Q + k in k-step k.  Tap s then reads X slot
+//     lg*Q + k + s, which tap s - 1 reads in k-step k + 1: each k-step reads
+//     one new X value and keeps the last SB - 1 in registers.
+// Staged pixel rows are P floats apart, chosen so that the 4 rows a wave reads
+// per MFMA fall in disjoint bank groups (offsets 16 mod 32 and 16 or 48 mod
+// 64 banks between lane groups): P = 80 for the interleaved form (rows 1
+// apart), 112 for odd Q and 88 for Q = 2 mod 4 (rows Q apart); Q = 0 mod 4
+// has no such pitch and keeps the interleaved form.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -39,9 +50,24 @@ namespace cw {
 
 namespace {
 
-constexpr int kPitch = 80;      // floats per staged pixel row (64 channels + pad)
+constexpr int kPitch = 80;      // floats per staged pixel row, interleaved form (64 channels + pad)
 constexpr int kMaxWt = 64;      // output pixels per unit
 constexpr int kMaxXSpan = 80;   // staged X pixels per unit
+
+// Calls f(integral_constant<K>) for K = 0, 1, ... while K < n (and K < N), as
+// nested conditional blocks: step K is entered only from step K - 1, and the
+// steps not taken all join once, after the last.  A flat unrolled loop of
+// `if (k < n)` blocks joins after every step instead, and a wait inserted at
+// such a join must cover the LDS reads in flight on any incoming path.
+template <int K, int N, typename F>
+__device__ __forceinline__ void steps_while(int n, F&& f) {
+  if constexpr (K < N) {
+    if (K < n) {
+      f(std::integral_constant<int, K>{});
+      steps_while<K + 1, N>(n, f);
+    }
+  }
+}
 
 struct RowsArgs {
   const void* x;
@@ -56,16 +82,20 @@ struct RowsArgs {
   int32_t wt, wchunks, xspan;
   int32_t units, units_per_slice, ks_count;
   int32_t tiles, work;   // tiles per slice, tiles * ks_count
+  int32_t q;             // pixels per lane group in the quarters form
   float* dbo;            // bias-gradient partial of slice 0 (slab_stride apart), or nullptr
 };
 
 // kUnit: column stride 1 and column dilation 1 are compile-time (every LDS offset of the
 // MFMA loop is an immediate); otherwise they are read from the arguments.
 // kSolo: the 256-lane form (no halves); otherwise 512 lanes in two halves.
-template <typename T, int SB, bool kUnit, bool kSolo>
+// P: the staged pixel pitch in floats; P != kPitch selects the quarters form.
+template <typename T, int SB, bool kUnit, bool kSolo, int P>
 __global__ __launch_bounds__(kSolo ? 256 : 512, kSolo ? 2 : 1) void dense_rows_kernel(RowsArgs a) {
   extern __shared__ float smem[];
-  constexpr int kBuf = (kMaxWt + kMaxXSpan) * kPitch;  // floats per half's buffer
+  constexpr bool kQuarters = P != kPitch;
+  static_assert(!kQuarters || (kUnit && kSolo), "quarters form: unit stride and dilation, 256 lanes");
+  constexpr int kBuf = (kMaxWt + kMaxXSpan) * P;  // floats per half's buffer
   const T* __restrict__ x = static_cast<const T*>(a.x);
   const T* __restrict__ dy = static_cast<const T*>(a.dy);
 
@@ -150,17 +180,17 @@ __global__ __launch_bounds__(kSolo ? 256 : 512, kSolo ? 2 : 1) void dense_rows_k
   auto store_unit = [&]() {
 #pragma unroll
     for (int i = 0; i < kMaxWt / 16; ++i) {
-      *reinterpret_cast<float4*>(&buf[(p0 + 16 * i) * kPitch + 4 * q]) =
+      *reinterpret_cast<float4*>(&buf[(p0 + 16 * i) * P + 4 * q]) =
           float4{ra[i][0], ra[i][1], ra[i][2], ra[i][3]};
       if (want_db) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) dbp[j] += ra[i][j];
       }
     }
-    float* xb = buf + kMaxWt * kPitch;
+    float* xb = buf + kMaxWt * P;
 #pragma unroll
     for (int i = 0; i < kMaxXSpan / 16; ++i)
-      *reinterpret_cast<float4*>(&xb[(p0 + 16 * i) * kPitch + 4 * q]) =
+      *reinterpret_cast<float4*>(&xb[(p0 + 16 * i) * P + 4 * q]) =
           float4{rb[i][0], rb[i][1], rb[i][2], rb[i][3]};
   };
 
@@ -174,38 +204,94 @@ __global__ __launch_bounds__(kSolo ? 256 : 512, kSolo ? 2 : 1) void dense_rows_k
   // Row li of M-block i is output channel m0 + 4*li + i, so a lane's four A
   // fragments are the 4 consecutive channels 4*li .. 4*li + 3 of its pixel
   // row: one 16-byte LDS read per k-step.
-  const float* const A = buf + lg * kPitch + 4 * li;                   // + 4*kstep rows
-  const float* const B = buf + kMaxWt * kPitch + lg * stride * kPitch + 16 * wave + li;
-  const int b_kstep = 4 * stride * kPitch;
-  const int b_tap = (kUnit ? 1 : a.dil_w) * kPitch;
+  const int row0 = kQuarters ? lg * a.q : lg;   // the lane group's first pixel slot
+  const float* const A = buf + row0 * P + 4 * li;
+  const float* const B = buf + kMaxWt * P + row0 * stride * P + 16 * wave + li;
+  const int b_kstep = (kQuarters ? 1 : 4) * stride * P;
+  const int b_tap = (kUnit ? 1 : a.dil_w) * P;
 
   // One unit's MFMAs: up to kMaxWt / 4 k-steps, fully unrolled so that every
   // LDS offset is an immediate (no VALU work between the MFMAs).  Two operand
   // sets alternate: the fragments of k-step k + 1 are read before the MFMAs of
   // k-step k issue.
-  auto compute_unit = [&](int npix) {
+  auto compute_interleaved = [&](int npix) {
     const int nk = (npix + 3) >> 2;
     float fa[2][4], fb[2][SB];
     auto read_k = [&](int k, float (&ra_)[4], float (&rb_)[SB]) {
-      const float4 av = *reinterpret_cast<const float4*>(A + 4 * k * kPitch);
+      const float4 av = *reinterpret_cast<const float4*>(A + 4 * k * P);
       ra_[0] = av.x; ra_[1] = av.y; ra_[2] = av.z; ra_[3] = av.w;
 #pragma unroll
       for (int s = 0; s < SB; ++s) rb_[s] = B[k * b_kstep + s * b_tap];
       // Keep the scheduler from hoisting the following MFMAs above the reads.
       __builtin_amdgcn_sched_barrier(0);
     };
+    auto mfmas = [&](int k) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int s = 0; s < SB; ++s)
+          acc[i][s] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[k & 1][i], fb[k & 1][s], acc[i][s], 0, 0, 0);
+    };
     if (nk > 0) read_k(0, fa[0], fb[0]);
+    if constexpr (kUnit) {
+      // Unit stride and dilation: the fragments one k-step past the last
+      // (pixel rows up to 63, X slots up to 66) lie inside the buffer, so the
+      // next step's reads need no condition and the steps nest.
+      steps_while<0, kMaxWt / 4>(nk, [&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        if constexpr (k + 1 < kMaxWt / 4) read_k(k + 1, fa[(k + 1) & 1], fb[(k + 1) & 1]);
+        mfmas(k);
+      });
+    } else {
+      // Strided or dilated X slots one step past the last may lie past the
+      // buffer: the reads stay conditional (a nested form with the last
+      // step's MFMAs duplicated measured 14 % slower).
 #pragma unroll
-    for (int k = 0; k < kMaxWt / 4; ++k) {
-      if (k < nk) {
-        if (k + 1 < nk) read_k(k + 1, fa[(k + 1) & 1], fb[(k + 1) & 1]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int s = 0; s < SB; ++s)
-            acc[i][s] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[k & 1][i], fb[k & 1][s], acc[i][s], 0, 0, 0);
+      for (int k = 0; k < kMaxWt / 4; ++k) {
+        if (k < nk) {
+          if (k + 1 < nk) read_k(k + 1, fa[(k + 1) & 1], fb[(k + 1) & 1]);
+          mfmas(k);
+        }
       }
     }
+  };
+  // Quarters form: k-step k reads the A fragments of pixel lg*Q + k + 1 and
+  // the one X value of slot lg*Q + k + SB ahead of its MFMAs; xw[j] holds X
+  // slot lg*Q + j (a register window of SB + 1 values once unrolled).  Every
+  // lane group has a valid pixel in k-step k < min(Q, npix); slots past npix
+  // hold zero dY.  The reads one step past the last (pixel row up to 4Q,
+  // X slot up to 4Q + SB - 1, Q <= 15) lie inside the buffer and are issued
+  // unconditionally, as in the interleaved form.
+  auto compute_quarters = [&](int npix) {
+    const int nk = min(a.q, npix);
+    float fa[2][4], xw[kMaxWt / 4 + SB];
+    auto read_a = [&](int k, float (&ra_)[4]) {
+      const float4 av = *reinterpret_cast<const float4*>(A + k * P);
+      ra_[0] = av.x; ra_[1] = av.y; ra_[2] = av.z; ra_[3] = av.w;
+    };
+    if (nk > 0) {
+      read_a(0, fa[0]);
+#pragma unroll
+      for (int s = 0; s < SB; ++s) xw[s] = B[s * P];
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    steps_while<0, kMaxWt / 4>(nk, [&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      if constexpr (k + 1 < kMaxWt / 4) {
+        read_a(k + 1, fa[(k + 1) & 1]);
+        xw[k + SB] = B[(k + SB) * P];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int s = 0; s < SB; ++s)
+          acc[i][s] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[k & 1][i], xw[k + s], acc[i][s], 0, 0, 0);
+    });
+  };
+  auto compute_unit = [&](int npix) {
+    if constexpr (kQuarters) compute_quarters(npix);
+    else compute_interleaved(npix);
   };
 
   if constexpr (kSolo) {
@@ -290,11 +376,11 @@ __global__ __launch_bounds__(kSolo ? 256 : 512, kSolo ? 2 : 1) void dense_rows_k
       }
 }
 
-template <typename T, int SB, bool kUnit, bool kSolo>
-hipError_t launch_sb(const RowsArgs& args, int64_t grid, hipStream_t stream) {
+template <typename T, int SB, bool kUnit, bool kSolo, int P>
+hipError_t launch_p(const RowsArgs& args, int64_t grid, hipStream_t stream) {
   // One staging buffer (256 lanes) or one per half (512 lanes).
-  constexpr size_t kLds = (kSolo ? 1 : 2) * (kMaxWt + kMaxXSpan) * kPitch * sizeof(float);
-  const void* fn = reinterpret_cast<const void*>(dense_rows_kernel<T, SB, kUnit, kSolo>);
+  constexpr size_t kLds = (kSolo ? 1 : 2) * (kMaxWt + kMaxXSpan) * P * sizeof(float);
+  const void* fn = reinterpret_cast<const void*>(dense_rows_kernel<T, SB, kUnit, kSolo, P>);
   // More than 64 KB of dynamic LDS must be enabled per kernel (once).
   if (kLds > 64 * 1024) {
     static const hipError_t attr =
@@ -304,6 +390,19 @@ hipError_t launch_sb(const RowsArgs& args, int64_t grid, hipStream_t stream) {
   void* params[] = {const_cast<RowsArgs*>(&args)};
   const int64_t xcd_grid = (grid + 7) / 8 * 8;   // whole rounds over the 8 XCDs
   return launch_raw(fn, dim3((unsigned)xcd_grid), dim3(kSolo ? 256 : 512), params, kLds, stream);
+}
+
+// The quarters form when it applies (unit stride and dilation, 256 lanes, one
+// unit per output row, Q = ceil(Wo / 4) not a multiple of 4), else interleaved.
+template <typename T, int SB, bool kUnit, bool kSolo>
+hipError_t launch_sb(const RowsArgs& args, int64_t grid, hipStream_t stream) {
+  if constexpr (kUnit && kSolo) {
+    if (args.wchunks == 1 && args.q % 4 != 0) {
+      if (args.q & 1) return launch_p<T, SB, kUnit, kSolo, 112>(args, grid, stream);
+      return launch_p<T, SB, kUnit, kSolo, 88>(args, grid, stream);
+    }
+  }
+  return launch_p<T, SB, kUnit, kSolo, kPitch>(args, grid, stream);
 }
 
 template <typename T, bool kUnit, bool kSolo>
@@ -359,6 +458,7 @@ hipError_t launch_dense_rows(const Plan& plan, const void* x, const void* dy, St
   a.ks_count = plan.pub.ks_count;
   a.tiles = (int32_t)plan.pub.tiles;
   a.work = (int32_t)plan.pub.grid;
+  a.q = (int32_t)((p.Wo + 3) / 4);
   switch (p.dtype) {
     case CONV_WGRAD_F32: return launch_t<float>(plan, a, stream);
     case CONV_WGRAD_BF16: return launch_t<Bf16>(plan, a, stream);
