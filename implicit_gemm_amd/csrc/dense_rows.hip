@@ -41,8 +41,11 @@
 // Staged pixel rows are P floats apart, chosen so that the 4 rows a wave reads
 // per MFMA fall in disjoint bank groups (offsets 16 mod 32 and 16 or 48 mod
 // 64 banks between lane groups): P = 80 for the interleaved form (rows 1
-// apart), 112 for odd Q and 88 for Q = 2 mod 4 (rows Q apart); Q = 0 mod 4
-// has no such pitch and keeps the interleaved form.
+// apart) and for odd Q, 72 for Q = 2 mod 4 (rows Q apart); Q = 0 mod 4 has
+// no such pitch and keeps the interleaved form.  The quarters form reads at
+// most 64 dY and 64 X pixel rows, so two buffers fit beside the other
+// workgroup on the CU: a unit is staged into the buffer the unit before last
+// used, and one barrier per unit suffices.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -53,6 +56,7 @@ namespace {
 constexpr int kPitch = 80;      // floats per staged pixel row, interleaved form (64 channels + pad)
 constexpr int kMaxWt = 64;      // output pixels per unit
 constexpr int kMaxXSpan = 80;   // staged X pixels per unit
+constexpr int kQuartersXSpan = 64;  // staged X pixels per unit, quarters form
 
 // Calls f(integral_constant<K>) for K = 0, 1, ... while K < n (and K < N), as
 // nested conditional blocks: step K is entered only from step K - 1, and the
@@ -89,13 +93,14 @@ struct RowsArgs {
 // kUnit: column stride 1 and column dilation 1 are compile-time (every LDS offset of the
 // MFMA loop is an immediate); otherwise they are read from the arguments.
 // kSolo: the 256-lane form (no halves); otherwise 512 lanes in two halves.
-// P: the staged pixel pitch in floats; P != kPitch selects the quarters form.
-template <typename T, int SB, bool kUnit, bool kSolo, int P>
+// P: the staged pixel pitch in floats.  kQuarters: the quarters form (two
+// buffers, one barrier per unit).
+template <typename T, int SB, bool kUnit, bool kSolo, int P, bool kQuarters>
 __global__ __launch_bounds__(kSolo ? 256 : 512, kSolo ? 2 : 1) void dense_rows_kernel(RowsArgs a) {
   extern __shared__ float smem[];
-  constexpr bool kQuarters = P != kPitch;
   static_assert(!kQuarters || (kUnit && kSolo), "quarters form: unit stride and dilation, 256 lanes");
-  constexpr int kBuf = (kMaxWt + kMaxXSpan) * P;  // floats per half's buffer
+  constexpr int kXSpan = kQuarters ? kQuartersXSpan : kMaxXSpan;
+  constexpr int kBuf = (kMaxWt + kXSpan) * P;  // floats per buffer
   const T* __restrict__ x = static_cast<const T*>(a.x);
   const T* __restrict__ dy = static_cast<const T*>(a.dy);
 
@@ -137,16 +142,16 @@ __global__ __launch_bounds__(kSolo ? 256 : 512, kSolo ? 2 : 1) void dense_rows_k
   const int x_col0 = g * a.Cg + c0;          // first input channel of the tile
   const int dh = r * a.dil_h - a.pad_h;
   const int xw_off = s0 * a.dil_w - a.pad_w;
-  int oa[kMaxWt / 16], ob[kMaxXSpan / 16];
+  int oa[kMaxWt / 16], ob[kXSpan / 16];
 #pragma unroll
   for (int i = 0; i < kMaxWt / 16; ++i) oa[i] = ((p0 + 16 * i) * a.K + 4 * q) * kEs;
 #pragma unroll
-  for (int i = 0; i < kMaxXSpan / 16; ++i) ob[i] = ((p0 + 16 * i) * a.C + 4 * q) * kEs;
+  for (int i = 0; i < kXSpan / 16; ++i) ob[i] = ((p0 + 16 * i) * a.C + 4 * q) * kEs;
   const int x_row_bytes = (a.W * a.C - x_col0) * kEs;
 
   // Staged operands of one unit, as loaded.
   float ra[kMaxWt / 16][4];
-  float rb[kMaxXSpan / 16][4];
+  float rb[kXSpan / 16][4];
   int npix_reg = 0;
 
   auto load_unit = [&](int u) {
@@ -167,7 +172,7 @@ __global__ __launch_bounds__(kSolo ? 256 : 512, kSolo ? 2 : 1) void dense_rows_k
     const __amdgpu_buffer_rsrc_t rs_b = buf_rsrc(xp, row_ok ? x_row_bytes : 0);
     const int wb = w0 * a.C * kEs;
 #pragma unroll
-    for (int i = 0; i < kMaxXSpan / 16; ++i) buf_load4(rs_b, ob[i] + wb, xp, rb[i]);
+    for (int i = 0; i < kXSpan / 16; ++i) buf_load4(rs_b, ob[i] + wb, xp, rb[i]);
   };
 
   // Bias gradient: the tile with the first filter row, tap block and input
@@ -176,8 +181,7 @@ __global__ __launch_bounds__(kSolo ? 256 : 512, kSolo ? 2 : 1) void dense_rows_k
   // zero), per thread for its 4 channels.
   const bool want_db = a.dbo != nullptr && r == 0 && sb == 0 && ct == 0;
   float dbp[4] = {0.f, 0.f, 0.f, 0.f};
-  float* const buf = smem + half * kBuf;
-  auto store_unit = [&]() {
+  auto store_unit = [&](float* buf) {
 #pragma unroll
     for (int i = 0; i < kMaxWt / 16; ++i) {
       *reinterpret_cast<float4*>(&buf[(p0 + 16 * i) * P + 4 * q]) =
@@ -189,7 +193,7 @@ __global__ __launch_bounds__(kSolo ? 256 : 512, kSolo ? 2 : 1) void dense_rows_k
     }
     float* xb = buf + kMaxWt * P;
 #pragma unroll
-    for (int i = 0; i < kMaxXSpan / 16; ++i)
+    for (int i = 0; i < kXSpan / 16; ++i)
       *reinterpret_cast<float4*>(&xb[(p0 + 16 * i) * P + 4 * q]) =
           float4{rb[i][0], rb[i][1], rb[i][2], rb[i][3]};
   };
@@ -205,8 +209,9 @@ __global__ __launch_bounds__(kSolo ? 256 : 512, kSolo ? 2 : 1) void dense_rows_k
   // fragments are the 4 consecutive channels 4*li .. 4*li + 3 of its pixel
   // row: one 16-byte LDS read per k-step.
   const int row0 = kQuarters ? lg * a.q : lg;   // the lane group's first pixel slot
-  const float* const A = buf + row0 * P + 4 * li;
-  const float* const B = buf + kMaxWt * P + row0 * stride * P + 16 * wave + li;
+  float* const buf = smem + half * kBuf;         // the half's buffer (the first buffer)
+  const float* const A0 = buf + row0 * P + 4 * li;
+  const float* const B0 = buf + kMaxWt * P + row0 * stride * P + 16 * wave + li;
   const int b_kstep = (kQuarters ? 1 : 4) * stride * P;
   const int b_tap = (kUnit ? 1 : a.dil_w) * P;
 
@@ -216,6 +221,8 @@ __global__ __launch_bounds__(kSolo ? 256 : 512, kSolo ? 2 : 1) void dense_rows_k
   // k-step k issue.
   auto compute_interleaved = [&](int npix) {
     const int nk = (npix + 3) >> 2;
+    const float* const A = A0;
+    const float* const B = B0;
     float fa[2][4], fb[2][SB];
     auto read_k = [&](int k, float (&ra_)[4], float (&rb_)[SB]) {
       const float4 av = *reinterpret_cast<const float4*>(A + 4 * k * P);
@@ -262,8 +269,10 @@ __global__ __launch_bounds__(kSolo ? 256 : 512, kSolo ? 2 : 1) void dense_rows_k
   // hold zero dY.  The reads one step past the last (pixel row up to 4Q,
   // X slot up to 4Q + SB - 1, Q <= 15) lie inside the buffer and are issued
   // unconditionally, as in the interleaved form.
-  auto compute_quarters = [&](int npix) {
+  auto compute_quarters = [&](int npix, int boff) {
     const int nk = min(a.q, npix);
+    const float* const A = A0 + boff;
+    const float* const B = B0 + boff;
     float fa[2][4], xw[kMaxWt / 4 + SB];
     auto read_a = [&](int k, float (&ra_)[4]) {
       const float4 av = *reinterpret_cast<const float4*>(A + k * P);
@@ -289,24 +298,38 @@ __global__ __launch_bounds__(kSolo ? 256 : 512, kSolo ? 2 : 1) void dense_rows_k
           acc[i][s] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[k & 1][i], xw[k + s], acc[i][s], 0, 0, 0);
     });
   };
-  auto compute_unit = [&](int npix) {
-    if constexpr (kQuarters) compute_quarters(npix);
-    else compute_interleaved(npix);
-  };
 
-  if constexpr (kSolo) {
+  if constexpr (kQuarters) {
+    // Unit p is staged into buffer p & 1 (its loads were issued one unit
+    // earlier), the next unit's loads are issued, and after one barrier it
+    // is computed.  Buffer p & 1 was last read by unit p - 2, which every
+    // wave finished before the barrier of unit p - 1.
+    if (nu > 0) load_unit(u_begin);
+    for (int p = 0; p < nu; ++p) {
+      const int npix = npix_reg;
+      const int boff = (p & 1) * kBuf;
+      store_unit(smem + boff);
+      if (p + 1 < nu) load_unit(u_begin + p + 1);
+      lds_barrier();   // LDS only: the next unit's loads stay in flight
+      compute_quarters(npix, boff);
+    }
+    if (want_db)   // block_sum64 begins with a barrier: every wave is past its last unit
+      block_sum64<16, 4>(smem, p0, 4 * q, dbp,
+                         a.dbo + (int64_t)slice * a.slab_stride + (int64_t)g * a.Kg + m0,
+                         min(64, a.Kg - m0));
+  } else if constexpr (kSolo) {
     // Unit by unit: stage it (its loads were issued one unit earlier), issue
     // the next unit's loads, compute it; the second barrier keeps the next
     // staging off the buffer until every wave has read it.
     if (nu > 0) load_unit(u_begin);
     for (int p = 0; p < nu; ++p) {
       const int npix = npix_reg;
-      store_unit();
+      store_unit(buf);
       if (p + 1 < nu) load_unit(u_begin + p + 1);
       // LDS-only barriers: the next unit's loads stay in flight over the
       // MFMAs (__syncthreads would also wait for them).
       lds_barrier();
-      compute_unit(npix);
+      compute_interleaved(npix);
       lds_barrier();
     }
     if (want_db)   // 16 loader rows per channel quad
@@ -324,12 +347,12 @@ __global__ __launch_bounds__(kSolo ? 256 : 512, kSolo ? 2 : 1) void dense_rows_k
       const bool comp = (p & 1) != half && p >= 1;
       if (stage) {
         npix_cur = npix_reg;
-        store_unit();
+        store_unit(buf);
         if (p + 2 < nu) load_unit(u_begin + p + 2);
       }
       // Called on every phase (with no pixels when staging) so that the
       // accumulators take one path through the loop.
-      compute_unit(comp ? npix_cur : 0);
+      compute_interleaved(comp ? npix_cur : 0);
       lds_barrier();   // LDS only: the loads issued two phases ahead stay in flight
     }
 
@@ -376,11 +399,14 @@ __global__ __launch_bounds__(kSolo ? 256 : 512, kSolo ? 2 : 1) void dense_rows_k
       }
 }
 
-template <typename T, int SB, bool kUnit, bool kSolo, int P>
+template <typename T, int SB, bool kUnit, bool kSolo, int P, bool kQuarters>
 hipError_t launch_p(const RowsArgs& args, int64_t grid, hipStream_t stream) {
-  // One staging buffer (256 lanes) or one per half (512 lanes).
-  constexpr size_t kLds = (kSolo ? 1 : 2) * (kMaxWt + kMaxXSpan) * P * sizeof(float);
-  const void* fn = reinterpret_cast<const void*>(dense_rows_kernel<T, SB, kUnit, kSolo, P>);
+  // One staging buffer (256 lanes), one per half (512 lanes) or two of 128
+  // pixel rows (quarters form: 73.7 or 80 KB, two workgroups per CU).
+  constexpr size_t kLds = kQuarters ? 2 * (kMaxWt + kQuartersXSpan) * P * sizeof(float)
+                                    : (kSolo ? 1 : 2) * (kMaxWt + kMaxXSpan) * P * sizeof(float);
+  static_assert(2 * kLds <= 160 * 1024 || !kSolo, "two workgroups per CU");
+  const void* fn = reinterpret_cast<const void*>(dense_rows_kernel<T, SB, kUnit, kSolo, P, kQuarters>);
   // More than 64 KB of dynamic LDS must be enabled per kernel (once).
   if (kLds > 64 * 1024) {
     static const hipError_t attr =
@@ -398,11 +424,11 @@ template <typename T, int SB, bool kUnit, bool kSolo>
 hipError_t launch_sb(const RowsArgs& args, int64_t grid, hipStream_t stream) {
   if constexpr (kUnit && kSolo) {
     if (args.wchunks == 1 && args.q % 4 != 0) {
-      if (args.q & 1) return launch_p<T, SB, kUnit, kSolo, 112>(args, grid, stream);
-      return launch_p<T, SB, kUnit, kSolo, 88>(args, grid, stream);
+      if (args.q & 1) return launch_p<T, SB, kUnit, kSolo, 80, true>(args, grid, stream);
+      return launch_p<T, SB, kUnit, kSolo, 72, true>(args, grid, stream);
     }
   }
-  return launch_p<T, SB, kUnit, kSolo, kPitch>(args, grid, stream);
+  return launch_p<T, SB, kUnit, kSolo, kPitch, false>(args, grid, stream);
 }
 
 template <typename T, bool kUnit, bool kSolo>
