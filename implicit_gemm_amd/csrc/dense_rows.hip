@@ -46,6 +46,15 @@
 // most 64 dY and 64 X pixel rows, so two buffers fit beside the other
 // workgroup on the CU: a unit is staged into the buffer the unit before last
 // used, and one barrier per unit suffices.
+//   * packed rows (stride 1, dilation 1, Wo <= 14 and Wo + SB - 1 <= 16 (the
+//     16 columns the loader stages per row), 256 lanes): a unit is 4
+//     consecutive output rows of one image and lane group lg takes row lg,
+//     pixel k in k-step k.  dY row lg is staged at slots lg*QA .., its X
+//     segment (Wo + SB - 1 pixels) at X slots lg*QB .., with QA >= Wo and
+//     QB >= Wo + SB - 1 both 2 mod 4 under pitch 72 (lane groups in disjoint
+//     banks); tap s reads X slot lg*QB + k + s, so the one-new-X-value window
+//     of the quarters form applies, on 4x the pixels of a one-row unit.
+//     Two buffers of 64 dY + 72 X pixel rows, one barrier per unit.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -57,6 +66,11 @@ constexpr int kPitch = 80;      // floats per staged pixel row, interleaved form
 constexpr int kMaxWt = 64;      // output pixels per unit
 constexpr int kMaxXSpan = 80;   // staged X pixels per unit
 constexpr int kQuartersXSpan = 64;  // staged X pixels per unit, quarters form
+constexpr int kPackedXSpan = 72;    // staged X pixel slots per unit, packed rows
+constexpr int kPackedRows = 4;      // output rows per unit, packed rows
+
+// Forms of the kernel (template argument kForm).
+constexpr int kInterleaved = 0, kQuartersForm = 1, kPackedForm = 2;
 
 // Calls f(integral_constant<K>) for K = 0, 1, ... while K < n (and K < N), as
 // nested conditional blocks: step K is entered only from step K - 1, and the
@@ -86,20 +100,25 @@ struct RowsArgs {
   int32_t wt, wchunks, xspan;
   int32_t units, units_per_slice, ks_count;
   int32_t tiles, work;   // tiles per slice, tiles * ks_count
-  int32_t q;             // pixels per lane group in the quarters form
+  int32_t q;             // quarters: pixels per lane group; packed: dY slots between lane groups
+  int32_t qb;            // X slots between lane groups (quarters: q)
+  int32_t qk;            // k-steps per unit (quarters: q; packed: Wo)
+  int32_t hunits;        // packed: units per image (ceil(Ho / 4))
   float* dbo;            // bias-gradient partial of slice 0 (slab_stride apart), or nullptr
 };
 
 // kUnit: column stride 1 and column dilation 1 are compile-time (every LDS offset of the
 // MFMA loop is an immediate); otherwise they are read from the arguments.
 // kSolo: the 256-lane form (no halves); otherwise 512 lanes in two halves.
-// P: the staged pixel pitch in floats.  kQuarters: the quarters form (two
-// buffers, one barrier per unit).
-template <typename T, int SB, bool kUnit, bool kSolo, int P, bool kQuarters>
+// P: the staged pixel pitch in floats.  kForm: interleaved, quarters or
+// packed rows (the last two: two buffers, one barrier per unit).
+template <typename T, int SB, bool kUnit, bool kSolo, int P, int kForm>
 __global__ __launch_bounds__(kSolo ? 256 : 512, kSolo ? 2 : 1) void dense_rows_kernel(RowsArgs a) {
   extern __shared__ float smem[];
-  static_assert(!kQuarters || (kUnit && kSolo), "quarters form: unit stride and dilation, 256 lanes");
-  constexpr int kXSpan = kQuarters ? kQuartersXSpan : kMaxXSpan;
+  constexpr bool kQuarters = kForm != kInterleaved;   // quarters or packed: the window schedule
+  constexpr bool kPacked = kForm == kPackedForm;
+  static_assert(!kQuarters || (kUnit && kSolo), "quarters / packed: unit stride and dilation, 256 lanes");
+  constexpr int kXSpan = kPacked ? kPackedXSpan : kQuarters ? kQuartersXSpan : kMaxXSpan;
   constexpr int kBuf = (kMaxWt + kXSpan) * P;  // floats per buffer
   const T* __restrict__ x = static_cast<const T*>(a.x);
   const T* __restrict__ dy = static_cast<const T*>(a.dy);
@@ -154,7 +173,31 @@ __global__ __launch_bounds__(kSolo ? 256 : 512, kSolo ? 2 : 1) void dense_rows_k
   float rb[kXSpan / 16][4];
   int npix_reg = 0;
 
+  // Packed rows: lane row p0 is the pixel column (16 per row), ra[i] / rb[i]
+  // hold dY row ho0 + i and its X segment.
+  auto load_packed = [&](int u) {
+    const int n = u / a.hunits;
+    const int ho0 = (u - n * a.hunits) * kPackedRows;
+    npix_reg = a.Wo;
+    const int da = (p0 * a.K + 4 * q) * kEs;
+    const int xa = (p0 * a.C + 4 * q) * kEs + xw_off * a.C * kEs;
+#pragma unroll
+    for (int i = 0; i < kPackedRows; ++i) {
+      const int ho = ho0 + i;
+      const bool ok = ho < a.Ho;
+      const T* dyp = dy + ((int64_t)n * a.Ho + (ok ? ho : 0)) * a.Wo * a.K + dy_col0;
+      buf_load4(buf_rsrc(dyp, ok ? (a.Wo * a.K - dy_col0) * kEs : 0), da, dyp, ra[i]);
+      const int h = ho * a.stride_h + dh;
+      const bool xok = ok && h >= 0 && h < a.H;
+      const T* xp = x + (int64_t)n * a.x_img + (int64_t)(xok ? h : 0) * a.W * a.C + x_col0;
+      buf_load4(buf_rsrc(xp, xok ? x_row_bytes : 0), xa, xp, rb[i]);
+    }
+  };
   auto load_unit = [&](int u) {
+    if constexpr (kPacked) {
+      load_packed(u);
+      return;
+    }
     const int wc = u % a.wchunks;
     const int t = u / a.wchunks;
     const int ho = t % a.Ho, n = t / a.Ho;
@@ -181,7 +224,29 @@ __global__ __launch_bounds__(kSolo ? 256 : 512, kSolo ? 2 : 1) void dense_rows_k
   // zero), per thread for its 4 channels.
   const bool want_db = a.dbo != nullptr && r == 0 && sb == 0 && ct == 0;
   float dbp[4] = {0.f, 0.f, 0.f, 0.f};
+  auto store_packed = [&](float* buf) {
+    // Columns past a row's slots belong to the next row: dY columns from QA
+    // and X columns from QB on are not stored (they would be zero or unread).
+    float* xb = buf + kMaxWt * P;
+#pragma unroll
+    for (int i = 0; i < kPackedRows; ++i) {
+      if (p0 < a.q)
+        *reinterpret_cast<float4*>(&buf[(i * a.q + p0) * P + 4 * q]) =
+            float4{ra[i][0], ra[i][1], ra[i][2], ra[i][3]};
+      if (p0 < a.qb)
+        *reinterpret_cast<float4*>(&xb[(i * a.qb + p0) * P + 4 * q]) =
+            float4{rb[i][0], rb[i][1], rb[i][2], rb[i][3]};
+      if (want_db) {   // dY pixels from Wo on loaded as zero
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dbp[j] += ra[i][j];
+      }
+    }
+  };
   auto store_unit = [&](float* buf) {
+    if constexpr (kPacked) {
+      store_packed(buf);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < kMaxWt / 16; ++i) {
       *reinterpret_cast<float4*>(&buf[(p0 + 16 * i) * P + 4 * q]) =
@@ -208,10 +273,11 @@ __global__ __launch_bounds__(kSolo ? 256 : 512, kSolo ? 2 : 1) void dense_rows_k
   // Row li of M-block i is output channel m0 + 4*li + i, so a lane's four A
   // fragments are the 4 consecutive channels 4*li .. 4*li + 3 of its pixel
   // row: one 16-byte LDS read per k-step.
-  const int row0 = kQuarters ? lg * a.q : lg;   // the lane group's first pixel slot
+  const int row0 = kQuarters ? lg * a.q : lg;   // the lane group's first dY pixel slot
+  const int xrow0 = kQuarters ? lg * a.qb : lg;  // ... and first X pixel slot
   float* const buf = smem + half * kBuf;         // the half's buffer (the first buffer)
   const float* const A0 = buf + row0 * P + 4 * li;
-  const float* const B0 = buf + kMaxWt * P + row0 * stride * P + 16 * wave + li;
+  const float* const B0 = buf + kMaxWt * P + xrow0 * stride * P + 16 * wave + li;
   const int b_kstep = (kQuarters ? 1 : 4) * stride * P;
   const int b_tap = (kUnit ? 1 : a.dil_w) * P;
 
@@ -268,9 +334,12 @@ __global__ __launch_bounds__(kSolo ? 256 : 512, kSolo ? 2 : 1) void dense_rows_k
   // lane group has a valid pixel in k-step k < min(Q, npix); slots past npix
   // hold zero dY.  The reads one step past the last (pixel row up to 4Q,
   // X slot up to 4Q + SB - 1, Q <= 15) lie inside the buffer and are issued
-  // unconditionally, as in the interleaved form.
+  // unconditionally, as in the interleaved form.  Packed rows: the same with
+  // X slots lg*QB + k + s and nk = Wo (rows past the image hold zero dY);
+  // the reads one step past the last reach dY slot 3 QA + Wo <= 56 and X
+  // slot 3 QB + Wo + SB - 1 <= 71.
   auto compute_quarters = [&](int npix, int boff) {
-    const int nk = min(a.q, npix);
+    const int nk = min(a.qk, npix);
     const float* const A = A0 + boff;
     const float* const B = B0 + boff;
     float fa[2][4], xw[kMaxWt / 4 + SB];
@@ -399,14 +468,16 @@ __global__ __launch_bounds__(kSolo ? 256 : 512, kSolo ? 2 : 1) void dense_rows_k
       }
 }
 
-template <typename T, int SB, bool kUnit, bool kSolo, int P, bool kQuarters>
+template <typename T, int SB, bool kUnit, bool kSolo, int P, int kForm>
 hipError_t launch_p(const RowsArgs& args, int64_t grid, hipStream_t stream) {
-  // One staging buffer (256 lanes), one per half (512 lanes) or two of 128
-  // pixel rows (quarters form: 73.7 or 80 KB, two workgroups per CU).
-  constexpr size_t kLds = kQuarters ? 2 * (kMaxWt + kQuartersXSpan) * P * sizeof(float)
-                                    : (kSolo ? 1 : 2) * (kMaxWt + kMaxXSpan) * P * sizeof(float);
+  // One staging buffer (256 lanes), one per half (512 lanes), two of 128
+  // pixel rows (quarters form: 73.7 or 80 KB) or two of 136 (packed rows:
+  // 78.3 KB); two workgroups per CU in the 256-lane forms.
+  constexpr size_t kLds = kForm == kPackedForm ? 2 * (kMaxWt + kPackedXSpan) * P * sizeof(float)
+                          : kForm == kQuartersForm ? 2 * (kMaxWt + kQuartersXSpan) * P * sizeof(float)
+                                                   : (kSolo ? 1 : 2) * (kMaxWt + kMaxXSpan) * P * sizeof(float);
   static_assert(2 * kLds <= 160 * 1024 || !kSolo, "two workgroups per CU");
-  const void* fn = reinterpret_cast<const void*>(dense_rows_kernel<T, SB, kUnit, kSolo, P, kQuarters>);
+  const void* fn = reinterpret_cast<const void*>(dense_rows_kernel<T, SB, kUnit, kSolo, P, kForm>);
   // More than 64 KB of dynamic LDS must be enabled per kernel (once).
   if (kLds > 64 * 1024) {
     static const hipError_t attr =
@@ -418,17 +489,19 @@ hipError_t launch_p(const RowsArgs& args, int64_t grid, hipStream_t stream) {
   return launch_raw(fn, dim3((unsigned)xcd_grid), dim3(kSolo ? 256 : 512), params, kLds, stream);
 }
 
-// The quarters form when it applies (unit stride and dilation, 256 lanes, one
-// unit per output row, Q = ceil(Wo / 4) not a multiple of 4), else interleaved.
+// Packed rows when the plan has them (hunits > 0); else the quarters form
+// when it applies (unit stride and dilation, 256 lanes, one unit per output
+// row, Q = ceil(Wo / 4) not a multiple of 4); else interleaved.
 template <typename T, int SB, bool kUnit, bool kSolo>
 hipError_t launch_sb(const RowsArgs& args, int64_t grid, hipStream_t stream) {
   if constexpr (kUnit && kSolo) {
+    if (args.hunits > 0) return launch_p<T, SB, kUnit, kSolo, 72, kPackedForm>(args, grid, stream);
     if (args.wchunks == 1 && args.q % 4 != 0) {
-      if (args.q & 1) return launch_p<T, SB, kUnit, kSolo, 80, true>(args, grid, stream);
-      return launch_p<T, SB, kUnit, kSolo, 72, true>(args, grid, stream);
+      if (args.q & 1) return launch_p<T, SB, kUnit, kSolo, 80, kQuartersForm>(args, grid, stream);
+      return launch_p<T, SB, kUnit, kSolo, 72, kQuartersForm>(args, grid, stream);
     }
   }
-  return launch_p<T, SB, kUnit, kSolo, kPitch, false>(args, grid, stream);
+  return launch_p<T, SB, kUnit, kSolo, kPitch, kInterleaved>(args, grid, stream);
 }
 
 template <typename T, bool kUnit, bool kSolo>
@@ -484,7 +557,15 @@ hipError_t launch_dense_rows(const Plan& plan, const void* x, const void* dy, St
   a.ks_count = plan.pub.ks_count;
   a.tiles = (int32_t)plan.pub.tiles;
   a.work = (int32_t)plan.pub.grid;
-  a.q = (int32_t)((p.Wo + 3) / 4);
+  if (plan.ru > 1) {   // packed rows
+    a.q = plan.qa;
+    a.qb = plan.qb;
+    a.qk = (int32_t)p.Wo;
+    a.hunits = (int32_t)ceil_div(p.Ho, plan.ru);
+  } else {
+    a.q = a.qb = a.qk = (int32_t)((p.Wo + 3) / 4);
+    a.hunits = 0;
+  }
   switch (p.dtype) {
     case CONV_WGRAD_F32: return launch_t<float>(plan, a, stream);
     case CONV_WGRAD_BF16: return launch_t<Bf16>(plan, a, stream);

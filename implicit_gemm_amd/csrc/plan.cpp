@@ -244,6 +244,29 @@ bool plan_dense_rows(const Problem& p, Plan* out) {
   out->c_tiles = ceil_div(p.Cg, 64);
   out->m_tiles = ceil_div(p.Kg, 64);
   out->wchunks = ceil_div(p.Wo, wt);
+  // Packed rows (dense_rows.hip): four output rows of at most 14 pixels per
+  // unit at unit row stride and unit column stride and dilation, each row's
+  // X segment (Wo + SB - 1 pixels) within the 16 columns the loader stages.
+  // A unit's rows are staged QA (dY) and QB (X) pixel slots apart, each the
+  // smallest of 2, 6, 10, 14 (, 18) that holds the row (QA * 72 and QB * 72
+  // are then 16 or 48 mod 64 banks); the reads one k-step past the last must
+  // stay in the 64 dY and 72 X slots.
+  out->ru = 1;
+  out->qa = out->qb = 0;
+  if (p.stride_h == 1 && p.stride_w == 1 && p.dil_w == 1 && p.Wo <= 14) {
+    auto slots = [](int64_t need, int64_t cap) -> int64_t {
+      for (int64_t c = 2; c <= cap; c += 4)
+        if (c >= need) return c;
+      return 0;
+    };
+    const int64_t xw = p.Wo + sb - 1;   // X pixels of a row segment
+    const int64_t qa = slots(p.Wo, 14), qb = slots(xw, 18);
+    if (xw <= 16 && qa > 0 && qb > 0 && 3 * qa + p.Wo <= 63 && 3 * qb + xw <= 71) {
+      out->ru = 4;
+      out->qa = (int32_t)qa;
+      out->qb = (int32_t)qb;
+    }
+  }
   return true;
 }
 
@@ -564,6 +587,17 @@ conv_wgrad_status_t make_plan(const conv_wgrad_desc2_t* desc, Plan* out) {
     if (!mul4(p.groups, out->m_tiles, p.R, out->s_blocks, &tiles) ||
         !mul_ok(tiles, out->c_tiles, &tiles))
       return CONV_WGRAD_ERR_UNSUPPORTED;
+    if (out->ru > 1) {
+      // Packed rows: 256 lanes, two workgroups per CU, about 768 workgroups
+      // (3x3 fp32 C=K=512 14x14 N=8, 192 tiles, cold call at 1 / 2 / 3 / 4 /
+      // 8 slices: 107 / 104 / 113 / 89 / 101 us); slabs may cost up to 6x
+      // the algorithmic bytes, since a deep reduction over few, short rows
+      // otherwise leaves most of the CUs idle.
+      pub.unit_rows = out->ru * p.Wo;
+      if (!mul_ok(p.N, ceil_div(p.Ho, out->ru), &units)) return CONV_WGRAD_ERR_UNSUPPORTED;
+      out->threads = 256;
+      return choose_split(units, tiles, desc->split_k, 2, 768, 1, p, &pub, 0, 6);
+    }
     // Two workgroup shapes (Plan::threads).  256 lanes, two workgroups per
     // CU, each staging and computing its own units: the CU interleaves the
     // two, so one's staging and barriers overlap the other's MFMAs and two

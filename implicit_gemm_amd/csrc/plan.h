@@ -61,7 +61,8 @@ struct Plan {
   int32_t sb, wt, xspan;   // taps per tile, output pixels per unit, staged X pixels per unit
   int64_t c_tiles, s_blocks, wchunks;
   int32_t bv;              // 1x1 kernel: input channels per lane
-  int32_t ru, xrows;       // grouped16: output rows per unit, staged X rows
+  int32_t ru, xrows;       // grouped16, 16-bit and fp32 packed rows: output rows per unit; staged X rows
+  int32_t qa, qb;          // fp32 packed rows: dY and X pixel slots between a unit's rows
   // Depthwise: staged X row length (elements), LDS bytes, column of dY element 0.
   int32_t dw_xl, dw_lds, dw_off;
   // Direct path: lanes per workgroup.  Row-unit dense kernel: 256 (two

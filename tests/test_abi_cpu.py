@@ -185,6 +185,10 @@ def check_plan_invariants(d, p):
         ru = 64 // (Wo + 2)
         assert d.R == d.S == 3 and d.stride == d.dilation == 1 and ru >= 1
         assert p.unit_rows == ru * Wo and p.units == d.N * -(-Ho // ru)
+    elif (p.path == iga.PATH_DENSE and p.variant == 1 and d.stride == d.dilation == 1 and Wo <= 14
+          and Wo + min(d.S, 4) - 1 <= 16):
+        # fp32 row kernel, packed rows: units of 4 whole output rows
+        assert p.unit_rows == 4 * Wo and p.units == d.N * -(-Ho // 4)
     elif p.path == iga.PATH_DENSE and p.variant in (1, 3):   # row units: (n, ho, chunk of Wo)
         assert p.units == d.N * Ho * -(-Wo // p.unit_rows)
     elif p.variant in (12, 13):                       # depthwise, row-streaming grouped: one output row per unit
@@ -273,11 +277,14 @@ def test_split_pinning_and_auto():
     p = iga.get_plan(D(N=1, H=2, W=2, R=1, S=1, pad=0, split_k=1000))
     assert p.ks_count == p.units
     # Auto: the row kernel's 256-lane form (two workgroups per CU) when the
-    # split reaches 1.5 workgroups per CU, else the 512-lane form (one per CU).
+    # split reaches 1.5 workgroups per CU, else the 512-lane form (one per CU);
+    # rows of at most 14 pixels: packed rows, about 768 workgroups.
     pa = iga.get_plan(D(N=32, C=64, H=56, W=56, K=64, split_k=-1))
     assert pa.variant == 1 and 384 <= pa.grid <= 512
     pb = iga.get_plan(D(N=8, C=512, H=14, W=14, K=512, split_k=-1))
-    assert pb.variant == 1 and pb.grid < 384 and pb.grid <= 256
+    assert pb.variant == 1 and pb.unit_rows == 4 * 14 and (pb.ks_count, pb.grid) == (4, 768)
+    pc = iga.get_plan(D(N=8, C=512, H=16, W=16, K=512, split_k=-1))   # Wo = 16: one-row units
+    assert pc.variant == 1 and pc.unit_rows == 16 and pc.grid <= 256
     # Launch-bound (2 * L * E <= 2^20 FLOP, automatic split): one launch on the
     # general kernel, no fold, no workspace; a pinned split is honoured.
     tiny = D(N=2, C=8, H=8, W=8, K=4, R=1, S=1, pad=0, split_k=-1)
