@@ -176,17 +176,28 @@ __global__ __launch_bounds__(256) void dense_lds_kernel(DenseArgs a) {
     }
     __syncthreads();
     if (l0 + kBK < l_end) load_step(l0 + kBK);  // overlap the next step's loads with MFMA
+    // The operands of k-step kk + 1 are read before the MFMAs of kk issue
+    // (two register sets), so each read has the previous step's MFMAs to
+    // arrive instead of being waited for right before its own.
+    float fa[2][2], fb[2][2];
+    auto read_k = [&](int kk, float (&ra_)[2], float (&rb_)[2]) {
+      const int rrow = 4 * kk + lg;
+      ra_[0] = sA[rrow * kLdA + wm * 32 + li];
+      ra_[1] = sA[rrow * kLdA + wm * 32 + 16 + li];
+      rb_[0] = sB[rrow * kLdB + wn * 32 + li];
+      rb_[1] = sB[rrow * kLdB + wn * 32 + 16 + li];
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    read_k(0, fa[0], fb[0]);
 #pragma unroll
     for (int kk = 0; kk < kBK / 4; ++kk) {
-      const int rrow = 4 * kk + lg;
-      const float a0 = sA[rrow * kLdA + wm * 32 + li];
-      const float a1 = sA[rrow * kLdA + wm * 32 + 16 + li];
-      const float b0 = sB[rrow * kLdB + wn * 32 + li];
-      const float b1 = sB[rrow * kLdB + wn * 32 + 16 + li];
-      acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc[1][1], 0, 0, 0);
+      if (kk + 1 < kBK / 4) read_k(kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+      const float(&a)[2] = fa[kk & 1];
+      const float(&b)[2] = fb[kk & 1];
+      acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[1], acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[0], acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc[1][1], 0, 0, 0);
     }
   }
 
