@@ -630,7 +630,11 @@ conv_wgrad_status_t make_plan(const conv_wgrad_desc2_t* desc, Plan* out) {
   int64_t units = ceil_div(p.L, pub.unit_rows);
   int64_t tiles;
   if (!mul3(p.groups, out->m_tiles, out->n_tiles, &tiles)) return CONV_WGRAD_ERR_UNSUPPORTED;
-  return choose_split(units, tiles, tiny ? 1 : desc->split_k, 8, 1024, 4, p, &pub);
+  // About 8 workgroups per CU (the kernel's 20 KB of LDS allow it, and the
+  // waves hide each other's staging and loads), slabs up to the algorithmic
+  // bytes: 16x16 stride-16 patch embedding fp32 N=64 (144 tiles), 2 / 4 / 8 /
+  // 16 / 24 slices: 327 / 228 / 179 / 167 / 179 us hot.
+  return choose_split(units, tiles, tiny ? 1 : desc->split_k, 8, 2048, 1, p, &pub);
 }
 
 conv_wgrad_status_t make_igemm_plan(const conv_wgrad_desc2_t* desc, int32_t direction, Plan* out) {
