@@ -613,6 +613,13 @@ conv_wgrad_status_t make_plan(const conv_wgrad_desc2_t* desc, Plan* out) {
     if (st != CONV_WGRAD_OK) return st;
     if (pub.grid >= 384) {
       out->threads = 256;
+      // The interleaved form (strided or dilated columns, rows wider than a
+      // unit, or ceil(Wo / 4) a multiple of 4) gains from about 768
+      // workgroups (3x3 fp32 C=K=64 N=32, stride 2 / dilation 2, 163 vs 256
+      // slices: 91.3 vs 84.8 / 82.2 vs 79.8 us cold); the quarters form does
+      // not (56x56: 78.3 vs 95.3 us).
+      const bool quarters = p.stride_w == 1 && p.dil_w == 1 && out->wchunks == 1 && ((p.Wo + 3) / 4) % 4 != 0;
+      if (!quarters && desc->split_k < 1) return choose_split(units, tiles, desc->split_k, 2, 768, 1, p, &pub, 0, 2);
       return CONV_WGRAD_OK;
     }
     out->threads = 512;
