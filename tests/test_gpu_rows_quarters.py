@@ -134,3 +134,55 @@ def test_rows_kernel_packed_rows_16bit(dtype):
     assert err <= oracle.TOL[dtype]
     assert np.all(np.isfinite(got)) and np.count_nonzero(got == 0.0) == 0
     check_bias_against_oracle(dy, db.cpu().numpy(), dtype)
+
+
+def _random_rows_case(rng):
+    """A random fp32 problem the row kernel takes: channel counts in quads,
+    unit strides (row stride 2 now and then), filters up to 5x5, per-axis
+    padding, groups, output widths 1..14 (packed rows) half of the time and
+    15..64 otherwise, a random pinned or automatic split."""
+    groups = int(rng.choice([1, 1, 1, 2, 4]))
+    C = groups * 4 * int(rng.integers(1, 20))
+    K = groups * 4 * int(rng.integers(1, 20))
+    R, S = int(rng.integers(1, 6)), int(rng.integers(1, 6))
+    pad = (int(rng.integers(0, R)), int(rng.integers(0, S)))
+    stride = (int(rng.choice([1, 1, 1, 2])), 1)
+    Wo = int(rng.integers(1, 15)) if rng.integers(0, 2) else int(rng.integers(15, 65))
+    W = Wo - 1 + S - 2 * pad[1]
+    if W < 1:
+        pad = (pad[0], 0)
+        W = Wo - 1 + S
+    H = int(rng.integers(max(1, R - 2 * pad[0]), 24))
+    N = int(rng.integers(1, 17))
+    split = int(rng.choice([-1, -1, 1, 2, 3, 5, 17, 64, 1000]))
+    bias = bool(rng.integers(0, 2))
+    return N, C, H, W, K, R, S, pad, stride, groups, split, bias
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_rows_kernel_random_shapes(seed):
+    import torch
+    import implicit_gemm_amd as iga
+    rng = np.random.default_rng(9500 + seed)
+    for _ in range(50):   # draw until the planner gives the row kernel
+        N, C, H, W, K, R, S, pad, stride, groups, split, bias = _random_rows_case(rng)
+        d = iga.make_desc2(N, C, H, W, K, R, S, pad, stride, (1, 1), groups, 0, split, "exact", -1)
+        if iga.get_plan2(d).base.variant == ROWS_VARIANT:
+            break
+    else:
+        pytest.skip("no row-kernel shape drawn")
+    case = (N, C, H, W, K, R, S, pad, stride, groups, split, bias)
+    log("rows random case", seed, case)
+    x, dy = _inputs(N, C, H, W, K, R, S, pad, 9600 + seed, stride)
+    xd, dyd = to_device(x, "f32"), to_device(dy, "f32")
+    plan = iga.get_plan2(iga.desc2_for(xd, dyd, R, S, pad, stride, 1, groups, split, "exact", -1))
+    out = iga.wgrad(xd, dyd, R, S, pad, stride, 1, groups, split_k=split, bias=bias)
+    torch.cuda.synchronize()
+    got = (out[0] if bias else out).cpu().numpy().astype(np.float64)
+    ref, den = oracle.wgrad_ref(x, dy, R, S, pad, stride, 1, groups)
+    err = oracle.normalised_error(got, ref, den)
+    log("  unit rows", plan.base.unit_rows, "ks", plan.base.ks_count, "grid", plan.base.grid, "error %.3e" % err)
+    assert err <= oracle.TOL["f32"], "normalised error %.3e" % err
+    assert np.all(np.isfinite(got))
+    if bias:
+        check_bias_against_oracle(dy, out[1].cpu().numpy(), "f32")
