@@ -65,6 +65,8 @@ struct DwArgs {
   int32_t rows, rows_per_slice, ks_count;  // rows = N * Ho
   int32_t quads;           // ceil(C / 64)
   float* dbo;              // bias-gradient partial of slice 0 (slab_stride apart), or nullptr
+  int32_t balanced;        // slice s covers rows [starts[s], starts[s + 1]); else uniform runs
+  int32_t starts[Plan::kDwMaxSlices + 1];
 };
 
 // LDS layout for staged rows of XL columns.
@@ -132,8 +134,9 @@ __global__ __launch_bounds__(kThreads) void depthwise_mfma_kernel(DwArgs a) {
   const int quad = w % a.quads;
   const int slice = w / a.quads;
   const int c0 = quad * kQuadCh;
-  const int r_begin = slice * a.rows_per_slice;
-  const int r_end = min(a.rows, r_begin + a.rows_per_slice);
+  // Slices balanced by staging steps (boundaries from the plan), else uniform.
+  const int r_begin = a.balanced ? a.starts[slice] : slice * a.rows_per_slice;
+  const int r_end = a.balanced ? a.starts[slice + 1] : min(a.rows, r_begin + a.rows_per_slice);
 
   // Zero both dY buffers once: their columns outside the dY row are never written.
   for (int i = L::kDyBase + tid * 16; i < L::kBytes; i += kThreads * 16)
@@ -456,6 +459,9 @@ hipError_t launch_depthwise(const Plan& plan, const void* x, const void* dy, Sta
   a.ks_count = plan.pub.ks_count;
   a.quads = (int32_t)ceil_div(p.C, 64);
   a.dbo = out.db;
+  a.balanced = plan.dw_balanced;
+  if (a.balanced)
+    for (int i = 0; i <= a.ks_count; ++i) a.starts[i] = plan.dw_starts[i];
   if (p.dtype == CONV_WGRAD_BF16) return launch_b<true>(plan, a, stream);
   return launch_b<false>(plan, a, stream);
 }

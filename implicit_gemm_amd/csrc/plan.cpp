@@ -450,6 +450,60 @@ bool plan_depthwise(const Problem& p, Plan* out) {
 
 }  // namespace
 
+// Depthwise slices balanced by staging steps.  A slice of output rows stages,
+// per image segment of len rows, stride * (len - 1) + R X rows (one step
+// each); uniform runs of rows leave the slices that straddle an image
+// boundary R - 1 steps longer than the others, and the longest slice sets the
+// kernel's time.  For the planned slice count: the smallest largest-cost T a
+// greedy fill needs at most that many slices for (binary search), that fill,
+// then the slices with the most rows halved until the count is met (no slice
+// cost grows).  The count, and so the grid and the workspace, are unchanged.
+namespace {
+void balance_depthwise(const Problem& p, Plan* out) {
+  conv_wgrad_plan_t& pub = out->pub;
+  const int64_t ks = pub.ks_count, rows = p.N * p.Ho;
+  if (ks < 2 || ks > Plan::kDwMaxSlices || rows > (1 << 22)) return;
+  int32_t* st = out->dw_starts;
+  auto greedy = [&](int64_t T, bool fill) -> int64_t {
+    int64_t count = 0, cost = 0;
+    for (int64_t r = 0; r < rows; ++r) {
+      const int64_t add = r % p.Ho == 0 ? p.R : p.stride;   // a segment's first row stages R rows
+      if (count == 0 || cost + add > T) {
+        if (count >= ks) return count + 1;                   // over the count: T is too small
+        if (fill) st[count] = (int32_t)r;
+        ++count;
+        cost = p.R;
+      } else {
+        cost += add;
+      }
+    }
+    return count;
+  };
+  int64_t lo = p.R, hi = p.N * (p.stride * (p.Ho - 1) + p.R);
+  while (lo < hi) {
+    const int64_t mid = lo + (hi - lo) / 2;
+    if (greedy(mid, false) <= ks) hi = mid;
+    else lo = mid + 1;
+  }
+  int64_t count = greedy(lo, true);
+  st[count] = (int32_t)rows;
+  while (count < ks) {
+    int64_t best = 0;
+    for (int64_t i = 1; i < count; ++i)
+      if (st[i + 1] - st[i] > st[best + 1] - st[best]) best = i;
+    const int32_t len = st[best + 1] - st[best];
+    if (len < 2) return;   // cannot happen: ks <= rows (leave the uniform slices)
+    for (int64_t i = count + 1; i > best + 1; --i) st[i] = st[i - 1];
+    st[best + 1] = st[best] + len / 2;
+    ++count;
+  }
+  int32_t longest = 0;
+  for (int64_t i = 0; i < ks; ++i) longest = st[i + 1] - st[i] > longest ? st[i + 1] - st[i] : longest;
+  pub.units_per_slice = longest;
+  out->dw_balanced = 1;
+}
+}  // namespace
+
 conv_wgrad_status_t make_plan(const conv_wgrad_desc2_t* desc, Plan* out) {
   if (!desc || !out) return CONV_WGRAD_ERR_NULL_ARG;
   memset(out, 0, sizeof(*out));
@@ -476,7 +530,9 @@ conv_wgrad_status_t make_plan(const conv_wgrad_desc2_t* desc, Plan* out) {
     if (!mul_ok(p.N, p.Ho, &units)) return CONV_WGRAD_ERR_UNSUPPORTED;
     // Four-wave workgroups, as many per CU as the LDS holds.
     const int64_t per_cu = kDwLdsMax / out->dw_lds;
-    return choose_split(units, out->c_tiles, desc->split_k, 8, 256 * per_cu, 4, p, &pub);
+    st = choose_split(units, out->c_tiles, desc->split_k, 8, 256 * per_cu, 4, p, &pub);
+    if (st == CONV_WGRAD_OK) balance_depthwise(p, out);
+    return st;
   }
   if (small_groups && plan_grouped16_rows(p, out)) {
     pub.path = CONV_WGRAD_PATH_DIRECT;

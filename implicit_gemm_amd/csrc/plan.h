@@ -65,6 +65,12 @@ struct Plan {
   int32_t qa, qb;          // fp32 packed rows: dY and X pixel slots between a unit's rows
   // Depthwise: staged X row length (elements), LDS bytes, column of dY element 0.
   int32_t dw_xl, dw_lds, dw_off;
+  // Depthwise: slice s covers output rows [dw_starts[s], dw_starts[s + 1])
+  // when dw_balanced (slices balanced by staging steps), else uniform runs of
+  // units_per_slice rows.
+  static constexpr int kDwMaxSlices = 256;
+  int32_t dw_balanced;
+  int32_t dw_starts[kDwMaxSlices + 1];
   // Direct path: lanes per workgroup.  Row-unit dense kernel: 256 (two
   // workgroups per CU, each stages and computes its own units) or 512 (one
   // workgroup per CU in two ping-pong halves).

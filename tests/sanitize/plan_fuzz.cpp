@@ -31,8 +31,22 @@ int64_t pick(const int64_t* v, int n) { return v[next() % (uint64_t)n]; }
 int check(const cw::Plan& p, const char* what) {
   const conv_wgrad_plan_t& q = p.pub;
   if (q.ks_count < 1 || q.units_per_slice < 1 || q.units < 1) return fprintf(stderr, "%s: empty plan\n", what), 1;
-  if ((int64_t)(q.ks_count - 1) * q.units_per_slice >= q.units || (int64_t)q.ks_count * q.units_per_slice < q.units)
+  if (p.dw_balanced) {
+    // Depthwise slices balanced by staging steps: a boundary table from 0 to
+    // the units, strictly increasing, whose longest slice is units_per_slice.
+    if (q.ks_count > cw::Plan::kDwMaxSlices || p.dw_starts[0] != 0 || p.dw_starts[q.ks_count] != q.units)
+      return fprintf(stderr, "%s: balanced slices do not cover the units\n", what), 1;
+    int64_t longest = 0;
+    for (int i = 0; i < q.ks_count; ++i) {
+      const int64_t len = (int64_t)p.dw_starts[i + 1] - p.dw_starts[i];
+      if (len < 1) return fprintf(stderr, "%s: empty balanced slice\n", what), 1;
+      if (len > longest) longest = len;
+    }
+    if (longest != q.units_per_slice) return fprintf(stderr, "%s: balanced slice length\n", what), 1;
+  } else if ((int64_t)(q.ks_count - 1) * q.units_per_slice >= q.units ||
+             (int64_t)q.ks_count * q.units_per_slice < q.units) {
     return fprintf(stderr, "%s: slices do not cover the units exactly\n", what), 1;
+  }
   if (q.grid != q.tiles * q.ks_count) return fprintf(stderr, "%s: grid\n", what), 1;
   if ((q.ks_count > 1) != (q.ws_bytes > 0)) return fprintf(stderr, "%s: workspace\n", what), 1;
   return 0;

@@ -200,8 +200,12 @@ def check_plan_invariants(d, p):
         assert p.units == -(-p.L // p.unit_rows)
     ups, ks = p.units_per_slice, p.ks_count
     assert ks >= 1 and ups >= 1
-    assert (ks - 1) * ups < p.units <= ks * ups       # last slice non-empty, all covered
-    assert ks == -(-p.units // ups)
+    if p.variant == 12 and 2 <= ks <= 256:
+        # depthwise slices balanced by staging steps: ups is the longest slice
+        assert ks * ups >= p.units and ups >= -(-p.units // ks) and ks <= p.units
+    else:
+        assert (ks - 1) * ups < p.units <= ks * ups       # last slice non-empty, all covered
+        assert ks == -(-p.units // ups)
     if d.split_k >= 1:
         assert ks <= d.split_k
         assert ups == -(-p.units // min(d.split_k, p.units))
