@@ -111,8 +111,10 @@ typedef struct conv_wgrad_plan {
   int64_t E;               /* dW elements K*R*S*Cg */
   int64_t unit_rows;       /* reduction rows per unit (a unit is the smallest slice grain) */
   int64_t units;           /* reduction units: ceil(L / unit_rows) or per-path equivalent */
-  int64_t units_per_slice; /* ceil(units / requested degree) */
-  int32_t ks_count;        /* slices: ceil(units / units_per_slice) >= 1; no slice is empty */
+  int64_t units_per_slice; /* ceil(units / requested degree); depthwise with 2..256 slices: the
+                              longest slice (slices there are balanced by the X rows each stages) */
+  int32_t ks_count;        /* slices >= 1, none empty: ceil(units / units_per_slice), except for
+                              balanced depthwise slices, whose count is the uniform one's */
   int32_t needs_reduce;    /* 1 iff ks_count > 1: the only condition for launching stage 2 */
   int64_t tiles;           /* output tiles per slice */
   int64_t grid;            /* stage-1 workgroups = tiles * ks_count */

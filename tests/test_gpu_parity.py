@@ -389,3 +389,42 @@ def test_dense16_multirow_units(idx):
     x, dy = wd.random_inputs(shp, dtype, seed=700 + idx, x_dist=wd.Dist("normal", 1.0),
                              dy_dist=wd.Dist("normal", 0.1))
     check_against_oracle(x, dy, shp, dtype, split_k=split_k)
+
+
+# Depthwise slices balanced by the X rows each stages (2..256 slices), or
+# uniform (one slice, or more than 256): (N, C, H, W, R, pad, stride, split_k, bias)
+DW_BALANCED_CASES = [
+    (5, 64, 13, 13, 7, 3, 1, 2, True),      # two slices across five images
+    (5, 64, 13, 13, 7, 3, 1, 7, False),     # slices straddling image boundaries
+    (5, 64, 13, 13, 7, 3, 1, 13, True),
+    (3, 128, 20, 20, 5, 2, 1, 29, False),
+    (4, 64, 17, 17, 3, 1, 1, 64, True),     # one row per slice in places
+    (4, 64, 33, 33, 7, 3, 2, 11, True),     # stride 2
+    (128, 64, 6, 6, 3, 1, 1, 600, False),   # 384 slices: uniform
+    (2, 64, 9, 9, 11, 5, 1, 5, True),       # 11x11 (3x3 filter blocks)
+]
+
+
+@pytest.mark.parametrize("idx", range(len(DW_BALANCED_CASES)))
+def test_depthwise_balanced_slices(idx):
+    import torch
+    import implicit_gemm_amd as iga
+    N, C, H, W, R, pad, stride, split_k, bias = DW_BALANCED_CASES[idx]
+    log("depthwise balanced case", idx, DW_BALANCED_CASES[idx])
+    shp = wd.ConvShape(N, C, H, W, C, R, R, pad=pad, stride=stride, groups=C)
+    x, dy = wd.make_inputs(wd.Workload("dwb%d" % idx, shp, "bf16", wd.Dist("normal", 1.0), wd.Dist("normal", 0.1),
+                                       9700 + idx, ""))
+    xd, dyd = to_device(x, "bf16"), to_device(dy, "bf16")
+    plan = iga.get_plan(iga.desc_for(xd, dyd, R, R, pad, stride, 1, C, split_k))
+    ups = -(-plan.units // min(split_k, plan.units))
+    assert plan.variant == 12 and plan.ks_count == -(-plan.units // ups)
+    out = iga.wgrad(xd, dyd, R, R, pad, stride, 1, C, split_k=split_k, bias=bias)
+    torch.cuda.synchronize()
+    got = (out[0] if bias else out).cpu().numpy().astype(np.float64)
+    ref, den = oracle.wgrad_ref(x, dy, R, R, pad, stride, 1, C)
+    err = oracle.normalised_error(got, ref, den)
+    log("  ks", plan.ks_count, "longest slice", plan.units_per_slice, "error %.3e" % err)
+    assert err <= oracle.TOL["bf16"]
+    assert np.all(np.isfinite(got)) and np.count_nonzero(got == 0.0) == 0
+    if bias:
+        check_bias_against_oracle(dy, out[1].cpu().numpy(), "bf16")
