@@ -30,10 +30,11 @@
 //       the same SIMDs.  At the end the halves' accumulators are added (half 1
 //       into half 0, a fixed order) and half 0 writes the slab.
 //
-// Two assignments of reduction rows to the MFMA k index:
+// Three assignments of reduction rows to the MFMA k index:
 //   * interleaved: lane group lg (lanes 16lg .. 16lg + 15) takes pixel 4k + lg
 //     in k-step k, so each k-step reads SB X values (one per tap);
-//   * quarters (stride 1, dilation 1, one unit per output row, 256 lanes):
+//   * quarters (stride 1, dilation 1, one unit per output row, 256 lanes,
+//     rows the packed form below does not take):
 //     lane group lg takes the contiguous pixels lg*Q .. lg*Q + Q - 1,
 //     Q = ceil(Wo / 4), pixel lg*Q + k in k-step k.  Tap s then reads X slot
 //     lg*Q + k + s, which tap s - 1 reads in k-step k + 1: each k-step reads
